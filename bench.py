@@ -1,0 +1,181 @@
+"""Benchmark: one decode step of paged MLA latent attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch: write the batch's newest
+token rows into the paged cache (mla_cache_write), decode every request over its
+context in page-aligned partitions (mla_decode_bf16, partials kept), then merge the
+partitions by log-sum-exp (mla_merge_lse).  Inputs are synthetic and resident in
+HBM before timing starts.
+
+Default workload: the long-context batch, 4 requests x 262,144 tokens, 16 heads,
+64-token pages drawn at random from a 32,768-page pool, 64 partitions per request.
+Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload long_context]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+METRIC = "latent-cache read GB/s (fraction of HBM peak) + decode tokens/s, H=16"
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_context")
+    ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def _cpu_baseline(w, requests):
+    """Time the fp64 oracle on a bounded sample of the same workload, on the host cores."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    pool = w.poisoned_pool()
+    idx = np.concatenate([np.searchsorted(w.slots, _request_slots(w, b)) for b in requests])
+    oracle.cache_write(pool, w.latent[idx], w.k_pe[idx], w.slots[idx], w.fmt)
+    t = time.perf_counter()
+    oracle.decode(w.q, pool, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=requests)
+    dt = time.perf_counter() - t
+    tokens = int(sum(int(w.seq_lens[b]) for b in requests))
+    return {
+        "value": round(tokens * w.row_bytes / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 NumPy oracle, requests {list(requests)} of the {w.name} batch "
+                  f"({tokens} tokens, {w.heads} heads), {dt:.1f} s; tokens/s {tokens / dt:.0f}; "
+                  f"host cpu_count {os.cpu_count()}",
+    }
+
+
+def _request_slots(w, b):
+    t = np.arange(int(w.seq_lens[b]), dtype=np.int64)
+    return w.block_table[b].astype(np.int64)[t // w.page_size] * w.page_size + t % w.page_size
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the multi-GPU split of this path is described in DESIGN.md but not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_mla_latent_amd as mla
+    import workloads
+
+    w = workloads.NAMED[args.workload]()
+    S = args.splits or workloads.BENCH_SPLITS[args.workload]
+    dev = torch.device("cuda:0")
+    fmt = mla.MLA_CACHE_BF16_576 if w.fmt == "bf16" else mla.MLA_CACHE_FP8_656
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---- inputs resident in HBM ------------------------------------------------------
+    if w.fmt == "bf16":
+        pool = torch.full((w.num_pages, w.page_size, 576), 0x7FC0, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    else:
+        pool = torch.full((w.num_pages, w.page_size, 656), 0xFF, dtype=torch.uint8, device=dev)
+    mla.mla_cache_write(bf16(w.latent), bf16(w.k_pe), torch.from_numpy(w.slots).to(dev), pool, fmt)
+    q = bf16(w.q)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    new_lat, new_pe = bf16(w.new_latent), bf16(w.new_k_pe)
+    new_slots = torch.from_numpy(w.new_slots).to(dev)
+    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, mla.mla_decode_workspace_size(w.batch, w.heads, S)), dtype=torch.uint8, device=dev)
+    decode = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        mla.mla_cache_write(new_lat, new_pe, new_slots, pool, fmt)
+        if e: e[1].record(stream)
+        if S > 1:
+            po, pl = decode(q, pool, bt, lens, w.scale, num_splits=S, workspace=ws, partials_only=True)
+            if e: e[2].record(stream)
+            mla.mla_merge_lse(po, pl, out=out, lse=lse)
+        else:
+            decode(q, pool, bt, lens, w.scale, num_splits=1, out=out, lse=lse)
+            if e: e[2].record(stream)
+        if e: e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    t_write = np.mean([e[0].elapsed_time(e[1]) for e in ev])
+    t_decode = np.mean([e[1].elapsed_time(e[2]) for e in ev])
+    t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev])
+    live = (w.seq_lens > 0)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(o[live]).all() and np.isfinite(l[live]).all(), "non-finite decode output"
+
+    cache_bytes = w.cache_bytes_read()
+    gbs = cache_bytes / (ms_step * 1e-3) / 1e9
+    decode_gbs = cache_bytes / (t_decode * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.fmt,
+        "data": "synthetic",
+        "hbm_fraction": round(gbs / HBM_PEAK_GBS, 4),
+        "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "config": {
+            "workload": w.name, "batch": w.batch, "heads": w.heads, "context_tokens": w.tokens,
+            "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
+            "cache_row_bytes": w.row_bytes, "cache_bytes_per_step": cache_bytes,
+        },
+        "kernel_ms": {"cache_write": round(t_write, 4), "decode": round(t_decode, 4), "merge": round(t_merge, 4)},
+        "roofline": {
+            "kernel": "decode_kernel",
+            "bound": "hbm",
+            "achieved": round(decode_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        req = [0, 1] if w.batch >= 2 else [0]
+        result["cpu_baseline"] = _cpu_baseline(w, req)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * mla.h - C ABI of libmla.so: multi-head latent attention (MLA) decode over a
+ * paged latent KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sabi-mla-vllm, opening paragraph and "What the plugin does";
+ * vLLM pull request 55543, description and the review of its equivalence
+ * test): every cached token holds one 576-value row per layer, a 512-wide
+ * latent followed by one shared 64-wide rotary key.  An absorbed query per
+ * head, cat(q_latent[512], q_pe[64]), scores every row of its request's
+ * context, s_t = softmax_scale * <q, row_t> over all 576 values; the softmax
+ * runs over the cache tokens; the output is the softmax-weighted sum of the
+ * 512-wide latents, returned with the natural-log log-sum-exp of the scores.
+ *
+ * Paging: a request's token t lives in slot
+ *     block_table[b * block_table_stride + t / page_size] * page_size + t % page_size
+ * and the row starts at byte slot * row_bytes.  All slot and byte offsets are
+ * formed in 64-bit arithmetic (sabi-mla-vllm, "B300 fix (0.2.0)": a 32-bit
+ * element offset wraps at slot 2^31 / 576 = 3,728,270).
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers on the current HIP device, row-major,
+ *    contiguous; every pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *    are asynchronous on that stream, never synchronise the device and never
+ *    read device memory from the host.
+ *  - The caller owns all memory.  The library allocates nothing and keeps no
+ *    state beyond a per-device architecture check and a thread-local message.
+ *  - Arguments are validated on the host before any launch.  On error the call
+ *    returns a nonzero MLA_ERR_* code, launches nothing and records a message
+ *    (mla_last_error_message) naming the offending argument.  Nothing aborts,
+ *    throws or prints.
+ *  - Conditions that cannot be checked without reading device memory are
+ *    preconditions: block-table entries inside the context must lie in
+ *    [0, num_pages), and 0 <= seq_lens[b] <= block_table_stride * page_size.
+ *    Entries past a request's last page are never read (may hold -1).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MLA_API __attribute__((visibility("default")))
+#else
+#define MLA_API
+#endif
+
+enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,      /* a required pointer is NULL                            */
+  MLA_ERR_SHAPE = 2,     /* a size or count is out of range                       */
+  MLA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                      */
+  MLA_ERR_WORKSPACE = 4, /* workspace missing or smaller than required            */
+  MLA_ERR_ARCH = 5,      /* the current device is not gfx950                      */
+  MLA_ERR_HIP = 6        /* a HIP runtime call or kernel launch failed            */
+};
+
+enum {
+  MLA_CACHE_BF16_576 = 0, /* 576 bf16 values, 1152 bytes per row                  */
+  MLA_CACHE_FP8_656 = 1   /* 512 e4m3 codes, 4 fp32 block scales, 64 bf16 = 656 B */
+};
+
+enum { MLA_LATENT = 512, MLA_ROPE = 64, MLA_ROW = 576, MLA_MAX_HEADS = 16 };
+
+/* Bytes of workspace mla_decode_bf16 / mla_decode_fp8_656 need for num_splits
+ * partitions: num_splits * batch * num_heads * (512 + 1) * 4 rounded up to 256,
+ * or 0 when num_splits == 1.  Returns 0 for invalid arguments. */
+MLA_API size_t mla_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t num_splits);
+
+/* Decode over a bf16 cache (MLA_CACHE_BF16_576).
+ *
+ * q            bf16 [batch][num_heads][576], absorbed queries (latent part first).
+ * kv_cache     bf16 [num_pages][page_size][576].
+ * num_pages    pages in the pool (>= 1); page_size tokens per page (>= 1).
+ * block_table  int32 [batch][block_table_stride]; physical page of each logical page.
+ * seq_lens     int32 [batch]; context length of each request (0 allowed).
+ * num_heads    1..16.  softmax_scale: finite float, applied to the fp32 scores.
+ * num_splits   >= 1.  Each request's pages are cut into num_splits partitions of
+ *              ceil(P / num_splits) whole pages (P = pages the request uses); each
+ *              partition returns (out, lse) for its tokens and, when num_splits > 1,
+ *              a second kernel merges them by log-sum-exp (vLLM pull request 55543:
+ *              the partial-result merge contract with (0, -inf) as the neutral
+ *              element).  The result does not depend on num_splits beyond rounding.
+ * out          fp32 [batch][num_heads][512]: softmax-weighted latent sum.
+ * lse          fp32 [batch][num_heads]: natural-log log-sum-exp of the scaled scores.
+ *              A request with seq_lens == 0 gets out = +0.0 and lse = -inf.
+ * workspace    device scratch of at least mla_decode_workspace_size() bytes when
+ *              num_splits > 1 (may be NULL otherwise); holds the partials
+ *              [num_splits][batch][num_heads][512] then [num_splits][batch][num_heads].
+ *              Passing out == lse == NULL with num_splits > 1 stops there: the
+ *              partials stay in the workspace for the caller to merge later (for
+ *              example after exchanging them with other devices) with mla_merge_lse.
+ */
+MLA_API int mla_decode_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                    const int32_t* block_table, int64_t block_table_stride,
+                    const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                    int32_t page_size, float softmax_scale, int32_t num_splits,
+                    float* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Decode over an fp8 cache (MLA_CACHE_FP8_656).  Same arguments and results as
+ * mla_decode_bf16; kv_cache is uint8 [num_pages][page_size][656], each row
+ * [0,512) OCP e4m3fn codes, [512,528) four little-endian fp32 scales (scale k
+ * multiplies latent values [128k, 128k+128)), [528,656) 64 bf16 rope values
+ * (vLLM pull request 55543, description: the 656-byte fp8_ds_mla row with
+ * per-128-block scales and bf16 rope bytes; the byte order is this library's
+ * reading, as the page lists the parts but not their order).  Latent values are
+ * code * scale, exact; q is used in bf16 as given. */
+MLA_API int mla_decode_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                       const int32_t* block_table, int64_t block_table_stride,
+                       const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                       int32_t page_size, float softmax_scale, int32_t num_splits,
+                       float* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Merge num_splits partial results over disjoint token sets (vLLM pull request
+ * 55543: partial (o, lse) pairs merge by log-sum-exp; a partition with no
+ * tokens is (0, -inf)).
+ * part_out fp32 [num_splits][batch][num_heads][512], part_lse fp32 [num_splits][batch][num_heads].
+ * out fp32 [batch][num_heads][512], lse fp32 [batch][num_heads]:
+ *   M = max_p lse_p; if M = -inf: out = 0, lse = -inf;
+ *   else w_p = exp(lse_p - M), lse = M + ln sum_p w_p, out = sum_p w_p out_p / sum_p w_p.
+ * out/lse must not overlap the partials. */
+MLA_API int mla_merge_lse(const float* part_out, const float* part_lse, int32_t num_splits,
+                  int32_t batch, int32_t num_heads, float* out, float* lse, void* stream);
+
+/* Write new tokens' rows into the cache (the cache-write step of vLLM pull
+ * request 55543, which concatenates the latent and the 64-wide rotary key into
+ * the row at each token's slot).
+ * latent bf16 [num_tokens][512]; k_pe bf16 [num_tokens][64];
+ * slot_mapping int64 [num_tokens], slot of each token; negative = skip the token.
+ * kv_cache: num_slots rows in cache_format; slots must be < num_slots and distinct
+ * (two tokens writing one slot race).
+ * MLA_CACHE_BF16_576: row = latent ++ k_pe, copied bit for bit.
+ * MLA_CACHE_FP8_656: per 128-value block a = max|x|, s = a / 448 (fp32, IEEE
+ *   division), codes = e4m3fn(x / s) rounded to nearest-even and saturated at
+ *   +-448, sign kept; a block with a == 0 stores s = 0 and codes 0x00; then the
+ *   four scales and k_pe as bf16. */
+MLA_API int mla_cache_write(const void* latent, const void* k_pe, const int64_t* slot_mapping,
+                    int32_t num_tokens, void* kv_cache, int32_t cache_format,
+                    int64_t num_slots, void* stream);
+
+MLA_API const char* mla_status_string(int status);
+/* Message describing the last failed call on this thread ("" if none). */
+MLA_API const char* mla_last_error_message(void);
+MLA_API int mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,219 @@
+"""Python binding of libmla.so: paged MLA latent decode on AMD Instinct MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the library's
+HIP kernels; PyTorch supplies device memory and the current stream.  There is no
+CPU path: if the library is missing, every call raises.
+
+Entry points (same names as the C ABI in include/mla.h):
+
+    mla_decode_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, ...)
+    mla_decode_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, ...)
+    mla_merge_lse(part_out, part_lse, out=None, lse=None)
+    mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format)
+    mla_decode_workspace_size(batch, num_heads, num_splits)
+
+Tensors: q bf16 [B, H, 576]; kv_cache bf16 [num_pages, page_size, 576] or uint8
+[num_pages, page_size, 656]; block_table int32 [B, W]; seq_lens int32 [B];
+out fp32 [B, H, 512]; lse fp32 [B, H]; latent bf16 [T, 512]; k_pe bf16 [T, 64];
+slot_mapping int64 [T].  All on the same HIP device, contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+
+MLA_OK = 0
+MLA_CACHE_BF16_576 = 0
+MLA_CACHE_FP8_656 = 1
+LATENT, ROPE, ROW = 512, 64, 576
+ROW_BYTES = {MLA_CACHE_BF16_576: 1152, MLA_CACHE_FP8_656: 656}
+MAX_HEADS = 16
+
+EXPORTED = (
+    "mla_decode_workspace_size", "mla_decode_bf16", "mla_decode_fp8_656", "mla_merge_lse",
+    "mla_cache_write", "mla_status_string", "mla_last_error_message", "mla_abi_version",
+)
+
+
+class MlaError(RuntimeError):
+    """A libmla call returned a nonzero status."""
+
+    def __init__(self, fn: str, status: int, name: str, message: str):
+        super().__init__(f"{fn} failed: {name} ({status}): {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libmla.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_mla_latent_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_i32, c_i64, c_sz, c_f, vp = (ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                           ctypes.c_float, ctypes.c_void_p)
+    lib.mla_decode_workspace_size.argtypes = [c_i32, c_i32, c_i32]
+    lib.mla_decode_workspace_size.restype = c_sz
+    dec = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
+    for name in ("mla_decode_bf16", "mla_decode_fp8_656"):
+        getattr(lib, name).argtypes = dec
+        getattr(lib, name).restype = c_int
+    lib.mla_merge_lse.argtypes = [vp, vp, c_i32, c_i32, c_i32, vp, vp, vp]
+    lib.mla_merge_lse.restype = c_int
+    lib.mla_cache_write.argtypes = [vp, vp, vp, c_i32, vp, c_i32, c_i64, vp]
+    lib.mla_cache_write.restype = c_int
+    lib.mla_status_string.argtypes = [c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_last_error_message.argtypes = []
+    lib.mla_last_error_message.restype = ctypes.c_char_p
+    lib.mla_abi_version.argtypes = []
+    lib.mla_abi_version.restype = c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MLA_OK:
+        lib = library()
+        raise MlaError(fn, status, lib.mla_status_string(status).decode(), lib.mla_last_error_message().decode())
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device: torch.device | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on a HIP device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def mla_decode_workspace_size(batch: int, num_heads: int, num_splits: int) -> int:
+    return int(library().mla_decode_workspace_size(batch, num_heads, num_splits))
+
+
+def _decode(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
+            softmax_scale, num_splits, out, lse, workspace, partials_only=False):
+    lib = library()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(kv_cache, "kv_cache", cache_dtype, 3, dev)
+    if kv_cache.shape[2] != row_bytes_last:
+        raise ValueError(f"kv_cache rows must have {row_bytes_last} elements, got {kv_cache.shape[2]}")
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, H, D = q.shape
+    if D != ROW:
+        raise ValueError(f"q rows must have {ROW} values, got {D}")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have one row per request")
+    if partials_only:
+        if num_splits < 2 or out is not None or lse is not None:
+            raise ValueError("partials_only needs num_splits > 1 and no out/lse")
+    else:
+        if out is None:
+            out = torch.empty((B, H, LATENT), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, 3, dev)
+        _need(lse, "lse", torch.float32, 2, dev)
+    ws_bytes = 0
+    if num_splits > 1:
+        need = mla_decode_workspace_size(B, H, num_splits)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    status = getattr(lib, fn)(
+        q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1],
+        seq_lens.data_ptr(), B, H, kv_cache.shape[1], float(softmax_scale), int(num_splits),
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev))
+    _check(fn, status)
+    if partials_only:
+        n = num_splits * B * H
+        flat = workspace.view(torch.uint8)[: n * (LATENT + 1) * 4].view(torch.float32)
+        return flat[: n * LATENT].view(num_splits, B, H, LATENT), flat[n * LATENT:].view(num_splits, B, H)
+    return out, lse
+
+
+def mla_decode_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                    workspace=None, partials_only=False):
+    """Decode over a bf16 cache [num_pages, page_size, 576]; returns (out [B,H,512], lse [B,H]).
+
+    partials_only=True (num_splits > 1) skips the merge and returns the partials
+    (part_out [S,B,H,512], part_lse [S,B,H]) as views of the workspace.
+    """
+    return _decode("mla_decode_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
+                   softmax_scale, num_splits, out, lse, workspace, partials_only)
+
+
+def mla_decode_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                       workspace=None, partials_only=False):
+    """Decode over an fp8 cache uint8 [num_pages, page_size, 656]; returns (out, lse) or the partials."""
+    return _decode("mla_decode_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
+                   softmax_scale, num_splits, out, lse, workspace, partials_only)
+
+
+def mla_merge_lse(part_out, part_lse, out=None, lse=None):
+    """Merge partials [S, B, H, 512] / [S, B, H] by log-sum-exp; returns (out, lse)."""
+    lib = library()
+    _need(part_out, "part_out", torch.float32, 4)
+    dev = part_out.device
+    _need(part_lse, "part_lse", torch.float32, 3, dev)
+    S, B, H, D = part_out.shape
+    if D != LATENT or tuple(part_lse.shape) != (S, B, H):
+        raise ValueError("part_out must be [S, B, H, 512] and part_lse [S, B, H]")
+    if out is None:
+        out = torch.empty((B, H, LATENT), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    _check("mla_merge_lse", lib.mla_merge_lse(part_out.data_ptr(), part_lse.data_ptr(), S, B, H,
+                                              out.data_ptr(), lse.data_ptr(), _stream(dev)))
+    return out, lse
+
+
+def mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format):
+    """Write rows for new tokens at slot_mapping (negative = skip) into kv_cache."""
+    lib = library()
+    _need(latent, "latent", torch.bfloat16, 2)
+    dev = latent.device
+    _need(k_pe, "k_pe", torch.bfloat16, 2, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    if cache_format == MLA_CACHE_BF16_576:
+        _need(kv_cache, "kv_cache", torch.bfloat16, 3, dev)
+        if kv_cache.shape[2] != ROW:
+            raise ValueError("bf16 kv_cache rows must have 576 values")
+    elif cache_format == MLA_CACHE_FP8_656:
+        _need(kv_cache, "kv_cache", torch.uint8, 3, dev)
+        if kv_cache.shape[2] != 656:
+            raise ValueError("fp8 kv_cache rows must have 656 bytes")
+    else:
+        raise ValueError(f"unknown cache_format {cache_format}")
+    T = latent.shape[0]
+    if latent.shape[1] != LATENT or tuple(k_pe.shape) != (T, ROPE) or slot_mapping.shape[0] != T:
+        raise ValueError("latent must be [T, 512], k_pe [T, 64], slot_mapping [T]")
+    num_slots = kv_cache.shape[0] * kv_cache.shape[1]
+    _check("mla_cache_write", lib.mla_cache_write(latent.data_ptr(), k_pe.data_ptr(), slot_mapping.data_ptr(), T,
+                                                  kv_cache.data_ptr(), int(cache_format), num_slots, _stream(dev)))

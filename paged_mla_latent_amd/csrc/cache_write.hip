@@ -1,0 +1,88 @@
+// Cache write: the row of each new token, latent[512] ++ k_pe[64], goes to its slot
+// (vLLM pull request 55543: the cache-write step concatenates the latent and the
+// 64-wide rotary key into the 576-wide / 656-byte row).
+//
+// One wavefront per token.  Byte offsets are slot * row_bytes in 64-bit arithmetic.
+//  bf16: 1152 bytes copied bit for bit (64 lanes x 16 B latent, 8 lanes x 16 B rope).
+//  fp8 (656 bytes): lane l owns latent values 8l..8l+7; the 16 lanes of block k = l/16
+//    reduce a = max|x| (fp32, exact), s = a / 448 (IEEE division), each code is
+//    e4m3fn(x / s) rounded to nearest-even.  The quotient is clamped to +-448 before
+//    the hardware conversion, which rounds to nearest-even but does not saturate; a
+//    block with a == 0 stores s = 0 and zero codes.  Bytes: [0,512) codes,
+//    [512,528) scales (little-endian fp32), [528,656) k_pe as bf16.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+__global__ __launch_bounds__(256) void cache_write_bf16(const uint16_t* __restrict__ latent,
+                                                        const uint16_t* __restrict__ k_pe,
+                                                        const int64_t* __restrict__ slots, int T,
+                                                        uint8_t* __restrict__ cache) {
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= T) return;
+  const int64_t slot = slots[tok];
+  if (slot < 0) return;
+  uint8_t* row = cache + slot * (int64_t)kRowBytesBf16;
+  *(u32x4*)(row + 16 * lane) = *(const u32x4*)(latent + (int64_t)tok * kLatent + 8 * lane);
+  if (lane < 8) *(u32x4*)(row + 1024 + 16 * lane) = *(const u32x4*)(k_pe + (int64_t)tok * kRope + 8 * lane);
+}
+
+__device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__global__ __launch_bounds__(256) void cache_write_fp8(const uint16_t* __restrict__ latent,
+                                                       const uint16_t* __restrict__ k_pe,
+                                                       const int64_t* __restrict__ slots, int T,
+                                                       uint8_t* __restrict__ cache) {
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= T) return;
+  const int64_t slot = slots[tok];
+  if (slot < 0) return;
+  uint8_t* row = cache + slot * (int64_t)kRowBytesFp8;
+
+  const u32x4 raw = *(const u32x4*)(latent + (int64_t)tok * kLatent + 8 * lane);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_to_float(raw[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_to_float(raw[i] >> 16);
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+#pragma unroll
+  for (int mask = 8; mask >= 1; mask >>= 1) a = fmaxf(a, __shfl_xor(a, mask, 64));
+  const float s = a / 448.0f;
+  u32x2 codes = {0u, 0u};
+  if (s != 0.f) {
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(x[i] / s, -448.0f), 448.0f);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t v = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * w], y[4 * w + 1], 0, false);
+      codes[w] = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * w + 2], y[4 * w + 3], v, true);
+    }
+  }
+  *(u32x2*)(row + 8 * lane) = codes;
+  if ((lane & 15) == 0) *(float*)(row + 512 + 4 * (lane >> 4)) = s;
+  if (lane < 8) *(u32x4*)(row + 528 + 16 * lane) = *(const u32x4*)(k_pe + (int64_t)tok * kRope + 8 * lane);
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const uint16_t* latent, const uint16_t* k_pe, const int64_t* slots,
+                              int num_tokens, uint8_t* cache, int fp8, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const dim3 grid((unsigned)((num_tokens + 3) / 4));
+  if (fp8)
+    hipLaunchKernelGGL(cache_write_fp8, grid, dim3(256), 0, stream, latent, k_pe, slots, num_tokens, cache);
+  else
+    hipLaunchKernelGGL(cache_write_bf16, grid, dim3(256), 0, stream, latent, k_pe, slots, num_tokens, cache);
+  return hipGetLastError();
+}
+
+}  // namespace mla

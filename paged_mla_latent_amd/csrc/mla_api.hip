@@ -1,0 +1,213 @@
+// C ABI of libmla.so (declared in include/mla.h): host-side argument validation,
+// device-architecture check and kernel launches.  No allocation, no synchronisation.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local char g_message[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_message, sizeof(g_message), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device cache of the architecture check: 0 unknown, 1 gfx950, -1 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(MLA_ERR_ARCH, "no usable HIP device (hipGetDevice: %s)", hipGetErrorString(e));
+  if (dev >= kMaxDevices) return fail(MLA_ERR_ARCH, "device index %d exceeds %d", dev, kMaxDevices);
+  int state = g_arch[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(MLA_ERR_ARCH, "hipGetDeviceProperties(%d): %s", dev, hipGetErrorString(e));
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch[dev].store(state, std::memory_order_relaxed);
+    if (state < 0)
+      return fail(MLA_ERR_ARCH, "device %d is %s; this library is built for gfx950 (MI355X) only", dev,
+                  prop.gcnArchName);
+  }
+  if (state < 0) return fail(MLA_ERR_ARCH, "device %d is not gfx950 (MI355X)", dev);
+  return MLA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MLA_OK;
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t workspace_bytes_for(int64_t batch, int64_t heads, int64_t splits) {
+  if (splits <= 1) return 0;
+  const size_t n = (size_t)splits * (size_t)batch * (size_t)heads;
+  const size_t bytes = n * (MLA_LATENT + 1) * sizeof(float) + 64;  // + lse alignment slack
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int decode_common(int fp8, const void* q, const void* kv_cache, int64_t num_pages,
+                  const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
+                  int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
+                  int32_t num_splits, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  const char* fn = fp8 ? "mla_decode_fp8_656" : "mla_decode_bf16";
+  if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
+  if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
+  if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
+  if (!seq_lens) return fail(MLA_ERR_NULL, "%s: seq_lens is NULL", fn);
+  // out == lse == NULL with num_splits > 1 leaves the partials in the workspace (no merge).
+  const bool partials_only = !out && !lse && num_splits > 1;
+  if (!out && !partials_only) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
+  if (!lse && !partials_only) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
+  if (batch < 1 || batch > 65535) return fail(MLA_ERR_SHAPE, "%s: batch=%d outside [1, 65535]", fn, batch);
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
+    return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_HEADS);
+  if (page_size < 1) return fail(MLA_ERR_SHAPE, "%s: page_size=%d must be >= 1", fn, page_size);
+  if (num_pages < 1) return fail(MLA_ERR_SHAPE, "%s: num_pages=%lld must be >= 1", fn, (long long)num_pages);
+  if (block_table_stride < 1)
+    return fail(MLA_ERR_SHAPE, "%s: block_table_stride=%lld must be >= 1", fn, (long long)block_table_stride);
+  if (block_table_stride > ((int64_t)1 << 31) / page_size + 1)
+    return fail(MLA_ERR_SHAPE, "%s: block_table_stride * page_size exceeds the int32 token range", fn);
+  if (num_splits < 1 || num_splits > 65536)
+    return fail(MLA_ERR_SHAPE, "%s: num_splits=%d outside [1, 65536]", fn, num_splits);
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_SHAPE, "%s: softmax_scale is not finite", fn);
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(block_table) || !aligned16(seq_lens) ||
+      !aligned16(out) || !aligned16(lse))
+    return fail(MLA_ERR_ALIGN, "%s: every tensor pointer must be 16-byte aligned", fn);
+  float* part_out = nullptr;
+  float* part_lse = nullptr;
+  if (num_splits > 1) {
+    const size_t need = workspace_bytes_for(batch, num_heads, num_splits);
+    if (!workspace) return fail(MLA_ERR_WORKSPACE, "%s: num_splits=%d needs a workspace", fn, num_splits);
+    if (!aligned16(workspace)) return fail(MLA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+    if (workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
+    part_out = static_cast<float*>(workspace);
+    part_lse = part_out + (size_t)num_splits * batch * num_heads * MLA_LATENT;
+  }
+  int rc = check_device();
+  if (rc != MLA_OK) return rc;
+
+  mla::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.cache = static_cast<const uint8_t*>(kv_cache);
+  p.block_table = block_table;
+  p.bt_stride = block_table_stride;
+  p.seq_lens = seq_lens;
+  p.batch = batch;
+  p.heads = num_heads;
+  p.page_size = page_size;
+  p.num_splits = num_splits;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  p.out = out;
+  p.lse = lse;
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = hip_status(fp8 ? mla::launch_decode_fp8(p, s) : mla::launch_decode_bf16(p, s), fn);
+  if (rc != MLA_OK || num_splits == 1 || partials_only) return rc;
+  return hip_status(mla::launch_merge(part_out, part_lse, num_splits, batch, num_heads, out, lse, s),
+                    "mla_merge_lse (after decode)");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t num_splits) {
+  if (batch < 1 || num_heads < 1 || num_splits < 1) return 0;
+  return workspace_bytes_for(batch, num_heads, num_splits);
+}
+
+int mla_decode_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                    int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                    int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(0, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+                       page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                       int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                       int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+                       page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_merge_lse(const float* part_out, const float* part_lse, int32_t num_splits, int32_t batch,
+                  int32_t num_heads, float* out, float* lse, void* stream) {
+  const char* fn = "mla_merge_lse";
+  if (!part_out) return fail(MLA_ERR_NULL, "%s: part_out is NULL", fn);
+  if (!part_lse) return fail(MLA_ERR_NULL, "%s: part_lse is NULL", fn);
+  if (!out) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
+  if (!lse) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
+  if (num_splits < 1 || num_splits > 65536)
+    return fail(MLA_ERR_SHAPE, "%s: num_splits=%d outside [1, 65536]", fn, num_splits);
+  if (batch < 1) return fail(MLA_ERR_SHAPE, "%s: batch=%d must be >= 1", fn, batch);
+  if (num_heads < 1) return fail(MLA_ERR_SHAPE, "%s: num_heads=%d must be >= 1", fn, num_heads);
+  if ((int64_t)batch * num_heads > 0x7FFFFFFF) return fail(MLA_ERR_SHAPE, "%s: batch * num_heads too large", fn);
+  if (!aligned16(part_out) || !aligned16(out))
+    return fail(MLA_ERR_ALIGN, "%s: part_out and out must be 16-byte aligned", fn);
+  int rc = check_device();
+  if (rc != MLA_OK) return rc;
+  return hip_status(mla::launch_merge(part_out, part_lse, num_splits, batch, num_heads, out, lse,
+                                      static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int mla_cache_write(const void* latent, const void* k_pe, const int64_t* slot_mapping, int32_t num_tokens,
+                    void* kv_cache, int32_t cache_format, int64_t num_slots, void* stream) {
+  const char* fn = "mla_cache_write";
+  if (num_tokens < 0) return fail(MLA_ERR_SHAPE, "%s: num_tokens=%d is negative", fn, num_tokens);
+  if (cache_format != MLA_CACHE_BF16_576 && cache_format != MLA_CACHE_FP8_656)
+    return fail(MLA_ERR_SHAPE, "%s: cache_format=%d unknown", fn, cache_format);
+  if (num_slots < 1) return fail(MLA_ERR_SHAPE, "%s: num_slots=%lld must be >= 1", fn, (long long)num_slots);
+  if (num_tokens == 0) return MLA_OK;
+  if (!latent) return fail(MLA_ERR_NULL, "%s: latent is NULL", fn);
+  if (!k_pe) return fail(MLA_ERR_NULL, "%s: k_pe is NULL", fn);
+  if (!slot_mapping) return fail(MLA_ERR_NULL, "%s: slot_mapping is NULL", fn);
+  if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
+  if (!aligned16(latent) || !aligned16(k_pe) || !aligned16(slot_mapping) || !aligned16(kv_cache))
+    return fail(MLA_ERR_ALIGN, "%s: every tensor pointer must be 16-byte aligned", fn);
+  int rc = check_device();
+  if (rc != MLA_OK) return rc;
+  return hip_status(mla::launch_cache_write(static_cast<const uint16_t*>(latent), static_cast<const uint16_t*>(k_pe),
+                                            slot_mapping, num_tokens, static_cast<uint8_t*>(kv_cache),
+                                            cache_format == MLA_CACHE_FP8_656, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_ARCH: return "MLA_ERR_ARCH";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+const char* mla_last_error_message(void) { return g_message; }
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Device-side helpers shared by the gfx950 kernels of libmla.
+//
+// Lane layouts used below (CDNA4 matrix cores, 64-lane wavefronts):
+//   v_mfma_f32_16x16x32_bf16  A: lane l holds A[l%16][8*(l/16) + 0..7]
+//                             B: lane l holds B[8*(l/16) + 0..7][l%16]
+//                             D: lane l holds D[4*(l/16) + 0..3][l%16]
+//   v_mfma_f32_16x16x16_bf16  same with 4 K values per lane: A[l%16][4*(l/16) + 0..3]
+//   ds_read_b64_tr_b16        within each group of 16 lanes, output lane i gets
+//                             element (i & 3) of the 4-element chunks addressed by
+//                             lanes (i >> 2) + 4*v, v = 0..3
+//   global_load_lds (16 B)    lane l writes LDS[base + 16*l]
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kRow = kLatent + kRope;  // 576 values
+constexpr int kRowBytesBf16 = 2 * kRow;  // 1152
+constexpr int kRowBytesFp8 = 656;        // 512 codes + 16 scale bytes + 128 rope bytes
+constexpr int kMaxHeads = 16;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+// The "memory" clobber keeps LDS reads of DMA'd data below the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const MLA_LDS void*)p;
+}
+
+// 16-byte global -> LDS copy (global_load_lds_dwordx4); lane l lands at lds_addr + 16 * l.
+// lds_addr must be wave-uniform.  Written as inline assembly so that the compiler does
+// not treat every later LDS read as a possible reader of this DMA and wait for it:
+// completion is tracked explicitly with wait_vmcnt<>() before the data is read.  The
+// compiler's own vmcnt waits stay correct because these loads only add younger
+// entries to the in-order vector-memory counter.  M0 is written here; on gfx950 the
+// compiler does not keep values in M0 across code that uses no M0-based instruction.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_addr)
+               : "memory");
+}
+
+// 4-byte global -> LDS copy (global_load_lds_dword); lane l lands at lds_addr + 4 * l.
+__device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                   __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_addr) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)lds_addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Two floats -> packed bf16 pair (round to nearest even), lo in bits [15:0].
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+}  // namespace mla

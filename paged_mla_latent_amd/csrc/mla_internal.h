@@ -1,0 +1,33 @@
+// Internal launch interface between the C ABI (mla_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeParams {
+  const uint16_t* q;           // bf16 [B][H][576]
+  const uint8_t* cache;        // rows of row_bytes bytes
+  const int32_t* block_table;  // [B][bt_stride]
+  int64_t bt_stride;
+  const int32_t* seq_lens;     // [B]
+  int batch;
+  int heads;
+  int page_size;
+  int num_splits;
+  float scale_log2;            // softmax_scale * log2(e)
+  float* out;                  // [B][H][512]  (num_splits == 1)
+  float* lse;                  // [B][H]
+  float* part_out;             // [S][B][H][512] (num_splits > 1)
+  float* part_lse;             // [S][B][H]
+};
+
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_merge(const float* part_out, const float* part_lse, int num_splits, int batch,
+                        int heads, float* out, float* lse, hipStream_t stream);
+hipError_t launch_cache_write(const uint16_t* latent, const uint16_t* k_pe, const int64_t* slots,
+                              int num_tokens, uint8_t* cache, int fp8, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,162 @@
+"""The C ABI boundary without a GPU: symbols, versions, argument validation.
+
+Every call below carries at least one invalid argument, so the library must refuse
+it on the host before touching any device; none of these tests launches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_mla_latent_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"MLA_API\s+[\w\s\*]+?\b(mla_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.LIB_PATH):
+        pytest.fail("libmla.so is not built (run __graft_entry__.build())")
+    return mla.library()
+
+
+def test_header_declares_the_four_operations():
+    names = _declared_functions()
+    for op in ("mla_decode_bf16", "mla_decode_fp8_656", "mla_merge_lse", "mla_cache_write"):
+        assert op in names
+    assert set(names) == set(mla.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(mla.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_only_the_c_abi_is_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True).stdout
+    text_syms = [l.split()[-1] for l in out.splitlines() if " T " in l]
+    assert sorted(text_syms) == sorted(mla.EXPORTED)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mla_abi_version() == 1
+    names = [lib.mla_status_string(i).decode() for i in range(8)]
+    assert names[:7] == ["MLA_OK", "MLA_ERR_NULL", "MLA_ERR_SHAPE", "MLA_ERR_ALIGN", "MLA_ERR_WORKSPACE",
+                         "MLA_ERR_ARCH", "MLA_ERR_HIP"]
+    assert names[7] == "MLA_ERR_UNKNOWN"
+
+
+def test_workspace_size_formula(lib):
+    assert mla.mla_decode_workspace_size(4, 16, 1) == 0
+    n = 64 * 4 * 16
+    want = (n * 513 * 4 + 64 + 255) // 256 * 256
+    assert mla.mla_decode_workspace_size(4, 16, 64) == want
+    assert mla.mla_decode_workspace_size(0, 16, 4) == 0 and mla.mla_decode_workspace_size(1, 0, 4) == 0
+
+
+# A "pointer" value that is 16-byte aligned but never dereferenced: every call below
+# fails validation before any device access.
+P = 0x1000
+MIS = 0x1008
+
+
+def _decode(lib, fn="mla_decode_bf16", **kw):
+    args = dict(q=P, kv=P, num_pages=10, bt=P, stride=4, lens=P, batch=2, heads=16, ps=64, scale=0.07,
+                splits=1, out=P, lse=P, ws=None, ws_bytes=0)
+    args.update(kw)
+    rc = getattr(lib, fn)(args["q"], args["kv"], args["num_pages"], args["bt"], args["stride"], args["lens"],
+                          args["batch"], args["heads"], args["ps"], args["scale"], args["splits"], args["out"],
+                          args["lse"], args["ws"], args["ws_bytes"], None)
+    return rc, lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("fn", ["mla_decode_bf16", "mla_decode_fp8_656"])
+@pytest.mark.parametrize("field", ["q", "kv", "bt", "lens", "out", "lse"])
+def test_decode_rejects_null(lib, fn, field):
+    rc, msg = _decode(lib, fn, **{field: None})
+    assert rc == 1 and "NULL" in msg and fn in msg
+
+
+@pytest.mark.parametrize("fn", ["mla_decode_bf16", "mla_decode_fp8_656"])
+@pytest.mark.parametrize("kw, word", [
+    (dict(heads=0), "num_heads"), (dict(heads=17), "num_heads"), (dict(batch=0), "batch"),
+    (dict(batch=70000), "batch"), (dict(ps=0), "page_size"), (dict(num_pages=0), "num_pages"),
+    (dict(stride=0), "block_table_stride"), (dict(splits=0), "num_splits"),
+    (dict(splits=70000), "num_splits"), (dict(scale=float("nan")), "softmax_scale"),
+    (dict(scale=float("inf")), "softmax_scale"), (dict(stride=1 << 40), "int32"),
+])
+def test_decode_rejects_bad_shapes(lib, fn, kw, word):
+    rc, msg = _decode(lib, fn, **kw)
+    assert rc == 2 and word in msg
+
+
+@pytest.mark.parametrize("field", ["q", "kv", "bt", "lens", "out", "lse"])
+def test_decode_rejects_misaligned(lib, field):
+    rc, msg = _decode(lib, **{field: MIS})
+    assert rc == 3 and "aligned" in msg
+
+
+def test_decode_split_needs_workspace(lib):
+    rc, msg = _decode(lib, splits=4)
+    assert rc == 4 and "workspace" in msg
+    need = mla.mla_decode_workspace_size(2, 16, 4)
+    rc, msg = _decode(lib, splits=4, ws=P, ws_bytes=need - 1)
+    assert rc == 4 and str(need) in msg
+    rc, msg = _decode(lib, splits=4, ws=MIS, ws_bytes=need)
+    assert rc == 3
+
+
+def test_merge_validation(lib):
+    f = lib.mla_merge_lse
+    assert f(None, P, 2, 1, 1, P, P, None) == 1
+    assert f(P, P, 0, 1, 1, P, P, None) == 2
+    assert f(P, P, 2, 0, 1, P, P, None) == 2
+    assert f(P, P, 2, 1, 0, P, P, None) == 2
+    assert f(MIS, P, 2, 1, 1, P, P, None) == 3
+    assert "part_out" in lib.mla_last_error_message().decode()
+
+
+def test_cache_write_validation(lib):
+    f = lib.mla_cache_write
+    assert f(P, P, P, -1, P, 0, 10, None) == 2
+    assert f(P, P, P, 1, P, 7, 10, None) == 2
+    assert f(P, P, P, 1, P, 0, 0, None) == 2
+    assert f(None, P, P, 1, P, 0, 10, None) == 1
+    assert f(P, P, P, 1, None, 1, 10, None) == 1
+    assert f(P, MIS, P, 1, P, 1, 10, None) == 3
+    assert f(None, None, None, 0, None, 0, 10, None) == 0  # nothing to write: no device needed
+
+
+def test_error_message_is_thread_local(lib):
+    import threading
+    _decode(lib, heads=99)
+    main = lib.mla_last_error_message().decode()
+    seen = []
+
+    def other():
+        seen.append(lib.mla_last_error_message().decode())
+        _decode(lib, ps=0)
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen == [""]
+    assert lib.mla_last_error_message().decode() == main and "num_heads" in main
+
+
+def test_binding_marshalling_errors_without_device():
+    import torch
+    q = torch.zeros(1, 4, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        mla.mla_decode_bf16(q, q, torch.zeros(1, 1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32), 0.1)
+    with pytest.raises(TypeError, match="bfloat16"):
+        mla.mla_decode_bf16(q.float(), q, None, None, 0.1)

@@ -1,0 +1,251 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on an MI355X.
+
+Each case: seeded workload -> rows written by mla_cache_write on the device and by
+oracle.cache_write on the host -> row bytes compared bit for bit -> each side decodes
+its own pool -> per (request, head) max |out - ref| <= 1e-2 * max |ref| and
+|lse - ref_lse| <= 1e-3; empty contexts give exactly (+0, -inf).  Pools are filled
+with NaN (bf16) or 0xFF bytes (fp8) wherever no request reads, so a stray read
+shows up as a non-finite output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_mla_latent_amd as mla
+import workloads
+from gpu_util import (FMT_CODE, assert_parity, assert_rows_bitexact, bf16_dev, device_pool, device_rows,
+                      gpu_decode, host_pool, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    assert torch.cuda.get_device_properties(0).gcnArchName.startswith("gfx950")
+    mla.library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run_case(w, splits_list, requests=None, what=""):
+    say(f"case {what or w.name}: fmt={w.fmt} B={w.batch} H={w.heads} ps={w.page_size} "
+        f"pages={w.num_pages} tokens={w.tokens} splits={splits_list}")
+    pd = device_pool(w)
+    ph = host_pool(w)
+    assert_rows_bitexact(w, pd, ph)
+    ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt,
+                                 requests=requests)
+    for S in splits_list:
+        out, lse = gpu_decode(w, pd, S)
+        assert_parity(w, out, lse, ref_o, ref_l, requests, what=f"{what or w.name} S={S}")
+    return pd, ph
+
+
+# ------------------------------------------------------------------------ small cases
+@pytest.mark.parametrize("splits", [1, 2, 16])
+def test_tiny_workload(splits):
+    w = workloads.tiny()
+    pd, ph = _run_case(w, [splits])
+    got = pd.view(torch.uint8).cpu().numpy().reshape(-1)
+    assert np.array_equal(got, ph.reshape(-1))  # whole pool, poison included
+
+
+RAGGED = [0, 1, 15, 16, 17, 100, 333, 1000, 2500]
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("ps", [1, 3, 16, 64, 784])
+def test_ragged_lengths_and_page_sizes(fmt, ps):
+    pages = sum(-(-L // ps) for L in RAGGED) + 7
+    w = workloads.make_workload(f"ragged_ps{ps}", seq_lens=RAGGED, heads=16, page_size=ps, num_pages=pages,
+                                fmt=fmt, seed=ps)
+    _run_case(w, [1, 3])
+
+
+@pytest.mark.parametrize("heads", [1, 3, 8, 16])
+def test_head_counts(heads):
+    w = workloads.make_workload(f"heads{heads}", seq_lens=[700, 33, 1], heads=heads, page_size=64, num_pages=40,
+                                seed=heads)
+    _run_case(w, [1, 2])
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_row_magnitude_spread(fmt):
+    """Row scales log-uniform over four decades, odd page size, shuffled pages."""
+    w = workloads.make_workload("spread", seq_lens=[3000, 1500, 784, 785], heads=16, page_size=784, num_pages=16,
+                                fmt=fmt, seed=21, row_scale_log10=(-2.0, 2.0))
+    _run_case(w, [1, 4])
+
+
+def test_split_count_invariance():
+    w = workloads.make_workload("splits", seq_lens=[5000, 4097, 64, 0], heads=16, page_size=64, num_pages=200,
+                                seed=5)
+    _run_case(w, [1, 2, 7, 64, 200])
+
+
+def test_empty_and_single_token_requests():
+    for fmt in ("bf16", "fp8"):
+        w = workloads.make_workload("empties", seq_lens=[0, 0, 1, 2, 0], heads=16, page_size=16, num_pages=4,
+                                    fmt=fmt, seed=2)
+        _run_case(w, [1, 4])
+
+
+def test_garbage_rope_control_on_gpu():
+    """q_pe = 0: random rope bytes leave the output bit-identical; q_pe != 0 changes it."""
+    w = workloads.make_workload("rope", seq_lens=[300, 77], heads=16, page_size=16, num_pages=30, seed=9)
+    other = workloads.bf16_bits(np.random.default_rng(1).standard_normal(w.k_pe.shape).astype(np.float32) * 30)
+    q0 = w.q.copy()
+    q0[:, :, 512:] = 0
+    pa = device_pool(w)
+    pb = device_pool(w, k_pe=other)
+    a = gpu_decode(w, pa, 1, q=q0)
+    b = gpu_decode(w, pb, 1, q=q0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c = gpu_decode(w, pa, 1)
+    d = gpu_decode(w, pb, 1)
+    assert np.abs(c[1] - d[1]).max() > 1e-3
+
+
+# ------------------------------------------------------------------------ cache write
+def _special_latent(rng, T):
+    """bf16 latent rows with blocks that stress the fp8 quantiser."""
+    x = rng.standard_normal((T, 512)).astype(np.float32)
+    x[0] = 0.0
+    x[1, :128] = -0.0
+    x[1, 128:256] = np.float32(1e-38)  # bf16 subnormal-range values
+    x[1, 256:384] = np.float32(3e38)   # near the top of the bf16 range
+    ties = np.array([448.0, 1.0625, 1.1875, -1.0625, 0.0, -0.0, 2**-10, 3 * 2**-10, -448.0], np.float32)
+    x[2, :ties.size] = ties
+    x[2, ties.size:128] = 1.0
+    x[3] *= np.float32(10.0) ** rng.uniform(-30, 30, size=512).astype(np.float32)
+    x[4, ::2] = 0.0
+    return workloads.bf16_bits(x)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_cache_write_bitexact(fmt):
+    rng = np.random.default_rng(3)
+    T = 300
+    latent = _special_latent(rng, T)
+    k_pe = rng.integers(0, 1 << 16, size=(T, 64), dtype=np.uint16)
+    k_pe[(k_pe & 0x7F80) == 0x7F80] = 0x1234  # keep rope values finite
+    R = oracle.ROW_BYTES[fmt]
+    pool = (torch.full((8, 64, 576), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16) if fmt == "bf16"
+            else torch.full((8, 64, 656), 0xFF, dtype=torch.uint8, device="cuda"))
+    slots = rng.permutation(8 * 64)[:T].astype(np.int64)
+    slots[5] = -1  # skipped
+    mla.mla_cache_write(bf16_dev(latent), bf16_dev(k_pe), torch.from_numpy(slots).cuda(), pool, FMT_CODE[fmt])
+    torch.cuda.synchronize()
+    host = (np.full((8, 64, 576), 0x7FC0, np.uint16).view(np.uint8) if fmt == "bf16"
+            else np.full((8, 64, 656), 0xFF, np.uint8)).reshape(-1, R)
+    oracle.cache_write(host, latent, k_pe, slots, fmt)
+    got = pool.view(torch.uint8).cpu().numpy().reshape(-1, R)
+    bad = np.nonzero((got != host).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ; first slot {bad[0]}"
+
+
+# ------------------------------------------------------------------------------ merge
+def test_merge_kernel_matches_oracle():
+    rng = np.random.default_rng(4)
+    S, B, H = 37, 3, 16
+    po = rng.standard_normal((S, B, H, 512)).astype(np.float32)
+    pl = (rng.standard_normal((S, B, H)) * 5).astype(np.float32)
+    pl[rng.random((S, B, H)) < 0.3] = -np.inf  # empty partitions
+    pl[:, 1, 3] = -np.inf                       # a fully empty (request, head)
+    out, lse = mla.mla_merge_lse(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge(po.astype(np.float64), pl.astype(np.float64))
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.array_equal(out[1, 3], np.zeros(512)) and np.isneginf(lse[1, 3])
+    assert np.allclose(out, ro, rtol=1e-5, atol=1e-5)
+    fin = np.isfinite(rl)
+    assert np.allclose(lse[fin], rl[fin], rtol=0, atol=1e-5)
+
+
+# ----------------------------------------------------------------- 64-bit addressing
+@pytest.mark.parametrize("fmt, num_pages", [("bf16", 60000), ("fp8", 110000)])
+def test_pages_beyond_32bit_offsets(fmt, num_pages):
+    """Requests on the page that straddles slot 3,728,270 and on pages past 2^32 bytes."""
+    ps = 64
+    straddle = workloads.WRAP_SLOT // ps  # holds slots 3,728,256 .. 3,728,319
+    top = num_pages - 1
+    assert top * ps * oracle.ROW_BYTES[fmt] > 2**32
+    layout = [[straddle, straddle + 1, 17, top], [top - 1, top - 2, straddle + 2], [3, straddle], [top]]
+    lens = [4 * ps - 5, 3 * ps, 2 * ps, 40]
+    rng = np.random.default_rng(8)
+    w = workloads.make_workload(f"wrap_{fmt}", seq_lens=lens, heads=16, page_size=ps, num_pages=num_pages,
+                                fmt=fmt, seed=8)
+    # Re-place the pages by hand (keeping the generated rows' slot order): rows follow slots, so
+    # regenerate the workload's slot list from the new block table.
+    bt = np.full_like(w.block_table, -1)
+    for b, pages in enumerate(layout):
+        bt[b, :len(pages)] = pages
+    fill = {}
+    for b, pages in enumerate(layout):
+        for j, pg in enumerate(pages):
+            n = min(ps, lens[b] - j * ps)
+            fill[pg] = max(fill.get(pg, 0), n)
+    slots = np.concatenate([pg * ps + np.arange(n) for pg, n in sorted(fill.items())]).astype(np.int64)
+    T = slots.size
+    lat = workloads.bf16_bits(rng.standard_normal((T, 512)).astype(np.float32))
+    pe = workloads.bf16_bits(rng.standard_normal((T, 64)).astype(np.float32))
+    w.block_table, w.slots, w.latent, w.k_pe = bt, slots, lat, pe
+    assert any(s // ps == straddle for s in slots) and slots.max() * oracle.ROW_BYTES[fmt] > 2**32
+    say(f"case wrap_{fmt}: max slot {slots.max()} byte offset {slots.max() * oracle.ROW_BYTES[fmt]}")
+    # teeth: an int32 element offset would land elsewhere for these slots
+    assert any(oracle.element_offset_int32(int(s)) != oracle.element_offset(int(s)) for s in slots)
+    _run_case(w, [1, 2], what=f"wrap_{fmt}")
+
+
+# ------------------------------------------------------------------- full-size cases
+def _sample(w, n=4):
+    rng = np.random.default_rng(0)
+    picks = {0, w.batch // 2, w.batch - 1}
+    picks.update(rng.choice(w.batch, size=min(n, w.batch), replace=False).tolist())
+    return sorted(picks)
+
+
+def _request_slots(w, b):
+    t = np.arange(int(w.seq_lens[b]), dtype=np.int64)
+    return w.block_table[b].astype(np.int64)[t // w.page_size] * w.page_size + t % w.page_size
+
+
+@pytest.mark.parametrize("name", ["batched", "long_context", "high_slot", "fp8_ragged"])
+def test_full_size_workloads_sampled(name):
+    """The named workloads at full size in the bench's launch configuration.
+
+    Every row is written by mla_cache_write; the rows of the sampled requests plus 20,000
+    random slots are compared bit for bit with the oracle's packing, and the oracle
+    decodes the sampled requests from a host pool holding its own packing of their rows.
+    """
+    w = workloads.NAMED[name]()
+    S = workloads.BENCH_SPLITS[name]
+    req = _sample(w)
+    say(f"case {name}: fmt={w.fmt} B={w.batch} tokens={w.tokens} splits={S} oracle requests={req}")
+    pd = device_pool(w)
+    out, lse = gpu_decode(w, pd, S)
+    live = w.seq_lens > 0
+    assert np.isfinite(out[live]).all() and np.isfinite(lse[live]).all()  # no stray read of a poisoned slot
+    assert np.isneginf(lse[~live]).all() and (out[~live] == 0).all() and not np.signbit(out[~live]).any()
+    rng = np.random.default_rng(1)
+    req_slots = np.unique(np.concatenate([_request_slots(w, b) for b in req]))
+    idx = np.unique(np.concatenate([np.searchsorted(w.slots, req_slots),
+                                    rng.choice(w.slots.size, size=min(20000, w.slots.size), replace=False)]))
+    assert np.array_equal(w.slots[np.searchsorted(w.slots, req_slots)], req_slots)
+    want = oracle.pack_rows(w.latent[idx], w.k_pe[idx], w.fmt)
+    got = device_rows(pd, w.slots[idx], w.row_bytes)
+    assert np.array_equal(got, want), "cache rows differ"
+    ph = w.poisoned_pool()
+    ph.reshape(-1, w.row_bytes)[w.slots[idx]] = want
+    ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=req)
+    assert_parity(w, out, lse, ref_o, ref_l, requests=req, what=f"{name} S={S}")
+
+
+def test_errors_reach_python_without_launch():
+    w = workloads.tiny()
+    pd = device_pool(w)
+    q = bf16_dev(np.zeros((1, 17, 576), np.uint16))
+    with pytest.raises(mla.MlaError, match="num_heads"):
+        mla.mla_decode_bf16(q, pd, torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda(), 0.1)

@@ -316,3 +316,14 @@ NAMED = {
     "high_slot": high_slot,
     "fp8_ragged": fp8_ragged,
 }
+
+# Partition counts the benchmark launches each named workload with.  The long-context
+# workload uses 64 partitions per request (4 x 64 = 256 workgroups, one per compute
+# unit); the others aim for at least 256 workgroups.
+BENCH_SPLITS = {
+    "tiny": 1,
+    "batched": 16,
+    "long_context": 64,
+    "high_slot": 8,
+    "fp8_ragged": 8,
+}
