@@ -8,9 +8,13 @@ HBM before timing starts.
 
 Default workload: the long-context batch, 4 requests x 262,144 tokens, 16 heads,
 64-token pages drawn at random from a 32,768-page pool, 64 partitions per request.
-Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload long_context]
+Two timed passes of --steps steps each: eager launches with HIP events around every
+kernel (per-kernel durations, the roofline figure), then the same step captured once
+as a HIP graph and replayed (the reported value; every warm-up replay is checked
+bit for bit against the eager result).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload long_context] [--eager]
 """
 from __future__ import annotations
 
@@ -34,10 +38,29 @@ def _parse():
     ap.add_argument("--workload", default="long_context")
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time only eager launches (default: also replay the step from a captured HIP graph, "
+                         "which gives the reported value)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB a few times (counter calibration)")
     return ap.parse_args()
 
 
-def _cpu_baseline(w, requests):
+def _copy_calibration(mib: int):
+    """A plain copy of known size, for scaling the HBM byte counters of a profile."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+def _cpu_baseline(w, requests, min_seconds=10.0):
     """Time the fp64 oracle on a bounded sample of the same workload, on the host cores."""
     import oracle
     try:
@@ -48,19 +71,54 @@ def _cpu_baseline(w, requests):
     pool = w.poisoned_pool()
     idx = np.concatenate([np.searchsorted(w.slots, _request_slots(w, b)) for b in requests])
     oracle.cache_write(pool, w.latent[idx], w.k_pe[idx], w.slots[idx], w.fmt)
-    t = time.perf_counter()
-    oracle.decode(w.q, pool, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=requests)
-    dt = time.perf_counter() - t
+    # Repeat the sample until about 10 s of host time has been spent.
+    reps, t = 0, time.perf_counter()
+    while True:
+        oracle.decode(w.q, pool, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=requests)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds:
+            break
     tokens = int(sum(int(w.seq_lens[b]) for b in requests))
+    per = dt / reps
     return {
-        "value": round(tokens * w.row_bytes / dt / 1e9, 3),
+        "value": round(tokens * w.row_bytes / per / 1e9, 3),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 NumPy oracle, requests {list(requests)} of the {w.name} batch "
-                  f"({tokens} tokens, {w.heads} heads), {dt:.1f} s; tokens/s {tokens / dt:.0f}; "
+        "sample": f"fp64 NumPy oracle decoding requests {list(requests)} of the {w.name} batch "
+                  f"({tokens} context tokens x {w.heads} heads), {reps} passes in {dt:.1f} s; "
+                  f"{len(requests) / per:.1f} decode tokens/s; BLAS threads {threads}, "
                   f"host cpu_count {os.cpu_count()}",
     }
+
+
+KERNEL_SOURCES = ("paged_mla_latent_amd/csrc/decode.hip", "paged_mla_latent_amd/csrc/mla_device.h")
+COUNTERS = "profiles/decode_long_context_counters.txt"
+
+
+def _profiled_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter profile, or None.
+
+    None unless the workload is the profiled one and the decode sources still hash to
+    what was profiled.
+    """
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    if workload != "long_context" or not os.path.exists(os.path.join(root, COUNTERS)):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    vals = {}
+    for line in open(os.path.join(root, COUNTERS)):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return int(vals["decode_fetch_bytes"]) + int(vals["decode_write_bytes"])
 
 
 def _request_slots(w, b):
@@ -70,6 +128,9 @@ def _request_slots(w, b):
 
 def main():
     args = _parse()
+    if args.copy_calibration:
+        _copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
               f"(the multi-GPU split of this path is described in DESIGN.md but not built).", file=sys.stderr)
@@ -127,9 +188,37 @@ def main():
     for i in range(args.steps):
         step(ev[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall = eager_wall = time.perf_counter() - t0
+    launch_mode = "eager"
+
+    if not args.eager:
+        # The same step captured once and replayed: one submission per step.  Every
+        # replay must reproduce the eager result bit for bit.
+        eager_out, eager_lse = out.clone(), lse.clone()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager_out) and torch.equal(lse, eager_lse), "graph replay differs from eager"
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        launch_mode = "hip_graph"
 
     ms_step = wall * 1e3 / args.steps
+    ms_step_eager = eager_wall * 1e3 / args.steps
     t_write = np.mean([e[0].elapsed_time(e[1]) for e in ev])
     t_decode = np.mean([e[1].elapsed_time(e[2]) for e in ev])
     t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev])
@@ -160,6 +249,8 @@ def main():
             "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
             "cache_row_bytes": w.row_bytes, "cache_bytes_per_step": cache_bytes,
         },
+        "launch": launch_mode,
+        "eager_ms_per_step": round(ms_step_eager, 4),
         "kernel_ms": {"cache_write": round(t_write, 4), "decode": round(t_decode, 4), "merge": round(t_merge, 4)},
         "roofline": {
             "kernel": "decode_kernel",
@@ -168,12 +259,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": _profiled_traffic(w.name),
         },
     }
     if not args.no_cpu_baseline:
-        req = [0, 1] if w.batch >= 2 else [0]
-        result["cpu_baseline"] = _cpu_baseline(w, req)
+        result["cpu_baseline"] = _cpu_baseline(w, list(range(min(w.batch, 4))))
     print(json.dumps(result), flush=True)
 
 

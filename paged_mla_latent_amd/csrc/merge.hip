@@ -5,50 +5,63 @@
 //   M = max_p lse_p;  M = -inf  ->  (0, -inf)
 //   w_p = exp(lse_p - M);  lse = M + ln sum_p w_p;  out = sum_p w_p out_p / sum_p w_p
 //
-// One workgroup of 128 lanes per (request, head); each lane owns 4 of the 512
-// latent columns, so every partial row is read once with 16-byte loads.
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
 namespace {
 
-__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part_out,
-                                                    const float* __restrict__ part_lse, int S,
-                                                    int64_t rows, float* __restrict__ out,
-                                                    float* __restrict__ lse) {
+constexpr int kGroups = 8;    // partial streams per workgroup
+constexpr int kCols = 32;     // float4 columns per workgroup (128 of the 512 latent values)
+
+// grid = (batch * heads, 4): workgroup (bh, y) merges latent columns [128y, 128y + 128) of
+// row bh.  Lane t owns float4 column t % 32 and partials p = t / 32, t / 32 + 8, ...; the
+// eight partial streams are then summed through LDS.
+__global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __restrict__ part_out,
+                                                               const float* __restrict__ part_lse, int S,
+                                                               int64_t rows, float* __restrict__ out,
+                                                               float* __restrict__ lse) {
+  __shared__ f32x4 acc_s[kGroups][kCols];
+  __shared__ float w_s[kGroups];
+  __shared__ float m_s[kGroups * kCols / 64];
   const int64_t bh = blockIdx.x;
-  const int t = threadIdx.x;
+  const int col = blockIdx.y * kCols + (threadIdx.x % kCols);
+  const int grp = threadIdx.x / kCols;
+  // M = max_p lse_p: every lane loads a strided share (independent loads), then a
+  // wave reduction and a reduction over the waves through LDS.
   float M = -INFINITY;
-  for (int p = 0; p < S; ++p) M = fmaxf(M, part_lse[p * rows + bh]);
+  for (int p = threadIdx.x; p < S; p += kGroups * kCols) M = fmaxf(M, part_lse[p * rows + bh]);
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) M = fmaxf(M, __shfl_xor(M, mask, 64));
+  if ((threadIdx.x & 63) == 0) m_s[threadIdx.x >> 6] = M;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kGroups * kCols / 64; ++w) M = fmaxf(M, m_s[w]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
   if (M != -INFINITY) {
-    const float* src = part_out + bh * kLatent + 4 * t;
-    int p = 0;
-    for (; p + 4 <= S; p += 4) {
-      float w[4];
-      f32x4 v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w[i] = __expf(part_lse[(p + i) * rows + bh] - M);
-        v[i] = *(const f32x4*)(src + (int64_t)(p + i) * rows * kLatent);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        W += w[i];
-        acc += w[i] * v[i];
-      }
-    }
-    for (; p < S; ++p) {
+    const float* src = part_out + bh * kLatent + 4 * col;
+#pragma unroll 4
+    for (int p = grp; p < S; p += kGroups) {
       const float w = __expf(part_lse[p * rows + bh] - M);
       W += w;
       acc += w * *(const f32x4*)(src + (int64_t)p * rows * kLatent);
     }
-    acc *= 1.0f / W;
   }
-  *(f32x4*)(out + bh * kLatent + 4 * t) = acc;
-  if (t == 0) lse[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(W);
+  acc_s[grp][threadIdx.x % kCols] = acc;
+  if (threadIdx.x % kCols == 0) w_s[grp] = W;
+  __syncthreads();
+  if (grp != 0) return;
+  W = 0.f;
+  acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    W += w_s[g];
+    acc += acc_s[g][threadIdx.x];
+  }
+  if (M != -INFINITY) acc *= 1.0f / W;
+  *(f32x4*)(out + bh * kLatent + 4 * col) = acc;
+  if (blockIdx.y == 0 && threadIdx.x == 0) lse[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(W);
 }
 
 }  // namespace
@@ -56,8 +69,8 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
 hipError_t launch_merge(const float* part_out, const float* part_lse, int num_splits, int batch,
                         int heads, float* out, float* lse, hipStream_t stream) {
   const int64_t rows = (int64_t)batch * heads;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(128), 0, stream, part_out, part_lse,
-                     num_splits, rows, out, lse);
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows, kLatent / (4 * kCols)), dim3(kGroups * kCols), 0, stream,
+                     part_out, part_lse, num_splits, rows, out, lse);
   return hipGetLastError();
 }
 
