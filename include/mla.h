@@ -82,12 +82,14 @@ MLA_API size_t mla_decode_workspace_size(int32_t batch, int32_t num_heads, int32
  * block_table  int32 [batch][block_table_stride]; physical page of each logical page.
  * seq_lens     int32 [batch]; context length of each request (0 allowed).
  * num_heads    1..16.  softmax_scale: finite float, applied to the fp32 scores.
- * num_splits   >= 1.  Each request's pages are cut into num_splits partitions of
- *              ceil(P / num_splits) whole pages (P = pages the request uses); each
- *              partition returns (out, lse) for its tokens and, when num_splits > 1,
- *              a second kernel merges them by log-sum-exp (vLLM pull request 55543:
- *              the partial-result merge contract with (0, -inf) as the neutral
- *              element).  The result does not depend on num_splits beyond rounding.
+ * num_splits   1..65535.  Each request's pages are cut into partitions of
+ *              c = ceil(block_table_stride / num_splits) whole pages (the same c for
+ *              every request, so short requests use fewer partitions and the rest are
+ *              empty); each partition returns (out, lse) for its tokens and, when
+ *              num_splits > 1, a second kernel merges them by log-sum-exp (vLLM pull
+ *              request 55543: the partial-result merge contract with (0, -inf) as the
+ *              neutral element).  The result does not depend on num_splits beyond
+ *              rounding.
  * out          fp32 [batch][num_heads][512]: softmax-weighted latent sum.
  * lse          fp32 [batch][num_heads]: natural-log log-sum-exp of the scaled scores.
  *              A request with seq_lens == 0 gets out = +0.0 and lse = -inf.

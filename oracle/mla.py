@@ -145,16 +145,17 @@ def decode(q_bits, pool, block_table, seq_lens, page_size: int, scale: float, fm
     return out, lse
 
 
-def split_ranges(length: int, page_size: int, num_splits: int) -> list[tuple[int, int]]:
+def split_ranges(length: int, page_size: int, num_splits: int, width: int | None = None) -> list[tuple[int, int]]:
     """Token ranges of the partitions of one request (reading: whole pages per split).
 
-    The request's P = ceil(L / ps) pages are cut into num_splits runs of
-    c = ceil(P / num_splits) pages; split i covers pages [i*c, min((i+1)*c, P)),
-    clipped to L tokens.  Trailing splits may be empty.  The merged result does
-    not depend on this rule.
+    Partitions hold c = ceil(width / num_splits) whole pages, width being the block
+    table's width (the most pages any request of the batch may use; default: this
+    request's own page count P = ceil(L / ps)); split i covers pages
+    [i*c, min((i+1)*c, P)), clipped to L tokens.  Trailing splits may be empty.  The
+    merged result does not depend on this rule.
     """
     P = -(-length // page_size)
-    c = max(1, -(-P // num_splits))
+    c = max(1, -(-(P if width is None else width) // num_splits))
     out = []
     for i in range(num_splits):
         t0 = min(length, i * c * page_size)

@@ -9,7 +9,7 @@
 // return (out, lse); a merge kernel combines them by log-sum-exp.
 //
 // Mapping onto CDNA4:
-//  * grid = (partition, request); 4 waves per workgroup; each wave streams its own
+//  * grid = (request, partition); 4 waves per workgroup; each wave streams its own
 //    16-token tiles (tiles wave, wave+4, ...) and keeps its own online-softmax state,
 //    so the main loop has no workgroup barrier.  The 4 states merge through LDS at
 //    the end.
@@ -40,10 +40,13 @@ struct Range {
   int64_t t0, t1;
 };
 
-// Partition s of a request of L tokens: whole pages, ceil(P / S) pages per partition.
-__device__ __forceinline__ Range partition(int64_t L, int ps, int S, int s) {
+// Partition s of a request of L tokens: whole pages, c = ceil(W / S) pages per partition,
+// W = the block table's width (the most pages any request may use).  Every request's
+// partitions have the same size, so a batch of ragged lengths balances: short requests
+// use fewer (non-empty) partitions instead of smaller ones.
+__device__ __forceinline__ Range partition(int64_t L, int ps, int S, int s, int64_t W) {
   const int64_t P = (L + ps - 1) / ps;
-  int64_t c = (P + S - 1) / S;
+  int64_t c = (W + S - 1) / S;
   if (c < 1) c = 1;
   const int64_t p0 = min(P, (int64_t)s * c);
   const int64_t p1 = min(P, (int64_t)(s + 1) * c);
@@ -51,44 +54,63 @@ __device__ __forceinline__ Range partition(int64_t L, int ps, int S, int s) {
 }
 
 // ------------------------------------------------------------------------------------
-// bf16 rows: a tile is 16 tokens x 72 chunks of 16 bytes.  Chunk c of token t sits at
-// chunk position 16*c + (t ^ 8*(c & 1)).  QK reads (fixed c, all 16 tokens) and the
-// transposing PV reads (8 tokens x 2 chunks per 32 lanes) are both bank-conflict free,
-// and DMA instruction j (positions 64j..64j+63) makes lane L fetch chunk 4j + L/16 of
-// token (L & 15) ^ 8*((L >> 4) & 1): one token per lane per tile.
+// Tile layout in LDS.  A tile is 16 tokens x C chunks of 16 bytes (C = 72 for bf16 rows,
+// 41 for fp8 rows).  DMA instruction j fills chunk positions 64j .. 64j+63, lane L landing
+// at 64j + L; lane L = 4t + v fetches chunk 4j + (v ^ h(t)) of token t, so each group of
+// four lanes reads 64 contiguous bytes of one row (the coalesced form: four lanes per row
+// segment measured 6% faster than one lane per row).  Chunk c of token t therefore sits at
+//     P(t, c) = 64 * (c >> 2) + 4 * t + ((c & 3) ^ h(t)),   h(t) = bit-swap of t >> 2,
+// and both read patterns are bank-conflict free: the QK reads (one chunk of all 16 tokens:
+// 4 * (t & 3) + ((c & 3) ^ h(t)) covers 16 banks groups) and the transposing PV reads (8
+// tokens x 2 adjacent chunks per 32 lanes: tokens t and t + 4 use opposite chunk pairs).
 // ------------------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int t) { return (((t >> 2) & 1) << 1) | ((t >> 3) & 1); }
+__device__ __forceinline__ int chunk_pos(int t, int c) { return 64 * (c >> 2) + 4 * t + ((c & 3) ^ swz(t)); }
+
 struct Bf16Rows {
   static constexpr int kRowBytes = kRowBytesBf16;
   static constexpr int kDmaOps = 18;
+  static constexpr int kBufs = 2;  // tiles per wave resident in LDS (2 x 4 x 18 KB)
   static constexpr int kTileBytes = kTile * kRowBytes;  // 18,432
   static constexpr int kAcc = 32;                       // 16x16 output tiles per head group
 
   struct Aux {};
 
-  __device__ static __forceinline__ int dma_token(int lane) { return (lane & 15) ^ (8 * ((lane >> 4) & 1)); }
+  __device__ static __forceinline__ int dma_token(int lane) { return lane >> 2; }
 
   __device__ static __forceinline__ void issue(const uint8_t* row, uint32_t dst, int lane) {
-    const uint8_t* src = row + 16 * (lane >> 4);
+    const uint8_t* src = row + 16 * ((lane & 3) ^ swz(lane >> 2));
 #pragma unroll
     for (int j = 0; j < kDmaOps; ++j) dma16(src + 64 * j, dst + 1024 * j);
   }
 
+  // K-step j reads chunk 4j + g of token m (the A operand: token m, values 32j + 8g ..).
   __device__ static __forceinline__ f32x4 qk(const uint8_t* buf, int m, int g, const u32x4* qf, Aux&) {
-    const uint8_t* base = buf + 256 * g + 16 * (m ^ (8 * (g & 1)));
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* base = buf + 16 * chunk_pos(m, g);
+    // Two independent accumulation chains halve the dependent-MFMA latency.
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-    for (int j = 0; j < 18; ++j) s = mfma_16x16x32(*(const u32x4*)(base + 1024 * j), qf[j], s);
-    return s;
+    for (int j = 0; j < 18; j += 2) {
+      s0 = mfma_16x16x32(*(const u32x4*)(base + 1024 * j), qf[j], s0);
+      s1 = mfma_16x16x32(*(const u32x4*)(base + 1024 * (j + 1)), qf[j + 1], s1);
+    }
+    return s0 + s1;
   }
 
+  // 16-wide column group u: lane (m, g) addresses token 4g + (m >> 2), values
+  // 16u + 4(m & 3) .. +4, i.e. chunk 2u + ((m >> 1) & 1), half m & 1.
   __device__ static __forceinline__ void pv(const uint8_t* buf, int m, int g, const float (&p)[4],
                                             const Aux&, f32x4 (&O)[kAcc]) {
     const u32x2 pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
     const int t = 4 * g + (m >> 2);
     const int cc = (m >> 1) & 1;
-    const uint8_t* base = buf + 16 * (16 * cc + (t ^ (8 * cc))) + 8 * (m & 1);
+    const uint8_t* b0 = buf + 16 * chunk_pos(t, cc) + 8 * (m & 1);      // u even
+    const uint8_t* b1 = buf + 16 * chunk_pos(t, 2 + cc) + 8 * (m & 1);  // u odd
 #pragma unroll
-    for (int u = 0; u < kAcc; ++u) O[u] = mfma_16x16x16(lds_read_tr16(base + 512 * u), pb, O[u]);
+    for (int u = 0; u < kAcc; u += 2) {
+      O[u] = mfma_16x16x16(lds_read_tr16(b0 + 512 * u), pb, O[u]);
+      O[u + 1] = mfma_16x16x16(lds_read_tr16(b1 + 512 * u), pb, O[u + 1]);
+    }
   }
 
   // Accumulator u holds, for head m, d = 16u + 4g + r in element r.
@@ -99,15 +121,14 @@ struct Bf16Rows {
 };
 
 // ------------------------------------------------------------------------------------
-// fp8 656-byte rows: 41 chunks of 16 bytes per token (32 code chunks, 1 scale chunk,
-// 8 rope chunks).  Chunk c of token t sits at position 16*c + (t ^ (c & 3)); DMA
-// instruction j makes lane L fetch chunk 4j + L/16 of token (L & 15) ^ (L >> 4).  The
-// eleventh instruction only has 16 real chunks; its other lanes re-read an in-row chunk
-// into padding, so every access stays inside the row.
+// fp8 656-byte rows: 41 chunks per token (32 code chunks, 1 scale chunk, 8 rope chunks).
+// Eleven DMA instructions; in the last only chunk 40 exists, and the lanes whose chunk
+// would lie past it re-read chunk 40 into padding, so every access stays in the row.
 // ------------------------------------------------------------------------------------
 struct Fp8Rows {
   static constexpr int kRowBytes = kRowBytesFp8;
   static constexpr int kDmaOps = 11;
+  static constexpr int kBufs = 2;  // smaller tiles: three in flight per wave (3 x 4 x 11 KB)
   static constexpr int kTileBytes = kDmaOps * 1024;  // 10,496 used + padding
   static constexpr int kAcc = 32;
 
@@ -115,13 +136,13 @@ struct Fp8Rows {
     f32x4 sc[4];  // sc[r][k]: scale of block k of token 4g + r
   };
 
-  __device__ static __forceinline__ int dma_token(int lane) { return (lane & 15) ^ (lane >> 4); }
+  __device__ static __forceinline__ int dma_token(int lane) { return lane >> 2; }
 
   __device__ static __forceinline__ void issue(const uint8_t* row, uint32_t dst, int lane) {
-    const uint8_t* src = row + 16 * (lane >> 4);
+    const uint8_t* src = row + 16 * ((lane & 3) ^ swz(lane >> 2));
 #pragma unroll
     for (int j = 0; j < 10; ++j) dma16(src + 64 * j, dst + 1024 * j);
-    dma16(row + 16 * 40, dst + 1024 * 10);  // chunk 40 for lanes 0..15; padding for the rest
+    dma16(row + 16 * 40, dst + 1024 * 10);  // chunk 40 for one lane per token; padding for the rest
   }
 
   __device__ static __forceinline__ u32x4 widen8(u32x2 codes) {
@@ -135,16 +156,16 @@ struct Fp8Rows {
 
   __device__ static __forceinline__ f32x4 qk(const uint8_t* buf, int m, int g, const u32x4* qf, Aux& aux) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) aux.sc[r] = *(const f32x4*)(buf + 16 * (16 * 32 + 4 * g + r));
+    for (int r = 0; r < 4; ++r) aux.sc[r] = *(const f32x4*)(buf + 16 * chunk_pos(4 * g + r, 32));
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       f32x4 sk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int j = 4 * k + jj;
+        const int j = 4 * k + jj;  // codes 32j + 8g .. +8: chunk 2j + (g >> 1), half g & 1
         const int c = 2 * j + (g >> 1);
-        const u32x2 codes = *(const u32x2*)(buf + 16 * (16 * c + (m ^ (c & 3))) + 8 * (g & 1));
+        const u32x2 codes = *(const u32x2*)(buf + 16 * chunk_pos(m, c) + 8 * (g & 1));
         sk = mfma_16x16x32(widen8(codes), qf[j], sk);
       }
 #pragma unroll
@@ -152,10 +173,8 @@ struct Fp8Rows {
     }
     f32x4 sr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int jr = 0; jr < 2; ++jr) {
-      const int c = 33 + 4 * jr + g;
-      sr = mfma_16x16x32(*(const u32x4*)(buf + 16 * (16 * c + (m ^ (c & 3)))), qf[16 + jr], sr);
-    }
+    for (int jr = 0; jr < 2; ++jr)
+      sr = mfma_16x16x32(*(const u32x4*)(buf + 16 * chunk_pos(m, 33 + 4 * jr + g)), qf[16 + jr], sr);
     return s + sr;
   }
 
@@ -166,14 +185,13 @@ struct Fp8Rows {
     for (int k = 0; k < 4; ++k)
       pb[k] = u32x2{pack_bf16(p[0] * aux.sc[0][k], p[1] * aux.sc[1][k]),
                     pack_bf16(p[2] * aux.sc[2][k], p[3] * aux.sc[3][k])};
-    const int q = m >> 2;  // chunk c = 4i + q, so c & 3 == q
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       uint32_t lo[4], hi[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int c = 4 * i + q;
-        const uint32_t w = *(const uint32_t*)(buf + 16 * (16 * c + ((4 * g + r) ^ q)) + 4 * (m & 3));
+        // codes 64i + 4m .. +4 of token 4g + r: chunk 4i + (m >> 2), quarter m & 3
+        const uint32_t w = *(const uint32_t*)(buf + 16 * chunk_pos(4 * g + r, 4 * i + (m >> 2)) + 4 * (m & 3));
         lo[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
         hi[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
       }
@@ -205,26 +223,32 @@ struct Fp8Rows {
 constexpr int kRedStride = kLatent + 4;  // padded per-head row of the cross-wave merge
 constexpr int kRedBytes = kWaves * kMaxHeads * kRedStride * 4 + 2 * kWaves * kMaxHeads * 4;
 
-// Per wave: two tile buffers, then (after all waves' buffers) 512 bytes of page-id slots.
+// Per wave: kBufs tile buffers, then (after all waves' buffers) kBufs 256-byte page-id slots.
+template <class Fmt>
+constexpr int pipe_bytes() {
+  return kWaves * Fmt::kBufs * (Fmt::kTileBytes + 256);
+}
 template <class Fmt>
 constexpr int smem_bytes() {
-  return kWaves * 2 * Fmt::kTileBytes + kWaves * 512 > kRedBytes ? kWaves * 2 * Fmt::kTileBytes + kWaves * 512
-                                                                 : kRedBytes;
+  return pipe_bytes<Fmt>() > kRedBytes ? pipe_bytes<Fmt>() : kRedBytes;
 }
 
 template <class Fmt>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
 
-  const int s = blockIdx.x;
-  const int b = blockIdx.y;
+  // Partition-major grid: all requests' first partitions are dispatched first, then the
+  // second ones, ...; with equal-size partitions the empty tails of short requests come
+  // last and full partitions spread evenly over the compute units.
+  const int b = blockIdx.x;
+  const int s = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m = lane & 15;
   const int g = lane >> 4;
 
   const int64_t L = p.seq_lens[b];
-  const Range rg = partition(L, p.page_size, p.num_splits, s);
+  const Range rg = partition(L, p.page_size, p.num_splits, s, p.bt_stride);
   const int n = (int)(rg.t1 - rg.t0);
   const int ntiles = (n + kTile - 1) / kTile;
 
@@ -238,11 +262,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
 #pragma unroll
       for (int j = 0; j < 18; ++j) qf[j] = *(const u32x4*)(qrow + 32 * j);
     }
-    // Consume q here so the compiler's waits for these loads land before the
-    // pipeline: inside it, a compiler-generated vmcnt wait would also wait for the
-    // hand-counted row DMAs in flight.
-#pragma unroll
-    for (int j = 0; j < 18; ++j) asm volatile("" ::"v"(qf[j]));
   }
 
   float m_run = -INFINITY;  // running max (log2 domain) for head m
@@ -254,7 +273,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
   const uint32_t ps = (uint32_t)p.page_size;
   const int my_tok = Fmt::dma_token(lane);
-  uint8_t* wbuf = smem + wave * 2 * Fmt::kTileBytes;
+  uint8_t* wbuf = smem + wave * Fmt::kBufs * Fmt::kTileBytes;
   const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds_offset(wbuf));
 
   // Token this lane fetches in tile k, clamped into the partition (ragged tail).
@@ -266,10 +285,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
     return t > tlast ? tlast : t;
   };
   // Page ids travel HBM -> LDS by DMA as well (one 4-byte entry per lane, lane l's own
-  // token), two tiles ahead of use, so that no compiler-visible load sits in the loop:
-  // the only vector-memory operations are these DMAs, whose completion is counted by
-  // hand.  The slot for the tile issued in pipeline step i is pslot[i & 1].
-  uint8_t* pslot = smem + kWaves * 2 * Fmt::kTileBytes + wave * 512;
+  // token), well ahead of use, so that no compiler-visible load sits in the loop: the
+  // only vector-memory operations are these DMAs, whose completion is counted by hand.
+  uint8_t* pslot = smem + kWaves * Fmt::kBufs * Fmt::kTileBytes + wave * Fmt::kBufs * 256;
   const uint32_t plds = __builtin_amdgcn_readfirstlane(lds_offset(pslot));
   auto fetch_page = [&](int k, uint32_t slot) {
     const uint32_t pi = lane_token(k) / ps;
@@ -294,8 +312,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
       sc[r] = (4 * g + r < valid) ? raw[r] * p.scale_log2 : -INFINITY;
       mx = fmaxf(mx, sc[r]);
     }
-    mx = fmaxf(mx, xor_shfl(mx, 16));
-    mx = fmaxf(mx, xor_shfl(mx, 32));
+    mx = max_over_rows(mx);
     const bool grow = mx > m_run + kRescaleThreshold;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -314,35 +331,56 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
     Fmt::pv(buf, m, g, pr, aux, O);
   };
 
-  // Software pipeline over this wave's tiles k = wave, wave + 4, ...: tile k+4 is in
-  // flight while tile k is computed.  The page id of the tile after next is loaded
-  // before the next tile's row loads are issued, so consuming it never waits on them.
-  // Pipeline step i computes tile k = wave + 4i while tile k + 4 streams in; the page
-  // ids of tile k + 8 are fetched before tile k + 4's rows are issued.
+  // Software pipeline over this wave's tiles k = wave, wave + 4, ...  With NB = kBufs
+  // buffers, step i computes tile k while tiles k + 4 .. k + 4(NB - 1) stream in.  The
+  // vector-memory queue is kept in this order (completion is in order):
+  //     ... PID(k + 4(NB-1))  DMA(k)  PID(k + 4NB)  DMA(k + 4)  ...
+  // where PID(t) is the 4-byte page-id DMA of tile t and DMA(t) its D row DMAs.  Step i
+  // first waits until PID(k + 4(NB-1)) has landed (at most (NB-1)D + NB-2 younger ops),
+  // issues PID(k + 8(NB-1)) and DMA(k + 4(NB-1)), then waits until DMA(k) has landed (at
+  // most (NB-1)(D+1) younger ops).  The steady loop runs only while tile k + 4(NB-1)
+  // exists, so every counted op is really issued; page-id fetches past the end re-read
+  // the last tile's entries.  The last NB-1 tiles drain under a full wait.
+  constexpr int NB = Fmt::kBufs;
+  constexpr int D = Fmt::kDmaOps;
   int k = wave;
-  int it = 0;
+  // The first NB-1 tiles' page ids are ordinary loads issued with the q loads; all are
+  // consumed here, so the compiler's waits for them land before the pipeline (inside it
+  // a compiler-generated vmcnt wait would also wait for the hand-counted DMAs).
+  int32_t page_first[NB - 1];
+#pragma unroll
+  for (int t = 0; t < NB - 1; ++t) page_first[t] = (k + kWaves * t < ntiles) ? bt[lane_token(k + kWaves * t) / ps] : 0;
+#pragma unroll
+  for (int j = 0; j < 18; ++j) asm volatile("" ::"v"(qf[j]));
+#pragma unroll
+  for (int t = 0; t < NB - 1; ++t) asm volatile("" ::"v"(page_first[t]));
   if (k < ntiles) {
-    fetch_page(k, plds + 256);
-    wait_vmcnt<0>();
-    const int32_t page0 = read_page(pslot + 256);
-    fetch_page(min(k + kWaves, ntiles - 1), plds);
-    Fmt::issue(row_of(lane_token(k), page0), wlds, lane);
-    for (; k + kWaves < ntiles; k += kWaves, ++it) {
-      const int kn = k + kWaves;
-      wait_vmcnt<Fmt::kDmaOps>();  // page ids of tile kn have landed; tile k may be in flight
-      const int32_t page_n = read_page(pslot + 256 * (it & 1));
-      fetch_page(min(kn + kWaves, ntiles - 1), plds + 256 * ((it + 1) & 1));
-      Fmt::issue(row_of(lane_token(kn), page_n), wlds + ((it + 1) & 1) * Fmt::kTileBytes, lane);
-      wait_vmcnt<Fmt::kDmaOps + 1>();  // tile k has landed
-      compute(wbuf + (it & 1) * Fmt::kTileBytes, k);
+#pragma unroll
+    for (int t = 0; t < NB - 1; ++t) {
+      fetch_page(min(k + kWaves * (t + NB - 1), ntiles - 1), plds + 256 * t);
+      if (k + kWaves * t < ntiles)
+        Fmt::issue(row_of(lane_token(k + kWaves * t), page_first[t]), wlds + t * Fmt::kTileBytes, lane);
+    }
+    int cur = 0;  // buffer / page-id slot of tile k (step index mod NB)
+    for (; k + kWaves * (NB - 1) < ntiles; k += kWaves) {
+      const int ahead = cur == 0 ? NB - 1 : cur - 1;  // (cur + NB - 1) mod NB
+      wait_vmcnt<(NB - 1) * D + (NB - 2)>();  // page ids of tile k + 4(NB-1) have landed
+      const int32_t page_n = read_page(pslot + 256 * cur);
+      fetch_page(min(k + kWaves * 2 * (NB - 1), ntiles - 1), plds + 256 * ahead);
+      Fmt::issue(row_of(lane_token(k + kWaves * (NB - 1)), page_n), wlds + ahead * Fmt::kTileBytes, lane);
+      wait_vmcnt<(NB - 1) * (D + 1)>();  // tile k has landed
+      compute(wbuf + cur * Fmt::kTileBytes, k);
+      cur = cur + 1 == NB ? 0 : cur + 1;
     }
     wait_vmcnt<0>();
-    compute(wbuf + (it & 1) * Fmt::kTileBytes, k);
+    for (; k < ntiles; k += kWaves) {
+      compute(wbuf + cur * Fmt::kTileBytes, k);
+      cur = cur + 1 == NB ? 0 : cur + 1;
+    }
   }
 
   // ---- merge the waves' states through LDS ---------------------------------------
-  l_run += xor_shfl(l_run, 16);
-  l_run += xor_shfl(l_run, 32);
+  l_run = sum_over_rows(l_run);
   __syncthreads();
   float* red = (float*)smem;
   float* red_m = red + kWaves * kMaxHeads * kRedStride;
@@ -383,7 +421,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
 
 template <class Fmt>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)p.num_splits, (unsigned)p.batch);
+  dim3 grid((unsigned)p.batch, (unsigned)p.num_splits);
   hipLaunchKernelGGL(decode_kernel<Fmt>, grid, dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }

@@ -83,8 +83,8 @@ int decode_common(int fp8, const void* q, const void* kv_cache, int64_t num_page
     return fail(MLA_ERR_SHAPE, "%s: block_table_stride=%lld must be >= 1", fn, (long long)block_table_stride);
   if (block_table_stride > ((int64_t)1 << 31) / page_size + 1)
     return fail(MLA_ERR_SHAPE, "%s: block_table_stride * page_size exceeds the int32 token range", fn);
-  if (num_splits < 1 || num_splits > 65536)
-    return fail(MLA_ERR_SHAPE, "%s: num_splits=%d outside [1, 65536]", fn, num_splits);
+  if (num_splits < 1 || num_splits > 65535)
+    return fail(MLA_ERR_SHAPE, "%s: num_splits=%d outside [1, 65535]", fn, num_splits);
   if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_SHAPE, "%s: softmax_scale is not finite", fn);
   if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(block_table) || !aligned16(seq_lens) ||
       !aligned16(out) || !aligned16(lse))

@@ -88,6 +88,29 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// Values of lane l and lane l ^ 16 (row swap within 32-lane halves), and of lane l and
+// lane l ^ 32, via the gfx950 permlane swaps (VALU, no LDS round trip).  Each returns the
+// pair; callers combine the two symmetrically.
+__device__ __forceinline__ f32x2 pair_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2 pair_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48.
+__device__ __forceinline__ float max_over_rows(float v) {
+  f32x2 a = pair_xor16(v);
+  v = fmaxf(a[0], a[1]);
+  a = pair_xor32(v);
+  return fmaxf(a[0], a[1]);
+}
+__device__ __forceinline__ float sum_over_rows(float v) {
+  f32x2 a = pair_xor16(v);
+  v = a[0] + a[1];
+  a = pair_xor32(v);
+  return a[0] + a[1];
+}
 
 }  // namespace mla

@@ -434,7 +434,7 @@ def test_split_then_merge_equals_unsplit(S):
     for b in range(w.batch):
         L = int(w.seq_lens[b])
         rows = oracle.gather_rows_fast(pool, w.block_table, b, L, 16, "bf16")
-        rngs = oracle.split_ranges(L, 16, S)
+        rngs = oracle.split_ranges(L, 16, S, width=w.block_table.shape[1] if S % 2 else None)
         assert rngs[0][0] == 0 and rngs[-1][1] == L
         assert all(a[1] == c[0] for a, c in zip(rngs, rngs[1:]))
         assert all(t0 % 16 == 0 for t0, t1 in rngs if t1 > t0)
