@@ -243,6 +243,15 @@ def test_full_size_workloads_sampled(name):
     assert_parity(w, out, lse, ref_o, ref_l, requests=req, what=f"{name} S={S}")
 
 
+def test_decode_is_bit_reproducible():
+    """Fixed partitions and a fixed reduction order: two runs give identical bits."""
+    w = workloads.make_workload("repro", seq_lens=[30000, 777], heads=16, page_size=64, num_pages=500, seed=6)
+    pd = device_pool(w)
+    a = gpu_decode(w, pd, 16)
+    b = gpu_decode(w, pd, 16)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def test_errors_reach_python_without_launch():
     w = workloads.tiny()
     pd = device_pool(w)
