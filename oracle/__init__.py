@@ -9,8 +9,9 @@ and imports nothing from it; both sides take their inputs from ``workloads``.
 Contents
 --------
 numerics : bf16 and OCP e4m3fn formats; per-128-value block quantisation.
-mla      : slot addressing, row decoding, attention over gathered rows,
-           log-sum-exp merge of partitions, and the cache-row packing.
+mla      : slot addressing, row decoding, attention over gathered rows (with and
+           without the rotary part), log-sum-exp merge of partitions, and the
+           cache-row packing.
 
 Every function is pinned by ``tests/test_oracle.py`` against brute force,
 closed forms, invariants and library routines.  Parity pins for each function
@@ -18,13 +19,13 @@ are listed at the top of that test file.
 """
 from .numerics import (E4M3_MAX, E4M3_TABLE, bf16_to_f32, bf16_to_f64, e4m3_decode,
                        e4m3_encode, quantize_block128)
-from .mla import (LATENT, ROPE, ROW, ROW_BYTES, attend, cache_write, decode,
+from .mla import (LATENT, ROPE, ROW, ROW_BYTES, attend, cache_write, decode, decode_nope,
                   element_offset, element_offset_int32, gather_rows, gather_rows_fast,
                   merge, pack_rows, rows_from_bytes, slot_of, split_ranges)
 
 __all__ = [
     "E4M3_MAX", "E4M3_TABLE", "bf16_to_f32", "bf16_to_f64", "e4m3_decode", "e4m3_encode",
     "quantize_block128", "LATENT", "ROPE", "ROW", "ROW_BYTES", "attend", "cache_write",
-    "decode", "element_offset", "element_offset_int32", "gather_rows", "gather_rows_fast",
+    "decode", "decode_nope", "element_offset", "element_offset_int32", "gather_rows", "gather_rows_fast",
     "merge", "pack_rows", "rows_from_bytes", "slot_of", "split_ranges",
 ]

@@ -25,6 +25,10 @@ What is computed (per request b and head h), following the pages:
   rows neutralise to (0, -inf) per the decode-context-parallel merge contract).
 * Partial results over disjoint token sets merge by log-sum-exp (vLLM PR #55543,
   description: FlashMLA sparse returns the decode LSE needed for DCP and MTP).
+* NoPE-512 layers (no rotary part) keep the same row and write zeros into its rope part;
+  their query has 512 values, padded with zeros to 576, so the rope part adds nothing to
+  any score (vLLM PR #55543, description of the zero-rope approach).  decode_nope is the
+  definition itself: scores over the 512 latent values only.
 """
 from __future__ import annotations
 
@@ -145,6 +149,25 @@ def decode(q_bits, pool, block_table, seq_lens, page_size: int, scale: float, fm
     return out, lse
 
 
+def decode_nope(q_bits, pool, block_table, seq_lens, page_size: int, scale: float, fmt: str,
+                requests=None) -> tuple[np.ndarray, np.ndarray]:
+    """NoPE-512 decode: q_bits uint16 bf16 bits [B, H, 512]; scores s_t = scale * <q, latent_t>.
+
+    Same pool, paging and results as decode; the rows' 64 rope values take no part,
+    whatever bytes they hold.
+    """
+    q = bf16_to_f64(q_bits)
+    B, H, D = q.shape
+    if D != LATENT:
+        raise ValueError("NoPE queries have 512 values per head")
+    out = np.full((B, H, LATENT), np.nan)
+    lse = np.full((B, H), np.nan)
+    for b in (range(B) if requests is None else requests):
+        rows = gather_rows_fast(pool, block_table, b, int(seq_lens[b]), page_size, fmt)[:, :LATENT]
+        out[b], lse[b] = attend(q[b], rows, scale)
+    return out, lse
+
+
 def split_ranges(length: int, page_size: int, num_splits: int, width: int | None = None) -> list[tuple[int, int]]:
     """Token ranges of the partitions of one request (reading: whole pages per split).
 
@@ -185,16 +208,19 @@ def merge(part_out: np.ndarray, part_lse: np.ndarray) -> tuple[np.ndarray, np.nd
 
 
 # ------------------------------------------------------------------------ cache write
-def pack_rows(latent_bits: np.ndarray, k_pe_bits: np.ndarray, fmt: str) -> np.ndarray:
+def pack_rows(latent_bits: np.ndarray, k_pe_bits, fmt: str) -> np.ndarray:
     """Row bytes [T, row_bytes] for new tokens (latent [T, 512], k_pe [T, 64], bf16 bits).
 
     bf16: the 576 values latent ++ k_pe, little-endian (1152 bytes).
     fp8: per 128-value block a = max|x|, s = fl32(a/448), codes = e4m3(x/s);
     codes, then the 4 fp32 scales, then k_pe as bf16 (656 bytes).
+    k_pe None (a NoPE layer): the rope part is written as zeros.
     """
     latent_bits = np.ascontiguousarray(latent_bits, dtype=np.uint16)
-    k_pe_bits = np.ascontiguousarray(k_pe_bits, dtype=np.uint16)
     T = latent_bits.shape[0]
+    if k_pe_bits is None:
+        k_pe_bits = np.zeros((T, ROPE), dtype=np.uint16)
+    k_pe_bits = np.ascontiguousarray(k_pe_bits, dtype=np.uint16)
     if fmt == "bf16":
         row = np.concatenate([latent_bits, k_pe_bits], axis=1).astype("<u2")
         return row.view(np.uint8).reshape(T, ROW_BYTES["bf16"])
@@ -213,6 +239,6 @@ def cache_write(pool: np.ndarray, latent_bits, k_pe_bits, slot_mapping, fmt: str
     keep = slot_mapping >= 0
     if (slot_mapping[keep] >= rows.shape[0]).any():
         raise IndexError("slot outside the pool")
-    packed = pack_rows(np.asarray(latent_bits)[keep], np.asarray(k_pe_bits)[keep], fmt)
+    packed = pack_rows(np.asarray(latent_bits)[keep], None if k_pe_bits is None else np.asarray(k_pe_bits)[keep], fmt)
     rows[slot_mapping[keep]] = packed
 

@@ -15,6 +15,10 @@ mla.attend               closed forms (golden); pure-Python brute force (math.fs
                          1-token, uniform-score, duplication, hardmax, empty invariants;
                          a softmax-over-heads mistake planted in the oracle fails them
 mla.decode               page-permutation invariance; garbage-rope control
+mla.decode_nope          pure-Python brute force over the 512 latent values; equals decode
+                         with q_pe = 0 on finite rope; unchanged by NaN rope bytes, which
+                         turn decode with q_pe = 0 into NaN (the pages' control)
+mla.pack_rows(k_pe=None) rope bytes zero, latent bytes as with any k_pe
 mla.merge/split_ranges   split vs unsplit for S in {1, 2, 7, 64}; all-empty partials;
                          partition coverage
 workloads.bf16_bits      torch's float32 -> bfloat16 cast (round to nearest even)
@@ -232,7 +236,7 @@ def _brute_attend(q, rows, scale):
     H, L = len(q), len(rows)
     out, lse = [], []
     for h in range(H):
-        s = [scale * math.fsum(q[h][d] * rows[t][d] for d in range(576)) for t in range(L)]
+        s = [scale * math.fsum(q[h][d] * rows[t][d] for d in range(len(q[h]))) for t in range(L)]
         m = max(s)
         z = math.fsum(math.exp(x - m) for x in s)
         ls = m + math.log(z)
@@ -400,6 +404,63 @@ def test_garbage_rope_control(fmt):
     c = oracle.decode(w.q, pools[0], w.block_table, w.seq_lens, 16, w.scale, fmt)
     d = oracle.decode(w.q, pools[1], w.block_table, w.seq_lens, 16, w.scale, fmt)
     assert np.max(np.abs(c[1] - d[1])) > 1e-3
+
+
+# --------------------------------------------------------------------------- NoPE-512
+@pytest.mark.parametrize("ps", [1, 3])
+def test_nope_decode_matches_brute_force(ps):
+    rng = np.random.default_rng(30 + ps)
+    w = workloads.make_workload("nope_brute", seq_lens=[5, 2], heads=2, page_size=ps, num_pages=12, rng=rng)
+    pool = w.poisoned_pool()
+    oracle.cache_write(pool, w.latent, w.k_pe, w.slots, "bf16")
+    q512 = w.q[:, :, :512].copy()
+    out, lse = oracle.decode_nope(q512, pool, w.block_table, w.seq_lens, ps, w.scale, "bf16")
+    qf = oracle.bf16_to_f64(q512)
+    flat = pool.reshape(-1, 1152)
+    for b in range(w.batch):
+        rows = []
+        for t in range(int(w.seq_lens[b])):
+            slot = int(w.block_table[b][t // ps]) * ps + t % ps
+            rows.append(oracle.bf16_to_f64(flat[slot].view("<u2"))[:512].tolist())
+        bo, bl = _brute_attend(qf[b].tolist(), rows, w.scale)
+        assert np.max(np.abs(out[b] - bo)) < 1e-12 and np.max(np.abs(lse[b] - bl)) < 1e-12
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_nope_equals_decode_with_zero_q_pe_and_ignores_nan_rope(fmt):
+    w = workloads.make_workload("nope", seq_lens=[40, 0, 17], heads=4, page_size=16, num_pages=8, seed=13, fmt=fmt)
+    shape = (8, 16, 576) if fmt == "bf16" else (8, 16, 656)
+    fresh = (lambda: w.poisoned_pool()) if fmt == "bf16" else (lambda: np.full(shape, 0xFF, np.uint8))
+    zero_rope, nan_rope = fresh(), fresh()
+    oracle.cache_write(zero_rope, w.latent, None, w.slots, fmt)
+    nan_pe = np.full(w.k_pe.shape, 0x7FC0, np.uint16)  # bf16 NaN in every rope value
+    oracle.cache_write(nan_rope, w.latent, nan_pe, w.slots, fmt)
+    q0 = w.q.copy()
+    q0[:, :, 512:] = 0
+    q512 = w.q[:, :, :512].copy()
+    args = (w.block_table, w.seq_lens, 16, w.scale, fmt)
+    full0 = oracle.decode(q0, zero_rope, *args)
+    n0 = oracle.decode_nope(q512, zero_rope, *args)
+    n1 = oracle.decode_nope(q512, nan_rope, *args)
+    live = w.seq_lens > 0
+    assert np.max(np.abs(full0[0][live] - n0[0][live])) < 1e-12
+    assert np.max(np.abs(full0[1][live] - n0[1][live])) < 1e-12
+    assert np.array_equal(n0[0], n1[0]) and np.array_equal(n0[1], n1[1])  # rope bytes never read
+    assert (n0[0][~live] == 0).all() and np.isneginf(n0[1][~live]).all()
+    # the control: zero-padding q_pe does not protect against non-finite rope bytes
+    bad = oracle.decode(q0, nan_rope, *args)
+    assert np.isnan(bad[1][live]).all()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_pack_rows_without_k_pe_zeroes_the_rope_part(fmt):
+    w = workloads.make_workload("zr", seq_lens=[9], heads=1, page_size=16, num_pages=2, seed=3)
+    with_pe = oracle.pack_rows(w.latent, w.k_pe, fmt)
+    no_pe = oracle.pack_rows(w.latent, None, fmt)
+    rope = slice(1024, 1152) if fmt == "bf16" else slice(528, 656)
+    keep = slice(0, 1024) if fmt == "bf16" else slice(0, 528)
+    assert not no_pe[:, rope].any() and with_pe[:, rope].any()
+    assert np.array_equal(no_pe[:, keep], with_pe[:, keep])
 
 
 def test_fp8_decode_equals_bf16_decode_on_exactly_representable_rows():
