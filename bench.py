@@ -38,6 +38,9 @@ def _parse():
     ap.add_argument("--workload", default="long_context")
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--nope", action="store_true",
+                    help="decode the workload as a NoPE-512 layer: 512-wide queries, rows written with a zero "
+                         "rope part, which the NoPE kernels never read")
     ap.add_argument("--eager", action="store_true",
                     help="time only eager launches (default: also replay the step from a captured HIP graph, "
                          "which gives the reported value)")
@@ -60,7 +63,7 @@ def _copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
-def _cpu_baseline(w, requests, min_seconds=10.0):
+def _cpu_baseline(w, requests, nope=False, min_seconds=10.0):
     """Time the fp64 oracle on a bounded sample of the same workload, on the host cores."""
     import oracle
     try:
@@ -70,11 +73,13 @@ def _cpu_baseline(w, requests, min_seconds=10.0):
         threads = 1
     pool = w.poisoned_pool()
     idx = np.concatenate([np.searchsorted(w.slots, _request_slots(w, b)) for b in requests])
-    oracle.cache_write(pool, w.latent[idx], w.k_pe[idx], w.slots[idx], w.fmt)
+    oracle.cache_write(pool, w.latent[idx], None if nope else w.k_pe[idx], w.slots[idx], w.fmt)
+    q = np.ascontiguousarray(w.q[:, :, :512]) if nope else w.q
+    run = oracle.decode_nope if nope else oracle.decode
     # Repeat the sample until about 10 s of host time has been spent.
     reps, t = 0, time.perf_counter()
     while True:
-        oracle.decode(w.q, pool, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=requests)
+        run(q, pool, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=requests)
         reps += 1
         dt = time.perf_counter() - t
         if dt >= min_seconds:
@@ -82,11 +87,11 @@ def _cpu_baseline(w, requests, min_seconds=10.0):
     tokens = int(sum(int(w.seq_lens[b]) for b in requests))
     per = dt / reps
     return {
-        "value": round(tokens * w.row_bytes / per / 1e9, 3),
+        "value": round(tokens * (w.row_bytes - (128 if nope else 0)) / per / 1e9, 3),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 NumPy oracle decoding requests {list(requests)} of the {w.name} batch "
+        "sample": f"fp64 NumPy oracle ({'decode_nope' if nope else 'decode'}) decoding requests {list(requests)} of the {w.name} batch "
                   f"({tokens} context tokens x {w.heads} heads), {reps} passes in {dt:.1f} s; "
                   f"{len(requests) / per:.1f} decode tokens/s; BLAS threads {threads}, "
                   f"host cpu_count {os.cpu_count()}",
@@ -153,16 +158,21 @@ def main():
         pool = torch.full((w.num_pages, w.page_size, 576), 0x7FC0, dtype=torch.int16, device=dev).view(torch.bfloat16)
     else:
         pool = torch.full((w.num_pages, w.page_size, 656), 0xFF, dtype=torch.uint8, device=dev)
-    mla.mla_cache_write(bf16(w.latent), bf16(w.k_pe), torch.from_numpy(w.slots).to(dev), pool, fmt)
-    q = bf16(w.q)
+    nope = args.nope
+    mla.mla_cache_write(bf16(w.latent), None if nope else bf16(w.k_pe), torch.from_numpy(w.slots).to(dev), pool, fmt)
+    q = bf16(w.q[:, :, :512]) if nope else bf16(w.q)
     bt = torch.from_numpy(w.block_table).to(dev)
     lens = torch.from_numpy(w.seq_lens).to(dev)
-    new_lat, new_pe = bf16(w.new_latent), bf16(w.new_k_pe)
+    new_lat, new_pe = bf16(w.new_latent), None if nope else bf16(w.new_k_pe)
     new_slots = torch.from_numpy(w.new_slots).to(dev)
     out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device=dev)
     ws = torch.empty(max(1, mla.mla_decode_workspace_size(w.batch, w.heads, S)), dtype=torch.uint8, device=dev)
-    decode = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
+    if nope:
+        decode = mla.mla_decode_nope_bf16 if w.fmt == "bf16" else mla.mla_decode_nope_fp8_656
+    else:
+        decode = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
+    kernel = f"decode_kernel<{'Bf16' if w.fmt == 'bf16' else 'Fp8'}Rows<{0 if nope else 64}>>"
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -226,7 +236,8 @@ def main():
     o, l = out.cpu().numpy(), lse.cpu().numpy()
     assert np.isfinite(o[live]).all() and np.isfinite(l[live]).all(), "non-finite decode output"
 
-    cache_bytes = w.cache_bytes_read()
+    # bytes the decode must read: whole rows, or rows without their rope part (NoPE)
+    cache_bytes = w.tokens * (w.row_bytes - 128) if nope else w.cache_bytes_read()
     gbs = cache_bytes / (ms_step * 1e-3) / 1e9
     decode_gbs = cache_bytes / (t_decode * 1e-3) / 1e9
     result = {
@@ -247,23 +258,25 @@ def main():
         "config": {
             "workload": w.name, "batch": w.batch, "heads": w.heads, "context_tokens": w.tokens,
             "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
-            "cache_row_bytes": w.row_bytes, "cache_bytes_per_step": cache_bytes,
+            "layer": "nope-512" if nope else "rope-576",
+            "cache_row_bytes": w.row_bytes, "row_bytes_read": w.row_bytes - (128 if nope else 0),
+            "cache_bytes_per_step": cache_bytes,
         },
         "launch": launch_mode,
         "eager_ms_per_step": round(ms_step_eager, 4),
         "kernel_ms": {"cache_write": round(t_write, 4), "decode": round(t_decode, 4), "merge": round(t_merge, 4)},
         "roofline": {
-            "kernel": "decode_kernel",
+            "kernel": kernel,
             "bound": "hbm",
             "achieved": round(decode_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-            "traffic": _profiled_traffic(w.name),
+            "traffic": None if nope else _profiled_traffic(w.name),
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = _cpu_baseline(w, list(range(min(w.batch, 4))))
+        result["cpu_baseline"] = _cpu_baseline(w, list(range(min(w.batch, 4))), nope)
     print(json.dumps(result), flush=True)
 
 

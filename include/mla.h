@@ -122,6 +122,27 @@ MLA_API int mla_decode_fp8_656(const void* q, const void* kv_cache, int64_t num_
                        float* out, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* NoPE-512 decode: layers without a rotary part (vLLM pull request 55543, description
+ * of the NoPE-512 change: such layers keep the 576-value / 656-byte row, store zeros in
+ * its rope part and pad q_pe with zeros, so the rope part adds nothing to any score).
+ * Here the padding is not needed: q is bf16 [batch][num_heads][512] and the scores use
+ * the 512 latent values only, s_t = softmax_scale * <q, latent_t>.  The rows' rope part
+ * is never read and may hold anything, so a row costs 1,024 bytes of HBM traffic
+ * (bf16 cache) or 528 (fp8 cache) instead of 1,152 / 656.  kv_cache, every other
+ * argument, the results and the errors are those of mla_decode_bf16 / mla_decode_fp8_656. */
+MLA_API int mla_decode_nope_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                                 const int32_t* block_table, int64_t block_table_stride,
+                                 const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                 int32_t page_size, float softmax_scale, int32_t num_splits,
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+MLA_API int mla_decode_nope_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                                    const int32_t* block_table, int64_t block_table_stride,
+                                    const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                    int32_t page_size, float softmax_scale, int32_t num_splits,
+                                    float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* Merge num_splits partial results over disjoint token sets (vLLM pull request
  * 55543: partial (o, lse) pairs merge by log-sum-exp; a partition with no
  * tokens is (0, -inf)).
@@ -136,7 +157,8 @@ MLA_API int mla_merge_lse(const float* part_out, const float* part_lse, int32_t 
 /* Write new tokens' rows into the cache (the cache-write step of vLLM pull
  * request 55543, which concatenates the latent and the 64-wide rotary key into
  * the row at each token's slot).
- * latent bf16 [num_tokens][512]; k_pe bf16 [num_tokens][64];
+ * latent bf16 [num_tokens][512]; k_pe bf16 [num_tokens][64], or NULL for a NoPE layer:
+ * the rope part of each row is then written as zeros (+0.0 bf16 values);
  * slot_mapping int64 [num_tokens], slot of each token; negative = skip the token.
  * kv_cache: num_slots rows in cache_format; slots must be < num_slots and distinct
  * (two tokens writing one slot race).

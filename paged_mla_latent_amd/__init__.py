@@ -8,8 +8,9 @@ Entry points (same names as the C ABI in include/mla.h):
 
     mla_decode_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, ...)
     mla_decode_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, ...)
+    mla_decode_nope_bf16 / mla_decode_nope_fp8_656(q [B, H, 512], ...)   NoPE-512 layers
     mla_merge_lse(part_out, part_lse, out=None, lse=None)
-    mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format)
+    mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format)   k_pe None: zero rope
     mla_decode_workspace_size(batch, num_heads, num_splits)
 
 Tensors: q bf16 [B, H, 576]; kv_cache bf16 [num_pages, page_size, 576] or uint8
@@ -34,7 +35,8 @@ ROW_BYTES = {MLA_CACHE_BF16_576: 1152, MLA_CACHE_FP8_656: 656}
 MAX_HEADS = 16
 
 EXPORTED = (
-    "mla_decode_workspace_size", "mla_decode_bf16", "mla_decode_fp8_656", "mla_merge_lse",
+    "mla_decode_workspace_size", "mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16",
+    "mla_decode_nope_fp8_656", "mla_merge_lse",
     "mla_cache_write", "mla_status_string", "mla_last_error_message", "mla_abi_version",
 )
 
@@ -63,7 +65,7 @@ def library() -> ctypes.CDLL:
     lib.mla_decode_workspace_size.argtypes = [c_i32, c_i32, c_i32]
     lib.mla_decode_workspace_size.restype = c_sz
     dec = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
-    for name in ("mla_decode_bf16", "mla_decode_fp8_656"):
+    for name in ("mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = c_int
     lib.mla_merge_lse.argtypes = [vp, vp, c_i32, c_i32, c_i32, vp, vp, vp]
@@ -114,7 +116,7 @@ def mla_decode_workspace_size(batch: int, num_heads: int, num_splits: int) -> in
 
 
 def _decode(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
-            softmax_scale, num_splits, out, lse, workspace, partials_only=False):
+            softmax_scale, num_splits, out, lse, workspace, partials_only=False, q_dim=ROW):
     lib = library()
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
@@ -124,8 +126,8 @@ def _decode(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache,
     _need(block_table, "block_table", torch.int32, 2, dev)
     _need(seq_lens, "seq_lens", torch.int32, 1, dev)
     B, H, D = q.shape
-    if D != ROW:
-        raise ValueError(f"q rows must have {ROW} values, got {D}")
+    if D != q_dim:
+        raise ValueError(f"q rows must have {q_dim} values, got {D}")
     if block_table.shape[0] != B or seq_lens.shape[0] != B:
         raise ValueError("block_table and seq_lens must have one row per request")
     if partials_only:
@@ -174,6 +176,20 @@ def mla_decode_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_sp
                    softmax_scale, num_splits, out, lse, workspace, partials_only)
 
 
+def mla_decode_nope_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                         workspace=None, partials_only=False):
+    """NoPE-512 decode over a bf16 cache: q [B, H, 512]; the rows' rope part is never read."""
+    return _decode("mla_decode_nope_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=LATENT)
+
+
+def mla_decode_nope_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                            workspace=None, partials_only=False):
+    """NoPE-512 decode over an fp8 cache: q [B, H, 512]; the rows' rope bytes are never read."""
+    return _decode("mla_decode_nope_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=LATENT)
+
+
 def mla_merge_lse(part_out, part_lse, out=None, lse=None):
     """Merge partials [S, B, H, 512] / [S, B, H] by log-sum-exp; returns (out, lse)."""
     lib = library()
@@ -195,11 +211,14 @@ def mla_merge_lse(part_out, part_lse, out=None, lse=None):
 
 
 def mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format):
-    """Write rows for new tokens at slot_mapping (negative = skip) into kv_cache."""
+    """Write rows for new tokens at slot_mapping (negative = skip) into kv_cache.
+
+    k_pe None (a NoPE layer) writes zeros into the rows' rope part."""
     lib = library()
     _need(latent, "latent", torch.bfloat16, 2)
     dev = latent.device
-    _need(k_pe, "k_pe", torch.bfloat16, 2, dev)
+    if k_pe is not None:
+        _need(k_pe, "k_pe", torch.bfloat16, 2, dev)
     _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
     if cache_format == MLA_CACHE_BF16_576:
         _need(kv_cache, "kv_cache", torch.bfloat16, 3, dev)
@@ -212,8 +231,8 @@ def mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format):
     else:
         raise ValueError(f"unknown cache_format {cache_format}")
     T = latent.shape[0]
-    if latent.shape[1] != LATENT or tuple(k_pe.shape) != (T, ROPE) or slot_mapping.shape[0] != T:
-        raise ValueError("latent must be [T, 512], k_pe [T, 64], slot_mapping [T]")
+    if latent.shape[1] != LATENT or slot_mapping.shape[0] != T or (k_pe is not None and tuple(k_pe.shape) != (T, ROPE)):
+        raise ValueError("latent must be [T, 512], k_pe [T, 64] (or None), slot_mapping [T]")
     num_slots = kv_cache.shape[0] * kv_cache.shape[1]
-    _check("mla_cache_write", lib.mla_cache_write(latent.data_ptr(), k_pe.data_ptr(), slot_mapping.data_ptr(), T,
+    _check("mla_cache_write", lib.mla_cache_write(latent.data_ptr(), _ptr(k_pe), slot_mapping.data_ptr(), T,
                                                   kv_cache.data_ptr(), int(cache_format), num_slots, _stream(dev)))

@@ -10,11 +10,18 @@
 //    the hardware conversion, which rounds to nearest-even but does not saturate; a
 //    block with a == 0 stores s = 0 and zero codes.  Bytes: [0,512) codes,
 //    [512,528) scales (little-endian fp32), [528,656) k_pe as bf16.
+// k_pe == nullptr (a NoPE layer): the rope part is written as zeros.
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
 namespace {
+
+// 16 bytes (8 bf16 values) of token tok's rope part for lane < 8; zeros without k_pe.
+__device__ __forceinline__ u32x4 rope16(const uint16_t* __restrict__ k_pe, int tok, int lane) {
+  if (k_pe == nullptr) return u32x4{0u, 0u, 0u, 0u};
+  return *(const u32x4*)(k_pe + (int64_t)tok * kRope + 8 * lane);
+}
 
 __global__ __launch_bounds__(256) void cache_write_bf16(const uint16_t* __restrict__ latent,
                                                         const uint16_t* __restrict__ k_pe,
@@ -27,7 +34,7 @@ __global__ __launch_bounds__(256) void cache_write_bf16(const uint16_t* __restri
   if (slot < 0) return;
   uint8_t* row = cache + slot * (int64_t)kRowBytesBf16;
   *(u32x4*)(row + 16 * lane) = *(const u32x4*)(latent + (int64_t)tok * kLatent + 8 * lane);
-  if (lane < 8) *(u32x4*)(row + 1024 + 16 * lane) = *(const u32x4*)(k_pe + (int64_t)tok * kRope + 8 * lane);
+  if (lane < 8) *(u32x4*)(row + 1024 + 16 * lane) = rope16(k_pe, tok, lane);
 }
 
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -69,7 +76,7 @@ __global__ __launch_bounds__(256) void cache_write_fp8(const uint16_t* __restric
   }
   *(u32x2*)(row + 8 * lane) = codes;
   if ((lane & 15) == 0) *(float*)(row + 512 + 4 * (lane >> 4)) = s;
-  if (lane < 8) *(u32x4*)(row + 528 + 16 * lane) = *(const u32x4*)(k_pe + (int64_t)tok * kRope + 8 * lane);
+  if (lane < 8) *(u32x4*)(row + 528 + 16 * lane) = rope16(k_pe, tok, lane);
 }
 
 }  // namespace

@@ -67,11 +67,17 @@ __device__ __forceinline__ Range partition(int64_t L, int ps, int S, int s, int6
 __device__ __forceinline__ int swz(int t) { return (((t >> 2) & 1) << 1) | ((t >> 3) & 1); }
 __device__ __forceinline__ int chunk_pos(int t, int c) { return 64 * (c >> 2) + 4 * t + ((c & 3) ^ swz(t)); }
 
+// kRopeDim = 64: the full 576-value row.  kRopeDim = 0 (NoPE-512 layers): only the 512
+// latent values (the first 1,024 bytes of each row) are loaded and scored.
+template <int kRopeDim>
 struct Bf16Rows {
+  static_assert(kRopeDim == 64 || kRopeDim == 0, "rope part: 64 values or none");
   static constexpr int kRowBytes = kRowBytesBf16;
-  static constexpr int kDmaOps = 18;
+  static constexpr int kQDim = kLatent + kRopeDim;      // query values per head
+  static constexpr int kQSteps = kQDim / 32;            // QK K-steps of 32 values
+  static constexpr int kDmaOps = kQDim * 2 / 64;        // 18, or 16 without rope
   static constexpr int kBufs = 2;  // tiles per wave resident in LDS (2 x 4 x 18 KB)
-  static constexpr int kTileBytes = kTile * kRowBytes;  // 18,432
+  static constexpr int kTileBytes = kDmaOps * 1024;     // 18,432 / 16,384
   static constexpr int kAcc = 32;                       // 16x16 output tiles per head group
 
   struct Aux {};
@@ -90,7 +96,7 @@ struct Bf16Rows {
     // Two independent accumulation chains halve the dependent-MFMA latency.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-    for (int j = 0; j < 18; j += 2) {
+    for (int j = 0; j < kQSteps; j += 2) {
       s0 = mfma_16x16x32(*(const u32x4*)(base + 1024 * j), qf[j], s0);
       s1 = mfma_16x16x32(*(const u32x4*)(base + 1024 * (j + 1)), qf[j + 1], s1);
     }
@@ -124,12 +130,20 @@ struct Bf16Rows {
 // fp8 656-byte rows: 41 chunks per token (32 code chunks, 1 scale chunk, 8 rope chunks).
 // Eleven DMA instructions; in the last only chunk 40 exists, and the lanes whose chunk
 // would lie past it re-read chunk 40 into padding, so every access stays in the row.
+// Without rope (kRopeDim = 0) the first 528 bytes are loaded: eight full instructions
+// and a ninth for the scale chunk 32 alone.
 // ------------------------------------------------------------------------------------
+template <int kRopeDim>
 struct Fp8Rows {
+  static_assert(kRopeDim == 64 || kRopeDim == 0, "rope part: 64 values or none");
   static constexpr int kRowBytes = kRowBytesFp8;
-  static constexpr int kDmaOps = 11;
-  static constexpr int kBufs = 2;  // smaller tiles: three in flight per wave (3 x 4 x 11 KB)
-  static constexpr int kTileBytes = kDmaOps * 1024;  // 10,496 used + padding
+  static constexpr int kQDim = kLatent + kRopeDim;
+  static constexpr int kQSteps = kQDim / 32;
+  static constexpr int kFullOps = kRopeDim ? 10 : 8;    // instructions of 4 whole chunks
+  static constexpr int kLastChunk = kRopeDim ? 40 : 32;  // fetched alone by the last one
+  static constexpr int kDmaOps = kFullOps + 1;
+  static constexpr int kBufs = 2;  // two tiles per wave (2 x 4 x 11 KB)
+  static constexpr int kTileBytes = kDmaOps * 1024;  // used bytes + padding
   static constexpr int kAcc = 32;
 
   struct Aux {
@@ -141,8 +155,9 @@ struct Fp8Rows {
   __device__ static __forceinline__ void issue(const uint8_t* row, uint32_t dst, int lane) {
     const uint8_t* src = row + 16 * ((lane & 3) ^ swz(lane >> 2));
 #pragma unroll
-    for (int j = 0; j < 10; ++j) dma16(src + 64 * j, dst + 1024 * j);
-    dma16(row + 16 * 40, dst + 1024 * 10);  // chunk 40 for one lane per token; padding for the rest
+    for (int j = 0; j < kFullOps; ++j) dma16(src + 64 * j, dst + 1024 * j);
+    // chunk kLastChunk for one lane per token; padding for the rest
+    dma16(row + 16 * kLastChunk, dst + 1024 * kFullOps);
   }
 
   __device__ static __forceinline__ u32x4 widen8(u32x2 codes) {
@@ -171,11 +186,15 @@ struct Fp8Rows {
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[r] += aux.sc[r][k] * sk[r];
     }
-    f32x4 sr = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kRopeDim == 0) {
+      return s;
+    } else {
+      f32x4 sr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int jr = 0; jr < 2; ++jr)
-      sr = mfma_16x16x32(*(const u32x4*)(buf + 16 * chunk_pos(m, 33 + 4 * jr + g)), qf[16 + jr], sr);
-    return s + sr;
+      for (int jr = 0; jr < 2; ++jr)
+        sr = mfma_16x16x32(*(const u32x4*)(buf + 16 * chunk_pos(m, 33 + 4 * jr + g)), qf[16 + jr], sr);
+      return s + sr;
+    }
   }
 
   __device__ static __forceinline__ void pv(const uint8_t* buf, int m, int g, const float (&p)[4],
@@ -253,14 +272,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   const int ntiles = (n + kTile - 1) / kTile;
 
   // q as the B operand of the QK MFMA: lane (head m, slice g) holds q[m][32j + 8g .. +8].
-  u32x4 qf[18];
+  constexpr int QS = Fmt::kQSteps;
+  u32x4 qf[QS];
   {
 #pragma unroll
-    for (int j = 0; j < 18; ++j) qf[j] = u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < QS; ++j) qf[j] = u32x4{0u, 0u, 0u, 0u};
     if (m < p.heads) {
-      const uint16_t* qrow = p.q + ((int64_t)b * p.heads + m) * kRow + 8 * g;
+      const uint16_t* qrow = p.q + ((int64_t)b * p.heads + m) * Fmt::kQDim + 8 * g;
 #pragma unroll
-      for (int j = 0; j < 18; ++j) qf[j] = *(const u32x4*)(qrow + 32 * j);
+      for (int j = 0; j < QS; ++j) qf[j] = *(const u32x4*)(qrow + 32 * j);
     }
   }
 
@@ -351,7 +371,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t) page_first[t] = (k + kWaves * t < ntiles) ? bt[lane_token(k + kWaves * t) / ps] : 0;
 #pragma unroll
-  for (int j = 0; j < 18; ++j) asm volatile("" ::"v"(qf[j]));
+  for (int j = 0; j < QS; ++j) asm volatile("" ::"v"(qf[j]));
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t) asm volatile("" ::"v"(page_first[t]));
   if (k < ntiles) {
@@ -412,10 +432,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
         lsum += f * red_l[w * kMaxHeads + h];
         o += f * *(const f32x4*)(red + (w * kMaxHeads + h) * kRedStride + 4 * d4);
       }
-      o *= 1.0f / lsum;
+      o *= 1.0f / lsum;  // a NaN score anywhere made lsum NaN: NaN out
+    } else {
+      // No finite score.  The running maxima ignore NaN scores, but the sums do not: they
+      // are 0 for an empty partition, giving (+0, -inf), and NaN when every score was NaN.
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) lsum += red_l[w * kMaxHeads + h];
+      o *= lsum;
     }
     *(f32x4*)(out + (int64_t)h * kLatent + 4 * d4) = o;
-    if (d4 == 0) lse[h] = (M == -INFINITY) ? -INFINITY : (M + fast_log2(lsum)) * 0.69314718055994530942f;
+    if (d4 == 0) lse[h] = (M == -INFINITY) ? -INFINITY + lsum : (M + fast_log2(lsum)) * 0.69314718055994530942f;
   }
 }
 
@@ -428,7 +454,13 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) { return launch<Bf16Rows>(p, stream); }
-hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream) { return launch<Fp8Rows>(p, stream); }
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) { return launch<Bf16Rows<64>>(p, stream); }
+hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream) { return launch<Fp8Rows<64>>(p, stream); }
+hipError_t launch_decode_nope_bf16(const DecodeParams& p, hipStream_t stream) {
+  return launch<Bf16Rows<0>>(p, stream);
+}
+hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream) {
+  return launch<Fp8Rows<0>>(p, stream);
+}
 
 }  // namespace mla

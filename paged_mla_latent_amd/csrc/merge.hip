@@ -5,6 +5,9 @@
 //   M = max_p lse_p;  M = -inf  ->  (0, -inf)
 //   w_p = exp(lse_p - M);  lse = M + ln sum_p w_p;  out = sum_p w_p out_p / sum_p w_p
 //
+// A NaN partial makes the result NaN (as the definition does), also when every other
+// partition is empty.
+//
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -24,19 +27,36 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __r
   __shared__ f32x4 acc_s[kGroups][kCols];
   __shared__ float w_s[kGroups];
   __shared__ float m_s[kGroups * kCols / 64];
+  __shared__ float n_s[kGroups * kCols / 64];
   const int64_t bh = blockIdx.x;
   const int col = blockIdx.y * kCols + (threadIdx.x % kCols);
   const int grp = threadIdx.x / kCols;
   // M = max_p lse_p: every lane loads a strided share (independent loads), then a
   // wave reduction and a reduction over the waves through LDS.
+  // fmaxf skips NaN, so NaN partials are counted apart and force M = NaN.
   float M = -INFINITY;
-  for (int p = threadIdx.x; p < S; p += kGroups * kCols) M = fmaxf(M, part_lse[p * rows + bh]);
+  float nan = 0.f;
+  for (int p = threadIdx.x; p < S; p += kGroups * kCols) {
+    const float x = part_lse[p * rows + bh];
+    M = fmaxf(M, x);
+    nan = (x != x) ? 1.f : nan;
+  }
 #pragma unroll
-  for (int mask = 32; mask >= 1; mask >>= 1) M = fmaxf(M, __shfl_xor(M, mask, 64));
-  if ((threadIdx.x & 63) == 0) m_s[threadIdx.x >> 6] = M;
+  for (int mask = 32; mask >= 1; mask >>= 1) {
+    M = fmaxf(M, __shfl_xor(M, mask, 64));
+    nan = fmaxf(nan, __shfl_xor(nan, mask, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    m_s[threadIdx.x >> 6] = M;
+    n_s[threadIdx.x >> 6] = nan;
+  }
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < kGroups * kCols / 64; ++w) M = fmaxf(M, m_s[w]);
+  for (int w = 0; w < kGroups * kCols / 64; ++w) {
+    M = fmaxf(M, m_s[w]);
+    nan = fmaxf(nan, n_s[w]);
+  }
+  if (nan != 0.f) M = __builtin_nanf("");
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
   if (M != -INFINITY) {

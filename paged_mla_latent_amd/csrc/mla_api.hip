@@ -60,12 +60,17 @@ size_t workspace_bytes_for(int64_t batch, int64_t heads, int64_t splits) {
   return (bytes + 255) & ~(size_t)255;
 }
 
-int decode_common(int fp8, const void* q, const void* kv_cache, int64_t num_pages,
+// Kinds of decode: row format and whether the rope part takes part in the scores.
+enum DecodeKind { kBf16 = 0, kFp8 = 1, kNopeBf16 = 2, kNopeFp8 = 3 };
+
+int decode_common(int kind, const void* q, const void* kv_cache, int64_t num_pages,
                   const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
                   int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
                   int32_t num_splits, float* out, float* lse, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  const char* fn = fp8 ? "mla_decode_fp8_656" : "mla_decode_bf16";
+  static const char* const kNames[] = {"mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16",
+                                       "mla_decode_nope_fp8_656"};
+  const char* fn = kNames[kind];
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
@@ -119,7 +124,14 @@ int decode_common(int fp8, const void* q, const void* kv_cache, int64_t num_page
   p.part_out = part_out;
   p.part_lse = part_lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = hip_status(fp8 ? mla::launch_decode_fp8(p, s) : mla::launch_decode_bf16(p, s), fn);
+  hipError_t launched;
+  switch (kind) {
+    case kBf16: launched = mla::launch_decode_bf16(p, s); break;
+    case kFp8: launched = mla::launch_decode_fp8(p, s); break;
+    case kNopeBf16: launched = mla::launch_decode_nope_bf16(p, s); break;
+    default: launched = mla::launch_decode_nope_fp8(p, s); break;
+  }
+  rc = hip_status(launched, fn);
   if (rc != MLA_OK || num_splits == 1 || partials_only) return rc;
   return hip_status(mla::launch_merge(part_out, part_lse, num_splits, batch, num_heads, out, lse, s),
                     "mla_merge_lse (after decode)");
@@ -138,7 +150,7 @@ int mla_decode_bf16(const void* q, const void* kv_cache, int64_t num_pages, cons
                     int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                     int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(0, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+  return decode_common(kBf16, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
                        page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -146,8 +158,24 @@ int mla_decode_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, c
                        int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                        int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+  return decode_common(kFp8, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
                        page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_nope_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                         int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                         int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kNopeBf16, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_nope_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                            int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                            int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kNopeFp8, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
 int mla_merge_lse(const float* part_out, const float* part_lse, int32_t num_splits, int32_t batch,
@@ -180,7 +208,6 @@ int mla_cache_write(const void* latent, const void* k_pe, const int64_t* slot_ma
   if (num_slots < 1) return fail(MLA_ERR_SHAPE, "%s: num_slots=%lld must be >= 1", fn, (long long)num_slots);
   if (num_tokens == 0) return MLA_OK;
   if (!latent) return fail(MLA_ERR_NULL, "%s: latent is NULL", fn);
-  if (!k_pe) return fail(MLA_ERR_NULL, "%s: k_pe is NULL", fn);
   if (!slot_mapping) return fail(MLA_ERR_NULL, "%s: slot_mapping is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!aligned16(latent) || !aligned16(k_pe) || !aligned16(slot_mapping) || !aligned16(kv_cache))

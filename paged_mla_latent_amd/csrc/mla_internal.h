@@ -7,7 +7,7 @@
 namespace mla {
 
 struct DecodeParams {
-  const uint16_t* q;           // bf16 [B][H][576]
+  const uint16_t* q;           // bf16 [B][H][576] ([B][H][512] for the NoPE kernels)
   const uint8_t* cache;        // rows of row_bytes bytes
   const int32_t* block_table;  // [B][bt_stride]
   int64_t bt_stride;
@@ -25,6 +25,8 @@ struct DecodeParams {
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_nope_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_merge(const float* part_out, const float* part_lse, int num_splits, int batch,
                         int heads, float* out, float* lse, hipStream_t stream);
 hipError_t launch_cache_write(const uint16_t* latent, const uint16_t* k_pe, const int64_t* slots,

@@ -36,19 +36,21 @@ def poisoned_device_pool(w) -> torch.Tensor:
     return torch.full((w.num_pages, w.page_size, 656), 0xFF, dtype=torch.uint8, device="cuda")
 
 
-def device_pool(w, latent=None, k_pe=None, slots=None) -> torch.Tensor:
-    """Poisoned pool with the workload's rows written by mla_cache_write."""
+def device_pool(w, latent=None, k_pe=None, slots=None, zero_rope=False) -> torch.Tensor:
+    """Poisoned pool with the workload's rows written by mla_cache_write (zero_rope: k_pe NULL)."""
     pool = poisoned_device_pool(w)
     latent = w.latent if latent is None else latent
-    k_pe = w.k_pe if k_pe is None else k_pe
+    k_pe = None if zero_rope else (w.k_pe if k_pe is None else k_pe)
     slots = w.slots if slots is None else slots
-    mla.mla_cache_write(bf16_dev(latent), bf16_dev(k_pe), torch.from_numpy(slots).cuda(), pool, FMT_CODE[w.fmt])
+    mla.mla_cache_write(bf16_dev(latent), None if k_pe is None else bf16_dev(k_pe), torch.from_numpy(slots).cuda(),
+                        pool, FMT_CODE[w.fmt])
     return pool
 
 
-def host_pool(w, latent=None, k_pe=None, slots=None) -> np.ndarray:
+def host_pool(w, latent=None, k_pe=None, slots=None, zero_rope=False) -> np.ndarray:
     pool = w.poisoned_pool()
-    oracle.cache_write(pool, w.latent if latent is None else latent, w.k_pe if k_pe is None else k_pe,
+    oracle.cache_write(pool, w.latent if latent is None else latent,
+                       None if zero_rope else (w.k_pe if k_pe is None else k_pe),
                        w.slots if slots is None else slots, w.fmt)
     return pool
 
@@ -69,11 +71,18 @@ def assert_rows_bitexact(w, pool_dev: torch.Tensor, pool_host: np.ndarray, slots
     assert bad.size == 0, f"{bad.size} rows differ, first slot {slots[bad[0]]}"
 
 
-def gpu_decode(w, pool: torch.Tensor, splits: int, q=None):
-    q = bf16_dev(w.q if q is None else q)
+def gpu_decode(w, pool: torch.Tensor, splits: int, q=None, nope=False):
+    """Decode on the device; nope=True uses the NoPE-512 kernels with the first 512 q values."""
+    q = w.q if q is None else q
+    if nope:
+        q = np.ascontiguousarray(q[:, :, :512])
+    q = bf16_dev(q)
     bt = torch.from_numpy(w.block_table).cuda()
     lens = torch.from_numpy(w.seq_lens).cuda()
-    fn = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
+    if nope:
+        fn = mla.mla_decode_nope_bf16 if w.fmt == "bf16" else mla.mla_decode_nope_fp8_656
+    else:
+        fn = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
     out, lse = fn(q, pool, bt, lens, w.scale, num_splits=splits)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)

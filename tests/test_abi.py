@@ -79,14 +79,17 @@ def _decode(lib, fn="mla_decode_bf16", **kw):
     return rc, lib.mla_last_error_message().decode()
 
 
-@pytest.mark.parametrize("fn", ["mla_decode_bf16", "mla_decode_fp8_656"])
+DECODERS = ["mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656"]
+
+
+@pytest.mark.parametrize("fn", DECODERS)
 @pytest.mark.parametrize("field", ["q", "kv", "bt", "lens", "out", "lse"])
 def test_decode_rejects_null(lib, fn, field):
     rc, msg = _decode(lib, fn, **{field: None})
     assert rc == 1 and "NULL" in msg and fn in msg
 
 
-@pytest.mark.parametrize("fn", ["mla_decode_bf16", "mla_decode_fp8_656"])
+@pytest.mark.parametrize("fn", DECODERS)
 @pytest.mark.parametrize("kw, word", [
     (dict(heads=0), "num_heads"), (dict(heads=17), "num_heads"), (dict(batch=0), "batch"),
     (dict(batch=70000), "batch"), (dict(ps=0), "page_size"), (dict(num_pages=0), "num_pages"),
@@ -131,7 +134,9 @@ def test_cache_write_validation(lib):
     assert f(P, P, P, 1, P, 7, 10, None) == 2
     assert f(P, P, P, 1, P, 0, 0, None) == 2
     assert f(None, P, P, 1, P, 0, 10, None) == 1
+    assert f(P, P, None, 1, P, 0, 10, None) == 1
     assert f(P, P, P, 1, None, 1, 10, None) == 1
+    assert f(MIS, None, P, 1, P, 1, 10, None) == 3  # k_pe NULL is allowed (zero rope)
     assert f(P, MIS, P, 1, P, 1, 10, None) == 3
     assert f(None, None, None, 0, None, 0, 10, None) == 0  # nothing to write: no device needed
 

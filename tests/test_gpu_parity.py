@@ -164,6 +164,25 @@ def test_merge_kernel_matches_oracle():
     assert np.allclose(lse[fin], rl[fin], rtol=0, atol=1e-5)
 
 
+def test_merge_kernel_propagates_nan():
+    """NaN partials beside empty ones give NaN, not the empty result; all-empty stays (0, -inf)."""
+    S, B, H = 300, 1, 4
+    po = np.ones((S, B, H, 512), np.float32)
+    pl = np.full((S, B, H), -np.inf, np.float32)
+    pl[123, 0, 0] = np.nan                  # NaN among empties
+    pl[:, 0, 1] = 1.0
+    pl[299, 0, 1] = np.nan                  # NaN among finite partials
+    pl[7, 0, 2] = 3.0                       # one finite partial
+    out, lse = mla.mla_merge_lse(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    ro, rl = oracle.merge(po.astype(np.float64), pl.astype(np.float64))
+    for h in (0, 1):
+        assert np.isnan(lse[0, h]) and np.isnan(out[0, h]).all() and np.isnan(rl[0, h])
+    assert abs(lse[0, 2] - 3.0) < 1e-6 and np.allclose(out[0, 2], 1.0)
+    assert np.isneginf(lse[0, 3]) and (out[0, 3] == 0).all() and not np.signbit(out[0, 3]).any()
+
+
 # ----------------------------------------------------------------- 64-bit addressing
 @pytest.mark.parametrize("fmt, num_pages", [("bf16", 60000), ("fp8", 110000)])
 def test_pages_beyond_32bit_offsets(fmt, num_pages):
@@ -241,6 +260,66 @@ def test_full_size_workloads_sampled(name):
     ph.reshape(-1, w.row_bytes)[w.slots[idx]] = want
     ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=req)
     assert_parity(w, out, lse, ref_o, ref_l, requests=req, what=f"{name} S={S}")
+
+
+# ------------------------------------------------------------------------- NoPE-512
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("ps", [3, 16, 64])
+def test_nope_parity(fmt, ps):
+    """Zero-rope rows (k_pe NULL) bit for bit; NoPE decode against oracle.decode_nope."""
+    lens = [0, 1, 15, 17, 333, 2500]
+    pages = sum(-(-L // ps) for L in lens) + 5
+    w = workloads.make_workload(f"nope_ps{ps}", seq_lens=lens, heads=16, page_size=ps, num_pages=pages, fmt=fmt,
+                                seed=60 + ps)
+    say(f"case nope fmt={fmt} ps={ps}")
+    pd, ph = device_pool(w, zero_rope=True), host_pool(w, zero_rope=True)
+    assert_rows_bitexact(w, pd, ph)
+    q512 = np.ascontiguousarray(w.q[:, :, :512])
+    ref_o, ref_l = oracle.decode_nope(q512, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt)
+    for S in (1, 3):
+        out, lse = gpu_decode(w, pd, S, nope=True)
+        assert_parity(w, out, lse, ref_o, ref_l, what=f"nope {fmt} ps={ps} S={S}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_nope_never_reads_rope_bytes(fmt):
+    """NaN in every rope value: NoPE decode gives the same bits as on zero rope, while the
+    576-wide decode with q_pe = 0 turns NaN (zero-padding alone does not protect)."""
+    w = workloads.make_workload("nope_nan", seq_lens=[700, 40], heads=16, page_size=16, num_pages=50, fmt=fmt,
+                                seed=8)
+    nan_pe = np.full(w.k_pe.shape, 0x7FC0, np.uint16)
+    p0 = device_pool(w, zero_rope=True)
+    pn = device_pool(w, k_pe=nan_pe)
+    a = gpu_decode(w, p0, 2, nope=True)
+    b = gpu_decode(w, pn, 2, nope=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    q0 = w.q.copy()
+    q0[:, :, 512:] = 0
+    c = gpu_decode(w, p0, 2, q=q0)
+    assert np.isfinite(c[1]).all()
+    assert np.abs(c[1] - a[1]).max() < 1e-3  # same scores up to rounding when the rope is zero
+    d = gpu_decode(w, pn, 2, q=q0)
+    assert np.isnan(d[1]).all() and np.isnan(d[0]).all()  # as oracle.decode gives: every score NaN
+
+
+def test_nope_full_size_sampled():
+    """The fp8 ragged workload as a NoPE layer, at its bench split count."""
+    w = workloads.NAMED["fp8_ragged"]()
+    S = workloads.BENCH_SPLITS["fp8_ragged"]
+    req = _sample(w)
+    say(f"case nope fp8_ragged: B={w.batch} tokens={w.tokens} splits={S} oracle requests={req}")
+    pd = device_pool(w, zero_rope=True)
+    out, lse = gpu_decode(w, pd, S, nope=True)
+    live = w.seq_lens > 0
+    assert np.isfinite(out[live]).all() and np.isfinite(lse[live]).all()
+    ph = w.poisoned_pool()
+    idx = np.unique(np.searchsorted(w.slots, np.concatenate([_request_slots(w, b) for b in req])))
+    ph.reshape(-1, w.row_bytes)[w.slots[idx]] = oracle.pack_rows(w.latent[idx], None, w.fmt)
+    assert np.array_equal(device_rows(pd, w.slots[idx], w.row_bytes), ph.reshape(-1, w.row_bytes)[w.slots[idx]])
+    q512 = np.ascontiguousarray(w.q[:, :, :512])
+    ref_o, ref_l = oracle.decode_nope(q512, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt,
+                                      requests=req)
+    assert_parity(w, out, lse, ref_o, ref_l, requests=req, what=f"nope fp8_ragged S={S}")
 
 
 def test_decode_is_bit_reproducible():

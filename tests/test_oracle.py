@@ -20,7 +20,7 @@ mla.decode_nope          pure-Python brute force over the 512 latent values; equ
                          turn decode with q_pe = 0 into NaN (the pages' control)
 mla.pack_rows(k_pe=None) rope bytes zero, latent bytes as with any k_pe
 mla.merge/split_ranges   split vs unsplit for S in {1, 2, 7, 64}; all-empty partials;
-                         partition coverage
+                         a NaN partial is not an empty one; partition coverage
 workloads.bf16_bits      torch's float32 -> bfloat16 cast (round to nearest even)
 """
 import json
@@ -511,6 +511,20 @@ def test_split_then_merge_equals_unsplit(S):
 def test_merge_of_all_empty_partials():
     o, l = oracle.merge(np.full((5, 2, 3, 512), 7.0), np.full((5, 2, 3), -np.inf))
     assert np.array_equal(o, np.zeros((2, 3, 512))) and np.isneginf(l).all()
+
+
+def test_merge_and_attend_propagate_nan():
+    """A NaN partial (or score) is not an empty one: the merged result is NaN."""
+    po = np.ones((3, 1, 2, 512))
+    pl = np.array([[[np.nan, 1.0]], [[-np.inf, 2.0]], [[-np.inf, np.nan]]])
+    o, l = oracle.merge(po, pl)
+    assert np.isnan(l).all() and np.isnan(o).all()
+    q = np.zeros((1, 576))
+    q[0, 0] = 1.0
+    rows = np.ones((3, 576))
+    rows[1, 0] = np.nan
+    o, l = oracle.attend(q, rows, 0.5)
+    assert np.isnan(l).all() and np.isnan(o).all()
 
 
 def test_merge_two_single_token_partials_is_a_two_token_softmax():
