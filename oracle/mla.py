@@ -25,6 +25,12 @@ What is computed (per request b and head h), following the pages:
   rows neutralise to (0, -inf) per the decode-context-parallel merge contract).
 * Partial results over disjoint token sets merge by log-sum-exp (vLLM PR #55543,
   description: FlashMLA sparse returns the decode LSE needed for DCP and MTP).
+* A speculative-decoding verify step carries q_len = 1 + k query tokens per request, the
+  last q_len positions of its sequence, and reads the cache once for all of them
+  (qwen-mla-vllm, "16 GB GPUs": a verify step that reads the latent cache once per request
+  instead of once per draft token).  Reading (the pages do not spell out the mask): the
+  usual causal one, seq_lens counting the q_len new tokens, so query i of a request with
+  L tokens attends to tokens 0 .. L - q_len + i.
 * NoPE-512 layers (no rotary part) keep the same row and write zeros into its rope part;
   their query has 512 values, padded with zeros to 576, so the rope part adds nothing to
   any score (vLLM PR #55543, description of the zero-rope approach).  decode_nope is the
@@ -146,6 +152,25 @@ def decode(q_bits, pool, block_table, seq_lens, page_size: int, scale: float, fm
     for b in (range(B) if requests is None else requests):
         rows = gather_rows_fast(pool, block_table, b, int(seq_lens[b]), page_size, fmt)
         out[b], lse[b] = attend(q[b], rows, scale)
+    return out, lse
+
+
+def decode_mtp(q_bits, pool, block_table, seq_lens, page_size: int, scale: float, fmt: str,
+               requests=None) -> tuple[np.ndarray, np.ndarray]:
+    """Multi-token verify decode: q_bits [B, q_len, H, 576]; out [B, q_len, H, 512], lse [B, q_len, H].
+
+    Query i of request b attends to its first max(0, L_b - q_len + 1 + i) tokens.
+    """
+    q = bf16_to_f64(q_bits)
+    B, T, H, _ = q.shape
+    out = np.full((B, T, H, LATENT), np.nan)
+    lse = np.full((B, T, H), np.nan)
+    for b in (range(B) if requests is None else requests):
+        L = int(seq_lens[b])
+        rows = gather_rows_fast(pool, block_table, b, L, page_size, fmt)
+        for i in range(T):
+            n = max(0, L - T + 1 + i)
+            out[b, i], lse[b, i] = attend(q[b, i], rows[:n], scale)
     return out, lse
 
 

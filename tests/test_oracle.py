@@ -15,6 +15,9 @@ mla.attend               closed forms (golden); pure-Python brute force (math.fs
                          1-token, uniform-score, duplication, hardmax, empty invariants;
                          a softmax-over-heads mistake planted in the oracle fails them
 mla.decode               page-permutation invariance; garbage-rope control
+mla.decode_mtp           pure-Python brute force with the causal limits written out;
+                         each query equals decode over its truncated context; rows after a
+                         query's position never change it (a planted off-by-one fails)
 mla.decode_nope          pure-Python brute force over the 512 latent values; equals decode
                          with q_pe = 0 on finite rope; unchanged by NaN rope bytes, which
                          turn decode with q_pe = 0 into NaN (the pages' control)
@@ -404,6 +407,68 @@ def test_garbage_rope_control(fmt):
     c = oracle.decode(w.q, pools[0], w.block_table, w.seq_lens, 16, w.scale, fmt)
     d = oracle.decode(w.q, pools[1], w.block_table, w.seq_lens, 16, w.scale, fmt)
     assert np.max(np.abs(c[1] - d[1])) > 1e-3
+
+
+# ----------------------------------------------------------------- multi-token verify
+def test_mtp_matches_brute_force():
+    rng = np.random.default_rng(41)
+    T = 3
+    w = workloads.make_workload("mtp_brute", seq_lens=[5, 2, 0], heads=2, page_size=2, num_pages=8, rng=rng)
+    q = workloads.bf16_bits(rng.standard_normal((w.batch, T, w.heads, 576)).astype(np.float32))
+    pool = w.poisoned_pool()
+    oracle.cache_write(pool, w.latent, w.k_pe, w.slots, "bf16")
+    out, lse = oracle.decode_mtp(q, pool, w.block_table, w.seq_lens, 2, w.scale, "bf16")
+    qf = oracle.bf16_to_f64(q)
+    flat = pool.reshape(-1, 1152)
+    # visible token counts written out by hand: L=5 -> 3, 4, 5; L=2 -> 0, 1, 2; L=0 -> 0, 0, 0
+    visible = {0: [3, 4, 5], 1: [0, 1, 2], 2: [0, 0, 0]}
+    for b in range(w.batch):
+        for i in range(T):
+            rows = []
+            for t in range(visible[b][i]):
+                slot = int(w.block_table[b][t // 2]) * 2 + t % 2
+                rows.append(oracle.bf16_to_f64(flat[slot].view("<u2")).tolist())
+            if not rows:
+                assert (out[b, i] == 0).all() and np.isneginf(lse[b, i]).all()
+                continue
+            bo, bl = _brute_attend(qf[b, i].tolist(), rows, w.scale)
+            assert np.max(np.abs(out[b, i] - bo)) < 1e-12 and np.max(np.abs(lse[b, i] - bl)) < 1e-12
+
+
+def _mtp_case(seed, T=4):
+    rng = np.random.default_rng(seed)
+    w = workloads.make_workload("mtp", seq_lens=[50, 3, 17], heads=4, page_size=8, num_pages=12, rng=rng)
+    q = workloads.bf16_bits(rng.standard_normal((w.batch, T, w.heads, 576)).astype(np.float32))
+    pool = w.poisoned_pool()
+    oracle.cache_write(pool, w.latent, w.k_pe, w.slots, "bf16")
+    return w, q, pool
+
+
+def test_mtp_query_equals_decode_over_its_truncated_context():
+    w, q, pool = _mtp_case(42)
+    T = q.shape[1]
+    out, lse = oracle.decode_mtp(q, pool, w.block_table, w.seq_lens, 8, w.scale, "bf16")
+    for i in range(T):
+        lens_i = np.maximum(0, w.seq_lens - T + 1 + i)
+        o, l = oracle.decode(np.ascontiguousarray(q[:, i]), pool, w.block_table, lens_i, 8, w.scale, "bf16")
+        assert np.array_equal(o, out[:, i]) and np.array_equal(l, lse[:, i])
+
+
+def test_mtp_rows_after_a_query_do_not_change_it():
+    """Rewriting the rows of positions > L - T + i leaves query i unchanged and changes the
+    last query (which sees them).  The brute-force test above pins the exact limits."""
+    w, q, pool = _mtp_case(43)
+    T = q.shape[1]
+    ref = oracle.decode_mtp(q, pool, w.block_table, w.seq_lens, 8, w.scale, "bf16")
+    b, L = 0, int(w.seq_lens[0])
+    for i in range(T - 1):
+        p2 = pool.copy()
+        t = np.arange(L - T + 1 + i, L)  # tokens query i must not see
+        slots = w.block_table[b][t // 8].astype(np.int64) * 8 + t % 8
+        p2.reshape(-1, 1152)[slots] = pool.reshape(-1, 1152)[slots][::-1] ^ np.uint8(0x01)
+        o, l = oracle.decode_mtp(q, p2, w.block_table, w.seq_lens, 8, w.scale, "bf16")
+        assert np.array_equal(o[b, i], ref[0][b, i]) and np.array_equal(l[b, i], ref[1][b, i])
+        assert np.abs(l[b, T - 1] - ref[1][b, T - 1]).max() > 1e-9
 
 
 # --------------------------------------------------------------------------- NoPE-512
