@@ -67,7 +67,8 @@ enum {
   MLA_CACHE_FP8_656 = 1   /* 512 e4m3 codes, 4 fp32 block scales, 64 bf16 = 656 B */
 };
 
-enum { MLA_LATENT = 512, MLA_ROPE = 64, MLA_ROW = 576, MLA_MAX_HEADS = 16 };
+enum { MLA_LATENT = 512, MLA_ROPE = 64, MLA_ROW = 576, MLA_MAX_HEADS = 16, MLA_MAX_Q_LEN = 16,
+       MLA_MAX_QUERY_ROWS = 64 };
 
 /* Bytes of workspace mla_decode_bf16 / mla_decode_fp8_656 need for num_splits
  * partitions: num_splits * batch * num_heads * (512 + 1) * 4 rounded up to 256,
@@ -142,6 +143,34 @@ MLA_API int mla_decode_nope_fp8_656(const void* q, const void* kv_cache, int64_t
                                     int32_t page_size, float softmax_scale, int32_t num_splits,
                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/* Multi-token verify decode (speculative decoding): q_len query tokens per request, the
+ * last q_len positions of its sequence, scored against the cache in one pass that reads
+ * every row once per request (qwen-mla-vllm, "16 GB GPUs": a verify step reading the latent
+ * cache once per request instead of once per draft token).  Causal: seq_lens[b] = L counts
+ * the q_len new tokens, whose rows must already be in the cache, and query i (0-based)
+ * attends to tokens 0 .. L - q_len + i; a query that sees no token (L < q_len) gets
+ * (+0, -inf).  The mask is this library's reading; the pages do not spell it out.
+ * q      bf16 [batch][q_len][num_heads][576]
+ * out    fp32 [batch][q_len][num_heads][512];  lse fp32 [batch][q_len][num_heads]
+ * q_len  1..MLA_MAX_Q_LEN with q_len * num_heads <= MLA_MAX_QUERY_ROWS (64); q_len = 1 is
+ *        mla_decode_bf16 / mla_decode_fp8_656.
+ * The workspace is sized as for num_heads' = q_len * num_heads
+ * (mla_decode_workspace_size(batch, q_len * num_heads, num_splits)); partials and
+ * mla_merge_lse treat the q_len * num_heads query rows of a request as its heads.
+ * Every other argument, result and error as mla_decode_bf16 / mla_decode_fp8_656. */
+MLA_API int mla_decode_mtp_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                                const int32_t* block_table, int64_t block_table_stride,
+                                const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t num_heads,
+                                int32_t page_size, float softmax_scale, int32_t num_splits,
+                                float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream);
+MLA_API int mla_decode_mtp_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                                   const int32_t* block_table, int64_t block_table_stride,
+                                   const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                                   int32_t num_heads, int32_t page_size, float softmax_scale,
+                                   int32_t num_splits, float* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* Merge num_splits partial results over disjoint token sets (vLLM pull request
  * 55543: partial (o, lse) pairs merge by log-sum-exp; a partition with no

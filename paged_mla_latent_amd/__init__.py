@@ -9,6 +9,7 @@ Entry points (same names as the C ABI in include/mla.h):
     mla_decode_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, ...)
     mla_decode_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, ...)
     mla_decode_nope_bf16 / mla_decode_nope_fp8_656(q [B, H, 512], ...)   NoPE-512 layers
+    mla_decode_mtp_bf16 / mla_decode_mtp_fp8_656(q [B, q_len, H, 576], ...)   verify step
     mla_merge_lse(part_out, part_lse, out=None, lse=None)
     mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format)   k_pe None: zero rope
     mla_decode_workspace_size(batch, num_heads, num_splits)
@@ -33,10 +34,12 @@ MLA_CACHE_FP8_656 = 1
 LATENT, ROPE, ROW = 512, 64, 576
 ROW_BYTES = {MLA_CACHE_BF16_576: 1152, MLA_CACHE_FP8_656: 656}
 MAX_HEADS = 16
+MAX_Q_LEN = 16
+MAX_QUERY_ROWS = 64
 
 EXPORTED = (
     "mla_decode_workspace_size", "mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16",
-    "mla_decode_nope_fp8_656", "mla_merge_lse",
+    "mla_decode_nope_fp8_656", "mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656", "mla_merge_lse",
     "mla_cache_write", "mla_status_string", "mla_last_error_message", "mla_abi_version",
 )
 
@@ -67,6 +70,10 @@ def library() -> ctypes.CDLL:
     dec = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
     for name in ("mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656"):
         getattr(lib, name).argtypes = dec
+        getattr(lib, name).restype = c_int
+    mtp = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
+    for name in ("mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656"):
+        getattr(lib, name).argtypes = mtp
         getattr(lib, name).restype = c_int
     lib.mla_merge_lse.argtypes = [vp, vp, c_i32, c_i32, c_i32, vp, vp, vp]
     lib.mla_merge_lse.restype = c_int
@@ -188,6 +195,57 @@ def mla_decode_nope_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, n
     """NoPE-512 decode over an fp8 cache: q [B, H, 512]; the rows' rope bytes are never read."""
     return _decode("mla_decode_nope_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
                    softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=LATENT)
+
+
+def _decode_mtp(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
+                softmax_scale, num_splits, out, lse, workspace):
+    lib = library()
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _need(kv_cache, "kv_cache", cache_dtype, 3, dev)
+    if kv_cache.shape[2] != row_bytes_last:
+        raise ValueError(f"kv_cache rows must have {row_bytes_last} elements, got {kv_cache.shape[2]}")
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, T, H, D = q.shape
+    if D != ROW:
+        raise ValueError(f"q rows must have {ROW} values, got {D}")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have one row per request")
+    if out is None:
+        out = torch.empty((B, T, H, LATENT), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 4, dev)
+    _need(lse, "lse", torch.float32, 3, dev)
+    ws_bytes = 0
+    if num_splits > 1:
+        need = mla_decode_workspace_size(B, T * H, num_splits)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    status = getattr(lib, fn)(
+        q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1],
+        seq_lens.data_ptr(), B, T, H, kv_cache.shape[1], float(softmax_scale), int(num_splits),
+        out.data_ptr(), lse.data_ptr(), _ptr(workspace), ws_bytes, _stream(dev))
+    _check(fn, status)
+    return out, lse
+
+
+def mla_decode_mtp_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                        workspace=None):
+    """Verify-step decode over a bf16 cache: q [B, q_len, H, 576] -> (out [B, q_len, H, 512], lse [B, q_len, H]).
+
+    seq_lens count the q_len new tokens; query i sees tokens 0 .. L - q_len + i."""
+    return _decode_mtp("mla_decode_mtp_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
+                       softmax_scale, num_splits, out, lse, workspace)
+
+
+def mla_decode_mtp_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                           workspace=None):
+    """Verify-step decode over an fp8 cache uint8 [num_pages, page_size, 656]."""
+    return _decode_mtp("mla_decode_mtp_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
+                       softmax_scale, num_splits, out, lse, workspace)
 
 
 def mla_merge_lse(part_out, part_lse, out=None, lse=None):

@@ -252,8 +252,19 @@ constexpr int smem_bytes() {
   return pipe_bytes<Fmt>() > kRedBytes ? pipe_bytes<Fmt>() : kRedBytes;
 }
 
-template <class Fmt>
+// Query rows.  A launch decodes R = q_len x heads query rows per request (q_len > 1: the
+// query tokens of a speculative-decoding verify step, query i of a request with L tokens
+// seeing tokens 0 .. L - q_len + i).  Row r = i * heads + h.  The rows are cut into G
+// groups of 16 (one MFMA N-tile each):
+//  * G = 1 (R <= 16): every wave streams its own tiles k = wave, wave + 4, ... and scores
+//    them for all rows; the four waves' states are merged at the end (no barrier).
+//  * G = 2 or 4: every wave still streams its own tiles, but a workgroup barrier per step
+//    makes the step's four tiles visible to all waves, and wave w scores tiles
+//    G(w/G) .. G(w/G) + G - 1 of the step for row group w % G.  The cache is read once
+//    per request whatever q_len is; the arithmetic per byte grows with G.
+template <class Fmt, int G>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) {
+  static_assert(G == 1 || G == 2 || G == 4, "row groups per workgroup");
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
 
   // Partition-major grid: all requests' first partitions are dispatched first, then the
@@ -271,20 +282,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   const int n = (int)(rg.t1 - rg.t0);
   const int ntiles = (n + kTile - 1) / kTile;
 
-  // q as the B operand of the QK MFMA: lane (head m, slice g) holds q[m][32j + 8g .. +8].
+  const int H = p.heads;
+  const int R = p.q_len * H;                     // query rows of a request
+  const int row = 16 * (G == 1 ? 0 : wave % G) + m;  // this lane's query row
+  // This lane's row sees the tokens before `lim` (absolute); as an offset into the
+  // partition, clamped to its end.
+  const int64_t lim = L - p.q_len + 1 + (row < R ? row / H : 0);
+  const int n_vis = (int)(min(rg.t1, lim) - rg.t0);
+
+  // q as the B operand of the QK MFMA: lane (row m, slice g) holds q[row][32j + 8g .. +8].
   constexpr int QS = Fmt::kQSteps;
   u32x4 qf[QS];
   {
 #pragma unroll
     for (int j = 0; j < QS; ++j) qf[j] = u32x4{0u, 0u, 0u, 0u};
-    if (m < p.heads) {
-      const uint16_t* qrow = p.q + ((int64_t)b * p.heads + m) * Fmt::kQDim + 8 * g;
+    if (row < R) {
+      const uint16_t* qrow = p.q + ((int64_t)b * R + row) * Fmt::kQDim + 8 * g;
 #pragma unroll
       for (int j = 0; j < QS; ++j) qf[j] = *(const u32x4*)(qrow + 32 * j);
     }
   }
 
-  float m_run = -INFINITY;  // running max (log2 domain) for head m
+  float m_run = -INFINITY;  // running max (log2 domain) of this lane's row
   float l_run = 0.f;        // this lane's share of the softmax denominator
   f32x4 O[Fmt::kAcc];
 #pragma unroll
@@ -320,11 +339,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   };
   auto read_page = [&](const uint8_t* slot) -> int32_t { return *(const int32_t*)(slot + 4 * lane); };
 
-  // One tile of work: QK^T, online softmax, PV on the tile in `buf`.
+  // One tile of work: QK^T, online softmax, PV on tile k (partition-relative) in `buf`.
+  // Tokens at or past this lane's visibility limit, or past the partition, get p = 0.
   auto compute = [&](const uint8_t* buf, int k) {
     typename Fmt::Aux aux;
     const f32x4 raw = Fmt::qk(buf, m, g, qf, aux);
-    const int valid = n - k * kTile;
+    const int valid = n_vis - k * kTile;
     float sc[4];
     float mx = -INFINITY;
 #pragma unroll
@@ -335,32 +355,27 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
     mx = max_over_rows(mx);
     const bool grow = mx > m_run + kRescaleThreshold;
     if (__builtin_amdgcn_ballot_w64(grow)) {
+      // Rows that do not grow keep alpha = 1 (exp2(m_run - m_run) would be NaN for a row
+      // that has seen no visible token, m_run = -inf).
       const float m_new = grow ? mx : m_run;
-      const float alpha = fast_exp2(m_run - m_new);
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int u = 0; u < Fmt::kAcc; ++u) O[u] *= alpha;
       m_run = m_new;
     }
+    // A row that has seen no visible token yet keeps m_run = -inf: its masked scores
+    // must give exp2(-inf) = 0, not exp2(-inf - -inf) = NaN.
+    const float m_base = m_run == -INFINITY ? 0.f : m_run;
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pr[r] = fast_exp2(sc[r] - m_run);
+      pr[r] = fast_exp2(sc[r] - m_base);
       l_run += pr[r];
     }
     Fmt::pv(buf, m, g, pr, aux, O);
   };
 
-  // Software pipeline over this wave's tiles k = wave, wave + 4, ...  With NB = kBufs
-  // buffers, step i computes tile k while tiles k + 4 .. k + 4(NB - 1) stream in.  The
-  // vector-memory queue is kept in this order (completion is in order):
-  //     ... PID(k + 4(NB-1))  DMA(k)  PID(k + 4NB)  DMA(k + 4)  ...
-  // where PID(t) is the 4-byte page-id DMA of tile t and DMA(t) its D row DMAs.  Step i
-  // first waits until PID(k + 4(NB-1)) has landed (at most (NB-1)D + NB-2 younger ops),
-  // issues PID(k + 8(NB-1)) and DMA(k + 4(NB-1)), then waits until DMA(k) has landed (at
-  // most (NB-1)(D+1) younger ops).  The steady loop runs only while tile k + 4(NB-1)
-  // exists, so every counted op is really issued; page-id fetches past the end re-read
-  // the last tile's entries.  The last NB-1 tiles drain under a full wait.
   constexpr int NB = Fmt::kBufs;
   constexpr int D = Fmt::kDmaOps;
   int k = wave;
@@ -369,7 +384,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   // a compiler-generated vmcnt wait would also wait for the hand-counted DMAs).
   int32_t page_first[NB - 1];
 #pragma unroll
-  for (int t = 0; t < NB - 1; ++t) page_first[t] = (k + kWaves * t < ntiles) ? bt[lane_token(k + kWaves * t) / ps] : 0;
+  for (int t = 0; t < NB - 1; ++t)
+    page_first[t] = (k + kWaves * t < ntiles) ? bt[lane_token(k + kWaves * t) / ps] : 0;
 #pragma unroll
   for (int j = 0; j < QS; ++j) asm volatile("" ::"v"(qf[j]));
 #pragma unroll
@@ -381,25 +397,64 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
       if (k + kWaves * t < ntiles)
         Fmt::issue(row_of(lane_token(k + kWaves * t), page_first[t]), wlds + t * Fmt::kTileBytes, lane);
     }
-    int cur = 0;  // buffer / page-id slot of tile k (step index mod NB)
-    for (; k + kWaves * (NB - 1) < ntiles; k += kWaves) {
-      const int ahead = cur == 0 ? NB - 1 : cur - 1;  // (cur + NB - 1) mod NB
-      wait_vmcnt<(NB - 1) * D + (NB - 2)>();  // page ids of tile k + 4(NB-1) have landed
-      const int32_t page_n = read_page(pslot + 256 * cur);
-      fetch_page(min(k + kWaves * 2 * (NB - 1), ntiles - 1), plds + 256 * ahead);
-      Fmt::issue(row_of(lane_token(k + kWaves * (NB - 1)), page_n), wlds + ahead * Fmt::kTileBytes, lane);
-      wait_vmcnt<(NB - 1) * (D + 1)>();  // tile k has landed
-      compute(wbuf + cur * Fmt::kTileBytes, k);
-      cur = cur + 1 == NB ? 0 : cur + 1;
+  }
+
+  if constexpr (G == 1) {
+    // Software pipeline over this wave's tiles k = wave, wave + 4, ...  With NB = kBufs
+    // buffers, step i computes tile k while tiles k + 4 .. k + 4(NB - 1) stream in.  The
+    // vector-memory queue is kept in this order (completion is in order):
+    //     ... PID(k + 4(NB-1))  DMA(k)  PID(k + 4NB)  DMA(k + 4)  ...
+    // where PID(t) is the 4-byte page-id DMA of tile t and DMA(t) its D row DMAs.  Step i
+    // first waits until PID(k + 4(NB-1)) has landed (at most (NB-1)D + NB-2 younger ops),
+    // issues PID(k + 8(NB-1)) and DMA(k + 4(NB-1)), then waits until DMA(k) has landed (at
+    // most (NB-1)(D+1) younger ops).  The steady loop runs only while tile k + 4(NB-1)
+    // exists, so every counted op is really issued; page-id fetches past the end re-read
+    // the last tile's entries.  The last NB-1 tiles drain under a full wait.
+    if (k < ntiles) {
+      int cur = 0;  // buffer / page-id slot of tile k (step index mod NB)
+      for (; k + kWaves * (NB - 1) < ntiles; k += kWaves) {
+        const int ahead = cur == 0 ? NB - 1 : cur - 1;  // (cur + NB - 1) mod NB
+        wait_vmcnt<(NB - 1) * D + (NB - 2)>();  // page ids of tile k + 4(NB-1) have landed
+        const int32_t page_n = read_page(pslot + 256 * cur);
+        fetch_page(min(k + kWaves * 2 * (NB - 1), ntiles - 1), plds + 256 * ahead);
+        Fmt::issue(row_of(lane_token(k + kWaves * (NB - 1)), page_n), wlds + ahead * Fmt::kTileBytes, lane);
+        wait_vmcnt<(NB - 1) * (D + 1)>();  // tile k has landed
+        compute(wbuf + cur * Fmt::kTileBytes, k);
+        cur = cur + 1 == NB ? 0 : cur + 1;
+      }
+      wait_vmcnt<0>();
+      for (; k < ntiles; k += kWaves) {
+        compute(wbuf + cur * Fmt::kTileBytes, k);
+        cur = cur + 1 == NB ? 0 : cur + 1;
+      }
     }
-    wait_vmcnt<0>();
-    for (; k < ntiles; k += kWaves) {
-      compute(wbuf + cur * Fmt::kTileBytes, k);
-      cur = cur + 1 == NB ? 0 : cur + 1;
+  } else {
+    static_assert(NB == 2, "the shared-tile pipeline is written for two buffers per wave");
+    // Step i: every wave waits for its own tile 4i + wave (and the page ids of its next
+    // one), the barrier makes all four tiles of the step visible and tells every wave that
+    // the others are done with step i-1, whose buffers the next tiles then overwrite.
+    const int nsteps = (ntiles + kWaves - 1) / kWaves;
+    const int u0 = G * (wave / G);  // first tile of a step this wave scores
+#pragma unroll 1
+    for (int i = 0; i < nsteps; ++i) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      const int kn = kWaves * (i + 1) + wave;  // this wave's tile of step i + 1
+      if (kn < ntiles) {
+        const int32_t page_n = read_page(pslot + 256 * (i & 1));
+        fetch_page(min(kn + kWaves, ntiles - 1), plds + 256 * ((i + 1) & 1));
+        Fmt::issue(row_of(lane_token(kn), page_n), wlds + ((i + 1) & 1) * Fmt::kTileBytes, lane);
+      }
+#pragma unroll 1
+      for (int u = u0; u < u0 + G; ++u) {
+        const int kt = kWaves * i + u;
+        if (kt < ntiles) compute(smem + (u * NB + (i & 1)) * Fmt::kTileBytes, kt);
+      }
     }
   }
 
   // ---- merge the waves' states through LDS ---------------------------------------
+  // Row group gg's states are held by the waves w with w % G == gg.
   l_run = sum_over_rows(l_run);
   __syncthreads();
   float* red = (float*)smem;
@@ -412,43 +467,50 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   }
   __syncthreads();
 
-  const int H = p.heads;
   const bool split = p.num_splits > 1;
-  const int64_t row_bh = (int64_t)b * H;
-  float* out = split ? p.part_out + ((int64_t)s * p.batch * H + row_bh) * kLatent : p.out + row_bh * kLatent;
-  float* lse = split ? p.part_lse + (int64_t)s * p.batch * H + row_bh : p.lse + row_bh;
-  for (int idx = threadIdx.x; idx < H * (kLatent / 4); idx += kWaves * 64) {
-    const int h = idx / (kLatent / 4);
+  const int64_t row_b = (int64_t)b * R;
+  float* out = split ? p.part_out + ((int64_t)s * p.batch * R + row_b) * kLatent : p.out + row_b * kLatent;
+  float* lse = split ? p.part_lse + (int64_t)s * p.batch * R + row_b : p.lse + row_b;
+  for (int idx = threadIdx.x; idx < R * (kLatent / 4); idx += kWaves * 64) {
+    const int r = idx / (kLatent / 4);
     const int d4 = idx % (kLatent / 4);
+    const int gg = r / 16;
+    const int mm = r % 16;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w * kMaxHeads + h]);
+    for (int w = gg; w < kWaves; w += G) M = fmaxf(M, red_m[w * kMaxHeads + mm]);
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = fast_exp2(red_m[w * kMaxHeads + h] - M);
-        lsum += f * red_l[w * kMaxHeads + h];
-        o += f * *(const f32x4*)(red + (w * kMaxHeads + h) * kRedStride + 4 * d4);
+      for (int w = gg; w < kWaves; w += G) {
+        const float f = fast_exp2(red_m[w * kMaxHeads + mm] - M);
+        lsum += f * red_l[w * kMaxHeads + mm];
+        o += f * *(const f32x4*)(red + (w * kMaxHeads + mm) * kRedStride + 4 * d4);
       }
       o *= 1.0f / lsum;  // a NaN score anywhere made lsum NaN: NaN out
     } else {
       // No finite score.  The running maxima ignore NaN scores, but the sums do not: they
       // are 0 for an empty partition, giving (+0, -inf), and NaN when every score was NaN.
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) lsum += red_l[w * kMaxHeads + h];
+      for (int w = gg; w < kWaves; w += G) lsum += red_l[w * kMaxHeads + mm];
       o *= lsum;
     }
-    *(f32x4*)(out + (int64_t)h * kLatent + 4 * d4) = o;
-    if (d4 == 0) lse[h] = (M == -INFINITY) ? -INFINITY + lsum : (M + fast_log2(lsum)) * 0.69314718055994530942f;
+    *(f32x4*)(out + (int64_t)r * kLatent + 4 * d4) = o;
+    if (d4 == 0) lse[r] = (M == -INFINITY) ? -INFINITY + lsum : (M + fast_log2(lsum)) * 0.69314718055994530942f;
   }
 }
 
 template <class Fmt>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.batch, (unsigned)p.num_splits);
-  hipLaunchKernelGGL(decode_kernel<Fmt>, grid, dim3(kWaves * 64), 0, stream, p);
+  const int R = p.q_len * p.heads;
+  if (R <= 16)
+    hipLaunchKernelGGL((decode_kernel<Fmt, 1>), grid, dim3(kWaves * 64), 0, stream, p);
+  else if (R <= 32)
+    hipLaunchKernelGGL((decode_kernel<Fmt, 2>), grid, dim3(kWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<Fmt, 4>), grid, dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -63,14 +63,14 @@ size_t workspace_bytes_for(int64_t batch, int64_t heads, int64_t splits) {
 // Kinds of decode: row format and whether the rope part takes part in the scores.
 enum DecodeKind { kBf16 = 0, kFp8 = 1, kNopeBf16 = 2, kNopeFp8 = 3 };
 
-int decode_common(int kind, const void* q, const void* kv_cache, int64_t num_pages,
+int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, int64_t num_pages,
                   const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
                   int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
                   int32_t num_splits, float* out, float* lse, void* workspace, size_t workspace_bytes,
                   void* stream) {
   static const char* const kNames[] = {"mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16",
                                        "mla_decode_nope_fp8_656"};
-  const char* fn = kNames[kind];
+  const char* fn = q_len == 1 ? kNames[kind] : (kind == kBf16 ? "mla_decode_mtp_bf16" : "mla_decode_mtp_fp8_656");
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
@@ -82,6 +82,10 @@ int decode_common(int kind, const void* q, const void* kv_cache, int64_t num_pag
   if (batch < 1 || batch > 65535) return fail(MLA_ERR_SHAPE, "%s: batch=%d outside [1, 65535]", fn, batch);
   if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
     return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_HEADS);
+  if (q_len < 1 || q_len > MLA_MAX_Q_LEN)
+    return fail(MLA_ERR_SHAPE, "%s: q_len=%d outside [1, %d]", fn, q_len, MLA_MAX_Q_LEN);
+  if (q_len * num_heads > MLA_MAX_QUERY_ROWS)
+    return fail(MLA_ERR_SHAPE, "%s: q_len * num_heads = %d exceeds %d", fn, q_len * num_heads, MLA_MAX_QUERY_ROWS);
   if (page_size < 1) return fail(MLA_ERR_SHAPE, "%s: page_size=%d must be >= 1", fn, page_size);
   if (num_pages < 1) return fail(MLA_ERR_SHAPE, "%s: num_pages=%lld must be >= 1", fn, (long long)num_pages);
   if (block_table_stride < 1)
@@ -97,13 +101,13 @@ int decode_common(int kind, const void* q, const void* kv_cache, int64_t num_pag
   float* part_out = nullptr;
   float* part_lse = nullptr;
   if (num_splits > 1) {
-    const size_t need = workspace_bytes_for(batch, num_heads, num_splits);
+    const size_t need = workspace_bytes_for(batch, (int64_t)q_len * num_heads, num_splits);
     if (!workspace) return fail(MLA_ERR_WORKSPACE, "%s: num_splits=%d needs a workspace", fn, num_splits);
     if (!aligned16(workspace)) return fail(MLA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
     if (workspace_bytes < need)
       return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
     part_out = static_cast<float*>(workspace);
-    part_lse = part_out + (size_t)num_splits * batch * num_heads * MLA_LATENT;
+    part_lse = part_out + (size_t)num_splits * batch * q_len * num_heads * MLA_LATENT;
   }
   int rc = check_device();
   if (rc != MLA_OK) return rc;
@@ -116,6 +120,7 @@ int decode_common(int kind, const void* q, const void* kv_cache, int64_t num_pag
   p.seq_lens = seq_lens;
   p.batch = batch;
   p.heads = num_heads;
+  p.q_len = q_len;
   p.page_size = page_size;
   p.num_splits = num_splits;
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
@@ -133,7 +138,7 @@ int decode_common(int kind, const void* q, const void* kv_cache, int64_t num_pag
   }
   rc = hip_status(launched, fn);
   if (rc != MLA_OK || num_splits == 1 || partials_only) return rc;
-  return hip_status(mla::launch_merge(part_out, part_lse, num_splits, batch, num_heads, out, lse, s),
+  return hip_status(mla::launch_merge(part_out, part_lse, num_splits, batch, q_len * num_heads, out, lse, s),
                     "mla_merge_lse (after decode)");
 }
 
@@ -150,7 +155,7 @@ int mla_decode_bf16(const void* q, const void* kv_cache, int64_t num_pages, cons
                     int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                     int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kBf16, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+  return decode_common(kBf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
                        page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -158,7 +163,7 @@ int mla_decode_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, c
                        int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                        int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kFp8, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+  return decode_common(kFp8, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
                        page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -166,7 +171,7 @@ int mla_decode_nope_bf16(const void* q, const void* kv_cache, int64_t num_pages,
                          int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                          int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kNopeBf16, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+  return decode_common(kNopeBf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                        num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -174,7 +179,23 @@ int mla_decode_nope_fp8_656(const void* q, const void* kv_cache, int64_t num_pag
                             int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                             int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kNopeFp8, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+  return decode_common(kNopeFp8, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_mtp_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                        int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                        int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_splits, float* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kBf16, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_mtp_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                           int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                           int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_splits, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kFp8, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                        num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 

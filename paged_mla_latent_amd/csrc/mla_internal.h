@@ -7,20 +7,21 @@
 namespace mla {
 
 struct DecodeParams {
-  const uint16_t* q;           // bf16 [B][H][576] ([B][H][512] for the NoPE kernels)
+  const uint16_t* q;           // bf16 [B][q_len][H][576] ([..][512] for the NoPE kernels)
   const uint8_t* cache;        // rows of row_bytes bytes
   const int32_t* block_table;  // [B][bt_stride]
   int64_t bt_stride;
   const int32_t* seq_lens;     // [B]
   int batch;
   int heads;
+  int q_len;                   // query tokens per request (1 = plain decode)
   int page_size;
   int num_splits;
   float scale_log2;            // softmax_scale * log2(e)
-  float* out;                  // [B][H][512]  (num_splits == 1)
-  float* lse;                  // [B][H]
-  float* part_out;             // [S][B][H][512] (num_splits > 1)
-  float* part_lse;             // [S][B][H]
+  float* out;                  // [B][q_len][H][512]  (num_splits == 1)
+  float* lse;                  // [B][q_len][H]
+  float* part_out;             // [S][B][q_len][H][512] (num_splits > 1)
+  float* part_lse;             // [S][B][q_len][H]
 };
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);

@@ -108,6 +108,34 @@ def test_decode_rejects_misaligned(lib, field):
     assert rc == 3 and "aligned" in msg
 
 
+def _mtp(lib, fn="mla_decode_mtp_bf16", **kw):
+    args = dict(q=P, kv=P, num_pages=10, bt=P, stride=4, lens=P, batch=2, q_len=4, heads=16, ps=64, scale=0.07,
+                splits=1, out=P, lse=P, ws=None, ws_bytes=0)
+    args.update(kw)
+    rc = getattr(lib, fn)(args["q"], args["kv"], args["num_pages"], args["bt"], args["stride"], args["lens"],
+                          args["batch"], args["q_len"], args["heads"], args["ps"], args["scale"], args["splits"],
+                          args["out"], args["lse"], args["ws"], args["ws_bytes"], None)
+    return rc, lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("fn", ["mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656"])
+@pytest.mark.parametrize("kw, word", [
+    (dict(q_len=0), "q_len"), (dict(q_len=17), "q_len"), (dict(q_len=5, heads=16), "q_len * num_heads"),
+    (dict(q_len=16, heads=5), "q_len * num_heads"), (dict(heads=0), "num_heads"), (dict(splits=0), "num_splits"),
+])
+def test_mtp_rejects_bad_shapes(lib, fn, kw, word):
+    rc, msg = _mtp(lib, fn, **kw)
+    assert rc == 2 and word in msg and fn in msg
+
+
+def test_mtp_workspace_counts_query_rows(lib):
+    need = mla.mla_decode_workspace_size(2, 4 * 16, 8)
+    rc, msg = _mtp(lib, splits=8, ws=P, ws_bytes=need - 1)
+    assert rc == 4 and str(need) in msg
+    rc, msg = _mtp(lib, q=None)
+    assert rc == 1 and "q is NULL" in msg
+
+
 def test_decode_split_needs_workspace(lib):
     rc, msg = _decode(lib, splits=4)
     assert rc == 4 and "workspace" in msg

@@ -7,6 +7,8 @@ its own pool -> per (request, head) max |out - ref| <= 1e-2 * max |ref| and
 with NaN (bf16) or 0xFF bytes (fp8) wherever no request reads, so a stray read
 shows up as a non-finite output.
 """
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -260,6 +262,70 @@ def test_full_size_workloads_sampled(name):
     ph.reshape(-1, w.row_bytes)[w.slots[idx]] = want
     ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=req)
     assert_parity(w, out, lse, ref_o, ref_l, requests=req, what=f"{name} S={S}")
+
+
+# ---------------------------------------------------------------- multi-token verify
+def _gpu_mtp(w, pool, q_bits, splits):
+    bt = torch.from_numpy(w.block_table).cuda()
+    lens = torch.from_numpy(w.seq_lens).cuda()
+    fn = mla.mla_decode_mtp_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_fp8_656
+    out, lse = fn(bf16_dev(q_bits), pool, bt, lens, w.scale, num_splits=splits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what, requests=None):
+    """Per (request, query) the usual bar; queries that see no token give exactly (+0, -inf)."""
+    requests = range(w.batch) if requests is None else requests
+    for i in range(T):
+        lens_i = np.maximum(0, w.seq_lens - T + 1 + i)
+        view = types.SimpleNamespace(batch=w.batch, seq_lens=lens_i)
+        assert_parity(view, out[:, i], lse[:, i], ref_o[:, i], ref_l[:, i], requests, what=f"{what} query {i}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("T, H", [(1, 16), (2, 16), (3, 16), (4, 16), (4, 4), (5, 3), (16, 4)])
+def test_mtp_parity(fmt, T, H):
+    lens = [0, 1, T - 1, T, T + 1, 17, 64, 65, 500, 2047, 3000]
+    ps = 16
+    pages = sum(-(-L // ps) for L in lens) + 4
+    w = workloads.make_workload(f"mtp{T}x{H}", seq_lens=[max(0, L) for L in lens], heads=H, page_size=ps,
+                                num_pages=pages, fmt=fmt, seed=70 + 4 * T + H)
+    q = workloads.bf16_bits(np.random.default_rng(T * 100 + H).standard_normal((w.batch, T, H, 576))
+                            .astype(np.float32))
+    say(f"case mtp fmt={fmt} q_len={T} heads={H} rows={T * H}")
+    pd, ph = device_pool(w), host_pool(w)
+    ref_o, ref_l = oracle.decode_mtp(q, ph, w.block_table, w.seq_lens, ps, w.scale, fmt)
+    for S in (1, 4, 16):
+        out, lse = _gpu_mtp(w, pd, q, S)
+        _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp {fmt} T={T} H={H} S={S}")
+
+
+def test_mtp_single_query_is_plain_decode():
+    w = workloads.make_workload("mtp1", seq_lens=[3000, 5, 0, 777], heads=16, page_size=64, num_pages=70, seed=5)
+    pd = device_pool(w)
+    for S in (1, 7):
+        a = _gpu_mtp(w, pd, w.q[:, None], S)
+        b = gpu_decode(w, pd, S)
+        assert np.array_equal(a[0][:, 0], b[0]) and np.array_equal(a[1][:, 0], b[1])
+
+
+def test_mtp_full_size_long_context_sampled():
+    """Four verify tokens per request over the long-context batch, at its bench split count."""
+    w = workloads.NAMED["long_context"]()
+    S = workloads.BENCH_SPLITS["long_context"]
+    T = 4
+    q = workloads.bf16_bits(np.random.default_rng(7).standard_normal((w.batch, T, w.heads, 576)).astype(np.float32))
+    req = [0, w.batch - 1]
+    say(f"case mtp long_context: q_len={T} splits={S} oracle requests={req}")
+    pd = device_pool(w)
+    out, lse = _gpu_mtp(w, pd, q, S)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ph = w.poisoned_pool()
+    idx = np.unique(np.searchsorted(w.slots, np.concatenate([_request_slots(w, b) for b in req])))
+    ph.reshape(-1, w.row_bytes)[w.slots[idx]] = oracle.pack_rows(w.latent[idx], w.k_pe[idx], w.fmt)
+    ref_o, ref_l = oracle.decode_mtp(q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=req)
+    _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp long_context S={S}", requests=req)
 
 
 # ------------------------------------------------------------------------- NoPE-512
