@@ -38,6 +38,9 @@ def _parse():
     ap.add_argument("--workload", default="long_context")
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per request: > 1 times a speculative-decoding verify step "
+                         "(mla_decode_mtp_*), which reads the cache once per request")
     ap.add_argument("--nope", action="store_true",
                     help="decode the workload as a NoPE-512 layer: 512-wide queries, rows written with a zero "
                          "rope part, which the NoPE kernels never read")
@@ -63,7 +66,7 @@ def _copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
-def _cpu_baseline(w, requests, nope=False, min_seconds=10.0):
+def _cpu_baseline(w, requests, nope=False, q_mtp=None, min_seconds=10.0):
     """Time the fp64 oracle on a bounded sample of the same workload, on the host cores."""
     import oracle
     try:
@@ -74,8 +77,8 @@ def _cpu_baseline(w, requests, nope=False, min_seconds=10.0):
     pool = w.poisoned_pool()
     idx = np.concatenate([np.searchsorted(w.slots, _request_slots(w, b)) for b in requests])
     oracle.cache_write(pool, w.latent[idx], None if nope else w.k_pe[idx], w.slots[idx], w.fmt)
-    q = np.ascontiguousarray(w.q[:, :, :512]) if nope else w.q
-    run = oracle.decode_nope if nope else oracle.decode
+    q = np.ascontiguousarray(w.q[:, :, :512]) if nope else (w.q if q_mtp is None else q_mtp)
+    run = oracle.decode_nope if nope else (oracle.decode if q_mtp is None else oracle.decode_mtp)
     # Repeat the sample until about 10 s of host time has been spent.
     reps, t = 0, time.perf_counter()
     while True:
@@ -91,7 +94,7 @@ def _cpu_baseline(w, requests, nope=False, min_seconds=10.0):
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 NumPy oracle ({'decode_nope' if nope else 'decode'}) decoding requests {list(requests)} of the {w.name} batch "
+        "sample": f"fp64 NumPy oracle ({run.__name__}) decoding requests {list(requests)} of the {w.name} batch "
                   f"({tokens} context tokens x {w.heads} heads), {reps} passes in {dt:.1f} s; "
                   f"{len(requests) / per:.1f} decode tokens/s; BLAS threads {threads}, "
                   f"host cpu_count {os.cpu_count()}",
@@ -158,21 +161,39 @@ def main():
         pool = torch.full((w.num_pages, w.page_size, 576), 0x7FC0, dtype=torch.int16, device=dev).view(torch.bfloat16)
     else:
         pool = torch.full((w.num_pages, w.page_size, 656), 0xFF, dtype=torch.uint8, device=dev)
-    nope = args.nope
+    nope, T = args.nope, args.q_len
+    if nope and T != 1:
+        raise SystemExit("--nope and --q-len > 1 are not combined by this benchmark")
     mla.mla_cache_write(bf16(w.latent), None if nope else bf16(w.k_pe), torch.from_numpy(w.slots).to(dev), pool, fmt)
-    q = bf16(w.q[:, :, :512]) if nope else bf16(w.q)
     bt = torch.from_numpy(w.block_table).to(dev)
     lens = torch.from_numpy(w.seq_lens).to(dev)
-    new_lat, new_pe = bf16(w.new_latent), None if nope else bf16(w.new_k_pe)
-    new_slots = torch.from_numpy(w.new_slots).to(dev)
-    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device=dev)
-    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(1, mla.mla_decode_workspace_size(w.batch, w.heads, S)), dtype=torch.uint8, device=dev)
-    if nope:
+    q_mtp = None
+    if T > 1:
+        q_mtp, ns, nl, npe = workloads.verify_step(w, T)
+        q = bf16(q_mtp)
+        new_lat, new_pe, new_slots = bf16(nl), bf16(npe), torch.from_numpy(ns).to(dev)
+    else:
+        q = bf16(w.q[:, :, :512]) if nope else bf16(w.q)
+        new_lat, new_pe = bf16(w.new_latent), None if nope else bf16(w.new_k_pe)
+        new_slots = torch.from_numpy(w.new_slots).to(dev)
+    rows = T * w.heads  # query rows per request
+    out = torch.empty((w.batch, rows, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, rows), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, mla.mla_decode_workspace_size(w.batch, rows, S)), dtype=torch.uint8, device=dev)
+    if T > 1:
+        mtp = mla.mla_decode_mtp_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_fp8_656
+        out4, lse3 = out.view(w.batch, T, w.heads, 512), lse.view(w.batch, T, w.heads)
+
+        def decode(q, pool, bt, lens, scale, num_splits, out=None, lse=None, workspace=None, partials_only=False):
+            return mtp(q, pool, bt, lens, scale, num_splits=num_splits, workspace=workspace,
+                       partials_only=partials_only, out=None if out is None else out4,
+                       lse=None if lse is None else lse3)
+    elif nope:
         decode = mla.mla_decode_nope_bf16 if w.fmt == "bf16" else mla.mla_decode_nope_fp8_656
     else:
         decode = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
-    kernel = f"decode_kernel<{'Bf16' if w.fmt == 'bf16' else 'Fp8'}Rows<{0 if nope else 64}>>"
+    groups = 1 if rows <= 16 else (2 if rows <= 32 else 4)
+    kernel = f"decode_kernel<{'Bf16' if w.fmt == 'bf16' else 'Fp8'}Rows<{0 if nope else 64}>, {groups}>"
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -232,9 +253,12 @@ def main():
     t_write = np.mean([e[0].elapsed_time(e[1]) for e in ev])
     t_decode = np.mean([e[1].elapsed_time(e[2]) for e in ev])
     t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev])
-    live = (w.seq_lens > 0)
+    # rows that see at least one token (query i of a verify step sees L - q_len + 1 + i)
+    vis = (w.seq_lens[:, None] - T + 1 + np.arange(T)[None, :]) > 0
+    live = np.repeat(vis, w.heads, axis=1)
     o, l = out.cpu().numpy(), lse.cpu().numpy()
     assert np.isfinite(o[live]).all() and np.isfinite(l[live]).all(), "non-finite decode output"
+    assert np.isneginf(l[~live]).all() and (o[~live] == 0).all(), "a row that sees no token is not (0, -inf)"
 
     # bytes the decode must read: whole rows, or rows without their rope part (NoPE)
     cache_bytes = w.tokens * (w.row_bytes - 128) if nope else w.cache_bytes_read()
@@ -254,11 +278,11 @@ def main():
         "dtype": w.fmt,
         "data": "synthetic",
         "hbm_fraction": round(gbs / HBM_PEAK_GBS, 4),
-        "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "decode_tokens_per_s": round(w.batch * T / (ms_step * 1e-3), 1),
         "config": {
             "workload": w.name, "batch": w.batch, "heads": w.heads, "context_tokens": w.tokens,
             "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
-            "layer": "nope-512" if nope else "rope-576",
+            "layer": "nope-512" if nope else "rope-576", "query_tokens_per_request": T,
             "cache_row_bytes": w.row_bytes, "row_bytes_read": w.row_bytes - (128 if nope else 0),
             "cache_bytes_per_step": cache_bytes,
         },
@@ -272,11 +296,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None if nope else _profiled_traffic(w.name),
+            "traffic": None if (nope or T > 1) else _profiled_traffic(w.name),
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = _cpu_baseline(w, list(range(min(w.batch, 4))), nope)
+        result["cpu_baseline"] = _cpu_baseline(w, list(range(min(w.batch, 4))), nope, q_mtp)
     print(json.dumps(result), flush=True)
 
 

@@ -198,7 +198,7 @@ def mla_decode_nope_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, n
 
 
 def _decode_mtp(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
-                softmax_scale, num_splits, out, lse, workspace):
+                softmax_scale, num_splits, out, lse, workspace, partials_only=False):
     lib = library()
     _need(q, "q", torch.bfloat16, 4)
     dev = q.device
@@ -212,12 +212,16 @@ def _decode_mtp(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_ca
         raise ValueError(f"q rows must have {ROW} values, got {D}")
     if block_table.shape[0] != B or seq_lens.shape[0] != B:
         raise ValueError("block_table and seq_lens must have one row per request")
-    if out is None:
-        out = torch.empty((B, T, H, LATENT), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.float32, 4, dev)
-    _need(lse, "lse", torch.float32, 3, dev)
+    if partials_only:
+        if num_splits < 2 or out is not None or lse is not None:
+            raise ValueError("partials_only needs num_splits > 1 and no out/lse")
+    else:
+        if out is None:
+            out = torch.empty((B, T, H, LATENT), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, 4, dev)
+        _need(lse, "lse", torch.float32, 3, dev)
     ws_bytes = 0
     if num_splits > 1:
         need = mla_decode_workspace_size(B, T * H, num_splits)
@@ -227,25 +231,30 @@ def _decode_mtp(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_ca
     status = getattr(lib, fn)(
         q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1],
         seq_lens.data_ptr(), B, T, H, kv_cache.shape[1], float(softmax_scale), int(num_splits),
-        out.data_ptr(), lse.data_ptr(), _ptr(workspace), ws_bytes, _stream(dev))
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev))
     _check(fn, status)
+    if partials_only:  # [S, B, q_len * H, 512] / [S, B, q_len * H]: query rows act as heads
+        n = num_splits * B * T * H
+        flat = workspace.view(torch.uint8)[: n * (LATENT + 1) * 4].view(torch.float32)
+        return flat[: n * LATENT].view(num_splits, B, T * H, LATENT), flat[n * LATENT:].view(num_splits, B, T * H)
     return out, lse
 
 
 def mla_decode_mtp_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                        workspace=None):
+                        workspace=None, partials_only=False):
     """Verify-step decode over a bf16 cache: q [B, q_len, H, 576] -> (out [B, q_len, H, 512], lse [B, q_len, H]).
 
-    seq_lens count the q_len new tokens; query i sees tokens 0 .. L - q_len + i."""
+    seq_lens count the q_len new tokens; query i sees tokens 0 .. L - q_len + i.
+    partials_only=True (num_splits > 1) returns the partials [S, B, q_len * H, ...] instead."""
     return _decode_mtp("mla_decode_mtp_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
-                       softmax_scale, num_splits, out, lse, workspace)
+                       softmax_scale, num_splits, out, lse, workspace, partials_only)
 
 
 def mla_decode_mtp_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                           workspace=None):
+                           workspace=None, partials_only=False):
     """Verify-step decode over an fp8 cache uint8 [num_pages, page_size, 656]."""
     return _decode_mtp("mla_decode_mtp_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
-                       softmax_scale, num_splits, out, lse, workspace)
+                       softmax_scale, num_splits, out, lse, workspace, partials_only)
 
 
 def mla_merge_lse(part_out, part_lse, out=None, lse=None):

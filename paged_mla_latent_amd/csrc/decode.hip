@@ -433,6 +433,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
     // Step i: every wave waits for its own tile 4i + wave (and the page ids of its next
     // one), the barrier makes all four tiles of the step visible and tells every wave that
     // the others are done with step i-1, whose buffers the next tiles then overwrite.
+    // (A second barrier that lets the next loads start before this wait was measured
+    // slower: the step is bound by its compute and the barrier, not by load depth.)
     const int nsteps = (ntiles + kWaves - 1) / kWaves;
     const int u0 = G * (wave / G);  // first tile of a step this wave scores
 #pragma unroll 1

@@ -234,6 +234,26 @@ def make_workload(
     )
 
 
+def verify_step(w: Workload, q_len: int, seed: int = 1):
+    """Inputs of a speculative-decoding verify step over workload w.
+
+    Returns (q, new_slots, new_latent, new_k_pe): q uint16 bf16 bits [B, q_len, H, 576],
+    N(0, 1) rounded to bf16; the slots of the last q_len positions of every request
+    (ascending, unique) with the workload's own rows for them, which the step writes into
+    the cache before attending.  Query i of request b sits at position L_b - q_len + i.
+    """
+    rng = np.random.default_rng(seed)
+    q = bf16_bits(rng.standard_normal((w.batch, q_len, w.heads, ROW), dtype=np.float32))
+    new = []
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        for t in range(max(0, L - q_len), L):
+            new.append(int(w.block_table[b, t // w.page_size]) * w.page_size + t % w.page_size)
+    new_slots = np.unique(np.asarray(new, dtype=np.int64))
+    idx = np.searchsorted(w.slots, new_slots)
+    return q, new_slots, w.latent[idx].copy(), w.k_pe[idx].copy()
+
+
 def _slots_of_pages(used_pages: np.ndarray, fill: np.ndarray, ps: int) -> np.ndarray:
     """Slots p*ps + [0, fill[p]) for every page p in used_pages, ascending."""
     if used_pages.size == 0:
