@@ -31,6 +31,12 @@ What is computed (per request b and head h), following the pages:
   instead of once per draft token).  Reading (the pages do not spell out the mask): the
   usual causal one, seq_lens counting the q_len new tokens, so query i of a request with
   L tokens attends to tokens 0 .. L - q_len + i.
+* Prefill reads the cached context with 64-bit indices (sabi-mla-vllm, "B300 fix (0.2.0)":
+  prefill gathers the cache with int64 indices) into a 576-wide workspace, upconverting
+  fp8 rows to bf16 on the way (vLLM PR #55543, commit on the context-gather path: the
+  gather reads 656-byte rows into a workspace 576 rows wide).  Reading (the pages give no
+  formula): a bf16 row is copied; an fp8 latent value becomes bf16(fl32(code * scale)),
+  the product rounded to float32 and then to bf16, both to nearest even; rope copied.
 * NoPE-512 layers (no rotary part) keep the same row and write zeros into its rope part;
   their query has 512 values, padded with zeros to 576, so the rope part adds nothing to
   any score (vLLM PR #55543, description of the zero-rope approach).  decode_nope is the
@@ -40,7 +46,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import bf16_to_f64, e4m3_decode, quantize_block128
+from .numerics import bf16_to_f64, e4m3_decode, f32_to_bf16_bits, quantize_block128
 
 LATENT = 512
 ROPE = 64
@@ -230,6 +236,38 @@ def merge(part_out: np.ndarray, part_lse: np.ndarray) -> tuple[np.ndarray, np.nd
     out = np.where(empty[..., None], 0.0, out)
     lse = np.where(empty, -np.inf, Ms + np.log(Ws))
     return out, lse
+
+
+# --------------------------------------------------------------- context gather
+def upconvert_rows(row_bytes: np.ndarray, fmt: str) -> np.ndarray:
+    """bf16 bits [n, 576] of raw rows [n, row_bytes]: bf16 rows as stored; fp8 latent values
+    bf16(fl32(code * scale)), rope values as stored."""
+    row_bytes = np.ascontiguousarray(row_bytes, dtype=np.uint8)
+    n = row_bytes.shape[0]
+    if fmt == "bf16":
+        return row_bytes.view("<u2").reshape(n, ROW).copy()
+    codes = e4m3_decode(row_bytes[:, FP8_CODES]).astype(np.float32).reshape(n, 4, 128)  # exact
+    scales = np.ascontiguousarray(row_bytes[:, FP8_SCALES]).view("<f4").reshape(n, 4, 1)
+    prod = (codes * scales).astype(np.float32)  # IEEE float32 multiply
+    out = np.empty((n, ROW), dtype=np.uint16)
+    out[:, :LATENT] = f32_to_bf16_bits(prod.reshape(n, LATENT))
+    out[:, LATENT:] = np.ascontiguousarray(row_bytes[:, FP8_ROPE]).view("<u2").reshape(n, ROPE)
+    return out
+
+
+def gather_context(pool, block_table, cu_rows, seq_starts, page_size: int, fmt: str) -> np.ndarray:
+    """bf16 bits [cu_rows[-1], 576]: row cu_rows[b] + j is token seq_starts[b] + j of request b
+    (seq_starts None: 0), upconverted as in upconvert_rows."""
+    rows = _pool_rows(pool, fmt)
+    cu_rows = np.asarray(cu_rows, dtype=np.int64)
+    B = cu_rows.size - 1
+    slots = []
+    for b in range(B):
+        start = 0 if seq_starts is None else int(seq_starts[b])
+        for j in range(int(cu_rows[b + 1] - cu_rows[b])):
+            slots.append(slot_of(block_table, b, start + j, page_size))
+    slots = np.asarray(slots, dtype=np.int64)
+    return upconvert_rows(rows[slots], fmt)
 
 
 # ------------------------------------------------------------------------ cache write

@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this module.
 
-* bf16: the upper 16 bits of an IEEE-754 binary32; widening to fp64 is exact.
+* bf16: the upper 16 bits of an IEEE-754 binary32; widening to fp64 is exact;
+  narrowing float32 to bf16 rounds to nearest, ties to even.
 * e4m3fn (OCP 8-bit floating point, E4M3 variant): 1 sign bit, 4 exponent bits
   with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals
   m/8 * 2^-6; codes 0x7F and 0xFF are NaN; there is no infinity; the largest
@@ -34,6 +35,20 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return u.view(np.float32)
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """bf16 bits of float32 values: round to nearest, ties to even; NaN stays NaN.
+
+    Rounding by integer arithmetic on the binary32 pattern: adding 0x7FFF plus the
+    lowest kept bit, then dropping the low 16 bits, rounds half-way cases to the even
+    neighbour and carries into the exponent when the mantissa overflows (up to inf).
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    r = np.where(nan, (u >> np.uint64(16)) | np.uint64(0x0040), r)
+    return r.astype(np.uint16)
 
 
 def _e4m3_value(code: int) -> float:

@@ -24,6 +24,11 @@ mla.decode_nope          pure-Python brute force over the 512 latent values; equ
 mla.pack_rows(k_pe=None) rope bytes zero, latent bytes as with any k_pe
 mla.merge/split_ranges   split vs unsplit for S in {1, 2, 7, 64}; all-empty partials;
                          a NaN partial is not an empty one; partition coverage
+numerics.f32_to_bf16_bits  torch's float32 -> bfloat16 cast: specials, exact ties, 10^6 random
+mla.gather_context       hand-written gather loop (bf16 rows bit for bit); fp8 rows built
+                         exactly representable upconvert to the bf16 gather; general fp8
+                         rows land on a bf16 neighbour of the exact product within the
+                         double-rounding bound; rope values copied
 workloads.bf16_bits      torch's float32 -> bfloat16 cast (round to nearest even)
 """
 import json
@@ -600,6 +605,73 @@ def test_merge_two_single_token_partials_is_a_two_token_softmax():
 
 
 # ------------------------------------------------------------------------ generators
+def test_oracle_f32_to_bf16_matches_torch():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(1_000_000).astype(np.float32) * np.float32(2.0) ** rng.integers(-140, 120, 1_000_000)
+    ties = (rng.integers(0, 1 << 16, 4096, dtype=np.uint32) << 16 | 0x8000).view(np.float32)  # exact half-way
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, -3.3895314e38, 3.4028235e38, 1e-45, -1e-45,
+                        1.1754942e-38, 2.0 ** -133], np.float32)
+    for v in (x, ties, special):
+        ours = oracle.f32_to_bf16_bits(v)
+        ref = torch.from_numpy(v.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(v)  # NaN stays NaN; the payload is not specified
+        assert np.isnan(oracle.bf16_to_f32(ours[nan])).all()
+        assert np.array_equal(ours[~nan], ref[~nan])
+    nan = oracle.f32_to_bf16_bits(np.array([np.nan, -np.nan], np.float32))
+    assert np.isnan(oracle.bf16_to_f32(nan)).all()
+
+
+# ------------------------------------------------------------------- context gather
+def test_gather_bf16_rows_by_hand():
+    rng = np.random.default_rng(50)
+    w = workloads.make_workload("g", seq_lens=[13, 0, 7], heads=1, page_size=4, num_pages=8, rng=rng)
+    pool = w.poisoned_pool()
+    oracle.cache_write(pool, w.latent, w.k_pe, w.slots, "bf16")
+    starts = np.array([3, 0, 5])
+    counts = np.array([9, 0, 2])
+    cu = np.concatenate([[0], np.cumsum(counts)])
+    got = oracle.gather_context(pool, w.block_table, cu, starts, 4, "bf16")
+    flat = pool.reshape(-1, 1152)
+    want = []
+    for b in range(3):
+        for j in range(counts[b]):
+            t = starts[b] + j
+            want.append(flat[int(w.block_table[b][t // 4]) * 4 + t % 4].view("<u2"))
+    assert np.array_equal(got, np.array(want))
+
+
+def test_fp8_upconvert_exact_on_representable_rows():
+    rng = np.random.default_rng(51)
+    w = workloads.make_workload("g8", seq_lens=[40, 25], heads=1, page_size=16, num_pages=6, seed=51)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    codes = rng.choice(finite, size=w.latent.shape)
+    codes[:, ::128] = 0x7E
+    k = rng.integers(-8, 2, size=(w.latent.shape[0], 4))
+    vals = oracle.e4m3_decode(codes).reshape(-1, 4, 128) * (2.0 ** k)[..., None]
+    lat = workloads.bf16_bits(vals.reshape(-1, 512).astype(np.float32))
+    p16, p8 = w.poisoned_pool(), np.full((6, 16, 656), 0xFF, np.uint8)
+    oracle.cache_write(p16, lat, w.k_pe, w.slots, "bf16")
+    oracle.cache_write(p8, lat, w.k_pe, w.slots, "fp8")
+    cu = np.concatenate([[0], np.cumsum(w.seq_lens)])
+    a = oracle.gather_context(p16, w.block_table, cu, None, 16, "bf16")
+    b = oracle.gather_context(p8, w.block_table, cu, None, 16, "fp8")
+    assert np.array_equal(a, b)
+
+
+def test_fp8_upconvert_rounds_the_exact_product():
+    w = workloads.make_workload("g9", seq_lens=[300], heads=1, page_size=16, num_pages=20, seed=52,
+                                row_scale_log10=(-3.0, 3.0))
+    p8 = np.full((20, 16, 656), 0xFF, np.uint8)
+    oracle.cache_write(p8, w.latent, w.k_pe, w.slots, "fp8")
+    rows = p8.reshape(-1, 656)[w.slots]
+    got = oracle.upconvert_rows(rows, "fp8")
+    exact = oracle.rows_from_bytes(rows, "fp8")[:, :512]  # fp64, exact code * scale
+    v = oracle.bf16_to_f64(got[:, :512])
+    ulp16 = np.where(exact == 0, 0.0, 2.0 ** (np.floor(np.log2(np.abs(np.where(exact == 0, 1, exact)))) - 7))
+    assert (np.abs(v - exact) <= 0.5 * ulp16 * (1 + 2.0 ** -16) + 1e-300).all()
+    assert np.array_equal(got[:, 512:], w.k_pe)  # rope copied bit for bit
+
+
 def test_bf16_rounding_matches_torch():
     rng = np.random.default_rng(13)
     x = (rng.standard_normal(200_000) * np.exp(rng.uniform(-30, 30, 200_000))).astype(np.float32)
