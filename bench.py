@@ -47,6 +47,9 @@ def _parse():
     ap.add_argument("--eager", action="store_true",
                     help="time only eager launches (default: also replay the step from a captured HIP graph, "
                          "which gives the reported value)")
+    ap.add_argument("--op", choices=("decode", "gather"), default="decode",
+                    help="gather: time mla_gather_context over the workload's whole context instead "
+                         "(prefill-side context gather, fp8 rows upconverted to bf16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times (counter calibration)")
     return ap.parse_args()
@@ -134,6 +137,70 @@ def _request_slots(w, b):
     return w.block_table[b].astype(np.int64)[t // w.page_size] * w.page_size + t % w.page_size
 
 
+def _bench_gather(args):
+    """Context gather of every token of the workload into bf16 [tokens, 576] rows."""
+    import torch
+    import oracle
+    import paged_mla_latent_amd as mla
+    import workloads
+
+    w = workloads.NAMED[args.workload]()
+    dev = torch.device("cuda:0")
+    fmt = mla.MLA_CACHE_BF16_576 if w.fmt == "bf16" else mla.MLA_CACHE_FP8_656
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if w.fmt == "bf16":
+        pool = torch.full((w.num_pages, w.page_size, 576), 0x7FC0, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    else:
+        pool = torch.full((w.num_pages, w.page_size, 656), 0xFF, dtype=torch.uint8, device=dev)
+    mla.mla_cache_write(bf16(w.latent), bf16(w.k_pe), torch.from_numpy(w.slots).to(dev), pool, fmt)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    cu_np = np.concatenate([[0], np.cumsum(w.seq_lens.astype(np.int64))])
+    cu = torch.from_numpy(cu_np).to(dev)
+    rows = int(cu_np[-1])
+    out = torch.empty((rows, 576), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        mla.mla_gather_context(pool, fmt, bt, cu, rows, out=out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        mla.mla_gather_context(pool, fmt, bt, cu, rows, out=out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # spot check against the oracle: the first and last request's first rows
+    check = [0, w.batch - 1]
+    for b in check:
+        n = min(64, int(w.seq_lens[b]))
+        if n == 0:
+            continue
+        got = out[cu_np[b]: cu_np[b] + n].view(torch.int16).cpu().numpy().view(np.uint16)
+        t = np.arange(n)
+        slots = w.block_table[b].astype(np.int64)[t // w.page_size] * w.page_size + t % w.page_size
+        raw = pool.view(torch.uint8).view(-1, w.row_bytes)[torch.from_numpy(slots).to(dev)].cpu().numpy()
+        assert np.array_equal(got, oracle.upconvert_rows(raw, w.fmt)), f"gather of request {b} differs"
+    moved = rows * (w.row_bytes + 1152)
+    gbs = moved / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "context gather GB/s (cache rows read + bf16 rows written)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.fmt, "data": "synthetic",
+        "config": {"workload": w.name, "op": "gather", "rows": rows, "cache_row_bytes": w.row_bytes,
+                   "bytes_per_step": moved},
+        "kernel_ms": {"gather": round(ms, 4)},
+        "roofline": {"kernel": f"gather_kernel<{'true' if w.fmt == 'fp8' else 'false'}>", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }), flush=True)
+
+
 def main():
     args = _parse()
     if args.copy_calibration:
@@ -143,6 +210,10 @@ def main():
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
               f"(the multi-GPU split of this path is described in DESIGN.md but not built).", file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "gather":
+        _bench_gather(args)
+        return
 
     import torch
     import paged_mla_latent_amd as mla

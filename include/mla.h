@@ -200,6 +200,26 @@ MLA_API int mla_cache_write(const void* latent, const void* k_pe, const int64_t*
                     int32_t num_tokens, void* kv_cache, int32_t cache_format,
                     int64_t num_slots, void* stream);
 
+/* Context gather for prefill (the int64 cache gather of sabi-mla-vllm, "B300 fix (0.2.0)",
+ * and the fp8 context-gather-and-upconvert path of vLLM pull request 55543, which reads
+ * 656-byte rows into a workspace 576 values wide).  Writes bf16 [total_rows][576]:
+ *   out row cu_rows[b] + j = token seq_starts[b] + j of request b, j < cu_rows[b+1] - cu_rows[b]
+ * read through the block table with 64-bit slot and byte offsets.  MLA_CACHE_BF16_576: the
+ * row as stored.  MLA_CACHE_FP8_656: each latent value is bf16(fl32(code * scale)), the
+ * float32 product rounded to nearest even and then to bf16, nearest even (this library's
+ * reading; the pages name the operation, not its rounding); rope values as stored.
+ * cu_rows    int64 [batch + 1], cu_rows[0] = 0, non-decreasing, cu_rows[batch] = total_rows.
+ * seq_starts int32 [batch], first context position to gather per request, or NULL for 0.
+ * total_rows passed by the caller (the library never reads device memory on the host).
+ * Preconditions (not checkable without reading device memory): the cu_rows layout above;
+ * seq_starts[b] + rows of b <= block_table_stride * page_size; the block-table entries
+ * those tokens use lie in [0, num_pages).  total_rows == 0 launches nothing. */
+MLA_API int mla_gather_context(const void* kv_cache, int32_t cache_format, int64_t num_pages,
+                               int32_t page_size, const int32_t* block_table,
+                               int64_t block_table_stride, const int64_t* cu_rows,
+                               const int32_t* seq_starts, int32_t batch, int64_t total_rows,
+                               void* out, void* stream);
+
 MLA_API const char* mla_status_string(int status);
 /* Message describing the last failed call on this thread ("" if none). */
 MLA_API const char* mla_last_error_message(void);

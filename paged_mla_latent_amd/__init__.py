@@ -12,6 +12,7 @@ Entry points (same names as the C ABI in include/mla.h):
     mla_decode_mtp_bf16 / mla_decode_mtp_fp8_656(q [B, q_len, H, 576], ...)   verify step
     mla_merge_lse(part_out, part_lse, out=None, lse=None)
     mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format)   k_pe None: zero rope
+    mla_gather_context(kv_cache, cache_format, block_table, cu_rows, total_rows, seq_starts=None)
     mla_decode_workspace_size(batch, num_heads, num_splits)
 
 Tensors: q bf16 [B, H, 576]; kv_cache bf16 [num_pages, page_size, 576] or uint8
@@ -40,7 +41,7 @@ MAX_QUERY_ROWS = 64
 EXPORTED = (
     "mla_decode_workspace_size", "mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16",
     "mla_decode_nope_fp8_656", "mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656", "mla_merge_lse",
-    "mla_cache_write", "mla_status_string", "mla_last_error_message", "mla_abi_version",
+    "mla_cache_write", "mla_gather_context", "mla_status_string", "mla_last_error_message", "mla_abi_version",
 )
 
 
@@ -79,6 +80,8 @@ def library() -> ctypes.CDLL:
     lib.mla_merge_lse.restype = c_int
     lib.mla_cache_write.argtypes = [vp, vp, vp, c_i32, vp, c_i32, c_i64, vp]
     lib.mla_cache_write.restype = c_int
+    lib.mla_gather_context.argtypes = [vp, c_i32, c_i64, c_i32, vp, c_i64, vp, vp, c_i32, c_i64, vp, vp]
+    lib.mla_gather_context.restype = c_int
     lib.mla_status_string.argtypes = [c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error_message.argtypes = []
@@ -303,3 +306,39 @@ def mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format):
     num_slots = kv_cache.shape[0] * kv_cache.shape[1]
     _check("mla_cache_write", lib.mla_cache_write(latent.data_ptr(), _ptr(k_pe), slot_mapping.data_ptr(), T,
                                                   kv_cache.data_ptr(), int(cache_format), num_slots, _stream(dev)))
+
+
+def mla_gather_context(kv_cache, cache_format, block_table, cu_rows, total_rows, seq_starts=None, out=None):
+    """Context rows of every request as bf16 [total_rows, 576] (fp8 rows upconverted).
+
+    cu_rows int64 [B + 1] on the device (request b fills rows cu_rows[b] .. cu_rows[b+1]),
+    total_rows = cu_rows[B] as a host int; seq_starts int32 [B] (None: gather from token 0)."""
+    lib = library()
+    if cache_format == MLA_CACHE_BF16_576:
+        _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    elif cache_format == MLA_CACHE_FP8_656:
+        _need(kv_cache, "kv_cache", torch.uint8, 3)
+    else:
+        raise ValueError(f"unknown cache_format {cache_format}")
+    dev = kv_cache.device
+    if kv_cache.shape[2] != (ROW if cache_format == MLA_CACHE_BF16_576 else 656):
+        raise ValueError("kv_cache rows have the wrong width for cache_format")
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(cu_rows, "cu_rows", torch.int64, 1, dev)
+    B = block_table.shape[0]
+    if cu_rows.shape[0] != B + 1:
+        raise ValueError("cu_rows must have batch + 1 entries")
+    if seq_starts is not None:
+        _need(seq_starts, "seq_starts", torch.int32, 1, dev)
+        if seq_starts.shape[0] != B:
+            raise ValueError("seq_starts must have one entry per request")
+    if out is None:
+        out = torch.empty((int(total_rows), ROW), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, 2, dev)
+    if out.shape[0] < total_rows or out.shape[1] != ROW:
+        raise ValueError("out must be [total_rows, 576]")
+    _check("mla_gather_context", lib.mla_gather_context(
+        kv_cache.data_ptr(), int(cache_format), kv_cache.shape[0], kv_cache.shape[1], block_table.data_ptr(),
+        block_table.shape[1], cu_rows.data_ptr(), _ptr(seq_starts), B, int(total_rows), out.data_ptr(),
+        _stream(dev)))
+    return out

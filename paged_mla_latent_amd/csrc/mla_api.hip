@@ -241,6 +241,36 @@ int mla_cache_write(const void* latent, const void* k_pe, const int64_t* slot_ma
                     fn);
 }
 
+int mla_gather_context(const void* kv_cache, int32_t cache_format, int64_t num_pages, int32_t page_size,
+                       const int32_t* block_table, int64_t block_table_stride, const int64_t* cu_rows,
+                       const int32_t* seq_starts, int32_t batch, int64_t total_rows, void* out, void* stream) {
+  const char* fn = "mla_gather_context";
+  if (cache_format != MLA_CACHE_BF16_576 && cache_format != MLA_CACHE_FP8_656)
+    return fail(MLA_ERR_SHAPE, "%s: cache_format=%d unknown", fn, cache_format);
+  if (total_rows < 0) return fail(MLA_ERR_SHAPE, "%s: total_rows=%lld is negative", fn, (long long)total_rows);
+  if (total_rows > ((int64_t)1 << 36))
+    return fail(MLA_ERR_SHAPE, "%s: total_rows=%lld exceeds 2^36", fn, (long long)total_rows);
+  if (batch < 1) return fail(MLA_ERR_SHAPE, "%s: batch=%d must be >= 1", fn, batch);
+  if (num_pages < 1) return fail(MLA_ERR_SHAPE, "%s: num_pages=%lld must be >= 1", fn, (long long)num_pages);
+  if (page_size < 1) return fail(MLA_ERR_SHAPE, "%s: page_size=%d must be >= 1", fn, page_size);
+  if (block_table_stride < 1)
+    return fail(MLA_ERR_SHAPE, "%s: block_table_stride=%lld must be >= 1", fn, (long long)block_table_stride);
+  if (total_rows == 0) return MLA_OK;
+  if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
+  if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
+  if (!cu_rows) return fail(MLA_ERR_NULL, "%s: cu_rows is NULL", fn);
+  if (!out) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
+  if (!aligned16(kv_cache) || !aligned16(block_table) || !aligned16(cu_rows) || !aligned16(seq_starts) ||
+      !aligned16(out))
+    return fail(MLA_ERR_ALIGN, "%s: every tensor pointer must be 16-byte aligned", fn);
+  int rc = check_device();
+  if (rc != MLA_OK) return rc;
+  return hip_status(mla::launch_gather(static_cast<const uint8_t*>(kv_cache), cache_format == MLA_CACHE_FP8_656,
+                                       block_table, block_table_stride, cu_rows, seq_starts, batch, page_size,
+                                       total_rows, static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 const char* mla_status_string(int status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";

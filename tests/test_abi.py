@@ -169,6 +169,25 @@ def test_cache_write_validation(lib):
     assert f(None, None, None, 0, None, 0, 10, None) == 0  # nothing to write: no device needed
 
 
+def test_gather_validation(lib):
+    f = lib.mla_gather_context
+    #        kv fmt pages ps  bt stride cu  starts batch total out
+    ok = dict(kv=P, fmt=0, pages=10, ps=16, bt=P, stride=4, cu=P, st=None, batch=2, total=100, out=P)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["kv"], a["fmt"], a["pages"], a["ps"], a["bt"], a["stride"], a["cu"], a["st"], a["batch"],
+                 a["total"], a["out"], None), lib.mla_last_error_message().decode()
+    for kw, rc, word in [(dict(fmt=5), 2, "cache_format"), (dict(total=-1), 2, "total_rows"),
+                         (dict(total=1 << 40), 2, "total_rows"), (dict(batch=0), 2, "batch"),
+                         (dict(pages=0), 2, "num_pages"), (dict(ps=0), 2, "page_size"), (dict(stride=0), 2, "stride"),
+                         (dict(kv=None), 1, "kv_cache"), (dict(cu=None), 1, "cu_rows"), (dict(out=None), 1, "out"),
+                         (dict(bt=None), 1, "block_table"), (dict(st=MIS), 3, "aligned"), (dict(cu=MIS), 3, "aligned")]:
+        got, msg = call(**kw)
+        assert got == rc and word in msg and "mla_gather_context" in msg, (kw, got, msg)
+    assert call(total=0, kv=None, out=None)[0] == 0  # nothing to gather: no device needed
+
+
 def test_error_message_is_thread_local(lib):
     import threading
     _decode(lib, heads=99)

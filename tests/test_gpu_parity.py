@@ -328,6 +328,76 @@ def test_mtp_full_size_long_context_sampled():
     _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp long_context S={S}", requests=req)
 
 
+# ------------------------------------------------------------------- context gather
+def _gpu_gather(w, pool, cu, starts):
+    out = mla.mla_gather_context(pool, FMT_CODE[w.fmt], torch.from_numpy(w.block_table).cuda(),
+                                 torch.from_numpy(np.asarray(cu, np.int64)).cuda(), int(cu[-1]),
+                                 None if starts is None else torch.from_numpy(np.asarray(starts, np.int32)).cuda())
+    torch.cuda.synchronize()
+    return out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("ps", [1, 3, 16, 64])
+def test_gather_parity(fmt, ps):
+    """Random context windows of ragged requests, bit for bit against oracle.gather_context."""
+    lens = [0, 1, 15, 17, 333, 2500, 64]
+    pages = sum(-(-L // ps) for L in lens) + 3
+    w = workloads.make_workload(f"gather_ps{ps}", seq_lens=lens, heads=1, page_size=ps, num_pages=pages, fmt=fmt,
+                                seed=80 + ps)
+    rng = np.random.default_rng(ps)
+    starts = np.array([rng.integers(0, L + 1) for L in lens])
+    counts = np.array([rng.integers(0, L - s + 1) for L, s in zip(lens, starts)])
+    counts[-1] = lens[-1] - starts[-1]  # one window that runs to the end of its context
+    cu = np.concatenate([[0], np.cumsum(counts)])
+    say(f"case gather fmt={fmt} ps={ps} rows={cu[-1]}")
+    pd, ph = device_pool(w), host_pool(w)
+    got = _gpu_gather(w, pd, cu, starts)
+    want = oracle.gather_context(ph, w.block_table, cu, starts, ps, fmt)
+    assert got.shape == want.shape and np.array_equal(got, want)
+    whole = np.concatenate([[0], np.cumsum(lens)])  # every token, seq_starts NULL
+    assert np.array_equal(_gpu_gather(w, pd, whole, None), oracle.gather_context(ph, w.block_table, whole, None, ps, fmt))
+
+
+@pytest.mark.parametrize("fmt, num_pages", [("bf16", 60000), ("fp8", 110000)])
+def test_gather_beyond_32bit_offsets(fmt, num_pages):
+    """Pages that straddle slot 3,728,270 and pages past 2^32 bytes, gathered whole."""
+    ps = 64
+    top, straddle = num_pages - 1, workloads.WRAP_SLOT // ps
+    layout = [[straddle, top, 5], [top - 1, straddle + 1]]
+    lens = [3 * ps - 9, 2 * ps]
+    w = workloads.make_workload(f"gwrap_{fmt}", seq_lens=lens, heads=1, page_size=ps, num_pages=num_pages, fmt=fmt,
+                                seed=9)
+    bt = np.full_like(w.block_table, -1)
+    for b, pg in enumerate(layout):
+        bt[b, :len(pg)] = pg
+    fill = {}
+    for b, pg in enumerate(layout):
+        for j, p in enumerate(pg):
+            fill[p] = max(fill.get(p, 0), min(ps, lens[b] - j * ps))
+    slots = np.concatenate([p * ps + np.arange(n) for p, n in sorted(fill.items())]).astype(np.int64)
+    rng = np.random.default_rng(10)
+    w.block_table, w.slots = bt, slots
+    w.latent = workloads.bf16_bits(rng.standard_normal((slots.size, 512)).astype(np.float32))
+    w.k_pe = workloads.bf16_bits(rng.standard_normal((slots.size, 64)).astype(np.float32))
+    pd, ph = device_pool(w), host_pool(w)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    assert np.array_equal(_gpu_gather(w, pd, cu, None), oracle.gather_context(ph, bt, cu, None, ps, fmt))
+
+
+def test_gather_full_size_fp8_ragged():
+    """The whole fp8 ragged context (695,528 rows), upconverted; every row against the
+    oracle's upconvert of the same cache bytes read back from the device."""
+    w = workloads.NAMED["fp8_ragged"]()
+    pd = device_pool(w)
+    cu = np.concatenate([[0], np.cumsum(w.seq_lens.astype(np.int64))])
+    say(f"case gather fp8_ragged: rows={cu[-1]}")
+    got = _gpu_gather(w, pd, cu, None)
+    slots = np.concatenate([_request_slots(w, b) for b in range(w.batch)])
+    want = oracle.upconvert_rows(device_rows(pd, slots, w.row_bytes), "fp8")
+    assert np.array_equal(got, want)
+
+
 # ------------------------------------------------------------------------- NoPE-512
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 @pytest.mark.parametrize("ps", [3, 16, 64])
