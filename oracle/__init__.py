@@ -19,13 +19,14 @@ are listed at the top of that test file.
 """
 from .numerics import (E4M3_MAX, E4M3_TABLE, bf16_to_f32, bf16_to_f64, e4m3_decode,
                        e4m3_encode, f32_to_bf16_bits, quantize_block128)
-from .mla import (LATENT, ROPE, ROW, ROW_BYTES, attend, cache_write, decode, decode_mtp, decode_nope,
+from .mla import (LATENT, ROPE, ROW, ROW_BYTES, attend, attend_kv, cache_write, decode, decode_gla2, decode_mtp, decode_nope,
+                  decode_rank,
                   element_offset, element_offset_int32, gather_context, gather_rows, gather_rows_fast,
                   merge, pack_rows, rows_from_bytes, slot_of, split_ranges, upconvert_rows)
 
 __all__ = [
     "E4M3_MAX", "E4M3_TABLE", "bf16_to_f32", "bf16_to_f64", "e4m3_decode", "e4m3_encode", "f32_to_bf16_bits", "gather_context", "upconvert_rows",
     "quantize_block128", "LATENT", "ROPE", "ROW", "ROW_BYTES", "attend", "cache_write",
-    "decode", "decode_mtp", "decode_nope", "element_offset", "element_offset_int32", "gather_rows", "gather_rows_fast",
+    "decode", "decode_mtp", "decode_nope", "attend_kv", "decode_gla2", "decode_rank", "element_offset", "element_offset_int32", "gather_rows", "gather_rows_fast",
     "merge", "pack_rows", "rows_from_bytes", "slot_of", "split_ranges",
 ]

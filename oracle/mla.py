@@ -37,6 +37,12 @@ What is computed (per request b and head h), following the pages:
   gather reads 656-byte rows into a workspace 576 rows wide).  Reading (the pages give no
   formula): a bf16 row is copied; an fp8 latent value becomes bf16(fl32(code * scale)),
   the product rounded to float32 and then to bf16, both to nearest even; rope copied.
+* Other latent geometries (qwen-mla-vllm, "How it works": per-layer latent ranks 256 /
+  768 / 1792 plus a small rotary tail; opening section: GLA-g2 splits the latent into two
+  head groups).  Readings (the pages give no row layout): a rank-D layer caches bf16 rows
+  of D latent values followed by the 64 rope values; GLA-g2 keeps the 576-value / 656-byte
+  row, heads [0, H/2) use latent values [0, 256) and heads [H/2, H) use [256, 512), both
+  groups share the rope, and each head's output is its group's 256 values.
 * NoPE-512 layers (no rotary part) keep the same row and write zeros into its rope part;
   their query has 512 values, padded with zeros to 576, so the rope part adds nothing to
   any score (vLLM PR #55543, description of the zero-rope approach).  decode_nope is the
@@ -177,6 +183,56 @@ def decode_mtp(q_bits, pool, block_table, seq_lens, page_size: int, scale: float
         for i in range(T):
             n = max(0, L - T + 1 + i)
             out[b, i], lse[b, i] = attend(q[b, i], rows[:n], scale)
+    return out, lse
+
+
+def attend_kv(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float):
+    """Attention of q [H, K] over keys [L, K] with values [L, V]: (out [H, V], lse [H])."""
+    H = q.shape[0]
+    if keys.shape[0] == 0:
+        return np.zeros((H, values.shape[1])), np.full(H, -np.inf)
+    s = float(scale) * (q @ keys.T)
+    m = s.max(axis=1, keepdims=True)
+    lse = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
+    return np.exp(s - lse) @ values, lse[:, 0]
+
+
+def decode_gla2(q_bits, pool, block_table, seq_lens, page_size: int, scale: float, fmt: str,
+                requests=None) -> tuple[np.ndarray, np.ndarray]:
+    """GLA-g2 decode on the 576-value row: q_bits [B, H, 320] (group latent 256 ++ rope 64),
+    H even; head h in group g = h // (H/2) scores latent[256g : 256g + 256] ++ rope.
+    Returns out [B, H, 256], lse [B, H]."""
+    q = bf16_to_f64(q_bits)
+    B, H, D = q.shape
+    if D != 256 + ROPE or H % 2:
+        raise ValueError("GLA-g2 queries are [B, H, 320] with H even")
+    out = np.full((B, H, 256), np.nan)
+    lse = np.full((B, H), np.nan)
+    for b in (range(B) if requests is None else requests):
+        rows = gather_rows_fast(pool, block_table, b, int(seq_lens[b]), page_size, fmt)
+        for g in range(2):
+            hs = slice(g * H // 2, (g + 1) * H // 2)
+            keys = np.concatenate([rows[:, 256 * g:256 * g + 256], rows[:, LATENT:]], axis=1)
+            out[b, hs], lse[b, hs] = attend_kv(q[b, hs], keys, rows[:, 256 * g:256 * g + 256], scale)
+    return out, lse
+
+
+def decode_rank(q_bits, pool_bits, block_table, seq_lens, page_size: int, scale: float,
+                requests=None) -> tuple[np.ndarray, np.ndarray]:
+    """Decode of a rank-D layer: bf16 rows of D latent ++ 64 rope values, pool_bits uint16
+    [num_slots, D + 64]; q_bits [B, H, D + 64].  out [B, H, D], lse [B, H]."""
+    q = bf16_to_f64(q_bits)
+    B, H, K = q.shape
+    D = K - ROPE
+    flat = np.asarray(pool_bits, dtype=np.uint16).reshape(-1, K)
+    out = np.full((B, H, D), np.nan)
+    lse = np.full((B, H), np.nan)
+    for b in (range(B) if requests is None else requests):
+        L = int(seq_lens[b])
+        t = np.arange(L, dtype=np.int64)
+        pages = np.asarray(block_table[b], dtype=np.int64)[t // page_size]
+        rows = bf16_to_f64(flat[pages * page_size + t % page_size])
+        out[b], lse[b] = attend_kv(q[b], rows, rows[:, :D], scale)
     return out, lse
 
 

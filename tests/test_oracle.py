@@ -18,6 +18,11 @@ mla.decode               page-permutation invariance; garbage-rope control
 mla.decode_mtp           pure-Python brute force with the causal limits written out;
                          each query equals decode over its truncated context; rows after a
                          query's position never change it (a planted off-by-one fails)
+mla.attend_kv            pure-Python brute force with separate keys and values
+mla.decode_rank          brute force on rank-256 rows written out by hand
+mla.decode_gla2          equals decode_rank on each group's rows cut out of the 576-value
+                         row; rewriting one group's latent half leaves the other group's
+                         heads bit-identical (a swapped half fails)
 mla.decode_nope          pure-Python brute force over the 512 latent values; equals decode
                          with q_pe = 0 on finite rope; unchanged by NaN rope bytes, which
                          turn decode with q_pe = 0 into NaN (the pages' control)
@@ -474,6 +479,75 @@ def test_mtp_rows_after_a_query_do_not_change_it():
         o, l = oracle.decode_mtp(q, p2, w.block_table, w.seq_lens, 8, w.scale, "bf16")
         assert np.array_equal(o[b, i], ref[0][b, i]) and np.array_equal(l[b, i], ref[1][b, i])
         assert np.abs(l[b, T - 1] - ref[1][b, T - 1]).max() > 1e-9
+
+
+# ------------------------------------------------------------- other latent geometries
+def test_attend_kv_matches_brute_force():
+    rng = np.random.default_rng(90)
+    q, keys, vals = rng.standard_normal((2, 7)), rng.standard_normal((5, 7)), rng.standard_normal((5, 3))
+    out, lse = oracle.attend_kv(q, keys, vals, 0.3)
+    for h in range(2):
+        s = [0.3 * math.fsum(q[h][d] * keys[t][d] for d in range(7)) for t in range(5)]
+        m = max(s)
+        ls = m + math.log(math.fsum(math.exp(x - m) for x in s))
+        w = [math.exp(x - ls) for x in s]
+        assert abs(lse[h] - ls) < 1e-12
+        assert max(abs(out[h][c] - math.fsum(w[t] * vals[t][c] for t in range(5))) for c in range(3)) < 1e-12
+
+
+def _rank_pool(rng, w, D):
+    """bf16 bits [num_slots, D + 64] with random rows at the workload's slots (rest NaN)."""
+    pool = np.full((w.num_pages * w.page_size, D + 64), 0x7FC0, np.uint16)
+    pool[w.slots] = workloads.bf16_bits(rng.standard_normal((w.slots.size, D + 64)).astype(np.float32))
+    return pool
+
+
+def test_rank256_decode_matches_brute_force():
+    rng = np.random.default_rng(91)
+    w = workloads.make_workload("r256", seq_lens=[6, 3], heads=2, page_size=3, num_pages=6, rng=rng)
+    pool = _rank_pool(rng, w, 256)
+    q = workloads.bf16_bits(rng.standard_normal((2, 2, 320)).astype(np.float32))
+    out, lse = oracle.decode_rank(q, pool, w.block_table, w.seq_lens, 3, w.scale)
+    qf = oracle.bf16_to_f64(q)
+    for b in range(2):
+        rows = [oracle.bf16_to_f64(pool[int(w.block_table[b][t // 3]) * 3 + t % 3]).tolist()
+                for t in range(int(w.seq_lens[b]))]
+        for h in range(2):
+            s = [w.scale * math.fsum(qf[b, h, d] * r[d] for d in range(320)) for r in rows]
+            m = max(s)
+            ls = m + math.log(math.fsum(math.exp(x - m) for x in s))
+            assert abs(lse[b, h] - ls) < 1e-12
+            for c in (0, 100, 255):
+                ref = math.fsum(math.exp(x - ls) * r[c] for x, r in zip(s, rows))
+                assert abs(out[b, h, c] - ref) < 1e-12
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_gla2_is_two_rank256_problems(fmt):
+    rng = np.random.default_rng(92)
+    w = workloads.make_workload("gla", seq_lens=[40, 0, 19], heads=4, page_size=8, num_pages=12, rng=rng, fmt=fmt)
+    pool = w.poisoned_pool() if fmt == "bf16" else np.full((12, 8, 656), 0xFF, np.uint8)
+    oracle.cache_write(pool, w.latent, w.k_pe, w.slots, fmt)
+    q = workloads.bf16_bits(rng.standard_normal((3, 4, 320)).astype(np.float32))
+    out, lse = oracle.decode_gla2(q, pool, w.block_table, w.seq_lens, 8, w.scale, fmt)
+    vals = oracle.rows_from_bytes(pool.reshape(-1, oracle.ROW_BYTES[fmt])[w.slots], fmt)  # fp64, exact
+    if fmt == "bf16":  # decode_rank takes bf16 rows; dequantised fp8 values need not be bf16 values
+        for g in range(2):
+            pg = np.full((12 * 8, 320), 0x7FC0, np.uint16)
+            cut = np.concatenate([vals[:, 256 * g:256 * g + 256], vals[:, 512:]], axis=1)
+            pg[w.slots] = workloads.bf16_bits(cut.astype(np.float32))  # exact: the values are bf16
+            o, l = oracle.decode_rank(q[:, 2 * g:2 * g + 2], pg, w.block_table, w.seq_lens, 8, w.scale)
+            assert np.array_equal(o, out[:, 2 * g:2 * g + 2]) and np.array_equal(l, lse[:, 2 * g:2 * g + 2])
+    # rewriting group 1's latent half (fp8: its scale blocks 2 and 3) leaves group 0's heads
+    # unchanged, and changes group 1's
+    p2 = pool.copy()
+    lat2 = w.latent.copy()
+    lat2[:, 256:] = workloads.bf16_bits(rng.standard_normal((lat2.shape[0], 256)).astype(np.float32))
+    oracle.cache_write(p2, lat2, w.k_pe, w.slots, fmt)
+    o2, l2 = oracle.decode_gla2(q, p2, w.block_table, w.seq_lens, 8, w.scale, fmt)
+    assert np.array_equal(o2[:, :2], out[:, :2]) and np.array_equal(l2[:, :2], lse[:, :2])
+    live = w.seq_lens > 0
+    assert np.abs(l2[live, 2:] - lse[live, 2:]).max() > 1e-6
 
 
 # --------------------------------------------------------------------------- NoPE-512
