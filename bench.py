@@ -41,6 +41,9 @@ def _parse():
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per request: > 1 times a speculative-decoding verify step "
                          "(mla_decode_mtp_*), which reads the cache once per request")
+    ap.add_argument("--geometry", choices=("mla", "gla2", "rank256"), default="mla",
+                    help="gla2: GLA-g2 head groups on the same rows; rank256: a rank-256 layer (640-byte bf16 "
+                         "rows made from the workload's rows; no cache write in the step)")
     ap.add_argument("--nope", action="store_true",
                     help="decode the workload as a NoPE-512 layer: 512-wide queries, rows written with a zero "
                          "rope part, which the NoPE kernels never read")
@@ -69,7 +72,17 @@ def _copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
-def _cpu_baseline(w, requests, nope=False, q_mtp=None, min_seconds=10.0):
+def _rank256_rows(w):
+    """Rank-256 rows (bf16 [slots, 320]) made from the workload's rows: latent[:256] ++ k_pe."""
+    return np.concatenate([w.latent[:, :256], w.k_pe], axis=1)
+
+
+def _geometry_q(w):
+    """320 query values per head (the first 256 latent values, then the rope part)."""
+    return np.ascontiguousarray(np.concatenate([w.q[:, :, :256], w.q[:, :, 512:]], axis=2))
+
+
+def _cpu_baseline(w, requests, nope=False, q_mtp=None, geometry="mla", min_seconds=10.0):
     """Time the fp64 oracle on a bounded sample of the same workload, on the host cores."""
     import oracle
     try:
@@ -82,6 +95,16 @@ def _cpu_baseline(w, requests, nope=False, q_mtp=None, min_seconds=10.0):
     oracle.cache_write(pool, w.latent[idx], None if nope else w.k_pe[idx], w.slots[idx], w.fmt)
     q = np.ascontiguousarray(w.q[:, :, :512]) if nope else (w.q if q_mtp is None else q_mtp)
     run = oracle.decode_nope if nope else (oracle.decode if q_mtp is None else oracle.decode_mtp)
+    row_bytes = w.row_bytes - (128 if nope else 0)
+    if geometry == "gla2":
+        q, run = _geometry_q(w), oracle.decode_gla2
+    elif geometry == "rank256":
+        flat = np.full((w.num_slots, 320), 0x7FC0, np.uint16)
+        flat[w.slots[idx]] = _rank256_rows(w)[idx]
+        q, pool, row_bytes = _geometry_q(w), flat, 640
+
+        def run(q, pool, bt, lens, ps, scale, fmt, requests):
+            return oracle.decode_rank(q, pool, bt, lens, ps, scale, requests=requests)
     # Repeat the sample until about 10 s of host time has been spent.
     reps, t = 0, time.perf_counter()
     while True:
@@ -93,7 +116,7 @@ def _cpu_baseline(w, requests, nope=False, q_mtp=None, min_seconds=10.0):
     tokens = int(sum(int(w.seq_lens[b]) for b in requests))
     per = dt / reps
     return {
-        "value": round(tokens * (w.row_bytes - (128 if nope else 0)) / per / 1e9, 3),
+        "value": round(tokens * row_bytes / per / 1e9, 3),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
@@ -265,6 +288,26 @@ def main():
         decode = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
     groups = 1 if rows <= 16 else (2 if rows <= 32 else 4)
     kernel = f"decode_kernel<{'Bf16' if w.fmt == 'bf16' else 'Fp8'}Rows<{0 if nope else 64}>, {groups}>"
+    geom, width, write_rows, row_bytes_read = args.geometry, 512, True, w.row_bytes - (128 if nope else 0)
+    if geom != "mla":
+        if nope or T > 1:
+            raise SystemExit("--geometry is not combined with --nope or --q-len by this benchmark")
+        width = 256
+        q = bf16(_geometry_q(w))
+        if geom == "gla2":
+            decode = mla.mla_decode_gla2_bf16 if w.fmt == "bf16" else mla.mla_decode_gla2_fp8_656
+            kernel = f"decode_kernel<{'Bf16Rows<512, 64>' if w.fmt == 'bf16' else 'Fp8Rows<64>'}, 1, true>"
+        else:
+            if w.fmt != "bf16":
+                raise SystemExit("--geometry rank256 needs a bf16 workload")
+            host = np.full((w.num_slots, 320), 0x7FC0, np.uint16)
+            host[w.slots] = _rank256_rows(w)
+            del pool
+            pool = bf16(host).view(w.num_pages, w.page_size, 320)
+            del host
+            decode, write_rows, row_bytes_read = mla.mla_decode_rank256_bf16, False, 640
+            kernel = "decode_kernel<Bf16Rows<256, 64>, 1>"
+        out = torch.empty((w.batch, rows, width), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -272,12 +315,16 @@ def main():
 
     def step(e=None):
         if e: e[0].record(stream)
-        mla.mla_cache_write(new_lat, new_pe, new_slots, pool, fmt)
+        if write_rows:
+            mla.mla_cache_write(new_lat, new_pe, new_slots, pool, fmt)
         if e: e[1].record(stream)
         if S > 1:
             po, pl = decode(q, pool, bt, lens, w.scale, num_splits=S, workspace=ws, partials_only=True)
             if e: e[2].record(stream)
-            mla.mla_merge_lse(po, pl, out=out, lse=lse)
+            if width == 512:
+                mla.mla_merge_lse(po, pl, out=out, lse=lse)
+            else:
+                mla.mla_merge_lse_width(po, pl, out=out, lse=lse)
         else:
             decode(q, pool, bt, lens, w.scale, num_splits=1, out=out, lse=lse)
             if e: e[2].record(stream)
@@ -331,8 +378,9 @@ def main():
     assert np.isfinite(o[live]).all() and np.isfinite(l[live]).all(), "non-finite decode output"
     assert np.isneginf(l[~live]).all() and (o[~live] == 0).all(), "a row that sees no token is not (0, -inf)"
 
-    # bytes the decode must read: whole rows, or rows without their rope part (NoPE)
-    cache_bytes = w.tokens * (w.row_bytes - 128) if nope else w.cache_bytes_read()
+    # bytes the decode must read: whole rows, rows without their rope part (NoPE), or
+    # 640-byte rank-256 rows
+    cache_bytes = w.tokens * row_bytes_read
     gbs = cache_bytes / (ms_step * 1e-3) / 1e9
     decode_gbs = cache_bytes / (t_decode * 1e-3) / 1e9
     result = {
@@ -353,8 +401,9 @@ def main():
         "config": {
             "workload": w.name, "batch": w.batch, "heads": w.heads, "context_tokens": w.tokens,
             "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
-            "layer": "nope-512" if nope else "rope-576", "query_tokens_per_request": T,
-            "cache_row_bytes": w.row_bytes, "row_bytes_read": w.row_bytes - (128 if nope else 0),
+            "layer": "nope-512" if nope else "rope-576", "query_tokens_per_request": T, "geometry": geom,
+            "cache_row_bytes": 640 if geom == "rank256" else w.row_bytes, "row_bytes_read": row_bytes_read,
+            "step": "decode + merge" if not write_rows else "cache write + decode + merge",
             "cache_bytes_per_step": cache_bytes,
         },
         "launch": launch_mode,
@@ -367,11 +416,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None if (nope or T > 1) else _profiled_traffic(w.name),
+            "traffic": None if (nope or T > 1 or geom != "mla") else _profiled_traffic(w.name),
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = _cpu_baseline(w, list(range(min(w.batch, 4))), nope, q_mtp)
+        result["cpu_baseline"] = _cpu_baseline(w, list(range(min(w.batch, 4))), nope, q_mtp, geom)
     print(json.dumps(result), flush=True)
 
 

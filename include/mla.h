@@ -172,6 +172,51 @@ MLA_API int mla_decode_mtp_fp8_656(const void* q, const void* kv_cache, int64_t 
                                    int32_t num_splits, float* out, float* lse, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Other latent geometries (qwen-mla-vllm: per-layer latent ranks 256 / 768 / 1792 with a small
+ * rotary tail, "How it works"; GLA-g2, the latent split into two head groups, opening section).
+ * The row layouts are this library's reading; the pages give none.
+ *
+ * mla_decode_rank256_bf16: a rank-256 layer.  kv_cache bf16 [num_pages][page_size][320] (256
+ * latent values, then 64 rope values), q bf16 [batch][num_heads][320], out fp32
+ * [batch][num_heads][256]; scores over all 320 values, output the weighted latent sum.
+ *
+ * mla_decode_gla2_bf16 / mla_decode_gla2_fp8_656: GLA-g2 on the 576-value / 656-byte row.
+ * num_heads even; heads [0, H/2) use latent values [0, 256), heads [H/2, H) use [256, 512),
+ * both groups share the 64 rope values.  q bf16 [batch][num_heads][320] (the head's group
+ * latent part, then its rope part); out fp32 [batch][num_heads][256], the weighted sum of the
+ * group's latent values.  The row is read once for both groups.
+ *
+ * Every other argument, result and error as mla_decode_bf16; the partials left in the
+ * workspace (out == lse == NULL) are 256 wide: merge them with mla_merge_lse_width(.., 256, ..).
+ * Ranks 768 and 1792 are not provided: their 16-row output tile needs 192 / 448 accumulator
+ * registers per lane and their 16-token tiles 26 / 59 KB of LDS, past what this kernel's
+ * single pass holds (the pages' own kernels take two passes for 1792). */
+MLA_API int mla_decode_rank256_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                                    const int32_t* block_table, int64_t block_table_stride,
+                                    const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                    int32_t page_size, float softmax_scale, int32_t num_splits,
+                                    float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+MLA_API int mla_decode_gla2_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                                 const int32_t* block_table, int64_t block_table_stride,
+                                 const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                 int32_t page_size, float softmax_scale, int32_t num_splits,
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+MLA_API int mla_decode_gla2_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                                    const int32_t* block_table, int64_t block_table_stride,
+                                    const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                    int32_t page_size, float softmax_scale, int32_t num_splits,
+                                    float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* mla_merge_lse for partial rows of `width` values (256 or 512): part_out fp32
+ * [num_splits][batch][num_rows][width], part_lse [num_splits][batch][num_rows], out
+ * [batch][num_rows][width], lse [batch][num_rows]; same formula and NaN / empty rules. */
+MLA_API int mla_merge_lse_width(const float* part_out, const float* part_lse, int32_t num_splits,
+                                int32_t batch, int32_t num_rows, int32_t width, float* out,
+                                float* lse, void* stream);
+
 /* Merge num_splits partial results over disjoint token sets (vLLM pull request
  * 55543: partial (o, lse) pairs merge by log-sum-exp; a partition with no
  * tokens is (0, -inf)).

@@ -10,6 +10,9 @@ Entry points (same names as the C ABI in include/mla.h):
     mla_decode_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, ...)
     mla_decode_nope_bf16 / mla_decode_nope_fp8_656(q [B, H, 512], ...)   NoPE-512 layers
     mla_decode_mtp_bf16 / mla_decode_mtp_fp8_656(q [B, q_len, H, 576], ...)   verify step
+    mla_decode_rank256_bf16(q [B, H, 320], kv_cache [pages, ps, 320], ...)   rank-256 layer
+    mla_decode_gla2_bf16 / mla_decode_gla2_fp8_656(q [B, H, 320], ...)   GLA-g2 head groups
+    mla_merge_lse_width(part_out, part_lse, out=None, lse=None)   256- or 512-wide partials
     mla_merge_lse(part_out, part_lse, out=None, lse=None)
     mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format)   k_pe None: zero rope
     mla_gather_context(kv_cache, cache_format, block_table, cu_rows, total_rows, seq_starts=None)
@@ -40,7 +43,8 @@ MAX_QUERY_ROWS = 64
 
 EXPORTED = (
     "mla_decode_workspace_size", "mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16",
-    "mla_decode_nope_fp8_656", "mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656", "mla_merge_lse",
+    "mla_decode_nope_fp8_656", "mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656", "mla_decode_rank256_bf16",
+    "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656", "mla_merge_lse", "mla_merge_lse_width",
     "mla_cache_write", "mla_gather_context", "mla_status_string", "mla_last_error_message", "mla_abi_version",
 )
 
@@ -69,7 +73,8 @@ def library() -> ctypes.CDLL:
     lib.mla_decode_workspace_size.argtypes = [c_i32, c_i32, c_i32]
     lib.mla_decode_workspace_size.restype = c_sz
     dec = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
-    for name in ("mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656"):
+    for name in ("mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656",
+                 "mla_decode_rank256_bf16", "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = c_int
     mtp = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
@@ -78,6 +83,8 @@ def library() -> ctypes.CDLL:
         getattr(lib, name).restype = c_int
     lib.mla_merge_lse.argtypes = [vp, vp, c_i32, c_i32, c_i32, vp, vp, vp]
     lib.mla_merge_lse.restype = c_int
+    lib.mla_merge_lse_width.argtypes = [vp, vp, c_i32, c_i32, c_i32, c_i32, vp, vp, vp]
+    lib.mla_merge_lse_width.restype = c_int
     lib.mla_cache_write.argtypes = [vp, vp, vp, c_i32, vp, c_i32, c_i64, vp]
     lib.mla_cache_write.restype = c_int
     lib.mla_gather_context.argtypes = [vp, c_i32, c_i64, c_i32, vp, c_i64, vp, vp, c_i32, c_i64, vp, vp]
@@ -126,7 +133,7 @@ def mla_decode_workspace_size(batch: int, num_heads: int, num_splits: int) -> in
 
 
 def _decode(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
-            softmax_scale, num_splits, out, lse, workspace, partials_only=False, q_dim=ROW):
+            softmax_scale, num_splits, out, lse, workspace, partials_only=False, q_dim=ROW, out_width=LATENT):
     lib = library()
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
@@ -145,7 +152,7 @@ def _decode(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache,
             raise ValueError("partials_only needs num_splits > 1 and no out/lse")
     else:
         if out is None:
-            out = torch.empty((B, H, LATENT), dtype=torch.float32, device=dev)
+            out = torch.empty((B, H, out_width), dtype=torch.float32, device=dev)
         if lse is None:
             lse = torch.empty((B, H), dtype=torch.float32, device=dev)
         _need(out, "out", torch.float32, 3, dev)
@@ -163,8 +170,8 @@ def _decode(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache,
     _check(fn, status)
     if partials_only:
         n = num_splits * B * H
-        flat = workspace.view(torch.uint8)[: n * (LATENT + 1) * 4].view(torch.float32)
-        return flat[: n * LATENT].view(num_splits, B, H, LATENT), flat[n * LATENT:].view(num_splits, B, H)
+        flat = workspace.view(torch.uint8)[: n * (out_width + 1) * 4].view(torch.float32)
+        return flat[: n * out_width].view(num_splits, B, H, out_width), flat[n * out_width:].view(num_splits, B, H)
     return out, lse
 
 
@@ -258,6 +265,47 @@ def mla_decode_mtp_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, nu
     """Verify-step decode over an fp8 cache uint8 [num_pages, page_size, 656]."""
     return _decode_mtp("mla_decode_mtp_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
                        softmax_scale, num_splits, out, lse, workspace, partials_only)
+
+
+def mla_decode_rank256_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                            workspace=None, partials_only=False):
+    """Rank-256 layer: kv_cache bf16 [pages, ps, 320], q [B, H, 320] -> out [B, H, 256], lse [B, H]."""
+    return _decode("mla_decode_rank256_bf16", torch.bfloat16, 320, q, kv_cache, block_table, seq_lens,
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=320, out_width=256)
+
+
+def mla_decode_gla2_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                         workspace=None, partials_only=False):
+    """GLA-g2 on the 576-value row: q [B, H, 320] (H even) -> out [B, H, 256], lse [B, H]."""
+    return _decode("mla_decode_gla2_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=320, out_width=256)
+
+
+def mla_decode_gla2_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                            workspace=None, partials_only=False):
+    """GLA-g2 on the 656-byte fp8 row: q [B, H, 320] (H even) -> out [B, H, 256], lse [B, H]."""
+    return _decode("mla_decode_gla2_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=320, out_width=256)
+
+
+def mla_merge_lse_width(part_out, part_lse, out=None, lse=None):
+    """Merge partials [S, B, R, W] / [S, B, R] with W = 256 or 512; returns (out [B, R, W], lse [B, R])."""
+    lib = library()
+    _need(part_out, "part_out", torch.float32, 4)
+    dev = part_out.device
+    _need(part_lse, "part_lse", torch.float32, 3, dev)
+    S, B, R, W = part_out.shape
+    if tuple(part_lse.shape) != (S, B, R):
+        raise ValueError("part_lse must be [S, B, R]")
+    if out is None:
+        out = torch.empty((B, R, W), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, R), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    _check("mla_merge_lse_width", lib.mla_merge_lse_width(part_out.data_ptr(), part_lse.data_ptr(), S, B, R, W,
+                                                          out.data_ptr(), lse.data_ptr(), _stream(dev)))
+    return out, lse
 
 
 def mla_merge_lse(part_out, part_lse, out=None, lse=None):

@@ -67,18 +67,22 @@ __device__ __forceinline__ Range partition(int64_t L, int ps, int S, int s, int6
 __device__ __forceinline__ int swz(int t) { return (((t >> 2) & 1) << 1) | ((t >> 3) & 1); }
 __device__ __forceinline__ int chunk_pos(int t, int c) { return 64 * (c >> 2) + 4 * t + ((c & 3) ^ swz(t)); }
 
-// kRopeDim = 64: the full 576-value row.  kRopeDim = 0 (NoPE-512 layers): only the 512
-// latent values (the first 1,024 bytes of each row) are loaded and scored.
-template <int kRopeDim>
+// Rows of kLat latent values followed by 64 rope values, bf16.  kLat = 512, kRopeDim = 64:
+// the 576-value row.  kRopeDim = 0 (NoPE-512 layers): only the 512 latent values (the
+// first 1,024 bytes of each row) are loaded and scored.  kLat = 256: rank-256 layers,
+// 320-value (640-byte) rows.
+template <int kLat, int kRopeDim>
 struct Bf16Rows {
   static_assert(kRopeDim == 64 || kRopeDim == 0, "rope part: 64 values or none");
-  static constexpr int kRowBytes = kRowBytesBf16;
-  static constexpr int kQDim = kLatent + kRopeDim;      // query values per head
+  static_assert(kLat == 512 || (kLat == 256 && kRopeDim == 64), "latent widths 512 and 256");
+  static constexpr int kLatent = kLat;
+  static constexpr int kRowBytes = 2 * (kLat + 64);     // rows are stored with their rope part
+  static constexpr int kQDim = kLat + kRopeDim;         // query values per head
   static constexpr int kQSteps = kQDim / 32;            // QK K-steps of 32 values
-  static constexpr int kDmaOps = kQDim * 2 / 64;        // 18, or 16 without rope
+  static constexpr int kDmaOps = kQDim * 2 / 64;        // 18; 16 without rope; 10 at rank 256
   static constexpr int kBufs = 2;  // tiles per wave resident in LDS (2 x 4 x 18 KB)
-  static constexpr int kTileBytes = kDmaOps * 1024;     // 18,432 / 16,384
-  static constexpr int kAcc = 32;                       // 16x16 output tiles per head group
+  static constexpr int kTileBytes = kDmaOps * 1024;     // 18,432 / 16,384 / 10,240
+  static constexpr int kAcc = kLat / 16;                // 16x16 output tiles per row group
 
   struct Aux {};
 
@@ -136,6 +140,7 @@ struct Bf16Rows {
 template <int kRopeDim>
 struct Fp8Rows {
   static_assert(kRopeDim == 64 || kRopeDim == 0, "rope part: 64 values or none");
+  static constexpr int kLatent = 512;
   static constexpr int kRowBytes = kRowBytesFp8;
   static constexpr int kQDim = kLatent + kRopeDim;
   static constexpr int kQSteps = kQDim / 32;
@@ -262,9 +267,16 @@ constexpr int smem_bytes() {
 //    makes the step's four tiles visible to all waves, and wave w scores tiles
 //    G(w/G) .. G(w/G) + G - 1 of the step for row group w % G.  The cache is read once
 //    per request whatever q_len is; the arithmetic per byte grows with G.
-template <class Fmt, int G>
+// kGla2: GLA-g2 heads.  Head h of H belongs to group gh = h / (H / 2) and scores latent
+// values [256 gh, 256 gh + 256) plus the shared rope: q holds 320 values per head (group
+// latent, rope), scattered into a 576-wide fragment that is zero outside the group, and
+// the output of each head is its group's 256 columns.  The row is read once for both
+// groups; the MFMA work is that of the 576-wide decode.
+template <class Fmt, int G, bool kGla2 = false>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) {
   static_assert(G == 1 || G == 2 || G == 4, "row groups per workgroup");
+  static_assert(!kGla2 || (Fmt::kLatent == 512 && Fmt::kQDim == 576), "GLA-g2 on the 576-value row");
+  constexpr int kOut = kGla2 ? 256 : Fmt::kLatent;  // output values per query row
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
 
   // Partition-major grid: all requests' first partitions are dispatched first, then the
@@ -297,9 +309,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
 #pragma unroll
     for (int j = 0; j < QS; ++j) qf[j] = u32x4{0u, 0u, 0u, 0u};
     if (row < R) {
-      const uint16_t* qrow = p.q + ((int64_t)b * R + row) * Fmt::kQDim + 8 * g;
+      if constexpr (kGla2) {
+        // 320 values per head: group latent [0, 256) then rope [256, 320).
+        const int gh = (row % H) >= H / 2 ? 1 : 0;
+        const uint16_t* qrow = p.q + ((int64_t)b * R + row) * 320 + 8 * g;
 #pragma unroll
-      for (int j = 0; j < QS; ++j) qf[j] = *(const u32x4*)(qrow + 32 * j);
+        for (int j = 0; j < QS; ++j) {
+          if (j >= 16)
+            qf[j] = *(const u32x4*)(qrow + 256 + 32 * (j - 16));
+          else if (j / 8 == gh)
+            qf[j] = *(const u32x4*)(qrow + 32 * (j - 8 * gh));
+        }
+      } else {
+        const uint16_t* qrow = p.q + ((int64_t)b * R + row) * Fmt::kQDim + 8 * g;
+#pragma unroll
+        for (int j = 0; j < QS; ++j) qf[j] = *(const u32x4*)(qrow + 32 * j);
+      }
     }
   }
 
@@ -471,13 +496,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
 
   const bool split = p.num_splits > 1;
   const int64_t row_b = (int64_t)b * R;
-  float* out = split ? p.part_out + ((int64_t)s * p.batch * R + row_b) * kLatent : p.out + row_b * kLatent;
+  float* out = split ? p.part_out + ((int64_t)s * p.batch * R + row_b) * kOut : p.out + row_b * kOut;
   float* lse = split ? p.part_lse + (int64_t)s * p.batch * R + row_b : p.lse + row_b;
-  for (int idx = threadIdx.x; idx < R * (kLatent / 4); idx += kWaves * 64) {
-    const int r = idx / (kLatent / 4);
-    const int d4 = idx % (kLatent / 4);
+  for (int idx = threadIdx.x; idx < R * (kOut / 4); idx += kWaves * 64) {
+    const int r = idx / (kOut / 4);
+    const int d4 = idx % (kOut / 4);
     const int gg = r / 16;
     const int mm = r % 16;
+    // first O column of this row's output (GLA-g2: its head group's half)
+    const int c0 = kGla2 ? ((r % H) >= H / 2 ? 256 : 0) : 0;
     float M = -INFINITY;
 #pragma unroll
     for (int w = gg; w < kWaves; w += G) M = fmaxf(M, red_m[w * kMaxHeads + mm]);
@@ -488,7 +515,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
       for (int w = gg; w < kWaves; w += G) {
         const float f = fast_exp2(red_m[w * kMaxHeads + mm] - M);
         lsum += f * red_l[w * kMaxHeads + mm];
-        o += f * *(const f32x4*)(red + (w * kMaxHeads + mm) * kRedStride + 4 * d4);
+        o += f * *(const f32x4*)(red + (w * kMaxHeads + mm) * kRedStride + c0 + 4 * d4);
       }
       o *= 1.0f / lsum;  // a NaN score anywhere made lsum NaN: NaN out
     } else {
@@ -498,7 +525,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
       for (int w = gg; w < kWaves; w += G) lsum += red_l[w * kMaxHeads + mm];
       o *= lsum;
     }
-    *(f32x4*)(out + (int64_t)r * kLatent + 4 * d4) = o;
+    *(f32x4*)(out + (int64_t)r * kOut + 4 * d4) = o;
     if (d4 == 0) lse[r] = (M == -INFINITY) ? -INFINITY + lsum : (M + fast_log2(lsum)) * 0.69314718055994530942f;
   }
 }
@@ -518,10 +545,28 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) { return launch<Bf16Rows<64>>(p, stream); }
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
+  return launch<Bf16Rows<512, 64>>(p, stream);
+}
 hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream) { return launch<Fp8Rows<64>>(p, stream); }
 hipError_t launch_decode_nope_bf16(const DecodeParams& p, hipStream_t stream) {
-  return launch<Bf16Rows<0>>(p, stream);
+  return launch<Bf16Rows<512, 0>>(p, stream);
+}
+// Single-token decodes of the other geometries (at most 16 query rows: one row group).
+hipError_t launch_decode_rank256_bf16(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<Bf16Rows<256, 64>, 1>), dim3((unsigned)p.batch, (unsigned)p.num_splits),
+                     dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+hipError_t launch_decode_gla2_bf16(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<Bf16Rows<512, 64>, 1, true>), dim3((unsigned)p.batch, (unsigned)p.num_splits),
+                     dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+hipError_t launch_decode_gla2_fp8(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<Fp8Rows<64>, 1, true>), dim3((unsigned)p.batch, (unsigned)p.num_splits),
+                     dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
 }
 hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream) {
   return launch<Fp8Rows<0>>(p, stream);

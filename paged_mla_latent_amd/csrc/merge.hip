@@ -15,14 +15,15 @@ namespace mla {
 namespace {
 
 constexpr int kGroups = 8;    // partial streams per workgroup
-constexpr int kCols = 32;     // float4 columns per workgroup (128 of the 512 latent values)
+constexpr int kCols = 32;     // float4 columns per workgroup (128 output values)
 
-// grid = (batch * heads, 4): workgroup (bh, y) merges latent columns [128y, 128y + 128) of
-// row bh.  Lane t owns float4 column t % 32 and partials p = t / 32, t / 32 + 8, ...; the
-// eight partial streams are then summed through LDS.
+// grid = (batch * heads, width / 128): workgroup (bh, y) merges columns [128y, 128y + 128)
+// of row bh (width = 512 for the latent rows, 256 for the rank-256 / GLA-g2 outputs).
+// Lane t owns float4 column t % 32 and partials p = t / 32, t / 32 + 8, ...; the eight
+// partial streams are then summed through LDS.
 __global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __restrict__ part_out,
                                                                const float* __restrict__ part_lse, int S,
-                                                               int64_t rows, float* __restrict__ out,
+                                                               int64_t rows, int width, float* __restrict__ out,
                                                                float* __restrict__ lse) {
   __shared__ f32x4 acc_s[kGroups][kCols];
   __shared__ float w_s[kGroups];
@@ -60,12 +61,12 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __r
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
   if (M != -INFINITY) {
-    const float* src = part_out + bh * kLatent + 4 * col;
+    const float* src = part_out + bh * width + 4 * col;
 #pragma unroll 4
     for (int p = grp; p < S; p += kGroups) {
       const float w = __expf(part_lse[p * rows + bh] - M);
       W += w;
-      acc += w * *(const f32x4*)(src + (int64_t)p * rows * kLatent);
+      acc += w * *(const f32x4*)(src + (int64_t)p * rows * width);
     }
   }
   acc_s[grp][threadIdx.x % kCols] = acc;
@@ -80,17 +81,17 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __r
     acc += acc_s[g][threadIdx.x];
   }
   if (M != -INFINITY) acc *= 1.0f / W;
-  *(f32x4*)(out + bh * kLatent + 4 * col) = acc;
+  *(f32x4*)(out + bh * width + 4 * col) = acc;
   if (blockIdx.y == 0 && threadIdx.x == 0) lse[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(W);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const float* part_out, const float* part_lse, int num_splits, int batch,
-                        int heads, float* out, float* lse, hipStream_t stream) {
+                        int heads, float* out, float* lse, hipStream_t stream, int width) {
   const int64_t rows = (int64_t)batch * heads;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows, kLatent / (4 * kCols)), dim3(kGroups * kCols), 0, stream,
-                     part_out, part_lse, num_splits, rows, out, lse);
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows, (unsigned)(width / (4 * kCols))), dim3(kGroups * kCols), 0,
+                     stream, part_out, part_lse, num_splits, rows, width, out, lse);
   return hipGetLastError();
 }
 

@@ -61,15 +61,19 @@ size_t workspace_bytes_for(int64_t batch, int64_t heads, int64_t splits) {
 }
 
 // Kinds of decode: row format and whether the rope part takes part in the scores.
-enum DecodeKind { kBf16 = 0, kFp8 = 1, kNopeBf16 = 2, kNopeFp8 = 3 };
+enum DecodeKind { kBf16 = 0, kFp8 = 1, kNopeBf16 = 2, kNopeFp8 = 3, kRank256Bf16 = 4, kGla2Bf16 = 5, kGla2Fp8 = 6 };
 
 int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, int64_t num_pages,
                   const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
                   int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
                   int32_t num_splits, float* out, float* lse, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  static const char* const kNames[] = {"mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16",
-                                       "mla_decode_nope_fp8_656"};
+  static const char* const kNames[] = {"mla_decode_bf16",         "mla_decode_fp8_656",
+                                       "mla_decode_nope_bf16",    "mla_decode_nope_fp8_656",
+                                       "mla_decode_rank256_bf16", "mla_decode_gla2_bf16",
+                                       "mla_decode_gla2_fp8_656"};
+  const bool gla = kind == kGla2Bf16 || kind == kGla2Fp8;
+  const int out_width = (kind == kRank256Bf16 || gla) ? 256 : MLA_LATENT;
   const char* fn = q_len == 1 ? kNames[kind] : (kind == kBf16 ? "mla_decode_mtp_bf16" : "mla_decode_mtp_fp8_656");
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
@@ -84,6 +88,8 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
     return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_HEADS);
   if (q_len < 1 || q_len > MLA_MAX_Q_LEN)
     return fail(MLA_ERR_SHAPE, "%s: q_len=%d outside [1, %d]", fn, q_len, MLA_MAX_Q_LEN);
+  if (gla && num_heads % 2)
+    return fail(MLA_ERR_SHAPE, "%s: num_heads=%d must be even (two head groups)", fn, num_heads);
   if (q_len * num_heads > MLA_MAX_QUERY_ROWS)
     return fail(MLA_ERR_SHAPE, "%s: q_len * num_heads = %d exceeds %d", fn, q_len * num_heads, MLA_MAX_QUERY_ROWS);
   if (page_size < 1) return fail(MLA_ERR_SHAPE, "%s: page_size=%d must be >= 1", fn, page_size);
@@ -107,7 +113,7 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
     if (workspace_bytes < need)
       return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
     part_out = static_cast<float*>(workspace);
-    part_lse = part_out + (size_t)num_splits * batch * q_len * num_heads * MLA_LATENT;
+    part_lse = part_out + (size_t)num_splits * batch * q_len * num_heads * out_width;
   }
   int rc = check_device();
   if (rc != MLA_OK) return rc;
@@ -134,11 +140,14 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
     case kBf16: launched = mla::launch_decode_bf16(p, s); break;
     case kFp8: launched = mla::launch_decode_fp8(p, s); break;
     case kNopeBf16: launched = mla::launch_decode_nope_bf16(p, s); break;
-    default: launched = mla::launch_decode_nope_fp8(p, s); break;
+    case kNopeFp8: launched = mla::launch_decode_nope_fp8(p, s); break;
+    case kRank256Bf16: launched = mla::launch_decode_rank256_bf16(p, s); break;
+    case kGla2Bf16: launched = mla::launch_decode_gla2_bf16(p, s); break;
+    default: launched = mla::launch_decode_gla2_fp8(p, s); break;
   }
   rc = hip_status(launched, fn);
   if (rc != MLA_OK || num_splits == 1 || partials_only) return rc;
-  return hip_status(mla::launch_merge(part_out, part_lse, num_splits, batch, q_len * num_heads, out, lse, s),
+  return hip_status(mla::launch_merge(part_out, part_lse, num_splits, batch, q_len * num_heads, out, lse, s, out_width),
                     "mla_merge_lse (after decode)");
 }
 
@@ -197,6 +206,52 @@ int mla_decode_mtp_fp8_656(const void* q, const void* kv_cache, int64_t num_page
                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_common(kFp8, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                        num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_rank256_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                            int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                            int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kRank256Bf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_gla2_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                         int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                         int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kGla2Bf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_gla2_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                            int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                            int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kGla2Fp8, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_merge_lse_width(const float* part_out, const float* part_lse, int32_t num_splits, int32_t batch,
+                        int32_t num_rows, int32_t width, float* out, float* lse, void* stream) {
+  const char* fn = "mla_merge_lse_width";
+  if (width != 256 && width != 512) return fail(MLA_ERR_SHAPE, "%s: width=%d must be 256 or 512", fn, width);
+  if (!part_out) return fail(MLA_ERR_NULL, "%s: part_out is NULL", fn);
+  if (!part_lse) return fail(MLA_ERR_NULL, "%s: part_lse is NULL", fn);
+  if (!out) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
+  if (!lse) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
+  if (num_splits < 1 || num_splits > 65536)
+    return fail(MLA_ERR_SHAPE, "%s: num_splits=%d outside [1, 65536]", fn, num_splits);
+  if (batch < 1) return fail(MLA_ERR_SHAPE, "%s: batch=%d must be >= 1", fn, batch);
+  if (num_rows < 1) return fail(MLA_ERR_SHAPE, "%s: num_rows=%d must be >= 1", fn, num_rows);
+  if ((int64_t)batch * num_rows > 0x7FFFFFFF) return fail(MLA_ERR_SHAPE, "%s: batch * num_rows too large", fn);
+  if (!aligned16(part_out) || !aligned16(out))
+    return fail(MLA_ERR_ALIGN, "%s: part_out and out must be 16-byte aligned", fn);
+  int rc = check_device();
+  if (rc != MLA_OK) return rc;
+  return hip_status(mla::launch_merge(part_out, part_lse, num_splits, batch, num_rows, out, lse,
+                                      static_cast<hipStream_t>(stream), width),
+                    fn);
 }
 
 int mla_merge_lse(const float* part_out, const float* part_lse, int32_t num_splits, int32_t batch,

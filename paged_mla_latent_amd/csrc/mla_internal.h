@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mla_device.h"
+
 namespace mla {
 
 struct DecodeParams {
@@ -28,11 +30,14 @@ hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_nope_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_rank256_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_gla2_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_gla2_fp8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const uint8_t* cache, int fp8, const int32_t* block_table, int64_t bt_stride,
                          const int64_t* cu_rows, const int32_t* seq_starts, int batch, int page_size,
                          int64_t total_rows, uint16_t* out, hipStream_t stream);
 hipError_t launch_merge(const float* part_out, const float* part_lse, int num_splits, int batch,
-                        int heads, float* out, float* lse, hipStream_t stream);
+                        int heads, float* out, float* lse, hipStream_t stream, int width = kLatent);
 hipError_t launch_cache_write(const uint16_t* latent, const uint16_t* k_pe, const int64_t* slots,
                               int num_tokens, uint8_t* cache, int fp8, hipStream_t stream);
 

@@ -79,7 +79,8 @@ def _decode(lib, fn="mla_decode_bf16", **kw):
     return rc, lib.mla_last_error_message().decode()
 
 
-DECODERS = ["mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656"]
+DECODERS = ["mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656",
+            "mla_decode_rank256_bf16", "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656"]
 
 
 @pytest.mark.parametrize("fn", DECODERS)
@@ -126,6 +127,20 @@ def _mtp(lib, fn="mla_decode_mtp_bf16", **kw):
 def test_mtp_rejects_bad_shapes(lib, fn, kw, word):
     rc, msg = _mtp(lib, fn, **kw)
     assert rc == 2 and word in msg and fn in msg
+
+
+@pytest.mark.parametrize("fn", ["mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656"])
+def test_gla2_needs_an_even_head_count(lib, fn):
+    rc, msg = _decode(lib, fn, heads=3)
+    assert rc == 2 and "even" in msg
+
+
+def test_merge_width_validation(lib):
+    f = lib.mla_merge_lse_width
+    assert f(P, P, 2, 1, 4, 384, P, P, None) == 2 and "width" in lib.mla_last_error_message().decode()
+    assert f(None, P, 2, 1, 4, 256, P, P, None) == 1
+    assert f(P, P, 2, 1, 0, 256, P, P, None) == 2
+    assert f(MIS, P, 2, 1, 4, 256, P, P, None) == 3
 
 
 def test_mtp_workspace_counts_query_rows(lib):

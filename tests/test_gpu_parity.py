@@ -398,6 +398,57 @@ def test_gather_full_size_fp8_ragged():
     assert np.array_equal(got, want)
 
 
+# ------------------------------------------------------------- other latent geometries
+GEOM_LENS = [0, 1, 15, 17, 333, 2500]
+
+
+@pytest.mark.parametrize("heads, ps", [(16, 64), (4, 3), (1, 16)])
+def test_rank256_parity(heads, ps):
+    """Rank-256 rows (320 bf16 values) placed on the device as generated; decode vs oracle.decode_rank."""
+    pages = sum(-(-L // ps) for L in GEOM_LENS) + 3
+    w = workloads.make_workload(f"r256_{heads}_{ps}", seq_lens=GEOM_LENS, heads=heads, page_size=ps, num_pages=pages,
+                                seed=100 + heads + ps)
+    rng = np.random.default_rng(heads * 7 + ps)
+    pool = np.full((pages * ps, 320), 0x7FC0, np.uint16)
+    pool[w.slots] = workloads.bf16_bits(rng.standard_normal((w.slots.size, 320)).astype(np.float32))
+    q = workloads.bf16_bits(rng.standard_normal((w.batch, heads, 320)).astype(np.float32))
+    ref_o, ref_l = oracle.decode_rank(q, pool, w.block_table, w.seq_lens, ps, w.scale)
+    pd = bf16_dev(pool).view(pages, ps, 320)
+    bt, lens = torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    for S in (1, 3):
+        out, lse = mla.mla_decode_rank256_bf16(bf16_dev(q), pd, bt, lens, w.scale, num_splits=S)
+        torch.cuda.synchronize()
+        assert_parity(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l,
+                      what=f"rank256 H={heads} ps={ps} S={S}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("heads", [2, 4, 16])
+def test_gla2_parity(fmt, heads):
+    """GLA-g2 on rows written by mla_cache_write; decode vs oracle.decode_gla2, and the
+    256-wide partials merged by mla_merge_lse_width."""
+    ps = 16
+    pages = sum(-(-L // ps) for L in GEOM_LENS) + 3
+    w = workloads.make_workload(f"gla2_{fmt}_{heads}", seq_lens=GEOM_LENS, heads=heads, page_size=ps,
+                                num_pages=pages, fmt=fmt, seed=110 + heads)
+    q = workloads.bf16_bits(np.random.default_rng(heads).standard_normal((w.batch, heads, 320)).astype(np.float32))
+    pd, ph = device_pool(w), host_pool(w)
+    ref_o, ref_l = oracle.decode_gla2(q, ph, w.block_table, w.seq_lens, ps, w.scale, fmt)
+    fn = mla.mla_decode_gla2_bf16 if fmt == "bf16" else mla.mla_decode_gla2_fp8_656
+    bt, lens = torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    for S in (1, 3):
+        out, lse = fn(bf16_dev(q), pd, bt, lens, w.scale, num_splits=S)
+        torch.cuda.synchronize()
+        assert_parity(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l,
+                      what=f"gla2 {fmt} H={heads} S={S}")
+    po, pl = fn(bf16_dev(q), pd, bt, lens, w.scale, num_splits=5, partials_only=True)
+    assert po.shape == (5, w.batch, heads, 256)
+    out, lse = mla.mla_merge_lse_width(po, pl)
+    torch.cuda.synchronize()
+    assert_parity(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l,
+                  what=f"gla2 {fmt} H={heads} partials + merge")
+
+
 # ------------------------------------------------------------------------- NoPE-512
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 @pytest.mark.parametrize("ps", [3, 16, 64])
