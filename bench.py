@@ -44,6 +44,9 @@ def _parse():
     ap.add_argument("--geometry", choices=("mla", "gla2", "rank256"), default="mla",
                     help="gla2: GLA-g2 head groups on the same rows; rank256: a rank-256 layer (640-byte bf16 "
                          "rows made from the workload's rows; no cache write in the step)")
+    ap.add_argument("--balanced", type=int, default=0, metavar="W",
+                    help="batch-balanced decode with W workgroups (tokens cut evenly across requests); "
+                         "the decode time then covers its three kernels (plan, decode, merge)")
     ap.add_argument("--nope", action="store_true",
                     help="decode the workload as a NoPE-512 layer: 512-wide queries, rows written with a zero "
                          "rope part, which the NoPE kernels never read")
@@ -308,6 +311,15 @@ def main():
             decode, write_rows, row_bytes_read = mla.mla_decode_rank256_bf16, False, 640
             kernel = "decode_kernel<Bf16Rows<256, 64>, 1>"
         out = torch.empty((w.batch, rows, width), dtype=torch.float32, device=dev)
+    balanced = args.balanced
+    if balanced:
+        if nope or T > 1 or geom != "mla":
+            raise SystemExit("--balanced is not combined with --nope, --q-len or --geometry by this benchmark")
+        decode_bal = mla.mla_decode_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_fp8_656
+        ws = torch.empty(mla.mla_decode_balanced_workspace_size(w.batch, rows, balanced), dtype=torch.uint8,
+                         device=dev)
+        S = 1
+        kernel = f"decode_flat_kernel<{'Bf16Rows<512, 64>' if w.fmt == 'bf16' else 'Fp8Rows<64>'}>"
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -318,7 +330,10 @@ def main():
         if write_rows:
             mla.mla_cache_write(new_lat, new_pe, new_slots, pool, fmt)
         if e: e[1].record(stream)
-        if S > 1:
+        if balanced:
+            decode_bal(q, pool, bt, lens, w.scale, num_workgroups=balanced, out=out, lse=lse, workspace=ws)
+            if e: e[2].record(stream)
+        elif S > 1:
             po, pl = decode(q, pool, bt, lens, w.scale, num_splits=S, workspace=ws, partials_only=True)
             if e: e[2].record(stream)
             if width == 512:
@@ -401,6 +416,7 @@ def main():
         "config": {
             "workload": w.name, "batch": w.batch, "heads": w.heads, "context_tokens": w.tokens,
             "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
+            "schedule": f"batch-balanced, {balanced} workgroups" if balanced else "per-request partitions",
             "layer": "nope-512" if nope else "rope-576", "query_tokens_per_request": T, "geometry": geom,
             "cache_row_bytes": 640 if geom == "rank256" else w.row_bytes, "row_bytes_read": row_bytes_read,
             "step": "decode + merge" if not write_rows else "cache write + decode + merge",
@@ -416,7 +432,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None if (nope or T > 1 or geom != "mla") else _profiled_traffic(w.name),
+            "traffic": None if (nope or T > 1 or geom != "mla" or balanced) else _profiled_traffic(w.name),
         },
     }
     if not args.no_cpu_baseline:

@@ -68,7 +68,7 @@ enum {
 };
 
 enum { MLA_LATENT = 512, MLA_ROPE = 64, MLA_ROW = 576, MLA_MAX_HEADS = 16, MLA_MAX_Q_LEN = 16,
-       MLA_MAX_QUERY_ROWS = 64 };
+       MLA_MAX_QUERY_ROWS = 64, MLA_MAX_BALANCED_BATCH = 1024 };
 
 /* Bytes of workspace mla_decode_bf16 / mla_decode_fp8_656 need for num_splits
  * partitions: num_splits * batch * num_heads * (512 + 1) * 4 rounded up to 256,
@@ -122,6 +122,39 @@ MLA_API int mla_decode_fp8_656(const void* q, const void* kv_cache, int64_t num_
                        int32_t page_size, float softmax_scale, int32_t num_splits,
                        float* out, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Batch-balanced decode: the same results as mla_decode_bf16 / mla_decode_fp8_656
+ * (single-token queries), with the work cut across the whole batch instead of per
+ * request.  The split-KV partition with log-sum-exp merge (vLLM pull request 55543: the
+ * partial-result merge contract) is applied to the batch's concatenated context: the
+ * requests' tokens, request after request, each non-empty request preceded by a fixed
+ * allowance for the start-up of a segment, are cut into num_workgroups equal ranges (fewer
+ * when the batch is smaller); a workgroup decodes every request segment its range meets
+ * into a partial (out, lse), and a merge kernel combines each request's partials.  Every
+ * workgroup gets the same cost whatever the length mix, so a ragged batch finishes in one
+ * balanced wave instead of a tail of long requests.  Two launches, no host synchronisation.
+ *
+ * batch           1..MLA_MAX_BALANCED_BATCH (1024).
+ * num_workgroups  1..65535; one per compute unit (256 on MI355X) is the intended use.
+ * workspace       device scratch of at least mla_decode_balanced_workspace_size(batch,
+ *                 num_heads, num_workgroups) bytes, 16-byte aligned: int64 range
+ *                 bounds [batch + 1], then up to batch + num_workgroups - 1 partials.
+ * The decode reads seq_lens on the device (no host synchronisation); a request with
+ * seq_lens == 0 gets (+0.0, -inf).  Every other argument, result and error as
+ * mla_decode_bf16 / mla_decode_fp8_656. */
+MLA_API size_t mla_decode_balanced_workspace_size(int32_t batch, int32_t num_heads, int32_t num_workgroups);
+MLA_API int mla_decode_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                                     const int32_t* block_table, int64_t block_table_stride,
+                                     const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                     int32_t page_size, float softmax_scale, int32_t num_workgroups,
+                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+MLA_API int mla_decode_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                                        const int32_t* block_table, int64_t block_table_stride,
+                                        const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                        int32_t page_size, float softmax_scale, int32_t num_workgroups,
+                                        float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /* NoPE-512 decode: layers without a rotary part (vLLM pull request 55543, description
  * of the NoPE-512 change: such layers keep the 576-value / 656-byte row, store zeros in

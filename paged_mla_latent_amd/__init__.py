@@ -12,11 +12,13 @@ Entry points (same names as the C ABI in include/mla.h):
     mla_decode_mtp_bf16 / mla_decode_mtp_fp8_656(q [B, q_len, H, 576], ...)   verify step
     mla_decode_rank256_bf16(q [B, H, 320], kv_cache [pages, ps, 320], ...)   rank-256 layer
     mla_decode_gla2_bf16 / mla_decode_gla2_fp8_656(q [B, H, 320], ...)   GLA-g2 head groups
+    mla_decode_balanced_bf16 / mla_decode_balanced_fp8_656(..., num_workgroups=256)   ragged batches
     mla_merge_lse_width(part_out, part_lse, out=None, lse=None)   256- or 512-wide partials
     mla_merge_lse(part_out, part_lse, out=None, lse=None)
     mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format)   k_pe None: zero rope
     mla_gather_context(kv_cache, cache_format, block_table, cu_rows, total_rows, seq_starts=None)
     mla_decode_workspace_size(batch, num_heads, num_splits)
+    mla_decode_balanced_workspace_size(batch, num_heads, num_workgroups)
 
 Tensors: q bf16 [B, H, 576]; kv_cache bf16 [num_pages, page_size, 576] or uint8
 [num_pages, page_size, 656]; block_table int32 [B, W]; seq_lens int32 [B];
@@ -40,12 +42,14 @@ ROW_BYTES = {MLA_CACHE_BF16_576: 1152, MLA_CACHE_FP8_656: 656}
 MAX_HEADS = 16
 MAX_Q_LEN = 16
 MAX_QUERY_ROWS = 64
+MLA_MAX_BALANCED_BATCH = 1024
 
 EXPORTED = (
     "mla_decode_workspace_size", "mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16",
     "mla_decode_nope_fp8_656", "mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656", "mla_decode_rank256_bf16",
     "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656", "mla_merge_lse", "mla_merge_lse_width",
     "mla_cache_write", "mla_gather_context", "mla_status_string", "mla_last_error_message", "mla_abi_version",
+    "mla_decode_balanced_workspace_size", "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
 )
 
 
@@ -72,9 +76,12 @@ def library() -> ctypes.CDLL:
                                            ctypes.c_float, ctypes.c_void_p)
     lib.mla_decode_workspace_size.argtypes = [c_i32, c_i32, c_i32]
     lib.mla_decode_workspace_size.restype = c_sz
+    lib.mla_decode_balanced_workspace_size.argtypes = [c_i32, c_i32, c_i32]
+    lib.mla_decode_balanced_workspace_size.restype = c_sz
     dec = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
     for name in ("mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656",
-                 "mla_decode_rank256_bf16", "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656"):
+                 "mla_decode_rank256_bf16", "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656",
+                 "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = c_int
     mtp = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
@@ -205,6 +212,57 @@ def mla_decode_nope_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, n
     """NoPE-512 decode over an fp8 cache: q [B, H, 512]; the rows' rope bytes are never read."""
     return _decode("mla_decode_nope_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
                    softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=LATENT)
+
+
+def mla_decode_balanced_workspace_size(batch: int, num_heads: int, num_workgroups: int) -> int:
+    return int(library().mla_decode_balanced_workspace_size(batch, num_heads, num_workgroups))
+
+
+def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
+                     softmax_scale, num_workgroups, out, lse, workspace):
+    lib = library()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(kv_cache, "kv_cache", cache_dtype, 3, dev)
+    if kv_cache.shape[2] != row_bytes_last:
+        raise ValueError(f"kv_cache rows must have {row_bytes_last} elements, got {kv_cache.shape[2]}")
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, H, D = q.shape
+    if D != ROW:
+        raise ValueError(f"q rows must have {ROW} values, got {D}")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have one row per request")
+    if out is None:
+        out = torch.empty((B, H, LATENT), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    if workspace is None:
+        need = mla_decode_balanced_workspace_size(B, H, num_workgroups)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    status = getattr(lib, fn)(
+        q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1],
+        seq_lens.data_ptr(), B, H, kv_cache.shape[1], float(softmax_scale), int(num_workgroups),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(fn, status)
+    return out, lse
+
+
+def mla_decode_balanced_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256, out=None,
+                             lse=None, workspace=None):
+    """Batch-balanced decode over a bf16 cache (B <= 1024): the batch's tokens cut into
+    num_workgroups equal-cost ranges across request boundaries; returns (out [B,H,512], lse [B,H])."""
+    return _decode_balanced("mla_decode_balanced_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
+                            softmax_scale, num_workgroups, out, lse, workspace)
+
+
+def mla_decode_balanced_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256, out=None,
+                                lse=None, workspace=None):
+    """Batch-balanced decode over an fp8 cache uint8 [num_pages, page_size, 656]."""
+    return _decode_balanced("mla_decode_balanced_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
+                            softmax_scale, num_workgroups, out, lse, workspace)
 
 
 def _decode_mtp(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,

@@ -147,7 +147,7 @@ struct Fp8Rows {
   static constexpr int kFullOps = kRopeDim ? 10 : 8;    // instructions of 4 whole chunks
   static constexpr int kLastChunk = kRopeDim ? 40 : 32;  // fetched alone by the last one
   static constexpr int kDmaOps = kFullOps + 1;
-  static constexpr int kBufs = 2;  // two tiles per wave (2 x 4 x 11 KB)
+  static constexpr int kBufs = 3;  // three tiles per wave with one row group (3 x 4 x 11 KB)
   static constexpr int kTileBytes = kDmaOps * 1024;  // used bytes + padding
   static constexpr int kAcc = 32;
 
@@ -272,25 +272,20 @@ constexpr int smem_bytes() {
 // latent, rope), scattered into a 576-wide fragment that is zero outside the group, and
 // the output of each head is its group's 256 columns.  The row is read once for both
 // groups; the MFMA work is that of the 576-wide decode.
-template <class Fmt, int G, bool kGla2 = false>
-__global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) {
+template <class Fmt, int G, bool kGla2>
+__device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* smem, int b, int64_t L,
+                                               int64_t t0_abs, int64_t t1_abs, float* out, float* lse) {
   static_assert(G == 1 || G == 2 || G == 4, "row groups per workgroup");
   static_assert(!kGla2 || (Fmt::kLatent == 512 && Fmt::kQDim == 576), "GLA-g2 on the 576-value row");
   constexpr int kOut = kGla2 ? 256 : Fmt::kLatent;  // output values per query row
-  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
-
-  // Partition-major grid: all requests' first partitions are dispatched first, then the
-  // second ones, ...; with equal-size partitions the empty tails of short requests come
-  // last and full partitions spread evenly over the compute units.
-  const int b = blockIdx.x;
-  const int s = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int m = lane & 15;
   const int g = lane >> 4;
 
-  const int64_t L = p.seq_lens[b];
-  const Range rg = partition(L, p.page_size, p.num_splits, s, p.bt_stride);
+  // Tokens [t0_abs, t1_abs) of request b, whose context holds L tokens (a partition of it,
+  // or a segment of a workgroup's share of the batch).
+  const Range rg = {t0_abs, t1_abs};
   const int n = (int)(rg.t1 - rg.t0);
   const int ntiles = (n + kTile - 1) / kTile;
 
@@ -337,7 +332,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
   const uint32_t ps = (uint32_t)p.page_size;
   const int my_tok = Fmt::dma_token(lane);
-  uint8_t* wbuf = smem + wave * Fmt::kBufs * Fmt::kTileBytes;
+  // Tile buffers per wave: Fmt::kBufs for one row group; the shared-tile loop of G > 1 is
+  // written for two.
+  constexpr int NB = G == 1 ? Fmt::kBufs : 2;
+  uint8_t* wbuf = smem + wave * NB * Fmt::kTileBytes;
   const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds_offset(wbuf));
 
   // Token this lane fetches in tile k, clamped into the partition (ragged tail).
@@ -351,7 +349,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   // Page ids travel HBM -> LDS by DMA as well (one 4-byte entry per lane, lane l's own
   // token), well ahead of use, so that no compiler-visible load sits in the loop: the
   // only vector-memory operations are these DMAs, whose completion is counted by hand.
-  uint8_t* pslot = smem + kWaves * Fmt::kBufs * Fmt::kTileBytes + wave * Fmt::kBufs * 256;
+  uint8_t* pslot = smem + kWaves * NB * Fmt::kTileBytes + wave * NB * 256;
   const uint32_t plds = __builtin_amdgcn_readfirstlane(lds_offset(pslot));
   auto fetch_page = [&](int k, uint32_t slot) {
     const uint32_t pi = lane_token(k) / ps;
@@ -401,7 +399,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
     Fmt::pv(buf, m, g, pr, aux, O);
   };
 
-  constexpr int NB = Fmt::kBufs;
   constexpr int D = Fmt::kDmaOps;
   int k = wave;
   // The first NB-1 tiles' page ids are ordinary loads issued with the q loads; all are
@@ -494,10 +491,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   }
   __syncthreads();
 
-  const bool split = p.num_splits > 1;
-  const int64_t row_b = (int64_t)b * R;
-  float* out = split ? p.part_out + ((int64_t)s * p.batch * R + row_b) * kOut : p.out + row_b * kOut;
-  float* lse = split ? p.part_lse + (int64_t)s * p.batch * R + row_b : p.lse + row_b;
+  // out / lse: this segment's R rows ([R][kOut] and [R]).
   for (int idx = threadIdx.x; idx < R * (kOut / 4); idx += kWaves * 64) {
     const int r = idx / (kOut / 4);
     const int d4 = idx % (kOut / 4);
@@ -527,6 +521,108 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
     }
     *(f32x4*)(out + (int64_t)r * kOut + 4 * d4) = o;
     if (d4 == 0) lse[r] = (M == -INFINITY) ? -INFINITY + lsum : (M + fast_log2(lsum)) * 0.69314718055994530942f;
+  }
+}
+
+// Per-request partitions: grid (request, partition), partition-major so that all requests'
+// first partitions are dispatched first, then the second ones, ...; with equal-size
+// partitions the empty tails of short requests come last and full partitions spread evenly
+// over the compute units.
+template <class Fmt, int G, bool kGla2 = false>
+__global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
+  constexpr int kOut = kGla2 ? 256 : Fmt::kLatent;
+  const int b = blockIdx.x;
+  const int s = blockIdx.y;
+  const int64_t L = p.seq_lens[b];
+  const Range rg = partition(L, p.page_size, p.num_splits, s, p.bt_stride);
+  const int R = p.q_len * p.heads;
+  const int64_t row_b = (int64_t)b * R;
+  const bool split = p.num_splits > 1;
+  float* out = split ? p.part_out + ((int64_t)s * p.batch * R + row_b) * kOut : p.out + row_b * kOut;
+  float* lse = split ? p.part_lse + (int64_t)s * p.batch * R + row_b : p.lse + row_b;
+  decode_segment<Fmt, G, kGla2>(p, smem, b, L, rg.t0, rg.t1, out, lse);
+}
+
+// Batch-balanced decode.  The batch's requests are laid end to end on a cost axis: request
+// b occupies [v[b], v[b + 1]) with v[b + 1] - v[b] = kSegmentCost + L_b for L_b > 0 (0 for
+// an empty request), its tokens at the last L_b positions; the first kSegmentCost stand
+// for the start-up of a segment (first loads in flight, epilogue), measured at about as
+// long as streaming that many rows.  The axis, of length V = v[B], is cut into W =
+// min(gridDim.x, V) equal ranges [floor(wV/W), floor((w+1)V/W)); workgroup w decodes the
+// tokens of every request its range meets (possibly none, when the range lies in a
+// request's start-up part) into partial slot b + w (unique: along the axis, b or w grows at
+// every segment start), so request b's partials are the slots b + w_first(b) .. b +
+// w_last(b), at most B + W - 1 slots in all.  Every workgroup scans seq_lens into v itself
+// (no planning launch, no dependent global reads before its first tile); workgroup 0 also
+// stores v for the merge.
+template <class Fmt>
+__global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
+  __shared__ int64_t v_s[kMaxBalancedBatch + 1];
+  const int B = p.batch;
+  {
+    // Thread t sums the costs of requests 4t .. 4t + 3; the 256 sums are scanned with wave
+    // shuffles and a pass over the four wave totals.
+    constexpr int kPer = kMaxBalancedBatch / (kWaves * 64);
+    const int t = threadIdx.x;
+    int64_t c[kPer];
+    int64_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int b = kPer * t + i;
+      const int64_t L = b < B ? (int64_t)p.seq_lens[b] : 0;
+      c[i] = L > 0 ? L + kSegmentCost : 0;
+      sum += c[i];
+    }
+    int64_t incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t o = __shfl_up(incl, d, 64);
+      if ((t & 63) >= d) incl += o;
+    }
+    int64_t* wave_tot = (int64_t*)smem;
+    if ((t & 63) == 63) wave_tot[t >> 6] = incl;
+    __syncthreads();
+    int64_t run = incl - sum;
+    for (int w = 0; w < (t >> 6); ++w) run += wave_tot[w];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int b = kPer * t + i;
+      if (b < B) {
+        run += c[i];
+        v_s[b + 1] = run;
+      }
+    }
+    if (t == 0) v_s[0] = 0;
+    __syncthreads();
+  }
+  if (blockIdx.x == 0)
+    for (int b = threadIdx.x; b <= B; b += kWaves * 64) p.cu[b] = v_s[b];
+
+  const int64_t V = v_s[B];
+  const int64_t W = min((int64_t)gridDim.x, V);
+  const int64_t w = blockIdx.x;
+  if (w >= W) return;
+  const int64_t lo = flat_begin(V, W, w), hi = flat_begin(V, W, w + 1);
+  int bl = 0, bh = B;  // v[bl] <= lo < v[bh]
+  while (bh - bl > 1) {
+    const int mid = (bl + bh) >> 1;
+    if (v_s[mid] <= lo) bl = mid; else bh = mid;
+  }
+  const int H = p.heads;
+  for (int b = bl; b < B; ++b) {
+    const int64_t v0 = v_s[b], v1 = v_s[b + 1];
+    if (v0 >= hi) break;
+    if (v1 <= lo || v1 == v0) continue;  // empty requests have no partial
+    const int64_t s0 = v0 + kSegmentCost;  // axis position of token 0
+    const int64_t L = v1 - s0;
+    const int64_t t0 = max(lo, s0) - s0;
+    const int64_t t1 = max(min(hi, v1) - s0, (int64_t)0);  // 0: the range holds start-up only
+    const int64_t slot = (int64_t)b + w;
+    decode_segment<Fmt, 1, false>(p, smem, b, L, t0, max(t0, t1), p.part_out + slot * H * kLatent,
+                                  p.part_lse + slot * H);
+    __syncthreads();  // the epilogue's LDS reads finish before the next segment's loads land
   }
 }
 
@@ -566,6 +662,16 @@ hipError_t launch_decode_gla2_bf16(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_decode_gla2_fp8(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<Fp8Rows<64>, 1, true>), dim3((unsigned)p.batch, (unsigned)p.num_splits),
                      dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+hipError_t launch_decode_flat_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_flat_kernel<Bf16Rows<512, 64>>), dim3((unsigned)num_workgroups), dim3(kWaves * 64), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+hipError_t launch_decode_flat_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_flat_kernel<Fp8Rows<64>>, dim3((unsigned)num_workgroups), dim3(kWaves * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream) {

@@ -17,19 +17,15 @@ namespace {
 constexpr int kGroups = 8;    // partial streams per workgroup
 constexpr int kCols = 32;     // float4 columns per workgroup (128 output values)
 
-// grid = (batch * heads, width / 128): workgroup (bh, y) merges columns [128y, 128y + 128)
-// of row bh (width = 512 for the latent rows, 256 for the rank-256 / GLA-g2 outputs).
-// Lane t owns float4 column t % 32 and partials p = t / 32, t / 32 + 8, ...; the eight
-// partial streams are then summed through LDS.
-__global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __restrict__ part_out,
-                                                               const float* __restrict__ part_lse, int S,
-                                                               int64_t rows, int width, float* __restrict__ out,
-                                                               float* __restrict__ lse) {
+// Merges the `count` partials of one output row (row bh of `out`), partial i at row
+// base + i * stride of part_out / part_lse.
+__device__ __forceinline__ void merge_row(const float* __restrict__ part_out, const float* __restrict__ part_lse,
+                                          int count, int64_t base, int64_t stride, int width, int64_t bh,
+                                          float* __restrict__ out, float* __restrict__ lse) {
   __shared__ f32x4 acc_s[kGroups][kCols];
   __shared__ float w_s[kGroups];
   __shared__ float m_s[kGroups * kCols / 64];
   __shared__ float n_s[kGroups * kCols / 64];
-  const int64_t bh = blockIdx.x;
   const int col = blockIdx.y * kCols + (threadIdx.x % kCols);
   const int grp = threadIdx.x / kCols;
   // M = max_p lse_p: every lane loads a strided share (independent loads), then a
@@ -37,8 +33,8 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __r
   // fmaxf skips NaN, so NaN partials are counted apart and force M = NaN.
   float M = -INFINITY;
   float nan = 0.f;
-  for (int p = threadIdx.x; p < S; p += kGroups * kCols) {
-    const float x = part_lse[p * rows + bh];
+  for (int p = threadIdx.x; p < count; p += kGroups * kCols) {
+    const float x = part_lse[base + p * stride];
     M = fmaxf(M, x);
     nan = (x != x) ? 1.f : nan;
   }
@@ -61,12 +57,12 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __r
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
   if (M != -INFINITY) {
-    const float* src = part_out + bh * width + 4 * col;
+    const float* src = part_out + base * width + 4 * col;
 #pragma unroll 4
-    for (int p = grp; p < S; p += kGroups) {
-      const float w = __expf(part_lse[p * rows + bh] - M);
+    for (int p = grp; p < count; p += kGroups) {
+      const float w = __expf(part_lse[base + p * stride] - M);
       W += w;
-      acc += w * *(const f32x4*)(src + (int64_t)p * rows * width);
+      acc += w * *(const f32x4*)(src + (int64_t)p * stride * width);
     }
   }
   acc_s[grp][threadIdx.x % kCols] = acc;
@@ -85,7 +81,53 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __r
   if (blockIdx.y == 0 && threadIdx.x == 0) lse[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(W);
 }
 
+// grid = (batch * heads, width / 128): workgroup (bh, y) merges columns [128y, 128y + 128)
+// of row bh (width = 512 for the latent rows, 256 for the rank-256 / GLA-g2 outputs).
+// Lane t owns float4 column t % 32 and partials p = t / 32, t / 32 + 8, ...; the eight
+// partial streams are then summed through LDS.  Partial p of row bh: row p * rows + bh.
+__global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __restrict__ part_out,
+                                                               const float* __restrict__ part_lse, int S,
+                                                               int64_t rows, int width, float* __restrict__ out,
+                                                               float* __restrict__ lse) {
+  const int64_t bh = blockIdx.x;
+  merge_row(part_out, part_lse, S, bh, rows, width, bh, out, lse);
+}
+
+// Batch-balanced mode: request b's partials are the slots b + w for the workgroups w whose
+// cost-axis ranges meet [cu[b], cu[b + 1]) (the axis the decode stored); head h of slot q
+// is row q * heads + h.
+__global__ __launch_bounds__(kGroups * kCols) void merge_flat_kernel(const float* __restrict__ part_out,
+                                                                    const float* __restrict__ part_lse,
+                                                                    const int64_t* __restrict__ cu, int heads,
+                                                                    int num_workgroups, float* __restrict__ out,
+                                                                    float* __restrict__ lse) {
+  const int64_t bh = blockIdx.x;
+  const int b = (int)(bh / heads), h = (int)(bh % heads);
+  const int64_t N = cu[gridDim.x / heads], c0 = cu[b], c1 = cu[b + 1];
+  const int64_t W = min((int64_t)num_workgroups, N);  // the workgroups that took part
+  int count = 0;
+  int64_t first = 0;
+  if (c1 > c0) {
+    // The workgroup whose range holds axis position x < N: the largest w with
+    // floor(w N / W) <= x, i.e. w N < (x + 1) W, i.e. w = floor(((x + 1) W - 1) / N).
+    // (x + 1) W < 2^41 * 2^16 fits in 64 bits.
+    auto owner = [&](int64_t x) -> int64_t { return ((x + 1) * W - 1) / N; };
+    const int64_t w0 = owner(c0), w1 = owner(c1 - 1);
+    first = ((int64_t)b + w0) * heads + h;
+    count = (int)(w1 - w0 + 1);
+  }
+  merge_row(part_out, part_lse, count, first, heads, kLatent, bh, out, lse);
+}
+
 }  // namespace
+
+hipError_t launch_merge_flat(const float* part_out, const float* part_lse, const int64_t* cu, int batch, int heads,
+                             int num_workgroups, float* out, float* lse, hipStream_t stream) {
+  const int64_t rows = (int64_t)batch * heads;
+  hipLaunchKernelGGL(merge_flat_kernel, dim3((unsigned)rows, (unsigned)(kLatent / (4 * kCols))),
+                     dim3(kGroups * kCols), 0, stream, part_out, part_lse, cu, heads, num_workgroups, out, lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const float* part_out, const float* part_lse, int num_splits, int batch,
                         int heads, float* out, float* lse, hipStream_t stream, int width) {

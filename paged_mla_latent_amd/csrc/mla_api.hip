@@ -134,6 +134,7 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
   p.lse = lse;
   p.part_out = part_out;
   p.part_lse = part_lse;
+  p.cu = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t launched;
   switch (kind) {
@@ -151,9 +152,104 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
                     "mla_merge_lse (after decode)");
 }
 
+// Batch-balanced workspace: int64 prefix sums [batch + 1] (padded to 256 bytes), then
+// batch + W - 1 partial slots of [heads][512] fp32 and their [heads] lse.
+size_t balanced_cu_bytes(int64_t batch) { return ((size_t)(batch + 1) * sizeof(int64_t) + 255) & ~(size_t)255; }
+size_t balanced_bytes_for(int64_t batch, int64_t heads, int64_t workgroups) {
+  const size_t slots = (size_t)(batch + workgroups - 1);
+  const size_t bytes = balanced_cu_bytes(batch) + slots * (size_t)heads * (MLA_LATENT + 1) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int decode_balanced(bool fp8, const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                    int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                    int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = fp8 ? "mla_decode_balanced_fp8_656" : "mla_decode_balanced_bf16";
+  if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
+  if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
+  if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
+  if (!seq_lens) return fail(MLA_ERR_NULL, "%s: seq_lens is NULL", fn);
+  if (!out) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
+  if (!lse) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
+  if (batch < 1 || batch > MLA_MAX_BALANCED_BATCH)
+    return fail(MLA_ERR_SHAPE, "%s: batch=%d outside [1, %d]", fn, batch, MLA_MAX_BALANCED_BATCH);
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
+    return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_HEADS);
+  if (page_size < 1) return fail(MLA_ERR_SHAPE, "%s: page_size=%d must be >= 1", fn, page_size);
+  if (num_pages < 1) return fail(MLA_ERR_SHAPE, "%s: num_pages=%lld must be >= 1", fn, (long long)num_pages);
+  if (block_table_stride < 1)
+    return fail(MLA_ERR_SHAPE, "%s: block_table_stride=%lld must be >= 1", fn, (long long)block_table_stride);
+  if (block_table_stride > ((int64_t)1 << 31) / page_size + 1)
+    return fail(MLA_ERR_SHAPE, "%s: block_table_stride * page_size exceeds the int32 token range", fn);
+  if (num_workgroups < 1 || num_workgroups > 65535)
+    return fail(MLA_ERR_SHAPE, "%s: num_workgroups=%d outside [1, 65535]", fn, num_workgroups);
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_SHAPE, "%s: softmax_scale is not finite", fn);
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(block_table) || !aligned16(seq_lens) ||
+      !aligned16(out) || !aligned16(lse))
+    return fail(MLA_ERR_ALIGN, "%s: every tensor pointer must be 16-byte aligned", fn);
+  const size_t need = balanced_bytes_for(batch, num_heads, num_workgroups);
+  if (!workspace) return fail(MLA_ERR_WORKSPACE, "%s: a workspace is required", fn);
+  if (!aligned16(workspace)) return fail(MLA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
+  int rc = check_device();
+  if (rc != MLA_OK) return rc;
+
+  int64_t* cu = static_cast<int64_t*>(workspace);
+  float* part_out = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + balanced_cu_bytes(batch));
+  float* part_lse = part_out + (size_t)(batch + num_workgroups - 1) * num_heads * MLA_LATENT;
+  mla::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.cache = static_cast<const uint8_t*>(kv_cache);
+  p.block_table = block_table;
+  p.bt_stride = block_table_stride;
+  p.seq_lens = seq_lens;
+  p.batch = batch;
+  p.heads = num_heads;
+  p.q_len = 1;
+  p.page_size = page_size;
+  p.num_splits = 1;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  p.out = nullptr;
+  p.lse = nullptr;
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.cu = cu;
+  static_assert(MLA_MAX_BALANCED_BATCH == mla::kMaxBalancedBatch, "batch limit of the balanced kernels");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = hip_status(fp8 ? mla::launch_decode_flat_fp8(p, num_workgroups, s)
+                      : mla::launch_decode_flat_bf16(p, num_workgroups, s),
+                  fn);
+  if (rc != MLA_OK) return rc;
+  return hip_status(mla::launch_merge_flat(part_out, part_lse, cu, batch, num_heads, num_workgroups, out, lse, s),
+                    "mla_merge_lse (after balanced decode)");
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mla_decode_balanced_workspace_size(int32_t batch, int32_t num_heads, int32_t num_workgroups) {
+  if (batch < 1 || num_heads < 1 || num_workgroups < 1) return 0;
+  return balanced_bytes_for(batch, num_heads, num_workgroups);
+}
+
+int mla_decode_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                             int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                             int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_balanced(false, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+                         page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                                int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
+                                int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups,
+                                float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_balanced(true, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+                         page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes, stream);
+}
 
 size_t mla_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t num_splits) {
   if (batch < 1 || num_heads < 1 || num_splits < 1) return 0;

@@ -24,7 +24,17 @@ struct DecodeParams {
   float* lse;                  // [B][q_len][H]
   float* part_out;             // [S][B][q_len][H][512] (num_splits > 1)
   float* part_lse;             // [S][B][q_len][H]
+  int64_t* cu;                 // batch-balanced mode: cost-axis starts v [B + 1], stored by the decode
 };
+
+// Batch-balanced mode: at most kMaxBalancedBatch requests; each non-empty request adds
+// kSegmentCost positions to the cost axis, and workgroup w of W takes axis positions
+// [flat_begin(V, W, w), flat_begin(V, W, w + 1)), V = the axis length.
+constexpr int kMaxBalancedBatch = 1024;
+constexpr int64_t kSegmentCost = 256;
+__device__ __forceinline__ int64_t flat_begin(int64_t N, int64_t W, int64_t w) {
+  return (N / W) * w + ((N % W) * w) / W;  // floor(w N / W) without 64-bit overflow
+}
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream);
@@ -33,6 +43,10 @@ hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_rank256_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_gla2_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_gla2_fp8(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_flat_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream);
+hipError_t launch_decode_flat_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream);
+hipError_t launch_merge_flat(const float* part_out, const float* part_lse, const int64_t* cu, int batch, int heads,
+                             int num_workgroups, float* out, float* lse, hipStream_t stream);
 hipError_t launch_gather(const uint8_t* cache, int fp8, const int32_t* block_table, int64_t bt_stride,
                          const int64_t* cu_rows, const int32_t* seq_starts, int batch, int page_size,
                          int64_t total_rows, uint16_t* out, hipStream_t stream);

@@ -71,14 +71,20 @@ def assert_rows_bitexact(w, pool_dev: torch.Tensor, pool_host: np.ndarray, slots
     assert bad.size == 0, f"{bad.size} rows differ, first slot {slots[bad[0]]}"
 
 
-def gpu_decode(w, pool: torch.Tensor, splits: int, q=None, nope=False):
-    """Decode on the device; nope=True uses the NoPE-512 kernels with the first 512 q values."""
+def gpu_decode(w, pool: torch.Tensor, splits: int, q=None, nope=False, balanced=False):
+    """Decode on the device; nope=True uses the NoPE-512 kernels with the first 512 q values;
+    balanced=True uses the batch-balanced kernels with `splits` workgroups."""
     q = w.q if q is None else q
     if nope:
         q = np.ascontiguousarray(q[:, :, :512])
     q = bf16_dev(q)
     bt = torch.from_numpy(w.block_table).cuda()
     lens = torch.from_numpy(w.seq_lens).cuda()
+    if balanced:
+        fn = mla.mla_decode_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_fp8_656
+        out, lse = fn(q, pool, bt, lens, w.scale, num_workgroups=splits)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
     if nope:
         fn = mla.mla_decode_nope_bf16 if w.fmt == "bf16" else mla.mla_decode_nope_fp8_656
     else:

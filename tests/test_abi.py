@@ -103,6 +103,44 @@ def test_decode_rejects_bad_shapes(lib, fn, kw, word):
     assert rc == 2 and word in msg
 
 
+BALANCED = ["mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656"]
+
+
+@pytest.mark.parametrize("fn", BALANCED)
+@pytest.mark.parametrize("field", ["q", "kv", "bt", "lens", "out", "lse"])
+def test_balanced_rejects_null(lib, fn, field):
+    rc, msg = _decode(lib, fn, ws=P, ws_bytes=1 << 30, **{field: None})
+    assert rc == 1 and "NULL" in msg and fn in msg
+
+
+@pytest.mark.parametrize("fn", BALANCED)
+@pytest.mark.parametrize("kw, word", [
+    (dict(heads=0), "num_heads"), (dict(heads=17), "num_heads"), (dict(batch=0), "batch"),
+    (dict(batch=1025), "batch"), (dict(ps=0), "page_size"), (dict(num_pages=0), "num_pages"),
+    (dict(stride=0), "block_table_stride"), (dict(splits=0), "num_workgroups"),
+    (dict(splits=70000), "num_workgroups"), (dict(scale=float("nan")), "softmax_scale"),
+    (dict(stride=1 << 40), "int32"),
+])
+def test_balanced_rejects_bad_shapes(lib, fn, kw, word):
+    rc, msg = _decode(lib, fn, ws=P, ws_bytes=1 << 30, **kw)
+    assert rc == 2 and word in msg
+
+
+@pytest.mark.parametrize("fn", BALANCED)
+def test_balanced_workspace(lib, fn):
+    need = mla.mla_decode_balanced_workspace_size(2, 16, 512)
+    # prefix sums [3] padded to 256 bytes, then 2 + 512 - 1 slots of 16 x 513 floats
+    assert need == (256 + 513 * 16 * 513 * 4 + 255) // 256 * 256
+    assert mla.mla_decode_balanced_workspace_size(0, 16, 4) == 0
+    assert mla.mla_decode_balanced_workspace_size(2, 16, 0) == 0
+    rc, msg = _decode(lib, fn, splits=512)
+    assert rc == 4 and "workspace" in msg
+    rc, msg = _decode(lib, fn, splits=512, ws=P, ws_bytes=need - 1)
+    assert rc == 4 and str(need) in msg
+    rc, msg = _decode(lib, fn, splits=512, ws=MIS, ws_bytes=need)
+    assert rc == 3 and "aligned" in msg
+
+
 @pytest.mark.parametrize("field", ["q", "kv", "bt", "lens", "out", "lse"])
 def test_decode_rejects_misaligned(lib, field):
     rc, msg = _decode(lib, **{field: MIS})

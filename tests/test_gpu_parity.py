@@ -31,9 +31,9 @@ def _device():
     torch.cuda.synchronize()
 
 
-def _run_case(w, splits_list, requests=None, what=""):
+def _run_case(w, splits_list, requests=None, what="", balanced=()):
     say(f"case {what or w.name}: fmt={w.fmt} B={w.batch} H={w.heads} ps={w.page_size} "
-        f"pages={w.num_pages} tokens={w.tokens} splits={splits_list}")
+        f"pages={w.num_pages} tokens={w.tokens} splits={splits_list} balanced={list(balanced)}")
     pd = device_pool(w)
     ph = host_pool(w)
     assert_rows_bitexact(w, pd, ph)
@@ -42,6 +42,9 @@ def _run_case(w, splits_list, requests=None, what=""):
     for S in splits_list:
         out, lse = gpu_decode(w, pd, S)
         assert_parity(w, out, lse, ref_o, ref_l, requests, what=f"{what or w.name} S={S}")
+    for W in balanced:
+        out, lse = gpu_decode(w, pd, W, balanced=True)
+        assert_parity(w, out, lse, ref_o, ref_l, requests, what=f"{what or w.name} balanced W={W}")
     return pd, ph
 
 
@@ -226,6 +229,68 @@ def _sample(w, n=4):
     picks = {0, w.batch // 2, w.batch - 1}
     picks.update(rng.choice(w.batch, size=min(n, w.batch), replace=False).tolist())
     return sorted(picks)
+
+
+# ------------------------------------------------------------------- batch-balanced mode
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("ps", [1, 3, 16, 64])
+def test_balanced_ragged(fmt, ps):
+    """Workgroup ranges cut requests mid-page and mid-tile, cover several requests, or hold a
+    single token (W close to or above the token count)."""
+    pages = sum(-(-L // ps) for L in RAGGED) + 7
+    w = workloads.make_workload(f"bal_ps{ps}", seq_lens=RAGGED, heads=16, page_size=ps, num_pages=pages,
+                                fmt=fmt, seed=40 + ps)
+    # cost axis: 3,982 tokens + 8 non-empty requests x 256 = 6,030 positions
+    _run_case(w, [], balanced=[1, 2, 7, 64, 256, 1000, 6029, 6030, 9000])
+
+
+@pytest.mark.parametrize("heads", [1, 3, 16])
+def test_balanced_heads_and_empties(heads):
+    for fmt in ("bf16", "fp8"):
+        w = workloads.make_workload("bal_empties", seq_lens=[0, 0, 1, 2, 0, 33, 0], heads=heads, page_size=16,
+                                    num_pages=8, fmt=fmt, seed=3)
+        # cost axis: 36 tokens + 3 x 256 = 804 positions; most ranges hold start-up only
+        _run_case(w, [], balanced=[1, 3, 4, 36, 256, 803, 804, 2000])
+
+
+def test_balanced_max_batch():
+    """MLA_MAX_BALANCED_BATCH requests, short ragged lengths, many requests per workgroup."""
+    lens = np.random.default_rng(11).integers(0, 40, size=mla.MLA_MAX_BALANCED_BATCH)
+    pages = int(sum(-(-int(L) // 16) for L in lens)) + 3
+    w = workloads.make_workload("bal_max", seq_lens=lens.tolist(), heads=4, page_size=16, num_pages=pages,
+                                fmt="fp8", seed=12)
+    _run_case(w, [], balanced=[1, 97, 256, 5000])
+
+
+def test_balanced_all_empty():
+    w = workloads.make_workload("bal_none", seq_lens=[0, 0, 0], heads=16, page_size=16, num_pages=2, seed=4)
+    _run_case(w, [], balanced=[1, 256])
+
+
+def test_balanced_matches_per_request_mode():
+    """Same cache, two schedules: both within the bar of each other's reference."""
+    w = workloads.make_workload("bal_vs", seq_lens=[5000, 4097, 64, 0, 1, 3000], heads=16, page_size=64,
+                                num_pages=220, seed=6)
+    _run_case(w, [1, 64], balanced=[256, 1024])
+
+
+@pytest.mark.parametrize("name", ["batched", "fp8_ragged"])
+def test_balanced_full_size_sampled(name):
+    """The ragged named workloads at full size, batch-balanced with the bench's workgroup count."""
+    w = workloads.NAMED[name]()
+    W = workloads.BENCH_BALANCED_WORKGROUPS
+    req = _sample(w)
+    say(f"case {name} balanced: fmt={w.fmt} B={w.batch} tokens={w.tokens} W={W} oracle requests={req}")
+    pd = device_pool(w)
+    out, lse = gpu_decode(w, pd, W, balanced=True)
+    live = w.seq_lens > 0
+    assert np.isfinite(out[live]).all() and np.isfinite(lse[live]).all()
+    assert np.isneginf(lse[~live]).all() and (out[~live] == 0).all() and not np.signbit(out[~live]).any()
+    idx = np.searchsorted(w.slots, np.unique(np.concatenate([_request_slots(w, b) for b in req])))
+    ph = w.poisoned_pool()
+    ph.reshape(-1, w.row_bytes)[w.slots[idx]] = oracle.pack_rows(w.latent[idx], w.k_pe[idx], w.fmt)
+    ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=req)
+    assert_parity(w, out, lse, ref_o, ref_l, requests=req, what=f"{name} balanced W={W}")
 
 
 def _request_slots(w, b):

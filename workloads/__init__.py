@@ -348,3 +348,7 @@ BENCH_SPLITS = {
     "high_slot": 8,
     "fp8_ragged": 12,
 }
+
+# Workgroups of the batch-balanced decode in the bench's launch configuration (one per
+# compute unit).
+BENCH_BALANCED_WORKGROUPS = 256
