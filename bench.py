@@ -44,9 +44,9 @@ def _parse():
     ap.add_argument("--geometry", choices=("mla", "gla2", "rank256"), default="mla",
                     help="gla2: GLA-g2 head groups on the same rows; rank256: a rank-256 layer (640-byte bf16 "
                          "rows made from the workload's rows; no cache write in the step)")
-    ap.add_argument("--balanced", type=int, default=0, metavar="W",
+    ap.add_argument("--balanced", type=int, default=None, metavar="W",
                     help="batch-balanced decode with W workgroups (tokens cut evenly across requests); "
-                         "the decode time then covers its three kernels (plan, decode, merge)")
+                         "default: the workload's measured schedule")
     ap.add_argument("--nope", action="store_true",
                     help="decode the workload as a NoPE-512 layer: 512-wide queries, rows written with a zero "
                          "rope part, which the NoPE kernels never read")
@@ -130,30 +130,32 @@ def _cpu_baseline(w, requests, nope=False, q_mtp=None, geometry="mla", min_secon
     }
 
 
-KERNEL_SOURCES = ("paged_mla_latent_amd/csrc/decode.hip", "paged_mla_latent_amd/csrc/mla_device.h")
-COUNTERS = "profiles/decode_long_context_counters.txt"
+KERNEL_SOURCES = ("paged_mla_latent_amd/csrc/decode.hip", "paged_mla_latent_amd/csrc/mla_device.h",
+                  "paged_mla_latent_amd/csrc/mla_internal.h")
 
 
-def _profiled_traffic(workload: str):
-    """HBM bytes per decode launch from the committed counter profile, or None.
+def _profiled_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from its committed counter profile
+    (profiles/decode_<workload>_counters.txt), or None.
 
-    None unless the workload is the profiled one and the decode sources still hash to
-    what was profiled.
+    None unless that profile exists, names the same kernel and the kernel sources still
+    hash to what was profiled.
     """
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
-    if workload != "long_context" or not os.path.exists(os.path.join(root, COUNTERS)):
+    path = os.path.join(root, "profiles", f"decode_{workload}_counters.txt")
+    if not os.path.exists(path):
         return None
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(root, f), "rb") as fh:
             h.update(fh.read())
     vals = {}
-    for line in open(os.path.join(root, COUNTERS)):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_sources_sha256_16") != h.hexdigest()[:16]:
+    if vals.get("kernel_sources_sha256_16") != h.hexdigest()[:16] or vals.get("kernel") != kernel.split("<")[0]:
         return None
     return int(vals["decode_fetch_bytes"]) + int(vals["decode_write_bytes"])
 
@@ -247,6 +249,11 @@ def main():
 
     w = workloads.NAMED[args.workload]()
     S = args.splits or workloads.BENCH_SPLITS[args.workload]
+    balanced = args.balanced
+    if balanced is None:
+        default_bal = workloads.BENCH_SCHEDULE[args.workload] == "balanced"
+        plain = args.q_len == 1 and not args.nope and args.geometry == "mla" and not args.splits
+        balanced = workloads.BENCH_BALANCED_WORKGROUPS if (default_bal and plain) else 0
     dev = torch.device("cuda:0")
     fmt = mla.MLA_CACHE_BF16_576 if w.fmt == "bf16" else mla.MLA_CACHE_FP8_656
 
@@ -290,7 +297,8 @@ def main():
     else:
         decode = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
     groups = 1 if rows <= 16 else (2 if rows <= 32 else 4)
-    kernel = f"decode_kernel<{'Bf16' if w.fmt == 'bf16' else 'Fp8'}Rows<{0 if nope else 64}>, {groups}>"
+    rope = 0 if nope else 64
+    kernel = f"decode_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}>'}, {groups}>"
     geom, width, write_rows, row_bytes_read = args.geometry, 512, True, w.row_bytes - (128 if nope else 0)
     if geom != "mla":
         if nope or T > 1:
@@ -311,7 +319,6 @@ def main():
             decode, write_rows, row_bytes_read = mla.mla_decode_rank256_bf16, False, 640
             kernel = "decode_kernel<Bf16Rows<256, 64>, 1>"
         out = torch.empty((w.batch, rows, width), dtype=torch.float32, device=dev)
-    balanced = args.balanced
     if balanced:
         if nope or T > 1 or geom != "mla":
             raise SystemExit("--balanced is not combined with --nope, --q-len or --geometry by this benchmark")
@@ -331,8 +338,9 @@ def main():
             mla.mla_cache_write(new_lat, new_pe, new_slots, pool, fmt)
         if e: e[1].record(stream)
         if balanced:
-            decode_bal(q, pool, bt, lens, w.scale, num_workgroups=balanced, out=out, lse=lse, workspace=ws)
+            decode_bal(q, pool, bt, lens, w.scale, num_workgroups=balanced, workspace=ws, partials_only=True)
             if e: e[2].record(stream)
+            mla.mla_merge_lse_balanced(ws, w.batch, rows, balanced, out=out, lse=lse)
         elif S > 1:
             po, pl = decode(q, pool, bt, lens, w.scale, num_splits=S, workspace=ws, partials_only=True)
             if e: e[2].record(stream)
@@ -432,7 +440,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None if (nope or T > 1 or geom != "mla" or balanced) else _profiled_traffic(w.name),
+            "traffic": None if (nope or T > 1 or geom != "mla") else _profiled_traffic(w.name, kernel),
         },
     }
     if not args.no_cpu_baseline:

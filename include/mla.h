@@ -140,8 +140,9 @@ MLA_API int mla_decode_fp8_656(const void* q, const void* kv_cache, int64_t num_
  *                 num_heads, num_workgroups) bytes, 16-byte aligned: int64 range
  *                 bounds [batch + 1], then up to batch + num_workgroups - 1 partials.
  * The decode reads seq_lens on the device (no host synchronisation); a request with
- * seq_lens == 0 gets (+0.0, -inf).  Every other argument, result and error as
- * mla_decode_bf16 / mla_decode_fp8_656. */
+ * seq_lens == 0 gets (+0.0, -inf).  Passing out == lse == NULL stops after the decode
+ * kernel: the partials stay in the workspace and mla_merge_lse_balanced combines them
+ * later.  Every other argument, result and error as mla_decode_bf16 / mla_decode_fp8_656. */
 MLA_API size_t mla_decode_balanced_workspace_size(int32_t batch, int32_t num_heads, int32_t num_workgroups);
 MLA_API int mla_decode_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pages,
                                      const int32_t* block_table, int64_t block_table_stride,
@@ -149,6 +150,15 @@ MLA_API int mla_decode_balanced_bf16(const void* q, const void* kv_cache, int64_
                                      int32_t page_size, float softmax_scale, int32_t num_workgroups,
                                      float* out, float* lse, void* workspace, size_t workspace_bytes,
                                      void* stream);
+/* Merge step of the batch-balanced decode: combines each request's partials left in the
+ * workspace by a mla_decode_balanced_* call made with out == lse == NULL and the same
+ * batch, num_heads and num_workgroups (the log-sum-exp merge contract of vLLM pull request
+ * 55543).  out fp32 [batch][num_heads][512], lse fp32 [batch][num_heads]; a request with
+ * no token gets (+0.0, -inf).  Errors as mla_merge_lse; MLA_ERR_WORKSPACE if
+ * workspace_bytes is below mla_decode_balanced_workspace_size(). */
+MLA_API int mla_merge_lse_balanced(const void* workspace, size_t workspace_bytes, int32_t batch,
+                                   int32_t num_heads, int32_t num_workgroups, float* out, float* lse,
+                                   void* stream);
 MLA_API int mla_decode_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
                                         const int32_t* block_table, int64_t block_table_stride,
                                         const int32_t* seq_lens, int32_t batch, int32_t num_heads,

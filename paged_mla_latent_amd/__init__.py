@@ -19,6 +19,7 @@ Entry points (same names as the C ABI in include/mla.h):
     mla_gather_context(kv_cache, cache_format, block_table, cu_rows, total_rows, seq_starts=None)
     mla_decode_workspace_size(batch, num_heads, num_splits)
     mla_decode_balanced_workspace_size(batch, num_heads, num_workgroups)
+    mla_merge_lse_balanced(workspace, batch, num_heads, num_workgroups, out=None, lse=None)
 
 Tensors: q bf16 [B, H, 576]; kv_cache bf16 [num_pages, page_size, 576] or uint8
 [num_pages, page_size, 656]; block_table int32 [B, W]; seq_lens int32 [B];
@@ -50,6 +51,7 @@ EXPORTED = (
     "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656", "mla_merge_lse", "mla_merge_lse_width",
     "mla_cache_write", "mla_gather_context", "mla_status_string", "mla_last_error_message", "mla_abi_version",
     "mla_decode_balanced_workspace_size", "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
+    "mla_merge_lse_balanced",
 )
 
 
@@ -88,6 +90,8 @@ def library() -> ctypes.CDLL:
     for name in ("mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656"):
         getattr(lib, name).argtypes = mtp
         getattr(lib, name).restype = c_int
+    lib.mla_merge_lse_balanced.argtypes = [vp, c_sz, c_i32, c_i32, c_i32, vp, vp, vp]
+    lib.mla_merge_lse_balanced.restype = c_int
     lib.mla_merge_lse.argtypes = [vp, vp, c_i32, c_i32, c_i32, vp, vp, vp]
     lib.mla_merge_lse.restype = c_int
     lib.mla_merge_lse_width.argtypes = [vp, vp, c_i32, c_i32, c_i32, c_i32, vp, vp, vp]
@@ -219,7 +223,7 @@ def mla_decode_balanced_workspace_size(batch: int, num_heads: int, num_workgroup
 
 
 def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
-                     softmax_scale, num_workgroups, out, lse, workspace):
+                     softmax_scale, num_workgroups, out, lse, workspace, partials_only=False):
     lib = library()
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
@@ -233,12 +237,16 @@ def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, 
         raise ValueError(f"q rows must have {ROW} values, got {D}")
     if block_table.shape[0] != B or seq_lens.shape[0] != B:
         raise ValueError("block_table and seq_lens must have one row per request")
-    if out is None:
-        out = torch.empty((B, H, LATENT), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.float32, 3, dev)
-    _need(lse, "lse", torch.float32, 2, dev)
+    if partials_only:
+        if out is not None or lse is not None:
+            raise ValueError("partials_only takes no out/lse")
+    else:
+        if out is None:
+            out = torch.empty((B, H, LATENT), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, 3, dev)
+        _need(lse, "lse", torch.float32, 2, dev)
     if workspace is None:
         need = mla_decode_balanced_workspace_size(B, H, num_workgroups)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -247,22 +255,40 @@ def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, 
         seq_lens.data_ptr(), B, H, kv_cache.shape[1], float(softmax_scale), int(num_workgroups),
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     _check(fn, status)
+    return workspace if partials_only else (out, lse)
+
+
+def mla_merge_lse_balanced(workspace, batch, num_heads, num_workgroups, out=None, lse=None):
+    """Merge the partials a balanced decode left in `workspace` (partials_only=True)."""
+    lib = library()
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on a HIP device")
+    dev = workspace.device
+    if out is None:
+        out = torch.empty((batch, num_heads, LATENT), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, num_heads), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    status = lib.mla_merge_lse_balanced(workspace.data_ptr(), workspace.numel() * workspace.element_size(), batch,
+                                        num_heads, num_workgroups, out.data_ptr(), lse.data_ptr(), _stream(dev))
+    _check("mla_merge_lse_balanced", status)
     return out, lse
 
 
 def mla_decode_balanced_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256, out=None,
-                             lse=None, workspace=None):
+                             lse=None, workspace=None, partials_only=False):
     """Batch-balanced decode over a bf16 cache (B <= 1024): the batch's tokens cut into
     num_workgroups equal-cost ranges across request boundaries; returns (out [B,H,512], lse [B,H])."""
     return _decode_balanced("mla_decode_balanced_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
-                            softmax_scale, num_workgroups, out, lse, workspace)
+                            softmax_scale, num_workgroups, out, lse, workspace, partials_only)
 
 
 def mla_decode_balanced_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256, out=None,
-                                lse=None, workspace=None):
+                                lse=None, workspace=None, partials_only=False):
     """Batch-balanced decode over an fp8 cache uint8 [num_pages, page_size, 656]."""
     return _decode_balanced("mla_decode_balanced_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
-                            softmax_scale, num_workgroups, out, lse, workspace)
+                            softmax_scale, num_workgroups, out, lse, workspace, partials_only)
 
 
 def _decode_mtp(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,

@@ -161,6 +161,19 @@ size_t balanced_bytes_for(int64_t batch, int64_t heads, int64_t workgroups) {
   return (bytes + 255) & ~(size_t)255;
 }
 
+struct BalancedWorkspace {
+  int64_t* cu;
+  float* part_out;
+  float* part_lse;
+};
+BalancedWorkspace balanced_layout(void* workspace, int64_t batch, int64_t heads, int64_t workgroups) {
+  BalancedWorkspace w;
+  w.cu = static_cast<int64_t*>(workspace);
+  w.part_out = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + balanced_cu_bytes(batch));
+  w.part_lse = w.part_out + (size_t)(batch + workgroups - 1) * heads * MLA_LATENT;
+  return w;
+}
+
 int decode_balanced(bool fp8, const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                     int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                     int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out, float* lse,
@@ -170,8 +183,10 @@ int decode_balanced(bool fp8, const void* q, const void* kv_cache, int64_t num_p
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
   if (!seq_lens) return fail(MLA_ERR_NULL, "%s: seq_lens is NULL", fn);
-  if (!out) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
-  if (!lse) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
+  // out == lse == NULL leaves the partials in the workspace for mla_merge_lse_balanced.
+  const bool partials_only = !out && !lse;
+  if (!out && !partials_only) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
+  if (!lse && !partials_only) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
   if (batch < 1 || batch > MLA_MAX_BALANCED_BATCH)
     return fail(MLA_ERR_SHAPE, "%s: batch=%d outside [1, %d]", fn, batch, MLA_MAX_BALANCED_BATCH);
   if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
@@ -196,9 +211,7 @@ int decode_balanced(bool fp8, const void* q, const void* kv_cache, int64_t num_p
   int rc = check_device();
   if (rc != MLA_OK) return rc;
 
-  int64_t* cu = static_cast<int64_t*>(workspace);
-  float* part_out = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + balanced_cu_bytes(batch));
-  float* part_lse = part_out + (size_t)(batch + num_workgroups - 1) * num_heads * MLA_LATENT;
+  BalancedWorkspace ws = balanced_layout(workspace, batch, num_heads, num_workgroups);
   mla::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.cache = static_cast<const uint8_t*>(kv_cache);
@@ -213,17 +226,18 @@ int decode_balanced(bool fp8, const void* q, const void* kv_cache, int64_t num_p
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   p.out = nullptr;
   p.lse = nullptr;
-  p.part_out = part_out;
-  p.part_lse = part_lse;
-  p.cu = cu;
+  p.part_out = ws.part_out;
+  p.part_lse = ws.part_lse;
+  p.cu = ws.cu;
   static_assert(MLA_MAX_BALANCED_BATCH == mla::kMaxBalancedBatch, "batch limit of the balanced kernels");
   hipStream_t s = static_cast<hipStream_t>(stream);
   rc = hip_status(fp8 ? mla::launch_decode_flat_fp8(p, num_workgroups, s)
                       : mla::launch_decode_flat_bf16(p, num_workgroups, s),
                   fn);
-  if (rc != MLA_OK) return rc;
-  return hip_status(mla::launch_merge_flat(part_out, part_lse, cu, batch, num_heads, num_workgroups, out, lse, s),
-                    "mla_merge_lse (after balanced decode)");
+  if (rc != MLA_OK || partials_only) return rc;
+  return hip_status(
+      mla::launch_merge_flat(ws.part_out, ws.part_lse, ws.cu, batch, num_heads, num_workgroups, out, lse, s),
+      "mla_merge_lse_balanced (after balanced decode)");
 }
 
 }  // namespace
@@ -326,6 +340,31 @@ int mla_decode_gla2_fp8_656(const void* q, const void* kv_cache, int64_t num_pag
                             void* workspace, size_t workspace_bytes, void* stream) {
   return decode_common(kGla2Fp8, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                        num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_merge_lse_balanced(const void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_heads,
+                           int32_t num_workgroups, float* out, float* lse, void* stream) {
+  const char* fn = "mla_merge_lse_balanced";
+  if (!workspace) return fail(MLA_ERR_NULL, "%s: workspace is NULL", fn);
+  if (!out) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
+  if (!lse) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
+  if (batch < 1 || batch > MLA_MAX_BALANCED_BATCH)
+    return fail(MLA_ERR_SHAPE, "%s: batch=%d outside [1, %d]", fn, batch, MLA_MAX_BALANCED_BATCH);
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
+    return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_HEADS);
+  if (num_workgroups < 1 || num_workgroups > 65535)
+    return fail(MLA_ERR_SHAPE, "%s: num_workgroups=%d outside [1, 65535]", fn, num_workgroups);
+  if (!aligned16(workspace) || !aligned16(out) || !aligned16(lse))
+    return fail(MLA_ERR_ALIGN, "%s: workspace, out and lse must be 16-byte aligned", fn);
+  const size_t need = balanced_bytes_for(batch, num_heads, num_workgroups);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
+  int rc = check_device();
+  if (rc != MLA_OK) return rc;
+  BalancedWorkspace ws = balanced_layout(const_cast<void*>(workspace), batch, num_heads, num_workgroups);
+  return hip_status(mla::launch_merge_flat(ws.part_out, ws.part_lse, ws.cu, batch, num_heads, num_workgroups, out,
+                                           lse, static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 int mla_merge_lse_width(const float* part_out, const float* part_lse, int32_t num_splits, int32_t batch,

@@ -141,6 +141,26 @@ def test_balanced_workspace(lib, fn):
     assert rc == 3 and "aligned" in msg
 
 
+def test_merge_balanced_validation(lib):
+    need = mla.mla_decode_balanced_workspace_size(4, 16, 256)
+
+    def call(ws=P, ws_bytes=need, batch=4, heads=16, wgs=256, out=P, lse=P):
+        rc = lib.mla_merge_lse_balanced(ws, ws_bytes, batch, heads, wgs, out, lse, None)
+        return rc, lib.mla_last_error_message().decode()
+
+    for kw in (dict(ws=None), dict(out=None), dict(lse=None)):
+        rc, msg = call(**kw)
+        assert rc == 1 and "NULL" in msg
+    for kw, word in ((dict(batch=0), "batch"), (dict(batch=1025), "batch"), (dict(heads=17), "num_heads"),
+                     (dict(wgs=0), "num_workgroups"), (dict(wgs=65536), "num_workgroups")):
+        rc, msg = call(**kw)
+        assert rc == 2 and word in msg
+    rc, msg = call(out=MIS)
+    assert rc == 3 and "aligned" in msg
+    rc, msg = call(ws_bytes=need - 1)
+    assert rc == 4 and str(need) in msg
+
+
 @pytest.mark.parametrize("field", ["q", "kv", "bt", "lens", "out", "lse"])
 def test_decode_rejects_misaligned(lib, field):
     rc, msg = _decode(lib, **{field: MIS})

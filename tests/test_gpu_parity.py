@@ -274,9 +274,24 @@ def test_balanced_matches_per_request_mode():
     _run_case(w, [1, 64], balanced=[256, 1024])
 
 
-@pytest.mark.parametrize("name", ["batched", "fp8_ragged"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_balanced_partials_then_merge(fmt):
+    """Decode with out == lse == NULL, then mla_merge_lse_balanced: bit-identical to one call."""
+    w = workloads.make_workload("bal_two_step", seq_lens=[3000, 0, 17, 900, 64], heads=16, page_size=16,
+                                num_pages=260, fmt=fmt, seed=8)
+    pd = device_pool(w)
+    q, bt, lens = bf16_dev(w.q), torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    fn = mla.mla_decode_balanced_bf16 if fmt == "bf16" else mla.mla_decode_balanced_fp8_656
+    out1, lse1 = fn(q, pd, bt, lens, w.scale, num_workgroups=100)
+    ws = fn(q, pd, bt, lens, w.scale, num_workgroups=100, partials_only=True)
+    out2, lse2 = mla.mla_merge_lse_balanced(ws, w.batch, w.heads, 100)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("name", ["batched", "fp8_ragged", "high_slot"])
 def test_balanced_full_size_sampled(name):
-    """The ragged named workloads at full size, batch-balanced with the bench's workgroup count."""
+    """The named workloads at full size, batch-balanced with the bench's workgroup count."""
     w = workloads.NAMED[name]()
     W = workloads.BENCH_BALANCED_WORKGROUPS
     req = _sample(w)

@@ -352,3 +352,13 @@ BENCH_SPLITS = {
 # Workgroups of the batch-balanced decode in the bench's launch configuration (one per
 # compute unit).
 BENCH_BALANCED_WORKGROUPS = 256
+
+# Schedule the benchmark times each named workload with, picked by measurement: per-request
+# partitions for uniform or short contexts, batch-balanced ranges for long ragged batches.
+BENCH_SCHEDULE = {
+    "tiny": "per-request",
+    "batched": "per-request",
+    "long_context": "per-request",
+    "high_slot": "balanced",
+    "fp8_ragged": "balanced",
+}
