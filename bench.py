@@ -41,7 +41,7 @@ def _parse():
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per request: > 1 times a speculative-decoding verify step "
                          "(mla_decode_mtp_*), which reads the cache once per request")
-    ap.add_argument("--geometry", choices=("mla", "gla2", "rank256"), default="mla",
+    ap.add_argument("--geometry", choices=("mla", "gla2", "rank256", "rank768", "rank1792"), default="mla",
                     help="gla2: GLA-g2 head groups on the same rows; rank256: a rank-256 layer (640-byte bf16 "
                          "rows made from the workload's rows; no cache write in the step)")
     ap.add_argument("--balanced", type=int, default=None, metavar="W",
@@ -50,6 +50,8 @@ def _parse():
     ap.add_argument("--nope", action="store_true",
                     help="decode the workload as a NoPE-512 layer: 512-wide queries, rows written with a zero "
                          "rope part, which the NoPE kernels never read")
+    ap.add_argument("--graph-steps", type=int, default=10,
+                    help="steps captured per HIP graph (the largest divisor of --steps up to this)")
     ap.add_argument("--eager", action="store_true",
                     help="time only eager launches (default: also replay the step from a captured HIP graph, "
                          "which gives the reported value)")
@@ -75,14 +77,29 @@ def _copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
-def _rank256_rows(w):
-    """Rank-256 rows (bf16 [slots, 320]) made from the workload's rows: latent[:256] ++ k_pe."""
-    return np.concatenate([w.latent[:, :256], w.k_pe], axis=1)
+RANKS = {"rank256": 256, "rank768": 768, "rank1792": 1792}
+
+
+def _rank_cols(D):
+    """Latent columns of a rank-D row made from a 512-wide one: column c is latent column c mod 512."""
+    return np.arange(D) % 512
+
+
+def _rank_rows(w, D, idx=None):
+    """Rank-D rows (bf16 bits [n, D + 64]) made from the workload's rows: the latent columns
+    of _rank_cols(D), then k_pe."""
+    lat, pe = (w.latent, w.k_pe) if idx is None else (w.latent[idx], w.k_pe[idx])
+    return np.concatenate([lat[:, _rank_cols(D)], pe], axis=1)
+
+
+def _rank_q(w, D):
+    """D + 64 query values per head, made from the workload's q like the rows."""
+    return np.ascontiguousarray(np.concatenate([w.q[:, :, _rank_cols(D)], w.q[:, :, 512:]], axis=2))
 
 
 def _geometry_q(w):
     """320 query values per head (the first 256 latent values, then the rope part)."""
-    return np.ascontiguousarray(np.concatenate([w.q[:, :, :256], w.q[:, :, 512:]], axis=2))
+    return _rank_q(w, 256)
 
 
 def _cpu_baseline(w, requests, nope=False, q_mtp=None, geometry="mla", min_seconds=10.0):
@@ -101,10 +118,11 @@ def _cpu_baseline(w, requests, nope=False, q_mtp=None, geometry="mla", min_secon
     row_bytes = w.row_bytes - (128 if nope else 0)
     if geometry == "gla2":
         q, run = _geometry_q(w), oracle.decode_gla2
-    elif geometry == "rank256":
-        flat = np.full((w.num_slots, 320), 0x7FC0, np.uint16)
-        flat[w.slots[idx]] = _rank256_rows(w)[idx]
-        q, pool, row_bytes = _geometry_q(w), flat, 640
+    elif geometry in RANKS:
+        D = RANKS[geometry]
+        flat = np.full((w.num_slots, D + 64), 0x7FC0, np.uint16)
+        flat[w.slots[idx]] = _rank_rows(w, D, idx)
+        q, pool, row_bytes = _rank_q(w, D), flat, 2 * (D + 64)
 
         def run(q, pool, bt, lens, ps, scale, fmt, requests):
             return oracle.decode_rank(q, pool, bt, lens, ps, scale, requests=requests)
@@ -310,14 +328,26 @@ def main():
             kernel = f"decode_kernel<{'Bf16Rows<512, 64>' if w.fmt == 'bf16' else 'Fp8Rows<64>'}, 1, true>"
         else:
             if w.fmt != "bf16":
-                raise SystemExit("--geometry rank256 needs a bf16 workload")
-            host = np.full((w.num_slots, 320), 0x7FC0, np.uint16)
-            host[w.slots] = _rank256_rows(w)
+                raise SystemExit(f"--geometry {geom} needs a bf16 workload")
+            D = RANKS[geom]
+            K, width = D + 64, D
+            q = bf16(_rank_q(w, D))
+            # rank-D rows assembled on the device from the workload's rows (see _rank_rows)
             del pool
-            pool = bf16(host).view(w.num_pages, w.page_size, 320)
-            del host
-            decode, write_rows, row_bytes_read = mla.mla_decode_rank256_bf16, False, 640
-            kernel = "decode_kernel<Bf16Rows<256, 64>, 1>"
+            flat = torch.full((w.num_slots, K), 0x7FC0, dtype=torch.int16, device=dev).view(torch.bfloat16)
+            cols = torch.from_numpy(_rank_cols(D)).to(dev)
+            for c0 in range(0, w.slots.size, 1 << 18):
+                sl = slice(c0, c0 + (1 << 18))
+                flat[torch.from_numpy(w.slots[sl]).to(dev)] = torch.cat(
+                    [bf16(w.latent[sl])[:, cols], bf16(w.k_pe[sl])], dim=1)
+            pool = flat.view(w.num_pages, w.page_size, K)
+            decode = {256: mla.mla_decode_rank256_bf16, 768: mla.mla_decode_rank768_bf16,
+                      1792: mla.mla_decode_rank1792_bf16}[D]
+            write_rows, row_bytes_read = False, 2 * K
+            kernel = "decode_kernel<Bf16Rows<256, 64>, 1>" if D == 256 else f"decode_wide_kernel<{D}>"
+            if D > 512:
+                ws = torch.empty(max(1, mla.mla_decode_rank_workspace_size(w.batch, rows, S, D)), dtype=torch.uint8,
+                                 device=dev)
         out = torch.empty((w.batch, rows, width), dtype=torch.float32, device=dev)
     if balanced:
         if nope or T > 1 or geom != "mla":
@@ -364,8 +394,11 @@ def main():
     launch_mode = "eager"
 
     if not args.eager:
-        # The same step captured once and replayed: one submission per step.  Every
-        # replay must reproduce the eager result bit for bit.
+        # n consecutive steps captured into one graph (as a serving loop captures a whole
+        # forward pass, one decode per layer) and replayed K / n times: every step's kernels
+        # still run, in order, with one host submission per n steps.  Every warm-up replay
+        # must reproduce the eager result bit for bit.
+        n_graph = max(d for d in range(1, min(args.graph_steps, args.steps) + 1) if args.steps % d == 0)
         eager_out, eager_lse = out.clone(), lse.clone()
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream(dev)
@@ -375,19 +408,20 @@ def main():
         stream.wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            step()
-        for _ in range(args.warmup):
+            for _ in range(n_graph):
+                step()
+        for _ in range(max(1, args.warmup // n_graph)):
             out.zero_()
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(out, eager_out) and torch.equal(lse, eager_lse), "graph replay differs from eager"
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(args.steps // n_graph):
             g.replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        launch_mode = "hip_graph"
+        launch_mode = f"hip_graph, {n_graph} steps per graph"
 
     ms_step = wall * 1e3 / args.steps
     ms_step_eager = eager_wall * 1e3 / args.steps
@@ -426,7 +460,8 @@ def main():
             "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
             "schedule": f"batch-balanced, {balanced} workgroups" if balanced else "per-request partitions",
             "layer": "nope-512" if nope else "rope-576", "query_tokens_per_request": T, "geometry": geom,
-            "cache_row_bytes": 640 if geom == "rank256" else w.row_bytes, "row_bytes_read": row_bytes_read,
+            "cache_row_bytes": 2 * (RANKS[geom] + 64) if geom in RANKS else w.row_bytes,
+            "row_bytes_read": row_bytes_read,
             "step": "decode + merge" if not write_rows else "cache write + decode + merge",
             "cache_bytes_per_step": cache_bytes,
         },

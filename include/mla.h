@@ -231,15 +231,35 @@ MLA_API int mla_decode_mtp_fp8_656(const void* q, const void* kv_cache, int64_t 
  *
  * Every other argument, result and error as mla_decode_bf16; the partials left in the
  * workspace (out == lse == NULL) are 256 wide: merge them with mla_merge_lse_width(.., 256, ..).
- * Ranks 768 and 1792 are not provided: their 16-row output tile needs 192 / 448 accumulator
- * registers per lane and their 16-token tiles 26 / 59 KB of LDS, past what this kernel's
- * single pass holds (the pages' own kernels take two passes for 1792). */
+ *
+ * mla_decode_rank768_bf16 / mla_decode_rank1792_bf16: rank-768 / rank-1792 layers.  kv_cache
+ * bf16 [num_pages][page_size][D + 64] (D latent values, then 64 rope values), q bf16
+ * [batch][num_heads][D + 64], out fp32 [batch][num_heads][D], D = 768 / 1792; scores over all
+ * D + 64 values.  The workspace (num_splits > 1) is mla_decode_rank_workspace_size(batch,
+ * num_heads, num_splits, D) bytes: partials [num_splits][batch][num_heads][D] then
+ * [num_splits][batch][num_heads]; merge left partials with mla_merge_lse_width(.., D, ..).
+ * One pass (the pages' own kernels take two for 1792, where one does not fit their shared
+ * memory). */
 MLA_API int mla_decode_rank256_bf16(const void* q, const void* kv_cache, int64_t num_pages,
                                     const int32_t* block_table, int64_t block_table_stride,
                                     const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                     int32_t page_size, float softmax_scale, int32_t num_splits,
                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
                                     void* stream);
+MLA_API size_t mla_decode_rank_workspace_size(int32_t batch, int32_t num_heads, int32_t num_splits,
+                                              int32_t latent_rank);
+MLA_API int mla_decode_rank768_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                                    const int32_t* block_table, int64_t block_table_stride,
+                                    const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                    int32_t page_size, float softmax_scale, int32_t num_splits,
+                                    float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+MLA_API int mla_decode_rank1792_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                                     const int32_t* block_table, int64_t block_table_stride,
+                                     const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                     int32_t page_size, float softmax_scale, int32_t num_splits,
+                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 MLA_API int mla_decode_gla2_bf16(const void* q, const void* kv_cache, int64_t num_pages,
                                  const int32_t* block_table, int64_t block_table_stride,
                                  const int32_t* seq_lens, int32_t batch, int32_t num_heads,
@@ -253,7 +273,7 @@ MLA_API int mla_decode_gla2_fp8_656(const void* q, const void* kv_cache, int64_t
                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
                                     void* stream);
 
-/* mla_merge_lse for partial rows of `width` values (256 or 512): part_out fp32
+/* mla_merge_lse for partial rows of `width` values (256, 512, 768 or 1792): part_out fp32
  * [num_splits][batch][num_rows][width], part_lse [num_splits][batch][num_rows], out
  * [batch][num_rows][width], lse [batch][num_rows]; same formula and NaN / empty rules. */
 MLA_API int mla_merge_lse_width(const float* part_out, const float* part_lse, int32_t num_splits,

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI in include/mla.h):
     mla_decode_nope_bf16 / mla_decode_nope_fp8_656(q [B, H, 512], ...)   NoPE-512 layers
     mla_decode_mtp_bf16 / mla_decode_mtp_fp8_656(q [B, q_len, H, 576], ...)   verify step
     mla_decode_rank256_bf16(q [B, H, 320], kv_cache [pages, ps, 320], ...)   rank-256 layer
+    mla_decode_rank768_bf16 / mla_decode_rank1792_bf16(q [B, H, D + 64], ...)   rank-768 / 1792 layers
     mla_decode_gla2_bf16 / mla_decode_gla2_fp8_656(q [B, H, 320], ...)   GLA-g2 head groups
     mla_decode_balanced_bf16 / mla_decode_balanced_fp8_656(..., num_workgroups=256)   ragged batches
     mla_merge_lse_width(part_out, part_lse, out=None, lse=None)   256- or 512-wide partials
@@ -51,7 +52,8 @@ EXPORTED = (
     "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656", "mla_merge_lse", "mla_merge_lse_width",
     "mla_cache_write", "mla_gather_context", "mla_status_string", "mla_last_error_message", "mla_abi_version",
     "mla_decode_balanced_workspace_size", "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
-    "mla_merge_lse_balanced",
+    "mla_merge_lse_balanced", "mla_decode_rank_workspace_size", "mla_decode_rank768_bf16",
+    "mla_decode_rank1792_bf16",
 )
 
 
@@ -81,8 +83,11 @@ def library() -> ctypes.CDLL:
     lib.mla_decode_balanced_workspace_size.argtypes = [c_i32, c_i32, c_i32]
     lib.mla_decode_balanced_workspace_size.restype = c_sz
     dec = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
+    lib.mla_decode_rank_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32]
+    lib.mla_decode_rank_workspace_size.restype = c_sz
     for name in ("mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656",
                  "mla_decode_rank256_bf16", "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656",
+                 "mla_decode_rank768_bf16", "mla_decode_rank1792_bf16",
                  "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = c_int
@@ -170,7 +175,8 @@ def _decode(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache,
         _need(lse, "lse", torch.float32, 2, dev)
     ws_bytes = 0
     if num_splits > 1:
-        need = mla_decode_workspace_size(B, H, num_splits)
+        need = (mla_decode_rank_workspace_size(B, H, num_splits, out_width) if out_width in (768, 1792)
+                else mla_decode_workspace_size(B, H, num_splits))
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size()
@@ -358,6 +364,24 @@ def mla_decode_rank256_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, n
                    softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=320, out_width=256)
 
 
+def mla_decode_rank_workspace_size(batch: int, num_heads: int, num_splits: int, latent_rank: int) -> int:
+    return int(library().mla_decode_rank_workspace_size(batch, num_heads, num_splits, latent_rank))
+
+
+def mla_decode_rank768_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                            workspace=None, partials_only=False):
+    """Rank-768 layer: kv_cache bf16 [pages, ps, 832], q [B, H, 832] -> out [B, H, 768], lse [B, H]."""
+    return _decode("mla_decode_rank768_bf16", torch.bfloat16, 832, q, kv_cache, block_table, seq_lens,
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=832, out_width=768)
+
+
+def mla_decode_rank1792_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                             workspace=None, partials_only=False):
+    """Rank-1792 layer: kv_cache bf16 [pages, ps, 1856], q [B, H, 1856] -> out [B, H, 1792], lse [B, H]."""
+    return _decode("mla_decode_rank1792_bf16", torch.bfloat16, 1856, q, kv_cache, block_table, seq_lens,
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=1856, out_width=1792)
+
+
 def mla_decode_gla2_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
                          workspace=None, partials_only=False):
     """GLA-g2 on the 576-value row: q [B, H, 320] (H even) -> out [B, H, 256], lse [B, H]."""
@@ -373,7 +397,7 @@ def mla_decode_gla2_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, n
 
 
 def mla_merge_lse_width(part_out, part_lse, out=None, lse=None):
-    """Merge partials [S, B, R, W] / [S, B, R] with W = 256 or 512; returns (out [B, R, W], lse [B, R])."""
+    """Merge partials [S, B, R, W] / [S, B, R], W = 256, 512, 768 or 1792; returns (out [B, R, W], lse [B, R])."""
     lib = library()
     _need(part_out, "part_out", torch.float32, 4)
     dev = part_out.device

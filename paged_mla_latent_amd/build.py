@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_api.hip", "decode.hip", "merge.hip", "cache_write.hip", "gather.hip"]
+SOURCES = ["mla_api.hip", "decode.hip", "decode_wide.hip", "merge.hip", "cache_write.hip", "gather.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

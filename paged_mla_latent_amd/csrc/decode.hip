@@ -36,36 +36,6 @@ constexpr int kWaves = 4;
 constexpr int kTile = 16;
 constexpr float kRescaleThreshold = 8.0f;
 
-struct Range {
-  int64_t t0, t1;
-};
-
-// Partition s of a request of L tokens: whole pages, c = ceil(W / S) pages per partition,
-// W = the block table's width (the most pages any request may use).  Every request's
-// partitions have the same size, so a batch of ragged lengths balances: short requests
-// use fewer (non-empty) partitions instead of smaller ones.
-__device__ __forceinline__ Range partition(int64_t L, int ps, int S, int s, int64_t W) {
-  const int64_t P = (L + ps - 1) / ps;
-  int64_t c = (W + S - 1) / S;
-  if (c < 1) c = 1;
-  const int64_t p0 = min(P, (int64_t)s * c);
-  const int64_t p1 = min(P, (int64_t)(s + 1) * c);
-  return {min(L, p0 * ps), min(L, p1 * ps)};
-}
-
-// ------------------------------------------------------------------------------------
-// Tile layout in LDS.  A tile is 16 tokens x C chunks of 16 bytes (C = 72 for bf16 rows,
-// 41 for fp8 rows).  DMA instruction j fills chunk positions 64j .. 64j+63, lane L landing
-// at 64j + L; lane L = 4t + v fetches chunk 4j + (v ^ h(t)) of token t, so each group of
-// four lanes reads 64 contiguous bytes of one row (the coalesced form: four lanes per row
-// segment measured 6% faster than one lane per row).  Chunk c of token t therefore sits at
-//     P(t, c) = 64 * (c >> 2) + 4 * t + ((c & 3) ^ h(t)),   h(t) = bit-swap of t >> 2,
-// and both read patterns are bank-conflict free: the QK reads (one chunk of all 16 tokens:
-// 4 * (t & 3) + ((c & 3) ^ h(t)) covers 16 banks groups) and the transposing PV reads (8
-// tokens x 2 adjacent chunks per 32 lanes: tokens t and t + 4 use opposite chunk pairs).
-// ------------------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int t) { return (((t >> 2) & 1) << 1) | ((t >> 3) & 1); }
-__device__ __forceinline__ int chunk_pos(int t, int c) { return 64 * (c >> 2) + 4 * t + ((c & 3) ^ swz(t)); }
 
 // Rows of kLat latent values followed by 64 rope values, bf16.  kLat = 512, kRopeDim = 64:
 // the 576-value row.  kRopeDim = 0 (NoPE-512 layers): only the 512 latent values (the

@@ -53,15 +53,19 @@ int hip_status(hipError_t e, const char* what) {
   return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-size_t workspace_bytes_for(int64_t batch, int64_t heads, int64_t splits) {
+// Partials [splits][batch][rows][width] then [splits][batch][rows] fp32.
+size_t workspace_bytes_for(int64_t batch, int64_t heads, int64_t splits, int64_t width = MLA_LATENT) {
   if (splits <= 1) return 0;
   const size_t n = (size_t)splits * (size_t)batch * (size_t)heads;
-  const size_t bytes = n * (MLA_LATENT + 1) * sizeof(float) + 64;  // + lse alignment slack
+  const size_t bytes = n * (size_t)(width + 1) * sizeof(float) + 64;  // + lse alignment slack
   return (bytes + 255) & ~(size_t)255;
 }
 
 // Kinds of decode: row format and whether the rope part takes part in the scores.
-enum DecodeKind { kBf16 = 0, kFp8 = 1, kNopeBf16 = 2, kNopeFp8 = 3, kRank256Bf16 = 4, kGla2Bf16 = 5, kGla2Fp8 = 6 };
+enum DecodeKind {
+  kBf16 = 0, kFp8 = 1, kNopeBf16 = 2, kNopeFp8 = 3, kRank256Bf16 = 4, kGla2Bf16 = 5, kGla2Fp8 = 6,
+  kRank768Bf16 = 7, kRank1792Bf16 = 8
+};
 
 int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, int64_t num_pages,
                   const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
@@ -71,9 +75,14 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
   static const char* const kNames[] = {"mla_decode_bf16",         "mla_decode_fp8_656",
                                        "mla_decode_nope_bf16",    "mla_decode_nope_fp8_656",
                                        "mla_decode_rank256_bf16", "mla_decode_gla2_bf16",
-                                       "mla_decode_gla2_fp8_656"};
+                                       "mla_decode_gla2_fp8_656", "mla_decode_rank768_bf16",
+                                       "mla_decode_rank1792_bf16"};
   const bool gla = kind == kGla2Bf16 || kind == kGla2Fp8;
-  const int out_width = (kind == kRank256Bf16 || gla) ? 256 : MLA_LATENT;
+  const bool wide = kind == kRank768Bf16 || kind == kRank1792Bf16;
+  const int out_width = (kind == kRank256Bf16 || gla) ? 256
+                        : kind == kRank768Bf16        ? 768
+                        : kind == kRank1792Bf16       ? 1792
+                                                      : MLA_LATENT;
   const char* fn = q_len == 1 ? kNames[kind] : (kind == kBf16 ? "mla_decode_mtp_bf16" : "mla_decode_mtp_fp8_656");
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
@@ -107,7 +116,8 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
   float* part_out = nullptr;
   float* part_lse = nullptr;
   if (num_splits > 1) {
-    const size_t need = workspace_bytes_for(batch, (int64_t)q_len * num_heads, num_splits);
+    // the 256-wide outputs keep the 512-wide workspace size of the first ABI version
+    const size_t need = workspace_bytes_for(batch, (int64_t)q_len * num_heads, num_splits, wide ? out_width : MLA_LATENT);
     if (!workspace) return fail(MLA_ERR_WORKSPACE, "%s: num_splits=%d needs a workspace", fn, num_splits);
     if (!aligned16(workspace)) return fail(MLA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
     if (workspace_bytes < need)
@@ -144,6 +154,8 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
     case kNopeFp8: launched = mla::launch_decode_nope_fp8(p, s); break;
     case kRank256Bf16: launched = mla::launch_decode_rank256_bf16(p, s); break;
     case kGla2Bf16: launched = mla::launch_decode_gla2_bf16(p, s); break;
+    case kRank768Bf16: launched = mla::launch_decode_rank768_bf16(p, s); break;
+    case kRank1792Bf16: launched = mla::launch_decode_rank1792_bf16(p, s); break;
     default: launched = mla::launch_decode_gla2_fp8(p, s); break;
   }
   rc = hip_status(launched, fn);
@@ -270,6 +282,28 @@ size_t mla_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t num_s
   return workspace_bytes_for(batch, num_heads, num_splits);
 }
 
+size_t mla_decode_rank_workspace_size(int32_t batch, int32_t num_heads, int32_t num_splits, int32_t latent_rank) {
+  if (batch < 1 || num_heads < 1 || num_splits < 1) return 0;
+  if (latent_rank != 768 && latent_rank != 1792) return 0;
+  return workspace_bytes_for(batch, num_heads, num_splits, latent_rank);
+}
+
+int mla_decode_rank768_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                            int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                            int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kRank768Bf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_rank1792_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                             int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                             int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kRank1792Bf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
 int mla_decode_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                     int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                     int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
@@ -370,7 +404,8 @@ int mla_merge_lse_balanced(const void* workspace, size_t workspace_bytes, int32_
 int mla_merge_lse_width(const float* part_out, const float* part_lse, int32_t num_splits, int32_t batch,
                         int32_t num_rows, int32_t width, float* out, float* lse, void* stream) {
   const char* fn = "mla_merge_lse_width";
-  if (width != 256 && width != 512) return fail(MLA_ERR_SHAPE, "%s: width=%d must be 256 or 512", fn, width);
+  if (width != 256 && width != 512 && width != 768 && width != 1792)
+    return fail(MLA_ERR_SHAPE, "%s: width=%d must be 256, 512, 768 or 1792", fn, width);
   if (!part_out) return fail(MLA_ERR_NULL, "%s: part_out is NULL", fn);
   if (!part_lse) return fail(MLA_ERR_NULL, "%s: part_lse is NULL", fn);
   if (!out) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);

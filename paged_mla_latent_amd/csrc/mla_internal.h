@@ -27,6 +27,24 @@ struct DecodeParams {
   int64_t* cu;                 // batch-balanced mode: cost-axis starts v [B + 1], stored by the decode
 };
 
+// Tokens [t0, t1) of one request.
+struct Range {
+  int64_t t0, t1;
+};
+
+// Partition s of a request of L tokens: whole pages, c = ceil(W / S) pages per partition,
+// W = the block table's width (the most pages any request may use).  Every request's
+// partitions have the same size, so a batch of ragged lengths balances: short requests
+// use fewer (non-empty) partitions instead of smaller ones.
+__device__ __forceinline__ Range partition(int64_t L, int ps, int S, int s, int64_t W) {
+  const int64_t P = (L + ps - 1) / ps;
+  int64_t c = (W + S - 1) / S;
+  if (c < 1) c = 1;
+  const int64_t p0 = min(P, (int64_t)s * c);
+  const int64_t p1 = min(P, (int64_t)(s + 1) * c);
+  return {min(L, p0 * ps), min(L, p1 * ps)};
+}
+
 // Batch-balanced mode: at most kMaxBalancedBatch requests; each non-empty request adds
 // kSegmentCost positions to the cost axis, and workgroup w of W takes axis positions
 // [flat_begin(V, W, w), flat_begin(V, W, w + 1)), V = the axis length.
@@ -42,6 +60,8 @@ hipError_t launch_decode_nope_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_rank256_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_gla2_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_rank768_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_rank1792_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_gla2_fp8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_flat_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream);
 hipError_t launch_decode_flat_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream);

@@ -80,7 +80,8 @@ def _decode(lib, fn="mla_decode_bf16", **kw):
 
 
 DECODERS = ["mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656",
-            "mla_decode_rank256_bf16", "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656"]
+            "mla_decode_rank256_bf16", "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656",
+            "mla_decode_rank768_bf16", "mla_decode_rank1792_bf16"]
 
 
 @pytest.mark.parametrize("fn", DECODERS)
@@ -199,6 +200,26 @@ def test_merge_width_validation(lib):
     assert f(None, P, 2, 1, 4, 256, P, P, None) == 1
     assert f(P, P, 2, 1, 0, 256, P, P, None) == 2
     assert f(MIS, P, 2, 1, 4, 256, P, P, None) == 3
+
+
+def test_merge_width_accepts_wide_ranks(lib):
+    f = lib.mla_merge_lse_width
+    for width in (256, 512, 768, 1792):  # valid arguments: only the missing device stops the call
+        rc = f(P, P, 2, 1, 4, width, P, P, None)
+        assert rc == 5 and "width" not in lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("rank, fn", [(768, "mla_decode_rank768_bf16"), (1792, "mla_decode_rank1792_bf16")])
+def test_wide_rank_workspace(lib, rank, fn):
+    need = mla.mla_decode_rank_workspace_size(2, 16, 4, rank)
+    assert need == (4 * 2 * 16 * (rank + 1) * 4 + 64 + 255) // 256 * 256
+    assert mla.mla_decode_rank_workspace_size(2, 16, 1, rank) == 0
+    assert mla.mla_decode_rank_workspace_size(2, 16, 4, 512) == 0
+    assert mla.mla_decode_rank_workspace_size(0, 16, 4, rank) == 0
+    rc, msg = _decode(lib, fn, splits=4, ws=P, ws_bytes=need - 1)
+    assert rc == 4 and str(need) in msg
+    rc, msg = _decode(lib, fn, splits=4, ws=P, ws_bytes=mla.mla_decode_workspace_size(2, 16, 4))
+    assert rc == 4  # the 512-wide size is too small for rank-wide partials
 
 
 def test_mtp_workspace_counts_query_rows(lib):

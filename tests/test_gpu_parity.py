@@ -502,6 +502,36 @@ def test_rank256_parity(heads, ps):
                       what=f"rank256 H={heads} ps={ps} S={S}")
 
 
+@pytest.mark.parametrize("rank", [768, 1792])
+@pytest.mark.parametrize("heads, ps", [(16, 64), (4, 3), (1, 16), (16, 1)])
+def test_wide_rank_parity(rank, heads, ps):
+    """Rank-768 / 1792 rows (D + 64 bf16 values); decode vs oracle.decode_rank, unsplit and split,
+    and the partials left in the workspace merged by mla_merge_lse_width(D)."""
+    K = rank + 64
+    pages = sum(-(-L // ps) for L in GEOM_LENS) + 3
+    w = workloads.make_workload(f"r{rank}_{heads}_{ps}", seq_lens=GEOM_LENS, heads=heads, page_size=ps,
+                                num_pages=pages, seed=200 + heads + ps)
+    rng = np.random.default_rng(rank + heads * 7 + ps)
+    pool = np.full((pages * ps, K), 0x7FC0, np.uint16)
+    pool[w.slots] = workloads.bf16_bits(rng.standard_normal((w.slots.size, K)).astype(np.float32))
+    q = workloads.bf16_bits(rng.standard_normal((w.batch, heads, K)).astype(np.float32))
+    ref_o, ref_l = oracle.decode_rank(q, pool, w.block_table, w.seq_lens, ps, w.scale)
+    pd = bf16_dev(pool).view(pages, ps, K)
+    bt, lens = torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    fn = mla.mla_decode_rank768_bf16 if rank == 768 else mla.mla_decode_rank1792_bf16
+    for S in (1, 3, 40):
+        out, lse = fn(bf16_dev(q), pd, bt, lens, w.scale, num_splits=S)
+        torch.cuda.synchronize()
+        assert out.shape == (w.batch, heads, rank)
+        assert_parity(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l,
+                      what=f"rank{rank} H={heads} ps={ps} S={S}")
+    po, pl = fn(bf16_dev(q), pd, bt, lens, w.scale, num_splits=3, partials_only=True)
+    out2, lse2 = mla.mla_merge_lse_width(po, pl)
+    out3, lse3 = fn(bf16_dev(q), pd, bt, lens, w.scale, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out3) and torch.equal(lse2, lse3)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 @pytest.mark.parametrize("heads", [2, 4, 16])
 def test_gla2_parity(fmt, heads):
