@@ -369,6 +369,54 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
     Fmt::pv(buf, m, g, pr, aux, O);
   };
 
+  // The G tiles u0 .. u0 + G - 1 of step i for this lane's row group (G > 1), GB at a time
+  // (fp8 rows keep 16 block scales per tile between QK and PV, so four fp8 tiles at once
+  // would spill).  Tiles past the partition hold finite rows and score -inf.
+  constexpr int GB = (G == 4 && sizeof(typename Fmt::Aux) > 16) ? 2 : G;
+  auto compute_tiles = [&](int i, int u0) {
+    typename Fmt::Aux aux[GB];
+    f32x4 raw[GB];
+#pragma unroll
+    for (int v = 0; v < GB; ++v)
+      raw[v] = Fmt::qk(smem + ((u0 + v) * NB + (i & 1)) * Fmt::kTileBytes, m, g, qf, aux[v]);
+    float sc[GB][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < GB; ++v) {
+      const int valid = n_vis - (kWaves * i + u0 + v) * kTile;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[v][r] = (4 * g + r < valid) ? raw[v][r] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[v][r]);
+      }
+    }
+    mx = max_over_rows(mx);
+    const bool grow = mx > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int u = 0; u < Fmt::kAcc; ++u) O[u] *= alpha;
+      m_run = m_new;
+    }
+    const float m_base = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int v = 0; v < GB; ++v) {
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = fast_exp2(sc[v][r] - m_base);
+        l_run += pr[r];
+      }
+      Fmt::pv(smem + ((u0 + v) * NB + (i & 1)) * Fmt::kTileBytes, m, g, pr, aux[v], O);
+    }
+  };
+  auto compute_step = [&](int i, int u0) {
+#pragma unroll
+    for (int h = 0; h < G; h += GB) compute_tiles(i, u0 + h);
+  };
+
   constexpr int D = Fmt::kDmaOps;
   int k = wave;
   // The first NB-1 tiles' page ids are ordinary loads issued with the q loads; all are
@@ -377,16 +425,19 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   int32_t page_first[NB - 1];
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t)
-    page_first[t] = (k + kWaves * t < ntiles) ? bt[lane_token(k + kWaves * t) / ps] : 0;
+    page_first[t] = (G == 1 ? k + kWaves * t < ntiles : ntiles > 0) ? bt[lane_token(k + kWaves * t) / ps] : 0;
 #pragma unroll
   for (int j = 0; j < QS; ++j) asm volatile("" ::"v"(qf[j]));
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t) asm volatile("" ::"v"(page_first[t]));
-  if (k < ntiles) {
+  // G > 1: every wave loads a tile even where its tile lies past the partition (the
+  // partition's last rows again, clamped by lane_token), so that every buffer of a step holds
+  // finite rows and the step's tiles can be scored without a branch per tile.
+  if (G == 1 ? k < ntiles : ntiles > 0) {
 #pragma unroll
     for (int t = 0; t < NB - 1; ++t) {
       fetch_page(min(k + kWaves * (t + NB - 1), ntiles - 1), plds + 256 * t);
-      if (k + kWaves * t < ntiles)
+      if (G > 1 || k + kWaves * t < ntiles)
         Fmt::issue(row_of(lane_token(k + kWaves * t), page_first[t]), wlds + t * Fmt::kTileBytes, lane);
     }
   }
@@ -427,23 +478,24 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
     // the others are done with step i-1, whose buffers the next tiles then overwrite.
     // (A second barrier that lets the next loads start before this wait was measured
     // slower: the step is bound by its compute and the barrier, not by load depth.)
+    //   The G tiles a wave scores per step are processed together: the scores of all G
+    // first (independent MFMA chains), one running-max update over the step's 16 G tokens,
+    // then the G PV products.  With one wave per SIMD, per-tile processing left the MFMA
+    // pipe idle on each tile's dependent chain (scores -> max -> exp -> PV).
     const int nsteps = (ntiles + kWaves - 1) / kWaves;
     const int u0 = G * (wave / G);  // first tile of a step this wave scores
 #pragma unroll 1
     for (int i = 0; i < nsteps; ++i) {
       wait_vmcnt<0>();
       __syncthreads();
-      const int kn = kWaves * (i + 1) + wave;  // this wave's tile of step i + 1
-      if (kn < ntiles) {
+      if (i + 1 < nsteps) {
+        // this wave's tile of step i + 1, clamped to the partition's last tile
+        const int kn = min(kWaves * (i + 1) + wave, ntiles - 1);
         const int32_t page_n = read_page(pslot + 256 * (i & 1));
         fetch_page(min(kn + kWaves, ntiles - 1), plds + 256 * ((i + 1) & 1));
         Fmt::issue(row_of(lane_token(kn), page_n), wlds + ((i + 1) & 1) * Fmt::kTileBytes, lane);
       }
-#pragma unroll 1
-      for (int u = u0; u < u0 + G; ++u) {
-        const int kt = kWaves * i + u;
-        if (kt < ntiles) compute(smem + (u * NB + (i & 1)) * Fmt::kTileBytes, kt);
-      }
+      compute_step(i, u0);
     }
   }
 

@@ -35,7 +35,7 @@ struct Wide {
   static constexpr int kRowBytes = 2 * kQDim;         // 1,664 / 3,712
   static constexpr int kOps = kQDim / 32;             // DMA instructions = QK K-steps per tile: 26 / 58
   static constexpr int kTileBytes = kOps * 1024;      // 26,624 / 59,392
-  static constexpr int kBufs = kLat == 768 ? 4 : 2;   // shared tiles resident: 104 / 116 KB
+  static constexpr int kBufs = kLat == 768 ? 4 : 2;   // shared tiles resident: 104 / 116 KB (5 for 768: slower)
   static constexpr int kColGroups = kLat / 64;        // 16-column groups per wave: 12 / 28
   static constexpr int kMaxSteps = (kOps + 3) / 4;    // K-steps of the widest wave slice: 7 / 15
   static constexpr int kPidBytes = kWaves * kBufs * 256;
