@@ -183,6 +183,30 @@ def _request_slots(w, b):
     return w.block_table[b].astype(np.int64)[t // w.page_size] * w.page_size + t % w.page_size
 
 
+def _cpu_baseline_gather(w, requests, min_seconds=10.0):
+    """Time the oracle's context gather on a bounded sample (whole requests) on the host cores."""
+    import oracle
+    pool = w.poisoned_pool()
+    idx = np.concatenate([np.searchsorted(w.slots, _request_slots(w, b)) for b in requests])
+    oracle.cache_write(pool, w.latent[idx], w.k_pe[idx], w.slots[idx], w.fmt)
+    bt = w.block_table[requests]
+    cu = np.concatenate([[0], np.cumsum(w.seq_lens[requests].astype(np.int64))])
+    reps, t = 0, time.perf_counter()
+    while True:
+        oracle.gather_context(pool, bt, cu, None, w.page_size, w.fmt)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds:
+            break
+    rows = int(cu[-1])
+    per = dt / reps
+    return {
+        "value": round(rows * (w.row_bytes + 1152) / per / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"NumPy oracle (gather_context) gathering requests {list(requests)} of the {w.name} batch "
+                  f"({rows} rows), {reps} passes in {dt:.1f} s; single-threaded NumPy",
+    }
+
+
 def _bench_gather(args):
     """Context gather of every token of the workload into bf16 [tokens, 576] rows."""
     import torch
@@ -233,7 +257,7 @@ def _bench_gather(args):
         assert np.array_equal(got, oracle.upconvert_rows(raw, w.fmt)), f"gather of request {b} differs"
     moved = rows * (w.row_bytes + 1152)
     gbs = moved / (ms * 1e-3) / 1e9
-    print(json.dumps({
+    result = {
         "metric": "context gather GB/s (cache rows read + bf16 rows written)",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
@@ -244,7 +268,10 @@ def _bench_gather(args):
         "roofline": {"kernel": f"gather_kernel<{'true' if w.fmt == 'fp8' else 'false'}>", "bound": "hbm",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
-    }), flush=True)
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_baseline_gather(w, [b for b in range(w.batch) if w.seq_lens[b] > 0][:2])
+    print(json.dumps(result), flush=True)
 
 
 def main():
@@ -270,7 +297,7 @@ def main():
     balanced = args.balanced
     if balanced is None:
         default_bal = workloads.BENCH_SCHEDULE[args.workload] == "balanced"
-        plain = args.q_len == 1 and not args.nope and args.geometry == "mla" and not args.splits
+        plain = args.q_len == 1 and args.geometry == "mla" and not args.splits
         balanced = workloads.BENCH_BALANCED_WORKGROUPS if (default_bal and plain) else 0
     dev = torch.device("cuda:0")
     fmt = mla.MLA_CACHE_BF16_576 if w.fmt == "bf16" else mla.MLA_CACHE_FP8_656
@@ -350,13 +377,16 @@ def main():
                                  device=dev)
         out = torch.empty((w.batch, rows, width), dtype=torch.float32, device=dev)
     if balanced:
-        if nope or T > 1 or geom != "mla":
-            raise SystemExit("--balanced is not combined with --nope, --q-len or --geometry by this benchmark")
-        decode_bal = mla.mla_decode_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_fp8_656
+        if T > 1 or geom != "mla":
+            raise SystemExit("--balanced is not combined with --q-len or --geometry by this benchmark")
+        if nope:
+            decode_bal = mla.mla_decode_balanced_nope_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_nope_fp8_656
+        else:
+            decode_bal = mla.mla_decode_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_fp8_656
         ws = torch.empty(mla.mla_decode_balanced_workspace_size(w.batch, rows, balanced), dtype=torch.uint8,
                          device=dev)
         S = 1
-        kernel = f"decode_flat_kernel<{'Bf16Rows<512, 64>' if w.fmt == 'bf16' else 'Fp8Rows<64>'}>"
+        kernel = f"decode_flat_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}>'}>"
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)

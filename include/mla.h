@@ -150,6 +150,22 @@ MLA_API int mla_decode_balanced_bf16(const void* q, const void* kv_cache, int64_
                                      int32_t page_size, float softmax_scale, int32_t num_workgroups,
                                      float* out, float* lse, void* workspace, size_t workspace_bytes,
                                      void* stream);
+/* Batch-balanced NoPE-512 decode: the schedule of mla_decode_balanced_* with the scores of
+ * mla_decode_nope_bf16 / mla_decode_nope_fp8_656 (q bf16 [batch][num_heads][512], the rows'
+ * rope part never read).  Arguments, workspace, results and errors as mla_decode_balanced_*. */
+MLA_API int mla_decode_balanced_nope_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                                          const int32_t* block_table, int64_t block_table_stride,
+                                          const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                          int32_t page_size, float softmax_scale, int32_t num_workgroups,
+                                          float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                          void* stream);
+MLA_API int mla_decode_balanced_nope_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                                             const int32_t* block_table, int64_t block_table_stride,
+                                             const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                             int32_t page_size, float softmax_scale, int32_t num_workgroups,
+                                             float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
 /* Merge step of the batch-balanced decode: combines each request's partials left in the
  * workspace by a mla_decode_balanced_* call made with out == lse == NULL and the same
  * batch, num_heads and num_workgroups (the log-sum-exp merge contract of vLLM pull request

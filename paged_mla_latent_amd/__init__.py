@@ -14,6 +14,7 @@ Entry points (same names as the C ABI in include/mla.h):
     mla_decode_rank768_bf16 / mla_decode_rank1792_bf16(q [B, H, D + 64], ...)   rank-768 / 1792 layers
     mla_decode_gla2_bf16 / mla_decode_gla2_fp8_656(q [B, H, 320], ...)   GLA-g2 head groups
     mla_decode_balanced_bf16 / mla_decode_balanced_fp8_656(..., num_workgroups=256)   ragged batches
+    mla_decode_balanced_nope_bf16 / mla_decode_balanced_nope_fp8_656(q [B, H, 512], ...)
     mla_merge_lse_width(part_out, part_lse, out=None, lse=None)   256- or 512-wide partials
     mla_merge_lse(part_out, part_lse, out=None, lse=None)
     mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format)   k_pe None: zero rope
@@ -53,7 +54,7 @@ EXPORTED = (
     "mla_cache_write", "mla_gather_context", "mla_status_string", "mla_last_error_message", "mla_abi_version",
     "mla_decode_balanced_workspace_size", "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
     "mla_merge_lse_balanced", "mla_decode_rank_workspace_size", "mla_decode_rank768_bf16",
-    "mla_decode_rank1792_bf16",
+    "mla_decode_rank1792_bf16", "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656",
 )
 
 
@@ -88,6 +89,7 @@ def library() -> ctypes.CDLL:
     for name in ("mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656",
                  "mla_decode_rank256_bf16", "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656",
                  "mla_decode_rank768_bf16", "mla_decode_rank1792_bf16",
+                 "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656",
                  "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = c_int
@@ -229,7 +231,7 @@ def mla_decode_balanced_workspace_size(batch: int, num_heads: int, num_workgroup
 
 
 def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
-                     softmax_scale, num_workgroups, out, lse, workspace, partials_only=False):
+                     softmax_scale, num_workgroups, out, lse, workspace, partials_only=False, q_dim=ROW):
     lib = library()
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
@@ -239,8 +241,8 @@ def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, 
     _need(block_table, "block_table", torch.int32, 2, dev)
     _need(seq_lens, "seq_lens", torch.int32, 1, dev)
     B, H, D = q.shape
-    if D != ROW:
-        raise ValueError(f"q rows must have {ROW} values, got {D}")
+    if D != q_dim:
+        raise ValueError(f"q rows must have {q_dim} values, got {D}")
     if block_table.shape[0] != B or seq_lens.shape[0] != B:
         raise ValueError("block_table and seq_lens must have one row per request")
     if partials_only:
@@ -262,6 +264,20 @@ def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, 
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     _check(fn, status)
     return workspace if partials_only else (out, lse)
+
+
+def mla_decode_balanced_nope_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256, out=None,
+                                  lse=None, workspace=None, partials_only=False):
+    """Batch-balanced NoPE-512 decode over a bf16 cache: q [B, H, 512]."""
+    return _decode_balanced("mla_decode_balanced_nope_bf16", torch.bfloat16, ROW, q, kv_cache, block_table,
+                            seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only, q_dim=LATENT)
+
+
+def mla_decode_balanced_nope_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256,
+                                     out=None, lse=None, workspace=None, partials_only=False):
+    """Batch-balanced NoPE-512 decode over an fp8 cache: q [B, H, 512]."""
+    return _decode_balanced("mla_decode_balanced_nope_fp8_656", torch.uint8, 656, q, kv_cache, block_table,
+                            seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only, q_dim=LATENT)
 
 
 def mla_merge_lse_balanced(workspace, batch, num_heads, num_workgroups, out=None, lse=None):

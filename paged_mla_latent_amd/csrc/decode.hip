@@ -696,6 +696,16 @@ hipError_t launch_decode_flat_fp8(const DecodeParams& p, int num_workgroups, hip
                      stream, p);
   return hipGetLastError();
 }
+hipError_t launch_decode_flat_nope_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_flat_kernel<Bf16Rows<512, 0>>), dim3((unsigned)num_workgroups), dim3(kWaves * 64), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+hipError_t launch_decode_flat_nope_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_flat_kernel<Fp8Rows<0>>, dim3((unsigned)num_workgroups), dim3(kWaves * 64), 0, stream,
+                     p);
+  return hipGetLastError();
+}
 hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream) {
   return launch<Fp8Rows<0>>(p, stream);
 }

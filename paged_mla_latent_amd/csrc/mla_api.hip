@@ -186,11 +186,13 @@ BalancedWorkspace balanced_layout(void* workspace, int64_t batch, int64_t heads,
   return w;
 }
 
-int decode_balanced(bool fp8, const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+int decode_balanced(int kind, const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                     int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                     int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = fp8 ? "mla_decode_balanced_fp8_656" : "mla_decode_balanced_bf16";
+  static const char* const kNames[] = {"mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
+                                       "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656"};
+  const char* fn = kNames[kind];
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
@@ -243,9 +245,14 @@ int decode_balanced(bool fp8, const void* q, const void* kv_cache, int64_t num_p
   p.cu = ws.cu;
   static_assert(MLA_MAX_BALANCED_BATCH == mla::kMaxBalancedBatch, "batch limit of the balanced kernels");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = hip_status(fp8 ? mla::launch_decode_flat_fp8(p, num_workgroups, s)
-                      : mla::launch_decode_flat_bf16(p, num_workgroups, s),
-                  fn);
+  hipError_t launched;
+  switch (kind) {
+    case kBf16: launched = mla::launch_decode_flat_bf16(p, num_workgroups, s); break;
+    case kFp8: launched = mla::launch_decode_flat_fp8(p, num_workgroups, s); break;
+    case kNopeBf16: launched = mla::launch_decode_flat_nope_bf16(p, num_workgroups, s); break;
+    default: launched = mla::launch_decode_flat_nope_fp8(p, num_workgroups, s); break;
+  }
+  rc = hip_status(launched, fn);
   if (rc != MLA_OK || partials_only) return rc;
   return hip_status(
       mla::launch_merge_flat(ws.part_out, ws.part_lse, ws.cu, batch, num_heads, num_workgroups, out, lse, s),
@@ -265,7 +272,7 @@ int mla_decode_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pa
                              int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                              int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_balanced(false, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+  return decode_balanced(kBf16, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
                          page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -273,8 +280,27 @@ int mla_decode_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num
                                 int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
                                 int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups,
                                 float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_balanced(true, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+  return decode_balanced(kFp8, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
                          page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_balanced_nope_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                                  int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
+                                  int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups,
+                                  float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_balanced(kNopeBf16, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                         num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
+                         stream);
+}
+
+int mla_decode_balanced_nope_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                                     const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
+                                     int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
+                                     int32_t num_workgroups, float* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return decode_balanced(kNopeFp8, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                         num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
+                         stream);
 }
 
 size_t mla_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t num_splits) {

@@ -65,6 +65,8 @@ hipError_t launch_decode_rank1792_bf16(const DecodeParams& p, hipStream_t stream
 hipError_t launch_decode_gla2_fp8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_flat_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream);
 hipError_t launch_decode_flat_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream);
+hipError_t launch_decode_flat_nope_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream);
+hipError_t launch_decode_flat_nope_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream);
 hipError_t launch_merge_flat(const float* part_out, const float* part_lse, const int64_t* cu, int batch, int heads,
                              int num_workgroups, float* out, float* lse, hipStream_t stream);
 hipError_t launch_gather(const uint8_t* cache, int fp8, const int32_t* block_table, int64_t bt_stride,

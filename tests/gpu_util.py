@@ -81,7 +81,10 @@ def gpu_decode(w, pool: torch.Tensor, splits: int, q=None, nope=False, balanced=
     bt = torch.from_numpy(w.block_table).cuda()
     lens = torch.from_numpy(w.seq_lens).cuda()
     if balanced:
-        fn = mla.mla_decode_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_fp8_656
+        if nope:
+            fn = mla.mla_decode_balanced_nope_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_nope_fp8_656
+        else:
+            fn = mla.mla_decode_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_fp8_656
         out, lse = fn(q, pool, bt, lens, w.scale, num_workgroups=splits)
         torch.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)

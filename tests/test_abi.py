@@ -104,7 +104,8 @@ def test_decode_rejects_bad_shapes(lib, fn, kw, word):
     assert rc == 2 and word in msg
 
 
-BALANCED = ["mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656"]
+BALANCED = ["mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656", "mla_decode_balanced_nope_bf16",
+            "mla_decode_balanced_nope_fp8_656"]
 
 
 @pytest.mark.parametrize("fn", BALANCED)

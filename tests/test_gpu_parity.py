@@ -576,6 +576,9 @@ def test_nope_parity(fmt, ps):
     for S in (1, 3):
         out, lse = gpu_decode(w, pd, S, nope=True)
         assert_parity(w, out, lse, ref_o, ref_l, what=f"nope {fmt} ps={ps} S={S}")
+    for W in (1, 7, 256, 5000):  # batch-balanced NoPE
+        out, lse = gpu_decode(w, pd, W, nope=True, balanced=True)
+        assert_parity(w, out, lse, ref_o, ref_l, what=f"nope {fmt} ps={ps} balanced W={W}")
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
@@ -599,14 +602,15 @@ def test_nope_never_reads_rope_bytes(fmt):
     assert np.isnan(d[1]).all() and np.isnan(d[0]).all()  # as oracle.decode gives: every score NaN
 
 
-def test_nope_full_size_sampled():
-    """The fp8 ragged workload as a NoPE layer, at its bench split count."""
+@pytest.mark.parametrize("balanced", [False, True])
+def test_nope_full_size_sampled(balanced):
+    """The fp8 ragged workload as a NoPE layer, at its bench split count and batch-balanced."""
     w = workloads.NAMED["fp8_ragged"]()
-    S = workloads.BENCH_SPLITS["fp8_ragged"]
+    S = workloads.BENCH_BALANCED_WORKGROUPS if balanced else workloads.BENCH_SPLITS["fp8_ragged"]
     req = _sample(w)
-    say(f"case nope fp8_ragged: B={w.batch} tokens={w.tokens} splits={S} oracle requests={req}")
+    say(f"case nope fp8_ragged: B={w.batch} tokens={w.tokens} splits={S} balanced={balanced} oracle requests={req}")
     pd = device_pool(w, zero_rope=True)
-    out, lse = gpu_decode(w, pd, S, nope=True)
+    out, lse = gpu_decode(w, pd, S, nope=True, balanced=balanced)
     live = w.seq_lens > 0
     assert np.isfinite(out[live]).all() and np.isfinite(lse[live]).all()
     ph = w.poisoned_pool()
@@ -616,7 +620,7 @@ def test_nope_full_size_sampled():
     q512 = np.ascontiguousarray(w.q[:, :, :512])
     ref_o, ref_l = oracle.decode_nope(q512, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt,
                                       requests=req)
-    assert_parity(w, out, lse, ref_o, ref_l, requests=req, what=f"nope fp8_ragged S={S}")
+    assert_parity(w, out, lse, ref_o, ref_l, requests=req, what=f"nope fp8_ragged S={S} balanced={balanced}")
 
 
 def test_decode_is_bit_reproducible():
