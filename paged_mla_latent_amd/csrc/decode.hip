@@ -93,6 +93,27 @@ struct Bf16Rows {
     }
   }
 
+  // PV over two tiles at once with the 32-deep MFMA (the 16-deep one takes as many cycles for
+  // half the work): K slots 8g .. 8g + 3 carry tokens 4g .. 4g + 3 of tile a, slots 8g + 4 ..
+  // 8g + 7 the same tokens of tile b, in both operands, so no lane exchanges values.
+  __device__ static __forceinline__ void pv2(const uint8_t* bufa, const uint8_t* bufb, int m, int g,
+                                             const float (&pa)[4], const float (&pb)[4], const Aux&, const Aux&,
+                                             f32x4 (&O)[kAcc]) {
+    const u32x4 p8 = {pack_bf16(pa[0], pa[1]), pack_bf16(pa[2], pa[3]), pack_bf16(pb[0], pb[1]),
+                      pack_bf16(pb[2], pb[3])};
+    const int t = 4 * g + (m >> 2);
+    const int cc = (m >> 1) & 1;
+    const int o0 = 16 * chunk_pos(t, cc) + 8 * (m & 1);
+    const int o1 = 16 * chunk_pos(t, 2 + cc) + 8 * (m & 1);
+#pragma unroll
+    for (int u = 0; u < kAcc; u += 2) {
+      const u32x2 a0 = lds_read_tr16(bufa + o0 + 512 * u), b0 = lds_read_tr16(bufb + o0 + 512 * u);
+      const u32x2 a1 = lds_read_tr16(bufa + o1 + 512 * u), b1 = lds_read_tr16(bufb + o1 + 512 * u);
+      O[u] = mfma_16x16x32(u32x4{a0[0], a0[1], b0[0], b0[1]}, p8, O[u]);
+      O[u + 1] = mfma_16x16x32(u32x4{a1[0], a1[1], b1[0], b1[1]}, p8, O[u + 1]);
+    }
+  }
+
   // Accumulator u holds, for head m, d = 16u + 4g + r in element r.
   __device__ static __forceinline__ void store(const f32x4 (&O)[kAcc], float* row, int g) {
 #pragma unroll
@@ -172,34 +193,63 @@ struct Fp8Rows {
     }
   }
 
-  __device__ static __forceinline__ void pv(const uint8_t* buf, int m, int g, const float (&p)[4],
-                                            const Aux& aux, f32x4 (&O)[kAcc]) {
-    u32x2 pb[4];
+  // P of the 4 tokens of this lane, with each latent block's scale folded in.
+  __device__ static __forceinline__ void scaled_p(const float (&p)[4], const Aux& aux, u32x2 (&pb)[4]) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       pb[k] = u32x2{pack_bf16(p[0] * aux.sc[0][k], p[1] * aux.sc[1][k]),
                     pack_bf16(p[2] * aux.sc[2][k], p[3] * aux.sc[3][k])};
+  }
+
+  // A operands of column group i: a[e] = (x[0][e], x[1][e], x[2][e], x[3][e]) with x[r][e] =
+  // row(4g + r)[64i + 4m + e], the codes widened to bf16 exactly.
+  __device__ static __forceinline__ void pv_operands(const uint8_t* buf, int m, int g, int i, u32x2 (&a)[4]) {
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // codes 64i + 4m .. +4 of token 4g + r: chunk 4i + (m >> 2), quarter m & 3
+      const uint32_t w = *(const uint32_t*)(buf + 16 * chunk_pos(4 * g + r, 4 * i + (m >> 2)) + 4 * (m & 3));
+      lo[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+      hi[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    }
+    // lo[r] = (x[r][0], x[r][1]), hi[r] = (x[r][2], x[r][3])
+    a[0] = u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x05040100u), __builtin_amdgcn_perm(lo[3], lo[2], 0x05040100u)};
+    a[1] = u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u), __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u)};
+    a[2] = u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x05040100u), __builtin_amdgcn_perm(hi[3], hi[2], 0x05040100u)};
+    a[3] = u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u), __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u)};
+  }
+
+  __device__ static __forceinline__ void pv(const uint8_t* buf, int m, int g, const float (&p)[4],
+                                            const Aux& aux, f32x4 (&O)[kAcc]) {
+    u32x2 pb[4];
+    scaled_p(p, aux, pb);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t lo[4], hi[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // codes 64i + 4m .. +4 of token 4g + r: chunk 4i + (m >> 2), quarter m & 3
-        const uint32_t w = *(const uint32_t*)(buf + 16 * chunk_pos(4 * g + r, 4 * i + (m >> 2)) + 4 * (m & 3));
-        lo[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-        hi[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-      }
-      // lo[r] = (x[r][0], x[r][1]), hi[r] = (x[r][2], x[r][3]) with x[r][e] = row(4g+r)[64i + 4m + e].
-      // A operand e needs (x[0][e], x[1][e], x[2][e], x[3][e]).
-      const u32x2 a0 = {__builtin_amdgcn_perm(lo[1], lo[0], 0x05040100u), __builtin_amdgcn_perm(lo[3], lo[2], 0x05040100u)};
-      const u32x2 a1 = {__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u), __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u)};
-      const u32x2 a2 = {__builtin_amdgcn_perm(hi[1], hi[0], 0x05040100u), __builtin_amdgcn_perm(hi[3], hi[2], 0x05040100u)};
-      const u32x2 a3 = {__builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u), __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u)};
+      u32x2 a[4];
+      pv_operands(buf, m, g, i, a);
       const u32x2 b = pb[i >> 1];
-      O[4 * i + 0] = mfma_16x16x16(a0, b, O[4 * i + 0]);
-      O[4 * i + 1] = mfma_16x16x16(a1, b, O[4 * i + 1]);
-      O[4 * i + 2] = mfma_16x16x16(a2, b, O[4 * i + 2]);
-      O[4 * i + 3] = mfma_16x16x16(a3, b, O[4 * i + 3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O[4 * i + e] = mfma_16x16x16(a[e], b, O[4 * i + e]);
+    }
+  }
+
+  // Two tiles with the 32-deep MFMA: K slots 8g .. 8g + 3 are tile a's tokens 4g .. 4g + 3,
+  // slots 8g + 4 .. 8g + 7 tile b's, in both operands.
+  __device__ static __forceinline__ void pv2(const uint8_t* bufa, const uint8_t* bufb, int m, int g,
+                                             const float (&pa)[4], const float (&pb)[4], const Aux& auxa,
+                                             const Aux& auxb, f32x4 (&O)[kAcc]) {
+    u32x2 qa[4], qb[4];
+    scaled_p(pa, auxa, qa);
+    scaled_p(pb, auxb, qb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u32x2 a[4], b[4];
+      pv_operands(bufa, m, g, i, a);
+      pv_operands(bufb, m, g, i, b);
+      const u32x4 p8 = {qa[i >> 1][0], qa[i >> 1][1], qb[i >> 1][0], qb[i >> 1][1]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        O[4 * i + e] = mfma_16x16x32(u32x4{a[e][0], a[e][1], b[e][0], b[e][1]}, p8, O[4 * i + e]);
     }
   }
 
@@ -401,16 +451,19 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       m_run = m_new;
     }
     const float m_base = m_run == -INFINITY ? 0.f : m_run;
+    float pr[GB][4];
 #pragma unroll
-    for (int v = 0; v < GB; ++v) {
-      float pr[4];
+    for (int v = 0; v < GB; ++v)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pr[r] = fast_exp2(sc[v][r] - m_base);
-        l_run += pr[r];
+        pr[v][r] = fast_exp2(sc[v][r] - m_base);
+        l_run += pr[v][r];
       }
-      Fmt::pv(smem + ((u0 + v) * NB + (i & 1)) * Fmt::kTileBytes, m, g, pr, aux[v], O);
-    }
+    // PV two tiles at a time (GB is even)
+#pragma unroll
+    for (int v = 0; v < GB; v += 2)
+      Fmt::pv2(smem + ((u0 + v) * NB + (i & 1)) * Fmt::kTileBytes, smem + ((u0 + v + 1) * NB + (i & 1)) * Fmt::kTileBytes,
+               m, g, pr[v], pr[v + 1], aux[v], aux[v + 1], O);
   };
   auto compute_step = [&](int i, int u0) {
 #pragma unroll
