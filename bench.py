@@ -50,6 +50,9 @@ def _parse():
     ap.add_argument("--nope", action="store_true",
                     help="decode the workload as a NoPE-512 layer: 512-wide queries, rows written with a zero "
                          "rope part, which the NoPE kernels never read")
+    ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
+                    help="also time each decode after a pass over MIB MiB of other memory (evicts the "
+                         "last-level cache between repetitions); the roofline then uses these cold times")
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="steps captured per HIP graph (the largest divisor of --steps up to this)")
     ap.add_argument("--eager", action="store_true",
@@ -458,6 +461,19 @@ def main():
     t_write = np.mean([e[0].elapsed_time(e[1]) for e in ev])
     t_decode = np.mean([e[1].elapsed_time(e[2]) for e in ev])
     t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev])
+    t_decode_warm = t_decode
+    if args.flush_mib:
+        # Each step again, eagerly, after reading flush_mib MiB of other memory, so that the
+        # cache rows come from HBM rather than from the last-level cache.  The pass only reads
+        # (a write pass would leave dirty lines whose write-back lands in the timed decode).
+        flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device=dev)
+        ev_cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.amax()
+            step(ev_cold[i])
+        torch.cuda.synchronize()
+        t_decode = np.mean([e[1].elapsed_time(e[2]) for e in ev_cold])
+        del flush
     # rows that see at least one token (query i of a verify step sees L - q_len + 1 + i)
     vis = (w.seq_lens[:, None] - T + 1 + np.arange(T)[None, :]) > 0
     live = np.repeat(vis, w.heads, axis=1)
@@ -496,8 +512,10 @@ def main():
             "cache_bytes_per_step": cache_bytes,
         },
         "launch": launch_mode,
+        "flush_mib": args.flush_mib,
         "eager_ms_per_step": round(ms_step_eager, 4),
-        "kernel_ms": {"cache_write": round(t_write, 4), "decode": round(t_decode, 4), "merge": round(t_merge, 4)},
+        "kernel_ms": {"cache_write": round(t_write, 4), "decode": round(t_decode_warm, 4), "merge": round(t_merge, 4),
+                      **({"decode_after_flush": round(t_decode, 4)} if args.flush_mib else {})},
         "roofline": {
             "kernel": kernel,
             "bound": "hbm",
