@@ -90,7 +90,10 @@ MLA_API size_t mla_decode_workspace_size(int32_t batch, int32_t num_heads, int32
  *              num_splits > 1, a second kernel merges them by log-sum-exp (vLLM pull
  *              request 55543: the partial-result merge contract with (0, -inf) as the
  *              neutral element).  The result does not depend on num_splits beyond
- *              rounding.
+ *              rounding.  When batch x num_splits exceeds the device's compute units
+ *              (and batch <= 1024), the workgroups take the non-empty partitions first.
+ *              Merged here, empty partitions write no partial; kept (out == lse ==
+ *              NULL), every partition's partial is written.
  * out          fp32 [batch][num_heads][512]: softmax-weighted latent sum.
  * lse          fp32 [batch][num_heads]: natural-log log-sum-exp of the scaled scores.
  *              A request with seq_lens == 0 gets out = +0.0 and lse = -inf.

@@ -599,18 +599,102 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   }
 }
 
-// Per-request partitions: grid (request, partition), partition-major so that all requests'
-// first partitions are dispatched first, then the second ones, ...; with equal-size
-// partitions the empty tails of short requests come last and full partitions spread evenly
-// over the compute units.
+// Prefix sums over the requests of a batch of B <= kMaxBalancedBatch: out[0] = 0, out[b + 1] =
+// out[b] + value(b).  Thread t takes requests 4t .. 4t + 3; the 256 sums are scanned with wave
+// shuffles and a pass over the four wave totals (in `scratch`, kWaves values).  Ends with a
+// workgroup barrier, so `out` is visible to every thread.
+template <typename T, class F>
+__device__ __forceinline__ void scan_requests(int B, F value, T* out, T* scratch) {
+  constexpr int kPer = kMaxBalancedBatch / (kWaves * 64);
+  const int t = threadIdx.x;
+  T c[kPer];
+  T sum = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = kPer * t + i;
+    c[i] = b < B ? value(b) : T(0);
+    sum += c[i];
+  }
+  T incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const T o = __shfl_up(incl, d, 64);
+    if ((t & 63) >= d) incl += o;
+  }
+  if ((t & 63) == 63) scratch[t >> 6] = incl;
+  __syncthreads();
+  T run = incl - sum;
+  for (int w = 0; w < (t >> 6); ++w) run += scratch[w];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = kPer * t + i;
+    if (b < B) {
+      run += c[i];
+      out[b + 1] = run;
+    }
+  }
+  if (t == 0) out[0] = 0;
+  __syncthreads();
+}
+
+// The b with pre[b] <= x < pre[b + 1] (pre non-decreasing, pre[0] <= x < pre[B]).
+template <typename T>
+__device__ __forceinline__ int find_request(const T* pre, int B, T x) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Per-request partitions: grid (request, partition).  Without compaction the grid is
+// partition-major (all requests' first partitions are dispatched first, then the second
+// ones, ...).  With p.compact (a grid larger than one workgroup per compute unit, batch <=
+// kMaxBalancedBatch) every workgroup first counts the batch's non-empty partitions in LDS and
+// the dispatch index w is mapped onto them: workgroups 0 .. E - 1 take the E non-empty
+// partitions (request-major), the rest write the empty ones' (0, -inf), so no non-empty
+// partition waits behind empty ones for a compute unit.  The partial slots (s, b) and the
+// merge are the same either way.
 template <class Fmt, int G, bool kGla2 = false>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
   constexpr int kOut = kGla2 ? 256 : Fmt::kLatent;
-  const int b = blockIdx.x;
-  const int s = blockIdx.y;
-  const int64_t L = p.seq_lens[b];
+  int b = blockIdx.x;
+  int s = blockIdx.y;
+  int64_t L;
+  if (p.compact) {
+    __shared__ int32_t len_s[kMaxBalancedBatch];
+    __shared__ int32_t full_s[kMaxBalancedBatch + 1];   // prefix of non-empty partition counts
+    __shared__ int32_t empty_s[kMaxBalancedBatch + 1];  // prefix of empty partition counts
+    const int B = p.batch, S = p.num_splits;
+    const int64_t c = max((p.bt_stride + S - 1) / S, (int64_t)1);  // pages per partition
+    auto nonempty = [&](int r) -> int32_t {
+      const int32_t Lr = p.seq_lens[r];
+      len_s[r] = Lr;
+      return (int32_t)((((int64_t)Lr + p.page_size - 1) / p.page_size + c - 1) / c);
+    };
+    scan_requests<int32_t>(B, nonempty, full_s, (int32_t*)smem);
+    scan_requests<int32_t>(
+        B, [&](int r) -> int32_t { return S - (full_s[r + 1] - full_s[r]); }, empty_s, (int32_t*)smem + kWaves);
+    const int32_t w = (int32_t)(blockIdx.y * gridDim.x + blockIdx.x);
+    const int32_t E = full_s[B];
+    if (w >= E && p.skip_empty) return;  // an empty partition: nothing to write (uniform)
+    if (w < E) {
+      b = find_request(full_s, B, w);
+      s = w - full_s[b];
+    } else {
+      const int32_t k = w - E;
+      b = find_request(empty_s, B, k);
+      s = (full_s[b + 1] - full_s[b]) + (k - empty_s[b]);
+    }
+    L = len_s[b];
+    __syncthreads();  // the scratch words are tile memory from here on
+  } else {
+    L = p.seq_lens[b];
+  }
   const Range rg = partition(L, p.page_size, p.num_splits, s, p.bt_stride);
+  if (p.skip_empty && rg.t0 >= rg.t1) return;  // empty partition, no partial (uniform)
   const int R = p.q_len * p.heads;
   const int64_t row_b = (int64_t)b * R;
   const bool split = p.num_splits > 1;
@@ -636,42 +720,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
   __shared__ int64_t v_s[kMaxBalancedBatch + 1];
   const int B = p.batch;
-  {
-    // Thread t sums the costs of requests 4t .. 4t + 3; the 256 sums are scanned with wave
-    // shuffles and a pass over the four wave totals.
-    constexpr int kPer = kMaxBalancedBatch / (kWaves * 64);
-    const int t = threadIdx.x;
-    int64_t c[kPer];
-    int64_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int b = kPer * t + i;
-      const int64_t L = b < B ? (int64_t)p.seq_lens[b] : 0;
-      c[i] = L > 0 ? L + kSegmentCost : 0;
-      sum += c[i];
-    }
-    int64_t incl = sum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int64_t o = __shfl_up(incl, d, 64);
-      if ((t & 63) >= d) incl += o;
-    }
-    int64_t* wave_tot = (int64_t*)smem;
-    if ((t & 63) == 63) wave_tot[t >> 6] = incl;
-    __syncthreads();
-    int64_t run = incl - sum;
-    for (int w = 0; w < (t >> 6); ++w) run += wave_tot[w];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int b = kPer * t + i;
-      if (b < B) {
-        run += c[i];
-        v_s[b + 1] = run;
-      }
-    }
-    if (t == 0) v_s[0] = 0;
-    __syncthreads();
-  }
+  scan_requests<int64_t>(
+      B,
+      [&](int r) -> int64_t {
+        const int64_t L = p.seq_lens[r];
+        return L > 0 ? L + kSegmentCost : 0;
+      },
+      v_s, (int64_t*)smem);
   if (blockIdx.x == 0)
     for (int b = threadIdx.x; b <= B; b += kWaves * 64) p.cu[b] = v_s[b];
 

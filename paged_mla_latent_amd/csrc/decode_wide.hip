@@ -73,6 +73,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_wide_kernel(DecodeParam
   const Range rg = partition(L, p.page_size, p.num_splits, s, p.bt_stride);
   const int n = (int)(rg.t1 - rg.t0);
   const int ntiles = (n + kTile - 1) / kTile;
+  if (p.skip_empty && n == 0) return;  // empty partition: no partial (the merge counts)
 
   const int j0 = Wd::j0(wave), j1 = Wd::j0(wave + 1);
   const int nj = j1 - j0;

@@ -93,6 +93,23 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_kernel(const float* __r
   merge_row(part_out, part_lse, S, bh, rows, width, bh, out, lse);
 }
 
+// Per-request split decode whose empty partitions wrote nothing: row bh of request b =
+// bh / rows_per_request merges partials s = 0 .. n_b - 1 (row s * rows + bh), n_b = the number
+// of non-empty partitions of b under the decode's partition rule; n_b = 0 gives (0, -inf).
+__global__ __launch_bounds__(kGroups * kCols) void merge_counted_kernel(const float* __restrict__ part_out,
+                                                                       const float* __restrict__ part_lse, int S,
+                                                                       int64_t rows, int rows_per_request, int width,
+                                                                       const int32_t* __restrict__ seq_lens,
+                                                                       int page_size, int64_t bt_stride,
+                                                                       float* __restrict__ out,
+                                                                       float* __restrict__ lse) {
+  const int64_t bh = blockIdx.x;
+  const int64_t L = seq_lens[bh / rows_per_request];
+  const int64_t c = max((bt_stride + S - 1) / S, (int64_t)1);
+  const int n = (int)(((L + page_size - 1) / page_size + c - 1) / c);
+  merge_row(part_out, part_lse, n, bh, rows, width, bh, out, lse);
+}
+
 // Batch-balanced mode: request b's partials are the slots b + w for the workgroups w whose
 // cost-axis ranges meet [cu[b], cu[b + 1]) (the axis the decode stored); head h of slot q
 // is row q * heads + h.
@@ -126,6 +143,16 @@ hipError_t launch_merge_flat(const float* part_out, const float* part_lse, const
   const int64_t rows = (int64_t)batch * heads;
   hipLaunchKernelGGL(merge_flat_kernel, dim3((unsigned)rows, (unsigned)(kLatent / (4 * kCols))),
                      dim3(kGroups * kCols), 0, stream, part_out, part_lse, cu, heads, num_workgroups, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_counted(const float* part_out, const float* part_lse, int num_splits, int batch,
+                                int rows_per_request, int width, const int32_t* seq_lens, int page_size,
+                                int64_t bt_stride, float* out, float* lse, hipStream_t stream) {
+  const int64_t rows = (int64_t)batch * rows_per_request;
+  hipLaunchKernelGGL(merge_counted_kernel, dim3((unsigned)rows, (unsigned)(width / (4 * kCols))),
+                     dim3(kGroups * kCols), 0, stream, part_out, part_lse, num_splits, rows, rows_per_request, width,
+                     seq_lens, page_size, bt_stride, out, lse);
   return hipGetLastError();
 }
 

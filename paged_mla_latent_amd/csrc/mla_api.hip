@@ -23,9 +23,11 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Per-device cache of the architecture check: 0 unknown, 1 gfx950, -1 other.
+// Per-device cache of the architecture check: 0 unknown, 1 gfx950, -1 other; and of the
+// compute-unit count.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];
 
 int check_device() {
   int dev = -1;
@@ -39,6 +41,7 @@ int check_device() {
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(MLA_ERR_ARCH, "hipGetDeviceProperties(%d): %s", dev, hipGetErrorString(e));
     state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     g_arch[dev].store(state, std::memory_order_relaxed);
     if (state < 0)
       return fail(MLA_ERR_ARCH, "device %d is %s; this library is built for gfx950 (MI355X) only", dev,
@@ -46,6 +49,13 @@ int check_device() {
   }
   if (state < 0) return fail(MLA_ERR_ARCH, "device %d is not gfx950 (MI355X)", dev);
   return MLA_OK;
+}
+
+// Compute units of the current device (after check_device succeeded).
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  return g_cus[dev].load(std::memory_order_relaxed);
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -145,6 +155,11 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
   p.part_out = part_out;
   p.part_lse = part_lse;
   p.cu = nullptr;
+  // More workgroups than compute units: put the non-empty partitions first (see decode_kernel).
+  p.compact = batch <= MLA_MAX_BALANCED_BATCH && (int64_t)batch * num_splits > device_cus();
+  // Merged here: empty partitions need not leave the (0, -inf) partial that a caller's own merge
+  // of the workspace would read.
+  p.skip_empty = num_splits > 1 && !partials_only;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t launched;
   switch (kind) {
@@ -160,7 +175,8 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
   }
   rc = hip_status(launched, fn);
   if (rc != MLA_OK || num_splits == 1 || partials_only) return rc;
-  return hip_status(mla::launch_merge(part_out, part_lse, num_splits, batch, q_len * num_heads, out, lse, s, out_width),
+  return hip_status(mla::launch_merge_counted(part_out, part_lse, num_splits, batch, q_len * num_heads, out_width,
+                                              seq_lens, page_size, block_table_stride, out, lse, s),
                     "mla_merge_lse (after decode)");
 }
 
@@ -243,6 +259,8 @@ int decode_balanced(int kind, const void* q, const void* kv_cache, int64_t num_p
   p.part_out = ws.part_out;
   p.part_lse = ws.part_lse;
   p.cu = ws.cu;
+  p.compact = 0;
+  p.skip_empty = 0;
   static_assert(MLA_MAX_BALANCED_BATCH == mla::kMaxBalancedBatch, "batch limit of the balanced kernels");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t launched;

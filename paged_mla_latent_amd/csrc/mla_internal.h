@@ -25,6 +25,9 @@ struct DecodeParams {
   float* part_out;             // [S][B][q_len][H][512] (num_splits > 1)
   float* part_lse;             // [S][B][q_len][H]
   int64_t* cu;                 // batch-balanced mode: cost-axis starts v [B + 1], stored by the decode
+  int compact;                 // per-request mode: map workgroups onto the non-empty partitions first
+  int skip_empty;              // per-request split mode: empty partitions write no partial (the
+                               // merge counts each request's non-empty partitions itself)
 };
 
 // Tokens [t0, t1) of one request.
@@ -74,6 +77,12 @@ hipError_t launch_gather(const uint8_t* cache, int fp8, const int32_t* block_tab
                          int64_t total_rows, uint16_t* out, hipStream_t stream);
 hipError_t launch_merge(const float* part_out, const float* part_lse, int num_splits, int batch,
                         int heads, float* out, float* lse, hipStream_t stream, int width = kLatent);
+// Merge of the per-request split decode when empty partitions left no partial: request b's
+// non-empty partitions are the first ceil(ceil(L_b / page_size) / c) ones, c = ceil(bt_stride /
+// num_splits) pages (the partition rule of the decode).
+hipError_t launch_merge_counted(const float* part_out, const float* part_lse, int num_splits, int batch,
+                                int rows_per_request, int width, const int32_t* seq_lens, int page_size,
+                                int64_t bt_stride, float* out, float* lse, hipStream_t stream);
 hipError_t launch_cache_write(const uint16_t* latent, const uint16_t* k_pe, const int64_t* slots,
                               int num_tokens, uint8_t* cache, int fp8, hipStream_t stream);
 
