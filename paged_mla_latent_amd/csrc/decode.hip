@@ -9,17 +9,23 @@
 // return (out, lse); a merge kernel combines them by log-sum-exp.
 //
 // Mapping onto CDNA4:
-//  * grid = (request, partition); 4 waves per workgroup; each wave streams its own
-//    16-token tiles (tiles wave, wave+4, ...) and keeps its own online-softmax state,
-//    so the main loop has no workgroup barrier.  The 4 states merge through LDS at
-//    the end.
-//  * Rows go HBM -> LDS with 16-byte direct-to-LDS loads (no VGPR round trip), double
-//    buffered per wave; the page lookup for tile k+1 is issued before tile k's loads
-//    so that issuing k+1 never waits for k's data.
+//  * Two schedules share one per-segment routine (decode_segment): decode_kernel, grid
+//    (request, partition) with equal page-aligned partitions (dispatched non-empty first when
+//    the grid exceeds the compute units), and decode_flat_kernel, the batch-balanced schedule
+//    that cuts the whole batch's tokens into equal ranges across request boundaries.
+//  * 4 waves per workgroup; each wave streams its own 16-token tiles (tiles wave, wave+4,
+//    ...) and keeps its own online-softmax state, so the single-token loop has no
+//    workgroup barrier.  The 4 states merge through LDS at the end.  Multi-token verify
+//    steps with more than 16 query rows share each step's four tiles between the waves
+//    (one barrier per step), each wave scoring them for its 16-row group.
+//  * Rows go HBM -> LDS with 16-byte direct-to-LDS loads (no VGPR round trip), two or three
+//    buffers per wave; the page ids travel by DMA as well, ahead of the rows that need
+//    them, and completion is counted by hand, so no compiler-inserted wait stalls the loop.
 //  * All 16 heads share every row, so QK^T is a real 16 x 16 x 576 contraction per
 //    tile (v_mfma_f32_16x16x32_bf16, rows as A, q^T as B) and PV a 512 x 16 x 16 one
-//    (v_mfma_f32_16x16x16_bf16, rows^T as A via ds_read_b64_tr_b16, P^T as B).  The
-//    QK output layout (lane = head, 4 tokens per lane) is exactly PV's B operand.
+//    (v_mfma_f32_16x16x16_bf16, rows^T as A via ds_read_b64_tr_b16, P^T as B; two tiles
+//    per 16x16x32 instruction where a wave holds several).  The QK output layout (lane =
+//    head, 4 tokens per lane) is exactly PV's B operand.
 //  * Online softmax in the log2 domain with a lazy rescale: the running max moves
 //    only when a tile's max exceeds it by more than 8, so probabilities stay <= 2^8
 //    and the 128-register accumulator is rescaled a handful of times per partition.
