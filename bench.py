@@ -10,11 +10,18 @@ Default workload: the long-context batch, 4 requests x 262,144 tokens, 16 heads,
 64-token pages drawn at random from a 32,768-page pool, 64 partitions per request.
 
 Two timed passes of --steps steps each: eager launches with HIP events around every
-kernel (per-kernel durations, the roofline figure), then the same step captured once
-as a HIP graph and replayed (the reported value; every warm-up replay is checked
-bit for bit against the eager result).  Prints one JSON line.
+kernel (per-kernel durations, the roofline figure), then the step captured as a HIP
+graph (10 steps per graph) and replayed (the reported value; every warm-up replay is
+checked bit for bit against the eager result).  Prints one JSON line.  Each workload
+is timed with the schedule that measured faster for it (per-request partitions or the
+batch-balanced ranges).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload long_context] [--eager]
+
+Other lines of the same path: --q-len (multi-token verify), --nope (NoPE-512 layer),
+--geometry (GLA-g2, rank 256 / 768 / 1792), --balanced / --splits (schedule),
+--flush-mib (decode times after a last-level-cache flush), --op gather | cache_write |
+merge (the context gather, the cache write and the LSE merge on their own).
 """
 from __future__ import annotations
 
@@ -58,7 +65,7 @@ def _parse():
     ap.add_argument("--eager", action="store_true",
                     help="time only eager launches (default: also replay the step from a captured HIP graph, "
                          "which gives the reported value)")
-    ap.add_argument("--op", choices=("decode", "gather"), default="decode",
+    ap.add_argument("--op", choices=("decode", "gather", "cache_write", "merge"), default="decode",
                     help="gather: time mla_gather_context over the workload's whole context instead "
                          "(prefill-side context gather, fp8 rows upconverted to bf16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -277,6 +284,134 @@ def _bench_gather(args):
     print(json.dumps(result), flush=True)
 
 
+def _time_events(fn, steps, warmup, stream):
+    """Mean HIP-event milliseconds of fn() on `stream`, and the wall time of the timed loop."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])), time.perf_counter() - t0
+
+
+def _bench_cache_write(args):
+    """Cache write of every token of the workload (the pool fill): latent + k_pe + slot read,
+    one row written per token."""
+    import torch
+    import oracle
+    import paged_mla_latent_amd as mla
+    import workloads
+
+    w = workloads.NAMED[args.workload]()
+    dev = torch.device("cuda:0")
+    fmt = mla.MLA_CACHE_BF16_576 if w.fmt == "bf16" else mla.MLA_CACHE_FP8_656
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    shape = (w.num_pages, w.page_size, 576 if w.fmt == "bf16" else 656)
+    pool = torch.zeros(shape, dtype=torch.bfloat16 if w.fmt == "bf16" else torch.uint8, device=dev)
+    lat, pe, slots = bf16(w.latent), bf16(w.k_pe), torch.from_numpy(w.slots).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    ms, wall = _time_events(lambda: mla.mla_cache_write(lat, pe, slots, pool, fmt), args.steps, args.warmup, stream)
+    # the rows of a sample of tokens against the oracle's packing
+    idx = np.random.default_rng(0).choice(w.slots.size, size=min(4096, w.slots.size), replace=False)
+    got = pool.view(torch.uint8).view(-1, w.row_bytes)[torch.from_numpy(w.slots[idx]).to(dev)].cpu().numpy()
+    assert np.array_equal(got, oracle.pack_rows(w.latent[idx], w.k_pe[idx], w.fmt)), "cache rows differ"
+    T = int(w.slots.size)
+    moved = T * (1024 + 128 + 8 + w.row_bytes)
+    gbs = moved / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "cache write GB/s (new rows read + cache rows written)", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.fmt, "data": "synthetic",
+        "config": {"workload": w.name, "op": "cache_write", "tokens": T, "cache_row_bytes": w.row_bytes,
+                   "bytes_per_step": moved},
+        "kernel_ms": {"cache_write": round(ms, 4)},
+        "roofline": {"kernel": f"cache_write_{w.fmt}", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        n = 2048 if w.fmt == "fp8" else 65536
+        host = w.poisoned_pool()
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            oracle.cache_write(host, w.latent[:n], w.k_pe[:n], w.slots[:n], w.fmt)
+            reps += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(n * reps * (1024 + 128 + 8 + w.row_bytes) / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"NumPy oracle (cache_write) writing the first {n} tokens of the {w.name} workload, {reps} "
+                      f"passes in {dt:.1f} s; single-threaded NumPy"}
+    print(json.dumps(result), flush=True)
+
+
+def _bench_merge(args):
+    """Log-sum-exp merge of the workload's split-decode partials (the bench's split count)."""
+    import torch
+    import oracle
+    import paged_mla_latent_amd as mla
+    import workloads
+
+    w = workloads.NAMED[args.workload]()
+    S = args.splits or workloads.BENCH_SPLITS[args.workload]
+    if S < 2:
+        raise SystemExit("--op merge needs a split count above 1")
+    dev = torch.device("cuda:0")
+    fmt = mla.MLA_CACHE_BF16_576 if w.fmt == "bf16" else mla.MLA_CACHE_FP8_656
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    shape = (w.num_pages, w.page_size, 576 if w.fmt == "bf16" else 656)
+    pool = torch.zeros(shape, dtype=torch.bfloat16 if w.fmt == "bf16" else torch.uint8, device=dev)
+    mla.mla_cache_write(bf16(w.latent), bf16(w.k_pe), torch.from_numpy(w.slots).to(dev), pool, fmt)
+    decode = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
+    po, pl = decode(bf16(w.q), pool, torch.from_numpy(w.block_table).to(dev), torch.from_numpy(w.seq_lens).to(dev),
+                    w.scale, num_splits=S, partials_only=True)
+    po, pl = po.clone(), pl.clone()
+    del pool
+    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ms, wall = _time_events(lambda: mla.mla_merge_lse(po, pl, out=out, lse=lse), args.steps, args.warmup, stream)
+    hpo, hpl = po.cpu().numpy(), pl.cpu().numpy()
+    ref_o, ref_l = oracle.merge(hpo, hpl)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    live = np.isfinite(ref_l)
+    assert np.allclose(o, ref_o, rtol=1e-5, atol=1e-6) and np.allclose(l[live], ref_l[live], atol=1e-5), "merge differs"
+    moved = (S + 1) * w.batch * w.heads * 513 * 4
+    gbs = moved / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "LSE merge GB/s (partials read + merged rows written)", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "op": "merge", "num_splits": S, "rows": w.batch * w.heads,
+                   "bytes_per_step": moved},
+        "kernel_ms": {"merge": round(ms, 4)},
+        "roofline": {"kernel": "merge_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            oracle.merge(hpo, hpl)
+            reps += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(moved * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"NumPy oracle (merge) over the same {S} x {w.batch} x {w.heads} partials, {reps} passes in "
+                      f"{dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = _parse()
     if args.copy_calibration:
@@ -289,6 +424,12 @@ def main():
 
     if args.op == "gather":
         _bench_gather(args)
+        return
+    if args.op == "cache_write":
+        _bench_cache_write(args)
+        return
+    if args.op == "merge":
+        _bench_merge(args)
         return
 
     import torch
