@@ -32,6 +32,8 @@
 //  * fp8 rows: codes widen to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1);
 //    each 128-value block's scale multiplies that block's partial score (fp32) and is
 //    folded into P for that block's PV, so no dequantised value is ever rounded.
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -270,6 +272,97 @@ struct Fp8Rows {
   }
 };
 
+// fp8 tiles widened once into bf16 tiles in LDS, for the multi-token loop where every wave
+// scores every tile of a step for its own query rows: each wave converts the tile it loaded
+// (codes to bf16 exactly, rope copied, block scales kept apart) and all waves then read bf16
+// tiles with the 576-value row's layout.  The block scales still multiply the partial scores
+// in fp32 and are folded into P, so no dequantised value is rounded.
+struct Fp8Conv {
+  static constexpr int kLatent = 512;
+  static constexpr int kTileBytes = 18 * 1024;          // the 576-value bf16 tile
+  static constexpr int kSlotBytes = kTileBytes + 256;   // + 16 tokens x 4 fp32 block scales
+  static constexpr int kAcc = 32;
+  using Aux = Fp8Rows<64>::Aux;
+
+  // Wave-wide: the raw fp8 tile (Fp8Rows<64> layout) at `raw` into the bf16 tile at `conv`.
+  __device__ static __forceinline__ void convert(const uint8_t* raw, uint8_t* conv, int lane) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // 16 tokens x 32 code chunks, 8 per lane
+      const int q = lane + 64 * j;
+      const int tk = q >> 5, c = q & 31;  // token, chunk of 16 codes (latent values 16c ..)
+      const u32x4 codes = *(const u32x4*)(raw + 16 * chunk_pos(tk, c));
+      uint32_t v[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        v[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[w], 1.0f, false));
+        v[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[w], 1.0f, true));
+      }
+      *(u32x4*)(conv + 16 * chunk_pos(tk, 2 * c)) = u32x4{v[0], v[1], v[2], v[3]};
+      *(u32x4*)(conv + 16 * chunk_pos(tk, 2 * c + 1)) = u32x4{v[4], v[5], v[6], v[7]};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // 16 tokens x 8 rope chunks
+      const int q = lane + 64 * j;
+      const int tk = q >> 3, r = q & 7;
+      *(u32x4*)(conv + 16 * chunk_pos(tk, 64 + r)) = *(const u32x4*)(raw + 16 * chunk_pos(tk, 33 + r));
+    }
+    if (lane < 16) *(u32x4*)(conv + kTileBytes + 16 * lane) = *(const u32x4*)(raw + 16 * chunk_pos(lane, 32));
+  }
+
+  __device__ static __forceinline__ f32x4 qk(const uint8_t* buf, int m, int g, const u32x4* qf, Aux& aux) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) aux.sc[r] = *(const f32x4*)(buf + kTileBytes + 16 * (4 * g + r));
+    const uint8_t* base = buf + 16 * chunk_pos(m, g);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f32x4 sk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) sk = mfma_16x16x32(*(const u32x4*)(base + 1024 * (4 * k + jj)), qf[4 * k + jj], sk);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] += aux.sc[r][k] * sk[r];
+    }
+    f32x4 sr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jr = 0; jr < 2; ++jr) sr = mfma_16x16x32(*(const u32x4*)(base + 1024 * (16 + jr)), qf[16 + jr], sr);
+    return s + sr;
+  }
+
+  // Two tiles per 32-deep MFMA as in Bf16Rows::pv2; column group u belongs to latent block u / 8,
+  // whose scale is folded into P.
+  __device__ static __forceinline__ void pv2(const uint8_t* bufa, const uint8_t* bufb, int m, int g,
+                                             const float (&pa)[4], const float (&pb)[4], const Aux& auxa,
+                                             const Aux& auxb, f32x4 (&O)[kAcc]) {
+    u32x4 p8[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      p8[k] = u32x4{pack_bf16(pa[0] * auxa.sc[0][k], pa[1] * auxa.sc[1][k]),
+                    pack_bf16(pa[2] * auxa.sc[2][k], pa[3] * auxa.sc[3][k]),
+                    pack_bf16(pb[0] * auxb.sc[0][k], pb[1] * auxb.sc[1][k]),
+                    pack_bf16(pb[2] * auxb.sc[2][k], pb[3] * auxb.sc[3][k])};
+    const int t = 4 * g + (m >> 2);
+    const int cc = (m >> 1) & 1;
+    const int o0 = 16 * chunk_pos(t, cc) + 8 * (m & 1);
+    const int o1 = 16 * chunk_pos(t, 2 + cc) + 8 * (m & 1);
+#pragma unroll
+    for (int u = 0; u < kAcc; u += 2) {
+      const u32x2 a0 = lds_read_tr16(bufa + o0 + 512 * u), b0 = lds_read_tr16(bufb + o0 + 512 * u);
+      const u32x2 a1 = lds_read_tr16(bufa + o1 + 512 * u), b1 = lds_read_tr16(bufb + o1 + 512 * u);
+      O[u] = mfma_16x16x32(u32x4{a0[0], a0[1], b0[0], b0[1]}, p8[u >> 3], O[u]);
+      O[u + 1] = mfma_16x16x32(u32x4{a1[0], a1[1], b1[0], b1[1]}, p8[u >> 3], O[u + 1]);
+    }
+  }
+
+  // Accumulator u holds, for head m, d = 16u + 4g + r in element r (the bf16 layout).
+  __device__ static __forceinline__ void store(const f32x4 (&O)[kAcc], float* row, int g) {
+#pragma unroll
+    for (int u = 0; u < kAcc; ++u) *(f32x4*)(row + 16 * u + 4 * g) = O[u];
+  }
+};
+
+template <class Fmt, int G>
+constexpr bool kConvTiles = G > 1 && std::is_same<Fmt, Fp8Rows<64>>::value;
+
 constexpr int kRedStride = kLatent + 4;  // padded per-head row of the cross-wave merge
 constexpr int kRedBytes = kWaves * kMaxHeads * kRedStride * 4 + 2 * kWaves * kMaxHeads * 4;
 
@@ -304,6 +397,9 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   static_assert(G == 1 || G == 2 || G == 4, "row groups per workgroup");
   static_assert(!kGla2 || (Fmt::kLatent == 512 && Fmt::kQDim == 576), "GLA-g2 on the 576-value row");
   constexpr int kOut = kGla2 ? 256 : Fmt::kLatent;  // output values per query row
+  // fp8 rows in the multi-token loop: tiles widened once per step into bf16 (Fp8Conv).
+  constexpr bool kConv = kConvTiles<Fmt, G>;
+  using TF = typename std::conditional<kConv, Fp8Conv, Fmt>::type;  // layout the scores read
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int m = lane & 15;
@@ -361,7 +457,8 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   // Tile buffers per wave: Fmt::kBufs for one row group; the shared-tile loop of G > 1 is
   // written for two.
   constexpr int NB = G == 1 ? Fmt::kBufs : 2;
-  uint8_t* wbuf = smem + wave * NB * Fmt::kTileBytes;
+  constexpr int NR = kConv ? 1 : NB;  // raw tile buffers per wave (one when tiles are widened)
+  uint8_t* wbuf = smem + wave * NR * Fmt::kTileBytes;
   const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds_offset(wbuf));
 
   // Token this lane fetches in tile k, clamped into the partition (ragged tail).
@@ -375,8 +472,12 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   // Page ids travel HBM -> LDS by DMA as well (one 4-byte entry per lane, lane l's own
   // token), well ahead of use, so that no compiler-visible load sits in the loop: the
   // only vector-memory operations are these DMAs, whose completion is counted by hand.
-  uint8_t* pslot = smem + kWaves * NB * Fmt::kTileBytes + wave * NB * 256;
+  uint8_t* pslot = smem + kWaves * NR * Fmt::kTileBytes + wave * NB * 256;
   const uint32_t plds = __builtin_amdgcn_readfirstlane(lds_offset(pslot));
+  // widened tiles, one slot per wave, after the raw tiles and page-id slots
+  uint8_t* conv = smem + kWaves * NR * Fmt::kTileBytes + kWaves * NB * 256;
+  static_assert(!kConv || kWaves * (Fmt::kTileBytes + NB * 256 + Fp8Conv::kSlotBytes) <= smem_bytes<Fmt>(),
+                "widened tiles fit in the workgroup's LDS");
   auto fetch_page = [&](int k, uint32_t slot) {
     const uint32_t pi = lane_token(k) / ps;
     dma4(bt + pi, slot);
@@ -428,13 +529,15 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   // The G tiles u0 .. u0 + G - 1 of step i for this lane's row group (G > 1), GB at a time
   // (fp8 rows keep 16 block scales per tile between QK and PV, so four fp8 tiles at once
   // would spill).  Tiles past the partition hold finite rows and score -inf.
-  constexpr int GB = (G == 4 && sizeof(typename Fmt::Aux) > 16) ? 2 : G;
+  constexpr int GB = (G == 4 && sizeof(typename TF::Aux) > 16) ? 2 : G;
+  auto tile_of = [&](int i, int u) -> const uint8_t* {
+    return kConv ? conv + u * Fp8Conv::kSlotBytes : smem + (u * NB + (i & 1)) * Fmt::kTileBytes;
+  };
   auto compute_tiles = [&](int i, int u0) {
-    typename Fmt::Aux aux[GB];
+    typename TF::Aux aux[GB];
     f32x4 raw[GB];
 #pragma unroll
-    for (int v = 0; v < GB; ++v)
-      raw[v] = Fmt::qk(smem + ((u0 + v) * NB + (i & 1)) * Fmt::kTileBytes, m, g, qf, aux[v]);
+    for (int v = 0; v < GB; ++v) raw[v] = TF::qk(tile_of(i, u0 + v), m, g, qf, aux[v]);
     float sc[GB][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -468,8 +571,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
     // PV two tiles at a time (GB is even)
 #pragma unroll
     for (int v = 0; v < GB; v += 2)
-      Fmt::pv2(smem + ((u0 + v) * NB + (i & 1)) * Fmt::kTileBytes, smem + ((u0 + v + 1) * NB + (i & 1)) * Fmt::kTileBytes,
-               m, g, pr[v], pr[v + 1], aux[v], aux[v + 1], O);
+      TF::pv2(tile_of(i, u0 + v), tile_of(i, u0 + v + 1), m, g, pr[v], pr[v + 1], aux[v], aux[v + 1], O);
   };
   auto compute_step = [&](int i, int u0) {
 #pragma unroll
@@ -547,13 +649,18 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
     for (int i = 0; i < nsteps; ++i) {
       wait_vmcnt<0>();
       __syncthreads();
+      // Widened tiles: each wave converts the tile it loaded; its raw buffer is then free for
+      // the next step's tile, and a second barrier publishes the four bf16 tiles.  (The first
+      // barrier also tells every wave that the others are done with step i - 1's tiles.)
+      if constexpr (kConv) Fp8Conv::convert(wbuf, conv + wave * Fp8Conv::kSlotBytes, lane);
       if (i + 1 < nsteps) {
         // this wave's tile of step i + 1, clamped to the partition's last tile
         const int kn = min(kWaves * (i + 1) + wave, ntiles - 1);
         const int32_t page_n = read_page(pslot + 256 * (i & 1));
         fetch_page(min(kn + kWaves, ntiles - 1), plds + 256 * ((i + 1) & 1));
-        Fmt::issue(row_of(lane_token(kn), page_n), wlds + ((i + 1) & 1) * Fmt::kTileBytes, lane);
+        Fmt::issue(row_of(lane_token(kn), page_n), wlds + (kConv ? 0 : ((i + 1) & 1) * Fmt::kTileBytes), lane);
       }
+      if constexpr (kConv) __syncthreads();
       compute_step(i, u0);
     }
   }
@@ -565,7 +672,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   float* red = (float*)smem;
   float* red_m = red + kWaves * kMaxHeads * kRedStride;
   float* red_l = red_m + kWaves * kMaxHeads;
-  Fmt::store(O, red + (wave * kMaxHeads + m) * kRedStride, g);
+  TF::store(O, red + (wave * kMaxHeads + m) * kRedStride, g);
   if (g == 0) {
     red_m[wave * kMaxHeads + m] = m_run;
     red_l[wave * kMaxHeads + m] = l_run;
@@ -670,9 +777,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   int s = blockIdx.y;
   int64_t L;
   if (p.compact) {
-    __shared__ int32_t len_s[kMaxBalancedBatch];
-    __shared__ int32_t full_s[kMaxBalancedBatch + 1];   // prefix of non-empty partition counts
-    __shared__ int32_t empty_s[kMaxBalancedBatch + 1];  // prefix of empty partition counts
+    // Scratch in the tile memory, which the pipeline only uses after this prologue.
+    static_assert(smem_bytes<Fmt>() >= (3 * kMaxBalancedBatch + 2 + 2 * kWaves) * 4, "compaction scratch");
+    int32_t* len_s = (int32_t*)smem + 2 * kWaves;
+    int32_t* full_s = len_s + kMaxBalancedBatch;       // prefix of non-empty partition counts
+    int32_t* empty_s = full_s + kMaxBalancedBatch + 1;  // prefix of empty partition counts
     const int B = p.batch, S = p.num_splits;
     const int64_t c = max((p.bt_stride + S - 1) / S, (int64_t)1);  // pages per partition
     auto nonempty = [&](int r) -> int32_t {
@@ -695,7 +804,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
       s = (full_s[b + 1] - full_s[b]) + (k - empty_s[b]);
     }
     L = len_s[b];
-    __syncthreads();  // the scratch words are tile memory from here on
+    __syncthreads();  // the scratch is tile memory from here on
   } else {
     L = p.seq_lens[b];
   }
