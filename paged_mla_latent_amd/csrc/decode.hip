@@ -376,6 +376,60 @@ constexpr int smem_bytes() {
   return pipe_bytes<Fmt>() > kRedBytes ? pipe_bytes<Fmt>() : kRedBytes;
 }
 
+// Merges the four waves' softmax states through LDS and writes this segment's R query rows
+// of out ([R][kOut]) and lse ([R]).  Row group gg's states are held by the waves w with
+// w % G == gg.
+template <class TF, int G, bool kGla2, int kOut>
+__device__ __forceinline__ void finish_rows(uint8_t* smem, const f32x4 (&O)[TF::kAcc], float m_run, float l_run,
+                                            int R, int H, float* out, float* lse) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  l_run = sum_over_rows(l_run);
+  __syncthreads();
+  float* red = (float*)smem;
+  float* red_m = red + kWaves * kMaxHeads * kRedStride;
+  float* red_l = red_m + kWaves * kMaxHeads;
+  TF::store(O, red + (wave * kMaxHeads + m) * kRedStride, g);
+  if (g == 0) {
+    red_m[wave * kMaxHeads + m] = m_run;
+    red_l[wave * kMaxHeads + m] = l_run;
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < R * (kOut / 4); idx += kWaves * 64) {
+    const int r = idx / (kOut / 4);
+    const int d4 = idx % (kOut / 4);
+    const int gg = r / 16;
+    const int mm = r % 16;
+    // first O column of this row's output (GLA-g2: its head group's half)
+    const int c0 = kGla2 ? ((r % H) >= H / 2 ? 256 : 0) : 0;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = gg; w < kWaves; w += G) M = fmaxf(M, red_m[w * kMaxHeads + mm]);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = gg; w < kWaves; w += G) {
+        const float f = fast_exp2(red_m[w * kMaxHeads + mm] - M);
+        lsum += f * red_l[w * kMaxHeads + mm];
+        o += f * *(const f32x4*)(red + (w * kMaxHeads + mm) * kRedStride + c0 + 4 * d4);
+      }
+      o *= 1.0f / lsum;  // a NaN score anywhere made lsum NaN: NaN out
+    } else {
+      // No finite score.  The running maxima ignore NaN scores, but the sums do not: they
+      // are 0 for an empty partition, giving (+0, -inf), and NaN when every score was NaN.
+#pragma unroll
+      for (int w = gg; w < kWaves; w += G) lsum += red_l[w * kMaxHeads + mm];
+      o *= lsum;
+    }
+    *(f32x4*)(out + (int64_t)r * kOut + 4 * d4) = o;
+    if (d4 == 0) lse[r] = (M == -INFINITY) ? -INFINITY + lsum : (M + fast_log2(lsum)) * 0.69314718055994530942f;
+  }
+}
+
 // Query rows.  A launch decodes R = q_len x heads query rows per request (q_len > 1: the
 // query tokens of a speculative-decoding verify step, query i of a request with L tokens
 // seeing tokens 0 .. L - q_len + i).  Row r = i * heads + h.  The rows are cut into G
@@ -510,8 +564,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       const float m_new = grow ? mx : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
       l_run *= alpha;
-#pragma unroll
-      for (int u = 0; u < Fmt::kAcc; ++u) O[u] *= alpha;
+      scale_acc(O, alpha);
       m_run = m_new;
     }
     // A row that has seen no visible token yet keeps m_run = -inf: its masked scores
@@ -555,8 +608,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       const float m_new = grow ? mx : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
       l_run *= alpha;
-#pragma unroll
-      for (int u = 0; u < Fmt::kAcc; ++u) O[u] *= alpha;
+      scale_acc(O, alpha);
       m_run = m_new;
     }
     const float m_base = m_run == -INFINITY ? 0.f : m_run;
@@ -582,13 +634,15 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   int k = wave;
   // The first NB-1 tiles' page ids are ordinary loads issued with the q loads; all are
   // consumed here, so the compiler's waits for them land before the pipeline (inside it
-  // a compiler-generated vmcnt wait would also wait for the hand-counted DMAs).
+  // a compiler-generated vmcnt wait would also wait for the hand-counted DMAs).  The q
+  // fragments move to the matrix-core registers (AGPRs, beside O), which MFMA reads as
+  // directly as VGPRs: that leaves about 70 more VGPRs to the compiler's schedule.
   int32_t page_first[NB - 1];
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t)
     page_first[t] = (G == 1 ? k + kWaves * t < ntiles : ntiles > 0) ? bt[lane_token(k + kWaves * t) / ps] : 0;
 #pragma unroll
-  for (int j = 0; j < QS; ++j) asm volatile("" ::"v"(qf[j]));
+  for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t) asm volatile("" ::"v"(page_first[t]));
   // G > 1: every wave loads a tile even where its tile lies past the partition (the
@@ -665,51 +719,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
     }
   }
 
-  // ---- merge the waves' states through LDS ---------------------------------------
-  // Row group gg's states are held by the waves w with w % G == gg.
-  l_run = sum_over_rows(l_run);
-  __syncthreads();
-  float* red = (float*)smem;
-  float* red_m = red + kWaves * kMaxHeads * kRedStride;
-  float* red_l = red_m + kWaves * kMaxHeads;
-  TF::store(O, red + (wave * kMaxHeads + m) * kRedStride, g);
-  if (g == 0) {
-    red_m[wave * kMaxHeads + m] = m_run;
-    red_l[wave * kMaxHeads + m] = l_run;
-  }
-  __syncthreads();
-
-  // out / lse: this segment's R rows ([R][kOut] and [R]).
-  for (int idx = threadIdx.x; idx < R * (kOut / 4); idx += kWaves * 64) {
-    const int r = idx / (kOut / 4);
-    const int d4 = idx % (kOut / 4);
-    const int gg = r / 16;
-    const int mm = r % 16;
-    // first O column of this row's output (GLA-g2: its head group's half)
-    const int c0 = kGla2 ? ((r % H) >= H / 2 ? 256 : 0) : 0;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = gg; w < kWaves; w += G) M = fmaxf(M, red_m[w * kMaxHeads + mm]);
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = gg; w < kWaves; w += G) {
-        const float f = fast_exp2(red_m[w * kMaxHeads + mm] - M);
-        lsum += f * red_l[w * kMaxHeads + mm];
-        o += f * *(const f32x4*)(red + (w * kMaxHeads + mm) * kRedStride + c0 + 4 * d4);
-      }
-      o *= 1.0f / lsum;  // a NaN score anywhere made lsum NaN: NaN out
-    } else {
-      // No finite score.  The running maxima ignore NaN scores, but the sums do not: they
-      // are 0 for an empty partition, giving (+0, -inf), and NaN when every score was NaN.
-#pragma unroll
-      for (int w = gg; w < kWaves; w += G) lsum += red_l[w * kMaxHeads + mm];
-      o *= lsum;
-    }
-    *(f32x4*)(out + (int64_t)r * kOut + 4 * d4) = o;
-    if (d4 == 0) lse[r] = (M == -INFINITY) ? -INFINITY + lsum : (M + fast_log2(lsum)) * 0.69314718055994530942f;
-  }
+  finish_rows<TF, G, kGla2, kOut>(smem, O, m_run, l_run, R, H, out, lse);
 }
 
 // Prefix sums over the requests of a batch of B <= kMaxBalancedBatch: out[0] = 0, out[b + 1] =

@@ -152,8 +152,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_wide_kernel(DecodeParam
       const float m_new = grow ? mx : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
       l_run *= alpha;
-#pragma unroll
-      for (int u = 0; u < NU; ++u) O[u] *= alpha;
+      scale_acc(O, alpha);
       m_run = m_new;
     }
     const float m_base = m_run == -INFINITY ? 0.f : m_run;

@@ -64,6 +64,23 @@ __device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds_addr) {
                : "memory");
 }
 
+// Softmax rescale of the output accumulators, O *= alpha, for a rare wave-uniform branch (the
+// running maximum settles early).  Every accumulator is pinned to the matrix-core registers
+// (AGPRs) before and after by empty volatile asm, which also keeps the branch from being
+// executed speculatively.  Without the pin the compiler carries O around the tile loop in ordinary
+// VGPRs, where the multiply happens, and copies all of it into AGPRs and back around every
+// batch of MFMAs; executed unconditionally with alpha = 1 the multiply would cost 128 VALU
+// instructions per tile.
+template <int N>
+__device__ __forceinline__ void scale_acc(f32x4 (&O)[N], float alpha) {
+#pragma unroll
+  for (int u = 0; u < N; ++u) asm volatile("" : "+a"(O[u]));  // the copies out stay in the branch
+#pragma unroll
+  for (int u = 0; u < N; ++u) O[u] *= alpha;
+#pragma unroll
+  for (int u = 0; u < N; ++u) asm volatile("" : "+a"(O[u]));
+}
+
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
