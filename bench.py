@@ -441,7 +441,7 @@ def main():
     balanced = args.balanced
     if balanced is None:
         default_bal = workloads.BENCH_SCHEDULE[args.workload] == "balanced"
-        plain = args.q_len == 1 and args.geometry == "mla" and not args.splits
+        plain = args.geometry == "mla" and not args.splits
         balanced = workloads.BENCH_BALANCED_WORKGROUPS if (default_bal and plain) else 0
     dev = torch.device("cuda:0")
     fmt = mla.MLA_CACHE_BF16_576 if w.fmt == "bf16" else mla.MLA_CACHE_FP8_656
@@ -521,16 +521,18 @@ def main():
                                  device=dev)
         out = torch.empty((w.batch, rows, width), dtype=torch.float32, device=dev)
     if balanced:
-        if T > 1 or geom != "mla":
-            raise SystemExit("--balanced is not combined with --q-len or --geometry by this benchmark")
+        if geom != "mla":
+            raise SystemExit("--balanced is not combined with --geometry by this benchmark")
         if nope:
             decode_bal = mla.mla_decode_balanced_nope_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_nope_fp8_656
+        elif T > 1:
+            decode_bal = mla.mla_decode_mtp_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_balanced_fp8_656
         else:
             decode_bal = mla.mla_decode_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_fp8_656
         ws = torch.empty(mla.mla_decode_balanced_workspace_size(w.batch, rows, balanced), dtype=torch.uint8,
                          device=dev)
         S = 1
-        kernel = f"decode_flat_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}>'}>"
+        kernel = f"decode_flat_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}>'}, {groups}>"
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)

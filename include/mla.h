@@ -173,8 +173,10 @@ MLA_API int mla_decode_balanced_nope_fp8_656(const void* q, const void* kv_cache
  * workspace by a mla_decode_balanced_* call made with out == lse == NULL and the same
  * batch, num_heads and num_workgroups (the log-sum-exp merge contract of vLLM pull request
  * 55543).  out fp32 [batch][num_heads][512], lse fp32 [batch][num_heads]; a request with
- * no token gets (+0.0, -inf).  Errors as mla_merge_lse; MLA_ERR_WORKSPACE if
- * workspace_bytes is below mla_decode_balanced_workspace_size(). */
+ * no token gets (+0.0, -inf).  After mla_decode_mtp_balanced_* pass num_heads' = q_len *
+ * num_heads (1..MLA_MAX_QUERY_ROWS): the query rows of a request act as its heads.  Errors
+ * as mla_merge_lse; MLA_ERR_WORKSPACE if workspace_bytes is below
+ * mla_decode_balanced_workspace_size(). */
 MLA_API int mla_merge_lse_balanced(const void* workspace, size_t workspace_bytes, int32_t batch,
                                    int32_t num_heads, int32_t num_workgroups, float* out, float* lse,
                                    void* stream);
@@ -233,6 +235,31 @@ MLA_API int mla_decode_mtp_fp8_656(const void* q, const void* kv_cache, int64_t 
                                    int32_t num_heads, int32_t page_size, float softmax_scale,
                                    int32_t num_splits, float* out, float* lse, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/* Batch-balanced verify decode: the results of mla_decode_mtp_bf16 / mla_decode_mtp_fp8_656
+ * (q_len query tokens per request, the same causal reading) with the schedule of
+ * mla_decode_balanced_* (the batch's tokens cut into num_workgroups equal-cost ranges across
+ * request boundaries, each range's partials merged by log-sum-exp), so a ragged batch of
+ * verify steps finishes in one balanced wave.  The cache is still read once per request
+ * range, for all q_len query tokens.
+ * workspace  at least mla_decode_balanced_workspace_size(batch, q_len * num_heads,
+ *            num_workgroups) bytes: a partial slot holds the q_len * num_heads query rows
+ *            of its request.  Passing out == lse == NULL leaves the partials there for
+ *            mla_merge_lse_balanced(..., q_len * num_heads, num_workgroups, ...).
+ * q, out, lse, q_len as mla_decode_mtp_*; batch, num_workgroups and every other argument,
+ * result and error as mla_decode_balanced_*. */
+MLA_API int mla_decode_mtp_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                                         const int32_t* block_table, int64_t block_table_stride,
+                                         const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                                         int32_t num_heads, int32_t page_size, float softmax_scale,
+                                         int32_t num_workgroups, float* out, float* lse, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+MLA_API int mla_decode_mtp_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                                            const int32_t* block_table, int64_t block_table_stride,
+                                            const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                                            int32_t num_heads, int32_t page_size, float softmax_scale,
+                                            int32_t num_workgroups, float* out, float* lse, void* workspace,
+                                            size_t workspace_bytes, void* stream);
 
 /* Other latent geometries (qwen-mla-vllm: per-layer latent ranks 256 / 768 / 1792 with a small
  * rotary tail, "How it works"; GLA-g2, the latent split into two head groups, opening section).

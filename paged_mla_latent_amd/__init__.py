@@ -55,6 +55,7 @@ EXPORTED = (
     "mla_decode_balanced_workspace_size", "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
     "mla_merge_lse_balanced", "mla_decode_rank_workspace_size", "mla_decode_rank768_bf16",
     "mla_decode_rank1792_bf16", "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656",
+    "mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656",
 )
 
 
@@ -94,7 +95,8 @@ def library() -> ctypes.CDLL:
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = c_int
     mtp = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
-    for name in ("mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656"):
+    for name in ("mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656", "mla_decode_mtp_balanced_bf16",
+                 "mla_decode_mtp_balanced_fp8_656"):
         getattr(lib, name).argtypes = mtp
         getattr(lib, name).restype = c_int
     lib.mla_merge_lse_balanced.argtypes = [vp, c_sz, c_i32, c_i32, c_i32, vp, vp, vp]
@@ -281,7 +283,8 @@ def mla_decode_balanced_nope_fp8_656(q, kv_cache, block_table, seq_lens, softmax
 
 
 def mla_merge_lse_balanced(workspace, batch, num_heads, num_workgroups, out=None, lse=None):
-    """Merge the partials a balanced decode left in `workspace` (partials_only=True)."""
+    """Merge the partials a balanced decode left in `workspace` (partials_only=True).  After a
+    balanced verify step num_heads is q_len * heads and out / lse are [B, q_len * heads, ...]."""
     lib = library()
     if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on a HIP device")
@@ -354,6 +357,58 @@ def _decode_mtp(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_ca
         flat = workspace.view(torch.uint8)[: n * (LATENT + 1) * 4].view(torch.float32)
         return flat[: n * LATENT].view(num_splits, B, T * H, LATENT), flat[n * LATENT:].view(num_splits, B, T * H)
     return out, lse
+
+
+def _decode_mtp_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
+                         softmax_scale, num_workgroups, out, lse, workspace, partials_only=False):
+    lib = library()
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _need(kv_cache, "kv_cache", cache_dtype, 3, dev)
+    if kv_cache.shape[2] != row_bytes_last:
+        raise ValueError(f"kv_cache rows must have {row_bytes_last} elements, got {kv_cache.shape[2]}")
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, T, H, D = q.shape
+    if D != ROW:
+        raise ValueError(f"q rows must have {ROW} values, got {D}")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have one row per request")
+    if partials_only:
+        if out is not None or lse is not None:
+            raise ValueError("partials_only takes no out/lse")
+    else:
+        if out is None:
+            out = torch.empty((B, T, H, LATENT), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, 4, dev)
+        _need(lse, "lse", torch.float32, 3, dev)
+    if workspace is None:
+        need = mla_decode_balanced_workspace_size(B, T * H, num_workgroups)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    status = getattr(lib, fn)(
+        q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1],
+        seq_lens.data_ptr(), B, T, H, kv_cache.shape[1], float(softmax_scale), int(num_workgroups),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(fn, status)
+    return workspace if partials_only else (out, lse)
+
+
+def mla_decode_mtp_balanced_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256, out=None,
+                                 lse=None, workspace=None, partials_only=False):
+    """Batch-balanced verify step over a bf16 cache: q [B, q_len, H, 576] -> (out [B, q_len, H, 512],
+    lse [B, q_len, H]); partials_only=True returns the workspace for mla_merge_lse_balanced(ws, B,
+    q_len * H, num_workgroups)."""
+    return _decode_mtp_balanced("mla_decode_mtp_balanced_bf16", torch.bfloat16, ROW, q, kv_cache, block_table,
+                                seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only)
+
+
+def mla_decode_mtp_balanced_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256,
+                                    out=None, lse=None, workspace=None, partials_only=False):
+    """Batch-balanced verify step over an fp8 cache uint8 [num_pages, page_size, 656]."""
+    return _decode_mtp_balanced("mla_decode_mtp_balanced_fp8_656", torch.uint8, 656, q, kv_cache, block_table,
+                                seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only)
 
 
 def mla_decode_mtp_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,

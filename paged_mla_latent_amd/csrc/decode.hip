@@ -12,7 +12,8 @@
 //  * Two schedules share one per-segment routine (decode_segment): decode_kernel, grid
 //    (request, partition) with equal page-aligned partitions (dispatched non-empty first when
 //    the grid exceeds the compute units), and decode_flat_kernel, the batch-balanced schedule
-//    that cuts the whole batch's tokens into equal ranges across request boundaries.
+//    that cuts the whole batch's tokens into equal ranges across request boundaries (both for
+//    single-token and multi-token verify queries).
 //  * 4 waves per workgroup; each wave streams its own 16-token tiles (tiles wave, wave+4,
 //    ...) and keeps its own online-softmax state, so the single-token loop has no
 //    workgroup barrier.  The 4 states merge through LDS at the end.  Multi-token verify
@@ -28,7 +29,8 @@
 //    head, 4 tokens per lane) is exactly PV's B operand.
 //  * Online softmax in the log2 domain with a lazy rescale: the running max moves
 //    only when a tile's max exceeds it by more than 8, so probabilities stay <= 2^8
-//    and the 128-register accumulator is rescaled a handful of times per partition.
+//    and the 128-register accumulator is rescaled a handful of times per partition.  The
+//    accumulator and the q fragments stay in the matrix-core registers (AGPRs).
 //  * fp8 rows: codes widen to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1);
 //    each 128-value block's scale multiplies that block's partial score (fp32) and is
 //    folded into P for that block's PV, so no dequantised value is ever rounded.
@@ -839,8 +841,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
 // every segment start), so request b's partials are the slots b + w_first(b) .. b +
 // w_last(b), at most B + W - 1 slots in all.  Every workgroup scans seq_lens into v itself
 // (no planning launch, no dependent global reads before its first tile); workgroup 0 also
-// stores v for the merge.
-template <class Fmt>
+// stores v for the merge.  A slot holds the R = q_len x heads query rows of its request (G row
+// groups of 16, as in decode_kernel).
+template <class Fmt, int G>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
   __shared__ int64_t v_s[kMaxBalancedBatch + 1];
@@ -865,7 +868,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
     const int mid = (bl + bh) >> 1;
     if (v_s[mid] <= lo) bl = mid; else bh = mid;
   }
-  const int H = p.heads;
+  const int R = p.q_len * p.heads;
   for (int b = bl; b < B; ++b) {
     const int64_t v0 = v_s[b], v1 = v_s[b + 1];
     if (v0 >= hi) break;
@@ -875,8 +878,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
     const int64_t t0 = max(lo, s0) - s0;
     const int64_t t1 = max(min(hi, v1) - s0, (int64_t)0);  // 0: the range holds start-up only
     const int64_t slot = (int64_t)b + w;
-    decode_segment<Fmt, 1, false>(p, smem, b, L, t0, max(t0, t1), p.part_out + slot * H * kLatent,
-                                  p.part_lse + slot * H);
+    decode_segment<Fmt, G, false>(p, smem, b, L, t0, max(t0, t1), p.part_out + slot * R * kLatent,
+                                  p.part_lse + slot * R);
     __syncthreads();  // the epilogue's LDS reads finish before the next segment's loads land
   }
 }
@@ -891,6 +894,21 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<Fmt, 2>), grid, dim3(kWaves * 64), 0, stream, p);
   else
     hipLaunchKernelGGL((decode_kernel<Fmt, 4>), grid, dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Balanced launches: one row group per 16 of the R = q_len x heads query rows (kMaxG = 1: the
+// single-token geometries).
+template <class Fmt, int kMaxG>
+hipError_t launch_flat(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
+  const int R = p.q_len * p.heads;
+  const dim3 grid((unsigned)num_workgroups), block(kWaves * 64);
+  if (kMaxG == 1 || R <= 16)
+    hipLaunchKernelGGL((decode_flat_kernel<Fmt, 1>), grid, block, 0, stream, p);
+  else if (R <= 32)
+    hipLaunchKernelGGL((decode_flat_kernel<Fmt, kMaxG >= 2 ? 2 : 1>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_flat_kernel<Fmt, kMaxG>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -920,24 +938,16 @@ hipError_t launch_decode_gla2_fp8(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 hipError_t launch_decode_flat_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_flat_kernel<Bf16Rows<512, 64>>), dim3((unsigned)num_workgroups), dim3(kWaves * 64), 0,
-                     stream, p);
-  return hipGetLastError();
+  return launch_flat<Bf16Rows<512, 64>, 4>(p, num_workgroups, stream);
 }
 hipError_t launch_decode_flat_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_flat_kernel<Fp8Rows<64>>, dim3((unsigned)num_workgroups), dim3(kWaves * 64), 0,
-                     stream, p);
-  return hipGetLastError();
+  return launch_flat<Fp8Rows<64>, 4>(p, num_workgroups, stream);
 }
 hipError_t launch_decode_flat_nope_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_flat_kernel<Bf16Rows<512, 0>>), dim3((unsigned)num_workgroups), dim3(kWaves * 64), 0,
-                     stream, p);
-  return hipGetLastError();
+  return launch_flat<Bf16Rows<512, 0>, 1>(p, num_workgroups, stream);
 }
 hipError_t launch_decode_flat_nope_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_flat_kernel<Fp8Rows<0>>, dim3((unsigned)num_workgroups), dim3(kWaves * 64), 0, stream,
-                     p);
-  return hipGetLastError();
+  return launch_flat<Fp8Rows<0>, 1>(p, num_workgroups, stream);
 }
 hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream) {
   return launch<Fp8Rows<0>>(p, stream);

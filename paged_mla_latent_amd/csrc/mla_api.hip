@@ -202,13 +202,16 @@ BalancedWorkspace balanced_layout(void* workspace, int64_t batch, int64_t heads,
   return w;
 }
 
-int decode_balanced(int kind, const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
-                    int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
-                    int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out, float* lse,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+// mtp (kinds kBf16 / kFp8 only): the verify step of mla_decode_mtp_*, a slot holding the
+// q_len x num_heads query rows of its request; otherwise q_len = 1.
+int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void* kv_cache, int64_t num_pages,
+                    const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
+                    int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   static const char* const kNames[] = {"mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
                                        "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656"};
-  const char* fn = kNames[kind];
+  static const char* const kMtpNames[] = {"mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656"};
+  const char* fn = mtp ? kMtpNames[kind == kFp8] : kNames[kind];
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
@@ -221,6 +224,10 @@ int decode_balanced(int kind, const void* q, const void* kv_cache, int64_t num_p
     return fail(MLA_ERR_SHAPE, "%s: batch=%d outside [1, %d]", fn, batch, MLA_MAX_BALANCED_BATCH);
   if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
     return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_HEADS);
+  if (q_len < 1 || q_len > MLA_MAX_Q_LEN)
+    return fail(MLA_ERR_SHAPE, "%s: q_len=%d outside [1, %d]", fn, q_len, MLA_MAX_Q_LEN);
+  if (q_len * num_heads > MLA_MAX_QUERY_ROWS)
+    return fail(MLA_ERR_SHAPE, "%s: q_len * num_heads = %d exceeds %d", fn, q_len * num_heads, MLA_MAX_QUERY_ROWS);
   if (page_size < 1) return fail(MLA_ERR_SHAPE, "%s: page_size=%d must be >= 1", fn, page_size);
   if (num_pages < 1) return fail(MLA_ERR_SHAPE, "%s: num_pages=%lld must be >= 1", fn, (long long)num_pages);
   if (block_table_stride < 1)
@@ -233,7 +240,8 @@ int decode_balanced(int kind, const void* q, const void* kv_cache, int64_t num_p
   if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(block_table) || !aligned16(seq_lens) ||
       !aligned16(out) || !aligned16(lse))
     return fail(MLA_ERR_ALIGN, "%s: every tensor pointer must be 16-byte aligned", fn);
-  const size_t need = balanced_bytes_for(batch, num_heads, num_workgroups);
+  const int32_t rows = q_len * num_heads;  // query rows per request
+  const size_t need = balanced_bytes_for(batch, rows, num_workgroups);
   if (!workspace) return fail(MLA_ERR_WORKSPACE, "%s: a workspace is required", fn);
   if (!aligned16(workspace)) return fail(MLA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
   if (workspace_bytes < need)
@@ -241,7 +249,7 @@ int decode_balanced(int kind, const void* q, const void* kv_cache, int64_t num_p
   int rc = check_device();
   if (rc != MLA_OK) return rc;
 
-  BalancedWorkspace ws = balanced_layout(workspace, batch, num_heads, num_workgroups);
+  BalancedWorkspace ws = balanced_layout(workspace, batch, rows, num_workgroups);
   mla::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.cache = static_cast<const uint8_t*>(kv_cache);
@@ -250,7 +258,7 @@ int decode_balanced(int kind, const void* q, const void* kv_cache, int64_t num_p
   p.seq_lens = seq_lens;
   p.batch = batch;
   p.heads = num_heads;
-  p.q_len = 1;
+  p.q_len = q_len;
   p.page_size = page_size;
   p.num_splits = 1;
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
@@ -273,7 +281,7 @@ int decode_balanced(int kind, const void* q, const void* kv_cache, int64_t num_p
   rc = hip_status(launched, fn);
   if (rc != MLA_OK || partials_only) return rc;
   return hip_status(
-      mla::launch_merge_flat(ws.part_out, ws.part_lse, ws.cu, batch, num_heads, num_workgroups, out, lse, s),
+      mla::launch_merge_flat(ws.part_out, ws.part_lse, ws.cu, batch, rows, num_workgroups, out, lse, s),
       "mla_merge_lse_balanced (after balanced decode)");
 }
 
@@ -290,23 +298,25 @@ int mla_decode_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pa
                              int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                              int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_balanced(kBf16, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
-                         page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes, stream);
+  return decode_balanced(kBf16, false, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                         num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
+                         stream);
 }
 
 int mla_decode_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                                 int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
                                 int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups,
                                 float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_balanced(kFp8, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
-                         page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes, stream);
+  return decode_balanced(kFp8, false, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                         num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
+                         stream);
 }
 
 int mla_decode_balanced_nope_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                                   int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
                                   int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups,
                                   float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_balanced(kNopeBf16, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+  return decode_balanced(kNopeBf16, false, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                          num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
                          stream);
 }
@@ -316,7 +326,26 @@ int mla_decode_balanced_nope_fp8_656(const void* q, const void* kv_cache, int64_
                                      int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
                                      int32_t num_workgroups, float* out, float* lse, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  return decode_balanced(kNopeFp8, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+  return decode_balanced(kNopeFp8, false, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                         num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
+                         stream);
+}
+
+int mla_decode_mtp_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                                 int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                                 int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups,
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_balanced(kBf16, true, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                         num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
+                         stream);
+}
+
+int mla_decode_mtp_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                                    const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
+                                    int32_t batch, int32_t q_len, int32_t num_heads, int32_t page_size,
+                                    float softmax_scale, int32_t num_workgroups, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_balanced(kFp8, true, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                          num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
                          stream);
 }
@@ -428,8 +457,9 @@ int mla_merge_lse_balanced(const void* workspace, size_t workspace_bytes, int32_
   if (!lse) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
   if (batch < 1 || batch > MLA_MAX_BALANCED_BATCH)
     return fail(MLA_ERR_SHAPE, "%s: batch=%d outside [1, %d]", fn, batch, MLA_MAX_BALANCED_BATCH);
-  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
-    return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_HEADS);
+  // num_heads: the query rows of a request (q_len * num_heads after a verify-step decode)
+  if (num_heads < 1 || num_heads > MLA_MAX_QUERY_ROWS)
+    return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_QUERY_ROWS);
   if (num_workgroups < 1 || num_workgroups > 65535)
     return fail(MLA_ERR_SHAPE, "%s: num_workgroups=%d outside [1, 65535]", fn, num_workgroups);
   if (!aligned16(workspace) || !aligned16(out) || !aligned16(lse))

@@ -153,7 +153,7 @@ def test_merge_balanced_validation(lib):
     for kw in (dict(ws=None), dict(out=None), dict(lse=None)):
         rc, msg = call(**kw)
         assert rc == 1 and "NULL" in msg
-    for kw, word in ((dict(batch=0), "batch"), (dict(batch=1025), "batch"), (dict(heads=17), "num_heads"),
+    for kw, word in ((dict(batch=0), "batch"), (dict(batch=1025), "batch"), (dict(heads=65), "num_heads"),
                      (dict(wgs=0), "num_workgroups"), (dict(wgs=65536), "num_workgroups")):
         rc, msg = call(**kw)
         assert rc == 2 and word in msg
@@ -187,6 +187,42 @@ def _mtp(lib, fn="mla_decode_mtp_bf16", **kw):
 def test_mtp_rejects_bad_shapes(lib, fn, kw, word):
     rc, msg = _mtp(lib, fn, **kw)
     assert rc == 2 and word in msg and fn in msg
+
+
+MTP_BALANCED = ["mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656"]
+
+
+@pytest.mark.parametrize("fn", MTP_BALANCED)
+@pytest.mark.parametrize("kw, word", [
+    (dict(q_len=0), "q_len"), (dict(q_len=17), "q_len"), (dict(q_len=5, heads=16), "q_len * num_heads"),
+    (dict(heads=0), "num_heads"), (dict(heads=17, q_len=1), "num_heads"), (dict(batch=1025), "batch"),
+    (dict(splits=0), "num_workgroups"), (dict(splits=70000), "num_workgroups"),
+    (dict(scale=float("nan")), "softmax_scale"),
+])
+def test_mtp_balanced_rejects_bad_shapes(lib, fn, kw, word):
+    rc, msg = _mtp(lib, fn, ws=P, ws_bytes=1 << 30, **kw)
+    assert rc == 2 and word in msg and fn in msg
+
+
+@pytest.mark.parametrize("fn", MTP_BALANCED)
+def test_mtp_balanced_workspace_counts_query_rows(lib, fn):
+    need = mla.mla_decode_balanced_workspace_size(2, 4 * 16, 256)
+    assert need > mla.mla_decode_balanced_workspace_size(2, 16, 256)
+    rc, msg = _mtp(lib, fn, splits=256)
+    assert rc == 4 and "workspace" in msg
+    rc, msg = _mtp(lib, fn, splits=256, ws=P, ws_bytes=need - 1)
+    assert rc == 4 and str(need) in msg
+    rc, msg = _mtp(lib, fn, splits=256, ws=P, ws_bytes=need, q=None)
+    assert rc == 1 and "q is NULL" in msg and fn in msg
+    rc, msg = _mtp(lib, fn, splits=256, ws=P, ws_bytes=need, out=MIS)
+    assert rc == 3 and "aligned" in msg
+
+
+def test_merge_balanced_takes_verify_rows(lib):
+    need = mla.mla_decode_balanced_workspace_size(4, 64, 256)
+    # 64 query rows per request (q_len 4 x 16 heads): valid, only the missing device stops it
+    assert lib.mla_merge_lse_balanced(P, need, 4, 64, 256, P, P, None) == 5
+    assert lib.mla_merge_lse_balanced(P, need, 4, 65, 256, P, P, None) == 2
 
 
 @pytest.mark.parametrize("fn", ["mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656"])

@@ -346,11 +346,17 @@ def test_full_size_workloads_sampled(name):
 
 
 # ---------------------------------------------------------------- multi-token verify
-def _gpu_mtp(w, pool, q_bits, splits):
+def _gpu_mtp(w, pool, q_bits, splits, balanced=False):
+    """Per-request split verify step (num_splits = splits), or the batch-balanced one with
+    splits workgroups."""
     bt = torch.from_numpy(w.block_table).cuda()
     lens = torch.from_numpy(w.seq_lens).cuda()
-    fn = mla.mla_decode_mtp_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_fp8_656
-    out, lse = fn(bf16_dev(q_bits), pool, bt, lens, w.scale, num_splits=splits)
+    if balanced:
+        fn = mla.mla_decode_mtp_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_balanced_fp8_656
+        out, lse = fn(bf16_dev(q_bits), pool, bt, lens, w.scale, num_workgroups=splits)
+    else:
+        fn = mla.mla_decode_mtp_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_fp8_656
+        out, lse = fn(bf16_dev(q_bits), pool, bt, lens, w.scale, num_splits=splits)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -380,6 +386,64 @@ def test_mtp_parity(fmt, T, H):
     for S in (1, 4, 16, 30):  # 11 x 30 workgroups: compacted dispatch
         out, lse = _gpu_mtp(w, pd, q, S)
         _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp {fmt} T={T} H={H} S={S}")
+    # batch-balanced: a cost axis of 5,697-5,742 tokens + 9 or 10 non-empty requests x 256
+    # (8,001-8,302 positions), cut into ranges that meet many requests, split one mid-tile,
+    # or hold start-up only
+    for W in (1, 5, 64, 256, 8001, 9000):
+        out, lse = _gpu_mtp(w, pd, q, W, balanced=True)
+        _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp balanced {fmt} T={T} H={H} W={W}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_mtp_balanced_partials_then_merge(fmt):
+    """Balanced verify step with out == lse == NULL, then mla_merge_lse_balanced over the
+    q_len x heads query rows: bit-identical to one call."""
+    T, H = 3, 16
+    w = workloads.make_workload("mtp_bal_two_step", seq_lens=[3000, 0, 17, 900, 2], heads=H, page_size=16,
+                                num_pages=260, fmt=fmt, seed=9)
+    q = workloads.bf16_bits(np.random.default_rng(19).standard_normal((w.batch, T, H, 576)).astype(np.float32))
+    pd = device_pool(w)
+    qd, bt, lens = bf16_dev(q), torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    fn = mla.mla_decode_mtp_balanced_bf16 if fmt == "bf16" else mla.mla_decode_mtp_balanced_fp8_656
+    out1, lse1 = fn(qd, pd, bt, lens, w.scale, num_workgroups=100)
+    ws = fn(qd, pd, bt, lens, w.scale, num_workgroups=100, partials_only=True)
+    out2, lse2 = mla.mla_merge_lse_balanced(ws, w.batch, T * H, 100)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(w.batch, T * H, -1), out2) and torch.equal(lse1.view(w.batch, T * H), lse2)
+
+
+def test_mtp_balanced_matches_per_request_mode():
+    """One cache, two schedules of the same verify step: each within the bar of the oracle."""
+    T, H = 4, 16
+    w = workloads.make_workload("mtp_bal_vs", seq_lens=[5000, 4097, 64, 0, 1, 3000], heads=H, page_size=64,
+                                num_pages=220, fmt="fp8", seed=16)
+    q = workloads.bf16_bits(np.random.default_rng(23).standard_normal((w.batch, T, H, 576)).astype(np.float32))
+    pd, ph = device_pool(w), host_pool(w)
+    ref_o, ref_l = oracle.decode_mtp(q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt)
+    for S, bal in ((8, False), (256, True)):
+        out, lse = _gpu_mtp(w, pd, q, S, balanced=bal)
+        _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp fp8 {'W' if bal else 'S'}={S}")
+
+
+def test_mtp_balanced_full_size_fp8_ragged_sampled():
+    """Four verify tokens per request over the fp8 ragged batch, batch-balanced with the bench's
+    workgroup count; the oracle checks the first, a middle and the last non-empty request."""
+    w = workloads.NAMED["fp8_ragged"]()
+    W, T = workloads.BENCH_BALANCED_WORKGROUPS, 4
+    q = workloads.bf16_bits(np.random.default_rng(8).standard_normal((w.batch, T, w.heads, 576)).astype(np.float32))
+    live = np.flatnonzero(w.seq_lens > 0)
+    req = sorted({int(live[0]), int(live[len(live) // 2]), int(live[-1])})
+    say(f"case mtp fp8_ragged balanced: q_len={T} W={W} oracle requests={req}")
+    pd = device_pool(w)
+    out, lse = _gpu_mtp(w, pd, q, W, balanced=True)
+    seen = w.seq_lens[:, None] - T + 1 + np.arange(T)[None, :] > 0
+    assert np.isfinite(out[seen]).all() and np.isfinite(lse[seen]).all()
+    assert np.isneginf(lse[~seen]).all() and (out[~seen] == 0).all()
+    ph = w.poisoned_pool()
+    idx = np.unique(np.searchsorted(w.slots, np.concatenate([_request_slots(w, b) for b in req])))
+    ph.reshape(-1, w.row_bytes)[w.slots[idx]] = oracle.pack_rows(w.latent[idx], w.k_pe[idx], w.fmt)
+    ref_o, ref_l = oracle.decode_mtp(q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=req)
+    _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp fp8_ragged balanced W={W}", requests=req)
 
 
 def test_mtp_single_query_is_plain_decode():
