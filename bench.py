@@ -62,6 +62,9 @@ def _parse():
                          "last-level cache between repetitions); the roofline then uses these cold times")
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="steps captured per HIP graph (the largest divisor of --steps up to this)")
+    ap.add_argument("--row-loads", choices=("streaming", "cached"), default=None,
+                    help="row-load policy of the bf16-row decodes (mla_set_row_loads); default: the "
+                         "workload's entry in workloads.BENCH_ROW_LOADS")
     ap.add_argument("--eager", action="store_true",
                     help="time only eager launches (default: also replay the step from a captured HIP graph, "
                          "which gives the reported value)")
@@ -443,6 +446,8 @@ def main():
         default_bal = workloads.BENCH_SCHEDULE[args.workload] == "balanced"
         plain = args.geometry == "mla" and not args.splits
         balanced = workloads.BENCH_BALANCED_WORKGROUPS if (default_bal and plain) else 0
+    row_loads = args.row_loads or workloads.BENCH_ROW_LOADS[args.workload]
+    mla.mla_set_row_loads(mla.MLA_ROW_LOADS_CACHED if row_loads == "cached" else mla.MLA_ROW_LOADS_STREAMING)
     dev = torch.device("cuda:0")
     fmt = mla.MLA_CACHE_BF16_576 if w.fmt == "bf16" else mla.MLA_CACHE_FP8_656
 
@@ -648,6 +653,7 @@ def main():
             "workload": w.name, "batch": w.batch, "heads": w.heads, "context_tokens": w.tokens,
             "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
             "schedule": f"batch-balanced, {balanced} workgroups" if balanced else "per-request partitions",
+            "row_loads": row_loads if w.fmt == "bf16" and geom not in ("rank768", "rank1792") else "plain",
             "layer": "nope-512" if nope else "rope-576", "query_tokens_per_request": T, "geometry": geom,
             "cache_row_bytes": 2 * (RANKS[geom] + 64) if geom in RANKS else w.row_bytes,
             "row_bytes_read": row_bytes_read,

@@ -40,6 +40,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 MLA_OK = 0
 MLA_CACHE_BF16_576 = 0
 MLA_CACHE_FP8_656 = 1
+MLA_ROW_LOADS_STREAMING = 0
+MLA_ROW_LOADS_CACHED = 1
 LATENT, ROPE, ROW = 512, 64, 576
 ROW_BYTES = {MLA_CACHE_BF16_576: 1152, MLA_CACHE_FP8_656: 656}
 MAX_HEADS = 16
@@ -55,7 +57,7 @@ EXPORTED = (
     "mla_decode_balanced_workspace_size", "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
     "mla_merge_lse_balanced", "mla_decode_rank_workspace_size", "mla_decode_rank768_bf16",
     "mla_decode_rank1792_bf16", "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656",
-    "mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656",
+    "mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656", "mla_set_row_loads",
 )
 
 
@@ -115,8 +117,19 @@ def library() -> ctypes.CDLL:
     lib.mla_last_error_message.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
     lib.mla_abi_version.restype = c_int
+    lib.mla_set_row_loads.argtypes = [c_int]
+    lib.mla_set_row_loads.restype = c_int
     _lib = lib
     return lib
+
+
+def mla_set_row_loads(policy: int) -> int:
+    """Row-load policy of the bf16-row decodes (MLA_ROW_LOADS_STREAMING, the default, or
+    MLA_ROW_LOADS_CACHED for batches that share pages within a step); returns the previous one."""
+    prev = library().mla_set_row_loads(int(policy))
+    if prev < 0:
+        _check("mla_set_row_loads", -prev)
+    return prev
 
 
 def _check(fn: str, status: int) -> None:

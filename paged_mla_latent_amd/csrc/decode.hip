@@ -66,41 +66,53 @@ struct Bf16Rows {
 
   struct Aux {};
 
-  __device__ static __forceinline__ int dma_token(int lane) { return lane >> 2; }
+  // Tiles in the line layout (line_pos): lane L fetches tokens L >> 3 and 8 + (L >> 3) of a
+  // tile, whole 128-byte lines, with the non-temporal hint unless cached loads were asked for.
+  static constexpr int kTokensPerLane = 2;
+  __device__ static __forceinline__ int fetch_token(int lane, int i) { return (lane >> 3) + 8 * i; }
 
-  __device__ static __forceinline__ void issue(const uint8_t* row, uint32_t dst, int lane) {
-    const uint8_t* src = row + 16 * ((lane & 3) ^ swz(lane >> 2));
+  __device__ static __forceinline__ void issue(const uint8_t* const (&rows)[2], uint32_t dst, int lane, bool nt) {
+    const int cv = 16 * ((lane & 7) ^ line_swz(lane >> 3));
+    if (nt) {
 #pragma unroll
-    for (int j = 0; j < kDmaOps; ++j) dma16(src + 64 * j, dst + 1024 * j);
+      for (int j = 0; j < kDmaOps; ++j) dma16_nt(rows[j & 1] + 128 * (j >> 1) + cv, dst + 1024 * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kDmaOps; ++j) dma16(rows[j & 1] + 128 * (j >> 1) + cv, dst + 1024 * j);
+    }
   }
 
-  // K-step j reads chunk 4j + g of token m (the A operand: token m, values 32j + 8g ..).
+  // K-step j reads chunk 4j + g of token m (the A operand: token m, values 32j + 8g ..), at
+  // line_pos(m, 4 (j & 1) + g) + 128 (j >> 1).
   __device__ static __forceinline__ f32x4 qk(const uint8_t* buf, int m, int g, const u32x4* qf, Aux&) {
-    const uint8_t* base = buf + 16 * chunk_pos(m, g);
+    const uint8_t* base0 = buf + 16 * line_pos(m, g);
+    const uint8_t* base1 = buf + 16 * line_pos(m, 4 + g);
     // Two independent accumulation chains halve the dependent-MFMA latency.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
     for (int j = 0; j < kQSteps; j += 2) {
-      s0 = mfma_16x16x32(*(const u32x4*)(base + 1024 * j), qf[j], s0);
-      s1 = mfma_16x16x32(*(const u32x4*)(base + 1024 * (j + 1)), qf[j + 1], s1);
+      s0 = mfma_16x16x32(*(const u32x4*)(base0 + 1024 * j), qf[j], s0);
+      s1 = mfma_16x16x32(*(const u32x4*)(base1 + 1024 * j), qf[j + 1], s1);
     }
     return s0 + s1;
   }
 
   // 16-wide column group u: lane (m, g) addresses token 4g + (m >> 2), values
-  // 16u + 4(m & 3) .. +4, i.e. chunk 2u + ((m >> 1) & 1), half m & 1.
+  // 16u + 4(m & 3) .. +4, i.e. chunk 2u + ((m >> 1) & 1), half m & 1: at
+  // line_pos(t, 2 (u & 3) + ((m >> 1) & 1)) + 128 (u >> 2).
+  __device__ static __forceinline__ void pv_bases(const uint8_t* buf, int m, int g, const uint8_t* (&b)[4]) {
+    const int t = 4 * g + (m >> 2);
+    const int cc = (m >> 1) & 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r] = buf + 16 * line_pos(t, 2 * r + cc) + 8 * (m & 1);
+  }
   __device__ static __forceinline__ void pv(const uint8_t* buf, int m, int g, const float (&p)[4],
                                             const Aux&, f32x4 (&O)[kAcc]) {
     const u32x2 pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-    const int t = 4 * g + (m >> 2);
-    const int cc = (m >> 1) & 1;
-    const uint8_t* b0 = buf + 16 * chunk_pos(t, cc) + 8 * (m & 1);      // u even
-    const uint8_t* b1 = buf + 16 * chunk_pos(t, 2 + cc) + 8 * (m & 1);  // u odd
+    const uint8_t* b[4];
+    pv_bases(buf, m, g, b);
 #pragma unroll
-    for (int u = 0; u < kAcc; u += 2) {
-      O[u] = mfma_16x16x16(lds_read_tr16(b0 + 512 * u), pb, O[u]);
-      O[u + 1] = mfma_16x16x16(lds_read_tr16(b1 + 512 * u), pb, O[u + 1]);
-    }
+    for (int u = 0; u < kAcc; ++u) O[u] = mfma_16x16x16(lds_read_tr16(b[u & 3] + 2048 * (u >> 2)), pb, O[u]);
   }
 
   // PV over two tiles at once with the 32-deep MFMA (the 16-deep one takes as many cycles for
@@ -111,16 +123,14 @@ struct Bf16Rows {
                                              f32x4 (&O)[kAcc]) {
     const u32x4 p8 = {pack_bf16(pa[0], pa[1]), pack_bf16(pa[2], pa[3]), pack_bf16(pb[0], pb[1]),
                       pack_bf16(pb[2], pb[3])};
-    const int t = 4 * g + (m >> 2);
-    const int cc = (m >> 1) & 1;
-    const int o0 = 16 * chunk_pos(t, cc) + 8 * (m & 1);
-    const int o1 = 16 * chunk_pos(t, 2 + cc) + 8 * (m & 1);
+    const uint8_t* ba[4];
+    pv_bases(bufa, m, g, ba);
+    const int db = (int)(bufb - bufa);
 #pragma unroll
-    for (int u = 0; u < kAcc; u += 2) {
-      const u32x2 a0 = lds_read_tr16(bufa + o0 + 512 * u), b0 = lds_read_tr16(bufb + o0 + 512 * u);
-      const u32x2 a1 = lds_read_tr16(bufa + o1 + 512 * u), b1 = lds_read_tr16(bufb + o1 + 512 * u);
-      O[u] = mfma_16x16x32(u32x4{a0[0], a0[1], b0[0], b0[1]}, p8, O[u]);
-      O[u + 1] = mfma_16x16x32(u32x4{a1[0], a1[1], b1[0], b1[1]}, p8, O[u + 1]);
+    for (int u = 0; u < kAcc; ++u) {
+      const uint8_t* a = ba[u & 3] + 2048 * (u >> 2);
+      const u32x2 x = lds_read_tr16(a), y = lds_read_tr16(a + db);
+      O[u] = mfma_16x16x32(u32x4{x[0], x[1], y[0], y[1]}, p8, O[u]);
     }
   }
 
@@ -156,9 +166,13 @@ struct Fp8Rows {
     f32x4 sc[4];  // sc[r][k]: scale of block k of token 4g + r
   };
 
-  __device__ static __forceinline__ int dma_token(int lane) { return lane >> 2; }
+  // Tiles in the chunk layout (chunk_pos): lane L fetches token L >> 2 of a tile, 64 bytes of
+  // its row per instruction (656-byte rows do not start on 128-byte lines).
+  static constexpr int kTokensPerLane = 1;
+  __device__ static __forceinline__ int fetch_token(int lane, int) { return lane >> 2; }
 
-  __device__ static __forceinline__ void issue(const uint8_t* row, uint32_t dst, int lane) {
+  __device__ static __forceinline__ void issue(const uint8_t* const (&rows)[1], uint32_t dst, int lane, bool) {
+    const uint8_t* row = rows[0];
     const uint8_t* src = row + 16 * ((lane & 3) ^ swz(lane >> 2));
 #pragma unroll
     for (int j = 0; j < kFullOps; ++j) dma16(src + 64 * j, dst + 1024 * j);
@@ -509,7 +523,8 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 
   const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
   const uint32_t ps = (uint32_t)p.page_size;
-  const int my_tok = Fmt::dma_token(lane);
+  const int my_tok = lane >> 2;  // the token whose page id this lane fetches
+  constexpr int TPL = Fmt::kTokensPerLane;  // the tokens whose rows this lane fetches
   // Tile buffers per wave: Fmt::kBufs for one row group; the shared-tile loop of G > 1 is
   // written for two.
   constexpr int NB = G == 1 ? Fmt::kBufs : 2;
@@ -521,13 +536,15 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   // Tokens and page indices fit in 32 bits (seq_lens are int32).
   const uint32_t t0 = (uint32_t)rg.t0;
   const uint32_t tlast = (uint32_t)(rg.t1 - 1);
-  auto lane_token = [&](int k) -> uint32_t {
-    const uint32_t t = t0 + (uint32_t)k * kTile + (uint32_t)my_tok;
+  auto clamp_token = [&](int k, int within) -> uint32_t {
+    const uint32_t t = t0 + (uint32_t)k * kTile + (uint32_t)within;
     return t > tlast ? tlast : t;
   };
-  // Page ids travel HBM -> LDS by DMA as well (one 4-byte entry per lane, lane l's own
-  // token), well ahead of use, so that no compiler-visible load sits in the loop: the
-  // only vector-memory operations are these DMAs, whose completion is counted by hand.
+  auto lane_token = [&](int k) -> uint32_t { return clamp_token(k, my_tok); };
+  // Page ids travel HBM -> LDS by DMA as well (one 4-byte entry per lane: lane l holds the
+  // page of token l >> 2, so token T's entry is at byte 16T), well ahead of use, so that no
+  // compiler-visible load sits in the loop: the only vector-memory operations are these DMAs,
+  // whose completion is counted by hand.
   uint8_t* pslot = smem + kWaves * NR * Fmt::kTileBytes + wave * NB * 256;
   const uint32_t plds = __builtin_amdgcn_readfirstlane(lds_offset(pslot));
   // widened tiles, one slot per wave, after the raw tiles and page-id slots
@@ -538,12 +555,22 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
     const uint32_t pi = lane_token(k) / ps;
     dma4(bt + pi, slot);
   };
-  auto row_of = [&](uint32_t tok, int32_t page) -> const uint8_t* {
-    const uint32_t within = tok % ps;
-    const int64_t slot = (int64_t)page * (int64_t)ps + (int64_t)within;
-    return p.cache + slot * (int64_t)Fmt::kRowBytes;
+  // The rows this lane fetches in tile k, from their pages.
+  using Pages = int32_t[TPL];
+  auto issue_tile = [&](int k, const Pages& page, uint32_t dst) {
+    const uint8_t* rows[TPL];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const uint32_t tok = clamp_token(k, Fmt::fetch_token(lane, i));
+      const int64_t slot = (int64_t)page[i] * (int64_t)ps + (int64_t)(tok % ps);
+      rows[i] = p.cache + slot * (int64_t)Fmt::kRowBytes;
+    }
+    Fmt::issue(rows, dst, lane, p.stream_rows != 0);
   };
-  auto read_page = [&](const uint8_t* slot) -> int32_t { return *(const int32_t*)(slot + 4 * lane); };
+  auto read_pages = [&](const uint8_t* slot, Pages& page) {
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) page[i] = *(const int32_t*)(slot + 16 * Fmt::fetch_token(lane, i));
+  };
 
   // One tile of work: QK^T, online softmax, PV on tile k (partition-relative) in `buf`.
   // Tokens at or past this lane's visibility limit, or past the partition, get p = 0.
@@ -639,14 +666,20 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   // a compiler-generated vmcnt wait would also wait for the hand-counted DMAs).  The q
   // fragments move to the matrix-core registers (AGPRs, beside O), which MFMA reads as
   // directly as VGPRs: that leaves about 70 more VGPRs to the compiler's schedule.
-  int32_t page_first[NB - 1];
+  int32_t page_first[NB - 1][TPL];
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t)
-    page_first[t] = (G == 1 ? k + kWaves * t < ntiles : ntiles > 0) ? bt[lane_token(k + kWaves * t) / ps] : 0;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+      page_first[t][i] = (G == 1 ? k + kWaves * t < ntiles : ntiles > 0)
+                             ? bt[clamp_token(k + kWaves * t, Fmt::fetch_token(lane, i)) / ps]
+                             : 0;
 #pragma unroll
   for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
 #pragma unroll
-  for (int t = 0; t < NB - 1; ++t) asm volatile("" ::"v"(page_first[t]));
+  for (int t = 0; t < NB - 1; ++t)
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) asm volatile("" ::"v"(page_first[t][i]));
   // G > 1: every wave loads a tile even where its tile lies past the partition (the
   // partition's last rows again, clamped by lane_token), so that every buffer of a step holds
   // finite rows and the step's tiles can be scored without a branch per tile.
@@ -654,8 +687,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 #pragma unroll
     for (int t = 0; t < NB - 1; ++t) {
       fetch_page(min(k + kWaves * (t + NB - 1), ntiles - 1), plds + 256 * t);
-      if (G > 1 || k + kWaves * t < ntiles)
-        Fmt::issue(row_of(lane_token(k + kWaves * t), page_first[t]), wlds + t * Fmt::kTileBytes, lane);
+      if (G > 1 || k + kWaves * t < ntiles) issue_tile(k + kWaves * t, page_first[t], wlds + t * Fmt::kTileBytes);
     }
   }
 
@@ -675,9 +707,10 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       for (; k + kWaves * (NB - 1) < ntiles; k += kWaves) {
         const int ahead = cur == 0 ? NB - 1 : cur - 1;  // (cur + NB - 1) mod NB
         wait_vmcnt<(NB - 1) * D + (NB - 2)>();  // page ids of tile k + 4(NB-1) have landed
-        const int32_t page_n = read_page(pslot + 256 * cur);
+        Pages page_n;
+        read_pages(pslot + 256 * cur, page_n);
         fetch_page(min(k + kWaves * 2 * (NB - 1), ntiles - 1), plds + 256 * ahead);
-        Fmt::issue(row_of(lane_token(k + kWaves * (NB - 1)), page_n), wlds + ahead * Fmt::kTileBytes, lane);
+        issue_tile(k + kWaves * (NB - 1), page_n, wlds + ahead * Fmt::kTileBytes);
         wait_vmcnt<(NB - 1) * (D + 1)>();  // tile k has landed
         compute(wbuf + cur * Fmt::kTileBytes, k);
         cur = cur + 1 == NB ? 0 : cur + 1;
@@ -712,9 +745,10 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       if (i + 1 < nsteps) {
         // this wave's tile of step i + 1, clamped to the partition's last tile
         const int kn = min(kWaves * (i + 1) + wave, ntiles - 1);
-        const int32_t page_n = read_page(pslot + 256 * (i & 1));
+        Pages page_n;
+        read_pages(pslot + 256 * (i & 1), page_n);
         fetch_page(min(kn + kWaves, ntiles - 1), plds + 256 * ((i + 1) & 1));
-        Fmt::issue(row_of(lane_token(kn), page_n), wlds + (kConv ? 0 : ((i + 1) & 1) * Fmt::kTileBytes), lane);
+        issue_tile(kn, page_n, wlds + (kConv ? 0 : ((i + 1) & 1) * Fmt::kTileBytes));
       }
       if constexpr (kConv) __syncthreads();
       compute_step(i, u0);

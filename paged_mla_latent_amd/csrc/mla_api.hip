@@ -58,6 +58,9 @@ int device_cus() {
   return g_cus[dev].load(std::memory_order_relaxed);
 }
 
+// Row-load policy of the bf16-row decodes (mla_set_row_loads), process-wide.
+std::atomic<int> g_row_loads{MLA_ROW_LOADS_STREAMING};
+
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return MLA_OK;
   return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -160,6 +163,7 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
   // Merged here: empty partitions need not leave the (0, -inf) partial that a caller's own merge
   // of the workspace would read.
   p.skip_empty = num_splits > 1 && !partials_only;
+  p.stream_rows = g_row_loads.load(std::memory_order_relaxed) == MLA_ROW_LOADS_STREAMING;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t launched;
   switch (kind) {
@@ -269,6 +273,7 @@ int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void
   p.cu = ws.cu;
   p.compact = 0;
   p.skip_empty = 0;
+  p.stream_rows = g_row_loads.load(std::memory_order_relaxed) == MLA_ROW_LOADS_STREAMING;
   static_assert(MLA_MAX_BALANCED_BATCH == mla::kMaxBalancedBatch, "batch limit of the balanced kernels");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t launched;
@@ -586,5 +591,13 @@ const char* mla_status_string(int status) {
 const char* mla_last_error_message(void) { return g_message; }
 
 int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+int mla_set_row_loads(int policy) {
+  if (policy != MLA_ROW_LOADS_STREAMING && policy != MLA_ROW_LOADS_CACHED) {
+    fail(MLA_ERR_SHAPE, "mla_set_row_loads: unknown policy %d", policy);
+    return -MLA_ERR_SHAPE;
+  }
+  return g_row_loads.exchange(policy, std::memory_order_relaxed);
+}
 
 }  // extern "C"

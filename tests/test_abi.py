@@ -319,6 +319,17 @@ def test_gather_validation(lib):
     assert call(total=0, kv=None, out=None)[0] == 0  # nothing to gather: no device needed
 
 
+def test_row_load_policy(lib):
+    # host-side state only: returns the previous policy, refuses unknown ones
+    assert lib.mla_set_row_loads(mla.MLA_ROW_LOADS_CACHED) == mla.MLA_ROW_LOADS_STREAMING
+    assert lib.mla_set_row_loads(mla.MLA_ROW_LOADS_STREAMING) == mla.MLA_ROW_LOADS_CACHED
+    assert lib.mla_set_row_loads(7) == -2
+    assert "policy" in lib.mla_last_error_message().decode()
+    assert mla.mla_set_row_loads(mla.MLA_ROW_LOADS_STREAMING) == mla.MLA_ROW_LOADS_STREAMING
+    with pytest.raises(mla.MlaError):
+        mla.mla_set_row_loads(-1)
+
+
 def test_error_message_is_thread_local(lib):
     import threading
     _decode(lib, heads=99)

@@ -446,6 +446,27 @@ def test_mtp_balanced_full_size_fp8_ragged_sampled():
     _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp fp8_ragged balanced W={W}", requests=req)
 
 
+def test_row_load_policies_agree():
+    """Streaming (non-temporal) and cached row loads give bit-identical results, per-request,
+    batch-balanced, verify-step and NoPE; the streaming result is checked against the oracle."""
+    w = workloads.make_workload("row_loads", seq_lens=[3000, 0, 17, 900, 64, 1], heads=16, page_size=16,
+                                num_pages=260, seed=21)
+    q4 = workloads.bf16_bits(np.random.default_rng(29).standard_normal((w.batch, 4, 16, 576)).astype(np.float32))
+    pd, ph = device_pool(w), host_pool(w)
+    runs = {}
+    try:
+        for policy in (mla.MLA_ROW_LOADS_STREAMING, mla.MLA_ROW_LOADS_CACHED):
+            mla.mla_set_row_loads(policy)
+            runs[policy] = [gpu_decode(w, pd, 4), gpu_decode(w, pd, 64, balanced=True),
+                            gpu_decode(w, pd, 4, nope=True), _gpu_mtp(w, pd, q4, 4), _gpu_mtp(w, pd, q4, 64, True)]
+    finally:
+        mla.mla_set_row_loads(mla.MLA_ROW_LOADS_STREAMING)
+    for a, b in zip(runs[mla.MLA_ROW_LOADS_STREAMING], runs[mla.MLA_ROW_LOADS_CACHED]):
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt)
+    assert_parity(w, *runs[mla.MLA_ROW_LOADS_STREAMING][0], ref_o, ref_l, what="streaming loads S=4")
+
+
 def test_mtp_single_query_is_plain_decode():
     w = workloads.make_workload("mtp1", seq_lens=[3000, 5, 0, 777], heads=16, page_size=64, num_pages=70, seed=5)
     pd = device_pool(w)

@@ -362,3 +362,15 @@ BENCH_SCHEDULE = {
     "high_slot": "balanced",
     "fp8_ragged": "balanced",
 }
+
+# Row-load policy of the bf16-row decodes per named workload: streaming (non-temporal) loads
+# where every row is read once per step; cached loads for the high-slot batch, whose requests
+# share pages (12,058 pages above the wrap slot for about 47,500 page reads), so repeated rows
+# can hit in the L2 and last-level cache.
+BENCH_ROW_LOADS = {
+    "tiny": "streaming",
+    "batched": "streaming",
+    "long_context": "streaming",
+    "high_slot": "cached",
+    "fp8_ragged": "streaming",
+}
