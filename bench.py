@@ -653,7 +653,7 @@ def main():
             "workload": w.name, "batch": w.batch, "heads": w.heads, "context_tokens": w.tokens,
             "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
             "schedule": f"batch-balanced, {balanced} workgroups" if balanced else "per-request partitions",
-            "row_loads": row_loads if w.fmt == "bf16" and geom not in ("rank768", "rank1792") else "plain",
+            "row_loads": row_loads if w.fmt == "bf16" and geom != "rank768" else "plain",
             "layer": "nope-512" if nope else "rope-576", "query_tokens_per_request": T, "geometry": geom,
             "cache_row_bytes": 2 * (RANKS[geom] + 64) if geom in RANKS else w.row_bytes,
             "row_bytes_read": row_bytes_read,

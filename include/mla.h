@@ -380,10 +380,10 @@ MLA_API int mla_gather_context(const void* kv_cache, int32_t cache_format, int64
  * streaming rate (long context, random pages: 211 -> 189 us per decode on MI355X) but keeps
  * rows out of the caches.  MLA_ROW_LOADS_CACHED: plain loads, for batches whose requests share
  * pages within a step (prefix sharing), whose repeated rows then hit in the L2 / last-level
- * cache.  Applies to every later mla_decode*_bf16 call in the process (also the batch-balanced
- * and verify-step ones; the rank-768 / rank-1792 decodes always use plain loads; fp8 rows do
- * not start on 128-byte lines and always use plain loads).  Returns the previous policy, or
- * -MLA_ERR_SHAPE for an unknown one. */
+ * cache.  Applies to every later mla_decode*_bf16 call in the process (also the batch-balanced,
+ * verify-step and rank-1792 ones; the rank-768 decode reads 64-byte row segments and always
+ * uses plain loads, as do fp8 rows, which do not start on 128-byte lines).  Returns the
+ * previous policy, or -MLA_ERR_SHAPE for an unknown one. */
 enum { MLA_ROW_LOADS_STREAMING = 0, MLA_ROW_LOADS_CACHED = 1 };
 MLA_API int mla_set_row_loads(int policy);
 
