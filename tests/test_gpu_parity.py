@@ -192,13 +192,16 @@ def test_merge_kernel_propagates_nan():
 # ----------------------------------------------------------------- 64-bit addressing
 @pytest.mark.parametrize("fmt, num_pages", [("bf16", 60000), ("fp8", 110000)])
 def test_pages_beyond_32bit_offsets(fmt, num_pages):
-    """Requests on the page that straddles slot 3,728,270 and on pages past 2^32 bytes."""
+    """Requests on the page that straddles slot 3,728,270 (int32 element offsets of 576-value
+    rows wrap there), on the page that straddles slot 3,273,603 (int32 byte offsets of 656-byte
+    rows wrap there) and on pages past 2^32 bytes."""
     ps = 64
     straddle = workloads.WRAP_SLOT // ps  # holds slots 3,728,256 .. 3,728,319
+    straddle8 = workloads.FP8_WRAP_SLOT // ps  # holds slots 3,273,600 .. 3,273,663
     top = num_pages - 1
     assert top * ps * oracle.ROW_BYTES[fmt] > 2**32
-    layout = [[straddle, straddle + 1, 17, top], [top - 1, top - 2, straddle + 2], [3, straddle], [top]]
-    lens = [4 * ps - 5, 3 * ps, 2 * ps, 40]
+    layout = [[straddle, straddle + 1, 17, top], [top - 1, top - 2, straddle + 2], [3, straddle, straddle8], [top]]
+    lens = [4 * ps - 5, 3 * ps, 3 * ps - 7, 40]
     rng = np.random.default_rng(8)
     w = workloads.make_workload(f"wrap_{fmt}", seq_lens=lens, heads=16, page_size=ps, num_pages=num_pages,
                                 fmt=fmt, seed=8)
@@ -218,6 +221,9 @@ def test_pages_beyond_32bit_offsets(fmt, num_pages):
     pe = workloads.bf16_bits(rng.standard_normal((T, 64)).astype(np.float32))
     w.block_table, w.slots, w.latent, w.k_pe = bt, slots, lat, pe
     assert any(s // ps == straddle for s in slots) and slots.max() * oracle.ROW_BYTES[fmt] > 2**32
+    # both sides of the 656-byte rows' int32 byte-offset wrap are read
+    assert any(s * 656 < 2**31 for s in slots if s // ps == straddle8)
+    assert any(2**31 <= s * 656 < 2**32 for s in slots if s // ps == straddle8)
     say(f"case wrap_{fmt}: max slot {slots.max()} byte offset {slots.max() * oracle.ROW_BYTES[fmt]}")
     # teeth: an int32 element offset would land elsewhere for these slots
     assert any(oracle.element_offset_int32(int(s)) != oracle.element_offset(int(s)) for s in slots)
@@ -273,6 +279,42 @@ def test_balanced_matches_per_request_mode():
     w = workloads.make_workload("bal_vs", seq_lens=[5000, 4097, 64, 0, 1, 3000], heads=16, page_size=64,
                                 num_pages=220, seed=6)
     _run_case(w, [1, 64], balanced=[256, 1024])
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_context_parallel_shares_merge(fmt):
+    """Decode context parallelism rehearsed on one device: each request's pages are dealt out
+    to 8 disjoint shares (as 8 devices would hold them), every share is decoded on its own with
+    its partials kept (out = lse = NULL), and one mla_merge_lse over all shares' partials gives
+    the whole requests' results (the partial-result merge contract of vLLM pull request 55543)."""
+    ps, G, S = 64, 8, 4
+    w = workloads.make_workload("cp_shares", seq_lens=[4096, 3000, 64, 0, 700], heads=16, page_size=ps,
+                                num_pages=200, fmt=fmt, seed=31)
+    pd, ph = device_pool(w), host_pool(w)
+    q = bf16_dev(w.q)
+    fn = mla.mla_decode_bf16 if fmt == "bf16" else mla.mla_decode_fp8_656
+    parts_o, parts_l = [], []
+    for share in range(G):
+        # share g holds pages g, g + 8, ... of every request (a strided deal, so every share
+        # sees every request's context spread out; a request shorter than the deal leaves
+        # some shares empty)
+        bt = np.zeros((w.batch, w.block_table.shape[1]), dtype=np.int32)
+        lens = np.zeros(w.batch, dtype=np.int32)
+        for b in range(w.batch):
+            n_pages = -(-int(w.seq_lens[b]) // ps)
+            mine = list(range(share, n_pages, G))
+            bt[b, :len(mine)] = w.block_table[b, mine]
+            last_full = n_pages - 1
+            lens[b] = sum(ps if pg < last_full else int(w.seq_lens[b]) - ps * last_full for pg in mine)
+        po, pl = fn(q, pd, torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(), w.scale, num_splits=S,
+                    partials_only=True)
+        parts_o.append(po.clone())
+        parts_l.append(pl.clone())
+    out, lse = mla.mla_merge_lse(torch.cat(parts_o), torch.cat(parts_l))
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, ps, w.scale, fmt)
+    assert_parity(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l,
+                  what=f"context-parallel shares {fmt}")
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])

@@ -274,6 +274,7 @@ def _slots_of_pages(used_pages: np.ndarray, fill: np.ndarray, ps: int) -> np.nda
 # --------------------------------------------------------------------------------------
 
 WRAP_SLOT = 2**31 // ROW  # 3,728,270: first slot whose int32 element offset overflows
+FP8_WRAP_SLOT = 2**31 // 656  # 3,273,603: the same for the int32 byte offset of 656-byte rows
 
 
 def tiny(seed: int = 0) -> Workload:
