@@ -24,7 +24,8 @@
  *    are asynchronous on that stream, never synchronise the device and never
  *    read device memory from the host.
  *  - The caller owns all memory.  The library allocates nothing and keeps no
- *    state beyond a per-device architecture check and a thread-local message.
+ *    state beyond a per-device architecture check, a thread-local message and
+ *    the process-wide row-load hint of mla_set_row_loads (performance only).
  *  - Arguments are validated on the host before any launch.  On error the call
  *    returns a nonzero MLA_ERR_* code, launches nothing and records a message
  *    (mla_last_error_message) naming the offending argument.  Nothing aborts,
