@@ -22,6 +22,8 @@
 //  * Rows go HBM -> LDS with 16-byte direct-to-LDS loads (no VGPR round trip), two or three
 //    buffers per wave; the page ids travel by DMA as well, ahead of the rows that need
 //    them, and completion is counted by hand, so no compiler-inserted wait stalls the loop.
+//    bf16 rows are loaded whole 128-byte lines per instruction (the line layout), so the
+//    loads can carry the non-temporal hint; fp8 rows, not line-aligned, 64 bytes per row.
 //  * All 16 heads share every row, so QK^T is a real 16 x 16 x 576 contraction per
 //    tile (v_mfma_f32_16x16x32_bf16, rows as A, q^T as B) and PV a 512 x 16 x 16 one
 //    (v_mfma_f32_16x16x16_bf16, rows^T as A via ds_read_b64_tr_b16, P^T as B; two tiles
@@ -45,7 +47,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kTile = 16;
 constexpr float kRescaleThreshold = 8.0f;
-
 
 // Rows of kLat latent values followed by 64 rope values, bf16.  kLat = 512, kRopeDim = 64:
 // the 576-value row.  kRopeDim = 0 (NoPE-512 layers): only the 512 latent values (the
