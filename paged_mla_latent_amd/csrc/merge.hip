@@ -111,16 +111,21 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_counted_kernel(const fl
 }
 
 // Batch-balanced mode: request b's partials are the slots b + w for the workgroups w whose
-// cost-axis ranges meet [cu[b], cu[b + 1]) (the axis the decode stored); head h of slot q
-// is row q * heads + h.
-__global__ __launch_bounds__(kGroups * kCols) void merge_flat_kernel(const float* __restrict__ part_out,
-                                                                    const float* __restrict__ part_lse,
-                                                                    const int64_t* __restrict__ cu, int heads,
-                                                                    int num_workgroups, float* __restrict__ out,
-                                                                    float* __restrict__ lse) {
+// cost-axis ranges meet [cu[b], cu[b + 1]) (the axis the decode stored); row h of slot q is row
+// q * heads + h.  A request has few partials here (one or two, a handful for the longest), so
+// one wavefront (one workgroup) merges one output row: lane l owns columns 8l .. 8l + 7 of every
+// partial and the partials' LSEs are read by every lane (no LDS, no barrier).  Partials are
+// taken four at a time, their loads issued together.
+constexpr int kFlatBatch = 4;
+__global__ __launch_bounds__(64) void merge_flat_kernel(const float* __restrict__ part_out,
+                                                         const float* __restrict__ part_lse,
+                                                         const int64_t* __restrict__ cu, int batch, int heads,
+                                                         int num_workgroups, float* __restrict__ out,
+                                                         float* __restrict__ lse) {
+  const int lane = threadIdx.x;
   const int64_t bh = blockIdx.x;
   const int b = (int)(bh / heads), h = (int)(bh % heads);
-  const int64_t N = cu[gridDim.x / heads], c0 = cu[b], c1 = cu[b + 1];
+  const int64_t N = cu[batch], c0 = cu[b], c1 = cu[b + 1];
   const int64_t W = min((int64_t)num_workgroups, N);  // the workgroups that took part
   int count = 0;
   int64_t first = 0;
@@ -133,7 +138,51 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_flat_kernel(const float
     first = ((int64_t)b + w0) * heads + h;
     count = (int)(w1 - w0 + 1);
   }
-  merge_row(part_out, part_lse, count, first, heads, kLatent, bh, out, lse);
+  // M = max_p lse_p; fmaxf skips NaN, so a NaN partial forces M = NaN.
+  float M = -INFINITY;
+  bool nan = false;
+  for (int p0 = 0; p0 < count; p0 += kFlatBatch) {
+    float x[kFlatBatch];
+#pragma unroll
+    for (int i = 0; i < kFlatBatch; ++i) x[i] = p0 + i < count ? part_lse[first + (int64_t)(p0 + i) * heads] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kFlatBatch; ++i) {
+      M = fmaxf(M, x[i]);
+      nan = nan || x[i] != x[i];
+    }
+  }
+  if (nan) M = __builtin_nanf("");
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int p0 = 0; p0 < count; p0 += kFlatBatch) {
+      float w[kFlatBatch];
+      f32x4 v0[kFlatBatch], v1[kFlatBatch];
+#pragma unroll
+      for (int i = 0; i < kFlatBatch; ++i) {
+        const bool in = p0 + i < count;
+        const int64_t row = first + (int64_t)(in ? p0 + i : p0) * heads;  // a valid row either way
+        const f32x4* src = (const f32x4*)(part_out + row * kLatent + 8 * lane);
+        w[i] = in ? part_lse[row] : -INFINITY;
+        v0[i] = src[0];
+        v1[i] = src[1];
+      }
+#pragma unroll
+      for (int i = 0; i < kFlatBatch; ++i) {
+        if (p0 + i >= count) continue;
+        const float e = __expf(w[i] - M);
+        wsum += e;
+        a0 += e * v0[i];
+        a1 += e * v1[i];
+      }
+    }
+    a0 *= 1.0f / wsum;
+    a1 *= 1.0f / wsum;
+  }
+  f32x4* dst = (f32x4*)(out + bh * kLatent + 8 * lane);
+  dst[0] = a0;
+  dst[1] = a1;
+  if (lane == 0) lse[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
 }
 
 }  // namespace
@@ -141,8 +190,8 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_flat_kernel(const float
 hipError_t launch_merge_flat(const float* part_out, const float* part_lse, const int64_t* cu, int batch, int heads,
                              int num_workgroups, float* out, float* lse, hipStream_t stream) {
   const int64_t rows = (int64_t)batch * heads;
-  hipLaunchKernelGGL(merge_flat_kernel, dim3((unsigned)rows, (unsigned)(kLatent / (4 * kCols))),
-                     dim3(kGroups * kCols), 0, stream, part_out, part_lse, cu, heads, num_workgroups, out, lse);
+  hipLaunchKernelGGL(merge_flat_kernel, dim3((unsigned)rows), dim3(64), 0, stream, part_out, part_lse, cu, batch, heads,
+                     num_workgroups, out, lse);
   return hipGetLastError();
 }
 
