@@ -110,19 +110,94 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_counted_kernel(const fl
   merge_row(part_out, part_lse, n, bh, rows, width, bh, out, lse);
 }
 
+// Merge of one output row by one 64-lane wavefront, for rows with few partials: lane l owns
+// float4 columns l, l + 64, ... (NV of them: width = 256 NV) of every partial; every lane reads
+// the partials' LSEs; partials are taken four at a time with their loads issued together.  No
+// LDS, no barrier.  Partial i of the row: row first + i * stride of part_out / part_lse.
+constexpr int kRowBatch = 4;
+template <int NV>
+__device__ __forceinline__ void merge_row_wave(const float* __restrict__ part_out, const float* __restrict__ part_lse,
+                                               int count, int64_t first, int64_t stride, int64_t bh,
+                                               float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int kWidth = 256 * NV;
+  const int lane = threadIdx.x & 63;
+  // M = max_p lse_p; fmaxf skips NaN, so a NaN partial forces M = NaN.
+  float M = -INFINITY;
+  bool nan = false;
+  for (int p0 = 0; p0 < count; p0 += kRowBatch) {
+    float x[kRowBatch];
+#pragma unroll
+    for (int i = 0; i < kRowBatch; ++i) x[i] = p0 + i < count ? part_lse[first + (int64_t)(p0 + i) * stride] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kRowBatch; ++i) {
+      M = fmaxf(M, x[i]);
+      nan = nan || x[i] != x[i];
+    }
+  }
+  if (nan) M = __builtin_nanf("");
+  f32x4 acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int p0 = 0; p0 < count; p0 += kRowBatch) {
+      float w[kRowBatch];
+      f32x4 val[kRowBatch][NV];
+#pragma unroll
+      for (int i = 0; i < kRowBatch; ++i) {
+        const bool in = p0 + i < count;
+        const int64_t row = first + (int64_t)(in ? p0 + i : p0) * stride;  // a valid row either way
+        const f32x4* src = (const f32x4*)(part_out + row * kWidth) + lane;
+        w[i] = in ? part_lse[row] : -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) val[i][v] = src[64 * v];
+      }
+#pragma unroll
+      for (int i = 0; i < kRowBatch; ++i) {
+        if (p0 + i >= count) continue;
+        const float e = __expf(w[i] - M);
+        wsum += e;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] += e * val[i][v];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[v] *= 1.0f / wsum;
+  }
+  f32x4* dst = (f32x4*)(out + bh * kWidth) + lane;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) dst[64 * v] = acc[v];
+  if (lane == 0) lse[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
+}
+
+// Per-request merges with at most kFewSplits partials per row: one row per 64-lane workgroup
+// (merge_row_wave); counted (empty partitions wrote nothing) or all S partials.
+constexpr int kFewSplits = 16;
+template <int NV, bool kCounted>
+__global__ __launch_bounds__(64) void merge_few_kernel(const float* __restrict__ part_out,
+                                                       const float* __restrict__ part_lse, int S, int64_t rows,
+                                                       int rows_per_request, const int32_t* __restrict__ seq_lens,
+                                                       int page_size, int64_t bt_stride, float* __restrict__ out,
+                                                       float* __restrict__ lse) {
+  const int64_t bh = blockIdx.x;
+  int n = S;
+  if constexpr (kCounted) {
+    const int64_t L = seq_lens[bh / rows_per_request];
+    const int64_t c = max((bt_stride + S - 1) / S, (int64_t)1);
+    n = (int)(((L + page_size - 1) / page_size + c - 1) / c);
+  }
+  merge_row_wave<NV>(part_out, part_lse, n, bh, rows, bh, out, lse);
+}
+
 // Batch-balanced mode: request b's partials are the slots b + w for the workgroups w whose
 // cost-axis ranges meet [cu[b], cu[b + 1]) (the axis the decode stored); row h of slot q is row
-// q * heads + h.  A request has few partials here (one or two, a handful for the longest), so
-// one wavefront (one workgroup) merges one output row: lane l owns columns 8l .. 8l + 7 of every
-// partial and the partials' LSEs are read by every lane (no LDS, no barrier).  Partials are
-// taken four at a time, their loads issued together.
-constexpr int kFlatBatch = 4;
+// q * heads + h.  A request has one or two partials here (a handful for the longest): one row
+// per 64-lane workgroup (merge_row_wave).
 __global__ __launch_bounds__(64) void merge_flat_kernel(const float* __restrict__ part_out,
-                                                         const float* __restrict__ part_lse,
-                                                         const int64_t* __restrict__ cu, int batch, int heads,
-                                                         int num_workgroups, float* __restrict__ out,
-                                                         float* __restrict__ lse) {
-  const int lane = threadIdx.x;
+                                                        const float* __restrict__ part_lse,
+                                                        const int64_t* __restrict__ cu, int batch, int heads,
+                                                        int num_workgroups, float* __restrict__ out,
+                                                        float* __restrict__ lse) {
   const int64_t bh = blockIdx.x;
   const int b = (int)(bh / heads), h = (int)(bh % heads);
   const int64_t N = cu[batch], c0 = cu[b], c1 = cu[b + 1];
@@ -138,51 +213,33 @@ __global__ __launch_bounds__(64) void merge_flat_kernel(const float* __restrict_
     first = ((int64_t)b + w0) * heads + h;
     count = (int)(w1 - w0 + 1);
   }
-  // M = max_p lse_p; fmaxf skips NaN, so a NaN partial forces M = NaN.
-  float M = -INFINITY;
-  bool nan = false;
-  for (int p0 = 0; p0 < count; p0 += kFlatBatch) {
-    float x[kFlatBatch];
-#pragma unroll
-    for (int i = 0; i < kFlatBatch; ++i) x[i] = p0 + i < count ? part_lse[first + (int64_t)(p0 + i) * heads] : -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kFlatBatch; ++i) {
-      M = fmaxf(M, x[i]);
-      nan = nan || x[i] != x[i];
-    }
+  merge_row_wave<kLatent / 256>(part_out, part_lse, count, first, heads, bh, out, lse);
+}
+
+template <bool kCounted>
+hipError_t launch_few(const float* part_out, const float* part_lse, int S, int64_t rows, int rows_per_request,
+                      int width, const int32_t* seq_lens, int page_size, int64_t bt_stride, float* out, float* lse,
+                      hipStream_t stream) {
+  const dim3 grid((unsigned)rows), block(64);
+  switch (width) {
+    case 256:
+      hipLaunchKernelGGL((merge_few_kernel<1, kCounted>), grid, block, 0, stream, part_out, part_lse, S, rows,
+                         rows_per_request, seq_lens, page_size, bt_stride, out, lse);
+      break;
+    case 768:
+      hipLaunchKernelGGL((merge_few_kernel<3, kCounted>), grid, block, 0, stream, part_out, part_lse, S, rows,
+                         rows_per_request, seq_lens, page_size, bt_stride, out, lse);
+      break;
+    case 1792:
+      hipLaunchKernelGGL((merge_few_kernel<7, kCounted>), grid, block, 0, stream, part_out, part_lse, S, rows,
+                         rows_per_request, seq_lens, page_size, bt_stride, out, lse);
+      break;
+    default:
+      hipLaunchKernelGGL((merge_few_kernel<2, kCounted>), grid, block, 0, stream, part_out, part_lse, S, rows,
+                         rows_per_request, seq_lens, page_size, bt_stride, out, lse);
+      break;
   }
-  if (nan) M = __builtin_nanf("");
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int p0 = 0; p0 < count; p0 += kFlatBatch) {
-      float w[kFlatBatch];
-      f32x4 v0[kFlatBatch], v1[kFlatBatch];
-#pragma unroll
-      for (int i = 0; i < kFlatBatch; ++i) {
-        const bool in = p0 + i < count;
-        const int64_t row = first + (int64_t)(in ? p0 + i : p0) * heads;  // a valid row either way
-        const f32x4* src = (const f32x4*)(part_out + row * kLatent + 8 * lane);
-        w[i] = in ? part_lse[row] : -INFINITY;
-        v0[i] = src[0];
-        v1[i] = src[1];
-      }
-#pragma unroll
-      for (int i = 0; i < kFlatBatch; ++i) {
-        if (p0 + i >= count) continue;
-        const float e = __expf(w[i] - M);
-        wsum += e;
-        a0 += e * v0[i];
-        a1 += e * v1[i];
-      }
-    }
-    a0 *= 1.0f / wsum;
-    a1 *= 1.0f / wsum;
-  }
-  f32x4* dst = (f32x4*)(out + bh * kLatent + 8 * lane);
-  dst[0] = a0;
-  dst[1] = a1;
-  if (lane == 0) lse[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -199,6 +256,9 @@ hipError_t launch_merge_counted(const float* part_out, const float* part_lse, in
                                 int rows_per_request, int width, const int32_t* seq_lens, int page_size,
                                 int64_t bt_stride, float* out, float* lse, hipStream_t stream) {
   const int64_t rows = (int64_t)batch * rows_per_request;
+  if (num_splits <= kFewSplits)
+    return launch_few<true>(part_out, part_lse, num_splits, rows, rows_per_request, width, seq_lens, page_size,
+                            bt_stride, out, lse, stream);
   hipLaunchKernelGGL(merge_counted_kernel, dim3((unsigned)rows, (unsigned)(width / (4 * kCols))),
                      dim3(kGroups * kCols), 0, stream, part_out, part_lse, num_splits, rows, rows_per_request, width,
                      seq_lens, page_size, bt_stride, out, lse);
@@ -208,6 +268,8 @@ hipError_t launch_merge_counted(const float* part_out, const float* part_lse, in
 hipError_t launch_merge(const float* part_out, const float* part_lse, int num_splits, int batch,
                         int heads, float* out, float* lse, hipStream_t stream, int width) {
   const int64_t rows = (int64_t)batch * heads;
+  if (num_splits <= kFewSplits)
+    return launch_few<false>(part_out, part_lse, num_splits, rows, 1, width, nullptr, 1, 1, out, lse, stream);
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows, (unsigned)(width / (4 * kCols))), dim3(kGroups * kCols), 0,
                      stream, part_out, part_lse, num_splits, rows, width, out, lse);
   return hipGetLastError();
