@@ -66,6 +66,7 @@ struct Bf16Rows {
   static constexpr int kAcc = kLat / 16;                // 16x16 output tiles per row group
 
   struct Aux {};
+  static constexpr bool kFlatTile = false;
 
   // Tiles in the line layout (line_pos): lane L fetches tokens L >> 3 and 8 + (L >> 3) of a
   // tile, whole 128-byte lines, with the non-temporal hint unless cached loads were asked for.
@@ -144,10 +145,18 @@ struct Bf16Rows {
 
 // ------------------------------------------------------------------------------------
 // fp8 656-byte rows: 41 chunks per token (32 code chunks, 1 scale chunk, 8 rope chunks).
-// Eleven DMA instructions; in the last only chunk 40 exists, and the lanes whose chunk
-// would lie past it re-read chunk 40 into padding, so every access stays in the row.
-// Without rope (kRopeDim = 0) the first 528 bytes are loaded: eight full instructions
-// and a ninth for the scale chunk 32 alone.
+// With rope the tile is row-major, the layout the 16 rows have in their page (token t's byte
+// b at 656 t + b, 10,496 bytes): DMA instruction j fetches tile bytes [1024 j, 1024 j + 1024),
+// lane L the chunk 64 j + L; the eleventh holds the last 16 chunks, which lanes L and L + 16,
+// L + 32, L + 48 fetch alike (the spares land in padding).  When the 16 tokens are consecutive
+// slots of one page, an instruction reads eight whole 128-byte lines of one contiguous run,
+// the form the non-temporal hint needs; otherwise (a tile that crosses a page or holds the
+// partition's clamped tail) each lane finds the token of every chunk it fetches.  Reads stay
+// bank-conflict free: token bases 656 t fall on 16 distinct 16-byte bank groups (656 = 144 mod
+// 256, 144 t / 16 a permutation of 0 .. 15).  Without rope (kRopeDim = 0) only the first 528
+// bytes of each row are loaded, which are not contiguous across rows, so those tiles keep the
+// chunk layout: eight full instructions and a ninth for the scale chunk 32 alone, the lanes
+// past it re-reading chunk 32 into padding.
 // ------------------------------------------------------------------------------------
 template <int kRopeDim>
 struct Fp8Rows {
@@ -167,18 +176,55 @@ struct Fp8Rows {
     f32x4 sc[4];  // sc[r][k]: scale of block k of token 4g + r
   };
 
-  // Tiles in the chunk layout (chunk_pos): lane L fetches token L >> 2 of a tile, 64 bytes of
-  // its row per instruction (656-byte rows do not start on 128-byte lines).
-  static constexpr int kTokensPerLane = 1;
-  __device__ static __forceinline__ int fetch_token(int lane, int) { return lane >> 2; }
+  static constexpr bool kFlatTile = kRopeDim != 0;  // row-major tiles (else the chunk layout)
+  static constexpr int kChunks = kRowBytes / 16;    // 41 chunks of 16 bytes per row
+  static_assert(!kFlatTile || 16 * kChunks == 64 * (kDmaOps - 1) + 16, "the last instruction: 16 chunks");
 
-  __device__ static __forceinline__ void issue(const uint8_t* const (&rows)[1], uint32_t dst, int lane, bool) {
-    const uint8_t* row = rows[0];
-    const uint8_t* src = row + 16 * ((lane & 3) ^ swz(lane >> 2));
+  // Byte offset of chunk c of token t in a tile.
+  __device__ static __forceinline__ int pos(int t, int c) {
+    return kFlatTile ? t * kRowBytes + 16 * c : 16 * chunk_pos(t, c);
+  }
+
+  // Row-major tiles: the tile chunk lane L fetches in instruction j, and its token.
+  __device__ static __forceinline__ int tile_chunk(int lane, int j) {
+    return 64 * j + (j == kDmaOps - 1 ? (lane & 15) : lane);
+  }
+  // Chunk layout: lane L fetches token L >> 2, 64 bytes of its row per instruction.
+  static constexpr int kTokensPerLane = kFlatTile ? kDmaOps : 1;
+  __device__ static __forceinline__ int fetch_token(int lane, int j) {
+    return kFlatTile ? tile_chunk(lane, j) / kChunks : lane >> 2;
+  }
+
+  // rows[j]: the row of token fetch_token(lane, j).  Row-major tiles take the non-temporal
+  // hint when `nt`; chunk-layout tiles read half lines and always use plain loads.
+  __device__ static __forceinline__ void issue(const uint8_t* const (&rows)[kTokensPerLane], uint32_t dst, int lane,
+                                               bool nt) {
+    if constexpr (kFlatTile) {
 #pragma unroll
-    for (int j = 0; j < kFullOps; ++j) dma16(src + 64 * j, dst + 1024 * j);
-    // chunk kLastChunk for one lane per token; padding for the rest
-    dma16(row + 16 * kLastChunk, dst + 1024 * kFullOps);
+      for (int j = 0; j < kDmaOps; ++j) {
+        const uint8_t* src = rows[j] + 16 * (tile_chunk(lane, j) % kChunks);
+        if (nt) dma16_nt(src, dst + 1024 * j); else dma16(src, dst + 1024 * j);
+      }
+    } else {
+      const uint8_t* row = rows[0];
+      const uint8_t* src = row + 16 * ((lane & 3) ^ swz(lane >> 2));
+#pragma unroll
+      for (int j = 0; j < kFullOps; ++j) dma16(src + 64 * j, dst + 1024 * j);
+      // chunk kLastChunk for one lane per token; padding for the rest
+      dma16(row + 16 * kLastChunk, dst + 1024 * kFullOps);
+    }
+  }
+
+  // Row-major tile whose 16 rows are consecutive slots from `tile` on.
+  __device__ static __forceinline__ void issue_contiguous(const uint8_t* tile, uint32_t dst, int lane, bool nt) {
+    static_assert(kFlatTile, "contiguous tiles are row-major");
+    if (nt) {
+#pragma unroll
+      for (int j = 0; j < kDmaOps; ++j) dma16_nt(tile + 16 * tile_chunk(lane, j), dst + 1024 * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kDmaOps; ++j) dma16(tile + 16 * tile_chunk(lane, j), dst + 1024 * j);
+    }
   }
 
   __device__ static __forceinline__ u32x4 widen8(u32x2 codes) {
@@ -192,7 +238,7 @@ struct Fp8Rows {
 
   __device__ static __forceinline__ f32x4 qk(const uint8_t* buf, int m, int g, const u32x4* qf, Aux& aux) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) aux.sc[r] = *(const f32x4*)(buf + 16 * chunk_pos(4 * g + r, 32));
+    for (int r = 0; r < 4; ++r) aux.sc[r] = *(const f32x4*)(buf + pos(4 * g + r, 32));
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -201,7 +247,7 @@ struct Fp8Rows {
       for (int jj = 0; jj < 4; ++jj) {
         const int j = 4 * k + jj;  // codes 32j + 8g .. +8: chunk 2j + (g >> 1), half g & 1
         const int c = 2 * j + (g >> 1);
-        const u32x2 codes = *(const u32x2*)(buf + 16 * chunk_pos(m, c) + 8 * (g & 1));
+        const u32x2 codes = *(const u32x2*)(buf + pos(m, c) + 8 * (g & 1));
         sk = mfma_16x16x32(widen8(codes), qf[j], sk);
       }
 #pragma unroll
@@ -213,7 +259,7 @@ struct Fp8Rows {
       f32x4 sr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jr = 0; jr < 2; ++jr)
-        sr = mfma_16x16x32(*(const u32x4*)(buf + 16 * chunk_pos(m, 33 + 4 * jr + g)), qf[16 + jr], sr);
+        sr = mfma_16x16x32(*(const u32x4*)(buf + pos(m, 33 + 4 * jr + g)), qf[16 + jr], sr);
       return s + sr;
     }
   }
@@ -233,7 +279,7 @@ struct Fp8Rows {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       // codes 64i + 4m .. +4 of token 4g + r: chunk 4i + (m >> 2), quarter m & 3
-      const uint32_t w = *(const uint32_t*)(buf + 16 * chunk_pos(4 * g + r, 4 * i + (m >> 2)) + 4 * (m & 3));
+      const uint32_t w = *(const uint32_t*)(buf + pos(4 * g + r, 4 * i + (m >> 2)) + 4 * (m & 3));
       lo[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
       hi[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
     }
@@ -301,13 +347,13 @@ struct Fp8Conv {
   static constexpr int kAcc = 32;
   using Aux = Fp8Rows<64>::Aux;
 
-  // Wave-wide: the raw fp8 tile (Fp8Rows<64> layout) at `raw` into the bf16 tile at `conv`.
+  // Wave-wide: the raw fp8 tile (Fp8Rows<64>, row-major) at `raw` into the bf16 tile at `conv`.
   __device__ static __forceinline__ void convert(const uint8_t* raw, uint8_t* conv, int lane) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {  // 16 tokens x 32 code chunks, 8 per lane
       const int q = lane + 64 * j;
       const int tk = q >> 5, c = q & 31;  // token, chunk of 16 codes (latent values 16c ..)
-      const u32x4 codes = *(const u32x4*)(raw + 16 * chunk_pos(tk, c));
+      const u32x4 codes = *(const u32x4*)(raw + Fp8Rows<64>::pos(tk, c));
       uint32_t v[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -321,9 +367,9 @@ struct Fp8Conv {
     for (int j = 0; j < 2; ++j) {  // 16 tokens x 8 rope chunks
       const int q = lane + 64 * j;
       const int tk = q >> 3, r = q & 7;
-      *(u32x4*)(conv + 16 * chunk_pos(tk, 64 + r)) = *(const u32x4*)(raw + 16 * chunk_pos(tk, 33 + r));
+      *(u32x4*)(conv + 16 * chunk_pos(tk, 64 + r)) = *(const u32x4*)(raw + Fp8Rows<64>::pos(tk, 33 + r));
     }
-    if (lane < 16) *(u32x4*)(conv + kTileBytes + 16 * lane) = *(const u32x4*)(raw + 16 * chunk_pos(lane, 32));
+    if (lane < 16) *(u32x4*)(conv + kTileBytes + 16 * lane) = *(const u32x4*)(raw + Fp8Rows<64>::pos(lane, 32));
   }
 
   __device__ static __forceinline__ f32x4 qk(const uint8_t* buf, int m, int g, const u32x4* qf, Aux& aux) {
@@ -386,7 +432,8 @@ constexpr int kRedBytes = kWaves * kMaxHeads * kRedStride * 4 + 2 * kWaves * kMa
 // Per wave: kBufs tile buffers, then (after all waves' buffers) kBufs 256-byte page-id slots.
 template <class Fmt>
 constexpr int pipe_bytes() {
-  return kWaves * Fmt::kBufs * (Fmt::kTileBytes + 256);
+  // row-major tiles add NB - 1 page-id slots per wave for the first tiles (the last bytes)
+  return kWaves * Fmt::kBufs * (Fmt::kTileBytes + 256) + (Fmt::kFlatTile ? kWaves * (Fmt::kBufs - 1) * 256 : 0);
 }
 template <class Fmt>
 constexpr int smem_bytes() {
@@ -572,6 +619,33 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 #pragma unroll
     for (int i = 0; i < TPL; ++i) page[i] = *(const int32_t*)(slot + 16 * Fmt::fetch_token(lane, i));
   };
+  // Row-major tiles (Fmt::kFlatTile) take their page ids from a page-id slot in LDS (token T's
+  // page at byte 16T): a tile of 16 consecutive slots of one page is fetched as one run (a single
+  // page id, read by every lane alike); any other tile row by row, each lane looking up the page
+  // of every token it fetches from.  Tokens past the partition are clamped to its last one.
+  auto issue_tile_flat = [&](int k, const uint8_t* pids, uint32_t dst) {
+    if constexpr (Fmt::kFlatTile) {
+      // the tile's first token; a tile past the partition (G > 1) is its last token, 16 times
+      const uint32_t a = min(t0 + (uint32_t)k * kTile, tlast);
+      const uint32_t q0 = a % ps;  // its slot in its page
+      const bool nt = p.stream_rows != 0;
+      if (a + (kTile - 1) <= tlast && q0 + kTile <= ps) {
+        const int32_t pg = __builtin_amdgcn_readfirstlane(*(const int32_t*)pids);
+        Fmt::issue_contiguous(p.cache + ((int64_t)pg * ps + q0) * Fmt::kRowBytes, dst, lane, nt);
+      } else {
+        const uint8_t* rows[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+          const uint32_t T = (uint32_t)Fmt::fetch_token(lane, i);
+          uint32_t off = q0 + min(T, tlast - a);  // slot of the clamped token, before wrapping
+          off = ps >= (uint32_t)kTile ? (off >= ps ? off - ps : off) : off % ps;
+          const int32_t pg = *(const int32_t*)(pids + 16 * T);
+          rows[i] = p.cache + ((int64_t)pg * ps + off) * Fmt::kRowBytes;
+        }
+        Fmt::issue(rows, dst, lane, nt);
+      }
+    }
+  };
 
   // One tile of work: QK^T, online softmax, PV on tile k (partition-relative) in `buf`.
   // Tokens at or past this lane's visibility limit, or past the partition, get p = 0.
@@ -662,33 +736,56 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 
   constexpr int D = Fmt::kDmaOps;
   int k = wave;
-  // The first NB-1 tiles' page ids are ordinary loads issued with the q loads; all are
-  // consumed here, so the compiler's waits for them land before the pipeline (inside it
-  // a compiler-generated vmcnt wait would also wait for the hand-counted DMAs).  The q
-  // fragments move to the matrix-core registers (AGPRs, beside O), which MFMA reads as
-  // directly as VGPRs: that leaves about 70 more VGPRs to the compiler's schedule.
-  int32_t page_first[NB - 1][TPL];
-#pragma unroll
-  for (int t = 0; t < NB - 1; ++t)
-#pragma unroll
-    for (int i = 0; i < TPL; ++i)
-      page_first[t][i] = (G == 1 ? k + kWaves * t < ntiles : ntiles > 0)
-                             ? bt[clamp_token(k + kWaves * t, Fmt::fetch_token(lane, i)) / ps]
-                             : 0;
-#pragma unroll
-  for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
-#pragma unroll
-  for (int t = 0; t < NB - 1; ++t)
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) asm volatile("" ::"v"(page_first[t][i]));
   // G > 1: every wave loads a tile even where its tile lies past the partition (the
   // partition's last rows again, clamped by lane_token), so that every buffer of a step holds
   // finite rows and the step's tiles can be scored without a branch per tile.
-  if (G == 1 ? k < ntiles : ntiles > 0) {
+  const bool first_tiles = G == 1 ? k < ntiles : ntiles > 0;
+  if constexpr (Fmt::kFlatTile) {
+    // The first NB-1 tiles' page ids go to LDS by DMA as well (slots after the pipeline's),
+    // awaited before any row is requested, so the queue order below is the loop's.
+    uint8_t* xslot = smem + smem_bytes<Fmt>() - kWaves * (NB - 1) * 256 + wave * (NB - 1) * 256;
+    const uint32_t xlds = __builtin_amdgcn_readfirstlane(lds_offset(xslot));
+    if (first_tiles) {
 #pragma unroll
-    for (int t = 0; t < NB - 1; ++t) {
-      fetch_page(min(k + kWaves * (t + NB - 1), ntiles - 1), plds + 256 * t);
-      if (G > 1 || k + kWaves * t < ntiles) issue_tile(k + kWaves * t, page_first[t], wlds + t * Fmt::kTileBytes);
+      for (int t = 0; t < NB - 1; ++t) fetch_page(min(k + kWaves * t, ntiles - 1), xlds + 256 * t);
+    }
+#pragma unroll
+    for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
+    wait_vmcnt<0>();
+    if (first_tiles) {
+#pragma unroll
+      for (int t = 0; t < NB - 1; ++t) {
+        fetch_page(min(k + kWaves * (t + NB - 1), ntiles - 1), plds + 256 * t);
+        if (G > 1 || k + kWaves * t < ntiles)
+          issue_tile_flat(k + kWaves * t, xslot + 256 * t, wlds + t * Fmt::kTileBytes);
+      }
+    }
+  } else {
+    // The first NB-1 tiles' page ids are ordinary loads issued with the q loads; all are
+    // consumed here, so the compiler's waits for them land before the pipeline (inside it
+    // a compiler-generated vmcnt wait would also wait for the hand-counted DMAs).  The q
+    // fragments move to the matrix-core registers (AGPRs, beside O), which MFMA reads as
+    // directly as VGPRs: that leaves about 70 more VGPRs to the compiler's schedule.
+    int32_t page_first[NB - 1][TPL];
+#pragma unroll
+    for (int t = 0; t < NB - 1; ++t)
+#pragma unroll
+      for (int i = 0; i < TPL; ++i)
+        page_first[t][i] = (G == 1 ? k + kWaves * t < ntiles : ntiles > 0)
+                               ? bt[clamp_token(k + kWaves * t, Fmt::fetch_token(lane, i)) / ps]
+                               : 0;
+#pragma unroll
+    for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
+#pragma unroll
+    for (int t = 0; t < NB - 1; ++t)
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) asm volatile("" ::"v"(page_first[t][i]));
+    if (first_tiles) {
+#pragma unroll
+      for (int t = 0; t < NB - 1; ++t) {
+        fetch_page(min(k + kWaves * (t + NB - 1), ntiles - 1), plds + 256 * t);
+        if (G > 1 || k + kWaves * t < ntiles) issue_tile(k + kWaves * t, page_first[t], wlds + t * Fmt::kTileBytes);
+      }
     }
   }
 
@@ -708,10 +805,15 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       for (; k + kWaves * (NB - 1) < ntiles; k += kWaves) {
         const int ahead = cur == 0 ? NB - 1 : cur - 1;  // (cur + NB - 1) mod NB
         wait_vmcnt<(NB - 1) * D + (NB - 2)>();  // page ids of tile k + 4(NB-1) have landed
-        Pages page_n;
-        read_pages(pslot + 256 * cur, page_n);
-        fetch_page(min(k + kWaves * 2 * (NB - 1), ntiles - 1), plds + 256 * ahead);
-        issue_tile(k + kWaves * (NB - 1), page_n, wlds + ahead * Fmt::kTileBytes);
+        if constexpr (Fmt::kFlatTile) {
+          fetch_page(min(k + kWaves * 2 * (NB - 1), ntiles - 1), plds + 256 * ahead);
+          issue_tile_flat(k + kWaves * (NB - 1), pslot + 256 * cur, wlds + ahead * Fmt::kTileBytes);
+        } else {
+          Pages page_n;
+          read_pages(pslot + 256 * cur, page_n);
+          fetch_page(min(k + kWaves * 2 * (NB - 1), ntiles - 1), plds + 256 * ahead);
+          issue_tile(k + kWaves * (NB - 1), page_n, wlds + ahead * Fmt::kTileBytes);
+        }
         wait_vmcnt<(NB - 1) * (D + 1)>();  // tile k has landed
         compute(wbuf + cur * Fmt::kTileBytes, k);
         cur = cur + 1 == NB ? 0 : cur + 1;
@@ -746,10 +848,16 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       if (i + 1 < nsteps) {
         // this wave's tile of step i + 1, clamped to the partition's last tile
         const int kn = min(kWaves * (i + 1) + wave, ntiles - 1);
-        Pages page_n;
-        read_pages(pslot + 256 * (i & 1), page_n);
-        fetch_page(min(kn + kWaves, ntiles - 1), plds + 256 * ((i + 1) & 1));
-        issue_tile(kn, page_n, wlds + (kConv ? 0 : ((i + 1) & 1) * Fmt::kTileBytes));
+        const uint32_t dst = wlds + (kConv ? 0 : ((i + 1) & 1) * Fmt::kTileBytes);
+        if constexpr (Fmt::kFlatTile) {
+          fetch_page(min(kn + kWaves, ntiles - 1), plds + 256 * ((i + 1) & 1));
+          issue_tile_flat(kn, pslot + 256 * (i & 1), dst);
+        } else {
+          Pages page_n;
+          read_pages(pslot + 256 * (i & 1), page_n);
+          fetch_page(min(kn + kWaves, ntiles - 1), plds + 256 * ((i + 1) & 1));
+          issue_tile(kn, page_n, dst);
+        }
       }
       if constexpr (kConv) __syncthreads();
       compute_step(i, u0);
@@ -910,8 +1018,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
     if (v1 <= lo || v1 == v0) continue;  // empty requests have no partial
     const int64_t s0 = v0 + kSegmentCost;  // axis position of token 0
     const int64_t L = v1 - s0;
-    const int64_t t0 = max(lo, s0) - s0;
-    const int64_t t1 = max(min(hi, v1) - s0, (int64_t)0);  // 0: the range holds start-up only
+    // Token boundaries fall on multiples of 16 (a tile), so that the tiles of a segment start
+    // where a page's tiles do; both workgroups that share a boundary round it alike.
+    auto on_tile = [&](int64_t t) -> int64_t { return t >= L ? L : t & ~(int64_t)(kTile - 1); };
+    const int64_t t0 = on_tile(max(lo, s0) - s0);
+    const int64_t t1 = on_tile(max(min(hi, v1) - s0, (int64_t)0));  // 0: the range holds start-up only
     const int64_t slot = (int64_t)b + w;
     decode_segment<Fmt, G, false>(p, smem, b, L, t0, max(t0, t1), p.part_out + slot * R * kLatent,
                                   p.part_lse + slot * R);
