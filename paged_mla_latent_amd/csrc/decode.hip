@@ -195,17 +195,23 @@ struct Fp8Rows {
     return kFlatTile ? tile_chunk(lane, j) / kChunks : lane >> 2;
   }
 
-  // rows[j]: the row of token fetch_token(lane, j).  Row-major tiles take the non-temporal
-  // hint when `nt`; chunk-layout tiles read half lines and always use plain loads.
-  __device__ static __forceinline__ void issue(const uint8_t* const (&rows)[kTokensPerLane], uint32_t dst, int lane,
-                                               bool nt) {
-    if constexpr (kFlatTile) {
+  // Row-major tile fetched row by row: row_of(j) is the row of token fetch_token(lane, j),
+  // found as each instruction is issued (a lane's rows are not all held at once).
+  template <class RowOf>
+  __device__ static __forceinline__ void issue_rows(RowOf&& row_of, uint32_t dst, int lane, bool nt) {
+    static_assert(kFlatTile, "row-major tiles");
 #pragma unroll
-      for (int j = 0; j < kDmaOps; ++j) {
-        const uint8_t* src = rows[j] + 16 * (tile_chunk(lane, j) % kChunks);
-        if (nt) dma16_nt(src, dst + 1024 * j); else dma16(src, dst + 1024 * j);
-      }
-    } else {
+    for (int j = 0; j < kDmaOps; ++j) {
+      const uint8_t* src = row_of(j) + 16 * (tile_chunk(lane, j) % kChunks);
+      if (nt) dma16_nt(src, dst + 1024 * j); else dma16(src, dst + 1024 * j);
+    }
+  }
+
+  // Chunk-layout tiles: rows[0] is the row of token fetch_token(lane, 0); they read half lines
+  // and always use plain loads.
+  __device__ static __forceinline__ void issue(const uint8_t* const (&rows)[kTokensPerLane], uint32_t dst, int lane,
+                                               bool) {
+    if constexpr (!kFlatTile) {
       const uint8_t* row = rows[0];
       const uint8_t* src = row + 16 * ((lane & 3) ^ swz(lane >> 2));
 #pragma unroll
@@ -626,23 +632,21 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   auto issue_tile_flat = [&](int k, const uint8_t* pids, uint32_t dst) {
     if constexpr (Fmt::kFlatTile) {
       // the tile's first token; a tile past the partition (G > 1) is its last token, 16 times
-      const uint32_t a = min(t0 + (uint32_t)k * kTile, tlast);
-      const uint32_t q0 = a % ps;  // its slot in its page
+      const uint32_t a = __builtin_amdgcn_readfirstlane(min(t0 + (uint32_t)k * kTile, tlast));
+      const uint32_t q0 = __builtin_amdgcn_readfirstlane(a % ps);  // its slot in its page (uniform)
       const bool nt = p.stream_rows != 0;
       if (a + (kTile - 1) <= tlast && q0 + kTile <= ps) {
         const int32_t pg = __builtin_amdgcn_readfirstlane(*(const int32_t*)pids);
         Fmt::issue_contiguous(p.cache + ((int64_t)pg * ps + q0) * Fmt::kRowBytes, dst, lane, nt);
       } else {
-        const uint8_t* rows[TPL];
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
+        auto row_of = [&](int i) -> const uint8_t* {
           const uint32_t T = (uint32_t)Fmt::fetch_token(lane, i);
           uint32_t off = q0 + min(T, tlast - a);  // slot of the clamped token, before wrapping
           off = ps >= (uint32_t)kTile ? (off >= ps ? off - ps : off) : off % ps;
           const int32_t pg = *(const int32_t*)(pids + 16 * T);
-          rows[i] = p.cache + ((int64_t)pg * ps + off) * Fmt::kRowBytes;
-        }
-        Fmt::issue(rows, dst, lane, nt);
+          return p.cache + ((int64_t)pg * ps + off) * Fmt::kRowBytes;
+        };
+        Fmt::issue_rows(row_of, dst, lane, nt);
       }
     }
   };

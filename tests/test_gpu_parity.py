@@ -61,7 +61,7 @@ RAGGED = [0, 1, 15, 16, 17, 100, 333, 1000, 2500]
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
-@pytest.mark.parametrize("ps", [1, 3, 16, 64, 784])
+@pytest.mark.parametrize("ps", [1, 3, 16, 24, 64, 784])
 def test_ragged_lengths_and_page_sizes(fmt, ps):
     pages = sum(-(-L // ps) for L in RAGGED) + 7
     w = workloads.make_workload(f"ragged_ps{ps}", seq_lens=RAGGED, heads=16, page_size=ps, num_pages=pages,
@@ -240,10 +240,11 @@ def _sample(w, n=4):
 
 # ------------------------------------------------------------------- batch-balanced mode
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
-@pytest.mark.parametrize("ps", [1, 3, 16, 64])
+@pytest.mark.parametrize("ps", [1, 3, 16, 24, 64])
 def test_balanced_ragged(fmt, ps):
-    """Workgroup ranges cut requests mid-page and mid-tile, cover several requests, or hold a
-    single token (W close to or above the token count)."""
+    """Workgroup ranges cut requests mid-page (at multiples of 16 tokens), cover several
+    requests, or hold no token at all (W close to or above the token count).  Page size 24
+    puts tiles across page boundaries (fp8 rows: fetched row by row)."""
     pages = sum(-(-L // ps) for L in RAGGED) + 7
     w = workloads.make_workload(f"bal_ps{ps}", seq_lens=RAGGED, heads=16, page_size=ps, num_pages=pages,
                                 fmt=fmt, seed=40 + ps)
