@@ -63,7 +63,7 @@ def _parse():
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="steps captured per HIP graph (the largest divisor of --steps up to this)")
     ap.add_argument("--row-loads", choices=("streaming", "cached"), default=None,
-                    help="row-load policy of the bf16-row decodes (mla_set_row_loads); default: the "
+                    help="row-load policy of the decodes (mla_set_row_loads); default: the "
                          "workload's entry in workloads.BENCH_ROW_LOADS")
     ap.add_argument("--eager", action="store_true",
                     help="time only eager launches (default: also replay the step from a captured HIP graph, "

@@ -375,16 +375,16 @@ MLA_API int mla_gather_context(const void* kv_cache, int32_t cache_format, int64
                                const int32_t* seq_starts, int32_t batch, int64_t total_rows,
                                void* out, void* stream);
 
-/* How the bf16-row decodes load cache rows (a performance hint; results are identical).
+/* How the decodes load cache rows (a performance hint; results are identical).
  * MLA_ROW_LOADS_STREAMING (the default): loads carry the non-temporal hint, for rows read
  * once per step; every load instruction reads whole 128-byte lines, and the hint lifts the
- * streaming rate (long context, random pages: 211 -> 189 us per decode on MI355X) but keeps
- * rows out of the caches.  MLA_ROW_LOADS_CACHED: plain loads, for batches whose requests share
- * pages within a step (prefix sharing), whose repeated rows then hit in the L2 / last-level
- * cache.  Applies to every later mla_decode*_bf16 call in the process (also the batch-balanced,
- * verify-step and rank-1792 ones; the rank-768 decode reads 64-byte row segments and always
- * uses plain loads, as do fp8 rows, which do not start on 128-byte lines).  Returns the
- * previous policy, or -MLA_ERR_SHAPE for an unknown one. */
+ * streaming rate (long context, random pages: bf16 rows 211 -> 189 us per decode, fp8 rows
+ * 147 -> 136 us on MI355X) but keeps rows out of the caches.  MLA_ROW_LOADS_CACHED: plain
+ * loads, for batches whose requests share pages within a step (prefix sharing), whose
+ * repeated rows then hit in the L2 / last-level cache.  Applies to every later mla_decode*
+ * call in the process (single-token, batch-balanced, verify-step and rank-1792 decodes, bf16
+ * and fp8 rows); the rank-768 decode and NoPE fp8 rows read 64-byte row segments and always
+ * use plain loads.  Returns the previous policy, or -MLA_ERR_SHAPE for an unknown one. */
 enum { MLA_ROW_LOADS_STREAMING = 0, MLA_ROW_LOADS_CACHED = 1 };
 MLA_API int mla_set_row_loads(int policy);
 

@@ -124,7 +124,7 @@ def library() -> ctypes.CDLL:
 
 
 def mla_set_row_loads(policy: int) -> int:
-    """Row-load policy of the bf16-row decodes (MLA_ROW_LOADS_STREAMING, the default, or
+    """Row-load policy of the decodes (MLA_ROW_LOADS_STREAMING, the default, or
     MLA_ROW_LOADS_CACHED for batches that share pages within a step); returns the previous one."""
     prev = library().mla_set_row_loads(int(policy))
     if prev < 0:

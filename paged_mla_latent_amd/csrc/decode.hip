@@ -22,8 +22,9 @@
 //  * Rows go HBM -> LDS with 16-byte direct-to-LDS loads (no VGPR round trip), two or three
 //    buffers per wave; the page ids travel by DMA as well, ahead of the rows that need
 //    them, and completion is counted by hand, so no compiler-inserted wait stalls the loop.
-//    bf16 rows are loaded whole 128-byte lines per instruction (the line layout), so the
-//    loads can carry the non-temporal hint; fp8 rows, not line-aligned, 64 bytes per row.
+//    Every instruction reads whole 128-byte lines, so the loads can carry the
+//    non-temporal hint: bf16 rows in the line layout, fp8 rows (not line-aligned) as
+//    row-major tiles, 16 consecutive rows of a page read as one run.
 //  * All 16 heads share every row, so QK^T is a real 16 x 16 x 576 contraction per
 //    tile (v_mfma_f32_16x16x32_bf16, rows as A, q^T as B) and PV a 512 x 16 x 16 one
 //    (v_mfma_f32_16x16x16_bf16, rows^T as A via ds_read_b64_tr_b16, P^T as B; two tiles

@@ -58,7 +58,7 @@ int device_cus() {
   return g_cus[dev].load(std::memory_order_relaxed);
 }
 
-// Row-load policy of the bf16-row decodes (mla_set_row_loads), process-wide.
+// Row-load policy of the decodes (mla_set_row_loads), process-wide.
 std::atomic<int> g_row_loads{MLA_ROW_LOADS_STREAMING};
 
 int hip_status(hipError_t e, const char* what) {

@@ -28,7 +28,7 @@ struct DecodeParams {
   int compact;                 // per-request mode: map workgroups onto the non-empty partitions first
   int skip_empty;              // per-request split mode: empty partitions write no partial (the
                                // merge counts each request's non-empty partitions itself)
-  int stream_rows;             // bf16 rows: non-temporal row loads (MLA_ROW_LOADS_STREAMING)
+  int stream_rows;             // non-temporal row loads (MLA_ROW_LOADS_STREAMING)
 };
 
 // Tokens [t0, t1) of one request.

@@ -364,7 +364,7 @@ BENCH_SCHEDULE = {
     "fp8_ragged": "balanced",
 }
 
-# Row-load policy of the bf16-row decodes per named workload: streaming (non-temporal) loads
+# Row-load policy of the decodes per named workload: streaming (non-temporal) loads
 # where every row is read once per step; cached loads for the high-slot batch, whose requests
 # share pages (12,058 pages above the wrap slot for about 47,500 page reads), so repeated rows
 # can hit in the L2 and last-level cache.
