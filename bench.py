@@ -61,13 +61,16 @@ def _parse():
                     help="also time each decode after a pass over MIB MiB of other memory (evicts the "
                          "last-level cache between repetitions); the roofline then uses these cold times")
     ap.add_argument("--graph-steps", type=int, default=10,
-                    help="steps captured per HIP graph (the largest divisor of --steps up to this)")
+                    help="with --graph: steps captured per HIP graph (the largest divisor of --steps up "
+                         "to this)")
     ap.add_argument("--row-loads", choices=("streaming", "cached"), default=None,
                     help="row-load policy of the decodes (mla_set_row_loads); default: the "
                          "workload's entry in workloads.BENCH_ROW_LOADS")
+    ap.add_argument("--graph", action="store_true",
+                    help="report the step replayed from a captured HIP graph instead of eager launches "
+                         "(measured slower here for every workload: 1-7 %% per step)")
     ap.add_argument("--eager", action="store_true",
-                    help="time only eager launches (default: also replay the step from a captured HIP graph, "
-                         "which gives the reported value)")
+                    help="eager launches (the default; kept for older command lines)")
     ap.add_argument("--op", choices=("decode", "gather", "cache_write", "merge"), default="decode",
                     help="gather: time mla_gather_context over the workload's whole context instead "
                          "(prefill-side context gather, fp8 rows upconverted to bf16)")
@@ -569,12 +572,20 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(ev[i])
+        step()
     torch.cuda.synchronize()
     wall = eager_wall = time.perf_counter() - t0
     launch_mode = "eager"
+    # Per-kernel HIP-event windows: the timed steps are enqueued behind untimed ones, with no
+    # synchronisation between, so the host runs ahead of the GPU and no launch latency falls
+    # inside a window (each window times its kernel as back-to-back execution runs it).
+    for _ in range(max(args.warmup, 8)):
+        step()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
 
-    if not args.eager:
+    if args.graph and not args.eager:
         # n consecutive steps captured into one graph (as a serving loop captures a whole
         # forward pass, one decode per layer) and replayed K / n times: every step's kernels
         # still run, in order, with one host submission per n steps.  Every warm-up replay
@@ -653,7 +664,8 @@ def main():
             "workload": w.name, "batch": w.batch, "heads": w.heads, "context_tokens": w.tokens,
             "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
             "schedule": f"batch-balanced, {balanced} workgroups" if balanced else "per-request partitions",
-            "row_loads": row_loads if w.fmt == "bf16" and geom != "rank768" else "plain",
+            # rank-768 rows and NoPE fp8 rows read 64-byte row segments with plain loads
+            "row_loads": "plain" if geom == "rank768" or (nope and w.fmt == "fp8") else row_loads,
             "layer": "nope-512" if nope else "rope-576", "query_tokens_per_request": T, "geometry": geom,
             "cache_row_bytes": 2 * (RANKS[geom] + 64) if geom in RANKS else w.row_bytes,
             "row_bytes_read": row_bytes_read,
