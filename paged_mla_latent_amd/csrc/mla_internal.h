@@ -53,7 +53,7 @@ __device__ __forceinline__ Range partition(int64_t L, int ps, int S, int s, int6
 // kSegmentCost positions to the cost axis, and workgroup w of W takes axis positions
 // [flat_begin(V, W, w), flat_begin(V, W, w + 1)), V = the axis length.
 constexpr int kMaxBalancedBatch = 1024;
-constexpr int64_t kSegmentCost = 384;
+constexpr int64_t kSegmentCost = 512;
 __device__ __forceinline__ int64_t flat_begin(int64_t N, int64_t W, int64_t w) {
   return (N / W) * w + ((N % W) * w) / W;  // floor(w N / W) without 64-bit overflow
 }

@@ -248,8 +248,8 @@ def test_balanced_ragged(fmt, ps):
     pages = sum(-(-L // ps) for L in RAGGED) + 7
     w = workloads.make_workload(f"bal_ps{ps}", seq_lens=RAGGED, heads=16, page_size=ps, num_pages=pages,
                                 fmt=fmt, seed=40 + ps)
-    # cost axis: 3,982 tokens + 8 non-empty requests x 384 = 7,054 positions
-    _run_case(w, [], balanced=[1, 2, 7, 64, 256, 1000, 7053, 7054, 9000])
+    # cost axis: 3,982 tokens + 8 non-empty requests x 512 = 8,078 positions
+    _run_case(w, [], balanced=[1, 2, 7, 64, 256, 1000, 8077, 8078, 9000])
 
 
 @pytest.mark.parametrize("heads", [1, 3, 16])
@@ -257,8 +257,8 @@ def test_balanced_heads_and_empties(heads):
     for fmt in ("bf16", "fp8"):
         w = workloads.make_workload("bal_empties", seq_lens=[0, 0, 1, 2, 0, 33, 0], heads=heads, page_size=16,
                                     num_pages=8, fmt=fmt, seed=3)
-        # cost axis: 36 tokens + 3 x 384 = 1,188 positions; most ranges hold start-up only
-        _run_case(w, [], balanced=[1, 3, 4, 36, 384, 1187, 1188, 2000])
+        # cost axis: 36 tokens + 3 x 512 = 1,572 positions; most ranges hold start-up only
+        _run_case(w, [], balanced=[1, 3, 4, 36, 512, 1571, 1572, 2000])
 
 
 def test_balanced_max_batch():
@@ -429,10 +429,10 @@ def test_mtp_parity(fmt, T, H):
     for S in (1, 4, 16, 30):  # 11 x 30 workgroups: compacted dispatch
         out, lse = _gpu_mtp(w, pd, q, S)
         _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp {fmt} T={T} H={H} S={S}")
-    # batch-balanced: a cost axis of 5,697-5,742 tokens + 9 or 10 non-empty requests x 384
-    # (9,153-9,582 positions), cut into ranges that meet many requests, split one mid-tile,
+    # batch-balanced: a cost axis of 5,697-5,742 tokens + 9 or 10 non-empty requests x 512
+    # (10,305-10,862 positions), cut into ranges that meet many requests, split one mid-page,
     # or hold start-up only
-    for W in (1, 5, 64, 256, 9153, 10000):
+    for W in (1, 5, 64, 256, 10305, 12000):
         out, lse = _gpu_mtp(w, pd, q, W, balanced=True)
         _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp balanced {fmt} T={T} H={H} W={W}")
 
