@@ -9,14 +9,16 @@ HBM before timing starts.
 Default workload: the long-context batch, 4 requests x 262,144 tokens, 16 heads,
 64-token pages drawn at random from a 32,768-page pool, 64 partitions per request.
 
-Two timed passes of --steps steps each: eager launches with HIP events around every
-kernel (per-kernel durations, the roofline figure), then the step captured as a HIP
-graph (10 steps per graph) and replayed (the reported value; every warm-up replay is
-checked bit for bit against the eager result).  Prints one JSON line.  Each workload
+Two timed passes of --steps steps each, eager launches on one stream: the first, between
+two synchronisations, gives the reported value; the second records HIP events around every
+kernel (per-kernel durations, the roofline figure), its timed steps enqueued behind untimed
+ones so that the host stays ahead of the GPU.  --graph reports instead the step captured
+as a HIP graph (10 steps per graph) and replayed (every warm-up replay checked bit for bit
+against the eager result).  Prints one JSON line.  Each workload
 is timed with the schedule that measured faster for it (per-request partitions or the
 batch-balanced ranges).
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload long_context] [--eager]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload long_context] [--eager]
 
 Other lines of the same path: --q-len (multi-token verify), --nope (NoPE-512 layer),
 --geometry (GLA-g2, rank 256 / 768 / 1792), --balanced / --splits (schedule),
@@ -40,8 +42,8 @@ METRIC = "latent-cache read GB/s (fraction of HBM peak) + decode tokens/s, H=16"
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long_context")
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
