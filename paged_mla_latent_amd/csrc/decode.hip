@@ -279,66 +279,58 @@ struct Fp8Rows {
                     pack_bf16(p[2] * aux.sc[2][k], p[3] * aux.sc[3][k])};
   }
 
-  // A operands of column group i: a[e] = (x[0][e], x[1][e], x[2][e], x[3][e]) with x[r][e] =
-  // row(4g + r)[64i + 4m + e], the codes widened to bf16 exactly.
-  __device__ static __forceinline__ void pv_operands(const uint8_t* buf, int m, int g, int i, u32x2 (&a)[4]) {
-    uint32_t lo[4], hi[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      // codes 64i + 4m .. +4 of token 4g + r: chunk 4i + (m >> 2), quarter m & 3
-      const uint32_t w = *(const uint32_t*)(buf + pos(4 * g + r, 4 * i + (m >> 2)) + 4 * (m & 3));
-      lo[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-      hi[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-    }
-    // lo[r] = (x[r][0], x[r][1]), hi[r] = (x[r][2], x[r][3])
-    a[0] = u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x05040100u), __builtin_amdgcn_perm(lo[3], lo[2], 0x05040100u)};
-    a[1] = u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u), __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u)};
-    a[2] = u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x05040100u), __builtin_amdgcn_perm(hi[3], hi[2], 0x05040100u)};
-    a[3] = u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u), __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u)};
+  // PV operands by transposing LDS reads (ds_read_b64_tr_b8): lane 16g + 2v + h addresses
+  // bytes 8h .. 8h + 7 of one chunk (16 codes: a 16-column block) of one row, and lane 16g + i
+  // then holds column i of the eight (row, chunk) pairs of its lane group, one byte each, in
+  // the order v = 0 .. 7.  Two 4-token halves of that, widened exactly (two codes per
+  // instruction), are the A operands of two 16 x 16 x 16 products, or one 16 x 16 x 32.
+  // Accumulator u holds, for head m, d = 16u + 4g + r in element r (the bf16 layout).
+  __device__ static __forceinline__ u32x4 widen_tr8(u32x2 w) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true))};
   }
 
+  // One tile: lane group g reads tokens 4g .. 4g + 3 of chunks 2c' and 2c' + 1 (v < 4 and
+  // v >= 4), so one read serves the products of two column blocks.
   __device__ static __forceinline__ void pv(const uint8_t* buf, int m, int g, const float (&p)[4],
                                             const Aux& aux, f32x4 (&O)[kAcc]) {
     u32x2 pb[4];
     scaled_p(p, aux, pb);
+    const int v = m >> 1, h = m & 1;
+    const uint8_t* src = buf + 8 * h;
+    const int t = 4 * g + (v & 3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x2 a[4];
-      pv_operands(buf, m, g, i, a);
-      const u32x2 b = pb[i >> 1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) O[4 * i + e] = mfma_16x16x16(a[e], b, O[4 * i + e]);
+    for (int c2 = 0; c2 < kAcc / 2; ++c2) {
+      const u32x4 a = widen_tr8(lds_read_tr8(src + pos(t, 2 * c2 + (v >> 2))));
+      const u32x2 b = pb[c2 >> 2];  // chunks 2c2, 2c2 + 1 lie in 128-value block c2 / 4
+      O[2 * c2] = mfma_16x16x16(u32x2{a[0], a[1]}, b, O[2 * c2]);
+      O[2 * c2 + 1] = mfma_16x16x16(u32x2{a[2], a[3]}, b, O[2 * c2 + 1]);
     }
   }
 
   // Two tiles with the 32-deep MFMA: K slots 8g .. 8g + 3 are tile a's tokens 4g .. 4g + 3,
-  // slots 8g + 4 .. 8g + 7 tile b's, in both operands.
+  // slots 8g + 4 .. 8g + 7 tile b's, in both operands (lanes v < 4 read tile a, v >= 4 tile b).
   __device__ static __forceinline__ void pv2(const uint8_t* bufa, const uint8_t* bufb, int m, int g,
                                              const float (&pa)[4], const float (&pb)[4], const Aux& auxa,
                                              const Aux& auxb, f32x4 (&O)[kAcc]) {
     u32x2 qa[4], qb[4];
     scaled_p(pa, auxa, qa);
     scaled_p(pb, auxb, qb);
+    const int v = m >> 1, h = m & 1;
+    const uint8_t* src = (v < 4 ? bufa : bufb) + 8 * h;
+    const int t = 4 * g + (v & 3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x2 a[4], b[4];
-      pv_operands(bufa, m, g, i, a);
-      pv_operands(bufb, m, g, i, b);
-      const u32x4 p8 = {qa[i >> 1][0], qa[i >> 1][1], qb[i >> 1][0], qb[i >> 1][1]};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        O[4 * i + e] = mfma_16x16x32(u32x4{a[e][0], a[e][1], b[e][0], b[e][1]}, p8, O[4 * i + e]);
+    for (int c = 0; c < kAcc; ++c) {
+      const u32x4 p8 = {qa[c >> 3][0], qa[c >> 3][1], qb[c >> 3][0], qb[c >> 3][1]};
+      O[c] = mfma_16x16x32(widen_tr8(lds_read_tr8(src + pos(t, c))), p8, O[c]);
     }
   }
 
-  // Accumulator 4i + e holds, for head m, d = 64i + 16g + 4r + e in element r.
   __device__ static __forceinline__ void store(const f32x4 (&O)[kAcc], float* row, int g) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *(f32x4*)(row + 64 * i + 16 * g + 4 * r) =
-            f32x4{O[4 * i + 0][r], O[4 * i + 1][r], O[4 * i + 2][r], O[4 * i + 3][r]};
+    for (int u = 0; u < kAcc; ++u) *(f32x4*)(row + 16 * u + 4 * g) = O[u];
   }
 };
 

@@ -8,6 +8,9 @@
 //   ds_read_b64_tr_b16        within each group of 16 lanes, output lane i gets
 //                             element (i & 3) of the 4-element chunks addressed by
 //                             lanes (i >> 2) + 4*v, v = 0..3
+//   ds_read_b64_tr_b8         within each group of 16 lanes, output lane i gets byte
+//                             (i & 7) of the 8-byte chunks addressed by lanes
+//                             (i >> 3) + 2*v, v = 0..7 (byte v of the result)
 //   global_load_lds (16 B)    lane l writes LDS[base + 16*l]
 #pragma once
 
@@ -98,6 +101,12 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                    __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* lds_addr) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)lds_addr);
+  return __builtin_bit_cast(u32x2, v);
 }
 
 __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_addr) {
