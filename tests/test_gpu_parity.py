@@ -489,11 +489,12 @@ def test_mtp_balanced_full_size_fp8_ragged_sampled():
     _assert_mtp_parity(w, out, lse, ref_o, ref_l, T, what=f"mtp fp8_ragged balanced W={W}", requests=req)
 
 
-def test_row_load_policies_agree():
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_row_load_policies_agree(fmt):
     """Streaming (non-temporal) and cached row loads give bit-identical results, per-request,
     batch-balanced, verify-step and NoPE; the streaming result is checked against the oracle."""
     w = workloads.make_workload("row_loads", seq_lens=[3000, 0, 17, 900, 64, 1], heads=16, page_size=16,
-                                num_pages=260, seed=21)
+                                num_pages=260, fmt=fmt, seed=21)
     q4 = workloads.bf16_bits(np.random.default_rng(29).standard_normal((w.batch, 4, 16, 576)).astype(np.float32))
     pd, ph = device_pool(w), host_pool(w)
     runs = {}
