@@ -666,8 +666,8 @@ def main():
             "workload": w.name, "batch": w.batch, "heads": w.heads, "context_tokens": w.tokens,
             "page_size": w.page_size, "pool_pages": w.num_pages, "num_splits": S,
             "schedule": f"batch-balanced, {balanced} workgroups" if balanced else "per-request partitions",
-            # rank-768 rows and NoPE fp8 rows read 64-byte row segments with plain loads
-            "row_loads": "plain" if geom == "rank768" or (nope and w.fmt == "fp8") else row_loads,
+            # rank-768 rows are read in 64-byte row segments with plain loads
+            "row_loads": "plain" if geom == "rank768" else row_loads,
             "layer": "nope-512" if nope else "rope-576", "query_tokens_per_request": T, "geometry": geom,
             "cache_row_bytes": 2 * (RANKS[geom] + 64) if geom in RANKS else w.row_bytes,
             "row_bytes_read": row_bytes_read,

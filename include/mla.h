@@ -193,8 +193,10 @@ MLA_API int mla_decode_balanced_fp8_656(const void* q, const void* kv_cache, int
  * its rope part and pad q_pe with zeros, so the rope part adds nothing to any score).
  * Here the padding is not needed: q is bf16 [batch][num_heads][512] and the scores use
  * the 512 latent values only, s_t = softmax_scale * <q, latent_t>.  The rows' rope part
- * is never read and may hold anything, so a row costs 1,024 bytes of HBM traffic
- * (bf16 cache) or 528 (fp8 cache) instead of 1,152 / 656.  kv_cache, every other
+ * never enters a score and may hold anything (non-finite values included).  A bf16 row
+ * costs 1,024 bytes of HBM traffic instead of 1,152; fp8 rows are streamed whole (656
+ * bytes: the 528 bytes a score uses are not contiguous across rows, and whole-line
+ * streaming of the full rows measured faster than reading the pieces).  kv_cache, every other
  * argument, the results and the errors are those of mla_decode_bf16 / mla_decode_fp8_656. */
 MLA_API int mla_decode_nope_bf16(const void* q, const void* kv_cache, int64_t num_pages,
                                  const int32_t* block_table, int64_t block_table_stride,
@@ -382,9 +384,9 @@ MLA_API int mla_gather_context(const void* kv_cache, int32_t cache_format, int64
  * 147 -> 136 us on MI355X) but keeps rows out of the caches.  MLA_ROW_LOADS_CACHED: plain
  * loads, for batches whose requests share pages within a step (prefix sharing), whose
  * repeated rows then hit in the L2 / last-level cache.  Applies to every later mla_decode*
- * call in the process (single-token, batch-balanced, verify-step and rank-1792 decodes, bf16
- * and fp8 rows); the rank-768 decode and NoPE fp8 rows read 64-byte row segments and always
- * use plain loads.  Returns the previous policy, or -MLA_ERR_SHAPE for an unknown one. */
+ * call in the process (single-token, batch-balanced, verify-step, NoPE and rank-1792 decodes,
+ * bf16 and fp8 rows); the rank-768 decode reads 64-byte row segments and always uses plain
+ * loads.  Returns the previous policy, or -MLA_ERR_SHAPE for an unknown one. */
 enum { MLA_ROW_LOADS_STREAMING = 0, MLA_ROW_LOADS_CACHED = 1 };
 MLA_API int mla_set_row_loads(int policy);
 

@@ -154,10 +154,10 @@ struct Bf16Rows {
 // the form the non-temporal hint needs; otherwise (a tile that crosses a page or holds the
 // partition's clamped tail) each lane finds the token of every chunk it fetches.  Reads stay
 // bank-conflict free: token bases 656 t fall on 16 distinct 16-byte bank groups (656 = 144 mod
-// 256, 144 t / 16 a permutation of 0 .. 15).  Without rope (kRopeDim = 0) only the first 528
-// bytes of each row are loaded, which are not contiguous across rows, so those tiles keep the
-// chunk layout: eight full instructions and a ninth for the scale chunk 32 alone, the lanes
-// past it re-reading chunk 32 into padding.
+// 256, 144 t / 16 a permutation of 0 .. 15).  Without rope (kRopeDim = 0) the scores use the
+// first 528 bytes of each row, but the whole rows are streamed all the same: those 528-byte
+// pieces are not contiguous across rows, and whole-line streaming of the full rows measured
+// faster than half-line plain loads of the pieces; the rope bytes land in LDS unused.
 // ------------------------------------------------------------------------------------
 template <int kRopeDim>
 struct Fp8Rows {
@@ -166,9 +166,7 @@ struct Fp8Rows {
   static constexpr int kRowBytes = kRowBytesFp8;
   static constexpr int kQDim = kLatent + kRopeDim;
   static constexpr int kQSteps = kQDim / 32;
-  static constexpr int kFullOps = kRopeDim ? 10 : 8;    // instructions of 4 whole chunks
-  static constexpr int kLastChunk = kRopeDim ? 40 : 32;  // fetched alone by the last one
-  static constexpr int kDmaOps = kFullOps + 1;
+  static constexpr int kDmaOps = (16 * kRowBytes + 1023) / 1024;  // 11 instructions per tile
   static constexpr int kBufs = 3;  // three tiles per wave with one row group (3 x 4 x 11 KB)
   static constexpr int kTileBytes = kDmaOps * 1024;  // used bytes + padding
   static constexpr int kAcc = 32;
@@ -177,30 +175,24 @@ struct Fp8Rows {
     f32x4 sc[4];  // sc[r][k]: scale of block k of token 4g + r
   };
 
-  static constexpr bool kFlatTile = kRopeDim != 0;  // row-major tiles (else the chunk layout)
-  static constexpr int kChunks = kRowBytes / 16;    // 41 chunks of 16 bytes per row
-  static_assert(!kFlatTile || 16 * kChunks == 64 * (kDmaOps - 1) + 16, "the last instruction: 16 chunks");
+  static constexpr bool kFlatTile = true;        // row-major tiles
+  static constexpr int kChunks = kRowBytes / 16;  // 41 chunks of 16 bytes per row
+  static_assert(16 * kChunks == 64 * (kDmaOps - 1) + 16, "the last instruction: 16 chunks");
 
   // Byte offset of chunk c of token t in a tile.
-  __device__ static __forceinline__ int pos(int t, int c) {
-    return kFlatTile ? t * kRowBytes + 16 * c : 16 * chunk_pos(t, c);
-  }
+  __device__ static __forceinline__ int pos(int t, int c) { return t * kRowBytes + 16 * c; }
 
-  // Row-major tiles: the tile chunk lane L fetches in instruction j, and its token.
+  // The tile chunk lane L fetches in instruction j, and its token.
   __device__ static __forceinline__ int tile_chunk(int lane, int j) {
     return 64 * j + (j == kDmaOps - 1 ? (lane & 15) : lane);
   }
-  // Chunk layout: lane L fetches token L >> 2, 64 bytes of its row per instruction.
-  static constexpr int kTokensPerLane = kFlatTile ? kDmaOps : 1;
-  __device__ static __forceinline__ int fetch_token(int lane, int j) {
-    return kFlatTile ? tile_chunk(lane, j) / kChunks : lane >> 2;
-  }
+  static constexpr int kTokensPerLane = kDmaOps;
+  __device__ static __forceinline__ int fetch_token(int lane, int j) { return tile_chunk(lane, j) / kChunks; }
 
   // Row-major tile fetched row by row: row_of(j) is the row of token fetch_token(lane, j),
   // found as each instruction is issued (a lane's rows are not all held at once).
   template <class RowOf>
   __device__ static __forceinline__ void issue_rows(RowOf&& row_of, uint32_t dst, int lane, bool nt) {
-    static_assert(kFlatTile, "row-major tiles");
 #pragma unroll
     for (int j = 0; j < kDmaOps; ++j) {
       const uint8_t* src = row_of(j) + 16 * (tile_chunk(lane, j) % kChunks);
@@ -208,23 +200,8 @@ struct Fp8Rows {
     }
   }
 
-  // Chunk-layout tiles: rows[0] is the row of token fetch_token(lane, 0); they read half lines
-  // and always use plain loads.
-  __device__ static __forceinline__ void issue(const uint8_t* const (&rows)[kTokensPerLane], uint32_t dst, int lane,
-                                               bool) {
-    if constexpr (!kFlatTile) {
-      const uint8_t* row = rows[0];
-      const uint8_t* src = row + 16 * ((lane & 3) ^ swz(lane >> 2));
-#pragma unroll
-      for (int j = 0; j < kFullOps; ++j) dma16(src + 64 * j, dst + 1024 * j);
-      // chunk kLastChunk for one lane per token; padding for the rest
-      dma16(row + 16 * kLastChunk, dst + 1024 * kFullOps);
-    }
-  }
-
   // Row-major tile whose 16 rows are consecutive slots from `tile` on.
   __device__ static __forceinline__ void issue_contiguous(const uint8_t* tile, uint32_t dst, int lane, bool nt) {
-    static_assert(kFlatTile, "contiguous tiles are row-major");
     if (nt) {
 #pragma unroll
       for (int j = 0; j < kDmaOps; ++j) dma16_nt(tile + 16 * tile_chunk(lane, j), dst + 1024 * j);
@@ -605,14 +582,16 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   // The rows this lane fetches in tile k, from their pages.
   using Pages = int32_t[TPL];
   auto issue_tile = [&](int k, const Pages& page, uint32_t dst) {
-    const uint8_t* rows[TPL];
+    if constexpr (!Fmt::kFlatTile) {
+      const uint8_t* rows[TPL];
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const uint32_t tok = clamp_token(k, Fmt::fetch_token(lane, i));
-      const int64_t slot = (int64_t)page[i] * (int64_t)ps + (int64_t)(tok % ps);
-      rows[i] = p.cache + slot * (int64_t)Fmt::kRowBytes;
+      for (int i = 0; i < TPL; ++i) {
+        const uint32_t tok = clamp_token(k, Fmt::fetch_token(lane, i));
+        const int64_t slot = (int64_t)page[i] * (int64_t)ps + (int64_t)(tok % ps);
+        rows[i] = p.cache + slot * (int64_t)Fmt::kRowBytes;
+      }
+      Fmt::issue(rows, dst, lane, p.stream_rows != 0);
     }
-    Fmt::issue(rows, dst, lane, p.stream_rows != 0);
   };
   auto read_pages = [&](const uint8_t* slot, Pages& page) {
 #pragma unroll

@@ -149,9 +149,9 @@ __device__ __forceinline__ float sum_over_rows(float v) {
 }
 
 // ------------------------------------------------------------------------------------
-// Chunk layout of a tile in LDS (rank-768 rows, NoPE fp8 rows, and the bf16 tiles that fp8
-// tiles are widened into).  A tile is 16 tokens x C chunks of 16 bytes (C = 72 for a
-// 576-value bf16 row, 33 for the loaded part of a NoPE fp8 row).  DMA instruction j fills
+// Chunk layout of a tile in LDS (rank-768 rows, and the bf16 tiles that fp8 tiles are
+// widened into for the multi-token loop).  A tile is 16 tokens x C chunks of 16 bytes (C = 72
+// for a 576-value bf16 row).  DMA instruction j fills
 // chunk positions 64j .. 64j+63, lane L landing at 64j + L; lane L = 4t + v fetches chunk
 // 4j + (v ^ h(t)) of token t, so each group of four lanes reads 64 contiguous bytes of one
 // row (the coalesced form: four lanes per row segment measured 6% faster than one lane per
