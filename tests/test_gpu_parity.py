@@ -691,7 +691,7 @@ def test_gla2_parity(fmt, heads):
 
 # ------------------------------------------------------------------------- NoPE-512
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
-@pytest.mark.parametrize("ps", [3, 16, 64])
+@pytest.mark.parametrize("ps", [3, 16, 24, 64])
 def test_nope_parity(fmt, ps):
     """Zero-rope rows (k_pe NULL) bit for bit; NoPE decode against oracle.decode_nope."""
     lens = [0, 1, 15, 17, 333, 2500]
