@@ -69,15 +69,15 @@ __global__ __launch_bounds__(kWavesPerGroup * 64, 4) void gather_kernel(const ui
 #pragma unroll
       for (int i = 0; i < kRowsInFlight; ++i) {
         if (off[i] < 0) continue;
-        lat[i] = *(const u32x4*)(cache + off[i] + 16 * lane);
-        if (lane < 8) pe[i] = *(const u32x4*)(cache + off[i] + 1024 + 16 * lane);
+        lat[i] = __builtin_nontemporal_load((const u32x4*)(cache + off[i] + 16 * lane));
+        if (lane < 8) pe[i] = __builtin_nontemporal_load((const u32x4*)(cache + off[i] + 1024 + 16 * lane));
       }
 #pragma unroll
       for (int i = 0; i < kRowsInFlight; ++i) {
         if (off[i] < 0) continue;
         uint16_t* o = out + (r0 + g + i) * kRow;
-        *(u32x4*)(o + 8 * lane) = lat[i];
-        if (lane < 8) *(u32x4*)(o + kLatent + 8 * lane) = pe[i];
+        __builtin_nontemporal_store(lat[i], (u32x4*)(o + 8 * lane));
+        if (lane < 8) __builtin_nontemporal_store(pe[i], (u32x4*)(o + kLatent + 8 * lane));
       }
     } else {
       // lane l: codes 8l .. 8l+7 of block l / 16; lanes 0..7: 16 rope bytes each.
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kWavesPerGroup * 64, 4) void gather_kernel(const ui
         const u32x4 packed = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
                               pack_bf16(v[6], v[7])};
         uint16_t* o = out + (r0 + g + i) * kRow;
-        *(u32x4*)(o + 8 * lane) = packed;
-        if (lane < 8) *(u32x4*)(o + kLatent + 8 * lane) = pe[i];
+        __builtin_nontemporal_store(packed, (u32x4*)(o + 8 * lane));
+        if (lane < 8) __builtin_nontemporal_store(pe[i], (u32x4*)(o + kLatent + 8 * lane));
       }
     }
   }
