@@ -33,8 +33,10 @@ __global__ __launch_bounds__(256) void cache_write_bf16(const uint16_t* __restri
   const int64_t slot = slots[tok];
   if (slot < 0) return;
   uint8_t* row = cache + slot * (int64_t)kRowBytesBf16;
-  *(u32x4*)(row + 16 * lane) = *(const u32x4*)(latent + (int64_t)tok * kLatent + 8 * lane);
-  if (lane < 8) *(u32x4*)(row + 1024 + 16 * lane) = rope16(k_pe, tok, lane);
+  // Whole 128-byte lines in and out, each touched once: non-temporal both ways.
+  __builtin_nontemporal_store(__builtin_nontemporal_load((const u32x4*)(latent + (int64_t)tok * kLatent + 8 * lane)),
+                              (u32x4*)(row + 16 * lane));
+  if (lane < 8) __builtin_nontemporal_store(rope16(k_pe, tok, lane), (u32x4*)(row + 1024 + 16 * lane));
 }
 
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
