@@ -66,7 +66,7 @@ def _parse():
                     help="with --graph: steps captured per HIP graph (the largest divisor of --steps up "
                          "to this)")
     ap.add_argument("--row-loads", choices=("streaming", "cached"), default=None,
-                    help="row-load policy of the decodes (mla_set_row_loads); default: the "
+                    help="row loads of the decodes (MLA_FLAG_CACHED_ROWS per call for cached); default: the "
                          "workload's entry in workloads.BENCH_ROW_LOADS")
     ap.add_argument("--graph", action="store_true",
                     help="report the step replayed from a captured HIP graph instead of eager launches "
@@ -452,7 +452,7 @@ def main():
         plain = args.geometry == "mla" and not args.splits
         balanced = workloads.BENCH_BALANCED_WORKGROUPS if (default_bal and plain) else 0
     row_loads = args.row_loads or workloads.BENCH_ROW_LOADS[args.workload]
-    mla.mla_set_row_loads(mla.MLA_ROW_LOADS_CACHED if row_loads == "cached" else mla.MLA_ROW_LOADS_STREAMING)
+    flags = mla.MLA_FLAG_CACHED_ROWS if row_loads == "cached" else 0  # per decode call
     dev = torch.device("cuda:0")
     fmt = mla.MLA_CACHE_BF16_576 if w.fmt == "bf16" else mla.MLA_CACHE_FP8_656
 
@@ -487,8 +487,9 @@ def main():
         mtp = mla.mla_decode_mtp_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_fp8_656
         out4, lse3 = out.view(w.batch, T, w.heads, 512), lse.view(w.batch, T, w.heads)
 
-        def decode(q, pool, bt, lens, scale, num_splits, out=None, lse=None, workspace=None, partials_only=False):
-            return mtp(q, pool, bt, lens, scale, num_splits=num_splits, workspace=workspace,
+        def decode(q, pool, bt, lens, scale, num_splits, out=None, lse=None, workspace=None, partials_only=False,
+                   flags=0):
+            return mtp(q, pool, bt, lens, scale, num_splits=num_splits, workspace=workspace, flags=flags,
                        partials_only=partials_only, out=None if out is None else out4,
                        lse=None if lse is None else lse3)
     elif nope:
@@ -554,18 +555,19 @@ def main():
             mla.mla_cache_write(new_lat, new_pe, new_slots, pool, fmt)
         if e: e[1].record(stream)
         if balanced:
-            decode_bal(q, pool, bt, lens, w.scale, num_workgroups=balanced, workspace=ws, partials_only=True)
+            decode_bal(q, pool, bt, lens, w.scale, num_workgroups=balanced, workspace=ws, partials_only=True,
+                       flags=flags)
             if e: e[2].record(stream)
             mla.mla_merge_lse_balanced(ws, w.batch, rows, balanced, out=out, lse=lse)
         elif S > 1:
-            po, pl = decode(q, pool, bt, lens, w.scale, num_splits=S, workspace=ws, partials_only=True)
+            po, pl = decode(q, pool, bt, lens, w.scale, num_splits=S, workspace=ws, partials_only=True, flags=flags)
             if e: e[2].record(stream)
             if width == 512:
                 mla.mla_merge_lse(po, pl, out=out, lse=lse)
             else:
                 mla.mla_merge_lse_width(po, pl, out=out, lse=lse)
         else:
-            decode(q, pool, bt, lens, w.scale, num_splits=1, out=out, lse=lse)
+            decode(q, pool, bt, lens, w.scale, num_splits=1, out=out, lse=lse, flags=flags)
             if e: e[2].record(stream)
         if e: e[3].record(stream)
 

@@ -24,8 +24,8 @@
  *    are asynchronous on that stream, never synchronise the device and never
  *    read device memory from the host.
  *  - The caller owns all memory.  The library allocates nothing and keeps no
- *    state beyond a per-device architecture check, a thread-local message and
- *    the process-wide row-load hint of mla_set_row_loads (performance only).
+ *    state beyond a per-device cache of the architecture check (and of the
+ *    device's compute-unit count) and a thread-local message.
  *  - Arguments are validated on the host before any launch.  On error the call
  *    returns a nonzero MLA_ERR_* code, launches nothing and records a message
  *    (mla_last_error_message) naming the offending argument.  Nothing aborts,
@@ -33,7 +33,29 @@
  *  - Conditions that cannot be checked without reading device memory are
  *    preconditions: block-table entries inside the context must lie in
  *    [0, num_pages), and 0 <= seq_lens[b] <= block_table_stride * page_size.
- *    Entries past a request's last page are never read (may hold -1).
+ *    Entries past a request's last page are never read (may hold -1).  A wrong
+ *    offset reads the wrong memory and then faults (sabi-mla-vllm, "B300 fix
+ *    (0.2.0)": correct first token, then garbage, then an illegal memory
+ *    access), so the library also comes as a checked build (libmla_checked.so,
+ *    same ABI) whose kernels test both preconditions before forming an address.
+ *
+ * Per-call options of every decode entry point (the two arguments before `stream`)
+ *  - flags: MLA_FLAG_* bits, 0 for the defaults; unknown bits are MLA_ERR_SHAPE.
+ *      MLA_FLAG_CACHED_ROWS: plain loads of the cache rows instead of the default
+ *      non-temporal (streaming) ones.  Results are bit-identical either way.  The
+ *      default suits rows read once per step: whole 128-byte lines per load
+ *      instruction with the non-temporal hint stream faster (long context, random
+ *      pages: bf16 rows 211 -> 189 us per decode, fp8 rows 147 -> 136 us on
+ *      MI355X) but stay out of the caches; plain loads suit batches whose requests
+ *      share pages within a step (prefix sharing), whose repeated rows then hit in
+ *      the L2 / last-level cache.  (The rank-768 decode reads 64-byte row segments
+ *      and always uses plain loads.)
+ *  - check_status: NULL, or (checked build only) a device int32 the caller zeroes
+ *      beforehand.  A checked build's kernels OR MLA_CHECK_* bits into it when a
+ *      precondition fails, and then read page 0 in place of an out-of-pool block id
+ *      and clamp a length into [0, block_table_stride * page_size], so that no read
+ *      leaves the cache or the block table; nothing traps.  The release build
+ *      refuses a non-NULL check_status with MLA_ERR_SHAPE (it checks nothing).
  */
 #ifndef MLA_H_
 #define MLA_H_
@@ -45,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define MLA_API __attribute__((visibility("default")))
@@ -66,6 +88,15 @@ enum {
 enum {
   MLA_CACHE_BF16_576 = 0, /* 576 bf16 values, 1152 bytes per row                  */
   MLA_CACHE_FP8_656 = 1   /* 512 e4m3 codes, 4 fp32 block scales, 64 bf16 = 656 B */
+};
+
+/* Decode option bits (the flags argument). */
+enum { MLA_FLAG_CACHED_ROWS = 1 };
+
+/* Bits a checked build ORs into *check_status. */
+enum {
+  MLA_CHECK_BLOCK_ID = 1, /* a block-table entry a context uses lies outside [0, num_pages) */
+  MLA_CHECK_SEQ_LEN = 2   /* seq_lens[b] < 0 or > block_table_stride * page_size          */
 };
 
 enum { MLA_LATENT = 512, MLA_ROPE = 64, MLA_ROW = 576, MLA_MAX_HEADS = 16, MLA_MAX_Q_LEN = 16,
@@ -110,7 +141,7 @@ MLA_API int mla_decode_bf16(const void* q, const void* kv_cache, int64_t num_pag
                     const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                     int32_t page_size, float softmax_scale, int32_t num_splits,
                     float* out, float* lse, void* workspace, size_t workspace_bytes,
-                    void* stream);
+                    uint32_t flags, int32_t* check_status, void* stream);
 
 /* Decode over an fp8 cache (MLA_CACHE_FP8_656).  Same arguments and results as
  * mla_decode_bf16; kv_cache is uint8 [num_pages][page_size][656], each row
@@ -125,7 +156,7 @@ MLA_API int mla_decode_fp8_656(const void* q, const void* kv_cache, int64_t num_
                        const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                        int32_t page_size, float softmax_scale, int32_t num_splits,
                        float* out, float* lse, void* workspace, size_t workspace_bytes,
-                       void* stream);
+                       uint32_t flags, int32_t* check_status, void* stream);
 
 /* Batch-balanced decode: the same results as mla_decode_bf16 / mla_decode_fp8_656
  * (single-token queries), with the work cut across the whole batch instead of per
@@ -139,10 +170,13 @@ MLA_API int mla_decode_fp8_656(const void* q, const void* kv_cache, int64_t num_
  * balanced wave instead of a tail of long requests.  Two launches, no host synchronisation.
  *
  * batch           1..MLA_MAX_BALANCED_BATCH (1024).
- * num_workgroups  1..65535; one per compute unit (256 on MI355X) is the intended use.
+ * num_workgroups  0..65535; 0 = one per compute unit of the current device (256 on MI355X),
+ *                 the intended use.
  * workspace       device scratch of at least mla_decode_balanced_workspace_size(batch,
  *                 num_heads, num_workgroups) bytes, 16-byte aligned: int64 range
  *                 bounds [batch + 1], then up to batch + num_workgroups - 1 partials.
+ *                 (The size function resolves num_workgroups = 0 the same way; it
+ *                 returns 0 when there is no usable device.)
  * The decode reads seq_lens on the device (no host synchronisation); a request with
  * seq_lens == 0 gets (+0.0, -inf).  Passing out == lse == NULL stops after the decode
  * kernel: the partials stay in the workspace and mla_merge_lse_balanced combines them
@@ -153,7 +187,7 @@ MLA_API int mla_decode_balanced_bf16(const void* q, const void* kv_cache, int64_
                                      const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                      int32_t page_size, float softmax_scale, int32_t num_workgroups,
                                      float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                     void* stream);
+                                     uint32_t flags, int32_t* check_status, void* stream);
 /* Batch-balanced NoPE-512 decode: the schedule of mla_decode_balanced_* with the scores of
  * mla_decode_nope_bf16 / mla_decode_nope_fp8_656 (q bf16 [batch][num_heads][512], the rows'
  * rope part never read).  Arguments, workspace, results and errors as mla_decode_balanced_*. */
@@ -162,13 +196,13 @@ MLA_API int mla_decode_balanced_nope_bf16(const void* q, const void* kv_cache, i
                                           const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                           int32_t page_size, float softmax_scale, int32_t num_workgroups,
                                           float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                          void* stream);
+                                          uint32_t flags, int32_t* check_status, void* stream);
 MLA_API int mla_decode_balanced_nope_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
                                              const int32_t* block_table, int64_t block_table_stride,
                                              const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                              int32_t page_size, float softmax_scale, int32_t num_workgroups,
                                              float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                             void* stream);
+                                             uint32_t flags, int32_t* check_status, void* stream);
 
 /* Merge step of the batch-balanced decode: combines each request's partials left in the
  * workspace by a mla_decode_balanced_* call made with out == lse == NULL and the same
@@ -186,7 +220,7 @@ MLA_API int mla_decode_balanced_fp8_656(const void* q, const void* kv_cache, int
                                         const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                         int32_t page_size, float softmax_scale, int32_t num_workgroups,
                                         float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                        void* stream);
+                                        uint32_t flags, int32_t* check_status, void* stream);
 
 /* NoPE-512 decode: layers without a rotary part (vLLM pull request 55543, description
  * of the NoPE-512 change: such layers keep the 576-value / 656-byte row, store zeros in
@@ -203,13 +237,13 @@ MLA_API int mla_decode_nope_bf16(const void* q, const void* kv_cache, int64_t nu
                                  const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                  int32_t page_size, float softmax_scale, int32_t num_splits,
                                  float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                 void* stream);
+                                 uint32_t flags, int32_t* check_status, void* stream);
 MLA_API int mla_decode_nope_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
                                     const int32_t* block_table, int64_t block_table_stride,
                                     const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                     int32_t page_size, float softmax_scale, int32_t num_splits,
                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                    void* stream);
+                                    uint32_t flags, int32_t* check_status, void* stream);
 
 /* Multi-token verify decode (speculative decoding): q_len query tokens per request, the
  * last q_len positions of its sequence, scored against the cache in one pass that reads
@@ -231,13 +265,13 @@ MLA_API int mla_decode_mtp_bf16(const void* q, const void* kv_cache, int64_t num
                                 const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t num_heads,
                                 int32_t page_size, float softmax_scale, int32_t num_splits,
                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                uint32_t flags, int32_t* check_status, void* stream);
 MLA_API int mla_decode_mtp_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
                                    const int32_t* block_table, int64_t block_table_stride,
                                    const int32_t* seq_lens, int32_t batch, int32_t q_len,
                                    int32_t num_heads, int32_t page_size, float softmax_scale,
                                    int32_t num_splits, float* out, float* lse, void* workspace,
-                                   size_t workspace_bytes, void* stream);
+                                   size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream);
 
 /* Batch-balanced verify decode: the results of mla_decode_mtp_bf16 / mla_decode_mtp_fp8_656
  * (q_len query tokens per request, the same causal reading) with the schedule of
@@ -256,13 +290,13 @@ MLA_API int mla_decode_mtp_balanced_bf16(const void* q, const void* kv_cache, in
                                          const int32_t* seq_lens, int32_t batch, int32_t q_len,
                                          int32_t num_heads, int32_t page_size, float softmax_scale,
                                          int32_t num_workgroups, float* out, float* lse, void* workspace,
-                                         size_t workspace_bytes, void* stream);
+                                         size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream);
 MLA_API int mla_decode_mtp_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
                                             const int32_t* block_table, int64_t block_table_stride,
                                             const int32_t* seq_lens, int32_t batch, int32_t q_len,
                                             int32_t num_heads, int32_t page_size, float softmax_scale,
                                             int32_t num_workgroups, float* out, float* lse, void* workspace,
-                                            size_t workspace_bytes, void* stream);
+                                            size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream);
 
 /* Other latent geometries (qwen-mla-vllm: per-layer latent ranks 256 / 768 / 1792 with a small
  * rotary tail, "How it works"; GLA-g2, the latent split into two head groups, opening section).
@@ -294,7 +328,7 @@ MLA_API int mla_decode_rank256_bf16(const void* q, const void* kv_cache, int64_t
                                     const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                     int32_t page_size, float softmax_scale, int32_t num_splits,
                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                    void* stream);
+                                    uint32_t flags, int32_t* check_status, void* stream);
 MLA_API size_t mla_decode_rank_workspace_size(int32_t batch, int32_t num_heads, int32_t num_splits,
                                               int32_t latent_rank);
 MLA_API int mla_decode_rank768_bf16(const void* q, const void* kv_cache, int64_t num_pages,
@@ -302,25 +336,25 @@ MLA_API int mla_decode_rank768_bf16(const void* q, const void* kv_cache, int64_t
                                     const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                     int32_t page_size, float softmax_scale, int32_t num_splits,
                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                    void* stream);
+                                    uint32_t flags, int32_t* check_status, void* stream);
 MLA_API int mla_decode_rank1792_bf16(const void* q, const void* kv_cache, int64_t num_pages,
                                      const int32_t* block_table, int64_t block_table_stride,
                                      const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                      int32_t page_size, float softmax_scale, int32_t num_splits,
                                      float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                     void* stream);
+                                     uint32_t flags, int32_t* check_status, void* stream);
 MLA_API int mla_decode_gla2_bf16(const void* q, const void* kv_cache, int64_t num_pages,
                                  const int32_t* block_table, int64_t block_table_stride,
                                  const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                  int32_t page_size, float softmax_scale, int32_t num_splits,
                                  float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                 void* stream);
+                                 uint32_t flags, int32_t* check_status, void* stream);
 MLA_API int mla_decode_gla2_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
                                     const int32_t* block_table, int64_t block_table_stride,
                                     const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                                     int32_t page_size, float softmax_scale, int32_t num_splits,
                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                    void* stream);
+                                    uint32_t flags, int32_t* check_status, void* stream);
 
 /* mla_merge_lse for partial rows of `width` values (256, 512, 768 or 1792): part_out fp32
  * [num_splits][batch][num_rows][width], part_lse [num_splits][batch][num_rows], out
@@ -352,7 +386,11 @@ MLA_API int mla_merge_lse(const float* part_out, const float* part_lse, int32_t 
  * MLA_CACHE_FP8_656: per 128-value block a = max|x|, s = a / 448 (fp32, IEEE
  *   division), codes = e4m3fn(x / s) rounded to nearest-even and saturated at
  *   +-448, sign kept; a block with a == 0 stores s = 0 and codes 0x00; then the
- *   four scales and k_pe as bf16. */
+ *   four scales and k_pe as bf16.  A block holding a NaN or an infinity stores the
+ *   quiet NaN scale 0x7FC00000 and 128 codes 0x7F (e4m3fn NaN), so every value of
+ *   that block decodes to NaN and a score that uses it is NaN (this library's
+ *   reading: the pages cover finite latents only; the bf16 row keeps such values
+ *   as they are). */
 MLA_API int mla_cache_write(const void* latent, const void* k_pe, const int64_t* slot_mapping,
                     int32_t num_tokens, void* kv_cache, int32_t cache_format,
                     int64_t num_slots, void* stream);
@@ -370,25 +408,31 @@ MLA_API int mla_cache_write(const void* latent, const void* k_pe, const int64_t*
  * total_rows passed by the caller (the library never reads device memory on the host).
  * Preconditions (not checkable without reading device memory): the cu_rows layout above;
  * seq_starts[b] + rows of b <= block_table_stride * page_size; the block-table entries
- * those tokens use lie in [0, num_pages).  total_rows == 0 launches nothing. */
+ * those tokens use lie in [0, num_pages).  total_rows == 0 launches nothing.
+ * check_status: as for the decodes (NULL in the release build); a checked build tests
+ * every block id the gather uses (MLA_CHECK_BLOCK_ID) and seq_starts[b] + rows of b
+ * against block_table_stride * page_size (MLA_CHECK_SEQ_LEN; the rows past that bound
+ * are then written as zeros). */
 MLA_API int mla_gather_context(const void* kv_cache, int32_t cache_format, int64_t num_pages,
                                int32_t page_size, const int32_t* block_table,
                                int64_t block_table_stride, const int64_t* cu_rows,
                                const int32_t* seq_starts, int32_t batch, int64_t total_rows,
-                               void* out, void* stream);
+                               void* out, int32_t* check_status, void* stream);
 
-/* How the decodes load cache rows (a performance hint; results are identical).
- * MLA_ROW_LOADS_STREAMING (the default): loads carry the non-temporal hint, for rows read
- * once per step; every load instruction reads whole 128-byte lines, and the hint lifts the
- * streaming rate (long context, random pages: bf16 rows 211 -> 189 us per decode, fp8 rows
- * 147 -> 136 us on MI355X) but keeps rows out of the caches.  MLA_ROW_LOADS_CACHED: plain
- * loads, for batches whose requests share pages within a step (prefix sharing), whose
- * repeated rows then hit in the L2 / last-level cache.  Applies to every later mla_decode*
- * call in the process (single-token, batch-balanced, verify-step, NoPE and rank-1792 decodes,
- * bf16 and fp8 rows); the rank-768 decode reads 64-byte row segments and always uses plain
- * loads.  Returns the previous policy, or -MLA_ERR_SHAPE for an unknown one. */
-enum { MLA_ROW_LOADS_STREAMING = 0, MLA_ROW_LOADS_CACHED = 1 };
-MLA_API int mla_set_row_loads(int policy);
+/* 1 for the checked build (libmla_checked.so), 0 for the release build (libmla.so). */
+MLA_API int mla_checked_build(void);
+
+/* The preconditions of the decodes, tested on the host over host copies of the block table
+ * and the lengths (the test the checked build's kernels make on the device, for callers that
+ * hold the tables on the host before uploading them): returns the MLA_CHECK_* bits that hold
+ * (0 when every context lies inside the pool and the table), or -MLA_ERR_NULL /
+ * -MLA_ERR_SHAPE for missing or out-of-range arguments.  Token t of request b uses entry
+ * block_table[b * block_table_stride + t / page_size] for t < seq_lens[b]; entries past a
+ * request's context are not looked at.  q_len and the schedule do not change the
+ * preconditions. */
+MLA_API int mla_check_preconditions_host(const int32_t* block_table, int64_t block_table_stride,
+                                         const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                                         int64_t num_pages);
 
 MLA_API const char* mla_status_string(int status);
 /* Message describing the last failed call on this thread ("" if none). */

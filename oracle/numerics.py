@@ -18,6 +18,11 @@ TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this module.
   magnitudes at or above 448 saturate to 448, sign kept (so -0.0 and negative
   values that round to zero give 0x80).  A block with a == 0 stores s = 0 and
   all codes 0x00.
+* Non-finite latents (reading: the pages quantise finite values only).  A block
+  holding a NaN or an infinity stores the quiet NaN scale (bits 0x7FC00000) and
+  the NaN code 0x7F for all 128 values, so that every value of the block decodes
+  to NaN, as the bf16 row would carry the non-finite value itself into the
+  scores.
 """
 from __future__ import annotations
 
@@ -106,6 +111,8 @@ def quantize_block128(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     shp = x.shape
     k = shp[-1] // 128
     xb = x.reshape(shp[:-1] + (k, 128))
+    bad = ~np.isfinite(xb).all(axis=-1)  # blocks holding a NaN or an infinity
+    xb = np.where(bad[..., None], np.float32(0), xb)
     a = np.max(np.abs(xb), axis=-1)  # float32, exact
     s = (a / np.float32(E4M3_MAX)).astype(np.float32)  # IEEE float32 division
     safe = np.where(s == 0, np.float32(1), s)
@@ -116,4 +123,6 @@ def quantize_block128(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     y = np.where(np.isinf(y), np.copysign(np.float32(E4M3_MAX), y), y).astype(np.float32)
     codes = e4m3_encode(y)
     codes = np.where((s == 0)[..., None], np.uint8(0), codes).astype(np.uint8)
-    return s.astype(np.float32), codes.reshape(shp)
+    codes = np.where(bad[..., None], np.uint8(0x7F), codes).astype(np.uint8)
+    s = np.where(bad, np.uint32(0x7FC00000).view(np.float32), s).astype(np.float32)
+    return s, codes.reshape(shp)

@@ -13,7 +13,7 @@ Entry points (same names as the C ABI in include/mla.h):
     mla_decode_rank256_bf16(q [B, H, 320], kv_cache [pages, ps, 320], ...)   rank-256 layer
     mla_decode_rank768_bf16 / mla_decode_rank1792_bf16(q [B, H, D + 64], ...)   rank-768 / 1792 layers
     mla_decode_gla2_bf16 / mla_decode_gla2_fp8_656(q [B, H, 320], ...)   GLA-g2 head groups
-    mla_decode_balanced_bf16 / mla_decode_balanced_fp8_656(..., num_workgroups=256)   ragged batches
+    mla_decode_balanced_bf16 / mla_decode_balanced_fp8_656(..., num_workgroups=0)   ragged batches
     mla_decode_balanced_nope_bf16 / mla_decode_balanced_nope_fp8_656(q [B, H, 512], ...)
     mla_merge_lse_width(part_out, part_lse, out=None, lse=None)   256- or 512-wide partials
     mla_merge_lse(part_out, part_lse, out=None, lse=None)
@@ -22,6 +22,12 @@ Entry points (same names as the C ABI in include/mla.h):
     mla_decode_workspace_size(batch, num_heads, num_splits)
     mla_decode_balanced_workspace_size(batch, num_heads, num_workgroups)
     mla_merge_lse_balanced(workspace, batch, num_heads, num_workgroups, out=None, lse=None)
+
+Every decode takes two per-call options: flags (MLA_FLAG_CACHED_ROWS: plain row loads for
+batches that share pages within a step; 0: streaming loads) and check_status (a one-element
+int32 device tensor the caller zeroes: the call then runs on the checked build,
+libmla_checked.so, whose kernels OR MLA_CHECK_* bits into it when a block id lies outside the
+pool or a length outside the block table).  The library keeps no other state.
 
 Tensors: q bf16 [B, H, 576]; kv_cache bf16 [num_pages, page_size, 576] or uint8
 [num_pages, page_size, 656]; block_table int32 [B, W]; seq_lens int32 [B];
@@ -36,12 +42,14 @@ import os
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+CHECKED_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_checked.so")
 
 MLA_OK = 0
 MLA_CACHE_BF16_576 = 0
 MLA_CACHE_FP8_656 = 1
-MLA_ROW_LOADS_STREAMING = 0
-MLA_ROW_LOADS_CACHED = 1
+MLA_FLAG_CACHED_ROWS = 1
+MLA_CHECK_BLOCK_ID = 1
+MLA_CHECK_SEQ_LEN = 2
 LATENT, ROPE, ROW = 512, 64, 576
 ROW_BYTES = {MLA_CACHE_BF16_576: 1152, MLA_CACHE_FP8_656: 656}
 MAX_HEADS = 16
@@ -57,7 +65,8 @@ EXPORTED = (
     "mla_decode_balanced_workspace_size", "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
     "mla_merge_lse_balanced", "mla_decode_rank_workspace_size", "mla_decode_rank768_bf16",
     "mla_decode_rank1792_bf16", "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656",
-    "mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656", "mla_set_row_loads",
+    "mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656", "mla_checked_build",
+    "mla_check_preconditions_host",
 )
 
 
@@ -69,24 +78,26 @@ class MlaError(RuntimeError):
         self.status = status
 
 
-_lib = None
+_libs: dict = {}
 
 
-def library() -> ctypes.CDLL:
-    """Load libmla.so (once).  Raises if it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_mla_latent_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+def library(checked: bool = False) -> ctypes.CDLL:
+    """Load libmla.so, or with checked=True libmla_checked.so (once each).  Raises if it has not
+    been built."""
+    path = CHECKED_LIB_PATH if checked else LIB_PATH
+    if path in _libs:
+        return _libs[path]
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m paged_mla_latent_amd.build`")
+    lib = ctypes.CDLL(path)
     c_int, c_i32, c_i64, c_sz, c_f, vp = (ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                                            ctypes.c_float, ctypes.c_void_p)
     lib.mla_decode_workspace_size.argtypes = [c_i32, c_i32, c_i32]
     lib.mla_decode_workspace_size.restype = c_sz
     lib.mla_decode_balanced_workspace_size.argtypes = [c_i32, c_i32, c_i32]
     lib.mla_decode_balanced_workspace_size.restype = c_sz
-    dec = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
+    c_u32 = ctypes.c_uint32
+    dec = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, c_u32, vp, vp]
     lib.mla_decode_rank_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32]
     lib.mla_decode_rank_workspace_size.restype = c_sz
     for name in ("mla_decode_bf16", "mla_decode_fp8_656", "mla_decode_nope_bf16", "mla_decode_nope_fp8_656",
@@ -96,7 +107,7 @@ def library() -> ctypes.CDLL:
                  "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = c_int
-    mtp = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, vp]
+    mtp = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, c_u32, vp, vp]
     for name in ("mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656", "mla_decode_mtp_balanced_bf16",
                  "mla_decode_mtp_balanced_fp8_656"):
         getattr(lib, name).argtypes = mtp
@@ -109,7 +120,7 @@ def library() -> ctypes.CDLL:
     lib.mla_merge_lse_width.restype = c_int
     lib.mla_cache_write.argtypes = [vp, vp, vp, c_i32, vp, c_i32, c_i64, vp]
     lib.mla_cache_write.restype = c_int
-    lib.mla_gather_context.argtypes = [vp, c_i32, c_i64, c_i32, vp, c_i64, vp, vp, c_i32, c_i64, vp, vp]
+    lib.mla_gather_context.argtypes = [vp, c_i32, c_i64, c_i32, vp, c_i64, vp, vp, c_i32, c_i64, vp, vp, vp]
     lib.mla_gather_context.restype = c_int
     lib.mla_status_string.argtypes = [c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -117,25 +128,42 @@ def library() -> ctypes.CDLL:
     lib.mla_last_error_message.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
     lib.mla_abi_version.restype = c_int
-    lib.mla_set_row_loads.argtypes = [c_int]
-    lib.mla_set_row_loads.restype = c_int
-    _lib = lib
+    lib.mla_checked_build.argtypes = []
+    lib.mla_checked_build.restype = c_int
+    lib.mla_check_preconditions_host.argtypes = [vp, c_i64, vp, c_i32, c_i32, c_i64]
+    lib.mla_check_preconditions_host.restype = c_int
+    _libs[path] = lib
     return lib
 
 
-def mla_set_row_loads(policy: int) -> int:
-    """Row-load policy of the decodes (MLA_ROW_LOADS_STREAMING, the default, or
-    MLA_ROW_LOADS_CACHED for batches that share pages within a step); returns the previous one."""
-    prev = library().mla_set_row_loads(int(policy))
-    if prev < 0:
-        _check("mla_set_row_loads", -prev)
-    return prev
+def mla_check_preconditions_host(block_table, seq_lens, page_size: int, num_pages: int) -> int:
+    """MLA_CHECK_* bits of host arrays (block_table int32 [B, W], seq_lens int32 [B]) against the
+    decode preconditions; 0 when they hold."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if bt.ndim != 2 or lens.shape != (bt.shape[0],):
+        raise ValueError("block_table must be [B, W] and seq_lens [B]")
+    lib = library()
+    rc = lib.mla_check_preconditions_host(bt.ctypes.data, bt.shape[1], lens.ctypes.data, bt.shape[0],
+                                          int(page_size), int(num_pages))
+    if rc < 0:
+        _check("mla_check_preconditions_host", -rc)
+    return rc
 
 
-def _check(fn: str, status: int) -> None:
+def _check(fn: str, status: int, lib=None) -> None:
     if status != MLA_OK:
-        lib = library()
+        lib = lib or library()
         raise MlaError(fn, status, lib.mla_status_string(status).decode(), lib.mla_last_error_message().decode())
+
+
+def _options(check_status, dev):
+    """The library to call and the check_status pointer: a status tensor selects the checked build."""
+    if check_status is None:
+        return library(), None
+    _need(check_status, "check_status", torch.int32, 1, dev)
+    return library(checked=True), check_status.data_ptr()
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -166,10 +194,11 @@ def mla_decode_workspace_size(batch: int, num_heads: int, num_splits: int) -> in
 
 
 def _decode(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
-            softmax_scale, num_splits, out, lse, workspace, partials_only=False, q_dim=ROW, out_width=LATENT):
-    lib = library()
+            softmax_scale, num_splits, out, lse, workspace, partials_only=False, q_dim=ROW, out_width=LATENT,
+            flags=0, check_status=None):
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
+    lib, status_ptr = _options(check_status, dev)
     _need(kv_cache, "kv_cache", cache_dtype, 3, dev)
     if kv_cache.shape[2] != row_bytes_last:
         raise ValueError(f"kv_cache rows must have {row_bytes_last} elements, got {kv_cache.shape[2]}")
@@ -200,8 +229,8 @@ def _decode(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache,
     status = getattr(lib, fn)(
         q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1],
         seq_lens.data_ptr(), B, H, kv_cache.shape[1], float(softmax_scale), int(num_splits),
-        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev))
-    _check(fn, status)
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, int(flags), status_ptr, _stream(dev))
+    _check(fn, status, lib)
     if partials_only:
         n = num_splits * B * H
         flat = workspace.view(torch.uint8)[: n * (out_width + 1) * 4].view(torch.float32)
@@ -210,35 +239,39 @@ def _decode(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache,
 
 
 def mla_decode_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                    workspace=None, partials_only=False):
+                    workspace=None, partials_only=False, flags=0, check_status=None):
     """Decode over a bf16 cache [num_pages, page_size, 576]; returns (out [B,H,512], lse [B,H]).
 
     partials_only=True (num_splits > 1) skips the merge and returns the partials
     (part_out [S,B,H,512], part_lse [S,B,H]) as views of the workspace.
     """
     return _decode("mla_decode_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
-                   softmax_scale, num_splits, out, lse, workspace, partials_only)
+                   softmax_scale, num_splits, out, lse, workspace, partials_only,
+                   flags=flags, check_status=check_status)
 
 
 def mla_decode_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                       workspace=None, partials_only=False):
+                       workspace=None, partials_only=False, flags=0, check_status=None):
     """Decode over an fp8 cache uint8 [num_pages, page_size, 656]; returns (out, lse) or the partials."""
     return _decode("mla_decode_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
-                   softmax_scale, num_splits, out, lse, workspace, partials_only)
+                   softmax_scale, num_splits, out, lse, workspace, partials_only,
+                   flags=flags, check_status=check_status)
 
 
 def mla_decode_nope_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                         workspace=None, partials_only=False):
+                         workspace=None, partials_only=False, flags=0, check_status=None):
     """NoPE-512 decode over a bf16 cache: q [B, H, 512]; the rows' rope part is never read."""
     return _decode("mla_decode_nope_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
-                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=LATENT)
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=LATENT,
+                   flags=flags, check_status=check_status)
 
 
 def mla_decode_nope_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                            workspace=None, partials_only=False):
+                            workspace=None, partials_only=False, flags=0, check_status=None):
     """NoPE-512 decode over an fp8 cache: q [B, H, 512]; the rows' rope bytes are never read."""
     return _decode("mla_decode_nope_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
-                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=LATENT)
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=LATENT,
+                   flags=flags, check_status=check_status)
 
 
 def mla_decode_balanced_workspace_size(batch: int, num_heads: int, num_workgroups: int) -> int:
@@ -246,10 +279,11 @@ def mla_decode_balanced_workspace_size(batch: int, num_heads: int, num_workgroup
 
 
 def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
-                     softmax_scale, num_workgroups, out, lse, workspace, partials_only=False, q_dim=ROW):
-    lib = library()
+                     softmax_scale, num_workgroups, out, lse, workspace, partials_only=False, q_dim=ROW, flags=0,
+                     check_status=None):
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
+    lib, status_ptr = _options(check_status, dev)
     _need(kv_cache, "kv_cache", cache_dtype, 3, dev)
     if kv_cache.shape[2] != row_bytes_last:
         raise ValueError(f"kv_cache rows must have {row_bytes_last} elements, got {kv_cache.shape[2]}")
@@ -276,23 +310,26 @@ def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, 
     status = getattr(lib, fn)(
         q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1],
         seq_lens.data_ptr(), B, H, kv_cache.shape[1], float(softmax_scale), int(num_workgroups),
-        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(fn, status)
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), int(flags), status_ptr,
+        _stream(dev))
+    _check(fn, status, lib)
     return workspace if partials_only else (out, lse)
 
 
-def mla_decode_balanced_nope_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256, out=None,
-                                  lse=None, workspace=None, partials_only=False):
+def mla_decode_balanced_nope_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=0, out=None,
+                                  lse=None, workspace=None, partials_only=False, flags=0, check_status=None):
     """Batch-balanced NoPE-512 decode over a bf16 cache: q [B, H, 512]."""
     return _decode_balanced("mla_decode_balanced_nope_bf16", torch.bfloat16, ROW, q, kv_cache, block_table,
-                            seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only, q_dim=LATENT)
+                            seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only, q_dim=LATENT,
+                            flags=flags, check_status=check_status)
 
 
-def mla_decode_balanced_nope_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256,
-                                     out=None, lse=None, workspace=None, partials_only=False):
+def mla_decode_balanced_nope_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=0,
+                                     out=None, lse=None, workspace=None, partials_only=False, flags=0, check_status=None):
     """Batch-balanced NoPE-512 decode over an fp8 cache: q [B, H, 512]."""
     return _decode_balanced("mla_decode_balanced_nope_fp8_656", torch.uint8, 656, q, kv_cache, block_table,
-                            seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only, q_dim=LATENT)
+                            seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only, q_dim=LATENT,
+                            flags=flags, check_status=check_status)
 
 
 def mla_merge_lse_balanced(workspace, batch, num_heads, num_workgroups, out=None, lse=None):
@@ -314,26 +351,28 @@ def mla_merge_lse_balanced(workspace, batch, num_heads, num_workgroups, out=None
     return out, lse
 
 
-def mla_decode_balanced_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256, out=None,
-                             lse=None, workspace=None, partials_only=False):
+def mla_decode_balanced_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=0, out=None,
+                             lse=None, workspace=None, partials_only=False, flags=0, check_status=None):
     """Batch-balanced decode over a bf16 cache (B <= 1024): the batch's tokens cut into
     num_workgroups equal-cost ranges across request boundaries; returns (out [B,H,512], lse [B,H])."""
     return _decode_balanced("mla_decode_balanced_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
-                            softmax_scale, num_workgroups, out, lse, workspace, partials_only)
+                            softmax_scale, num_workgroups, out, lse, workspace, partials_only,
+                            flags=flags, check_status=check_status)
 
 
-def mla_decode_balanced_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256, out=None,
-                                lse=None, workspace=None, partials_only=False):
+def mla_decode_balanced_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=0, out=None,
+                                lse=None, workspace=None, partials_only=False, flags=0, check_status=None):
     """Batch-balanced decode over an fp8 cache uint8 [num_pages, page_size, 656]."""
     return _decode_balanced("mla_decode_balanced_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
-                            softmax_scale, num_workgroups, out, lse, workspace, partials_only)
+                            softmax_scale, num_workgroups, out, lse, workspace, partials_only,
+                            flags=flags, check_status=check_status)
 
 
 def _decode_mtp(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
-                softmax_scale, num_splits, out, lse, workspace, partials_only=False):
-    lib = library()
+                softmax_scale, num_splits, out, lse, workspace, partials_only=False, flags=0, check_status=None):
     _need(q, "q", torch.bfloat16, 4)
     dev = q.device
+    lib, status_ptr = _options(check_status, dev)
     _need(kv_cache, "kv_cache", cache_dtype, 3, dev)
     if kv_cache.shape[2] != row_bytes_last:
         raise ValueError(f"kv_cache rows must have {row_bytes_last} elements, got {kv_cache.shape[2]}")
@@ -363,8 +402,8 @@ def _decode_mtp(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_ca
     status = getattr(lib, fn)(
         q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1],
         seq_lens.data_ptr(), B, T, H, kv_cache.shape[1], float(softmax_scale), int(num_splits),
-        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev))
-    _check(fn, status)
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, int(flags), status_ptr, _stream(dev))
+    _check(fn, status, lib)
     if partials_only:  # [S, B, q_len * H, 512] / [S, B, q_len * H]: query rows act as heads
         n = num_splits * B * T * H
         flat = workspace.view(torch.uint8)[: n * (LATENT + 1) * 4].view(torch.float32)
@@ -373,10 +412,11 @@ def _decode_mtp(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_ca
 
 
 def _decode_mtp_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
-                         softmax_scale, num_workgroups, out, lse, workspace, partials_only=False):
-    lib = library()
+                         softmax_scale, num_workgroups, out, lse, workspace, partials_only=False, flags=0,
+                         check_status=None):
     _need(q, "q", torch.bfloat16, 4)
     dev = q.device
+    lib, status_ptr = _options(check_status, dev)
     _need(kv_cache, "kv_cache", cache_dtype, 3, dev)
     if kv_cache.shape[2] != row_bytes_last:
         raise ValueError(f"kv_cache rows must have {row_bytes_last} elements, got {kv_cache.shape[2]}")
@@ -403,49 +443,55 @@ def _decode_mtp_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int,
     status = getattr(lib, fn)(
         q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1],
         seq_lens.data_ptr(), B, T, H, kv_cache.shape[1], float(softmax_scale), int(num_workgroups),
-        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(fn, status)
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), int(flags), status_ptr,
+        _stream(dev))
+    _check(fn, status, lib)
     return workspace if partials_only else (out, lse)
 
 
-def mla_decode_mtp_balanced_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256, out=None,
-                                 lse=None, workspace=None, partials_only=False):
+def mla_decode_mtp_balanced_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=0, out=None,
+                                 lse=None, workspace=None, partials_only=False, flags=0, check_status=None):
     """Batch-balanced verify step over a bf16 cache: q [B, q_len, H, 576] -> (out [B, q_len, H, 512],
     lse [B, q_len, H]); partials_only=True returns the workspace for mla_merge_lse_balanced(ws, B,
     q_len * H, num_workgroups)."""
     return _decode_mtp_balanced("mla_decode_mtp_balanced_bf16", torch.bfloat16, ROW, q, kv_cache, block_table,
-                                seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only)
+                                seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only,
+                                flags=flags, check_status=check_status)
 
 
-def mla_decode_mtp_balanced_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=256,
-                                    out=None, lse=None, workspace=None, partials_only=False):
+def mla_decode_mtp_balanced_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=0,
+                                    out=None, lse=None, workspace=None, partials_only=False, flags=0, check_status=None):
     """Batch-balanced verify step over an fp8 cache uint8 [num_pages, page_size, 656]."""
     return _decode_mtp_balanced("mla_decode_mtp_balanced_fp8_656", torch.uint8, 656, q, kv_cache, block_table,
-                                seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only)
+                                seq_lens, softmax_scale, num_workgroups, out, lse, workspace, partials_only,
+                                flags=flags, check_status=check_status)
 
 
 def mla_decode_mtp_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                        workspace=None, partials_only=False):
+                        workspace=None, partials_only=False, flags=0, check_status=None):
     """Verify-step decode over a bf16 cache: q [B, q_len, H, 576] -> (out [B, q_len, H, 512], lse [B, q_len, H]).
 
     seq_lens count the q_len new tokens; query i sees tokens 0 .. L - q_len + i.
     partials_only=True (num_splits > 1) returns the partials [S, B, q_len * H, ...] instead."""
     return _decode_mtp("mla_decode_mtp_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
-                       softmax_scale, num_splits, out, lse, workspace, partials_only)
+                       softmax_scale, num_splits, out, lse, workspace, partials_only,
+                       flags=flags, check_status=check_status)
 
 
 def mla_decode_mtp_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                           workspace=None, partials_only=False):
+                           workspace=None, partials_only=False, flags=0, check_status=None):
     """Verify-step decode over an fp8 cache uint8 [num_pages, page_size, 656]."""
     return _decode_mtp("mla_decode_mtp_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
-                       softmax_scale, num_splits, out, lse, workspace, partials_only)
+                       softmax_scale, num_splits, out, lse, workspace, partials_only,
+                       flags=flags, check_status=check_status)
 
 
 def mla_decode_rank256_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                            workspace=None, partials_only=False):
+                            workspace=None, partials_only=False, flags=0, check_status=None):
     """Rank-256 layer: kv_cache bf16 [pages, ps, 320], q [B, H, 320] -> out [B, H, 256], lse [B, H]."""
     return _decode("mla_decode_rank256_bf16", torch.bfloat16, 320, q, kv_cache, block_table, seq_lens,
-                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=320, out_width=256)
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=320, out_width=256,
+                   flags=flags, check_status=check_status)
 
 
 def mla_decode_rank_workspace_size(batch: int, num_heads: int, num_splits: int, latent_rank: int) -> int:
@@ -453,31 +499,35 @@ def mla_decode_rank_workspace_size(batch: int, num_heads: int, num_splits: int, 
 
 
 def mla_decode_rank768_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                            workspace=None, partials_only=False):
+                            workspace=None, partials_only=False, flags=0, check_status=None):
     """Rank-768 layer: kv_cache bf16 [pages, ps, 832], q [B, H, 832] -> out [B, H, 768], lse [B, H]."""
     return _decode("mla_decode_rank768_bf16", torch.bfloat16, 832, q, kv_cache, block_table, seq_lens,
-                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=832, out_width=768)
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=832, out_width=768,
+                   flags=flags, check_status=check_status)
 
 
 def mla_decode_rank1792_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                             workspace=None, partials_only=False):
+                             workspace=None, partials_only=False, flags=0, check_status=None):
     """Rank-1792 layer: kv_cache bf16 [pages, ps, 1856], q [B, H, 1856] -> out [B, H, 1792], lse [B, H]."""
     return _decode("mla_decode_rank1792_bf16", torch.bfloat16, 1856, q, kv_cache, block_table, seq_lens,
-                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=1856, out_width=1792)
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=1856, out_width=1792,
+                   flags=flags, check_status=check_status)
 
 
 def mla_decode_gla2_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                         workspace=None, partials_only=False):
+                         workspace=None, partials_only=False, flags=0, check_status=None):
     """GLA-g2 on the 576-value row: q [B, H, 320] (H even) -> out [B, H, 256], lse [B, H]."""
     return _decode("mla_decode_gla2_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
-                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=320, out_width=256)
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=320, out_width=256,
+                   flags=flags, check_status=check_status)
 
 
 def mla_decode_gla2_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
-                            workspace=None, partials_only=False):
+                            workspace=None, partials_only=False, flags=0, check_status=None):
     """GLA-g2 on the 656-byte fp8 row: q [B, H, 320] (H even) -> out [B, H, 256], lse [B, H]."""
     return _decode("mla_decode_gla2_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
-                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=320, out_width=256)
+                   softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=320, out_width=256,
+                   flags=flags, check_status=check_status)
 
 
 def mla_merge_lse_width(part_out, part_lse, out=None, lse=None):
@@ -548,12 +598,13 @@ def mla_cache_write(latent, k_pe, slot_mapping, kv_cache, cache_format):
                                                   kv_cache.data_ptr(), int(cache_format), num_slots, _stream(dev)))
 
 
-def mla_gather_context(kv_cache, cache_format, block_table, cu_rows, total_rows, seq_starts=None, out=None):
+def mla_gather_context(kv_cache, cache_format, block_table, cu_rows, total_rows, seq_starts=None, out=None,
+                       check_status=None):
     """Context rows of every request as bf16 [total_rows, 576] (fp8 rows upconverted).
 
     cu_rows int64 [B + 1] on the device (request b fills rows cu_rows[b] .. cu_rows[b+1]),
-    total_rows = cu_rows[B] as a host int; seq_starts int32 [B] (None: gather from token 0)."""
-    lib = library()
+    total_rows = cu_rows[B] as a host int; seq_starts int32 [B] (None: gather from token 0);
+    check_status: as for the decodes (runs the checked build)."""
     if cache_format == MLA_CACHE_BF16_576:
         _need(kv_cache, "kv_cache", torch.bfloat16, 3)
     elif cache_format == MLA_CACHE_FP8_656:
@@ -561,6 +612,7 @@ def mla_gather_context(kv_cache, cache_format, block_table, cu_rows, total_rows,
     else:
         raise ValueError(f"unknown cache_format {cache_format}")
     dev = kv_cache.device
+    lib, status_ptr = _options(check_status, dev)
     if kv_cache.shape[2] != (ROW if cache_format == MLA_CACHE_BF16_576 else 656):
         raise ValueError("kv_cache rows have the wrong width for cache_format")
     _need(block_table, "block_table", torch.int32, 2, dev)
@@ -580,5 +632,5 @@ def mla_gather_context(kv_cache, cache_format, block_table, cu_rows, total_rows,
     _check("mla_gather_context", lib.mla_gather_context(
         kv_cache.data_ptr(), int(cache_format), kv_cache.shape[0], kv_cache.shape[1], block_table.data_ptr(),
         block_table.shape[1], cu_rows.data_ptr(), _ptr(seq_starts), B, int(total_rows), out.data_ptr(),
-        _stream(dev)))
+        status_ptr, _stream(dev)), lib)
     return out

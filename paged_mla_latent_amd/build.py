@@ -1,9 +1,12 @@
-"""Build libmla.so (the gfx950 kernels and their C ABI) in place with hipcc.
+"""Build libmla.so (the gfx950 kernels and their C ABI) and its checked twin in place with hipcc.
 
-    python -m paged_mla_latent_amd.build
+    python -m paged_mla_latent_amd.build            # both libraries
+    python -m paged_mla_latent_amd.build --release  # libmla.so only
 
-Object files go to paged_mla_latent_amd/_build/, the library to
-paged_mla_latent_amd/libmla.so.  Every call recompiles.
+Object files go to paged_mla_latent_amd/_build/ (_build_checked/), the libraries to
+paged_mla_latent_amd/libmla.so and libmla_checked.so.  The checked build compiles the same
+sources with -DMLA_CHECKED: its kernels test the decode preconditions (block ids inside the
+pool, lengths inside the block table) before forming any address.  Every call recompiles.
 """
 from __future__ import annotations
 
@@ -17,8 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmla.so")
+CHECKED_LIB_PATH = os.path.join(HERE, "libmla_checked.so")
 SOURCES = ["mla_api.hip", "decode.hip", "decode_wide.hip", "merge.hip", "cache_write.hip", "gather.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -39,20 +42,35 @@ def _run(cmd: list[str]) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libmla.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *COMMON, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
+def _jobs(checked: bool):
+    build_dir = os.path.join(HERE, "_build_checked" if checked else "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    objs = [os.path.join(build_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    extra = ["-DMLA_CHECKED=1"] if checked else []
+    cmds = [[HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    return objs, cmds
+
+
+def _link(objs: list[str], path: str) -> None:
+    tmp = path + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False, checked: bool = True) -> str:
+    """Compile every source for gfx950 and link libmla.so (and, with checked=True, also
+    libmla_checked.so); returns the release library's path."""
+    variants = [False, True] if checked else [False]
+    plans = {v: _jobs(v) for v in variants}
+    cmds = [c for v in variants for c in plans[v][1]]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+    for v in variants:
+        _link(plans[v][0], CHECKED_LIB_PATH if v else LIB_PATH)
     return LIB_PATH
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, checked="--release" not in sys.argv))

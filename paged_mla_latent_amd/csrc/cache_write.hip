@@ -8,8 +8,11 @@
 //    reduce a = max|x| (fp32, exact), s = a / 448 (IEEE division), each code is
 //    e4m3fn(x / s) rounded to nearest-even.  The quotient is clamped to +-448 before
 //    the hardware conversion, which rounds to nearest-even but does not saturate; a
-//    block with a == 0 stores s = 0 and zero codes.  Bytes: [0,512) codes,
-//    [512,528) scales (little-endian fp32), [528,656) k_pe as bf16.
+//    block with a == 0 stores s = 0 and zero codes.  A block holding a NaN or an infinity
+//    stores the NaN scale 0x7FC00000 and the NaN code 0x7F for all 128 values, so that it
+//    decodes to NaN (a quotient by an infinite or NaN scale would otherwise turn into
+//    plausible finite codes).  Bytes: [0,512) codes, [512,528) scales (little-endian fp32),
+//    [528,656) k_pe as bf16.
 // k_pe == nullptr (a NoPE layer): the rope part is written as zeros.
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -60,13 +63,23 @@ __global__ __launch_bounds__(256) void cache_write_fp8(const uint16_t* __restric
     x[2 * i + 1] = bf16_to_float(raw[i] >> 16);
   }
   float a = 0.f;
+  int nonfinite = 0;  // a NaN or an infinity among this lane's values
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+  for (int i = 0; i < 8; ++i) {
+    a = fmaxf(a, fabsf(x[i]));
+    nonfinite |= (raw[i / 2] >> (16 * (i & 1)) & 0x7F80u) == 0x7F80u ? 1 : 0;  // exponent all ones
+  }
 #pragma unroll
-  for (int mask = 8; mask >= 1; mask >>= 1) a = fmaxf(a, __shfl_xor(a, mask, 64));
-  const float s = a / 448.0f;
+  for (int mask = 8; mask >= 1; mask >>= 1) {
+    a = fmaxf(a, __shfl_xor(a, mask, 64));
+    nonfinite |= __shfl_xor(nonfinite, mask, 64);
+  }
+  float s = a / 448.0f;
   u32x2 codes = {0u, 0u};
-  if (s != 0.f) {
+  if (nonfinite) {
+    s = __uint_as_float(0x7FC00000u);
+    codes = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+  } else if (s != 0.f) {
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(x[i] / s, -448.0f), 448.0f);

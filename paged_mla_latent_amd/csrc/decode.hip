@@ -547,6 +547,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 
   const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
   const uint32_t ps = (uint32_t)p.page_size;
+  uint32_t bad = 0;  // checked build: MLA_CHECK_* bits of the block ids this lane used
   const int my_tok = lane >> 2;  // the token whose page id this lane fetches
   constexpr int TPL = Fmt::kTokensPerLane;  // the tokens whose rows this lane fetches
   // Tile buffers per wave: Fmt::kBufs for one row group; the shared-tile loop of G > 1 is
@@ -595,7 +596,8 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   };
   auto read_pages = [&](const uint8_t* slot, Pages& page) {
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) page[i] = *(const int32_t*)(slot + 16 * Fmt::fetch_token(lane, i));
+    for (int i = 0; i < TPL; ++i)
+      page[i] = checked_page(*(const int32_t*)(slot + 16 * Fmt::fetch_token(lane, i)), p.num_pages, bad);
   };
   // Row-major tiles (Fmt::kFlatTile) take their page ids from a page-id slot in LDS (token T's
   // page at byte 16T): a tile of 16 consecutive slots of one page is fetched as one run (a single
@@ -608,14 +610,14 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       const uint32_t q0 = __builtin_amdgcn_readfirstlane(a % ps);  // its slot in its page (uniform)
       const bool nt = p.stream_rows != 0;
       if (a + (kTile - 1) <= tlast && q0 + kTile <= ps) {
-        const int32_t pg = __builtin_amdgcn_readfirstlane(*(const int32_t*)pids);
+        const int32_t pg = __builtin_amdgcn_readfirstlane(checked_page(*(const int32_t*)pids, p.num_pages, bad));
         Fmt::issue_contiguous(p.cache + ((int64_t)pg * ps + q0) * Fmt::kRowBytes, dst, lane, nt);
       } else {
         auto row_of = [&](int i) -> const uint8_t* {
           const uint32_t T = (uint32_t)Fmt::fetch_token(lane, i);
           uint32_t off = q0 + min(T, tlast - a);  // slot of the clamped token, before wrapping
           off = ps >= (uint32_t)kTile ? (off >= ps ? off - ps : off) : off % ps;
-          const int32_t pg = *(const int32_t*)(pids + 16 * T);
+          const int32_t pg = checked_page(*(const int32_t*)(pids + 16 * T), p.num_pages, bad);
           return p.cache + ((int64_t)pg * ps + off) * Fmt::kRowBytes;
         };
         Fmt::issue_rows(row_of, dst, lane, nt);
@@ -748,7 +750,8 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 #pragma unroll
       for (int i = 0; i < TPL; ++i)
         page_first[t][i] = (G == 1 ? k + kWaves * t < ntiles : ntiles > 0)
-                               ? bt[clamp_token(k + kWaves * t, Fmt::fetch_token(lane, i)) / ps]
+                               ? checked_page(bt[clamp_token(k + kWaves * t, Fmt::fetch_token(lane, i)) / ps],
+                                              p.num_pages, bad)
                                : 0;
 #pragma unroll
     for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
@@ -841,6 +844,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   }
 
   finish_rows<TF, G, kGla2, kOut>(smem, O, m_run, l_run, R, H, out, lse);
+  report_checks(bad, p.check_status);
 }
 
 // Prefix sums over the requests of a batch of B <= kMaxBalancedBatch: out[0] = 0, out[b + 1] =
@@ -907,6 +911,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   int b = blockIdx.x;
   int s = blockIdx.y;
   int64_t L;
+  uint32_t lbad = 0;  // checked build: a length outside [0, bt_stride * page_size]
   if (p.compact) {
     // Scratch in the tile memory, which the pipeline only uses after this prologue.
     static_assert(smem_bytes<Fmt>() >= (3 * kMaxBalancedBatch + 2 + 2 * kWaves) * 4, "compaction scratch");
@@ -914,15 +919,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
     int32_t* full_s = len_s + kMaxBalancedBatch;       // prefix of non-empty partition counts
     int32_t* empty_s = full_s + kMaxBalancedBatch + 1;  // prefix of empty partition counts
     const int B = p.batch, S = p.num_splits;
-    const int64_t c = max((p.bt_stride + S - 1) / S, (int64_t)1);  // pages per partition
     auto nonempty = [&](int r) -> int32_t {
-      const int32_t Lr = p.seq_lens[r];
+      const int32_t Lr = (int32_t)checked_len(p.seq_lens[r], p.bt_stride, p.page_size, lbad);
       len_s[r] = Lr;
-      return (int32_t)((((int64_t)Lr + p.page_size - 1) / p.page_size + c - 1) / c);
+      return counted_partitions(Lr, p.page_size, p.bt_stride, S);
     };
     scan_requests<int32_t>(B, nonempty, full_s, (int32_t*)smem);
     scan_requests<int32_t>(
         B, [&](int r) -> int32_t { return S - (full_s[r + 1] - full_s[r]); }, empty_s, (int32_t*)smem + kWaves);
+    report_checks(lbad, p.check_status);
     const int32_t w = (int32_t)(blockIdx.y * gridDim.x + blockIdx.x);
     const int32_t E = full_s[B];
     if (w >= E && p.skip_empty) return;  // an empty partition: nothing to write (uniform)
@@ -937,7 +942,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
     L = len_s[b];
     __syncthreads();  // the scratch is tile memory from here on
   } else {
-    L = p.seq_lens[b];
+    L = checked_len(p.seq_lens[b], p.bt_stride, p.page_size, lbad);
+    report_checks(lbad, p.check_status);
   }
   const Range rg = partition(L, p.page_size, p.num_splits, s, p.bt_stride);
   if (p.skip_empty && rg.t0 >= rg.t1) return;  // empty partition, no partial (uniform)
@@ -967,13 +973,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
   __shared__ int64_t v_s[kMaxBalancedBatch + 1];
   const int B = p.batch;
+  uint32_t lbad = 0;  // checked build: a length outside [0, bt_stride * page_size]
   scan_requests<int64_t>(
       B,
       [&](int r) -> int64_t {
-        const int64_t L = p.seq_lens[r];
+        const int64_t L = checked_len(p.seq_lens[r], p.bt_stride, p.page_size, lbad);
         return L > 0 ? L + kSegmentCost : 0;
       },
       v_s, (int64_t*)smem);
+  report_checks(lbad, p.check_status);
   if (blockIdx.x == 0)
     for (int b = threadIdx.x; b <= B; b += kWaves * 64) p.cu[b] = v_s[b];
 

@@ -80,7 +80,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_wide_kernel(DecodeParam
   const int s = blockIdx.y;
   const int H = p.heads;
 
-  const int64_t L = p.seq_lens[b];
+  uint32_t bad = 0;  // checked build: MLA_CHECK_* bits of this lane's length and block ids
+  const int64_t L = checked_len(p.seq_lens[b], p.bt_stride, p.page_size, bad);
+  report_checks(bad, p.check_status);
   const Range rg = partition(L, p.page_size, p.num_splits, s, p.bt_stride);
   const int n = (int)(rg.t1 - rg.t0);
   const int ntiles = (n + kTile - 1) / kTile;
@@ -160,7 +162,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_wide_kernel(DecodeParam
   };
   auto read_pages = [&](int slot, int32_t (&page)[TPL]) {
 #pragma unroll
-    for (int h = 0; h < TPL; ++h) page[h] = *(const int32_t*)(pslot + 256 * slot + 16 * (row_tok + 8 * h));
+    for (int h = 0; h < TPL; ++h)
+      page[h] = checked_page(*(const int32_t*)(pslot + 256 * slot + 16 * (row_tok + 8 * h)), p.num_pages, bad);
   };
   // Chunk c of token t in a tile: line_pos or chunk_pos.
   auto pos = [&](int tk, int c) { return Wd::kLine ? line_pos(tk, c) : chunk_pos(tk, c); };
@@ -234,7 +237,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_wide_kernel(DecodeParam
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t)
 #pragma unroll
-    for (int h = 0; h < TPL; ++h) page_first[t][h] = (t < ntiles) ? bt[clamp_token(t, row_tok + 8 * h) / ps] : 0;
+    for (int h = 0; h < TPL; ++h)
+      page_first[t][h] = (t < ntiles) ? checked_page(bt[clamp_token(t, row_tok + 8 * h) / ps], p.num_pages, bad) : 0;
 #pragma unroll
   for (int i = 0; i < QS; ++i) asm volatile("" : "+a"(qf[i]));
 #pragma unroll
@@ -285,6 +289,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_wide_kernel(DecodeParam
     if (wave == 0 && g == 0)
       *lse = m_run == -INFINITY ? -INFINITY + l : (m_run + fast_log2(l)) * 0.69314718055994530942f;
   }
+  report_checks(bad & kCheckBlockId, p.check_status);
 }
 
 }  // namespace

@@ -28,7 +28,8 @@ __global__ __launch_bounds__(kWavesPerGroup * 64, 4) void gather_kernel(const ui
                                                                      const int64_t* __restrict__ cu_rows,
                                                                      const int32_t* __restrict__ seq_starts,
                                                                      int batch, int page_size, int64_t total_rows,
-                                                                     uint16_t* __restrict__ out) {
+                                                                     uint16_t* __restrict__ out, int64_t num_pages,
+                                                                     int32_t* check_status) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int64_t r0 = ((int64_t)blockIdx.x * kWavesPerGroup + wave) * kRowsPerWave;
@@ -38,7 +39,9 @@ __global__ __launch_bounds__(kWavesPerGroup * 64, 4) void gather_kernel(const ui
   // Lane j < 32 resolves row r0 + j: its request (binary search over cu_rows; every lane
   // runs the same number of steps), token, page and byte offset, all in 64-bit.  The
   // lookups of the 32 rows run in parallel instead of one dependent chain per row.
+  constexpr int64_t kZeroRow = -2;  // checked build: a token past the block table, written as zeros
   int64_t my_off = -1;
+  uint32_t bad = 0;  // checked build: MLA_CHECK_* bits of this lane's row
   {
     const int64_t r = r0 + lane;
     if (lane < kRowsPerWave && r < total_rows) {
@@ -48,10 +51,16 @@ __global__ __launch_bounds__(kWavesPerGroup * 64, 4) void gather_kernel(const ui
         if (cu_rows[mid] <= r) lo = mid; else hi = mid;
       }
       const int64_t t = (seq_starts ? (int64_t)seq_starts[lo] : 0) + (r - cu_rows[lo]);
-      const int64_t page = block_table[(int64_t)lo * bt_stride + t / page_size];
-      my_off = (page * page_size + t % page_size) * (int64_t)kRowBytes;
+      if (kChecked && !len_in_table(t + 1, bt_stride, page_size)) {
+        bad |= kCheckSeqLen;
+        my_off = kZeroRow;
+      } else {
+        const int64_t page = checked_page(block_table[(int64_t)lo * bt_stride + t / page_size], num_pages, bad);
+        my_off = (page * page_size + t % page_size) * (int64_t)kRowBytes;
+      }
     }
   }
+  report_checks(bad, check_status);
   auto row_off = [&](int j) -> int64_t {  // wave-uniform offset of row r0 + j (-1: none)
     const uint32_t lo32 = __builtin_amdgcn_readlane((uint32_t)my_off, j);
     const uint32_t hi32 = __builtin_amdgcn_readlane((uint32_t)((uint64_t)my_off >> 32), j);
@@ -64,6 +73,15 @@ __global__ __launch_bounds__(kWavesPerGroup * 64, 4) void gather_kernel(const ui
     int64_t off[kRowsInFlight];
 #pragma unroll
     for (int i = 0; i < kRowsInFlight; ++i) off[i] = row_off(g + i);
+    if constexpr (kChecked) {
+#pragma unroll
+      for (int i = 0; i < kRowsInFlight; ++i) {
+        if (off[i] != kZeroRow) continue;
+        uint16_t* o = out + (r0 + g + i) * kRow;
+        *(u32x4*)(o + 8 * lane) = u32x4{0u, 0u, 0u, 0u};
+        if (lane < 8) *(u32x4*)(o + kLatent + 8 * lane) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
     if constexpr (!kFp8) {
       u32x4 lat[kRowsInFlight], pe[kRowsInFlight];
 #pragma unroll
@@ -116,18 +134,21 @@ __global__ __launch_bounds__(kWavesPerGroup * 64, 4) void gather_kernel(const ui
 
 }  // namespace
 
-hipError_t launch_gather(const uint8_t* cache, int fp8, const int32_t* block_table, int64_t bt_stride,
-                         const int64_t* cu_rows, const int32_t* seq_starts, int batch, int page_size,
-                         int64_t total_rows, uint16_t* out, hipStream_t stream) {
+hipError_t launch_gather(const uint8_t* cache, int fp8, int64_t num_pages, const int32_t* block_table,
+                         int64_t bt_stride, const int64_t* cu_rows, const int32_t* seq_starts, int batch,
+                         int page_size, int64_t total_rows, uint16_t* out, int32_t* check_status,
+                         hipStream_t stream) {
   if (total_rows == 0) return hipSuccess;
   const int64_t rows_per_group = (int64_t)kRowsPerWave * kWavesPerGroup;  // 128
   const dim3 grid((unsigned)((total_rows + rows_per_group - 1) / rows_per_group));
   if (fp8)
     hipLaunchKernelGGL(gather_kernel<true>, grid, dim3(kWavesPerGroup * 64), 0, stream, cache, block_table,
-                       bt_stride, cu_rows, seq_starts, batch, page_size, total_rows, out);
+                       bt_stride, cu_rows, seq_starts, batch, page_size, total_rows, out, num_pages,
+                       check_status);
   else
     hipLaunchKernelGGL(gather_kernel<false>, grid, dim3(kWavesPerGroup * 64), 0, stream, cache, block_table,
-                       bt_stride, cu_rows, seq_starts, batch, page_size, total_rows, out);
+                       bt_stride, cu_rows, seq_starts, batch, page_size, total_rows, out, num_pages,
+                       check_status);
   return hipGetLastError();
 }
 

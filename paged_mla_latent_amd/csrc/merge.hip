@@ -104,9 +104,7 @@ __global__ __launch_bounds__(kGroups * kCols) void merge_counted_kernel(const fl
                                                                        float* __restrict__ out,
                                                                        float* __restrict__ lse) {
   const int64_t bh = blockIdx.x;
-  const int64_t L = seq_lens[bh / rows_per_request];
-  const int64_t c = max((bt_stride + S - 1) / S, (int64_t)1);
-  const int n = (int)(((L + page_size - 1) / page_size + c - 1) / c);
+  const int n = counted_partitions(seq_lens[bh / rows_per_request], page_size, bt_stride, S);
   merge_row(part_out, part_lse, n, bh, rows, width, bh, out, lse);
 }
 
@@ -181,11 +179,7 @@ __global__ __launch_bounds__(64) void merge_few_kernel(const float* __restrict__
                                                        float* __restrict__ lse) {
   const int64_t bh = blockIdx.x;
   int n = S;
-  if constexpr (kCounted) {
-    const int64_t L = seq_lens[bh / rows_per_request];
-    const int64_t c = max((bt_stride + S - 1) / S, (int64_t)1);
-    n = (int)(((L + page_size - 1) / page_size + c - 1) / c);
-  }
+  if constexpr (kCounted) n = counted_partitions(seq_lens[bh / rows_per_request], page_size, bt_stride, S);
   merge_row_wave<NV>(part_out, part_lse, n, bh, rows, bh, out, lse);
 }
 

@@ -58,8 +58,19 @@ int device_cus() {
   return g_cus[dev].load(std::memory_order_relaxed);
 }
 
-// Row-load policy of the decodes (mla_set_row_loads), process-wide.
-std::atomic<int> g_row_loads{MLA_ROW_LOADS_STREAMING};
+// The per-call options of the decodes: known flag bits only; check_status only in the
+// checked build (the release build tests nothing and must not pretend to).
+int check_options(const char* fn, uint32_t flags, const int32_t* check_status) {
+  if (flags & ~(uint32_t)MLA_FLAG_CACHED_ROWS)
+    return fail(MLA_ERR_SHAPE, "%s: unknown flag bits 0x%x", fn, flags & ~(uint32_t)MLA_FLAG_CACHED_ROWS);
+  if (check_status) {
+    if (!mla::kChecked)
+      return fail(MLA_ERR_SHAPE, "%s: check_status needs the checked build (libmla_checked.so)", fn);
+    if ((reinterpret_cast<uintptr_t>(check_status) & 3u) != 0)
+      return fail(MLA_ERR_ALIGN, "%s: check_status must be 4-byte aligned", fn);
+  }
+  return MLA_OK;
+}
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return MLA_OK;
@@ -84,7 +95,7 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
                   const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
                   int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
                   int32_t num_splits, float* out, float* lse, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  uint32_t flags, int32_t* check_status, void* stream) {
   static const char* const kNames[] = {"mla_decode_bf16",         "mla_decode_fp8_656",
                                        "mla_decode_nope_bf16",    "mla_decode_nope_fp8_656",
                                        "mla_decode_rank256_bf16", "mla_decode_gla2_bf16",
@@ -97,6 +108,7 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
                         : kind == kRank1792Bf16       ? 1792
                                                       : MLA_LATENT;
   const char* fn = q_len == 1 ? kNames[kind] : (kind == kBf16 ? "mla_decode_mtp_bf16" : "mla_decode_mtp_fp8_656");
+  if (int rc0 = check_options(fn, flags, check_status)) return rc0;
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
@@ -163,7 +175,9 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
   // Merged here: empty partitions need not leave the (0, -inf) partial that a caller's own merge
   // of the workspace would read.
   p.skip_empty = num_splits > 1 && !partials_only;
-  p.stream_rows = g_row_loads.load(std::memory_order_relaxed) == MLA_ROW_LOADS_STREAMING;
+  p.stream_rows = (flags & MLA_FLAG_CACHED_ROWS) == 0;
+  p.num_pages = num_pages;
+  p.check_status = check_status;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t launched;
   switch (kind) {
@@ -211,11 +225,13 @@ BalancedWorkspace balanced_layout(void* workspace, int64_t batch, int64_t heads,
 int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void* kv_cache, int64_t num_pages,
                     const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
                     int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out,
-                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                    float* lse, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status,
+                    void* stream) {
   static const char* const kNames[] = {"mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
                                        "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656"};
   static const char* const kMtpNames[] = {"mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656"};
   const char* fn = mtp ? kMtpNames[kind == kFp8] : kNames[kind];
+  if (int rc0 = check_options(fn, flags, check_status)) return rc0;
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
@@ -238,20 +254,33 @@ int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void
     return fail(MLA_ERR_SHAPE, "%s: block_table_stride=%lld must be >= 1", fn, (long long)block_table_stride);
   if (block_table_stride > ((int64_t)1 << 31) / page_size + 1)
     return fail(MLA_ERR_SHAPE, "%s: block_table_stride * page_size exceeds the int32 token range", fn);
-  if (num_workgroups < 1 || num_workgroups > 65535)
-    return fail(MLA_ERR_SHAPE, "%s: num_workgroups=%d outside [1, 65535]", fn, num_workgroups);
+  if (num_workgroups < 0 || num_workgroups > 65535)
+    return fail(MLA_ERR_SHAPE, "%s: num_workgroups=%d outside [0, 65535]", fn, num_workgroups);
   if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_SHAPE, "%s: softmax_scale is not finite", fn);
   if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(block_table) || !aligned16(seq_lens) ||
       !aligned16(out) || !aligned16(lse))
     return fail(MLA_ERR_ALIGN, "%s: every tensor pointer must be 16-byte aligned", fn);
   const int32_t rows = q_len * num_heads;  // query rows per request
-  const size_t need = balanced_bytes_for(batch, rows, num_workgroups);
   if (!workspace) return fail(MLA_ERR_WORKSPACE, "%s: a workspace is required", fn);
   if (!aligned16(workspace)) return fail(MLA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
-  if (workspace_bytes < need)
-    return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
-  int rc = check_device();
+  // The workspace size depends on the workgroup count; 0 (one per compute unit) is resolved
+  // from the device first.
+  auto size_ok = [&]() -> int {
+    const size_t need = balanced_bytes_for(batch, rows, num_workgroups);
+    if (workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
+    return MLA_OK;
+  };
+  int rc = num_workgroups > 0 ? size_ok() : MLA_OK;
   if (rc != MLA_OK) return rc;
+  rc = check_device();
+  if (rc != MLA_OK) return rc;
+  if (num_workgroups == 0) {
+    num_workgroups = device_cus();
+    if (num_workgroups < 1) return fail(MLA_ERR_HIP, "%s: the device reports no compute units", fn);
+    rc = size_ok();
+    if (rc != MLA_OK) return rc;
+  }
 
   BalancedWorkspace ws = balanced_layout(workspace, batch, rows, num_workgroups);
   mla::DecodeParams p;
@@ -273,7 +302,9 @@ int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void
   p.cu = ws.cu;
   p.compact = 0;
   p.skip_empty = 0;
-  p.stream_rows = g_row_loads.load(std::memory_order_relaxed) == MLA_ROW_LOADS_STREAMING;
+  p.stream_rows = (flags & MLA_FLAG_CACHED_ROWS) == 0;
+  p.num_pages = num_pages;
+  p.check_status = check_status;
   static_assert(MLA_MAX_BALANCED_BATCH == mla::kMaxBalancedBatch, "batch limit of the balanced kernels");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t launched;
@@ -295,64 +326,69 @@ int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void
 extern "C" {
 
 size_t mla_decode_balanced_workspace_size(int32_t batch, int32_t num_heads, int32_t num_workgroups) {
-  if (batch < 1 || num_heads < 1 || num_workgroups < 1) return 0;
+  if (batch < 1 || num_heads < 1 || num_workgroups < 0) return 0;
+  if (num_workgroups == 0) {
+    if (check_device() != MLA_OK) return 0;
+    num_workgroups = device_cus();
+    if (num_workgroups < 1) return 0;
+  }
   return balanced_bytes_for(batch, num_heads, num_workgroups);
 }
 
 int mla_decode_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                              int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                              int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out, float* lse,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_balanced(kBf16, false, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                          num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
-                         stream);
+                         flags, check_status, stream);
 }
 
 int mla_decode_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                                 int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
                                 int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups,
-                                float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                                float* out, float* lse, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_balanced(kFp8, false, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                          num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
-                         stream);
+                         flags, check_status, stream);
 }
 
 int mla_decode_balanced_nope_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                                   int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
                                   int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups,
-                                  float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                                  float* out, float* lse, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_balanced(kNopeBf16, false, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                          num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
-                         stream);
+                         flags, check_status, stream);
 }
 
 int mla_decode_balanced_nope_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
                                      const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
                                      int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
                                      int32_t num_workgroups, float* out, float* lse, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+                                     size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_balanced(kNopeFp8, false, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                          num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
-                         stream);
+                         flags, check_status, stream);
 }
 
 int mla_decode_mtp_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                                  int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t q_len,
                                  int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups,
-                                 float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_balanced(kBf16, true, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                          num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
-                         stream);
+                         flags, check_status, stream);
 }
 
 int mla_decode_mtp_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
                                     const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
                                     int32_t batch, int32_t q_len, int32_t num_heads, int32_t page_size,
                                     float softmax_scale, int32_t num_workgroups, float* out, float* lse,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+                                    void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_balanced(kFp8, true, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                          num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace, workspace_bytes,
-                         stream);
+                         flags, check_status, stream);
 }
 
 size_t mla_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t num_splits) {
@@ -369,89 +405,89 @@ size_t mla_decode_rank_workspace_size(int32_t batch, int32_t num_heads, int32_t 
 int mla_decode_rank768_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                             int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                             int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kRank768Bf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
-                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_rank1792_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                              int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                              int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kRank1792Bf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
-                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                     int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                     int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kBf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
-                       page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                        int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                        int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kFp8, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
-                       page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_nope_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                          int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                          int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kNopeBf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
-                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_nope_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                             int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                             int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kNopeFp8, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
-                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_mtp_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                         int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t q_len,
                         int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_splits, float* out,
-                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                        float* lse, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kBf16, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
-                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_mtp_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                            int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t q_len,
                            int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_splits, float* out,
-                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                           float* lse, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kFp8, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
-                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_rank256_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                             int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                             int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kRank256Bf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
-                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_gla2_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                          int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                          int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kGla2Bf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
-                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_gla2_fp8_656(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
                             int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
                             int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kGla2Fp8, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
-                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
 }
 
 int mla_merge_lse_balanced(const void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_heads,
@@ -465,15 +501,22 @@ int mla_merge_lse_balanced(const void* workspace, size_t workspace_bytes, int32_
   // num_heads: the query rows of a request (q_len * num_heads after a verify-step decode)
   if (num_heads < 1 || num_heads > MLA_MAX_QUERY_ROWS)
     return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_QUERY_ROWS);
-  if (num_workgroups < 1 || num_workgroups > 65535)
-    return fail(MLA_ERR_SHAPE, "%s: num_workgroups=%d outside [1, 65535]", fn, num_workgroups);
+  if (num_workgroups < 0 || num_workgroups > 65535)
+    return fail(MLA_ERR_SHAPE, "%s: num_workgroups=%d outside [0, 65535]", fn, num_workgroups);
   if (!aligned16(workspace) || !aligned16(out) || !aligned16(lse))
     return fail(MLA_ERR_ALIGN, "%s: workspace, out and lse must be 16-byte aligned", fn);
-  const size_t need = balanced_bytes_for(batch, num_heads, num_workgroups);
-  if (workspace_bytes < need)
-    return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
+  if (num_workgroups > 0 && workspace_bytes < balanced_bytes_for(batch, num_heads, num_workgroups))
+    return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes,
+                balanced_bytes_for(batch, num_heads, num_workgroups));
   int rc = check_device();
   if (rc != MLA_OK) return rc;
+  if (num_workgroups == 0) {
+    num_workgroups = device_cus();
+    if (num_workgroups < 1) return fail(MLA_ERR_HIP, "%s: the device reports no compute units", fn);
+    const size_t need = balanced_bytes_for(batch, num_heads, num_workgroups);
+    if (workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
+  }
   BalancedWorkspace ws = balanced_layout(const_cast<void*>(workspace), batch, num_heads, num_workgroups);
   return hip_status(mla::launch_merge_flat(ws.part_out, ws.part_lse, ws.cu, batch, num_heads, num_workgroups, out,
                                            lse, static_cast<hipStream_t>(stream)),
@@ -547,8 +590,10 @@ int mla_cache_write(const void* latent, const void* k_pe, const int64_t* slot_ma
 
 int mla_gather_context(const void* kv_cache, int32_t cache_format, int64_t num_pages, int32_t page_size,
                        const int32_t* block_table, int64_t block_table_stride, const int64_t* cu_rows,
-                       const int32_t* seq_starts, int32_t batch, int64_t total_rows, void* out, void* stream) {
+                       const int32_t* seq_starts, int32_t batch, int64_t total_rows, void* out,
+                       int32_t* check_status, void* stream) {
   const char* fn = "mla_gather_context";
+  if (int rc0 = check_options(fn, 0, check_status)) return rc0;
   if (cache_format != MLA_CACHE_BF16_576 && cache_format != MLA_CACHE_FP8_656)
     return fail(MLA_ERR_SHAPE, "%s: cache_format=%d unknown", fn, cache_format);
   if (total_rows < 0) return fail(MLA_ERR_SHAPE, "%s: total_rows=%lld is negative", fn, (long long)total_rows);
@@ -570,8 +615,9 @@ int mla_gather_context(const void* kv_cache, int32_t cache_format, int64_t num_p
   int rc = check_device();
   if (rc != MLA_OK) return rc;
   return hip_status(mla::launch_gather(static_cast<const uint8_t*>(kv_cache), cache_format == MLA_CACHE_FP8_656,
-                                       block_table, block_table_stride, cu_rows, seq_starts, batch, page_size,
-                                       total_rows, static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)),
+                                       num_pages, block_table, block_table_stride, cu_rows, seq_starts, batch,
+                                       page_size, total_rows, static_cast<uint16_t*>(out), check_status,
+                                       static_cast<hipStream_t>(stream)),
                     fn);
 }
 
@@ -592,12 +638,33 @@ const char* mla_last_error_message(void) { return g_message; }
 
 int mla_abi_version(void) { return MLA_ABI_VERSION; }
 
-int mla_set_row_loads(int policy) {
-  if (policy != MLA_ROW_LOADS_STREAMING && policy != MLA_ROW_LOADS_CACHED) {
-    fail(MLA_ERR_SHAPE, "mla_set_row_loads: unknown policy %d", policy);
+int mla_checked_build(void) { return mla::kChecked ? 1 : 0; }
+
+int mla_check_preconditions_host(const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
+                                 int32_t batch, int32_t page_size, int64_t num_pages) {
+  const char* fn = "mla_check_preconditions_host";
+  if (!block_table || !seq_lens) {
+    fail(MLA_ERR_NULL, "%s: block_table and seq_lens are required", fn);
+    return -MLA_ERR_NULL;
+  }
+  if (batch < 0 || page_size < 1 || block_table_stride < 1 || num_pages < 0) {
+    fail(MLA_ERR_SHAPE, "%s: batch=%d, page_size=%d, block_table_stride=%lld, num_pages=%lld out of range", fn,
+         batch, page_size, (long long)block_table_stride, (long long)num_pages);
     return -MLA_ERR_SHAPE;
   }
-  return g_row_loads.exchange(policy, std::memory_order_relaxed);
+  int bits = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    int64_t L = seq_lens[b];
+    if (!mla::len_in_table(L, block_table_stride, page_size)) {
+      bits |= MLA_CHECK_SEQ_LEN;
+      L = L < 0 ? 0 : block_table_stride * page_size;
+    }
+    const int64_t pages = (L + page_size - 1) / page_size;  // the entries the context uses
+    const int32_t* row = block_table + (int64_t)b * block_table_stride;
+    for (int64_t j = 0; j < pages; ++j)
+      if (!mla::page_in_pool(row[j], num_pages)) bits |= MLA_CHECK_BLOCK_ID;
+  }
+  return bits;
 }
 
 }  // extern "C"

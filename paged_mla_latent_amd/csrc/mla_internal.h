@@ -28,8 +28,66 @@ struct DecodeParams {
   int compact;                 // per-request mode: map workgroups onto the non-empty partitions first
   int skip_empty;              // per-request split mode: empty partitions write no partial (the
                                // merge counts each request's non-empty partitions itself)
-  int stream_rows;             // non-temporal row loads (MLA_ROW_LOADS_STREAMING)
+  int stream_rows;             // non-temporal row loads (no MLA_FLAG_CACHED_ROWS)
+  int64_t num_pages;           // pages in the pool (checked build: block ids are tested against it)
+  int32_t* check_status;       // checked build: MLA_CHECK_* bits are ORed in here (may be NULL)
 };
+
+// ------------------------------------------------------------------------------------
+// Preconditions of the decodes (mla.h): every block id a context uses lies in [0, num_pages)
+// and 0 <= L <= block_table_stride * page_size.  The release build trusts them; the checked
+// build (-DMLA_CHECKED) tests them on the device before forming any address: an out-of-pool
+// block id reads page 0 instead and a length outside the range is clamped into it, so no read
+// leaves the cache or the block table, and the failed test's bit goes to *check_status.  The
+// host helper mla_check_preconditions_host applies the same predicates.
+// ------------------------------------------------------------------------------------
+#ifdef MLA_CHECKED
+constexpr bool kChecked = true;
+#else
+constexpr bool kChecked = false;
+#endif
+constexpr uint32_t kCheckBlockId = 1;  // MLA_CHECK_BLOCK_ID
+constexpr uint32_t kCheckSeqLen = 2;   // MLA_CHECK_SEQ_LEN
+
+__host__ __device__ __forceinline__ bool page_in_pool(int64_t page, int64_t num_pages) {
+  return page >= 0 && page < num_pages;
+}
+__host__ __device__ __forceinline__ bool len_in_table(int64_t L, int64_t bt_stride, int64_t page_size) {
+  return L >= 0 && L <= bt_stride * page_size;
+}
+
+// Checked build: page 0 in place of a block id outside the pool, and the bit in `bad`.
+__device__ __forceinline__ int32_t checked_page(int32_t page, int64_t num_pages, uint32_t& bad) {
+  if constexpr (kChecked) {
+    const bool ok = page_in_pool(page, num_pages);
+    bad |= ok ? 0u : kCheckBlockId;
+    return ok ? page : 0;
+  } else {
+    return page;
+  }
+}
+
+// Checked build: a context length clamped into [0, bt_stride * page_size], and the bit in `bad`.
+__device__ __forceinline__ int64_t checked_len(int64_t L, int64_t bt_stride, int64_t page_size, uint32_t& bad) {
+  if constexpr (kChecked) {
+    const bool ok = len_in_table(L, bt_stride, page_size);
+    bad |= ok ? 0u : kCheckSeqLen;
+    return L < 0 ? 0 : (ok ? L : bt_stride * page_size);
+  } else {
+    return L;
+  }
+}
+
+// Checked build: ORs the wave's `bad` bits into *status (one atomic per wave, only when a
+// test failed).  Called from wave-uniform control flow with every lane active.
+__device__ __forceinline__ void report_checks(uint32_t bad, int32_t* status) {
+  if constexpr (kChecked) {
+    uint32_t any = 0;
+    if (__builtin_amdgcn_ballot_w64((bad & kCheckBlockId) != 0)) any |= kCheckBlockId;
+    if (__builtin_amdgcn_ballot_w64((bad & kCheckSeqLen) != 0)) any |= kCheckSeqLen;
+    if (any != 0 && status != nullptr && (threadIdx.x & 63) == 0) atomicOr(status, (int32_t)any);
+  }
+}
 
 // Tokens [t0, t1) of one request.
 struct Range {
@@ -47,6 +105,15 @@ __device__ __forceinline__ Range partition(int64_t L, int ps, int S, int s, int6
   const int64_t p0 = min(P, (int64_t)s * c);
   const int64_t p1 = min(P, (int64_t)(s + 1) * c);
   return {min(L, p0 * ps), min(L, p1 * ps)};
+}
+
+// Non-empty partitions of a request of L tokens under the rule above: ceil(ceil(L / ps) / c),
+// kept within [0, S] so that a length past the block table (a broken precondition) can
+// never index a partial beyond the workspace.
+__device__ __forceinline__ int counted_partitions(int64_t L, int ps, int64_t W, int S) {
+  const int64_t c = max((W + S - 1) / S, (int64_t)1);
+  const int64_t n = ((max(L, (int64_t)0) + ps - 1) / ps + c - 1) / c;
+  return (int)min(n, (int64_t)S);
 }
 
 // Batch-balanced mode: at most kMaxBalancedBatch requests; each non-empty request adds
@@ -73,9 +140,10 @@ hipError_t launch_decode_flat_nope_bf16(const DecodeParams& p, int num_workgroup
 hipError_t launch_decode_flat_nope_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream);
 hipError_t launch_merge_flat(const float* part_out, const float* part_lse, const int64_t* cu, int batch, int heads,
                              int num_workgroups, float* out, float* lse, hipStream_t stream);
-hipError_t launch_gather(const uint8_t* cache, int fp8, const int32_t* block_table, int64_t bt_stride,
-                         const int64_t* cu_rows, const int32_t* seq_starts, int batch, int page_size,
-                         int64_t total_rows, uint16_t* out, hipStream_t stream);
+hipError_t launch_gather(const uint8_t* cache, int fp8, int64_t num_pages, const int32_t* block_table,
+                         int64_t bt_stride, const int64_t* cu_rows, const int32_t* seq_starts, int batch,
+                         int page_size, int64_t total_rows, uint16_t* out, int32_t* check_status,
+                         hipStream_t stream);
 hipError_t launch_merge(const float* part_out, const float* part_lse, int num_splits, int batch,
                         int heads, float* out, float* lse, hipStream_t stream, int width = kLatent);
 // Merge of the per-request split decode when empty partitions left no partial: request b's

@@ -71,9 +71,9 @@ def assert_rows_bitexact(w, pool_dev: torch.Tensor, pool_host: np.ndarray, slots
     assert bad.size == 0, f"{bad.size} rows differ, first slot {slots[bad[0]]}"
 
 
-def gpu_decode(w, pool: torch.Tensor, splits: int, q=None, nope=False, balanced=False):
+def gpu_decode(w, pool: torch.Tensor, splits: int, q=None, nope=False, balanced=False, flags=0):
     """Decode on the device; nope=True uses the NoPE-512 kernels with the first 512 q values;
-    balanced=True uses the batch-balanced kernels with `splits` workgroups."""
+    balanced=True uses the batch-balanced kernels with `splits` workgroups; flags per call."""
     q = w.q if q is None else q
     if nope:
         q = np.ascontiguousarray(q[:, :, :512])
@@ -85,14 +85,14 @@ def gpu_decode(w, pool: torch.Tensor, splits: int, q=None, nope=False, balanced=
             fn = mla.mla_decode_balanced_nope_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_nope_fp8_656
         else:
             fn = mla.mla_decode_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_fp8_656
-        out, lse = fn(q, pool, bt, lens, w.scale, num_workgroups=splits)
+        out, lse = fn(q, pool, bt, lens, w.scale, num_workgroups=splits, flags=flags)
         torch.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
     if nope:
         fn = mla.mla_decode_nope_bf16 if w.fmt == "bf16" else mla.mla_decode_nope_fp8_656
     else:
         fn = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
-    out, lse = fn(q, pool, bt, lens, w.scale, num_splits=splits)
+    out, lse = fn(q, pool, bt, lens, w.scale, num_splits=splits, flags=flags)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 

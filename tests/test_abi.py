@@ -48,7 +48,7 @@ def test_only_the_c_abi_is_exported():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
     names = [lib.mla_status_string(i).decode() for i in range(8)]
     assert names[:7] == ["MLA_OK", "MLA_ERR_NULL", "MLA_ERR_SHAPE", "MLA_ERR_ALIGN", "MLA_ERR_WORKSPACE",
                          "MLA_ERR_ARCH", "MLA_ERR_HIP"]
@@ -71,11 +71,11 @@ MIS = 0x1008
 
 def _decode(lib, fn="mla_decode_bf16", **kw):
     args = dict(q=P, kv=P, num_pages=10, bt=P, stride=4, lens=P, batch=2, heads=16, ps=64, scale=0.07,
-                splits=1, out=P, lse=P, ws=None, ws_bytes=0)
+                splits=1, out=P, lse=P, ws=None, ws_bytes=0, flags=0, cs=None)
     args.update(kw)
     rc = getattr(lib, fn)(args["q"], args["kv"], args["num_pages"], args["bt"], args["stride"], args["lens"],
                           args["batch"], args["heads"], args["ps"], args["scale"], args["splits"], args["out"],
-                          args["lse"], args["ws"], args["ws_bytes"], None)
+                          args["lse"], args["ws"], args["ws_bytes"], args["flags"], args["cs"], None)
     return rc, lib.mla_last_error_message().decode()
 
 
@@ -119,7 +119,7 @@ def test_balanced_rejects_null(lib, fn, field):
 @pytest.mark.parametrize("kw, word", [
     (dict(heads=0), "num_heads"), (dict(heads=17), "num_heads"), (dict(batch=0), "batch"),
     (dict(batch=1025), "batch"), (dict(ps=0), "page_size"), (dict(num_pages=0), "num_pages"),
-    (dict(stride=0), "block_table_stride"), (dict(splits=0), "num_workgroups"),
+    (dict(stride=0), "block_table_stride"), (dict(splits=-1), "num_workgroups"),
     (dict(splits=70000), "num_workgroups"), (dict(scale=float("nan")), "softmax_scale"),
     (dict(stride=1 << 40), "int32"),
 ])
@@ -134,6 +134,8 @@ def test_balanced_workspace(lib, fn):
     # prefix sums [3] padded to 256 bytes, then 2 + 512 - 1 slots of 16 x 513 floats
     assert need == (256 + 513 * 16 * 513 * 4 + 255) // 256 * 256
     assert mla.mla_decode_balanced_workspace_size(0, 16, 4) == 0
+    assert mla.mla_decode_balanced_workspace_size(2, 16, -1) == 0
+    # 0 workgroups = one per compute unit of the current device: no device here, so 0 bytes
     assert mla.mla_decode_balanced_workspace_size(2, 16, 0) == 0
     rc, msg = _decode(lib, fn, splits=512)
     assert rc == 4 and "workspace" in msg
@@ -154,7 +156,7 @@ def test_merge_balanced_validation(lib):
         rc, msg = call(**kw)
         assert rc == 1 and "NULL" in msg
     for kw, word in ((dict(batch=0), "batch"), (dict(batch=1025), "batch"), (dict(heads=65), "num_heads"),
-                     (dict(wgs=0), "num_workgroups"), (dict(wgs=65536), "num_workgroups")):
+                     (dict(wgs=-1), "num_workgroups"), (dict(wgs=65536), "num_workgroups")):
         rc, msg = call(**kw)
         assert rc == 2 and word in msg
     rc, msg = call(out=MIS)
@@ -171,11 +173,11 @@ def test_decode_rejects_misaligned(lib, field):
 
 def _mtp(lib, fn="mla_decode_mtp_bf16", **kw):
     args = dict(q=P, kv=P, num_pages=10, bt=P, stride=4, lens=P, batch=2, q_len=4, heads=16, ps=64, scale=0.07,
-                splits=1, out=P, lse=P, ws=None, ws_bytes=0)
+                splits=1, out=P, lse=P, ws=None, ws_bytes=0, flags=0, cs=None)
     args.update(kw)
     rc = getattr(lib, fn)(args["q"], args["kv"], args["num_pages"], args["bt"], args["stride"], args["lens"],
                           args["batch"], args["q_len"], args["heads"], args["ps"], args["scale"], args["splits"],
-                          args["out"], args["lse"], args["ws"], args["ws_bytes"], None)
+                          args["out"], args["lse"], args["ws"], args["ws_bytes"], args["flags"], args["cs"], None)
     return rc, lib.mla_last_error_message().decode()
 
 
@@ -196,7 +198,7 @@ MTP_BALANCED = ["mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656
 @pytest.mark.parametrize("kw, word", [
     (dict(q_len=0), "q_len"), (dict(q_len=17), "q_len"), (dict(q_len=5, heads=16), "q_len * num_heads"),
     (dict(heads=0), "num_heads"), (dict(heads=17, q_len=1), "num_heads"), (dict(batch=1025), "batch"),
-    (dict(splits=0), "num_workgroups"), (dict(splits=70000), "num_workgroups"),
+    (dict(splits=-1), "num_workgroups"), (dict(splits=70000), "num_workgroups"),
     (dict(scale=float("nan")), "softmax_scale"),
 ])
 def test_mtp_balanced_rejects_bad_shapes(lib, fn, kw, word):
@@ -308,7 +310,7 @@ def test_gather_validation(lib):
     def call(**kw):
         a = dict(ok, **kw)
         return f(a["kv"], a["fmt"], a["pages"], a["ps"], a["bt"], a["stride"], a["cu"], a["st"], a["batch"],
-                 a["total"], a["out"], None), lib.mla_last_error_message().decode()
+                 a["total"], a["out"], a.get("cs"), None), lib.mla_last_error_message().decode()
     for kw, rc, word in [(dict(fmt=5), 2, "cache_format"), (dict(total=-1), 2, "total_rows"),
                          (dict(total=1 << 40), 2, "total_rows"), (dict(batch=0), 2, "batch"),
                          (dict(pages=0), 2, "num_pages"), (dict(ps=0), 2, "page_size"), (dict(stride=0), 2, "stride"),
@@ -319,15 +321,84 @@ def test_gather_validation(lib):
     assert call(total=0, kv=None, out=None)[0] == 0  # nothing to gather: no device needed
 
 
-def test_row_load_policy(lib):
-    # host-side state only: returns the previous policy, refuses unknown ones
-    assert lib.mla_set_row_loads(mla.MLA_ROW_LOADS_CACHED) == mla.MLA_ROW_LOADS_STREAMING
-    assert lib.mla_set_row_loads(mla.MLA_ROW_LOADS_STREAMING) == mla.MLA_ROW_LOADS_CACHED
-    assert lib.mla_set_row_loads(7) == -2
-    assert "policy" in lib.mla_last_error_message().decode()
-    assert mla.mla_set_row_loads(mla.MLA_ROW_LOADS_STREAMING) == mla.MLA_ROW_LOADS_STREAMING
+ALL_DECODERS = DECODERS + ["mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656", "mla_decode_balanced_nope_bf16",
+                           "mla_decode_balanced_nope_fp8_656"]
+
+
+@pytest.mark.parametrize("fn", ALL_DECODERS)
+def test_decode_options_are_per_call(lib, fn):
+    ws = dict(ws=P, ws_bytes=1 << 30)
+    rc, msg = _decode(lib, fn, flags=2, **ws)
+    assert rc == 2 and "flag" in msg and fn in msg
+    rc, msg = _decode(lib, fn, flags=0x80000000, **ws)
+    assert rc == 2 and "flag" in msg
+    # the release build checks nothing, so it refuses a status word rather than ignore it
+    rc, msg = _decode(lib, fn, cs=P, **ws)
+    assert rc == 2 and "checked build" in msg
+    # valid options: only the missing device stops the call
+    assert _decode(lib, fn, flags=mla.MLA_FLAG_CACHED_ROWS, **ws)[0] == 5
+    assert _decode(lib, fn, flags=0, **ws)[0] == 5
+
+
+@pytest.mark.parametrize("fn", ["mla_decode_mtp_bf16", "mla_decode_mtp_balanced_fp8_656"])
+def test_mtp_options_are_per_call(lib, fn):
+    rc, msg = _mtp(lib, fn, flags=4, ws=P, ws_bytes=1 << 30)
+    assert rc == 2 and "flag" in msg
+    assert _mtp(lib, fn, flags=1, ws=P, ws_bytes=1 << 30)[0] == 5
+
+
+@pytest.fixture(scope="module")
+def checked_lib():
+    if not os.path.exists(mla.CHECKED_LIB_PATH):
+        pytest.fail("libmla_checked.so is not built (run __graft_entry__.build())")
+    return mla.library(checked=True)
+
+
+def test_checked_build_identifies_itself(lib, checked_lib):
+    assert lib.mla_checked_build() == 0 and checked_lib.mla_checked_build() == 1
+    assert checked_lib.mla_abi_version() == lib.mla_abi_version()
+
+
+def test_checked_build_exports_the_same_abi(checked_lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.CHECKED_LIB_PATH], capture_output=True, text=True).stdout
+    assert sorted(l.split()[-1] for l in out.splitlines() if " T " in l) == sorted(mla.EXPORTED)
+
+
+@pytest.mark.parametrize("fn", ["mla_decode_bf16", "mla_decode_balanced_fp8_656", "mla_decode_rank768_bf16"])
+def test_checked_build_takes_a_status_word(checked_lib, fn):
+    ws = dict(ws=P, ws_bytes=1 << 30)
+    assert _decode(checked_lib, fn, cs=P, **ws)[0] == 5  # accepted; no device here
+    rc, msg = _decode(checked_lib, fn, cs=P + 2, **ws)
+    assert rc == 3 and "check_status" in msg
+    rc, msg = _decode(checked_lib, fn, flags=8, cs=P, **ws)
+    assert rc == 2 and "flag" in msg
+
+
+def test_gather_status_word(lib, checked_lib):
+    a = (P, 0, 10, 16, P, 4, P, None, 2, 100, P)
+    assert lib.mla_gather_context(*a, P, None) == 2 and "checked build" in lib.mla_last_error_message().decode()
+    assert checked_lib.mla_gather_context(*a, P, None) == 5
+
+
+def test_host_precondition_check():
+    """The predicates the checked kernels apply, on host arrays: block ids a context uses in
+    [0, num_pages), lengths in [0, stride * page_size]; entries past a context are not read."""
+    import numpy as np
+    f = mla.mla_check_preconditions_host
+    bt = np.array([[3, 1, -1, -1], [0, 2, 4, 5]], np.int32)
+    assert f(bt, [20, 64], page_size=16, num_pages=6) == 0          # -1 tails past the context
+    assert f(bt, [33, 64], page_size=16, num_pages=6) == mla.MLA_CHECK_BLOCK_ID  # token 32 uses -1
+    assert f(bt, [0, 64], page_size=16, num_pages=5) == mla.MLA_CHECK_BLOCK_ID   # page 5 of 5
+    assert f(bt, [0, 48], page_size=16, num_pages=5) == 0            # ... not used at 48 tokens
+    assert f(bt, [0, 65], page_size=16, num_pages=6) == mla.MLA_CHECK_SEQ_LEN    # past the table
+    assert f(bt, [-1, 0], page_size=16, num_pages=6) == mla.MLA_CHECK_SEQ_LEN
+    assert f(bt, [40, 65], page_size=16, num_pages=6) == mla.MLA_CHECK_SEQ_LEN | mla.MLA_CHECK_BLOCK_ID
+    wrap = np.array([[58254, 70312]], np.int32)                      # high pages of a 70,313-page pool
+    assert f(wrap, [128], page_size=64, num_pages=70313) == 0
+    assert f(wrap, [128], page_size=64, num_pages=70312) == mla.MLA_CHECK_BLOCK_ID
     with pytest.raises(mla.MlaError):
-        mla.mla_set_row_loads(-1)
+        f(bt, [1, 1], page_size=0, num_pages=6)
 
 
 def test_error_message_is_thread_local(lib):

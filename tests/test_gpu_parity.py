@@ -152,6 +152,121 @@ def test_cache_write_bitexact(fmt):
     assert bad.size == 0, f"{bad.size} rows differ; first slot {bad[0]}"
 
 
+def _fp8_pool_write(latent, k_pe, rows):
+    pool = torch.full((rows, 656), 0xAB, dtype=torch.uint8, device="cuda").view(rows, 1, 656)
+    mla.mla_cache_write(bf16_dev(latent), bf16_dev(k_pe), torch.arange(rows, dtype=torch.int64, device="cuda"), pool,
+                        mla.MLA_CACHE_FP8_656)
+    torch.cuda.synchronize()
+    return pool.view(rows, 656).cpu().numpy()
+
+
+def _exhaustive_blocks(values, block_max):
+    """Blocks of 128 bf16 patterns: 127 of `values` each plus one `block_max` (the block's absmax)."""
+    per = 127
+    n = -(-values.size // per)
+    vals = np.concatenate([values, np.zeros(n * per - values.size, np.uint16)]).reshape(n, per)
+    blocks = np.concatenate([np.full((n, 1), block_max, np.uint16), vals], axis=1)
+    blocks = np.concatenate([blocks, np.zeros((-n % 4, 128), np.uint16)])  # whole rows of four blocks
+    return blocks.reshape(-1, 512)
+
+
+@pytest.mark.parametrize("block_max", [0x43E0, 0x447A, 0x4040])  # 448 (s = 1), 1000, 3 (s = 3/448)
+def test_cache_write_fp8_exhaustive_bf16(block_max):
+    """Every finite bf16 value x with |x| <= the block max, in blocks whose absmax is 448 (scale
+    1), 1000 or 3 (scales 1000/448 and 3/448), quantised by mla_cache_write: bytes equal the
+    oracle's packing bit for bit (the hardware e4m3 conversion's rounding, ties and subnormals)."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mag = workloads.bf16_as_f32(pats)
+    lim = workloads.bf16_as_f32(np.array([block_max], np.uint16))[0]
+    values = pats[np.isfinite(mag) & (np.abs(mag) <= lim)]
+    latent = _exhaustive_blocks(values, block_max)
+    say(f"exhaustive fp8 quantiser: {values.size} values, block max {lim}, {latent.shape[0]} rows")
+    k_pe = np.zeros((latent.shape[0], 64), np.uint16)
+    got = _fp8_pool_write(latent, k_pe, latent.shape[0])
+    want = oracle.pack_rows(latent, k_pe, "fp8")
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first row {bad[0]}"
+
+
+def test_cache_write_fp8_nonfinite_blocks_and_decode():
+    """A latent block holding a NaN or an infinity is stored as the NaN block (scale 0x7FC00000, codes
+    0x7F), bit-exact against the oracle; a request reading such a row decodes to NaN, the others
+    are unaffected."""
+    rng = np.random.default_rng(12)
+    T = 64
+    lat = workloads.bf16_bits(rng.standard_normal((T, 512)).astype(np.float32))
+    specials = np.array([0x7FC0, 0x7F80, 0xFF80, 0xFFC1, 0x7F81], np.uint16)  # NaN, +inf, -inf, NaNs
+    for i, pat in enumerate(specials):
+        lat[i, 130 * i % 512] = pat
+    k_pe = workloads.bf16_bits(rng.standard_normal((T, 64)).astype(np.float32))
+    got = _fp8_pool_write(lat, k_pe, T)
+    want = oracle.pack_rows(lat, k_pe, "fp8")
+    assert np.array_equal(got, want)
+    blk = (130 * np.arange(specials.size) % 512) // 128
+    for i in range(specials.size):
+        assert got[i, 512 + 4 * blk[i]:516 + 4 * blk[i]].view("<u4")[0] == 0x7FC00000
+    # decode: request 0 reads row 2 (an infinity), request 1 only finite rows
+    w = workloads.make_workload("nanrow", seq_lens=[40, 40], heads=16, page_size=16, num_pages=6, fmt="fp8", seed=3)
+    lat_w = w.latent.copy()
+    lat_w[np.searchsorted(w.slots, oracle.slot_of(w.block_table, 0, 5, 16)), 300] = 0x7F80
+    pd = device_pool(w, latent=lat_w)
+    out, lse = gpu_decode(w, pd, 1)
+    assert np.isnan(out[0]).all() and np.isnan(lse[0]).all()
+    ph = host_pool(w, latent=lat_w)
+    ro, rl = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, "fp8")
+    assert np.isnan(ro[0]).all()
+    assert_parity(w, out, lse, ro, rl, requests=[1], what="finite request beside a NaN row")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_compact_dispatch_keeps_every_partial(fmt):
+    """batch x splits above the compute units with the partials kept (no merge here): the
+    compacted dispatch must still write every partition's partial, the empty ones as (0, -inf);
+    the workspace is poisoned first, and the caller's own merge is checked against the oracle."""
+    lens = [0, 1, 15, 1000, 0, 2500, 333, 17, 0]
+    ps = 16
+    pages = sum(-(-L // ps) for L in lens) + 3
+    w = workloads.make_workload("compact_kept", seq_lens=lens, heads=16, page_size=ps, num_pages=pages, fmt=fmt,
+                                seed=14)
+    S = 40  # 9 x 40 = 360 workgroups > 256 compute units
+    pd, ph = device_pool(w), host_pool(w)
+    need = mla.mla_decode_workspace_size(w.batch, w.heads, S)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
+    fn = mla.mla_decode_bf16 if fmt == "bf16" else mla.mla_decode_fp8_656
+    po, pl = fn(bf16_dev(w.q), pd, torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda(),
+                w.scale, num_splits=S, workspace=ws, partials_only=True)
+    out, lse = mla.mla_merge_lse(po, pl)
+    torch.cuda.synchronize()
+    pl_h = pl.cpu().numpy()
+    assert not np.isnan(pl_h).any(), "a partition left its partial unwritten"
+    # the empty partitions' partials are exactly (+0, -inf)
+    W = w.block_table.shape[1]
+    c = -(-W // S)
+    for b, L in enumerate(lens):
+        n = -(-(-(-L // ps)) // c)
+        assert np.isneginf(pl_h[n:, b]).all()
+        assert (po[n:, b].cpu().numpy() == 0).all()
+    ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, fmt)
+    assert_parity(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l,
+                  what=f"compact kept {fmt}")
+
+
+def test_balanced_default_workgroups_is_one_per_compute_unit():
+    w = workloads.make_workload("bal0", seq_lens=[3000, 17, 0, 900], heads=16, page_size=64, num_pages=70, seed=15)
+    pd = device_pool(w)
+    q, bt, lens = bf16_dev(w.q), torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert mla.mla_decode_balanced_workspace_size(w.batch, w.heads, 0) == \
+        mla.mla_decode_balanced_workspace_size(w.batch, w.heads, cus)
+    a = mla.mla_decode_balanced_bf16(q, pd, bt, lens, w.scale, num_workgroups=0)
+    b = mla.mla_decode_balanced_bf16(q, pd, bt, lens, w.scale, num_workgroups=cus)
+    ws = mla.mla_decode_balanced_bf16(q, pd, bt, lens, w.scale, num_workgroups=0, partials_only=True)
+    c = mla.mla_merge_lse_balanced(ws, w.batch, w.heads, 0)
+    torch.cuda.synchronize()
+    for x in (b, c):
+        assert torch.equal(a[0], x[0]) and torch.equal(a[1], x[1])
+
+
 # ------------------------------------------------------------------------------ merge
 def test_merge_kernel_matches_oracle():
     rng = np.random.default_rng(4)
@@ -389,17 +504,17 @@ def test_full_size_workloads_sampled(name):
 
 
 # ---------------------------------------------------------------- multi-token verify
-def _gpu_mtp(w, pool, q_bits, splits, balanced=False):
+def _gpu_mtp(w, pool, q_bits, splits, balanced=False, flags=0):
     """Per-request split verify step (num_splits = splits), or the batch-balanced one with
     splits workgroups."""
     bt = torch.from_numpy(w.block_table).cuda()
     lens = torch.from_numpy(w.seq_lens).cuda()
     if balanced:
         fn = mla.mla_decode_mtp_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_balanced_fp8_656
-        out, lse = fn(bf16_dev(q_bits), pool, bt, lens, w.scale, num_workgroups=splits)
+        out, lse = fn(bf16_dev(q_bits), pool, bt, lens, w.scale, num_workgroups=splits, flags=flags)
     else:
         fn = mla.mla_decode_mtp_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_fp8_656
-        out, lse = fn(bf16_dev(q_bits), pool, bt, lens, w.scale, num_splits=splits)
+        out, lse = fn(bf16_dev(q_bits), pool, bt, lens, w.scale, num_splits=splits, flags=flags)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -498,17 +613,14 @@ def test_row_load_policies_agree(fmt):
     q4 = workloads.bf16_bits(np.random.default_rng(29).standard_normal((w.batch, 4, 16, 576)).astype(np.float32))
     pd, ph = device_pool(w), host_pool(w)
     runs = {}
-    try:
-        for policy in (mla.MLA_ROW_LOADS_STREAMING, mla.MLA_ROW_LOADS_CACHED):
-            mla.mla_set_row_loads(policy)
-            runs[policy] = [gpu_decode(w, pd, 4), gpu_decode(w, pd, 64, balanced=True),
-                            gpu_decode(w, pd, 4, nope=True), _gpu_mtp(w, pd, q4, 4), _gpu_mtp(w, pd, q4, 64, True)]
-    finally:
-        mla.mla_set_row_loads(mla.MLA_ROW_LOADS_STREAMING)
-    for a, b in zip(runs[mla.MLA_ROW_LOADS_STREAMING], runs[mla.MLA_ROW_LOADS_CACHED]):
+    for flags in (0, mla.MLA_FLAG_CACHED_ROWS):  # per call: streaming, then cached row loads
+        runs[flags] = [gpu_decode(w, pd, 4, flags=flags), gpu_decode(w, pd, 64, balanced=True, flags=flags),
+                       gpu_decode(w, pd, 4, nope=True, flags=flags), _gpu_mtp(w, pd, q4, 4, flags=flags),
+                       _gpu_mtp(w, pd, q4, 64, True, flags=flags)]
+    for a, b in zip(runs[0], runs[mla.MLA_FLAG_CACHED_ROWS]):
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt)
-    assert_parity(w, *runs[mla.MLA_ROW_LOADS_STREAMING][0], ref_o, ref_l, what="streaming loads S=4")
+    assert_parity(w, *runs[0][0], ref_o, ref_l, what="streaming loads S=4")
 
 
 def test_mtp_single_query_is_plain_decode():

@@ -7,7 +7,8 @@ numerics.e4m3_decode     OCP E4M3 anchor values (golden); torch float8_e4m3fn, a
 numerics.e4m3_encode     torch's float8_e4m3fn cast (round to nearest even) over every
                          bf16 value in [-464, 464] and 10^6 random fp32 values; round
                          trip on all finite codes; saturation above 448
-numerics.quantize_block  hand-worked 656-byte row (golden); power-of-two round trip
+numerics.quantize_block  hand-worked 656-byte row (golden); power-of-two round trip;
+                         every NaN / infinity pattern gives the NaN block (stated rule)
 mla.pack_rows/cache_write  hand-worked 656-byte row (golden); bf16 row = latent ++ k_pe
 mla.slot_of/gather_rows  Python-int gather vs int64-array gather; page-move invariance
 mla.element_offset*      wrap slot 3,728,270 printed on the sabi-mla-vllm page (golden)
@@ -133,6 +134,30 @@ def test_quantize_power_of_two_round_trip():
         assert (s == np.float32(2.0**k)).all()
         back = oracle.e4m3_decode(q).reshape(5, 4, 128) * s[..., None]
         assert np.array_equal(back.reshape(5, 512), x.astype(np.float64))
+
+
+def test_quantize_nonfinite_blocks_store_nan():
+    """A 128-value block holding a NaN or an infinity stores the NaN scale 0x7FC00000 and 128
+    codes 0x7F; the other blocks of the row quantise as if alone; the row decodes to NaN there."""
+    rng = np.random.default_rng(11)
+    x = workloads.bf16_bits(rng.standard_normal((1, 512)).astype(np.float32))
+    specials = [p for p in range(1 << 16) if (p & 0x7F80) == 0x7F80]  # every NaN and infinity pattern
+    assert len(specials) == 256
+    for pat in specials:
+        row = x.copy()
+        row[0, 5] = pat          # block 0
+        row[0, 256 + pat % 128] = pat  # block 2
+        s, q = oracle.quantize_block128(row)
+        sb = s.view(np.uint32)[0]
+        assert sb[0] == 0x7FC00000 and sb[2] == 0x7FC00000
+        assert (q[0, :128] == 0x7F).all() and (q[0, 256:384] == 0x7F).all()
+        s1, q1 = oracle.quantize_block128(np.tile(x[:, 128:256], (1, 4)))
+        assert s[0, 1] == s1[0, 0] and np.array_equal(q[0, 128:256], q1[0, :128])
+    vals = omla.rows_from_bytes(oracle.pack_rows(row, np.zeros((1, 64), np.uint16), "fp8"), "fp8")
+    assert np.isnan(vals[0, :128]).all() and np.isfinite(vals[0, 128:256]).all()
+    # finite blocks beside it: unchanged whatever the other blocks hold
+    s0, q0 = oracle.quantize_block128(x)
+    assert s[0, 1] == s0[0, 1] and np.array_equal(q[0, 128:256], q0[0, 128:256])
 
 
 # ----------------------------------------------------------------------- cache rows
