@@ -143,6 +143,26 @@ MLA_API int mla_decode_bf16(const void* q, const void* kv_cache, int64_t num_pag
                     float* out, float* lse, void* workspace, size_t workspace_bytes,
                     uint32_t flags, int32_t* check_status, void* stream);
 
+/* mla_decode_bf16 for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments, kernels and
+ * results as mla_decode_bf16 without workspace / workspace_bytes.  The split partials go to a
+ * scratch array of MLA_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on each device it
+ * runs on until the process ends (part of the loaded code object; nothing is allocated per call).
+ * num_splits is limited by it: mla_decode_workspace_size(batch, num_heads, num_splits) must not
+ * exceed MLA_NOALLOC_SCRATCH_BYTES (MLA_ERR_WORKSPACE otherwise; the long-context batch of 4
+ * requests x 16 heads at 64 splits needs 8.4 MB).  out and lse are required (the partials are
+ * not handed out).  Every call on a device shares that device's scratch: calls that overlap on
+ * one GPU (different streams, or threads without ordering) race and must be serialised by the
+ * caller.  Nothing in the scratch needs to start at any value.  No hipMalloc, hipFree or other
+ * allocating call is made. */
+enum { MLA_NOALLOC_SCRATCH_BYTES = 16 << 20 };
+MLA_API int mla_decode_bf16_noalloc(const void* q, const void* kv_cache, int64_t num_pages,
+                                    const int32_t* block_table, int64_t block_table_stride,
+                                    const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                    int32_t page_size, float softmax_scale, int32_t num_splits,
+                                    float* out, float* lse, uint32_t flags, int32_t* check_status,
+                                    void* stream);
+
 /* Decode over an fp8 cache (MLA_CACHE_FP8_656).  Same arguments and results as
  * mla_decode_bf16; kv_cache is uint8 [num_pages][page_size][656], each row
  * [0,512) OCP e4m3fn codes, [512,528) four little-endian fp32 scales (scale k

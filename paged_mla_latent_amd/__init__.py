@@ -66,8 +66,9 @@ EXPORTED = (
     "mla_merge_lse_balanced", "mla_decode_rank_workspace_size", "mla_decode_rank768_bf16",
     "mla_decode_rank1792_bf16", "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656",
     "mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656", "mla_checked_build",
-    "mla_check_preconditions_host",
+    "mla_check_preconditions_host", "mla_decode_bf16_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class MlaError(RuntimeError):
@@ -128,6 +129,9 @@ def library(checked: bool = False) -> ctypes.CDLL:
     lib.mla_last_error_message.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
     lib.mla_abi_version.restype = c_int
+    lib.mla_decode_bf16_noalloc.argtypes = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp,
+                                            c_u32, vp, vp]
+    lib.mla_decode_bf16_noalloc.restype = c_int
     lib.mla_checked_build.argtypes = []
     lib.mla_checked_build.restype = c_int
     lib.mla_check_preconditions_host.argtypes = [vp, c_i64, vp, c_i32, c_i32, c_i64]
@@ -248,6 +252,34 @@ def mla_decode_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_split
     return _decode("mla_decode_bf16", torch.bfloat16, ROW, q, kv_cache, block_table, seq_lens,
                    softmax_scale, num_splits, out, lse, workspace, partials_only,
                    flags=flags, check_status=check_status)
+
+
+def mla_decode_bf16_noalloc(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,
+                            flags=0, check_status=None):
+    """mla_decode_bf16 without a workspace: the split partials go to the library's 16 MiB
+    per-device scratch (for callers that cannot allocate; calls on one device must not overlap).
+    out / lse are allocated here when not given (the library itself allocates nothing)."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    lib, status_ptr = _options(check_status, dev)
+    _need(kv_cache, "kv_cache", torch.bfloat16, 3, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, H, D = q.shape
+    if D != ROW or kv_cache.shape[2] != ROW:
+        raise ValueError("q and kv_cache rows must have 576 values")
+    if out is None:
+        out = torch.empty((B, H, LATENT), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    status = lib.mla_decode_bf16_noalloc(
+        q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1],
+        seq_lens.data_ptr(), B, H, kv_cache.shape[1], float(softmax_scale), int(num_splits), out.data_ptr(),
+        lse.data_ptr(), int(flags), status_ptr, _stream(dev))
+    _check("mla_decode_bf16_noalloc", status, lib)
+    return out, lse
 
 
 def mla_decode_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "mla.h"
 #include "mla_internal.h"
@@ -85,6 +86,39 @@ size_t workspace_bytes_for(int64_t batch, int64_t heads, int64_t splits, int64_t
   return (bytes + 255) & ~(size_t)255;
 }
 
+// Scratch of mla_decode_bf16_noalloc: the split partials of one call, one copy per device,
+// held until the process ends.  Its name is a host-side stand-in, never a device address:
+// host code uses only the per-device address from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static_assert(kNoAllocScratchBytes == (size_t)MLA_NOALLOC_SCRATCH_BYTES, "scratch size in mla.h");
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mutex;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch, looked up once per device with that device
+// current.  No allocation: the array is part of the loaded code object.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(MLA_ERR_ARCH, "mla_decode_bf16_noalloc: no usable HIP device (%s)", hipGetErrorString(e));
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !ptr)
+        return fail(MLA_ERR_HIP, "mla_decode_bf16_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return MLA_OK;
+}
+
 // Kinds of decode: row format and whether the rope part takes part in the scores.
 enum DecodeKind {
   kBf16 = 0, kFp8 = 1, kNopeBf16 = 2, kNopeFp8 = 3, kRank256Bf16 = 4, kGla2Bf16 = 5, kGla2Fp8 = 6,
@@ -95,7 +129,7 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
                   const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
                   int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
                   int32_t num_splits, float* out, float* lse, void* workspace, size_t workspace_bytes,
-                  uint32_t flags, int32_t* check_status, void* stream) {
+                  uint32_t flags, int32_t* check_status, void* stream, bool use_scratch = false) {
   static const char* const kNames[] = {"mla_decode_bf16",         "mla_decode_fp8_656",
                                        "mla_decode_nope_bf16",    "mla_decode_nope_fp8_656",
                                        "mla_decode_rank256_bf16", "mla_decode_gla2_bf16",
@@ -107,14 +141,16 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
                         : kind == kRank768Bf16        ? 768
                         : kind == kRank1792Bf16       ? 1792
                                                       : MLA_LATENT;
-  const char* fn = q_len == 1 ? kNames[kind] : (kind == kBf16 ? "mla_decode_mtp_bf16" : "mla_decode_mtp_fp8_656");
+  const char* fn = use_scratch ? "mla_decode_bf16_noalloc"
+                   : q_len == 1  ? kNames[kind]
+                                 : (kind == kBf16 ? "mla_decode_mtp_bf16" : "mla_decode_mtp_fp8_656");
   if (int rc0 = check_options(fn, flags, check_status)) return rc0;
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
   if (!seq_lens) return fail(MLA_ERR_NULL, "%s: seq_lens is NULL", fn);
   // out == lse == NULL with num_splits > 1 leaves the partials in the workspace (no merge).
-  const bool partials_only = !out && !lse && num_splits > 1;
+  const bool partials_only = !out && !lse && num_splits > 1 && !use_scratch;
   if (!out && !partials_only) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
   if (!lse && !partials_only) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
   if (batch < 1 || batch > 65535) return fail(MLA_ERR_SHAPE, "%s: batch=%d outside [1, 65535]", fn, batch);
@@ -140,6 +176,20 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
     return fail(MLA_ERR_ALIGN, "%s: every tensor pointer must be 16-byte aligned", fn);
   float* part_out = nullptr;
   float* part_lse = nullptr;
+  if (num_splits > 1 && use_scratch) {
+    // the library's per-device scratch stands in for the workspace
+    const size_t need = workspace_bytes_for(batch, num_heads, num_splits);
+    if (need > kNoAllocScratchBytes)
+      return fail(MLA_ERR_WORKSPACE,
+                  "%s: %d splits x %d requests x %d heads need %zu bytes of partials, more than the %zu-byte "
+                  "scratch; use mla_decode_bf16 with a workspace",
+                  fn, num_splits, batch, num_heads, need, kNoAllocScratchBytes);
+    int rc = check_device();
+    if (rc != MLA_OK) return rc;
+    rc = scratch_address(&workspace);
+    if (rc != MLA_OK) return rc;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (num_splits > 1) {
     // the 256-wide outputs keep the 512-wide workspace size of the first ABI version
     const size_t need = workspace_bytes_for(batch, (int64_t)q_len * num_heads, num_splits, wide ? out_width : MLA_LATENT);
@@ -324,6 +374,15 @@ int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void
 }  // namespace
 
 extern "C" {
+
+int mla_decode_bf16_noalloc(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                            int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                            int32_t page_size, float softmax_scale, int32_t num_splits, float* out, float* lse,
+                            uint32_t flags, int32_t* check_status, void* stream) {
+  return decode_common(kBf16, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch, num_heads,
+                       page_size, softmax_scale, num_splits, out, lse, nullptr, 0, flags, check_status, stream,
+                       /*use_scratch=*/true);
+}
 
 size_t mla_decode_balanced_workspace_size(int32_t batch, int32_t num_heads, int32_t num_workgroups) {
   if (batch < 1 || num_heads < 1 || num_workgroups < 0) return 0;

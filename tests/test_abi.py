@@ -401,6 +401,32 @@ def test_host_precondition_check():
         f(bt, [1, 1], page_size=0, num_pages=6)
 
 
+def _noalloc(lib, **kw):
+    a = dict(q=P, kv=P, num_pages=10, bt=P, stride=4, lens=P, batch=4, heads=16, ps=64, scale=0.07, splits=64,
+             out=P, lse=P, flags=0, cs=None)
+    a.update(kw)
+    rc = lib.mla_decode_bf16_noalloc(a["q"], a["kv"], a["num_pages"], a["bt"], a["stride"], a["lens"], a["batch"],
+                                     a["heads"], a["ps"], a["scale"], a["splits"], a["out"], a["lse"], a["flags"],
+                                     a["cs"], None)
+    return rc, lib.mla_last_error_message().decode()
+
+
+def test_noalloc_validation(lib):
+    assert mla.NOALLOC_SCRATCH_BYTES == 16 << 20
+    # the long-context shape (4 requests x 16 heads x 64 splits) fits the scratch: only the device is missing
+    assert mla.mla_decode_workspace_size(4, 16, 64) <= mla.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib)[0] == 5
+    rc, msg = _noalloc(lib, splits=200)  # 200 x 4 x 16 partials: 26 MB
+    assert rc == 4 and "scratch" in msg and "mla_decode_bf16_noalloc" in msg
+    for kw in (dict(out=None), dict(lse=None)):
+        rc, msg = _noalloc(lib, **kw)
+        assert rc == 1 and "mla_decode_bf16_noalloc" in msg
+    rc, msg = _noalloc(lib, heads=17)
+    assert rc == 2 and "num_heads" in msg and "mla_decode_bf16_noalloc" in msg
+    rc, msg = _noalloc(lib, flags=2)
+    assert rc == 2 and "flag" in msg
+
+
 def test_error_message_is_thread_local(lib):
     import threading
     _decode(lib, heads=99)
