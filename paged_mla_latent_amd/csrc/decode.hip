@@ -847,6 +847,450 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   report_checks(bad, p.check_status);
 }
 
+// ------------------------------------------------------------------------------------
+// Verify steps with 33..64 query rows (q_len x heads, four 16-row groups): the scores are
+// split by row group and the PV by output columns.
+//
+// Each wave still streams its own tiles (wave w loads tile 4i + w of step i) and scores the
+// step's four tiles for its row group w (QK reads every tile once per row group: the A operand
+// of a 16-row group).  The PV is split the other way: wave w accumulates output columns
+// [128w, 128w + 128) of all 64 query rows (4 row groups x 8 column tiles = 32 accumulators, the
+// same 128 registers as one row group x 512 columns), so every column tile of a tile is read
+// from LDS once per step instead of once per row group (PV LDS reads per tile: 16 KB instead
+// of 64 KB).  The probabilities reach the other waves through LDS: bf16 rows exchange them as
+// the bf16 pairs the PV MFMA consumes; fp8 rows exchange them in fp32, because wave w folds the
+// scale of its own 128-value block (block w) into P before the one bf16 rounding, and reads
+// that block's codes straight from the raw 656-byte tile (no widened copy in LDS).  A softmax
+// rescale of row group r (rare: the running maximum moves in steps of at least 2^8) travels the
+// same way: its owner wave publishes alpha for its rows and a flag, and every wave scales its
+// accumulators of that row group before adding the step.
+//
+// Per step: each wave waits for its own tile, a barrier makes the four tiles (and the end of
+// the previous step) visible, the next tiles are requested, the owner waves score, rescale and
+// publish P, a second barrier, then every wave reads the four row groups' P and accumulates its
+// columns.  The owner of row group r keeps its running maximum and sum; the epilogue publishes
+// them and every wave writes its columns of every row.
+// ------------------------------------------------------------------------------------
+template <class Fmt>
+struct ColSplit {
+  static constexpr bool kFp8 = std::is_same<Fmt, Fp8Rows<64>>::value;
+  static_assert(kFp8 || std::is_same<Fmt, Bf16Rows<512, 64>>::value, "576-value rows");
+  static constexpr int kNB = kFp8 ? 3 : 2;  // tiles per wave resident: 3 x 4 x 11 KB / 2 x 4 x 18 KB
+  static constexpr int kTiles = kWaves * kNB * Fmt::kTileBytes;
+  static constexpr int kPids = kWaves * kNB * 256;
+  static constexpr int kXslots = Fmt::kFlatTile ? kWaves * (kNB - 1) * 256 : 0;
+  // P of a step: bf16, [row group][tile pair][lane] u32x4 (8 KB); fp8, fp32 [row group][tile][lane]
+  // f32x4 (16 KB).
+  static constexpr int kPex = kFp8 ? 4 * 4 * 64 * 16 : 4 * 2 * 64 * 16;
+  static constexpr int kAlpha = 4 * 16 * 4 + 16;  // alpha [row group][row], then 4 flags
+  // fp8: the step's block scales transposed, [2 steps][tile][block][token] fp32
+  static constexpr int kScales = kFp8 ? 2 * 4 * 4 * 16 * 4 : 0;
+  static constexpr int kBytes = kTiles + kPids + kXslots + kPex + kAlpha + kScales;
+  static_assert(kBytes <= 160 * 1024, "column-split verify step fits in the LDS");
+};
+
+// Scores of one 16-row group over four tiles: raw[v] = A(tile v) x q^T, as Fmt::qk computes
+// them, with the four tiles' MFMA chains interleaved K-step by K-step.
+template <class Fmt>
+__device__ __forceinline__ void score_tiles(const uint8_t* t0, const uint8_t* t1, const uint8_t* t2,
+                                            const uint8_t* t3, const uint8_t* sct, int m, int g, const u32x4* qf,
+                                            f32x4 (&raw)[4]) {
+  const uint8_t* const tile[4] = {t0, t1, t2, t3};
+  if constexpr (std::is_same<Fmt, Fp8Rows<64>>::value) {
+    // K-step j: codes 32j + 8g .. + 8 of token m (chunk 2j + (g >> 1), half g & 1), widened
+    // exactly; per 128-value block k the partial score is scaled by that block's scale (fp32),
+    // read for the lane's tokens 4g .. 4g + 3 from the transposed table sct ([tile][block][token]).
+#pragma unroll
+    for (int v = 0; v < 4; ++v) raw[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f32x4 sk[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sk[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * k + jj;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u32x2 codes = *(const u32x2*)(tile[v] + Fmt::pos(m, 2 * j + (g >> 1)) + 8 * (g & 1));
+          sk[v] = mfma_16x16x32(Fmt::widen8(codes), qf[j], sk[v]);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const f32x4 sc = *(const f32x4*)(sct + (16 * (4 * v + k) + 4 * g) * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) raw[v][r] += sc[r] * sk[v][r];
+      }
+    }
+    f32x4 sr[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sr[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jr = 0; jr < 2; ++jr)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        sr[v] = mfma_16x16x32(*(const u32x4*)(tile[v] + Fmt::pos(m, 33 + 4 * jr + g)), qf[16 + jr], sr[v]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) raw[v] += sr[v];
+    // 64 code reads + 16 scale reads + 8 rope reads, 72 MFMAs: kAhead reads ahead (see below)
+    constexpr int kAhead = 8;
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int n = 0; n < 72; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  } else {
+    // line layout: K-step j reads chunk 4 (j & 1) + g of token m, plus 128 (j >> 1) chunks
+    const int o0 = 16 * line_pos(m, g), o1 = 16 * line_pos(m, 4 + g);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) raw[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < Fmt::kQSteps; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        raw[v] = mfma_16x16x32(*(const u32x4*)(tile[v] + ((j & 1) ? o1 : o0) + 1024 * (j & ~1)), qf[j], raw[v]);
+    // Order: kAhead LDS reads first, then one MFMA per further read, so that kAhead reads are
+    // always in flight (left alone, the scheduler keeps one or two, and one wave per SIMD
+    // then waits out the LDS latency before nearly every MFMA).
+    constexpr int kN = 4 * Fmt::kQSteps, kAhead = 8;
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int n = 0; n < kN - kAhead; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+  }
+}
+
+template <class Fmt>
+__device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t* smem, int b, int64_t L,
+                                                  int64_t t0_abs, int64_t t1_abs, float* out, float* lse) {
+  using CS = ColSplit<Fmt>;
+  constexpr int NB = CS::kNB;
+  constexpr int D = Fmt::kDmaOps;
+  constexpr int QS = Fmt::kQSteps;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // = this wave's row group
+  const int m = lane & 15;
+  const int g = lane >> 4;
+
+  const Range rg = {t0_abs, t1_abs};
+  const int n = (int)(rg.t1 - rg.t0);
+  const int ntiles = (n + kTile - 1) / kTile;
+  const int nsteps = (ntiles + kWaves - 1) / kWaves;
+
+  const int H = p.heads;
+  const int R = p.q_len * H;
+  const int row = 16 * wave + m;  // this lane's query row in the scores (row group = wave)
+  const int64_t lim = L - p.q_len + 1 + (row < R ? row / H : 0);
+  const int n_vis = (int)(min(rg.t1, lim) - rg.t0);
+
+  u32x4 qf[QS];
+#pragma unroll
+  for (int j = 0; j < QS; ++j) qf[j] = u32x4{0u, 0u, 0u, 0u};
+  if (row < R) {
+    const uint16_t* qrow = p.q + ((int64_t)b * R + row) * Fmt::kQDim + 8 * g;
+#pragma unroll
+    for (int j = 0; j < QS; ++j) qf[j] = *(const u32x4*)(qrow + 32 * j);
+  }
+
+  float m_run = -INFINITY;  // row group `wave`: running max (log2 domain) of row m
+  float l_run = 0.f;        // and this lane's share of its sum
+  f32x4 O[32];              // O[8 r + c]: row group r, columns 128 wave + 16 c + 4 g .. + 3, row m
+#pragma unroll
+  for (int u = 0; u < 32; ++u) O[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint8_t* pex = smem + CS::kTiles + CS::kPids + CS::kXslots;
+  float* alpha_s = (float*)(pex + CS::kPex);
+  int32_t* flag_s = (int32_t*)(alpha_s + 64);
+  uint8_t* sct_base = pex + CS::kPex + CS::kAlpha;  // fp8 block scales, two steps
+
+  const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+  const uint32_t ps = (uint32_t)p.page_size;
+  uint32_t bad = 0;
+  const int my_tok = lane >> 2;
+  constexpr int TPL = Fmt::kTokensPerLane;
+  uint8_t* wbuf = smem + wave * NB * Fmt::kTileBytes;
+  const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds_offset(wbuf));
+  uint8_t* pslot = smem + CS::kTiles + wave * NB * 256;
+  const uint32_t plds = __builtin_amdgcn_readfirstlane(lds_offset(pslot));
+  const uint32_t t0 = (uint32_t)rg.t0;
+  const uint32_t tlast = (uint32_t)(rg.t1 - 1);
+  auto clamp_token = [&](int k, int within) -> uint32_t {
+    const uint32_t t = t0 + (uint32_t)k * kTile + (uint32_t)within;
+    return t > tlast ? tlast : t;
+  };
+  // This wave's tile of step i (past the partition: its last tile, loaded again).
+  auto tile_of_step = [&](int i) -> int { return min(kWaves * i + wave, ntiles - 1); };
+  auto fetch_page = [&](int k, uint32_t slot_lds) { dma4(bt + clamp_token(k, my_tok) / ps, slot_lds); };
+  using Pages = int32_t[TPL];
+  auto issue_tile = [&](int k, const Pages& page, uint32_t dst) {
+    if constexpr (!Fmt::kFlatTile) {
+      const uint8_t* rows[TPL];
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        const uint32_t tok = clamp_token(k, Fmt::fetch_token(lane, i));
+        rows[i] = p.cache + ((int64_t)page[i] * (int64_t)ps + (int64_t)(tok % ps)) * (int64_t)Fmt::kRowBytes;
+      }
+      Fmt::issue(rows, dst, lane, p.stream_rows != 0);
+    }
+  };
+  auto read_pages = [&](const uint8_t* slot, Pages& page) {
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+      page[i] = checked_page(*(const int32_t*)(slot + 16 * Fmt::fetch_token(lane, i)), p.num_pages, bad);
+  };
+  auto issue_tile_flat = [&](int k, const uint8_t* pids, uint32_t dst) {
+    if constexpr (Fmt::kFlatTile) {
+      const uint32_t a = __builtin_amdgcn_readfirstlane(min(t0 + (uint32_t)k * kTile, tlast));
+      const uint32_t q0 = __builtin_amdgcn_readfirstlane(a % ps);
+      const bool nt = p.stream_rows != 0;
+      if (a + (kTile - 1) <= tlast && q0 + kTile <= ps) {
+        const int32_t pg = __builtin_amdgcn_readfirstlane(checked_page(*(const int32_t*)pids, p.num_pages, bad));
+        Fmt::issue_contiguous(p.cache + ((int64_t)pg * ps + q0) * Fmt::kRowBytes, dst, lane, nt);
+      } else {
+        auto row_of = [&](int i) -> const uint8_t* {
+          const uint32_t T = (uint32_t)Fmt::fetch_token(lane, i);
+          uint32_t off = q0 + min(T, tlast - a);
+          off = ps >= (uint32_t)kTile ? (off >= ps ? off - ps : off) : off % ps;
+          const int32_t pg = checked_page(*(const int32_t*)(pids + 16 * T), p.num_pages, bad);
+          return p.cache + ((int64_t)pg * ps + off) * Fmt::kRowBytes;
+        };
+        Fmt::issue_rows(row_of, dst, lane, nt);
+      }
+    }
+  };
+  // Page ids of step s land in slot s % NB; this wave's tile of step s in buffer s % NB.
+  // Queue per wave: PID(NB - 1) DMA(0) PID(NB) DMA(1) ... ; step i then issues PID(i + 2NB - 2)
+  // and DMA(i + NB - 1), so the ops younger than DMA(i) at the start of step i are those of
+  // steps i - NB + 2 .. i - 1: (NB - 2)(D + 1) of them when those steps issued.
+  auto slot_lds = [&](int s) { return plds + 256 * (uint32_t)(s % NB); };
+  auto buf_lds = [&](int s) { return wlds + (uint32_t)(s % NB) * Fmt::kTileBytes; };
+  if (nsteps > 0) {
+    if constexpr (Fmt::kFlatTile) {
+      uint8_t* xslot = smem + CS::kTiles + CS::kPids + wave * (NB - 1) * 256;
+      const uint32_t xlds = __builtin_amdgcn_readfirstlane(lds_offset(xslot));
+#pragma unroll
+      for (int t = 0; t < NB - 1; ++t) fetch_page(tile_of_step(t), xlds + 256 * t);
+#pragma unroll
+      for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
+      wait_vmcnt<0>();
+#pragma unroll
+      for (int t = 0; t < NB - 1; ++t) {
+        fetch_page(tile_of_step(t + NB - 1), slot_lds(t + NB - 1));
+        issue_tile_flat(tile_of_step(t), xslot + 256 * t, buf_lds(t));
+      }
+    } else {
+      int32_t page_first[NB - 1][TPL];
+#pragma unroll
+      for (int t = 0; t < NB - 1; ++t)
+#pragma unroll
+        for (int i = 0; i < TPL; ++i)
+          page_first[t][i] =
+              checked_page(bt[clamp_token(tile_of_step(t), Fmt::fetch_token(lane, i)) / ps], p.num_pages, bad);
+#pragma unroll
+      for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
+#pragma unroll
+      for (int t = 0; t < NB - 1; ++t)
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) asm volatile("" ::"v"(page_first[t][i]));
+#pragma unroll
+      for (int t = 0; t < NB - 1; ++t) {
+        fetch_page(tile_of_step(t + NB - 1), slot_lds(t + NB - 1));
+        issue_tile(tile_of_step(t), page_first[t], buf_lds(t));
+      }
+    }
+  }
+
+  const uint8_t* tiles = smem;
+  auto tile_ptr = [&](int i, int u) -> const uint8_t* { return tiles + (u * NB + i % NB) * Fmt::kTileBytes; };
+
+#pragma unroll 1
+  for (int i = 0; i < nsteps; ++i) {
+    // this wave's tile of step i has landed (and with it the page ids of step i + NB - 1)
+    if (i == 0 || i + NB - 2 < nsteps) wait_vmcnt<(NB - 2) * (D + 1)>();
+    else wait_vmcnt<0>();
+    uint8_t* sct = sct_base + (i & 1) * (4 * 4 * 16 * 4);
+    if constexpr (CS::kFp8) {
+      // this wave's tile has landed: its 16 tokens x 4 block scales, transposed to [block][token]
+      const int t = lane >> 2, k = lane & 3;
+      ((float*)sct)[16 * (4 * wave + k) + t] = *(const float*)(tile_ptr(i, wave) + Fmt::pos(t, 32) + 4 * k);
+    }
+    __syncthreads();  // the step's four tiles are visible; every wave is done with step i - 1
+    if (i + NB - 1 < nsteps) {
+      const int s = i + NB - 1;  // into buffer (i - 1) % NB, free since the barrier
+      fetch_page(tile_of_step(min(s + NB - 1, nsteps - 1)), slot_lds(s + NB - 1));
+      if constexpr (Fmt::kFlatTile) {
+        issue_tile_flat(tile_of_step(s), pslot + 256 * (s % NB), buf_lds(s));
+      } else {
+        Pages page_n;
+        read_pages(pslot + 256 * (s % NB), page_n);
+        issue_tile(tile_of_step(s), page_n, buf_lds(s));
+      }
+    }
+
+    // ---- scores of row group `wave` over the step's four tiles, online softmax, P out.
+    // The four tiles are four independent MFMA chains advanced one K-step at a time, so that
+    // the LDS reads of the next K-steps can be in flight while a K-step's MFMAs run.
+    f32x4 raw[4];
+    score_tiles<Fmt>(tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3), sct, m, g, qf, raw);
+    float sc[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int valid = n_vis - (kWaves * i + v) * kTile;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[v][r] = (4 * g + r < valid) ? raw[v][r] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[v][r]);
+      }
+    }
+    mx = max_over_rows(mx);
+    const bool grow = mx > m_run + kRescaleThreshold;
+    const bool any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
+    if (any_grow) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+      m_run = m_new;
+      if (g == 0) alpha_s[16 * wave + m] = alpha;
+    }
+    if (lane == 0) flag_s[wave] = any_grow ? 1 : 0;
+    const float m_base = m_run == -INFINITY ? 0.f : m_run;
+    float pr[4][4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[v][r] = fast_exp2(sc[v][r] - m_base);
+        l_run += pr[v][r];
+      }
+    if constexpr (CS::kFp8) {
+      f32x4* dst = (f32x4*)pex + (wave * 4) * 64 + lane;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[64 * v] = f32x4{pr[v][0], pr[v][1], pr[v][2], pr[v][3]};
+    } else {
+      u32x4* dst = (u32x4*)pex + (wave * 2) * 64 + lane;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        dst[64 * j] = u32x4{pack_bf16(pr[2 * j][0], pr[2 * j][1]), pack_bf16(pr[2 * j][2], pr[2 * j][3]),
+                            pack_bf16(pr[2 * j + 1][0], pr[2 * j + 1][1]), pack_bf16(pr[2 * j + 1][2], pr[2 * j + 1][3])};
+    }
+    __syncthreads();  // P, alpha and the flags of all four row groups are visible
+
+    // ---- rescales, then PV over this wave's columns for all four row groups
+    const u32x4 fl = *(const u32x4*)flag_s;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (__builtin_amdgcn_readfirstlane(fl[r]) != 0) {
+        const float a = alpha_s[16 * r + m];
+        f32x4(&Or)[8] = *reinterpret_cast<f32x4(*)[8]>(&O[8 * r]);
+        scale_acc(Or, a);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* ta = tile_ptr(i, 2 * j);
+      const uint8_t* tb = tile_ptr(i, 2 * j + 1);
+      if constexpr (CS::kFp8) {
+        // scale of block `wave` for this lane's tokens 4g .. 4g + 3 of tiles a and b
+        const f32x4 sa = *(const f32x4*)(sct + (16 * (4 * (2 * j) + wave) + 4 * g) * 4);
+        const f32x4 sb = *(const f32x4*)(sct + (16 * (4 * (2 * j + 1) + wave) + 4 * g) * 4);
+        u32x4 bp[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 pa = ((const f32x4*)pex)[(r * 4 + 2 * j) * 64 + lane];
+          const f32x4 pb = ((const f32x4*)pex)[(r * 4 + 2 * j + 1) * 64 + lane];
+          bp[r] = u32x4{pack_bf16(pa[0] * sa[0], pa[1] * sa[1]), pack_bf16(pa[2] * sa[2], pa[3] * sa[3]),
+                        pack_bf16(pb[0] * sb[0], pb[1] * sb[1]), pack_bf16(pb[2] * sb[2], pb[3] * sb[3])};
+        }
+        // A operand: lanes v < 4 read tile a, v >= 4 tile b (Fp8Rows::pv2), chunks of block `wave`
+        const int v = m >> 1, h = m & 1;
+        const uint8_t* src = (v < 4 ? ta : tb) + 8 * h + Fmt::pos(4 * g + (v & 3), 8 * wave);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const u32x4 a = Fmt::widen_tr8(lds_read_tr8(src + 16 * c));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[8 * r + c] = mfma_16x16x32(a, bp[r], O[8 * r + c]);
+        }
+      } else {
+        u32x4 bp[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bp[r] = ((const u32x4*)pex)[(r * 2 + j) * 64 + lane];
+        const uint8_t* ba[4];
+        Fmt::pv_bases(ta, m, g, ba);
+        const int db = (int)(tb - ta);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          // global column tile 8 wave + c: base (c & 3), plus 2048 (2 wave + (c >> 2))
+          const uint8_t* a0 = ba[c & 3] + 2048 * (2 * wave + (c >> 2));
+          const u32x2 x = lds_read_tr16(a0), y = lds_read_tr16(a0 + db);
+          const u32x4 a = {x[0], x[1], y[0], y[1]};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[8 * r + c] = mfma_16x16x32(a, bp[r], O[8 * r + c]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: the owners publish (max, sum) of their rows; every wave writes its columns
+  const float l_row = sum_over_rows(l_run);
+  __syncthreads();  // every wave is done with the last step's P
+  float* fin = (float*)pex;  // [row group][row]: max, then sum
+  if (g == 0) {
+    fin[16 * wave + m] = m_run;
+    fin[64 + 16 * wave + m] = l_row;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rr = 16 * r + m;
+    const float M = fin[rr], l = fin[64 + rr];
+    if (rr < R) {
+      // no finite score: (+0, -inf), or NaN when every score was NaN (the sum is then NaN)
+      const float f = M == -INFINITY ? 0.f : 1.0f / l;
+      float* orow = out + (int64_t)rr * kLatent + 128 * wave + 4 * g;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        f32x4 o = M == -INFINITY ? f32x4{l * 0.f, l * 0.f, l * 0.f, l * 0.f} : O[8 * r + c] * f;
+        *(f32x4*)(orow + 16 * c) = o;
+      }
+      if (wave == 0 && g == 0)
+        lse[rr] = (M == -INFINITY) ? -INFINITY + l : (M + fast_log2(l)) * 0.69314718055994530942f;
+    }
+  }
+  report_checks(bad, p.check_status);
+}
+
+// Rows that take the column-split verify step (four row groups).  fp8 rows keep the shared
+// widened tiles of decode_segment: scored from the raw codes, every row group widens every code
+// again (four times the conversions), measured slower (fp8-ragged, q_len 4: 229 against 204 us).
+template <class Fmt, int G>
+constexpr bool kColSplit = G == 4 && std::is_same<Fmt, Bf16Rows<512, 64>>::value;
+
+template <class Fmt, int G>
+constexpr int kernel_smem_bytes() {
+  if constexpr (kColSplit<Fmt, G>) {
+    return ColSplit<Fmt>::kBytes > smem_bytes<Fmt>() ? ColSplit<Fmt>::kBytes : smem_bytes<Fmt>();
+  } else {
+    return smem_bytes<Fmt>();
+  }
+}
+
+template <class Fmt, int G, bool kGla2>
+__device__ __forceinline__ void decode_rows(const DecodeParams& p, uint8_t* smem, int b, int64_t L, int64_t t0,
+                                            int64_t t1, float* out, float* lse) {
+  if constexpr (kColSplit<Fmt, G>) {
+    static_assert(!kGla2, "GLA-g2 decodes one row group");
+    decode_segment_cs<Fmt>(p, smem, b, L, t0, t1, out, lse);
+  } else {
+    decode_segment<Fmt, G, kGla2>(p, smem, b, L, t0, t1, out, lse);
+  }
+}
+
 // Prefix sums over the requests of a batch of B <= kMaxBalancedBatch: out[0] = 0, out[b + 1] =
 // out[b] + value(b).  Thread t takes requests 4t .. 4t + 3; the 256 sums are scanned with wave
 // shuffles and a pass over the four wave totals (in `scratch`, kWaves values).  Ends with a
@@ -906,7 +1350,7 @@ __device__ __forceinline__ int find_request(const T* pre, int B, T x) {
 // merge are the same either way.
 template <class Fmt, int G, bool kGla2 = false>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kernel_smem_bytes<Fmt, G>()];
   constexpr int kOut = kGla2 ? 256 : Fmt::kLatent;
   int b = blockIdx.x;
   int s = blockIdx.y;
@@ -952,7 +1396,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   const bool split = p.num_splits > 1;
   float* out = split ? p.part_out + ((int64_t)s * p.batch * R + row_b) * kOut : p.out + row_b * kOut;
   float* lse = split ? p.part_lse + (int64_t)s * p.batch * R + row_b : p.lse + row_b;
-  decode_segment<Fmt, G, kGla2>(p, smem, b, L, rg.t0, rg.t1, out, lse);
+  decode_rows<Fmt, G, kGla2>(p, smem, b, L, rg.t0, rg.t1, out, lse);
 }
 
 // Batch-balanced decode.  The batch's requests are laid end to end on a cost axis: request
@@ -970,17 +1414,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
 // groups of 16, as in decode_kernel).
 template <class Fmt, int G>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
-  __shared__ int64_t v_s[kMaxBalancedBatch + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kernel_smem_bytes<Fmt, G>()];
   const int B = p.batch;
   uint32_t lbad = 0;  // checked build: a length outside [0, bt_stride * page_size]
-  scan_requests<int64_t>(
-      B,
-      [&](int r) -> int64_t {
-        const int64_t L = checked_len(p.seq_lens[r], p.bt_stride, p.page_size, lbad);
-        return L > 0 ? L + kSegmentCost : 0;
-      },
-      v_s, (int64_t*)smem);
+  auto cost = [&](int r) -> int64_t {
+    const int64_t L = checked_len(p.seq_lens[r], p.bt_stride, p.page_size, lbad);
+    return L > 0 ? L + kSegmentCost : 0;
+  };
+  // The axis v [B + 1] is scanned into the tile memory, which the segments only use after it;
+  // each workgroup then keeps the start of its first request and walks forward from there.
+  static_assert(kernel_smem_bytes<Fmt, G>() >= (kWaves + kMaxBalancedBatch + 1) * 8, "axis scratch");
+  int64_t* v_s = (int64_t*)smem + kWaves;
+  scan_requests<int64_t>(B, cost, v_s, (int64_t*)smem);
   report_checks(lbad, p.check_status);
   if (blockIdx.x == 0)
     for (int b = threadIdx.x; b <= B; b += kWaves * 64) p.cu[b] = v_s[b];
@@ -988,18 +1433,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
   const int64_t V = v_s[B];
   const int64_t W = min((int64_t)gridDim.x, V);
   const int64_t w = blockIdx.x;
-  if (w >= W) return;
+  if (w >= W) return;  // uniform over the workgroup
   const int64_t lo = flat_begin(V, W, w), hi = flat_begin(V, W, w + 1);
   int bl = 0, bh = B;  // v[bl] <= lo < v[bh]
   while (bh - bl > 1) {
     const int mid = (bl + bh) >> 1;
     if (v_s[mid] <= lo) bl = mid; else bh = mid;
   }
+  int64_t v0 = v_s[bl];
+  __syncthreads();  // the scratch is tile memory from here on
   const int R = p.q_len * p.heads;
   for (int b = bl; b < B; ++b) {
-    const int64_t v0 = v_s[b], v1 = v_s[b + 1];
+    const int64_t v1 = v0 + cost(b);
     if (v0 >= hi) break;
-    if (v1 <= lo || v1 == v0) continue;  // empty requests have no partial
+    if (v1 <= lo || v1 == v0) {  // empty requests have no partial
+      v0 = v1;
+      continue;
+    }
     const int64_t s0 = v0 + kSegmentCost;  // axis position of token 0
     const int64_t L = v1 - s0;
     // Token boundaries fall on multiples of 16 (a tile), so that the tiles of a segment start
@@ -1008,9 +1458,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
     const int64_t t0 = on_tile(max(lo, s0) - s0);
     const int64_t t1 = on_tile(max(min(hi, v1) - s0, (int64_t)0));  // 0: the range holds start-up only
     const int64_t slot = (int64_t)b + w;
-    decode_segment<Fmt, G, false>(p, smem, b, L, t0, max(t0, t1), p.part_out + slot * R * kLatent,
-                                  p.part_lse + slot * R);
+    decode_rows<Fmt, G, false>(p, smem, b, L, t0, max(t0, t1), p.part_out + slot * R * kLatent,
+                               p.part_lse + slot * R);
     __syncthreads();  // the epilogue's LDS reads finish before the next segment's loads land
+    v0 = v1;
   }
 }
 
