@@ -59,9 +59,14 @@ def _parse():
     ap.add_argument("--nope", action="store_true",
                     help="decode the workload as a NoPE-512 layer: 512-wide queries, rows written with a zero "
                          "rope part, which the NoPE kernels never read")
-    ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
+    ap.add_argument("--flush-mib", type=int, default=None, metavar="MIB",
                     help="also time each decode after a pass over MIB MiB of other memory (evicts the "
-                         "last-level cache between repetitions); the roofline then uses these cold times")
+                         "last-level cache between repetitions); the roofline then uses these cold times. "
+                         "Default: 1024 for workloads whose cache bytes fit in the 256 MB last-level "
+                         "cache, 0 otherwise")
+    ap.add_argument("--event-reps", type=int, default=50,
+                    help="minimum number of steps in the per-kernel HIP-event pass (medians over at "
+                         "least this many repetitions, whatever --steps is)")
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="with --graph: steps captured per HIP graph (the largest divisor of --steps up "
                          "to this)")
@@ -93,6 +98,32 @@ def _copy_calibration(mib: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+LLC_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
+
+
+def _read_ceiling(dev, stream, gib=2, reps=20):
+    """Same-run streaming-read ceiling: median HIP-event time of a read-only reduction (torch
+    amax) over `gib` GiB of fp32, i.e. what this machine streams from HBM with a plain kernel that
+    reads every byte once."""
+    import torch
+    buf = torch.ones(gib << 28, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        buf.amax()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        buf.amax()
+        b.record(stream)
+        times.append((a, b))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in times]))
+    del buf
+    gbs = (gib << 30) / (ms * 1e-3) / 1e9
+    return {"gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "how": f"torch amax over {gib} GiB of fp32, median of {reps} HIP-event windows"}
 
 
 RANKS = {"rank256": 256, "rank768": 768, "rank1792": 1792}
@@ -547,7 +578,14 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    reps = max(args.steps, args.event_reps)  # per-kernel event windows: at least this many
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    if args.steps < args.event_reps:
+        print(f"bench.py: {args.steps} timed steps give the value; the per-kernel medians use {reps} "
+              f"event-timed steps", file=sys.stderr)
+    flush_mib = args.flush_mib
+    if flush_mib is None:  # rows that fit in the last-level cache are timed after a flush as well
+        flush_mib = 1024 if w.tokens * w.row_bytes < LLC_BYTES else 0
 
     def step(e=None):
         if e: e[0].record(stream)
@@ -585,7 +623,7 @@ def main():
     # inside a window (each window times its kernel as back-to-back execution runs it).
     for _ in range(max(args.warmup, 8)):
         step()
-    for i in range(args.steps):
+    for i in range(reps):
         step(ev[i])
     torch.cuda.synchronize()
 
@@ -621,22 +659,26 @@ def main():
 
     ms_step = wall * 1e3 / args.steps
     ms_step_eager = eager_wall * 1e3 / args.steps
-    t_write = np.mean([e[0].elapsed_time(e[1]) for e in ev])
-    t_decode = np.mean([e[1].elapsed_time(e[2]) for e in ev])
-    t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev])
+    win = {name: [e[a].elapsed_time(e[b]) for e in ev]
+           for name, a, b in (("cache_write", 0, 1), ("decode", 1, 2), ("merge", 2, 3), ("step", 0, 3))}
+    t_write, t_decode, t_merge = (float(np.mean(win[k])) for k in ("cache_write", "decode", "merge"))
+    med = {k: round(float(np.median(v)), 4) for k, v in win.items()}
     t_decode_warm = t_decode
-    if args.flush_mib:
+    if flush_mib:
         # Each step again, eagerly, after reading flush_mib MiB of other memory, so that the
         # cache rows come from HBM rather than from the last-level cache.  The pass only reads
         # (a write pass would leave dirty lines whose write-back lands in the timed decode).
-        flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device=dev)
-        ev_cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-        for i in range(args.steps):
+        flush = torch.ones(flush_mib << 18, dtype=torch.float32, device=dev)
+        ev_cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+        for i in range(reps):
             flush.amax()
             step(ev_cold[i])
         torch.cuda.synchronize()
-        t_decode = np.mean([e[1].elapsed_time(e[2]) for e in ev_cold])
+        cold = [e[1].elapsed_time(e[2]) for e in ev_cold]
+        t_decode = float(np.mean(cold))
+        med["decode_after_flush"] = round(float(np.median(cold)), 4)
         del flush
+    ceiling = _read_ceiling(dev, stream)
     # rows that see at least one token (query i of a verify step sees L - q_len + 1 + i)
     vis = (w.seq_lens[:, None] - T + 1 + np.arange(T)[None, :]) > 0
     live = np.repeat(vis, w.heads, axis=1)
@@ -675,12 +717,19 @@ def main():
             "row_bytes_read": row_bytes_read,
             "step": "decode + merge" if not write_rows else "cache write + decode + merge",
             "cache_bytes_per_step": cache_bytes,
+            # distinct rows read: below cache_bytes_per_step when requests share pages (high_slot),
+            # whose figure is then an effective bandwidth, part of it served from the caches
+            "unique_cache_bytes": int(w.slots.size) * row_bytes_read,
+            "bandwidth": "effective (pages repeat across requests)" if w.slots.size < w.tokens else "hbm",
         },
         "launch": launch_mode,
-        "flush_mib": args.flush_mib,
+        "flush_mib": flush_mib,
+        "event_reps": reps,
+        "kernel_ms_median": med,
+        "read_ceiling": ceiling,
         "eager_ms_per_step": round(ms_step_eager, 4),
         "kernel_ms": {"cache_write": round(t_write, 4), "decode": round(t_decode_warm, 4), "merge": round(t_merge, 4),
-                      **({"decode_after_flush": round(t_decode, 4)} if args.flush_mib else {})},
+                      **({"decode_after_flush": round(t_decode, 4)} if flush_mib else {})},
         "roofline": {
             "kernel": kernel,
             "bound": "hbm",

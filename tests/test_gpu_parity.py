@@ -472,6 +472,39 @@ def _request_slots(w, b):
     return w.block_table[b].astype(np.int64)[t // w.page_size] * w.page_size + t % w.page_size
 
 
+def _oracle_pool(w):
+    """Host pool with every row of the workload packed by the oracle (in chunks)."""
+    ph = w.poisoned_pool()
+    for c in range(0, w.slots.size, 1 << 16):
+        sl = slice(c, c + (1 << 16))
+        oracle.cache_write(ph, w.latent[sl], w.k_pe[sl], w.slots[sl], w.fmt)
+    return ph
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["batched", "fp8_ragged", "high_slot"])
+def test_full_size_every_request(name):
+    """Every request of the full-size ragged workloads, in the bench's schedule and split count,
+    against the oracle decoding a pool of its own packing.  high_slot's requests share pages
+    (a page read for the wrong request would still give finite values), so the sampled checks
+    elsewhere are not enough there."""
+    import time
+    w = workloads.NAMED[name]()
+    balanced = workloads.BENCH_SCHEDULE[name] == "balanced"
+    S = workloads.BENCH_BALANCED_WORKGROUPS if balanced else workloads.BENCH_SPLITS[name]
+    say(f"case {name} every request: fmt={w.fmt} B={w.batch} tokens={w.tokens} "
+        f"{'balanced W' if balanced else 'splits'}={S}")
+    flags = mla.MLA_FLAG_CACHED_ROWS if workloads.BENCH_ROW_LOADS[name] == "cached" else 0
+    pd = device_pool(w)
+    out, lse = gpu_decode(w, pd, S, balanced=balanced, flags=flags)
+    del pd
+    t = time.perf_counter()
+    ph = _oracle_pool(w)
+    ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt)
+    say(f"  oracle: {time.perf_counter() - t:.1f} s")
+    assert_parity(w, out, lse, ref_o, ref_l, what=f"{name} every request")
+
+
 @pytest.mark.parametrize("name", ["batched", "long_context", "high_slot", "fp8_ragged"])
 def test_full_size_workloads_sampled(name):
     """The named workloads at full size in the bench's launch configuration.
