@@ -43,6 +43,13 @@ What is computed (per request b and head h), following the pages:
   of D latent values followed by the 64 rope values; GLA-g2 keeps the 576-value / 656-byte
   row, heads [0, H/2) use latent values [0, 256) and heads [H/2, H) use [256, 512), both
   groups share the rope, and each head's output is its group's 256 values.
+* Sparse (index-list) decode: each query token carries its own list of cache slots to attend
+  to, already converted to global slot numbers (vLLM PR #55543, the tests commit: a ragged
+  mixed batch whose valid counts include 0 and 1, with -1 tails, all-invalid rows giving
+  (0, -inf); the review of the mocked index converter, which hands the kernel the converted
+  per-query indices).  Reading: indices [T, topk] int32, shared by all heads of a query; an
+  entry below zero selects nothing wherever it stands; attention runs over exactly the listed
+  slots (a slot listed twice counts twice); row offsets are slot * row_bytes in 64-bit.
 * NoPE-512 layers (no rotary part) keep the same row and write zeros into its rope part;
   their query has 512 values, padded with zeros to 576, so the rope part adds nothing to
   any score (vLLM PR #55543, description of the zero-rope approach).  decode_nope is the
@@ -183,6 +190,24 @@ def decode_mtp(q_bits, pool, block_table, seq_lens, page_size: int, scale: float
         for i in range(T):
             n = max(0, L - T + 1 + i)
             out[b, i], lse[b, i] = attend(q[b, i], rows[:n], scale)
+    return out, lse
+
+
+def decode_sparse(q_bits, pool, indices, scale: float, fmt: str, tokens=None) -> tuple[np.ndarray, np.ndarray]:
+    """Sparse decode: q_bits [T, H, 576]; indices int [T, topk], the slots query t attends to
+    (entries < 0 select nothing).  Returns out [T, H, 512], lse [T, H]; queries not listed in
+    `tokens` are left as NaN."""
+    q = bf16_to_f64(q_bits)
+    T, H, _ = q.shape
+    rows_all = _pool_rows(pool, fmt)
+    idx = np.asarray(indices, dtype=np.int64)
+    out = np.full((T, H, LATENT), np.nan)
+    lse = np.full((T, H), np.nan)
+    for t in (range(T) if tokens is None else tokens):
+        slots = idx[t][idx[t] >= 0]
+        if (slots >= rows_all.shape[0]).any():
+            raise IndexError(f"query {t}: slot outside the pool")
+        out[t], lse[t] = attend(q[t], rows_from_bytes(rows_all[slots], fmt), scale)
     return out, lse
 
 

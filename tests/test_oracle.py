@@ -16,6 +16,10 @@ mla.attend               closed forms (golden); pure-Python brute force (math.fs
                          1-token, uniform-score, duplication, hardmax, empty invariants;
                          a softmax-over-heads mistake planted in the oracle fails them
 mla.decode               page-permutation invariance; garbage-rope control
+mla.decode_sparse        pure-Python brute force over the listed rows (-1 anywhere, counts 0 / 1 /
+                         partial, a repeated slot); equals the paged decode when a list enumerates
+                         a request's slots; list order and -1 placement irrelevant; a -1 never
+                         reads the pool's last row (a planted reading of it fails)
 mla.decode_mtp           pure-Python brute force with the causal limits written out;
                          each query equals decode over its truncated context; rows after a
                          query's position never change it (a planted off-by-one fails)
@@ -468,6 +472,74 @@ def test_mtp_matches_brute_force():
                 continue
             bo, bl = _brute_attend(qf[b, i].tolist(), rows, w.scale)
             assert np.max(np.abs(out[b, i] - bo)) < 1e-12 and np.max(np.abs(lse[b, i] - bl)) < 1e-12
+
+
+def _full_pool(rng, slots, fmt="bf16"):
+    """A pool of `slots` rows, every one finite and distinct (no poison), packed by the oracle."""
+    lat = workloads.bf16_bits(rng.standard_normal((slots, 512)).astype(np.float32))
+    pe = workloads.bf16_bits(rng.standard_normal((slots, 64)).astype(np.float32))
+    R = oracle.ROW_BYTES[fmt]
+    pool = np.zeros((slots, R), np.uint8)
+    oracle.cache_write(pool, lat, pe, np.arange(slots), fmt)
+    return pool
+
+
+def test_sparse_matches_brute_force():
+    """Index lists with -1 entries anywhere, valid counts 0, 1, partial and full, a repeated
+    slot, against explicit Python loops over the listed rows."""
+    rng = np.random.default_rng(51)
+    pool = _full_pool(rng, 20)
+    idx = np.array([[3, 7, -1, -1], [-1, -1, -1, -1], [19, -1, -1, -1], [5, -1, 0, 11], [2, 2, 9, 4]], np.int32)
+    q = workloads.bf16_bits(rng.standard_normal((5, 2, 576)).astype(np.float32))
+    out, lse = oracle.decode_sparse(q, pool, idx, 0.07, "bf16")
+    qf = oracle.bf16_to_f64(q)
+    for t in range(5):
+        rows = [oracle.bf16_to_f64(pool[int(i)].view("<u2")).tolist() for i in idx[t] if i >= 0]
+        if not rows:
+            assert (out[t] == 0).all() and not np.signbit(out[t]).any() and np.isneginf(lse[t]).all()
+            continue
+        bo, bl = _brute_attend(qf[t].tolist(), rows, 0.07)
+        assert np.max(np.abs(out[t] - bo)) < 1e-12 and np.max(np.abs(lse[t] - bl)) < 1e-12
+    # one valid entry: that row's latent, exactly
+    row = oracle.bf16_to_f64(pool[19].view("<u2"))
+    assert np.array_equal(out[2], np.broadcast_to(row[:512], (2, 512)))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_sparse_equals_block_table_decode_over_the_same_slots(fmt):
+    """A request's index list that enumerates its context's slots in token order (padded with a
+    -1 tail) gives the paged decode's result; reordering the list or moving its -1 entries
+    changes nothing beyond rounding."""
+    rng = np.random.default_rng(52)
+    w = workloads.make_workload("sparse_eq", seq_lens=[37, 1, 0, 64], heads=4, page_size=16, num_pages=12,
+                                fmt=fmt, rng=rng)
+    pool = w.poisoned_pool()
+    oracle.cache_write(pool, w.latent, w.k_pe, w.slots, fmt)
+    ref_o, ref_l = oracle.decode(w.q, pool, w.block_table, w.seq_lens, w.page_size, w.scale, fmt)
+    topk = 80
+    idx = np.full((w.batch, topk), -1, np.int64)
+    for b in range(w.batch):
+        for t in range(int(w.seq_lens[b])):
+            idx[b, t] = int(w.block_table[b][t // 16]) * 16 + t % 16
+    out, lse = oracle.decode_sparse(w.q, pool, idx, w.scale, fmt)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(ref_l))
+    assert np.allclose(out, ref_o, rtol=0, atol=1e-12) and np.allclose(lse[1:2], ref_l[1:2], atol=1e-12)
+    shuffled = np.array([rng.permutation(r) for r in idx])  # -1 entries land anywhere
+    out2, lse2 = oracle.decode_sparse(w.q, pool, shuffled, w.scale, fmt)
+    fin = np.isfinite(lse)
+    assert np.allclose(out2, out, rtol=0, atol=1e-12) and np.allclose(lse2[fin], lse[fin], rtol=0, atol=1e-12)
+
+
+def test_sparse_never_reads_a_negative_entry():
+    """A -1 entry must select nothing: array indexing would silently read the pool's last row,
+    which here differs from every listed row."""
+    rng = np.random.default_rng(53)
+    pool = _full_pool(rng, 10)
+    q = workloads.bf16_bits(rng.standard_normal((1, 2, 576)).astype(np.float32))
+    with_tail, _ = oracle.decode_sparse(q, pool, np.array([[1, 2, -1]]), 0.07, "bf16")
+    plain, _ = oracle.decode_sparse(q, pool, np.array([[1, 2]]), 0.07, "bf16")
+    wrong, _ = oracle.decode_sparse(q, pool, np.array([[1, 2, 9]]), 0.07, "bf16")  # what -1 would read
+    assert np.array_equal(with_tail, plain) and not np.allclose(with_tail, wrong)
 
 
 def _mtp_case(seed, T=4):
