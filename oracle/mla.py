@@ -196,9 +196,12 @@ def decode_mtp(q_bits, pool, block_table, seq_lens, page_size: int, scale: float
 def decode_sparse(q_bits, pool, indices, scale: float, fmt: str, tokens=None) -> tuple[np.ndarray, np.ndarray]:
     """Sparse decode: q_bits [T, H, 576]; indices int [T, topk], the slots query t attends to
     (entries < 0 select nothing).  Returns out [T, H, 512], lse [T, H]; queries not listed in
-    `tokens` are left as NaN."""
+    `tokens` are left as NaN.  q_bits [T, H, 512] is the NoPE-512 form (the layers the page
+    serves through the sparse backend): scores over the latent values only, as decode_nope."""
     q = bf16_to_f64(q_bits)
-    T, H, _ = q.shape
+    T, H, D = q.shape
+    if D not in (ROW, LATENT):
+        raise ValueError("sparse queries have 576 (or, NoPE-512, 512) values per head")
     rows_all = _pool_rows(pool, fmt)
     idx = np.asarray(indices, dtype=np.int64)
     out = np.full((T, H, LATENT), np.nan)
@@ -207,7 +210,7 @@ def decode_sparse(q_bits, pool, indices, scale: float, fmt: str, tokens=None) ->
         slots = idx[t][idx[t] >= 0]
         if (slots >= rows_all.shape[0]).any():
             raise IndexError(f"query {t}: slot outside the pool")
-        out[t], lse[t] = attend(q[t], rows_from_bytes(rows_all[slots], fmt), scale)
+        out[t], lse[t] = attend(q[t], rows_from_bytes(rows_all[slots], fmt)[:, :D], scale)
     return out, lse
 
 

@@ -19,7 +19,8 @@ mla.decode               page-permutation invariance; garbage-rope control
 mla.decode_sparse        pure-Python brute force over the listed rows (-1 anywhere, counts 0 / 1 /
                          partial, a repeated slot); equals the paged decode when a list enumerates
                          a request's slots; list order and -1 placement irrelevant; a -1 never
-                         reads the pool's last row (a planted reading of it fails)
+                         reads the pool's last row (a planted reading of it fails); NoPE-512
+                         queries: brute force over the latent values, NaN rope ignored
 mla.decode_mtp           pure-Python brute force with the causal limits written out;
                          each query equals decode over its truncated context; rows after a
                          query's position never change it (a planted off-by-one fails)
@@ -540,6 +541,30 @@ def test_sparse_never_reads_a_negative_entry():
     plain, _ = oracle.decode_sparse(q, pool, np.array([[1, 2]]), 0.07, "bf16")
     wrong, _ = oracle.decode_sparse(q, pool, np.array([[1, 2, 9]]), 0.07, "bf16")  # what -1 would read
     assert np.array_equal(with_tail, plain) and not np.allclose(with_tail, wrong)
+
+
+def test_sparse_nope_brute_force_and_rope_ignored():
+    """NoPE-512 queries (q [T, H, 512]): pure-Python brute force over the listed rows' 512 latent
+    values; NaN rope values in every row change nothing (they never enter a score)."""
+    rng = np.random.default_rng(54)
+    pool = _full_pool(rng, 12)
+    idx = np.array([[4, -1, 8, 1], [-1, -1, -1, -1], [11, -1, -1, -1]], np.int32)
+    q = workloads.bf16_bits(rng.standard_normal((3, 2, 512)).astype(np.float32))
+    out, lse = oracle.decode_sparse(q, pool, idx, 0.09, "bf16")
+    qf = oracle.bf16_to_f64(q)
+    for t in range(3):
+        rows = [oracle.bf16_to_f64(pool[int(i)].view("<u2"))[:512].tolist() for i in idx[t] if i >= 0]
+        if not rows:
+            assert (out[t] == 0).all() and np.isneginf(lse[t]).all()
+            continue
+        bo, bl = _brute_attend(qf[t].tolist(), rows, 0.09)
+        assert np.max(np.abs(out[t] - bo)) < 1e-12 and np.max(np.abs(lse[t] - bl)) < 1e-12
+    nan_rope = pool.copy()
+    nan_rope.view("<u2")[:, 512:] = 0x7FC0
+    out2, lse2 = oracle.decode_sparse(q, nan_rope, idx, 0.09, "bf16")
+    assert np.array_equal(out2, out) and np.array_equal(lse2, lse)
+    with pytest.raises(ValueError):
+        oracle.decode_sparse(q[:, :, :500], pool, idx, 0.09, "bf16")
 
 
 def _mtp_case(seed, T=4):
