@@ -78,7 +78,7 @@ def _parse():
                          "(measured slower here for every workload: 1-7 %% per step)")
     ap.add_argument("--eager", action="store_true",
                     help="eager launches (the default; kept for older command lines)")
-    ap.add_argument("--op", choices=("decode", "gather", "cache_write", "merge"), default="decode",
+    ap.add_argument("--op", choices=("decode", "gather", "cache_write", "merge", "sparse"), default="decode",
                     help="gather: time mla_gather_context over the workload's whole context instead "
                          "(prefill-side context gather, fp8 rows upconverted to bf16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -451,6 +451,146 @@ def _bench_merge(args):
     print(json.dumps(result), flush=True)
 
 
+def _bench_sparse(args):
+    """Sparse decode step: every request's newest token attends to workloads.SPARSE_TOPK slots of
+    its own context, listed per query (fewer for shorter contexts, -1 padded): the index-list
+    decode, then the merge of its partitions."""
+    import torch
+    import oracle
+    import paged_mla_latent_amd as mla
+    import workloads
+
+    w = workloads.NAMED[args.workload]()
+    topk = workloads.SPARSE_TOPK
+    idx_np = workloads.sparse_lists(w, topk)
+    S = args.splits or workloads.SPARSE_SPLITS[args.workload]
+    nope = args.nope
+    row_loads = args.row_loads or workloads.BENCH_ROW_LOADS[args.workload]
+    flags = mla.MLA_FLAG_CACHED_ROWS if row_loads == "cached" else 0
+    dev = torch.device("cuda:0")
+    fmt = mla.MLA_CACHE_BF16_576 if w.fmt == "bf16" else mla.MLA_CACHE_FP8_656
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # the pool at its full size, with the listed slots' rows written (the rest never read)
+    used = np.unique(idx_np[idx_np >= 0]).astype(np.int64)
+    rows_of = np.searchsorted(w.slots, used)
+    if w.fmt == "bf16":
+        pool = torch.full((w.num_pages, w.page_size, 576), 0x7FC0, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    else:
+        pool = torch.full((w.num_pages, w.page_size, 656), 0xFF, dtype=torch.uint8, device=dev)
+    mla.mla_cache_write(bf16(w.latent[rows_of]), bf16(w.k_pe[rows_of]), torch.from_numpy(used).to(dev), pool, fmt)
+    q_np = np.ascontiguousarray(w.q[:, :, :512]) if nope else w.q
+    q = bf16(q_np)
+    idx = torch.from_numpy(idx_np).to(dev)
+    name = f"mla_decode_sparse_{'nope_' if nope else ''}{'bf16' if w.fmt == 'bf16' else 'fp8_656'}"
+    fn = getattr(mla, name)
+    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, mla.mla_decode_workspace_size(w.batch, w.heads, S)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        if S > 1:
+            po, pl = fn(q, pool, idx, w.scale, num_splits=S, workspace=ws, partials_only=True, flags=flags)
+            if e: e[1].record(stream)
+            mla.mla_merge_lse(po, pl, out=out, lse=lse)
+        else:
+            fn(q, pool, idx, w.scale, num_splits=1, out=out, lse=lse, flags=flags)
+            if e: e[1].record(stream)
+        if e: e[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    reps = max(args.steps, args.event_reps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for _ in range(max(args.warmup, 8)):
+        step()
+    for e in ev:
+        step(e)
+    torch.cuda.synchronize()
+    warm = [e[0].elapsed_time(e[1]) for e in ev]
+    merge = [e[1].elapsed_time(e[2]) for e in ev]
+    row_bytes_read = w.row_bytes - (128 if nope and w.fmt == "bf16" else 0)
+    valid = int((idx_np >= 0).sum())
+    step_bytes = valid * row_bytes_read
+    flush_mib = args.flush_mib if args.flush_mib is not None else (1024 if step_bytes < LLC_BYTES else 0)
+    cold = warm
+    if flush_mib:
+        flush = torch.ones(flush_mib << 18, dtype=torch.float32, device=dev)
+        ev_cold = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for e in ev_cold:
+            flush.amax()
+            step(e)
+        torch.cuda.synchronize()
+        cold = [e[0].elapsed_time(e[1]) for e in ev_cold]
+        del flush
+    t_decode = float(np.median(cold))
+    # spot check: the first queries with 0, 1, some and all entries valid, against the oracle
+    counts = (idx_np >= 0).sum(axis=1)
+    picks = sorted({int(np.argmax(counts == c)) for c in (0, 1) if (counts == c).any()} |
+                   {int(np.argmax(counts == topk)) if (counts == topk).any() else 0, int(np.argmin(counts))})
+    compact = np.zeros((used.size, w.row_bytes), np.uint8)
+    oracle.cache_write(compact, w.latent[rows_of], w.k_pe[rows_of], np.arange(used.size), w.fmt)
+    local = np.where(idx_np >= 0, np.searchsorted(used, idx_np), -1)
+    ref_o, ref_l = oracle.decode_sparse(q_np, compact, local, w.scale, w.fmt, tokens=picks)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for t in picks:
+        if counts[t] == 0:
+            assert (o[t] == 0).all() and np.isneginf(l[t]).all(), f"query {t}: an empty list is not (0, -inf)"
+            continue
+        err = np.abs(o[t] - ref_o[t]).max(axis=1) / np.abs(ref_o[t]).max(axis=1)
+        assert err.max() <= 1e-2 and np.abs(l[t] - ref_l[t]).max() <= 1e-3, f"query {t} differs from the oracle"
+    ms_step = wall * 1e3 / args.steps
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    decode_gbs = step_bytes / (t_decode * 1e-3) / 1e9
+    rope = 0 if nope else 64
+    kernel = f"decode_sparse_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}>'}>"
+    result = {
+        "metric": "sparse decode GB/s (listed cache rows read)", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.fmt, "data": "synthetic",
+        "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "config": {"workload": w.name, "op": "sparse", "queries": w.batch, "heads": w.heads, "topk": topk,
+                   "valid_entries": valid, "num_splits": S, "layer": "nope-512" if nope else "rope-576",
+                   "row_loads": row_loads, "row_bytes_read": row_bytes_read, "bytes_per_step": step_bytes,
+                   "unique_cache_bytes": int(used.size) * row_bytes_read,
+                   "step": "decode + merge" if S > 1 else "decode"},
+        "flush_mib": flush_mib, "event_reps": reps,
+        "kernel_ms_median": {"decode": round(float(np.median(warm)), 4), "merge": round(float(np.median(merge)), 4),
+                             **({"decode_after_flush": round(t_decode, 4)} if flush_mib else {})},
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            threads = 1
+        # the step's queries in turn (longest lists first) until about 10 s of host time
+        order = [int(t) for t in np.argsort(-counts, kind="stable") if counts[t] > 0]
+        n, done, t0 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            t = order[n % len(order)]
+            oracle.decode_sparse(q_np, compact, local, w.scale, w.fmt, tokens=[t])
+            n, done = n + 1, done + int(counts[t]) * row_bytes_read
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle (decode_sparse) on {n} queries of the same step (longest lists first), "
+                      f"{dt:.1f} s; BLAS threads {threads}"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = _parse()
     if args.copy_calibration:
@@ -469,6 +609,9 @@ def main():
         return
     if args.op == "merge":
         _bench_merge(args)
+        return
+    if args.op == "sparse":
+        _bench_sparse(args)
         return
 
     import torch

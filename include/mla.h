@@ -100,7 +100,7 @@ enum {
 };
 
 enum { MLA_LATENT = 512, MLA_ROPE = 64, MLA_ROW = 576, MLA_MAX_HEADS = 16, MLA_MAX_Q_LEN = 16,
-       MLA_MAX_QUERY_ROWS = 64, MLA_MAX_BALANCED_BATCH = 1024 };
+       MLA_MAX_QUERY_ROWS = 64, MLA_MAX_BALANCED_BATCH = 1024, MLA_MAX_SPARSE_TOKENS = 1 << 20 };
 
 /* Bytes of workspace mla_decode_bf16 / mla_decode_fp8_656 need for num_splits
  * partitions: num_splits * batch * num_heads * (512 + 1) * 4 rounded up to 256,
@@ -264,6 +264,59 @@ MLA_API int mla_decode_nope_fp8_656(const void* q, const void* kv_cache, int64_t
                                     int32_t page_size, float softmax_scale, int32_t num_splits,
                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
                                     uint32_t flags, int32_t* check_status, void* stream);
+
+/* Decode over per-query index lists (sparse MLA: vLLM pull request 55543 serves the
+ * NoPE-512 layers through the FlashMLA sparse backend, where an indexer picks for every
+ * query token the cache slots it attends to; its ragged mixed-batch test gives lists with
+ * 0, 1 or some valid entries followed by -1).  Query token t attends to the slots listed in
+ * indices[t][0 .. topk): s_j = softmax_scale * <q_t, row(indices[t][j])> over the valid
+ * entries j, softmax over them, out = sum p_j latent(indices[t][j]).
+ * q           bf16 [num_tokens][num_heads][576] (_nope_: [num_tokens][num_heads][512], the
+ *             scores over the 512 latent values only, as mla_decode_nope_*).
+ * kv_cache    num_slots rows of 1,152 bytes (bf16 576) or 656 bytes (fp8_656), slot after
+ *             slot: a paged pool seen as its slots (slot = page * page_size + offset).
+ * num_slots   rows in kv_cache, >= 1.  Row offsets are formed in 64 bits (slot * row bytes),
+ *             so slots above 3,728,270 (where a 32-bit element offset of a 576-value row
+ *             wraps) are addressed like any other.
+ * indices     int32 [num_tokens][topk], row-major.  An entry in [0, num_slots) selects that
+ *             slot (a slot listed twice counts twice); a negative entry (-1 in the lists'
+ *             padding, but anywhere in a list) selects nothing.  A query whose list selects
+ *             nothing gets (+0.0, -inf), the neutral partial of the merge contract.  Entries
+ *             >= num_slots break the precondition: the release build reads outside the cache;
+ *             the checked build reads slot 0 instead and sets MLA_CHECK_BLOCK_ID.
+ * topk        entries per list, >= 1.    num_tokens  1..MLA_MAX_SPARSE_TOKENS.
+ * num_heads   1..MLA_MAX_HEADS.
+ * num_splits  1..65535: each list is cut into num_splits parts of ceil(topk / num_splits)
+ *             entries (trailing parts may be empty), decoded by separate workgroups and
+ *             merged by log-sum-exp; a workspace of mla_decode_workspace_size(num_tokens,
+ *             num_heads, num_splits) bytes is needed when num_splits > 1.
+ * out, lse    fp32 [num_tokens][num_heads][512] and [num_tokens][num_heads] (natural log).
+ *             out == lse == NULL with num_splits > 1 stops after the decode kernel: the
+ *             partials stay in the workspace ([num_splits][num_tokens][num_heads][512], then
+ *             [num_splits][num_tokens][num_heads]; every partition writes one, an empty one
+ *             (+0, -inf)) for mla_merge_lse.
+ * flags, check_status, stream, the errors and the rounding as mla_decode_bf16 /
+ * mla_decode_fp8_656. */
+MLA_API int mla_decode_sparse_bf16(const void* q, const void* kv_cache, int64_t num_slots,
+                                   const int32_t* indices, int32_t topk, int32_t num_tokens, int32_t num_heads,
+                                   float softmax_scale, int32_t num_splits, float* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, uint32_t flags,
+                                   int32_t* check_status, void* stream);
+MLA_API int mla_decode_sparse_fp8_656(const void* q, const void* kv_cache, int64_t num_slots,
+                                      const int32_t* indices, int32_t topk, int32_t num_tokens, int32_t num_heads,
+                                      float softmax_scale, int32_t num_splits, float* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, uint32_t flags,
+                                      int32_t* check_status, void* stream);
+MLA_API int mla_decode_sparse_nope_bf16(const void* q, const void* kv_cache, int64_t num_slots,
+                                        const int32_t* indices, int32_t topk, int32_t num_tokens, int32_t num_heads,
+                                        float softmax_scale, int32_t num_splits, float* out, float* lse,
+                                        void* workspace, size_t workspace_bytes, uint32_t flags,
+                                        int32_t* check_status, void* stream);
+MLA_API int mla_decode_sparse_nope_fp8_656(const void* q, const void* kv_cache, int64_t num_slots,
+                                           const int32_t* indices, int32_t topk, int32_t num_tokens, int32_t num_heads,
+                                           float softmax_scale, int32_t num_splits, float* out, float* lse,
+                                           void* workspace, size_t workspace_bytes, uint32_t flags,
+                                           int32_t* check_status, void* stream);
 
 /* Multi-token verify decode (speculative decoding): q_len query tokens per request, the
  * last q_len positions of its sequence, scored against the cache in one pass that reads

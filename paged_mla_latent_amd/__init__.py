@@ -66,8 +66,10 @@ EXPORTED = (
     "mla_merge_lse_balanced", "mla_decode_rank_workspace_size", "mla_decode_rank768_bf16",
     "mla_decode_rank1792_bf16", "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656",
     "mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656", "mla_checked_build",
-    "mla_check_preconditions_host", "mla_decode_bf16_noalloc",
+    "mla_check_preconditions_host", "mla_decode_bf16_noalloc", "mla_decode_sparse_bf16",
+    "mla_decode_sparse_fp8_656", "mla_decode_sparse_nope_bf16", "mla_decode_sparse_nope_fp8_656",
 )
+MAX_SPARSE_TOKENS = 1 << 20
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
@@ -132,6 +134,11 @@ def library(checked: bool = False) -> ctypes.CDLL:
     lib.mla_decode_bf16_noalloc.argtypes = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp,
                                             c_u32, vp, vp]
     lib.mla_decode_bf16_noalloc.restype = c_int
+    sparse = [vp, vp, c_i64, vp, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, c_u32, vp, vp]
+    for name in ("mla_decode_sparse_bf16", "mla_decode_sparse_fp8_656", "mla_decode_sparse_nope_bf16",
+                 "mla_decode_sparse_nope_fp8_656"):
+        getattr(lib, name).argtypes = sparse
+        getattr(lib, name).restype = c_int
     lib.mla_checked_build.argtypes = []
     lib.mla_checked_build.restype = c_int
     lib.mla_check_preconditions_host.argtypes = [vp, c_i64, vp, c_i32, c_i32, c_i64]
@@ -304,6 +311,79 @@ def mla_decode_nope_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, n
     return _decode("mla_decode_nope_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
                    softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=LATENT,
                    flags=flags, check_status=check_status)
+
+
+def _decode_sparse(fn: str, cache_dtype: torch.dtype, row_elems: int, q_dim: int, q, kv_cache, indices,
+                   softmax_scale, num_splits, out, lse, workspace, flags, check_status, partials_only=False):
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    lib, status_ptr = _options(check_status, dev)
+    if not isinstance(kv_cache, torch.Tensor) or kv_cache.dim() not in (2, 3):
+        raise ValueError("kv_cache must be [num_slots, row] or [num_pages, page_size, row]")
+    _need(kv_cache, "kv_cache", cache_dtype, kv_cache.dim(), dev)
+    if kv_cache.shape[-1] != row_elems:
+        raise ValueError(f"kv_cache rows must have {row_elems} elements, got {kv_cache.shape[-1]}")
+    _need(indices, "indices", torch.int32, 2, dev)
+    T, H, D = q.shape
+    if D != q_dim:
+        raise ValueError(f"q rows must have {q_dim} values, got {D}")
+    if indices.shape[0] != T:
+        raise ValueError("indices must have one row per query token")
+    if partials_only:
+        if num_splits < 2 or out is not None or lse is not None:
+            raise ValueError("partials_only needs num_splits > 1 and no out/lse")
+    else:
+        if out is None:
+            out = torch.empty((T, H, LATENT), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, 3, dev)
+        _need(lse, "lse", torch.float32, 2, dev)
+    ws_bytes = 0
+    if num_splits > 1:
+        if workspace is None:
+            workspace = torch.empty(mla_decode_workspace_size(T, H, num_splits), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    num_slots = kv_cache.numel() // row_elems
+    status = getattr(lib, fn)(
+        q.data_ptr(), kv_cache.data_ptr(), num_slots, indices.data_ptr(), indices.shape[1], T, H,
+        float(softmax_scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        int(flags), status_ptr, _stream(dev))
+    _check(fn, status, lib)
+    if partials_only:
+        n = num_splits * T * H
+        flat = workspace.view(torch.uint8)[: n * (LATENT + 1) * 4].view(torch.float32)
+        return flat[: n * LATENT].view(num_splits, T, H, LATENT), flat[n * LATENT:].view(num_splits, T, H)
+    return out, lse
+
+
+def mla_decode_sparse_bf16(q, kv_cache, indices, softmax_scale, num_splits=1, out=None, lse=None, workspace=None,
+                           flags=0, check_status=None, partials_only=False):
+    """Decode over per-query index lists: q [T, H, 576], kv_cache bf16 [..., 576] (its slots),
+    indices int32 [T, topk] (negative entries select nothing); returns (out [T,H,512], lse [T,H])."""
+    return _decode_sparse("mla_decode_sparse_bf16", torch.bfloat16, ROW, ROW, q, kv_cache, indices, softmax_scale,
+                          num_splits, out, lse, workspace, flags, check_status, partials_only)
+
+
+def mla_decode_sparse_fp8_656(q, kv_cache, indices, softmax_scale, num_splits=1, out=None, lse=None,
+                              workspace=None, flags=0, check_status=None, partials_only=False):
+    """Index-list decode over an fp8 cache uint8 [..., 656]."""
+    return _decode_sparse("mla_decode_sparse_fp8_656", torch.uint8, 656, ROW, q, kv_cache, indices, softmax_scale,
+                          num_splits, out, lse, workspace, flags, check_status, partials_only)
+
+
+def mla_decode_sparse_nope_bf16(q, kv_cache, indices, softmax_scale, num_splits=1, out=None, lse=None,
+                                workspace=None, flags=0, check_status=None, partials_only=False):
+    """NoPE-512 index-list decode over a bf16 cache: q [T, H, 512]."""
+    return _decode_sparse("mla_decode_sparse_nope_bf16", torch.bfloat16, ROW, LATENT, q, kv_cache, indices,
+                          softmax_scale, num_splits, out, lse, workspace, flags, check_status, partials_only)
+
+
+def mla_decode_sparse_nope_fp8_656(q, kv_cache, indices, softmax_scale, num_splits=1, out=None, lse=None,
+                                   workspace=None, flags=0, check_status=None, partials_only=False):
+    """NoPE-512 index-list decode over an fp8 cache: q [T, H, 512]."""
+    return _decode_sparse("mla_decode_sparse_nope_fp8_656", torch.uint8, 656, LATENT, q, kv_cache, indices,
+                          softmax_scale, num_splits, out, lse, workspace, flags, check_status, partials_only)
 
 
 def mla_decode_balanced_workspace_size(batch: int, num_heads: int, num_workgroups: int) -> int:

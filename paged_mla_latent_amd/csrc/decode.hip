@@ -49,6 +49,11 @@ constexpr int kWaves = 4;
 constexpr int kTile = 16;
 constexpr float kRescaleThreshold = 8.0f;
 
+// A row of zeros (as long as the longest row, 1,152 bytes) that index-list decodes load in place
+// of a negative entry: its score is masked, and its values (zeros, not whatever slot 0 holds,
+// which may be non-finite) add nothing to the output.  Never written.
+__device__ __align__(256) uint8_t g_zero_row[1152];
+
 // Rows of kLat latent values followed by 64 rope values, bf16.  kLat = 512, kRopeDim = 64:
 // the 576-value row.  kRopeDim = 0 (NoPE-512 layers): only the 512 latent values (the
 // first 1,024 bytes of each row) are loaded and scored.  kLat = 256: rank-256 layers,
@@ -485,9 +490,13 @@ __device__ __forceinline__ void finish_rows(uint8_t* smem, const f32x4 (&O)[TF::
 // latent, rope), scattered into a 576-wide fragment that is zero outside the group, and
 // the output of each head is its group's 256 columns.  The row is read once for both
 // groups; the MFMA work is that of the 576-wide decode.
-template <class Fmt, int G, bool kGla2>
+// kSparse (single-token decodes only): the block table is a per-query list of cache slots
+// (page size 1) whose negative entries select nothing: such a token is loaded from slot 0 and
+// masked out of the scores (a 16-bit validity mask per tile, taken when the tile's slots are read).
+template <class Fmt, int G, bool kGla2, bool kSparse = false>
 __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* smem, int b, int64_t L,
                                                int64_t t0_abs, int64_t t1_abs, float* out, float* lse) {
+  static_assert(!kSparse || (G == 1 && !kGla2), "index lists: single-token queries");
   static_assert(G == 1 || G == 2 || G == 4, "row groups per workgroup");
   static_assert(!kGla2 || (Fmt::kLatent == 512 && Fmt::kQDim == 576), "GLA-g2 on the 576-value row");
   constexpr int kOut = kGla2 ? 256 : Fmt::kLatent;  // output values per query row
@@ -548,6 +557,29 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
   const uint32_t ps = (uint32_t)p.page_size;
   uint32_t bad = 0;  // checked build: MLA_CHECK_* bits of the block ids this lane used
+  // A block id (with index lists: a slot) as used for an address.
+  auto page_id = [&](int32_t id) -> int32_t {
+    if constexpr (kSparse) {
+      return id < 0 ? -1 : checked_page(id, p.num_pages, bad);
+    } else {
+      return checked_page(id, p.num_pages, bad);
+    }
+  };
+  // Address of the row at offset `off` of page `pg` (index lists: a negative entry is the zero row).
+  auto row_addr = [&](int32_t pg, uint32_t off) -> const uint8_t* {
+    const uint8_t* a = p.cache + ((int64_t)pg * (int64_t)ps + (int64_t)off) * (int64_t)Fmt::kRowBytes;
+    if constexpr (kSparse) a = pg < 0 ? g_zero_row : a;
+    return a;
+  };
+  // Index lists: which of a tile's 16 slots are valid (bit T for token T), kept per tile buffer
+  // in vmask (16 bits per buffer).
+  uint64_t vmask = ~(uint64_t)0;
+  auto set_mask = [&](int buf, bool ok) {
+    if constexpr (kSparse) {
+      const uint64_t bits = (uint64_t)__builtin_amdgcn_ballot_w64(ok && lane < kTile) & 0xFFFFu;
+      vmask = (vmask & ~((uint64_t)0xFFFF << (16 * buf))) | (bits << (16 * buf));
+    }
+  };
   const int my_tok = lane >> 2;  // the token whose page id this lane fetches
   constexpr int TPL = Fmt::kTokensPerLane;  // the tokens whose rows this lane fetches
   // Tile buffers per wave: Fmt::kBufs for one row group; the shared-tile loop of G > 1 is
@@ -588,8 +620,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 #pragma unroll
       for (int i = 0; i < TPL; ++i) {
         const uint32_t tok = clamp_token(k, Fmt::fetch_token(lane, i));
-        const int64_t slot = (int64_t)page[i] * (int64_t)ps + (int64_t)(tok % ps);
-        rows[i] = p.cache + slot * (int64_t)Fmt::kRowBytes;
+        rows[i] = row_addr(page[i], tok % ps);
       }
       Fmt::issue(rows, dst, lane, p.stream_rows != 0);
     }
@@ -597,7 +628,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   auto read_pages = [&](const uint8_t* slot, Pages& page) {
 #pragma unroll
     for (int i = 0; i < TPL; ++i)
-      page[i] = checked_page(*(const int32_t*)(slot + 16 * Fmt::fetch_token(lane, i)), p.num_pages, bad);
+      page[i] = page_id(*(const int32_t*)(slot + 16 * Fmt::fetch_token(lane, i)));
   };
   // Row-major tiles (Fmt::kFlatTile) take their page ids from a page-id slot in LDS (token T's
   // page at byte 16T): a tile of 16 consecutive slots of one page is fetched as one run (a single
@@ -609,16 +640,15 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       const uint32_t a = __builtin_amdgcn_readfirstlane(min(t0 + (uint32_t)k * kTile, tlast));
       const uint32_t q0 = __builtin_amdgcn_readfirstlane(a % ps);  // its slot in its page (uniform)
       const bool nt = p.stream_rows != 0;
-      if (a + (kTile - 1) <= tlast && q0 + kTile <= ps) {
-        const int32_t pg = __builtin_amdgcn_readfirstlane(checked_page(*(const int32_t*)pids, p.num_pages, bad));
+      if (!kSparse && a + (kTile - 1) <= tlast && q0 + kTile <= ps) {
+        const int32_t pg = __builtin_amdgcn_readfirstlane(page_id(*(const int32_t*)pids));
         Fmt::issue_contiguous(p.cache + ((int64_t)pg * ps + q0) * Fmt::kRowBytes, dst, lane, nt);
       } else {
         auto row_of = [&](int i) -> const uint8_t* {
           const uint32_t T = (uint32_t)Fmt::fetch_token(lane, i);
           uint32_t off = q0 + min(T, tlast - a);  // slot of the clamped token, before wrapping
           off = ps >= (uint32_t)kTile ? (off >= ps ? off - ps : off) : off % ps;
-          const int32_t pg = checked_page(*(const int32_t*)(pids + 16 * T), p.num_pages, bad);
-          return p.cache + ((int64_t)pg * ps + off) * Fmt::kRowBytes;
+          return row_addr(page_id(*(const int32_t*)(pids + 16 * T)), off);
         };
         Fmt::issue_rows(row_of, dst, lane, nt);
       }
@@ -627,15 +657,17 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 
   // One tile of work: QK^T, online softmax, PV on tile k (partition-relative) in `buf`.
   // Tokens at or past this lane's visibility limit, or past the partition, get p = 0.
-  auto compute = [&](const uint8_t* buf, int k) {
+  auto compute = [&](const uint8_t* buf, int k, int cur) {
     typename Fmt::Aux aux;
     const f32x4 raw = Fmt::qk(buf, m, g, qf, aux);
     const int valid = n_vis - k * kTile;
+    const uint32_t tm = kSparse ? (uint32_t)(vmask >> (16 * cur)) : 0xFFFFu;  // the tile's valid slots
     float sc[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sc[r] = (4 * g + r < valid) ? raw[r] * p.scale_log2 : -INFINITY;
+      const bool in = (4 * g + r < valid) && (!kSparse || ((tm >> (4 * g + r)) & 1u));
+      sc[r] = in ? raw[r] * p.scale_log2 : -INFINITY;
       mx = fmaxf(mx, sc[r]);
     }
     mx = max_over_rows(mx);
@@ -734,6 +766,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 #pragma unroll
       for (int t = 0; t < NB - 1; ++t) {
         fetch_page(min(k + kWaves * (t + NB - 1), ntiles - 1), plds + 256 * t);
+        if constexpr (kSparse) set_mask(t, *(const int32_t*)(xslot + 256 * t + 16 * (lane & (kTile - 1))) >= 0);
         if (G > 1 || k + kWaves * t < ntiles)
           issue_tile_flat(k + kWaves * t, xslot + 256 * t, wlds + t * Fmt::kTileBytes);
       }
@@ -750,9 +783,13 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 #pragma unroll
       for (int i = 0; i < TPL; ++i)
         page_first[t][i] = (G == 1 ? k + kWaves * t < ntiles : ntiles > 0)
-                               ? checked_page(bt[clamp_token(k + kWaves * t, Fmt::fetch_token(lane, i)) / ps],
-                                              p.num_pages, bad)
+                               ? page_id(bt[clamp_token(k + kWaves * t, Fmt::fetch_token(lane, i)) / ps])
                                : 0;
+    if constexpr (kSparse) {
+#pragma unroll
+      for (int t = 0; t < NB - 1; ++t)
+        set_mask(t, k + kWaves * t < ntiles && lane < kTile && bt[clamp_token(k + kWaves * t, lane) / ps] >= 0);
+    }
 #pragma unroll
     for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
 #pragma unroll
@@ -784,6 +821,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       for (; k + kWaves * (NB - 1) < ntiles; k += kWaves) {
         const int ahead = cur == 0 ? NB - 1 : cur - 1;  // (cur + NB - 1) mod NB
         wait_vmcnt<(NB - 1) * D + (NB - 2)>();  // page ids of tile k + 4(NB-1) have landed
+        if constexpr (kSparse) set_mask(ahead, *(const int32_t*)(pslot + 256 * cur + 16 * (lane & (kTile - 1))) >= 0);
         if constexpr (Fmt::kFlatTile) {
           fetch_page(min(k + kWaves * 2 * (NB - 1), ntiles - 1), plds + 256 * ahead);
           issue_tile_flat(k + kWaves * (NB - 1), pslot + 256 * cur, wlds + ahead * Fmt::kTileBytes);
@@ -794,12 +832,12 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
           issue_tile(k + kWaves * (NB - 1), page_n, wlds + ahead * Fmt::kTileBytes);
         }
         wait_vmcnt<(NB - 1) * (D + 1)>();  // tile k has landed
-        compute(wbuf + cur * Fmt::kTileBytes, k);
+        compute(wbuf + cur * Fmt::kTileBytes, k, cur);
         cur = cur + 1 == NB ? 0 : cur + 1;
       }
       wait_vmcnt<0>();
       for (; k < ntiles; k += kWaves) {
-        compute(wbuf + cur * Fmt::kTileBytes, k);
+        compute(wbuf + cur * Fmt::kTileBytes, k, cur);
         cur = cur + 1 == NB ? 0 : cur + 1;
       }
     }
@@ -1399,6 +1437,26 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   decode_rows<Fmt, G, kGla2>(p, smem, b, L, rg.t0, rg.t1, out, lse);
 }
 
+// Decode over per-query index lists: grid (query token, partition).  Query t attends to the
+// cache slots indices[t][0 .. topk) (p.block_table with row stride p.bt_stride = topk, read as
+// a block table of page size 1); a negative entry selects nothing.  Every query's list has the
+// same length topk, split into p.num_splits equal parts; each partition writes its partial,
+// empty or not (a partition whose entries are all negative gives (0, -inf) like an empty one).
+template <class Fmt>
+__global__ __launch_bounds__(kWaves * 64, 1) void decode_sparse_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<Fmt>()];
+  const int b = blockIdx.x;
+  const int s = blockIdx.y;
+  const int64_t L = p.bt_stride;
+  const Range rg = partition(L, 1, p.num_splits, s, L);
+  const int R = p.heads;
+  const int64_t row_b = (int64_t)b * R;
+  const bool split = p.num_splits > 1;
+  float* out = split ? p.part_out + ((int64_t)s * p.batch * R + row_b) * Fmt::kLatent : p.out + row_b * Fmt::kLatent;
+  float* lse = split ? p.part_lse + (int64_t)s * p.batch * R + row_b : p.lse + row_b;
+  decode_segment<Fmt, 1, false, true>(p, smem, b, L, rg.t0, rg.t1, out, lse);
+}
+
 // Batch-balanced decode.  The batch's requests are laid end to end on a cost axis: request
 // b occupies [v[b], v[b + 1]) with v[b + 1] - v[b] = kSegmentCost + L_b for L_b > 0 (0 for
 // an empty request), its tokens at the last L_b positions; the first kSegmentCost stand
@@ -1532,6 +1590,20 @@ hipError_t launch_decode_flat_nope_fp8(const DecodeParams& p, int num_workgroups
 }
 hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream) {
   return launch<Fp8Rows<0>>(p, stream);
+}
+// Index-list decodes: p.batch query tokens of at most 16 heads, p.q_len = 1, p.page_size = 1,
+// p.bt_stride = topk.  Formats 0 bf16, 1 fp8 656-byte rows; nope: scores over the latent only.
+hipError_t launch_decode_sparse(const DecodeParams& p, int fp8, int nope, hipStream_t stream) {
+  const dim3 grid((unsigned)p.batch, (unsigned)p.num_splits), block(kWaves * 64);
+  if (!fp8 && !nope)
+    hipLaunchKernelGGL((decode_sparse_kernel<Bf16Rows<512, 64>>), grid, block, 0, stream, p);
+  else if (!fp8)
+    hipLaunchKernelGGL((decode_sparse_kernel<Bf16Rows<512, 0>>), grid, block, 0, stream, p);
+  else if (!nope)
+    hipLaunchKernelGGL((decode_sparse_kernel<Fp8Rows<64>>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_sparse_kernel<Fp8Rows<0>>), grid, block, 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace mla

@@ -371,6 +371,77 @@ int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void
       "mla_merge_lse_balanced (after balanced decode)");
 }
 
+// Decode over per-query index lists (mla_decode_sparse_*): fp8 selects the 656-byte rows, nope
+// the scores over the latent only.
+int decode_sparse_common(int fp8, int nope, const void* q, const void* kv_cache, int64_t num_slots,
+                         const int32_t* indices, int32_t topk, int32_t num_tokens, int32_t num_heads,
+                         float softmax_scale, int32_t num_splits, float* out, float* lse, void* workspace,
+                         size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
+  static const char* const kNames[2][2] = {{"mla_decode_sparse_bf16", "mla_decode_sparse_nope_bf16"},
+                                           {"mla_decode_sparse_fp8_656", "mla_decode_sparse_nope_fp8_656"}};
+  const char* fn = kNames[fp8][nope];
+  if (int rc0 = check_options(fn, flags, check_status)) return rc0;
+  if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
+  if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
+  if (!indices) return fail(MLA_ERR_NULL, "%s: indices is NULL", fn);
+  // out == lse == NULL with num_splits > 1 leaves the partials in the workspace (no merge).
+  const bool partials_only = !out && !lse && num_splits > 1;
+  if (!out && !partials_only) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
+  if (!lse && !partials_only) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
+  if (num_tokens < 1 || num_tokens > MLA_MAX_SPARSE_TOKENS)
+    return fail(MLA_ERR_SHAPE, "%s: num_tokens=%d outside [1, %d]", fn, num_tokens, (int)MLA_MAX_SPARSE_TOKENS);
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
+    return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_HEADS);
+  if (topk < 1) return fail(MLA_ERR_SHAPE, "%s: topk=%d must be >= 1", fn, topk);
+  if (num_slots < 1) return fail(MLA_ERR_SHAPE, "%s: num_slots=%lld must be >= 1", fn, (long long)num_slots);
+  if (num_splits < 1 || num_splits > 65535)
+    return fail(MLA_ERR_SHAPE, "%s: num_splits=%d outside [1, 65535]", fn, num_splits);
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_SHAPE, "%s: softmax_scale is not finite", fn);
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(indices) || !aligned16(out) || !aligned16(lse))
+    return fail(MLA_ERR_ALIGN, "%s: every tensor pointer must be 16-byte aligned", fn);
+  float* part_out = nullptr;
+  float* part_lse = nullptr;
+  if (num_splits > 1) {
+    const size_t need = workspace_bytes_for(num_tokens, num_heads, num_splits);
+    if (!workspace) return fail(MLA_ERR_WORKSPACE, "%s: num_splits=%d needs a workspace", fn, num_splits);
+    if (!aligned16(workspace)) return fail(MLA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+    if (workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
+    part_out = static_cast<float*>(workspace);
+    part_lse = part_out + (size_t)num_splits * num_tokens * num_heads * MLA_LATENT;
+  }
+  int rc = check_device();
+  if (rc != MLA_OK) return rc;
+
+  mla::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.cache = static_cast<const uint8_t*>(kv_cache);
+  p.block_table = indices;  // a block table of page size 1: one slot per entry
+  p.bt_stride = topk;
+  p.seq_lens = nullptr;
+  p.batch = num_tokens;
+  p.heads = num_heads;
+  p.q_len = 1;
+  p.page_size = 1;
+  p.num_splits = num_splits;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  p.out = out;
+  p.lse = lse;
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.cu = nullptr;
+  p.compact = 0;
+  p.skip_empty = 0;
+  p.stream_rows = (flags & MLA_FLAG_CACHED_ROWS) == 0;
+  p.num_pages = num_slots;
+  p.check_status = check_status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = hip_status(mla::launch_decode_sparse(p, fp8, nope, s), fn);
+  if (rc != MLA_OK || num_splits == 1 || partials_only) return rc;
+  return hip_status(mla::launch_merge(part_out, part_lse, num_splits, num_tokens, num_heads, out, lse, s),
+                    "mla_merge_lse (after sparse decode)");
+}
+
 }  // namespace
 
 extern "C" {
@@ -383,6 +454,21 @@ int mla_decode_bf16_noalloc(const void* q, const void* kv_cache, int64_t num_pag
                        page_size, softmax_scale, num_splits, out, lse, nullptr, 0, flags, check_status, stream,
                        /*use_scratch=*/true);
 }
+
+#define MLA_SPARSE_ENTRY(NAME, FP8, NOPE)                                                                   \
+  int NAME(const void* q, const void* kv_cache, int64_t num_slots, const int32_t* indices, int32_t topk,     \
+           int32_t num_tokens, int32_t num_heads, float softmax_scale, int32_t num_splits, float* out,       \
+           float* lse, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status,      \
+           void* stream) {                                                                                  \
+    return decode_sparse_common(FP8, NOPE, q, kv_cache, num_slots, indices, topk, num_tokens, num_heads,    \
+                                softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags,     \
+                                check_status, stream);                                                      \
+  }
+MLA_SPARSE_ENTRY(mla_decode_sparse_bf16, 0, 0)
+MLA_SPARSE_ENTRY(mla_decode_sparse_fp8_656, 1, 0)
+MLA_SPARSE_ENTRY(mla_decode_sparse_nope_bf16, 0, 1)
+MLA_SPARSE_ENTRY(mla_decode_sparse_nope_fp8_656, 1, 1)
+#undef MLA_SPARSE_ENTRY
 
 size_t mla_decode_balanced_workspace_size(int32_t batch, int32_t num_heads, int32_t num_workgroups) {
   if (batch < 1 || num_heads < 1 || num_workgroups < 0) return 0;

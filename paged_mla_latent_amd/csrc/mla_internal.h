@@ -134,6 +134,7 @@ hipError_t launch_decode_gla2_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_rank768_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_rank1792_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_gla2_fp8(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_sparse(const DecodeParams& p, int fp8, int nope, hipStream_t stream);
 hipError_t launch_decode_flat_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream);
 hipError_t launch_decode_flat_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream);
 hipError_t launch_decode_flat_nope_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream);

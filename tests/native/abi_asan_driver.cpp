@@ -138,6 +138,18 @@ int main() {
   expect(mla_decode_bf16_noalloc(P, P, 10, static_cast<const int32_t*>(P), 4, static_cast<const int32_t*>(P), 4, 16,
                                  64, 0.07f, 200, static_cast<float*>(P), static_cast<float*>(P), 0, nullptr,
                                  nullptr) == MLA_ERR_WORKSPACE, "noalloc scratch limit");
+  // index-list decodes: the longest name in every message, the largest workspace the checks admit
+  for (auto fn : {mla_decode_sparse_bf16, mla_decode_sparse_fp8_656, mla_decode_sparse_nope_bf16,
+                  mla_decode_sparse_nope_fp8_656}) {
+    const int32_t* idx = static_cast<const int32_t*>(P);
+    float* f = static_cast<float*>(P);
+    expect(fn(nullptr, P, 100, idx, 64, 3, 16, 0.07f, 1, f, f, nullptr, 0, 0, nullptr, nullptr) == MLA_ERR_NULL,
+           "sparse null q");
+    expect(fn(P, P, 100, idx, 0, 3, 16, 0.07f, 1, f, f, nullptr, 0, 0, nullptr, nullptr) == MLA_ERR_SHAPE,
+           "sparse topk");
+    expect(fn(P, P, 100, idx, 64, MLA_MAX_SPARSE_TOKENS, 16, 0.07f, 65535, f, f, P, 1, 0, nullptr, nullptr) ==
+               MLA_ERR_WORKSPACE, "sparse largest workspace");
+  }
   for (int st = -3; st < 10; ++st) expect(std::strlen(mla_status_string(st)) > 0, "status string");
 
   // the host precondition check against the reference on random tables (ragged, with -1 tails,

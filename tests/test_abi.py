@@ -427,6 +427,56 @@ def test_noalloc_validation(lib):
     assert rc == 2 and "flag" in msg
 
 
+SPARSE = ["mla_decode_sparse_bf16", "mla_decode_sparse_fp8_656", "mla_decode_sparse_nope_bf16",
+          "mla_decode_sparse_nope_fp8_656"]
+
+
+def _sparse(lib, fn, **kw):
+    a = dict(q=P, kv=P, num_slots=100, idx=P, topk=64, tokens=3, heads=16, scale=0.07, splits=1, out=P, lse=P,
+             ws=None, ws_bytes=0, flags=0, cs=None)
+    a.update(kw)
+    rc = getattr(lib, fn)(a["q"], a["kv"], a["num_slots"], a["idx"], a["topk"], a["tokens"], a["heads"], a["scale"],
+                          a["splits"], a["out"], a["lse"], a["ws"], a["ws_bytes"], a["flags"], a["cs"], None)
+    return rc, lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("fn", SPARSE)
+def test_sparse_validation(lib, fn):
+    for field in ("q", "kv", "idx", "out", "lse"):
+        rc, msg = _sparse(lib, fn, **{field: None})
+        assert rc == 1 and "NULL" in msg and fn in msg, field
+    for kw, word in [(dict(tokens=0), "num_tokens"), (dict(tokens=(1 << 20) + 1), "num_tokens"),
+                     (dict(heads=0), "num_heads"), (dict(heads=17), "num_heads"), (dict(topk=0), "topk"),
+                     (dict(num_slots=0), "num_slots"), (dict(splits=0), "num_splits"),
+                     (dict(splits=70000), "num_splits"), (dict(scale=float("nan")), "softmax_scale"),
+                     (dict(flags=4), "flag")]:
+        rc, msg = _sparse(lib, fn, **kw)
+        assert rc == 2 and word in msg and fn in msg, kw
+    for field in ("q", "kv", "idx", "out", "lse"):
+        rc, msg = _sparse(lib, fn, **{field: MIS})
+        assert rc == 3 and "aligned" in msg, field
+    need = mla.mla_decode_workspace_size(3, 16, 4)
+    rc, msg = _sparse(lib, fn, splits=4)
+    assert rc == 4 and "workspace" in msg
+    rc, msg = _sparse(lib, fn, splits=4, ws=P, ws_bytes=need - 1)
+    assert rc == 4 and str(need) in msg
+    # valid arguments: only the device is missing here
+    assert _sparse(lib, fn, splits=4, ws=P, ws_bytes=need)[0] == 5
+    assert _sparse(lib, fn)[0] == 5
+    rc, msg = _sparse(lib, fn, cs=P)
+    assert rc == 2 and "checked build" in msg
+    # out == lse == NULL: the partials stay in the workspace (num_splits > 1 only)
+    assert _sparse(lib, fn, out=None, lse=None, splits=4, ws=P, ws_bytes=need)[0] == 5
+    assert _sparse(lib, fn, out=None, lse=None)[0] == 1
+
+
+@pytest.mark.parametrize("fn", SPARSE)
+def test_sparse_checked_build_takes_a_status_word(checked_lib, fn):
+    assert _sparse(checked_lib, fn, cs=P)[0] == 5  # accepted; only the device is missing
+    rc, msg = _sparse(checked_lib, fn, cs=P + 2)
+    assert rc == 3 and "check_status" in msg
+
+
 def test_error_message_is_thread_local(lib):
     import threading
     _decode(lib, heads=99)

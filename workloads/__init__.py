@@ -254,6 +254,26 @@ def verify_step(w: Workload, q_len: int, seed: int = 1):
     return q, new_slots, w.latent[idx].copy(), w.k_pe[idx].copy()
 
 
+def sparse_lists(w: Workload, topk: int, seed: int = 2) -> np.ndarray:
+    """Per-query index lists for a sparse decode step over workload w: int32 [B, topk].
+
+    Request b's list holds min(L_b, topk) distinct slots of its own context (token
+    positions drawn uniformly without replacement, listed in random order, as an indexer's
+    top-k would come), then -1 padding; an empty request's list is all -1.
+    """
+    rng = np.random.default_rng(seed)
+    idx = np.full((w.batch, topk), -1, dtype=np.int32)
+    ps = w.page_size
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        n = min(L, topk)
+        if n == 0:
+            continue
+        t = rng.choice(L, size=n, replace=False)
+        idx[b, :n] = w.block_table[b, t // ps].astype(np.int64) * ps + t % ps
+    return idx
+
+
 def _slots_of_pages(used_pages: np.ndarray, fill: np.ndarray, ps: int) -> np.ndarray:
     """Slots p*ps + [0, fill[p]) for every page p in used_pages, ascending."""
     if used_pages.size == 0:
@@ -368,6 +388,12 @@ BENCH_SCHEDULE = {
 # where every row is read once per step; cached loads for the high-slot batch, whose requests
 # share pages (12,058 pages above the wrap slot for about 47,500 page reads), so repeated rows
 # can hit in the L2 and last-level cache.
+# Sparse decode step of the benchmark (--op sparse): every request's newest token attends to
+# SPARSE_TOPK slots of its own context (sparse_lists).  The pages do not give the list length;
+# 2048 is the top-k of the published sparse-attention MLA models, used here as the reading.
+SPARSE_TOPK = 2048
+SPARSE_SPLITS = {"batched": 4, "long_context": 64, "high_slot": 4, "fp8_ragged": 4, "tiny": 1}
+
 BENCH_ROW_LOADS = {
     "tiny": "streaming",
     "batched": "streaming",
