@@ -443,35 +443,52 @@ __device__ __forceinline__ void finish_rows(uint8_t* smem, const f32x4 (&O)[TF::
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < R * (kOut / 4); idx += kWaves * 64) {
-    const int r = idx / (kOut / 4);
-    const int d4 = idx % (kOut / 4);
+  // Thread t merges row r = t / 16 (+ 16 per pass) at float4 columns t % 16 + 16 j: the row's
+  // weights are formed once, every LDS read of a pass is independent of the others (no chain
+  // of waits), and 16 lanes store 256 contiguous bytes of a row.  Row r's states are those of
+  // the kWaves / G waves gg + G i, gg = r / 16, taken in that order.
+  constexpr int kPer = kWaves / G;        // waves holding a row group's states
+  constexpr int kCols = kOut / 4 / 16;    // float4 columns per thread and row
+  const int t = threadIdx.x;
+  for (int r = t / 16; r < R; r += kWaves * 64 / 16) {
     const int gg = r / 16;
     const int mm = r % 16;
     // first O column of this row's output (GLA-g2: its head group's half)
     const int c0 = kGla2 ? ((r % H) >= H / 2 ? 256 : 0) : 0;
+    float mw[kPer], lw[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      mw[i] = red_m[(gg + G * i) * kMaxHeads + mm];
+      lw[i] = red_l[(gg + G * i) * kMaxHeads + mm];
+    }
     float M = -INFINITY;
 #pragma unroll
-    for (int w = gg; w < kWaves; w += G) M = fmaxf(M, red_m[w * kMaxHeads + mm]);
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kPer; ++i) M = fmaxf(M, mw[i]);
+    const bool live = M != -INFINITY;
+    float f[kPer];
     float lsum = 0.f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int w = gg; w < kWaves; w += G) {
-        const float f = fast_exp2(red_m[w * kMaxHeads + mm] - M);
-        lsum += f * red_l[w * kMaxHeads + mm];
-        o += f * *(const f32x4*)(red + (w * kMaxHeads + mm) * kRedStride + c0 + 4 * d4);
-      }
-      o *= 1.0f / lsum;  // a NaN score anywhere made lsum NaN: NaN out
-    } else {
-      // No finite score.  The running maxima ignore NaN scores, but the sums do not: they
-      // are 0 for an empty partition, giving (+0, -inf), and NaN when every score was NaN.
-#pragma unroll
-      for (int w = gg; w < kWaves; w += G) lsum += red_l[w * kMaxHeads + mm];
-      o *= lsum;
+    for (int i = 0; i < kPer; ++i) {
+      f[i] = live ? fast_exp2(mw[i] - M) : 0.f;
+      // No finite score: the running maxima ignore NaN scores, but the sums do not: they are 0
+      // for an empty partition, giving (+0, -inf), and NaN when every score was NaN.
+      lsum += live ? f[i] * lw[i] : lw[i];
     }
-    *(f32x4*)(out + (int64_t)r * kOut + 4 * d4) = o;
-    if (d4 == 0) lse[r] = (M == -INFINITY) ? -INFINITY + lsum : (M + fast_log2(lsum)) * 0.69314718055994530942f;
+    // a NaN score anywhere made lsum NaN: NaN out
+    const float scale = live ? 1.0f / lsum : lsum;
+    const float* src = red + (gg * kMaxHeads + mm) * kRedStride + c0 + 4 * (t % 16);
+    float* dst = out + (int64_t)r * kOut + 4 * (t % 16);
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) o += f[i] * *(const f32x4*)(src + G * i * kMaxHeads * kRedStride + 64 * j);
+      }
+      o *= scale;
+      *(f32x4*)(dst + 64 * j) = o;
+    }
+    if (t % 16 == 0) lse[r] = (M == -INFINITY) ? -INFINITY + lsum : (M + fast_log2(lsum)) * 0.69314718055994530942f;
   }
 }
 
