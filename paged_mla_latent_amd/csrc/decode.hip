@@ -1487,20 +1487,31 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_sparse_kernel(DecodePar
 // (no planning launch, no dependent global reads before its first tile); workgroup 0 also
 // stores v for the merge.  A slot holds the R = q_len x heads query rows of its request (G row
 // groups of 16, as in decode_kernel).
+// LDS of the axis v [kMaxBalancedBatch + 1] (and the scan's per-wave totals) when it is kept apart
+// from the tile memory for the whole launch.
+constexpr int kAxisBytes = (kWaves + kMaxBalancedBatch + 1) * 8;
+template <class Fmt, int G>
+constexpr bool kAxisApart = kernel_smem_bytes<Fmt, G>() + kAxisBytes <= 160 * 1024;
+
 template <class Fmt, int G>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kernel_smem_bytes<Fmt, G>()];
+  constexpr int kTileMem = kernel_smem_bytes<Fmt, G>();
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kTileMem + (kAxisApart<Fmt, G> ? kAxisBytes : 0)];
   const int B = p.batch;
   uint32_t lbad = 0;  // checked build: a length outside [0, bt_stride * page_size]
   auto cost = [&](int r) -> int64_t {
     const int64_t L = checked_len(p.seq_lens[r], p.bt_stride, p.page_size, lbad);
     return L > 0 ? L + kSegmentCost : 0;
   };
-  // The axis v [B + 1] is scanned into the tile memory, which the segments only use after it;
-  // each workgroup then keeps the start of its first request and walks forward from there.
-  static_assert(kernel_smem_bytes<Fmt, G>() >= (kWaves + kMaxBalancedBatch + 1) * 8, "axis scratch");
-  int64_t* v_s = (int64_t*)smem + kWaves;
-  scan_requests<int64_t>(B, cost, v_s, (int64_t*)smem);
+  // The axis v [B + 1] is scanned into LDS; each workgroup then keeps the start of its first
+  // request and walks forward from there.  Where the LDS has room the axis stays apart from the
+  // tile memory and the walk reads the next request's end from it; otherwise it is scanned into
+  // the tile memory (used by the segments only after the scan) and the walk reads the lengths
+  // again.
+  static_assert(kTileMem >= kAxisBytes, "axis scratch");
+  int64_t* axis = (int64_t*)(smem + (kAxisApart<Fmt, G> ? kTileMem : 0));
+  int64_t* v_s = axis + kWaves;
+  scan_requests<int64_t>(B, cost, v_s, axis);
   report_checks(lbad, p.check_status);
   if (blockIdx.x == 0)
     for (int b = threadIdx.x; b <= B; b += kWaves * 64) p.cu[b] = v_s[b];
@@ -1519,7 +1530,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
   __syncthreads();  // the scratch is tile memory from here on
   const int R = p.q_len * p.heads;
   for (int b = bl; b < B; ++b) {
-    const int64_t v1 = v0 + cost(b);
+    const int64_t v1 = kAxisApart<Fmt, G> ? v_s[b + 1] : v0 + cost(b);
     if (v0 >= hi) break;
     if (v1 <= lo || v1 == v0) {  // empty requests have no partial
       v0 = v1;
