@@ -920,11 +920,19 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
 // same way: its owner wave publishes alpha for its rows and a flag, and every wave scales its
 // accumulators of that row group before adding the step.
 //
+// fp8 rows score with the K dimension split as well: the waves pair up by row half (waves 2h
+// and 2h + 1 own row groups 2h and 2h + 1) and each wave of a pair takes one half of the row
+// (latent blocks 2k and 2k + 1 and rope values [32k, 32k + 32) for wave 2h + k) for both row
+// groups of its half.  A code is then widened once per row half instead of once per row group,
+// and each wave reads half of every tile for its scores.  The partial scores of the partner's
+// row group go through LDS (in the slot that then carries that row group's P), a barrier, and
+// every owner adds them to its own partial: three barriers per step instead of two.
+//
 // Per step: each wave waits for its own tile, a barrier makes the four tiles (and the end of
-// the previous step) visible, the next tiles are requested, the owner waves score, rescale and
-// publish P, a second barrier, then every wave reads the four row groups' P and accumulates its
-// columns.  The owner of row group r keeps its running maximum and sum; the epilogue publishes
-// them and every wave writes its columns of every row.
+// the previous step) visible, the next tiles are requested, the owner waves score (fp8: the
+// pairs exchange partial scores), rescale and publish P, a barrier, then every wave reads the
+// four row groups' P and accumulates its columns.  The owner of row group r keeps its running
+// maximum and sum; the epilogue publishes them and every wave writes its columns of every row.
 // ------------------------------------------------------------------------------------
 template <class Fmt>
 struct ColSplit {
@@ -1020,6 +1028,80 @@ __device__ __forceinline__ void score_tiles(const uint8_t* t0, const uint8_t* t1
   }
 }
 
+// fp8 partial scores of two 16-row groups (own, partner) over four tiles and one half of the
+// row: latent blocks 2 kh and 2 kh + 1 (each block's partial scaled by its block scale, from the
+// transposed table sct) plus rope values [32 kh, 32 kh + 32).  qo / qp: the own / partner rows'
+// q fragments, [0, 8) the half's eight latent K-steps, [8] its rope K-step.  Each widened code
+// feeds both row groups' MFMAs.  A block's LDS reads (16 code fragments, its 4 scale vectors;
+// block 1 also the rope) are all issued before its first MFMA, so that one LDS latency is
+// exposed per block instead of one per read.  between() runs after block 0's MFMAs are issued
+// (the next tile's loads are requested there, while those MFMAs execute).
+template <class Between>
+__device__ __forceinline__ void score_tiles_half(const uint8_t* const (&tile)[4], const uint8_t* sct, int m, int g,
+                                                 int kh, const u32x4* qo, const u32x4* qp, f32x4 (&po)[4],
+                                                 f32x4 (&pp)[4], Between&& between) {
+  using F = Fp8Rows<64>;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) po[v] = pp[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 rope[4];
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    const int k = 2 * kh + bk;  // latent block
+    u32x2 codes[4][4];          // [K-step jj][tile v]: codes 32j + 8g .. + 8 of token m
+    f32x4 sc[4];                // [tile v]: block k's scales of tokens 4g .. 4g + 3
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 4 * k + jj;  // chunk 2j + (g >> 1), half g & 1
+        codes[jj][v] = *(const u32x2*)(tile[v] + F::pos(m, 2 * j + (g >> 1)) + 8 * (g & 1));
+      }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sc[v] = *(const f32x4*)(sct + (16 * (4 * v + k) + 4 * g) * 4);
+    if (bk == 1) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) rope[v] = *(const u32x4*)(tile[v] + F::pos(m, 33 + 4 * kh + g));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 so[4], sp[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) so[v] = sp[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const u32x4 a = F::widen8(codes[jj][v]);
+        so[v] = mfma_16x16x32(a, qo[4 * bk + jj], so[v]);
+        sp[v] = mfma_16x16x32(a, qp[4 * bk + jj], sp[v]);
+      }
+    // Widen the next operand while the current one's two MFMAs run (the matrix core and the
+    // vector ALU work side by side only when the instruction stream alternates them).
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    if (bk == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      between();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        po[v][r] += sc[v][r] * so[v][r];
+        pp[v][r] += sc[v][r] * sp[v][r];
+      }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    po[v] = mfma_16x16x32(rope[v], qo[8], po[v]);
+    pp[v] = mfma_16x16x32(rope[v], qp[8], pp[v]);
+  }
+}
+
 template <class Fmt>
 __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t* smem, int b, int64_t L,
                                                   int64_t t0_abs, int64_t t1_abs, float* out, float* lse) {
@@ -1043,10 +1125,26 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
   const int64_t lim = L - p.q_len + 1 + (row < R ? row / H : 0);
   const int n_vis = (int)(min(rg.t1, lim) - rg.t0);
 
+  // q as the B operand of the QK MFMA: lane (row m, slice g) holds q[row][32j + 8g .. + 8].  bf16:
+  // the own row group's 18 K-steps.  fp8: [0, 9) the own row group's, [9, 18) the partner row
+  // group's K-steps of this wave's half of the row (8 latent, then 1 rope).
+  [[maybe_unused]] const int kh = wave & 1;  // fp8: this wave's half of the row
   u32x4 qf[QS];
 #pragma unroll
   for (int j = 0; j < QS; ++j) qf[j] = u32x4{0u, 0u, 0u, 0u};
-  if (row < R) {
+  if constexpr (CS::kFp8) {
+    static_assert(QS == 18, "two row groups x (8 + 1) K-steps");
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int rr = 16 * (c == 0 ? wave : (wave ^ 1)) + m;
+      if (rr < R) {
+        const uint16_t* qrow = p.q + ((int64_t)b * R + rr) * Fmt::kQDim + 8 * g;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) qf[9 * c + jj] = *(const u32x4*)(qrow + 32 * (8 * kh + jj));
+        qf[9 * c + 8] = *(const u32x4*)(qrow + 512 + 32 * kh);
+      }
+    }
+  } else if (row < R) {
     const uint16_t* qrow = p.q + ((int64_t)b * R + row) * Fmt::kQDim + 8 * g;
 #pragma unroll
     for (int j = 0; j < QS; ++j) qf[j] = *(const u32x4*)(qrow + 32 * j);
@@ -1175,23 +1273,42 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
       ((float*)sct)[16 * (4 * wave + k) + t] = *(const float*)(tile_ptr(i, wave) + Fmt::pos(t, 32) + 4 * k);
     }
     __syncthreads();  // the step's four tiles are visible; every wave is done with step i - 1
-    if (i + NB - 1 < nsteps) {
-      const int s = i + NB - 1;  // into buffer (i - 1) % NB, free since the barrier
-      fetch_page(tile_of_step(min(s + NB - 1, nsteps - 1)), slot_lds(s + NB - 1));
-      if constexpr (Fmt::kFlatTile) {
-        issue_tile_flat(tile_of_step(s), pslot + 256 * (s % NB), buf_lds(s));
-      } else {
-        Pages page_n;
-        read_pages(pslot + 256 * (s % NB), page_n);
-        issue_tile(tile_of_step(s), page_n, buf_lds(s));
+    // The next tiles: into buffer (i - 1) % NB, free since the barrier (fp8: requested between
+    // the two halves of the scores' MFMAs, which execute meanwhile).
+    auto issue_next = [&]() {
+      if (i + NB - 1 < nsteps) {
+        const int s = i + NB - 1;
+        fetch_page(tile_of_step(min(s + NB - 1, nsteps - 1)), slot_lds(s + NB - 1));
+        if constexpr (Fmt::kFlatTile) {
+          issue_tile_flat(tile_of_step(s), pslot + 256 * (s % NB), buf_lds(s));
+        } else {
+          Pages page_n;
+          read_pages(pslot + 256 * (s % NB), page_n);
+          issue_tile(tile_of_step(s), page_n, buf_lds(s));
+        }
       }
-    }
+    };
+    if constexpr (!CS::kFp8) issue_next();
 
     // ---- scores of row group `wave` over the step's four tiles, online softmax, P out.
     // The four tiles are four independent MFMA chains advanced one K-step at a time, so that
     // the LDS reads of the next K-steps can be in flight while a K-step's MFMAs run.
     f32x4 raw[4];
-    score_tiles<Fmt>(tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3), sct, m, g, qf, raw);
+    if constexpr (CS::kFp8) {
+      const uint8_t* const tl[4] = {tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3)};
+      f32x4 part[4];  // the partner row group's partial scores
+      score_tiles_half(tl, sct, m, g, kh, qf, qf + 9, raw, part, issue_next);
+      // the partner's partial goes to its row group's slot (where its P goes next); ours arrives
+      f32x4* xo = (f32x4*)pex + ((wave ^ 1) * 4) * 64 + lane;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xo[64 * v] = part[v];
+      __syncthreads();
+      const f32x4* xi = (const f32x4*)pex + (wave * 4) * 64 + lane;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) raw[v] += xi[64 * v];
+    } else {
+      score_tiles<Fmt>(tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3), sct, m, g, qf, raw);
+    }
     float sc[4][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -1251,25 +1368,42 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
       const uint8_t* ta = tile_ptr(i, 2 * j);
       const uint8_t* tb = tile_ptr(i, 2 * j + 1);
       if constexpr (CS::kFp8) {
-        // scale of block `wave` for this lane's tokens 4g .. 4g + 3 of tiles a and b
+        // All LDS reads of the tile pair first (one exposed latency): the scales of block `wave`
+        // for this lane's tokens 4g .. 4g + 3 of tiles a and b, the four row groups' P, and the
+        // codes of block `wave` (A operand: lanes v < 4 read tile a, v >= 4 tile b, as
+        // Fp8Rows::pv2 does).
         const f32x4 sa = *(const f32x4*)(sct + (16 * (4 * (2 * j) + wave) + 4 * g) * 4);
         const f32x4 sb = *(const f32x4*)(sct + (16 * (4 * (2 * j + 1) + wave) + 4 * g) * 4);
-        u32x4 bp[4];
+        f32x4 pa[4], pb[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const f32x4 pa = ((const f32x4*)pex)[(r * 4 + 2 * j) * 64 + lane];
-          const f32x4 pb = ((const f32x4*)pex)[(r * 4 + 2 * j + 1) * 64 + lane];
-          bp[r] = u32x4{pack_bf16(pa[0] * sa[0], pa[1] * sa[1]), pack_bf16(pa[2] * sa[2], pa[3] * sa[3]),
-                        pack_bf16(pb[0] * sb[0], pb[1] * sb[1]), pack_bf16(pb[2] * sb[2], pb[3] * sb[3])};
+          pa[r] = ((const f32x4*)pex)[(r * 4 + 2 * j) * 64 + lane];
+          pb[r] = ((const f32x4*)pex)[(r * 4 + 2 * j + 1) * 64 + lane];
         }
-        // A operand: lanes v < 4 read tile a, v >= 4 tile b (Fp8Rows::pv2), chunks of block `wave`
         const int v = m >> 1, h = m & 1;
         const uint8_t* src = (v < 4 ? ta : tb) + 8 * h + Fmt::pos(4 * g + (v & 3), 8 * wave);
+        u32x2 cw[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) cw[c] = lds_read_tr8(src + 16 * c);
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 bp[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          bp[r] = u32x4{pack_bf16(pa[r][0] * sa[0], pa[r][1] * sa[1]), pack_bf16(pa[r][2] * sa[2], pa[r][3] * sa[3]),
+                        pack_bf16(pb[r][0] * sb[0], pb[r][1] * sb[1]), pack_bf16(pb[r][2] * sb[2], pb[r][3] * sb[3])};
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const u32x4 a = Fmt::widen_tr8(lds_read_tr8(src + 16 * c));
+          const u32x4 a = Fmt::widen_tr8(cw[c]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) O[8 * r + c] = mfma_16x16x32(a, bp[r], O[8 * r + c]);
+        }
+        // P products and the first operand, then each operand's four MFMAs beside the next
+        // operand's widening
+        __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
       } else {
         u32x4 bp[4];
@@ -1320,11 +1454,10 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
   report_checks(bad, p.check_status);
 }
 
-// Rows that take the column-split verify step (four row groups).  fp8 rows keep the shared
-// widened tiles of decode_segment: scored from the raw codes, every row group widens every code
-// again (four times the conversions), measured slower (fp8-ragged, q_len 4: 229 against 204 us).
+// Rows that take the column-split verify step (four row groups).
 template <class Fmt, int G>
-constexpr bool kColSplit = G == 4 && std::is_same<Fmt, Bf16Rows<512, 64>>::value;
+constexpr bool kColSplit = G == 4 && (std::is_same<Fmt, Bf16Rows<512, 64>>::value ||
+                                      std::is_same<Fmt, Fp8Rows<64>>::value);
 
 template <class Fmt, int G>
 constexpr int kernel_smem_bytes() {
