@@ -89,6 +89,13 @@ struct Bf16Rows {
       for (int j = 0; j < kDmaOps; ++j) dma16(rows[j & 1] + 128 * (j >> 1) + cv, dst + 1024 * j);
     }
   }
+  // Instruction j of issue() alone.
+  __device__ static __forceinline__ void issue_one(const uint8_t* const (&rows)[2], uint32_t dst, int lane, bool nt,
+                                                   int j) {
+    const int cv = 16 * ((lane & 7) ^ line_swz(lane >> 3));
+    if (nt) dma16_nt(rows[j & 1] + 128 * (j >> 1) + cv, dst + 1024 * j);
+    else dma16(rows[j & 1] + 128 * (j >> 1) + cv, dst + 1024 * j);
+  }
 
   // K-step j reads chunk 4j + g of token m (the A operand: token m, values 32j + 8g ..), at
   // line_pos(m, 4 (j & 1) + g) + 128 (j >> 1).
@@ -952,79 +959,36 @@ struct ColSplit {
   static_assert(kBytes <= 160 * 1024, "column-split verify step fits in the LDS");
 };
 
-// Scores of one 16-row group over four tiles: raw[v] = A(tile v) x q^T, as Fmt::qk computes
-// them, with the four tiles' MFMA chains interleaved K-step by K-step.
-template <class Fmt>
+// bf16 scores of one 16-row group over four tiles: raw[v] = A(tile v) x q^T, as Bf16Rows::qk
+// computes them, with the four tiles' MFMA chains interleaved K-step by K-step.  between(j) runs
+// after K-step j's four MFMAs are issued: the next tile's loads go out one instruction per
+// K-step there, spread over the MFMAs, instead of holding all four waves in a burst of
+// vector-memory instructions right after the step's barrier.
+template <class Fmt, class Between>
 __device__ __forceinline__ void score_tiles(const uint8_t* t0, const uint8_t* t1, const uint8_t* t2,
-                                            const uint8_t* t3, const uint8_t* sct, int m, int g, const u32x4* qf,
-                                            f32x4 (&raw)[4]) {
+                                            const uint8_t* t3, int m, int g, const u32x4* qf, f32x4 (&raw)[4],
+                                            Between&& between) {
+  static_assert(!Fmt::kFlatTile, "bf16 line-layout tiles");
   const uint8_t* const tile[4] = {t0, t1, t2, t3};
-  if constexpr (std::is_same<Fmt, Fp8Rows<64>>::value) {
-    // K-step j: codes 32j + 8g .. + 8 of token m (chunk 2j + (g >> 1), half g & 1), widened
-    // exactly; per 128-value block k the partial score is scaled by that block's scale (fp32),
-    // read for the lane's tokens 4g .. 4g + 3 from the transposed table sct ([tile][block][token]).
+  // line layout: K-step j reads chunk 4 (j & 1) + g of token m, plus 128 (j >> 1) chunks
+  const int o0 = 16 * line_pos(m, g), o1 = 16 * line_pos(m, 4 + g);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) raw[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int v = 0; v < 4; ++v) raw[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // K-step j's four A operands in a[j % 3], read two K-steps ahead (eight reads in flight: with
+  // one wave per SIMD, fewer leave the LDS latency exposed before the MFMAs)
+  auto read = [&](int j, u32x4 (&dst)[4]) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      f32x4 sk[4];
+    for (int v = 0; v < 4; ++v) dst[v] = *(const u32x4*)(tile[v] + ((j & 1) ? o1 : o0) + 1024 * (j & ~1));
+  };
+  u32x4 a[3][4];
+  read(0, a[0]);
+  read(1, a[1]);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sk[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < Fmt::kQSteps; ++j) {
+    if (j + 2 < Fmt::kQSteps) read(j + 2, a[(j + 2) % 3]);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = 4 * k + jj;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const u32x2 codes = *(const u32x2*)(tile[v] + Fmt::pos(m, 2 * j + (g >> 1)) + 8 * (g & 1));
-          sk[v] = mfma_16x16x32(Fmt::widen8(codes), qf[j], sk[v]);
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const f32x4 sc = *(const f32x4*)(sct + (16 * (4 * v + k) + 4 * g) * 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) raw[v][r] += sc[r] * sk[v][r];
-      }
-    }
-    f32x4 sr[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sr[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jr = 0; jr < 2; ++jr)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        sr[v] = mfma_16x16x32(*(const u32x4*)(tile[v] + Fmt::pos(m, 33 + 4 * jr + g)), qf[16 + jr], sr[v]);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) raw[v] += sr[v];
-    // 64 code reads + 16 scale reads + 8 rope reads, 72 MFMAs: kAhead reads ahead (see below)
-    constexpr int kAhead = 8;
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-    for (int n = 0; n < 72; ++n) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  } else {
-    // line layout: K-step j reads chunk 4 (j & 1) + g of token m, plus 128 (j >> 1) chunks
-    const int o0 = 16 * line_pos(m, g), o1 = 16 * line_pos(m, 4 + g);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) raw[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < Fmt::kQSteps; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        raw[v] = mfma_16x16x32(*(const u32x4*)(tile[v] + ((j & 1) ? o1 : o0) + 1024 * (j & ~1)), qf[j], raw[v]);
-    // Order: kAhead LDS reads first, then one MFMA per further read, so that kAhead reads are
-    // always in flight (left alone, the scheduler keeps one or two, and one wave per SIMD
-    // then waits out the LDS latency before nearly every MFMA).
-    constexpr int kN = 4 * Fmt::kQSteps, kAhead = 8;
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-    for (int n = 0; n < kN - kAhead; ++n) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+    for (int v = 0; v < 4; ++v) raw[v] = mfma_16x16x32(a[j % 3][v], qf[j], raw[v]);
+    between(j);
   }
 }
 
@@ -1035,7 +999,8 @@ __device__ __forceinline__ void score_tiles(const uint8_t* t0, const uint8_t* t1
 // feeds both row groups' MFMAs.  A block's LDS reads (16 code fragments, its 4 scale vectors;
 // block 1 also the rope) are all issued before its first MFMA, so that one LDS latency is
 // exposed per block instead of one per read.  between() runs after block 0's MFMAs are issued
-// (the next tile's loads are requested there, while those MFMAs execute).
+// (the next tile's loads are requested there, while those MFMAs execute; spread a few at a time
+// over the K-steps instead, as the bf16 scores do, they measured slower here).
 template <class Between>
 __device__ __forceinline__ void score_tiles_half(const uint8_t* const (&tile)[4], const uint8_t* sct, int m, int g,
                                                  int kh, const u32x4* qo, const u32x4* qp, f32x4 (&po)[4],
@@ -1273,22 +1238,41 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
       ((float*)sct)[16 * (4 * wave + k) + t] = *(const float*)(tile_ptr(i, wave) + Fmt::pos(t, 32) + 4 * k);
     }
     __syncthreads();  // the step's four tiles are visible; every wave is done with step i - 1
-    // The next tiles: into buffer (i - 1) % NB, free since the barrier (fp8: requested between
-    // the two halves of the scores' MFMAs, which execute meanwhile).
-    auto issue_next = [&]() {
-      if (i + NB - 1 < nsteps) {
+    // The next tiles: into buffer (i - 1) % NB, free since the barrier, requested while the
+    // scores' MFMAs execute (a burst of vector-memory instructions right after the barrier held
+    // all four waves for about a microsecond per step).  bf16: the page ids of a later step and
+    // the rows' addresses now, the row loads one instruction per K-step of the scores.
+    const bool have_next = i + NB - 1 < nsteps;
+    const uint8_t* next_rows[TPL];
+    if constexpr (!CS::kFp8) {
+      if (have_next) {
         const int s = i + NB - 1;
         fetch_page(tile_of_step(min(s + NB - 1, nsteps - 1)), slot_lds(s + NB - 1));
-        if constexpr (Fmt::kFlatTile) {
+        Pages page_n;
+        read_pages(pslot + 256 * (s % NB), page_n);
+#pragma unroll
+        for (int t = 0; t < TPL; ++t) {
+          const uint32_t tok = clamp_token(tile_of_step(s), Fmt::fetch_token(lane, t));
+          next_rows[t] = p.cache + ((int64_t)page_n[t] * (int64_t)ps + (int64_t)(tok % ps)) * (int64_t)Fmt::kRowBytes;
+        }
+      }
+    }
+    // bf16: one row-load instruction after each K-step of the scores.
+    auto dma_part = [&](int j) {
+      if constexpr (!CS::kFp8) {
+        if (have_next) Fmt::issue_one(next_rows, buf_lds(i + NB - 1), lane, p.stream_rows != 0, j);
+      }
+    };
+    // fp8: the whole tile between the two halves of the scores.
+    auto issue_next_fp8 = [&]() {
+      if constexpr (CS::kFp8) {
+        if (have_next) {
+          const int s = i + NB - 1;
+          fetch_page(tile_of_step(min(s + NB - 1, nsteps - 1)), slot_lds(s + NB - 1));
           issue_tile_flat(tile_of_step(s), pslot + 256 * (s % NB), buf_lds(s));
-        } else {
-          Pages page_n;
-          read_pages(pslot + 256 * (s % NB), page_n);
-          issue_tile(tile_of_step(s), page_n, buf_lds(s));
         }
       }
     };
-    if constexpr (!CS::kFp8) issue_next();
 
     // ---- scores of row group `wave` over the step's four tiles, online softmax, P out.
     // The four tiles are four independent MFMA chains advanced one K-step at a time, so that
@@ -1297,7 +1281,7 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
     if constexpr (CS::kFp8) {
       const uint8_t* const tl[4] = {tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3)};
       f32x4 part[4];  // the partner row group's partial scores
-      score_tiles_half(tl, sct, m, g, kh, qf, qf + 9, raw, part, issue_next);
+      score_tiles_half(tl, sct, m, g, kh, qf, qf + 9, raw, part, issue_next_fp8);
       // the partner's partial goes to its row group's slot (where its P goes next); ours arrives
       f32x4* xo = (f32x4*)pex + ((wave ^ 1) * 4) * 64 + lane;
 #pragma unroll
@@ -1307,7 +1291,7 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
 #pragma unroll
       for (int v = 0; v < 4; ++v) raw[v] += xi[64 * v];
     } else {
-      score_tiles<Fmt>(tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3), sct, m, g, qf, raw);
+      score_tiles<Fmt>(tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3), m, g, qf, raw, dma_part);
     }
     float sc[4][4];
     float mx = -INFINITY;
