@@ -1614,6 +1614,11 @@ template <class Fmt, int G>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParams p) {
   constexpr int kTileMem = kernel_smem_bytes<Fmt, G>();
   __shared__ __attribute__((aligned(16))) uint8_t smem[kTileMem + (kAxisApart<Fmt, G> ? kAxisBytes : 0)];
+  // The grid size lives in another line of the kernel arguments than the fields read first: read
+  // it here, with them, rather than after the scan, where its load would wait out a trip to
+  // memory before the workgroup can find its range.
+  const uint32_t grid_w = gridDim.x;
+  asm volatile("" ::"s"(grid_w));
   const int B = p.batch;
   uint32_t lbad = 0;  // checked build: a length outside [0, bt_stride * page_size]
   auto cost = [&](int r) -> int64_t {
@@ -1634,7 +1639,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
     for (int b = threadIdx.x; b <= B; b += kWaves * 64) p.cu[b] = v_s[b];
 
   const int64_t V = v_s[B];
-  const int64_t W = min((int64_t)gridDim.x, V);
+  const int64_t W = min((int64_t)grid_w, V);
   const int64_t w = blockIdx.x;
   if (w >= W) return;  // uniform over the workgroup
   const int64_t lo = flat_begin(V, W, w), hi = flat_begin(V, W, w + 1);
