@@ -478,7 +478,8 @@ MLA_API int mla_cache_write(const void* latent, const void* k_pe, const int64_t*
  * reading; the pages name the operation, not its rounding); rope values as stored.
  * cu_rows    int64 [batch + 1], cu_rows[0] = 0, non-decreasing, cu_rows[batch] = total_rows.
  * seq_starts int32 [batch], first context position to gather per request, or NULL for 0.
- * total_rows passed by the caller (the library never reads device memory on the host).
+ * total_rows passed by the caller (the library never reads device memory on the host),
+ *            0 .. 2^32.
  * Preconditions (not checkable without reading device memory): the cu_rows layout above;
  * seq_starts[b] + rows of b <= block_table_stride * page_size; the block-table entries
  * those tokens use lie in [0, num_pages).  total_rows == 0 launches nothing.

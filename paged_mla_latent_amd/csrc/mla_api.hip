@@ -742,8 +742,8 @@ int mla_gather_context(const void* kv_cache, int32_t cache_format, int64_t num_p
   if (cache_format != MLA_CACHE_BF16_576 && cache_format != MLA_CACHE_FP8_656)
     return fail(MLA_ERR_SHAPE, "%s: cache_format=%d unknown", fn, cache_format);
   if (total_rows < 0) return fail(MLA_ERR_SHAPE, "%s: total_rows=%lld is negative", fn, (long long)total_rows);
-  if (total_rows > ((int64_t)1 << 36))
-    return fail(MLA_ERR_SHAPE, "%s: total_rows=%lld exceeds 2^36", fn, (long long)total_rows);
+  if (total_rows > ((int64_t)1 << 32))  // bf16 output alone would be 4.9 TB; keeps the grid below 2^31
+    return fail(MLA_ERR_SHAPE, "%s: total_rows=%lld exceeds 2^32", fn, (long long)total_rows);
   if (batch < 1) return fail(MLA_ERR_SHAPE, "%s: batch=%d must be >= 1", fn, batch);
   if (num_pages < 1) return fail(MLA_ERR_SHAPE, "%s: num_pages=%lld must be >= 1", fn, (long long)num_pages);
   if (page_size < 1) return fail(MLA_ERR_SHAPE, "%s: page_size=%d must be >= 1", fn, page_size);

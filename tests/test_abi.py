@@ -312,7 +312,7 @@ def test_gather_validation(lib):
         return f(a["kv"], a["fmt"], a["pages"], a["ps"], a["bt"], a["stride"], a["cu"], a["st"], a["batch"],
                  a["total"], a["out"], a.get("cs"), None), lib.mla_last_error_message().decode()
     for kw, rc, word in [(dict(fmt=5), 2, "cache_format"), (dict(total=-1), 2, "total_rows"),
-                         (dict(total=1 << 40), 2, "total_rows"), (dict(batch=0), 2, "batch"),
+                         (dict(total=1 << 40), 2, "total_rows"), (dict(total=(1 << 32) + 1), 2, "total_rows"), (dict(batch=0), 2, "batch"),
                          (dict(pages=0), 2, "num_pages"), (dict(ps=0), 2, "page_size"), (dict(stride=0), 2, "stride"),
                          (dict(kv=None), 1, "kv_cache"), (dict(cu=None), 1, "cu_rows"), (dict(out=None), 1, "out"),
                          (dict(bt=None), 1, "block_table"), (dict(st=MIS), 3, "aligned"), (dict(cu=MIS), 3, "aligned")]:
