@@ -103,27 +103,50 @@ def _copy_calibration(mib: int):
 LLC_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 
 
-def _read_ceiling(dev, stream, gib=2, reps=20):
-    """Same-run streaming-read ceiling: median HIP-event time of a read-only reduction (torch
-    amax) over `gib` GiB of fp32, i.e. what this machine streams from HBM with a plain kernel that
-    reads every byte once."""
+def _read_ceiling(dev, stream, gib=2, reps=20, workgroups=2048):
+    """Same-run streaming-read reference: median HIP-event time of `mla_bench_stream_read`
+    (libmla_bench.so: every 16-byte word of a `gib` GiB buffer read once by a grid-stride walk,
+    eight loads in flight per thread), with plain loads and with the non-temporal hint; `gbs`
+    is the faster of the two.  This is what this machine streams from HBM with a kernel that does
+    nothing but read."""
+    import ctypes
     import torch
-    buf = torch.ones(gib << 28, dtype=torch.float32, device=dev)
-    for _ in range(3):
-        buf.amax()
-    times = []
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        buf.amax()
-        b.record(stream)
-        times.append((a, b))
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in times]))
-    del buf
-    gbs = (gib << 30) / (ms * 1e-3) / 1e9
-    return {"gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "how": f"torch amax over {gib} GiB of fp32, median of {reps} HIP-event windows"}
+    from paged_mla_latent_amd.build import BENCH_LIB_PATH
+    if not os.path.exists(BENCH_LIB_PATH):
+        raise SystemExit(f"bench.py: {BENCH_LIB_PATH} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(BENCH_LIB_PATH)
+    lib.mla_bench_stream_read.restype = ctypes.c_int
+    lib.mla_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_void_p]
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(4 * workgroups, dtype=torch.int32, device=dev)
+
+    def run(nt):
+        rc = lib.mla_bench_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                       workgroups, nt, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"mla_bench_stream_read failed ({rc})")
+
+    rates = {}
+    for nt in (0, 1):
+        for _ in range(3):
+            run(nt)
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run(nt)
+            b.record(stream)
+            times.append((a, b))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in times]))
+        rates["nontemporal" if nt else "plain"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf, sink
+    gbs = max(rates.values())
+    return {"gbs": gbs, "frac": round(gbs / HBM_PEAK_GBS, 4), "gbs_plain": rates["plain"],
+            "gbs_nontemporal": rates["nontemporal"],
+            "how": f"mla_bench_stream_read over {gib} GiB, {workgroups} workgroups, median of {reps} HIP-event windows"}
 
 
 RANKS = {"rank256": 256, "rank768": 768, "rank1792": 1792}

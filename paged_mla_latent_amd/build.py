@@ -4,7 +4,8 @@
     python -m paged_mla_latent_amd.build --release  # libmla.so only
 
 Object files go to paged_mla_latent_amd/_build/ (_build_checked/), the libraries to
-paged_mla_latent_amd/libmla.so and libmla_checked.so.  The checked build compiles the same
+paged_mla_latent_amd/libmla.so and libmla_checked.so; the measurement helper of bench.py (a
+streaming-read reference kernel, include/mla_bench.h) to libmla_bench.so.  The checked build compiles the same
 sources with -DMLA_CHECKED: its kernels test the decode preconditions (block ids inside the
 pool, lengths inside the block table) before forming any address.  Every call recompiles.
 """
@@ -23,6 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libmla.so")
 CHECKED_LIB_PATH = os.path.join(HERE, "libmla_checked.so")
 SOURCES = ["mla_api.hip", "decode.hip", "decode_wide.hip", "merge.hip", "cache_write.hip", "gather.hip"]
+BENCH_LIB_PATH = os.path.join(HERE, "libmla_bench.so")
+BENCH_SOURCE = "bench_read.hip"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -63,12 +66,15 @@ def build(verbose: bool = False, checked: bool = True) -> str:
     variants = [False, True] if checked else [False]
     plans = {v: _jobs(v) for v in variants}
     cmds = [c for v in variants for c in plans[v][1]]
+    bench_obj = os.path.join(HERE, "_build", os.path.splitext(BENCH_SOURCE)[0] + ".o")
+    cmds.append([HIPCC, *COMMON, "-c", os.path.join(CSRC, BENCH_SOURCE), "-o", bench_obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
     for v in variants:
         _link(plans[v][0], CHECKED_LIB_PATH if v else LIB_PATH)
+    _link([bench_obj], BENCH_LIB_PATH)
     return LIB_PATH
 
 

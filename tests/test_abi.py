@@ -501,3 +501,25 @@ def test_binding_marshalling_errors_without_device():
         mla.mla_decode_bf16(q, q, torch.zeros(1, 1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32), 0.1)
     with pytest.raises(TypeError, match="bfloat16"):
         mla.mla_decode_bf16(q.float(), q, None, None, 0.1)
+
+
+def test_bench_helper_library_exports_its_header():
+    """libmla_bench.so (bench.py's streaming-read reference) exports exactly what
+    include/mla_bench.h declares, and validates its arguments before any launch."""
+    import subprocess
+    from paged_mla_latent_amd.build import BENCH_LIB_PATH
+    if not os.path.exists(BENCH_LIB_PATH):
+        pytest.fail("libmla_bench.so is not built (run __graft_entry__.build())")
+    text = open(os.path.join(ROOT, "include", "mla_bench.h")).read()
+    declared = re.findall(r"MLA_BENCH_API\s+[\w\s\*]+?\b(mla_\w+)\s*\(", text)
+    out = subprocess.run(["nm", "-D", "--defined-only", BENCH_LIB_PATH], capture_output=True, text=True).stdout
+    assert sorted(l.split()[-1] for l in out.splitlines() if " T " in l) == sorted(declared) == ["mla_bench_stream_read"]
+    lib = ctypes.CDLL(BENCH_LIB_PATH)
+    fn = lib.mla_bench_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert fn(None, 1024, P, 8, 0, None) == 1
+    assert fn(P, 1024, None, 8, 0, None) == 1
+    for nbytes, wgs in ((0, 8), (8, 8), (1000, 8), (1024, 0), (1024, 65536)):
+        assert fn(P, nbytes, P, wgs, 0, None) == 2
+    assert fn(P + 8, 1024, P, 8, 0, None) == 3 and fn(P, 1024, P + 2, 8, 1, None) == 3
