@@ -367,7 +367,7 @@ BENCH_SPLITS = {
     "batched": 8,
     "long_context": 64,
     "high_slot": 8,
-    "fp8_ragged": 12,
+    "fp8_ragged": 10,
 }
 
 # Workgroups of the batch-balanced decode in the bench's launch configuration (one per
@@ -392,7 +392,7 @@ BENCH_SCHEDULE = {
 # SPARSE_TOPK slots of its own context (sparse_lists).  The pages do not give the list length;
 # 2048 is the top-k of the published sparse-attention MLA models, used here as the reading.
 SPARSE_TOPK = 2048
-SPARSE_SPLITS = {"batched": 8, "long_context": 64, "high_slot": 4, "fp8_ragged": 4, "tiny": 1}
+SPARSE_SPLITS = {"batched": 8, "long_context": 64, "high_slot": 4, "fp8_ragged": 5, "tiny": 1}
 
 BENCH_ROW_LOADS = {
     "tiny": "streaming",
