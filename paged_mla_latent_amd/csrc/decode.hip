@@ -1473,10 +1473,14 @@ __device__ __forceinline__ void scan_requests(int B, F value, T* out, T* scratch
   const int t = threadIdx.x;
   T c[kPer];
   T sum = 0;
+  // value() of an index clamped into [0, B) for every i, so that the loads behind it are issued
+  // together (under a branch per i the compiler waited for each load in turn); the surplus
+  // ones are then dropped.  value() may be called more than once for B - 1.
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) c[i] = value(min(kPer * t + i, B - 1));
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int b = kPer * t + i;
-    c[i] = b < B ? value(b) : T(0);
+    if (kPer * t + i >= B) c[i] = T(0);
     sum += c[i];
   }
   T incl = sum;
