@@ -542,7 +542,8 @@ def _bench_sparse(args):
     torch.cuda.synchronize()
     warm = [e[0].elapsed_time(e[1]) for e in ev]
     merge = [e[1].elapsed_time(e[2]) for e in ev]
-    row_bytes_read = w.row_bytes - (128 if nope and w.fmt == "bf16" else 0)
+    # NoPE rows: the latent part only (bf16: 1,024 bytes; fp8: 512 codes + 16 scale bytes)
+    row_bytes_read = w.row_bytes - (128 if nope else 0)
     valid = int((idx_np >= 0).sum())
     step_bytes = valid * row_bytes_read
     flush_mib = args.flush_mib if args.flush_mib is not None else (1024 if step_bytes < LLC_BYTES else 0)

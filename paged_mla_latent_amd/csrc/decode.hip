@@ -170,16 +170,21 @@ struct Bf16Rows {
 // first 528 bytes of each row, but the whole rows are streamed all the same: those 528-byte
 // pieces are not contiguous across rows, and whole-line streaming of the full rows measured
 // faster than half-line plain loads of the pieces; the rope bytes land in LDS unused.
+// kTrim (NoPE index lists, whose rows are fetched one by one anyway): only the first 528 bytes
+// of each row are fetched, the tile holds 528-byte rows (9 instructions, 9 KB), and the LDS
+// that frees holds a fourth tile per wave.
 // ------------------------------------------------------------------------------------
-template <int kRopeDim>
+template <int kRopeDim, bool kTrim = false>
 struct Fp8Rows {
   static_assert(kRopeDim == 64 || kRopeDim == 0, "rope part: 64 values or none");
+  static_assert(!kTrim || kRopeDim == 0, "trimmed rows: no rope part");
   static constexpr int kLatent = 512;
-  static constexpr int kRowBytes = kRowBytesFp8;
+  static constexpr int kRowBytes = kRowBytesFp8;                   // row stride in the cache
+  static constexpr int kSpan = kTrim ? kLatent + 16 : kRowBytes;  // bytes of a row in a tile
   static constexpr int kQDim = kLatent + kRopeDim;
   static constexpr int kQSteps = kQDim / 32;
-  static constexpr int kDmaOps = (16 * kRowBytes + 1023) / 1024;  // 11 instructions per tile
-  static constexpr int kBufs = 3;  // three tiles per wave with one row group (3 x 4 x 11 KB)
+  static constexpr int kDmaOps = (16 * kSpan + 1023) / 1024;  // 11 instructions per tile (trimmed: 9)
+  static constexpr int kBufs = kTrim ? 4 : 3;  // tiles per wave with one row group (3 x 4 x 11 KB)
   static constexpr int kTileBytes = kDmaOps * 1024;  // used bytes + padding
   static constexpr int kAcc = 32;
 
@@ -188,11 +193,11 @@ struct Fp8Rows {
   };
 
   static constexpr bool kFlatTile = true;        // row-major tiles
-  static constexpr int kChunks = kRowBytes / 16;  // 41 chunks of 16 bytes per row
+  static constexpr int kChunks = kSpan / 16;  // 41 chunks of 16 bytes per row (trimmed: 33)
   static_assert(16 * kChunks == 64 * (kDmaOps - 1) + 16, "the last instruction: 16 chunks");
 
   // Byte offset of chunk c of token t in a tile.
-  __device__ static __forceinline__ int pos(int t, int c) { return t * kRowBytes + 16 * c; }
+  __device__ static __forceinline__ int pos(int t, int c) { return t * kSpan + 16 * c; }
 
   // The tile chunk lane L fetches in instruction j, and its token.
   __device__ static __forceinline__ int tile_chunk(int lane, int j) {
@@ -214,6 +219,7 @@ struct Fp8Rows {
 
   // Row-major tile whose 16 rows are consecutive slots from `tile` on.
   __device__ static __forceinline__ void issue_contiguous(const uint8_t* tile, uint32_t dst, int lane, bool nt) {
+    static_assert(!kTrim, "a trimmed tile is fetched row by row");
     if (nt) {
 #pragma unroll
       for (int j = 0; j < kDmaOps; ++j) dma16_nt(tile + 16 * tile_chunk(lane, j), dst + 1024 * j);
@@ -664,9 +670,13 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
       const uint32_t a = __builtin_amdgcn_readfirstlane(min(t0 + (uint32_t)k * kTile, tlast));
       const uint32_t q0 = __builtin_amdgcn_readfirstlane(a % ps);  // its slot in its page (uniform)
       const bool nt = p.stream_rows != 0;
-      if (!kSparse && a + (kTile - 1) <= tlast && q0 + kTile <= ps) {
-        const int32_t pg = __builtin_amdgcn_readfirstlane(page_id(*(const int32_t*)pids));
-        Fmt::issue_contiguous(p.cache + ((int64_t)pg * ps + q0) * Fmt::kRowBytes, dst, lane, nt);
+      bool whole = false;  // (index lists: never one run)
+      if constexpr (!kSparse) whole = a + (kTile - 1) <= tlast && q0 + kTile <= ps;
+      if (whole) {
+        if constexpr (!kSparse) {
+          const int32_t pg = __builtin_amdgcn_readfirstlane(page_id(*(const int32_t*)pids));
+          Fmt::issue_contiguous(p.cache + ((int64_t)pg * ps + q0) * Fmt::kRowBytes, dst, lane, nt);
+        }
       } else {
         auto row_of = [&](int i) -> const uint8_t* {
           const uint32_t T = (uint32_t)Fmt::fetch_token(lane, i);
@@ -1756,7 +1766,7 @@ hipError_t launch_decode_sparse(const DecodeParams& p, int fp8, int nope, hipStr
   else if (!nope)
     hipLaunchKernelGGL((decode_sparse_kernel<Fp8Rows<64>>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_sparse_kernel<Fp8Rows<0>>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_sparse_kernel<Fp8Rows<0, true>>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
