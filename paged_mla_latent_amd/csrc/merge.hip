@@ -28,6 +28,18 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_out, co
   __shared__ float n_s[kGroups * kCols / 64];
   const int col = blockIdx.y * kCols + (threadIdx.x % kCols);
   const int grp = threadIdx.x / kCols;
+  // This lane's first kPre partials (rows and LSEs) are requested before M is known: they do
+  // not depend on it, so their loads travel with the LSE loads below instead of after them.
+  constexpr int kPre = 8;
+  const float* src = part_out + base * width + 4 * col;
+  f32x4 pre[kPre];
+  float pre_lse[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int p = grp + i * kGroups;
+    pre[i] = p < count ? *(const f32x4*)(src + (int64_t)p * stride * width) : f32x4{0.f, 0.f, 0.f, 0.f};
+    pre_lse[i] = p < count ? part_lse[base + p * stride] : -INFINITY;
+  }
   // M = max_p lse_p: every lane loads a strided share (independent loads), then a
   // wave reduction and a reduction over the waves through LDS.
   // fmaxf skips NaN, so NaN partials are counted apart and force M = NaN.
@@ -57,9 +69,16 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_out, co
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
   if (M != -INFINITY) {
-    const float* src = part_out + base * width + 4 * col;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      if (grp + i * kGroups < count) {
+        const float w = __expf(pre_lse[i] - M);
+        W += w;
+        acc += w * pre[i];
+      }
+    }
 #pragma unroll 4
-    for (int p = grp; p < count; p += kGroups) {
+    for (int p = grp + kPre * kGroups; p < count; p += kGroups) {
       const float w = __expf(part_lse[base + p * stride] - M);
       W += w;
       acc += w * *(const f32x4*)(src + (int64_t)p * stride * width);
