@@ -100,7 +100,8 @@ enum {
 };
 
 enum { MLA_LATENT = 512, MLA_ROPE = 64, MLA_ROW = 576, MLA_MAX_HEADS = 16, MLA_MAX_Q_LEN = 16,
-       MLA_MAX_QUERY_ROWS = 64, MLA_MAX_BALANCED_BATCH = 1024, MLA_MAX_SPARSE_TOKENS = 1 << 20 };
+       MLA_MAX_QUERY_ROWS = 64, MLA_MAX_BALANCED_BATCH = 1024, MLA_MAX_SPARSE_TOKENS = 1 << 20,
+       MLA_MAX_SPARSE_TOPK = 1 << 24 };
 
 /* Bytes of workspace mla_decode_bf16 / mla_decode_fp8_656 need for num_splits
  * partitions: num_splits * batch * num_heads * (512 + 1) * 4 rounded up to 256,
@@ -284,7 +285,7 @@ MLA_API int mla_decode_nope_fp8_656(const void* q, const void* kv_cache, int64_t
  *             nothing gets (+0.0, -inf), the neutral partial of the merge contract.  Entries
  *             >= num_slots break the precondition: the release build reads outside the cache;
  *             the checked build reads slot 0 instead and sets MLA_CHECK_BLOCK_ID.
- * topk        entries per list, >= 1.    num_tokens  1..MLA_MAX_SPARSE_TOKENS.
+ * topk        entries per list, 1..MLA_MAX_SPARSE_TOPK.    num_tokens  1..MLA_MAX_SPARSE_TOKENS.
  * num_heads   1..MLA_MAX_HEADS.
  * num_splits  1..65535: each list is cut into num_splits parts of ceil(topk / num_splits)
  *             entries (trailing parts may be empty), decoded by separate workgroups and

@@ -70,6 +70,7 @@ EXPORTED = (
     "mla_decode_sparse_fp8_656", "mla_decode_sparse_nope_bf16", "mla_decode_sparse_nope_fp8_656",
 )
 MAX_SPARSE_TOKENS = 1 << 20
+MAX_SPARSE_TOPK = 1 << 24
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
 

@@ -392,7 +392,8 @@ int decode_sparse_common(int fp8, int nope, const void* q, const void* kv_cache,
     return fail(MLA_ERR_SHAPE, "%s: num_tokens=%d outside [1, %d]", fn, num_tokens, (int)MLA_MAX_SPARSE_TOKENS);
   if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
     return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_HEADS);
-  if (topk < 1) return fail(MLA_ERR_SHAPE, "%s: topk=%d must be >= 1", fn, topk);
+  if (topk < 1 || topk > MLA_MAX_SPARSE_TOPK)
+    return fail(MLA_ERR_SHAPE, "%s: topk=%d outside [1, %d]", fn, topk, (int)MLA_MAX_SPARSE_TOPK);
   if (num_slots < 1) return fail(MLA_ERR_SHAPE, "%s: num_slots=%lld must be >= 1", fn, (long long)num_slots);
   if (num_splits < 1 || num_splits > 65535)
     return fail(MLA_ERR_SHAPE, "%s: num_splits=%d outside [1, 65535]", fn, num_splits);

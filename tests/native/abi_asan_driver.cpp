@@ -147,6 +147,8 @@ int main() {
            "sparse null q");
     expect(fn(P, P, 100, idx, 0, 3, 16, 0.07f, 1, f, f, nullptr, 0, 0, nullptr, nullptr) == MLA_ERR_SHAPE,
            "sparse topk");
+    expect(fn(P, P, 100, idx, MLA_MAX_SPARSE_TOPK + 1, 3, 16, 0.07f, 1, f, f, nullptr, 0, 0, nullptr, nullptr) ==
+               MLA_ERR_SHAPE, "sparse topk above the limit");
     expect(fn(P, P, 100, idx, 64, MLA_MAX_SPARSE_TOKENS, 16, 0.07f, 65535, f, f, P, 1, 0, nullptr, nullptr) ==
                MLA_ERR_WORKSPACE, "sparse largest workspace");
   }

@@ -446,7 +446,7 @@ def test_sparse_validation(lib, fn):
         rc, msg = _sparse(lib, fn, **{field: None})
         assert rc == 1 and "NULL" in msg and fn in msg, field
     for kw, word in [(dict(tokens=0), "num_tokens"), (dict(tokens=(1 << 20) + 1), "num_tokens"),
-                     (dict(heads=0), "num_heads"), (dict(heads=17), "num_heads"), (dict(topk=0), "topk"),
+                     (dict(heads=0), "num_heads"), (dict(heads=17), "num_heads"), (dict(topk=0), "topk"), (dict(topk=(1 << 24) + 1), "topk"),
                      (dict(num_slots=0), "num_slots"), (dict(splits=0), "num_splits"),
                      (dict(splits=70000), "num_splits"), (dict(scale=float("nan")), "softmax_scale"),
                      (dict(flags=4), "flag")]:
