@@ -36,14 +36,14 @@ int check_device() {
   if (e != hipSuccess || dev < 0)
     return fail(MLA_ERR_ARCH, "no usable HIP device (hipGetDevice: %s)", hipGetErrorString(e));
   if (dev >= kMaxDevices) return fail(MLA_ERR_ARCH, "device index %d exceeds %d", dev, kMaxDevices);
-  int state = g_arch[dev].load(std::memory_order_relaxed);
+  int state = g_arch[dev].load(std::memory_order_acquire);  // pairs with the release below
   if (state == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(MLA_ERR_ARCH, "hipGetDeviceProperties(%d): %s", dev, hipGetErrorString(e));
     state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
     g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
-    g_arch[dev].store(state, std::memory_order_relaxed);
+    g_arch[dev].store(state, std::memory_order_release);  // g_cus is visible once g_arch is
     if (state < 0)
       return fail(MLA_ERR_ARCH, "device %d is %s; this library is built for gfx950 (MI355X) only", dev,
                   prop.gcnArchName);
