@@ -656,6 +656,45 @@ def test_row_load_policies_agree(fmt):
     assert_parity(w, *runs[0][0], ref_o, ref_l, what="streaming loads S=4")
 
 
+def test_calls_in_flight_on_two_streams_do_not_interfere():
+    """The library keeps no state between calls: decodes in flight at once on two streams, with
+    different formats, row-load flags, split counts, schedules and workspaces, give the bits that
+    each gives alone."""
+    wa = workloads.make_workload("streams_a", seq_lens=[3000, 17, 0, 1200], heads=16, page_size=64, num_pages=120,
+                                 fmt="bf16", seed=31)
+    wb = workloads.make_workload("streams_b", seq_lens=[900, 2500, 1], heads=8, page_size=16, num_pages=400,
+                                 fmt="fp8", seed=32)
+    pa, pb = device_pool(wa), device_pool(wb)
+    qa, qb = bf16_dev(wa.q), bf16_dev(wb.q)
+    bta, btb = torch.from_numpy(wa.block_table).cuda(), torch.from_numpy(wb.block_table).cuda()
+    la, lb = torch.from_numpy(wa.seq_lens).cuda(), torch.from_numpy(wb.seq_lens).cuda()
+
+    def call_a():
+        return mla.mla_decode_bf16(qa, pa, bta, la, wa.scale, num_splits=8)
+
+    def call_b():
+        return mla.mla_decode_balanced_fp8_656(qb, pb, btb, lb, wb.scale, num_workgroups=64,
+                                               flags=mla.MLA_FLAG_CACHED_ROWS)
+
+    alone_a, alone_b = call_a(), call_b()
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    runs = []
+    for _ in range(4):
+        with torch.cuda.stream(sa):
+            ra = call_a()
+        with torch.cuda.stream(sb):
+            rb = call_b()
+        runs.append((ra, rb))
+    torch.cuda.synchronize()
+    for ra, rb in runs:
+        for x, y in zip(ra + rb, alone_a + alone_b):
+            assert torch.equal(x, y)
+    ref_o, ref_l = oracle.decode(wa.q, host_pool(wa), wa.block_table, wa.seq_lens, wa.page_size, wa.scale, "bf16")
+    assert_parity(wa, alone_a[0].cpu().numpy().astype(np.float64), alone_a[1].cpu().numpy().astype(np.float64),
+                  ref_o, ref_l, what="two streams, bf16")
+
+
 def test_mtp_single_query_is_plain_decode():
     w = workloads.make_workload("mtp1", seq_lens=[3000, 5, 0, 777], heads=16, page_size=64, num_pages=70, seed=5)
     pd = device_pool(w)
