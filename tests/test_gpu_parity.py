@@ -695,6 +695,61 @@ def test_calls_in_flight_on_two_streams_do_not_interfere():
                   ref_o, ref_l, what="two streams, bf16")
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_decode_step_replays_from_a_hip_graph(fmt):
+    """The calls enqueue kernels only (no allocation when the buffers are given, no
+    synchronisation, no memset): a decode step (cache write, split decode with the library's own
+    merge) captured in a HIP graph gives the eager bits on every replay, with eager work between
+    the replays, and follows its inputs when they change in place."""
+    w = workloads.make_workload("graph_step", seq_lens=[2000, 0, 513, 64], heads=16, page_size=64, num_pages=80,
+                                fmt=fmt, seed=41)
+    pd = device_pool(w)
+    # the step rewrites each live request's newest row (same values) at its slot
+    newest = [int(w.block_table[b, (L - 1) // w.page_size]) * w.page_size + (L - 1) % w.page_size
+              for b, L in enumerate(w.seq_lens) if L > 0]
+    last = np.array([np.nonzero(w.slots == sl)[0][0] for sl in newest])
+    lat, pe, slots = bf16_dev(w.latent[last]), bf16_dev(w.k_pe[last]), torch.from_numpy(w.slots[last]).cuda()
+    q = bf16_dev(w.q)
+    bt, lens = torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    S = 8
+    ws = torch.empty(mla.mla_decode_workspace_size(w.batch, w.heads, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda")
+    fn = mla.mla_decode_bf16 if fmt == "bf16" else mla.mla_decode_fp8_656
+
+    def step():
+        mla.mla_cache_write(lat, pe, slots, pd, FMT_CODE[fmt])
+        fn(q, pd, bt, lens, w.scale, num_splits=S, out=out, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = (out.clone(), lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.fill_(7.0)  # eager work between the replays
+        lse.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[0]) and torch.equal(lse, eager[1])
+    q.mul_(0.5)  # the inputs change in place: the replay reads them anew
+    g.replay()
+    torch.cuda.synchronize()
+    got = (out.clone(), lse.clone())
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], out) and torch.equal(got[1], lse)
+    assert not torch.equal(got[1], eager[1])
+
+
 def test_mtp_single_query_is_plain_decode():
     w = workloads.make_workload("mtp1", seq_lens=[3000, 5, 0, 777], heads=16, page_size=64, num_pages=70, seed=5)
     pd = device_pool(w)
