@@ -91,6 +91,28 @@ def test_split_count_invariance():
     _run_case(w, [1, 2, 7, 64, 200])
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_largest_split_count(fmt):
+    """num_splits = 65,535, the largest the boundary admits, on a short batch: all but a few
+    partitions are empty, the grid (2 x 65,535) is compacted, and the library's counted merge and
+    the caller's merge of all 131,070 kept partials (every empty one written as (0, -inf)) both
+    match the oracle."""
+    S = 65535
+    w = workloads.make_workload("max_splits", seq_lens=[1000, 0], heads=1, page_size=16, num_pages=80, fmt=fmt,
+                                seed=8)
+    pd, ph = device_pool(w), host_pool(w)
+    ref_o, ref_l = oracle.decode(w.q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt)
+    out, lse = gpu_decode(w, pd, S)
+    assert_parity(w, out, lse, ref_o, ref_l, what=f"{fmt} S={S}")
+    fn = mla.mla_decode_bf16 if fmt == "bf16" else mla.mla_decode_fp8_656
+    part_o, part_l = fn(bf16_dev(w.q), pd, torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda(),
+                        w.scale, num_splits=S, partials_only=True)
+    po, pl = mla.mla_merge_lse(part_o, part_l)
+    torch.cuda.synchronize()
+    assert_parity(w, po.cpu().numpy().astype(np.float64), pl.cpu().numpy().astype(np.float64), ref_o, ref_l,
+                  what=f"{fmt} S={S} partials merged by the caller")
+
+
 def test_empty_and_single_token_requests():
     for fmt in ("bf16", "fp8"):
         w = workloads.make_workload("empties", seq_lens=[0, 0, 1, 2, 0], heads=16, page_size=16, num_pages=4,

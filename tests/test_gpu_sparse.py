@@ -108,6 +108,13 @@ def test_sparse_list_length_edges(fmt):
     ref_o, ref_l = oracle.decode_sparse(w.q, ph, idx, w.scale, fmt)
     out, lse = _gpu(fmt, False, w.q, pd, idx, w.scale, 4)
     assert_parity(_view(idx), out, lse, ref_o, ref_l, what=f"sparse {fmt} last partition only")
+    # the largest split count the boundary admits (one query, 2.2 GB of partials): one entry per
+    # partition, the rest empty
+    idx = workloads.sparse_lists(w, 17, seed=17)[:1]
+    q1 = np.ascontiguousarray(w.q[:1])
+    ref_o, ref_l = oracle.decode_sparse(q1, ph, idx, w.scale, fmt)
+    out, lse = _gpu(fmt, False, q1, pd, idx, w.scale, 65535)
+    assert_parity(_view(idx), out, lse, ref_o, ref_l, what=f"sparse {fmt} S=65535")
 
 
 # Slots around the places where narrower offsets would wrap, and the pool's last slots.
