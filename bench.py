@@ -729,10 +729,13 @@ def main():
                 ws = torch.empty(max(1, mla.mla_decode_rank_workspace_size(w.batch, rows, S, D)), dtype=torch.uint8,
                                  device=dev)
         out = torch.empty((w.batch, rows, width), dtype=torch.float32, device=dev)
+    gla_balanced = bool(balanced) and geom == "gla2"
     if balanced:
-        if geom != "mla":
-            raise SystemExit("--balanced is not combined with --geometry by this benchmark")
-        if nope:
+        if geom not in ("mla", "gla2"):
+            raise SystemExit(f"--balanced is not combined with --geometry {geom} by this benchmark")
+        if gla_balanced:
+            decode_bal = mla.mla_decode_gla2_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_gla2_balanced_fp8_656
+        elif nope:
             decode_bal = mla.mla_decode_balanced_nope_bf16 if w.fmt == "bf16" else mla.mla_decode_balanced_nope_fp8_656
         elif T > 1:
             decode_bal = mla.mla_decode_mtp_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_balanced_fp8_656
@@ -742,6 +745,8 @@ def main():
                          device=dev)
         S = 1
         kernel = f"decode_flat_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}>'}, {groups}>"
+        if gla_balanced:
+            kernel = f"decode_flat_kernel<{'Bf16Rows<512, 64>' if w.fmt == 'bf16' else 'Fp8Rows<64>'}, 1, true>"
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -759,7 +764,11 @@ def main():
         if write_rows:
             mla.mla_cache_write(new_lat, new_pe, new_slots, pool, fmt)
         if e: e[1].record(stream)
-        if balanced:
+        if gla_balanced:  # no partials-only form: the decode window holds the merge as well
+            decode_bal(q, pool, bt, lens, w.scale, num_workgroups=balanced, workspace=ws, out=out, lse=lse,
+                       flags=flags)
+            if e: e[2].record(stream)
+        elif balanced:
             decode_bal(q, pool, bt, lens, w.scale, num_workgroups=balanced, workspace=ws, partials_only=True,
                        flags=flags)
             if e: e[2].record(stream)
@@ -830,6 +839,9 @@ def main():
            for name, a, b in (("cache_write", 0, 1), ("decode", 1, 2), ("merge", 2, 3), ("step", 0, 3))}
     t_write, t_decode, t_merge = (float(np.mean(win[k])) for k in ("cache_write", "decode", "merge"))
     med = {k: round(float(np.median(v)), 4) for k, v in win.items()}
+    if gla_balanced:  # the merge runs inside the decode call (its window holds both)
+        del med["merge"]
+        med["decode_with_merge"] = med.pop("decode")
     t_decode_warm = t_decode
     if flush_mib:
         # Each step again, eagerly, after reading flush_mib MiB of other memory, so that the

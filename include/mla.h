@@ -430,6 +430,26 @@ MLA_API int mla_decode_gla2_fp8_656(const void* q, const void* kv_cache, int64_t
                                     float* out, float* lse, void* workspace, size_t workspace_bytes,
                                     uint32_t flags, int32_t* check_status, void* stream);
 
+/* GLA-g2 heads under the batch-balanced schedule (ragged batches): q bf16
+ * [batch][num_heads][320], out fp32 [batch][num_heads][256], lse [batch][num_heads], head groups
+ * and rows as mla_decode_gla2_*; num_workgroups, the workspace
+ * (mla_decode_balanced_workspace_size(batch, num_heads, num_workgroups) bytes) and the schedule as
+ * mla_decode_balanced_*.  out and lse are required: these calls always merge their own partials
+ * (whose rows are 256 values wide), so there is no partials-only form.  flags, check_status,
+ * stream and the errors as mla_decode_bf16. */
+MLA_API int mla_decode_gla2_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pages,
+                                          const int32_t* block_table, int64_t block_table_stride,
+                                          const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                          int32_t page_size, float softmax_scale, int32_t num_workgroups,
+                                          float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                          uint32_t flags, int32_t* check_status, void* stream);
+MLA_API int mla_decode_gla2_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                                             const int32_t* block_table, int64_t block_table_stride,
+                                             const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                             int32_t page_size, float softmax_scale, int32_t num_workgroups,
+                                             float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                             uint32_t flags, int32_t* check_status, void* stream);
+
 /* mla_merge_lse for partial rows of `width` values (256, 512, 768 or 1792): part_out fp32
  * [num_splits][batch][num_rows][width], part_lse [num_splits][batch][num_rows], out
  * [batch][num_rows][width], lse [batch][num_rows]; same formula and NaN / empty rules. */

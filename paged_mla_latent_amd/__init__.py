@@ -68,6 +68,7 @@ EXPORTED = (
     "mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656", "mla_checked_build",
     "mla_check_preconditions_host", "mla_decode_bf16_noalloc", "mla_decode_sparse_bf16",
     "mla_decode_sparse_fp8_656", "mla_decode_sparse_nope_bf16", "mla_decode_sparse_nope_fp8_656",
+    "mla_decode_gla2_balanced_bf16", "mla_decode_gla2_balanced_fp8_656",
 )
 MAX_SPARSE_TOKENS = 1 << 20
 MAX_SPARSE_TOPK = 1 << 24
@@ -108,7 +109,8 @@ def library(checked: bool = False) -> ctypes.CDLL:
                  "mla_decode_rank256_bf16", "mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656",
                  "mla_decode_rank768_bf16", "mla_decode_rank1792_bf16",
                  "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656",
-                 "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656"):
+                 "mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656", "mla_decode_gla2_balanced_bf16",
+                 "mla_decode_gla2_balanced_fp8_656"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = c_int
     mtp = [vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, c_u32, vp, vp]
@@ -393,7 +395,7 @@ def mla_decode_balanced_workspace_size(batch: int, num_heads: int, num_workgroup
 
 def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, kv_cache, block_table, seq_lens,
                      softmax_scale, num_workgroups, out, lse, workspace, partials_only=False, q_dim=ROW, flags=0,
-                     check_status=None):
+                     check_status=None, out_width=LATENT):
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
     lib, status_ptr = _options(check_status, dev)
@@ -412,7 +414,7 @@ def _decode_balanced(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, q, 
             raise ValueError("partials_only takes no out/lse")
     else:
         if out is None:
-            out = torch.empty((B, H, LATENT), dtype=torch.float32, device=dev)
+            out = torch.empty((B, H, out_width), dtype=torch.float32, device=dev)
         if lse is None:
             lse = torch.empty((B, H), dtype=torch.float32, device=dev)
         _need(out, "out", torch.float32, 3, dev)
@@ -625,6 +627,23 @@ def mla_decode_rank1792_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, 
     return _decode("mla_decode_rank1792_bf16", torch.bfloat16, 1856, q, kv_cache, block_table, seq_lens,
                    softmax_scale, num_splits, out, lse, workspace, partials_only, q_dim=1856, out_width=1792,
                    flags=flags, check_status=check_status)
+
+
+def mla_decode_gla2_balanced_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=0, out=None,
+                                  lse=None, workspace=None, flags=0, check_status=None):
+    """GLA-g2 under the batch-balanced schedule, bf16 rows: q [B, H, 320] (H even) -> out [B, H, 256],
+    lse [B, H]."""
+    return _decode_balanced("mla_decode_gla2_balanced_bf16", torch.bfloat16, ROW, q, kv_cache, block_table,
+                            seq_lens, softmax_scale, num_workgroups, out, lse, workspace, q_dim=320, flags=flags,
+                            check_status=check_status, out_width=256)
+
+
+def mla_decode_gla2_balanced_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups=0, out=None,
+                                     lse=None, workspace=None, flags=0, check_status=None):
+    """GLA-g2 under the batch-balanced schedule, fp8 656-byte rows: q [B, H, 320] (H even)."""
+    return _decode_balanced("mla_decode_gla2_balanced_fp8_656", torch.uint8, 656, q, kv_cache, block_table,
+                            seq_lens, softmax_scale, num_workgroups, out, lse, workspace, q_dim=320, flags=flags,
+                            check_status=check_status, out_width=256)
 
 
 def mla_decode_gla2_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,

@@ -1624,8 +1624,9 @@ constexpr int kAxisBytes = (kWaves + kMaxBalancedBatch + 1) * 8;
 template <class Fmt, int G>
 constexpr bool kAxisApart = kernel_smem_bytes<Fmt, G>() + kAxisBytes <= 160 * 1024;
 
-template <class Fmt, int G>
+template <class Fmt, int G, bool kGla2 = false>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParams p) {
+  constexpr int kOut = kGla2 ? 256 : Fmt::kLatent;  // output values per query row
   constexpr int kTileMem = kernel_smem_bytes<Fmt, G>();
   __shared__ __attribute__((aligned(16))) uint8_t smem[kTileMem + (kAxisApart<Fmt, G> ? kAxisBytes : 0)];
   // The grid size lives in another line of the kernel arguments than the fields read first: read
@@ -1680,7 +1681,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
     const int64_t t0 = on_tile(max(lo, s0) - s0);
     const int64_t t1 = on_tile(max(min(hi, v1) - s0, (int64_t)0));  // 0: the range holds start-up only
     const int64_t slot = (int64_t)b + w;
-    decode_rows<Fmt, G, false>(p, smem, b, L, t0, max(t0, t1), p.part_out + slot * R * kLatent,
+    decode_rows<Fmt, G, kGla2>(p, smem, b, L, t0, max(t0, t1), p.part_out + slot * R * kOut,
                                p.part_lse + slot * R);
     __syncthreads();  // the epilogue's LDS reads finish before the next segment's loads land
     v0 = v1;
@@ -1751,6 +1752,15 @@ hipError_t launch_decode_flat_nope_bf16(const DecodeParams& p, int num_workgroup
 }
 hipError_t launch_decode_flat_nope_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
   return launch_flat<Fp8Rows<0>, 1>(p, num_workgroups, stream);
+}
+// GLA-g2 heads under the batch-balanced schedule (one row group; 256-value partial rows).
+hipError_t launch_decode_flat_gla2(const DecodeParams& p, int fp8, int num_workgroups, hipStream_t stream) {
+  const dim3 grid((unsigned)num_workgroups), block(kWaves * 64);
+  if (fp8)
+    hipLaunchKernelGGL((decode_flat_kernel<Fp8Rows<64>, 1, true>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_flat_kernel<Bf16Rows<512, 64>, 1, true>), grid, block, 0, stream, p);
+  return hipGetLastError();
 }
 hipError_t launch_decode_nope_fp8(const DecodeParams& p, hipStream_t stream) {
   return launch<Fp8Rows<0>>(p, stream);

@@ -206,6 +206,7 @@ __global__ __launch_bounds__(64) void merge_few_kernel(const float* __restrict__
 // cost-axis ranges meet [cu[b], cu[b + 1]) (the axis the decode stored); row h of slot q is row
 // q * heads + h.  A request has one or two partials here (a handful for the longest): one row
 // per 64-lane workgroup (merge_row_wave).
+template <int NV>
 __global__ __launch_bounds__(64) void merge_flat_kernel(const float* __restrict__ part_out,
                                                         const float* __restrict__ part_lse,
                                                         const int64_t* __restrict__ cu, int batch, int heads,
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(64) void merge_flat_kernel(const float* __restrict_
     first = ((int64_t)b + w0) * heads + h;
     count = (int)(w1 - w0 + 1);
   }
-  merge_row_wave<kLatent / 256>(part_out, part_lse, count, first, heads, bh, out, lse);
+  merge_row_wave<NV>(part_out, part_lse, count, first, heads, bh, out, lse);
 }
 
 template <bool kCounted>
@@ -258,10 +259,14 @@ hipError_t launch_few(const float* part_out, const float* part_lse, int S, int64
 }  // namespace
 
 hipError_t launch_merge_flat(const float* part_out, const float* part_lse, const int64_t* cu, int batch, int heads,
-                             int num_workgroups, float* out, float* lse, hipStream_t stream) {
+                             int num_workgroups, float* out, float* lse, hipStream_t stream, int width) {
   const int64_t rows = (int64_t)batch * heads;
-  hipLaunchKernelGGL(merge_flat_kernel, dim3((unsigned)rows), dim3(64), 0, stream, part_out, part_lse, cu, batch, heads,
-                     num_workgroups, out, lse);
+  if (width == 256)
+    hipLaunchKernelGGL(merge_flat_kernel<1>, dim3((unsigned)rows), dim3(64), 0, stream, part_out, part_lse, cu, batch,
+                       heads, num_workgroups, out, lse);
+  else
+    hipLaunchKernelGGL(merge_flat_kernel<kLatent / 256>, dim3((unsigned)rows), dim3(64), 0, stream, part_out, part_lse,
+                       cu, batch, heads, num_workgroups, out, lse);
   return hipGetLastError();
 }
 

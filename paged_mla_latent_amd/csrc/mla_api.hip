@@ -280,20 +280,26 @@ int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void
   static const char* const kNames[] = {"mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
                                        "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656"};
   static const char* const kMtpNames[] = {"mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656"};
-  const char* fn = mtp ? kMtpNames[kind == kFp8] : kNames[kind];
+  const bool gla = kind == kGla2Bf16 || kind == kGla2Fp8;
+  const char* fn = gla   ? (kind == kGla2Fp8 ? "mla_decode_gla2_balanced_fp8_656" : "mla_decode_gla2_balanced_bf16")
+                   : mtp ? kMtpNames[kind == kFp8]
+                         : kNames[kind];
   if (int rc0 = check_options(fn, flags, check_status)) return rc0;
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
   if (!seq_lens) return fail(MLA_ERR_NULL, "%s: seq_lens is NULL", fn);
-  // out == lse == NULL leaves the partials in the workspace for mla_merge_lse_balanced.
-  const bool partials_only = !out && !lse;
+  // out == lse == NULL leaves the partials in the workspace for mla_merge_lse_balanced (not for
+  // GLA-g2 heads, whose 256-value partial rows that merge does not take).
+  const bool partials_only = !out && !lse && !gla;
   if (!out && !partials_only) return fail(MLA_ERR_NULL, "%s: out is NULL", fn);
   if (!lse && !partials_only) return fail(MLA_ERR_NULL, "%s: lse is NULL", fn);
   if (batch < 1 || batch > MLA_MAX_BALANCED_BATCH)
     return fail(MLA_ERR_SHAPE, "%s: batch=%d outside [1, %d]", fn, batch, MLA_MAX_BALANCED_BATCH);
   if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
     return fail(MLA_ERR_SHAPE, "%s: num_heads=%d outside [1, %d]", fn, num_heads, MLA_MAX_HEADS);
+  if (gla && num_heads % 2)
+    return fail(MLA_ERR_SHAPE, "%s: num_heads=%d must be even (two head groups)", fn, num_heads);
   if (q_len < 1 || q_len > MLA_MAX_Q_LEN)
     return fail(MLA_ERR_SHAPE, "%s: q_len=%d outside [1, %d]", fn, q_len, MLA_MAX_Q_LEN);
   if (q_len * num_heads > MLA_MAX_QUERY_ROWS)
@@ -362,12 +368,14 @@ int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void
     case kBf16: launched = mla::launch_decode_flat_bf16(p, num_workgroups, s); break;
     case kFp8: launched = mla::launch_decode_flat_fp8(p, num_workgroups, s); break;
     case kNopeBf16: launched = mla::launch_decode_flat_nope_bf16(p, num_workgroups, s); break;
-    default: launched = mla::launch_decode_flat_nope_fp8(p, num_workgroups, s); break;
+    case kNopeFp8: launched = mla::launch_decode_flat_nope_fp8(p, num_workgroups, s); break;
+    default: launched = mla::launch_decode_flat_gla2(p, kind == kGla2Fp8, num_workgroups, s); break;
   }
   rc = hip_status(launched, fn);
   if (rc != MLA_OK || partials_only) return rc;
   return hip_status(
-      mla::launch_merge_flat(ws.part_out, ws.part_lse, ws.cu, batch, rows, num_workgroups, out, lse, s),
+      mla::launch_merge_flat(ws.part_out, ws.part_lse, ws.cu, batch, rows, num_workgroups, out, lse, s,
+                             gla ? 256 : MLA_LATENT),
       "mla_merge_lse_balanced (after balanced decode)");
 }
 
@@ -479,6 +487,26 @@ size_t mla_decode_balanced_workspace_size(int32_t batch, int32_t num_heads, int3
     if (num_workgroups < 1) return 0;
   }
   return balanced_bytes_for(batch, num_heads, num_workgroups);
+}
+
+int mla_decode_gla2_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                                  int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
+                                  int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups,
+                                  float* out, float* lse, void* workspace, size_t workspace_bytes, uint32_t flags,
+                                  int32_t* check_status, void* stream) {
+  return decode_balanced(kGla2Bf16, false, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens,
+                         batch, num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace,
+                         workspace_bytes, flags, check_status, stream);
+}
+
+int mla_decode_gla2_balanced_fp8_656(const void* q, const void* kv_cache, int64_t num_pages,
+                                     const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
+                                     int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
+                                     int32_t num_workgroups, float* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
+  return decode_balanced(kGla2Fp8, false, 1, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens,
+                         batch, num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace,
+                         workspace_bytes, flags, check_status, stream);
 }
 
 int mla_decode_balanced_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,

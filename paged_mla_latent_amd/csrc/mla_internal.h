@@ -139,8 +139,9 @@ hipError_t launch_decode_flat_bf16(const DecodeParams& p, int num_workgroups, hi
 hipError_t launch_decode_flat_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream);
 hipError_t launch_decode_flat_nope_bf16(const DecodeParams& p, int num_workgroups, hipStream_t stream);
 hipError_t launch_decode_flat_nope_fp8(const DecodeParams& p, int num_workgroups, hipStream_t stream);
+hipError_t launch_decode_flat_gla2(const DecodeParams& p, int fp8, int num_workgroups, hipStream_t stream);
 hipError_t launch_merge_flat(const float* part_out, const float* part_lse, const int64_t* cu, int batch, int heads,
-                             int num_workgroups, float* out, float* lse, hipStream_t stream);
+                             int num_workgroups, float* out, float* lse, hipStream_t stream, int width = kLatent);
 hipError_t launch_gather(const uint8_t* cache, int fp8, int64_t num_pages, const int32_t* block_table,
                          int64_t bt_stride, const int64_t* cu_rows, const int32_t* seq_starts, int batch,
                          int page_size, int64_t total_rows, uint16_t* out, int32_t* check_status,

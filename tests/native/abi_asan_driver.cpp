@@ -90,6 +90,8 @@ int main() {
       {"mla_decode_balanced_fp8_656", mla_decode_balanced_fp8_656},
       {"mla_decode_balanced_nope_bf16", mla_decode_balanced_nope_bf16},
       {"mla_decode_balanced_nope_fp8_656", mla_decode_balanced_nope_fp8_656},
+      {"mla_decode_gla2_balanced_bf16", mla_decode_gla2_balanced_bf16},
+      {"mla_decode_gla2_balanced_fp8_656", mla_decode_gla2_balanced_fp8_656},
   };
   for (const auto& d : decoders) {
     Args a;

@@ -105,7 +105,7 @@ def test_decode_rejects_bad_shapes(lib, fn, kw, word):
 
 
 BALANCED = ["mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656", "mla_decode_balanced_nope_bf16",
-            "mla_decode_balanced_nope_fp8_656"]
+            "mla_decode_balanced_nope_fp8_656", "mla_decode_gla2_balanced_bf16", "mla_decode_gla2_balanced_fp8_656"]
 
 
 @pytest.mark.parametrize("fn", BALANCED)
@@ -227,10 +227,17 @@ def test_merge_balanced_takes_verify_rows(lib):
     assert lib.mla_merge_lse_balanced(P, need, 4, 65, 256, P, P, None) == 2
 
 
-@pytest.mark.parametrize("fn", ["mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656"])
+@pytest.mark.parametrize("fn", ["mla_decode_gla2_bf16", "mla_decode_gla2_fp8_656", "mla_decode_gla2_balanced_bf16",
+                                "mla_decode_gla2_balanced_fp8_656"])
 def test_gla2_needs_an_even_head_count(lib, fn):
-    rc, msg = _decode(lib, fn, heads=3)
+    rc, msg = _decode(lib, fn, heads=3, ws=P, ws_bytes=1 << 30)
     assert rc == 2 and "even" in msg
+
+
+@pytest.mark.parametrize("fn", ["mla_decode_gla2_balanced_bf16", "mla_decode_gla2_balanced_fp8_656"])
+def test_gla2_balanced_has_no_partials_only_form(lib, fn):
+    rc, msg = _decode(lib, fn, out=None, lse=None, ws=P, ws_bytes=1 << 30)
+    assert rc == 1 and "out is NULL" in msg
 
 
 def test_merge_width_validation(lib):

@@ -950,6 +950,34 @@ def test_gla2_parity(fmt, heads):
                   what=f"gla2 {fmt} H={heads} partials + merge")
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("heads", [2, 16])
+def test_gla2_balanced_parity(fmt, heads):
+    """GLA-g2 under the batch-balanced schedule on a ragged batch with empty requests, page sizes
+    that cut tiles, and workgroup counts from one per request to many per request, against
+    oracle.decode_gla2; bit-identical to itself across runs."""
+    rng = np.random.default_rng(120 + heads)
+    lens = [0, 1, 17, 700, 3000, 0, 64, 1500]
+    for ps in (16, 24):
+        pages = sum(-(-L // ps) for L in lens) + 3
+        w = workloads.make_workload(f"gla2_bal_{fmt}_{heads}_{ps}", seq_lens=lens, heads=heads, page_size=ps,
+                                    num_pages=pages, fmt=fmt, seed=130 + heads + ps)
+        q = workloads.bf16_bits(rng.standard_normal((w.batch, heads, 320)).astype(np.float32))
+        pd, ph = device_pool(w), host_pool(w)
+        ref_o, ref_l = oracle.decode_gla2(q, ph, w.block_table, w.seq_lens, ps, w.scale, fmt)
+        fn = mla.mla_decode_gla2_balanced_bf16 if fmt == "bf16" else mla.mla_decode_gla2_balanced_fp8_656
+        bt, lens_d = torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+        for W in (3, 16, 256):
+            out, lse = fn(bf16_dev(q), pd, bt, lens_d, w.scale, num_workgroups=W)
+            torch.cuda.synchronize()
+            assert out.shape == (w.batch, heads, 256)
+            assert_parity(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o,
+                          ref_l, what=f"gla2 balanced {fmt} H={heads} ps={ps} W={W}")
+            again = fn(bf16_dev(q), pd, bt, lens_d, w.scale, num_workgroups=W)
+            torch.cuda.synchronize()
+            assert torch.equal(again[0], out) and torch.equal(again[1], lse)
+
+
 # ------------------------------------------------------------------------- NoPE-512
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 @pytest.mark.parametrize("ps", [3, 16, 24, 64])
