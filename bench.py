@@ -81,9 +81,32 @@ def _parse():
     ap.add_argument("--op", choices=("decode", "gather", "cache_write", "merge", "sparse"), default="decode",
                     help="gather: time mla_gather_context over the workload's whole context instead "
                          "(prefill-side context gather, fp8 rows upconverted to bf16)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="write the step's new rows with mla_cache_write before the decode (two launches) "
+                         "instead of letting the decode write them (mla_decode_append_*, the default where "
+                         "the configuration has that call: 576-value rows with rope, bf16 or fp8)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times (counter calibration)")
     return ap.parse_args()
+
+
+def _append_rows(w, T):
+    """The step's new rows per request for mla_decode_append_*: positions L - T .. L - 1 of request b
+    (the rows the cache already holds there, so every step writes the same bytes), [B, T, ...];
+    a negative position gets slot -1 (not written)."""
+    B, ps = w.batch, w.page_size
+    lat = np.zeros((B, T, 512), np.uint16)
+    pe = np.zeros((B, T, 64), np.uint16)
+    slots = np.full((B, T), -1, np.int64)
+    for b in range(B):
+        for i in range(T):
+            pos = int(w.seq_lens[b]) - T + i
+            if pos < 0:
+                continue
+            s = int(w.block_table[b, pos // ps]) * ps + pos % ps
+            r = int(np.searchsorted(w.slots, s))
+            lat[b, i], pe[b, i], slots[b, i] = w.latent[r], w.k_pe[r], s
+    return lat, pe, slots
 
 
 def _copy_calibration(mib: int):
@@ -747,6 +770,17 @@ def main():
         kernel = f"decode_flat_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}>'}, {groups}>"
         if gla_balanced:
             kernel = f"decode_flat_kernel<{'Bf16Rows<512, 64>' if w.fmt == 'bf16' else 'Fp8Rows<64>'}, 1, true>"
+    # The decode writes the step's new rows itself (one launch fewer) where it has that call.
+    fused_write = write_rows and not args.separate_write and geom == "mla" and not nope
+    if fused_write:
+        a_lat, a_pe, a_slots = _append_rows(w, T)
+        a_lat, a_pe, a_slots = bf16(a_lat), bf16(a_pe), torch.from_numpy(a_slots).to(dev)
+        q_app = q.view(w.batch, T, w.heads, 576)
+        if balanced:
+            app_fn = mla.mla_decode_append_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_append_balanced_fp8_656
+        else:
+            app_fn = mla.mla_decode_append_bf16 if w.fmt == "bf16" else mla.mla_decode_append_fp8_656
+        out4, lse3 = out.view(w.batch, T, w.heads, 512), lse.view(w.batch, T, w.heads)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -761,10 +795,25 @@ def main():
 
     def step(e=None):
         if e: e[0].record(stream)
-        if write_rows:
+        if write_rows and not fused_write:
             mla.mla_cache_write(new_lat, new_pe, new_slots, pool, fmt)
         if e: e[1].record(stream)
-        if gla_balanced:  # no partials-only form: the decode window holds the merge as well
+        if fused_write:  # the decode window holds the row writes
+            if balanced:
+                app_fn(q_app, a_lat, a_pe, a_slots, pool, bt, lens, w.scale, num_workgroups=balanced, workspace=ws,
+                       partials_only=True, flags=flags)
+                if e: e[2].record(stream)
+                mla.mla_merge_lse_balanced(ws, w.batch, rows, balanced, out=out, lse=lse)
+            elif S > 1:
+                po, pl = app_fn(q_app, a_lat, a_pe, a_slots, pool, bt, lens, w.scale, num_splits=S, workspace=ws,
+                                partials_only=True, flags=flags)
+                if e: e[2].record(stream)
+                mla.mla_merge_lse(po, pl, out=out, lse=lse)
+            else:
+                app_fn(q_app, a_lat, a_pe, a_slots, pool, bt, lens, w.scale, num_splits=1, out=out4, lse=lse3,
+                       flags=flags)
+                if e: e[2].record(stream)
+        elif gla_balanced:  # no partials-only form: the decode window holds the merge as well
             decode_bal(q, pool, bt, lens, w.scale, num_workgroups=balanced, workspace=ws, out=out, lse=lse,
                        flags=flags)
             if e: e[2].record(stream)
@@ -842,6 +891,9 @@ def main():
     if gla_balanced:  # the merge runs inside the decode call (its window holds both)
         del med["merge"]
         med["decode_with_merge"] = med.pop("decode")
+    if fused_write:  # the row writes run inside the decode (its window holds both)
+        del med["cache_write"]
+        med["decode_with_row_writes"] = med.pop("decode")
     t_decode_warm = t_decode
     if flush_mib:
         # Each step again, eagerly, after reading flush_mib MiB of other memory, so that the
@@ -894,7 +946,8 @@ def main():
             "layer": "nope-512" if nope else "rope-576", "query_tokens_per_request": T, "geometry": geom,
             "cache_row_bytes": 2 * (RANKS[geom] + 64) if geom in RANKS else w.row_bytes,
             "row_bytes_read": row_bytes_read,
-            "step": "decode + merge" if not write_rows else "cache write + decode + merge",
+            "step": ("decode + merge" if not write_rows
+                     else "decode writing the new rows + merge" if fused_write else "cache write + decode + merge"),
             "cache_bytes_per_step": cache_bytes,
             # distinct rows read: below cache_bytes_per_step when requests share pages (high_slot),
             # whose figure is then an effective bandwidth, part of it served from the caches
@@ -907,8 +960,8 @@ def main():
         "kernel_ms_median": med,
         "read_ceiling": ceiling,
         "eager_ms_per_step": round(ms_step_eager, 4),
-        "kernel_ms": {"cache_write": round(t_write, 4), "decode": round(t_decode_warm, 4), "merge": round(t_merge, 4),
-                      **({"decode_after_flush": round(t_decode, 4)} if flush_mib else {})},
+        "kernel_ms": {**({} if fused_write else {"cache_write": round(t_write, 4)}), "decode": round(t_decode_warm, 4),
+                      "merge": round(t_merge, 4), **({"decode_after_flush": round(t_decode, 4)} if flush_mib else {})},
         "roofline": {
             "kernel": kernel,
             "bound": "hbm",

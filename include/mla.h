@@ -372,6 +372,56 @@ MLA_API int mla_decode_mtp_balanced_fp8_656(const void* q, const void* kv_cache,
                                             int32_t num_workgroups, float* out, float* lse, void* workspace,
                                             size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream);
 
+/* Decode step with the cache write folded in: the results of mla_cache_write of the step's
+ * new rows followed by mla_decode_mtp_* (per-request partitions) or mla_decode_mtp_balanced_*
+ * (batch-balanced), in one launch of the decode (plus its merge).  The cache write and the
+ * decode read the same rows (vLLM pull request 55543: the cache-write step stores the new
+ * token's latent ++ rotary key row, which the decode then attends to); here the partition
+ * whose token range holds a new row's position stores that row before it reads any row, so
+ * no separate cache-write kernel runs (this library's arrangement, not the pages').
+ * new_latent bf16 [batch][q_len][512], new_k_pe bf16 [batch][q_len][64] or NULL (rope part
+ *            written as zeros); new_slots int64 [batch][q_len], negative = not written.
+ *            New row i of request b is context position seq_lens[b] - q_len + i; rows whose
+ *            position is negative (seq_lens[b] < q_len) are not written.
+ * kv_cache   written (the new rows, encoded as mla_cache_write encodes them) and read.
+ * Precondition (as for the separate calls): new_slots[b][i] is the slot the block table gives
+ * for that position, page_id * page_size + position % page_size, and the slots are distinct;
+ * the checked build leaves a slot outside [0, num_pages * page_size) unwritten and reports
+ * MLA_CHECK_BLOCK_ID.  q_len 1..MLA_MAX_Q_LEN (q_len = 1: the single-token decode).
+ * mla_decode_append_*: every other argument, result and error as mla_decode_mtp_*;
+ * mla_decode_append_balanced_*: as mla_decode_mtp_balanced_* (num_workgroups, workspace,
+ * out == lse == NULL for the partials). */
+MLA_API int mla_decode_append_bf16(const void* q, const void* new_latent, const void* new_k_pe,
+                                   const int64_t* new_slots, void* kv_cache, int64_t num_pages,
+                                   const int32_t* block_table, int64_t block_table_stride,
+                                   const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t num_heads,
+                                   int32_t page_size, float softmax_scale, int32_t num_splits, float* out,
+                                   float* lse, void* workspace, size_t workspace_bytes, uint32_t flags,
+                                   int32_t* check_status, void* stream);
+MLA_API int mla_decode_append_fp8_656(const void* q, const void* new_latent, const void* new_k_pe,
+                                      const int64_t* new_slots, void* kv_cache, int64_t num_pages,
+                                      const int32_t* block_table, int64_t block_table_stride,
+                                      const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t num_heads,
+                                      int32_t page_size, float softmax_scale, int32_t num_splits, float* out,
+                                      float* lse, void* workspace, size_t workspace_bytes, uint32_t flags,
+                                      int32_t* check_status, void* stream);
+MLA_API int mla_decode_append_balanced_bf16(const void* q, const void* new_latent, const void* new_k_pe,
+                                            const int64_t* new_slots, void* kv_cache, int64_t num_pages,
+                                            const int32_t* block_table, int64_t block_table_stride,
+                                            const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                                            int32_t num_heads, int32_t page_size, float softmax_scale,
+                                            int32_t num_workgroups, float* out, float* lse, void* workspace,
+                                            size_t workspace_bytes, uint32_t flags, int32_t* check_status,
+                                            void* stream);
+MLA_API int mla_decode_append_balanced_fp8_656(const void* q, const void* new_latent, const void* new_k_pe,
+                                               const int64_t* new_slots, void* kv_cache, int64_t num_pages,
+                                               const int32_t* block_table, int64_t block_table_stride,
+                                               const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                                               int32_t num_heads, int32_t page_size, float softmax_scale,
+                                               int32_t num_workgroups, float* out, float* lse, void* workspace,
+                                               size_t workspace_bytes, uint32_t flags, int32_t* check_status,
+                                               void* stream);
+
 /* Other latent geometries (qwen-mla-vllm: per-layer latent ranks 256 / 768 / 1792 with a small
  * rotary tail, "How it works"; GLA-g2, the latent split into two head groups, opening section).
  * The row layouts are this library's reading; the pages give none.

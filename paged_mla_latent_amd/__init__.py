@@ -68,7 +68,8 @@ EXPORTED = (
     "mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656", "mla_checked_build",
     "mla_check_preconditions_host", "mla_decode_bf16_noalloc", "mla_decode_sparse_bf16",
     "mla_decode_sparse_fp8_656", "mla_decode_sparse_nope_bf16", "mla_decode_sparse_nope_fp8_656",
-    "mla_decode_gla2_balanced_bf16", "mla_decode_gla2_balanced_fp8_656",
+    "mla_decode_gla2_balanced_bf16", "mla_decode_gla2_balanced_fp8_656", "mla_decode_append_bf16",
+    "mla_decode_append_fp8_656", "mla_decode_append_balanced_bf16", "mla_decode_append_balanced_fp8_656",
 )
 MAX_SPARSE_TOKENS = 1 << 20
 MAX_SPARSE_TOPK = 1 << 24
@@ -117,6 +118,12 @@ def library(checked: bool = False) -> ctypes.CDLL:
     for name in ("mla_decode_mtp_bf16", "mla_decode_mtp_fp8_656", "mla_decode_mtp_balanced_bf16",
                  "mla_decode_mtp_balanced_fp8_656"):
         getattr(lib, name).argtypes = mtp
+        getattr(lib, name).restype = c_int
+    app = [vp, vp, vp, vp, vp, c_i64, vp, c_i64, vp, c_i32, c_i32, c_i32, c_i32, c_f, c_i32, vp, vp, vp, c_sz, c_u32,
+           vp, vp]
+    for name in ("mla_decode_append_bf16", "mla_decode_append_fp8_656", "mla_decode_append_balanced_bf16",
+                 "mla_decode_append_balanced_fp8_656"):
+        getattr(lib, name).argtypes = app
         getattr(lib, name).restype = c_int
     lib.mla_merge_lse_balanced.argtypes = [vp, c_sz, c_i32, c_i32, c_i32, vp, vp, vp]
     lib.mla_merge_lse_balanced.restype = c_int
@@ -599,6 +606,101 @@ def mla_decode_mtp_fp8_656(q, kv_cache, block_table, seq_lens, softmax_scale, nu
     return _decode_mtp("mla_decode_mtp_fp8_656", torch.uint8, 656, q, kv_cache, block_table, seq_lens,
                        softmax_scale, num_splits, out, lse, workspace, partials_only,
                        flags=flags, check_status=check_status)
+
+
+def _decode_append(fn: str, cache_dtype: torch.dtype, row_bytes_last: int, balanced: bool, q, new_latent, new_k_pe,
+                   new_slots, kv_cache, block_table, seq_lens, softmax_scale, count, out, lse, workspace,
+                   partials_only=False, flags=0, check_status=None):
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    lib, status_ptr = _options(check_status, dev)
+    _need(kv_cache, "kv_cache", cache_dtype, 3, dev)
+    if kv_cache.shape[2] != row_bytes_last:
+        raise ValueError(f"kv_cache rows must have {row_bytes_last} elements, got {kv_cache.shape[2]}")
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, T, H, D = q.shape
+    if D != ROW:
+        raise ValueError(f"q rows must have {ROW} values, got {D}")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have one row per request")
+    _need(new_latent, "new_latent", torch.bfloat16, 3, dev)
+    _need(new_slots, "new_slots", torch.int64, 2, dev)
+    if new_k_pe is not None:
+        _need(new_k_pe, "new_k_pe", torch.bfloat16, 3, dev)
+    if (tuple(new_latent.shape) != (B, T, LATENT) or tuple(new_slots.shape) != (B, T)
+            or (new_k_pe is not None and tuple(new_k_pe.shape) != (B, T, ROPE))):
+        raise ValueError("new_latent must be [B, q_len, 512], new_k_pe [B, q_len, 64] (or None), new_slots [B, q_len]")
+    if partials_only:
+        if out is not None or lse is not None or (not balanced and count < 2):
+            raise ValueError("partials_only takes no out/lse (and, per request, num_splits > 1)")
+    else:
+        if out is None:
+            out = torch.empty((B, T, H, LATENT), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, 4, dev)
+        _need(lse, "lse", torch.float32, 3, dev)
+    if balanced:
+        if workspace is None:
+            workspace = torch.empty(max(mla_decode_balanced_workspace_size(B, T * H, count), 1), dtype=torch.uint8,
+                                    device=dev)
+    elif count > 1 and workspace is None:
+        workspace = torch.empty(mla_decode_workspace_size(B, T * H, count), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = getattr(lib, fn)(
+        q.data_ptr(), new_latent.data_ptr(), _ptr(new_k_pe), new_slots.data_ptr(), kv_cache.data_ptr(),
+        kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(), B, T, H,
+        kv_cache.shape[1], float(softmax_scale), int(count), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        int(flags), status_ptr, _stream(dev))
+    _check(fn, status, lib)
+    if partials_only and balanced:
+        return workspace
+    if partials_only:  # [S, B, q_len * H, 512] / [S, B, q_len * H]: query rows act as heads
+        n = count * B * T * H
+        flat = workspace.view(torch.uint8)[: n * (LATENT + 1) * 4].view(torch.float32)
+        return flat[: n * LATENT].view(count, B, T * H, LATENT), flat[n * LATENT:].view(count, B, T * H)
+    return out, lse
+
+
+def mla_decode_append_bf16(q, new_latent, new_k_pe, new_slots, kv_cache, block_table, seq_lens, softmax_scale,
+                           num_splits=1, out=None, lse=None, workspace=None, partials_only=False, flags=0,
+                           check_status=None):
+    """Decode step that writes its new rows itself: new_latent [B, q_len, 512], new_k_pe [B, q_len, 64]
+    (or None), new_slots int64 [B, q_len] go into the bf16 cache (row i of request b is position
+    L_b - q_len + i), then q [B, q_len, H, 576] is decoded as by mla_decode_mtp_bf16."""
+    return _decode_append("mla_decode_append_bf16", torch.bfloat16, ROW, False, q, new_latent, new_k_pe, new_slots,
+                          kv_cache, block_table, seq_lens, softmax_scale, num_splits, out, lse, workspace,
+                          partials_only, flags=flags, check_status=check_status)
+
+
+def mla_decode_append_fp8_656(q, new_latent, new_k_pe, new_slots, kv_cache, block_table, seq_lens, softmax_scale,
+                              num_splits=1, out=None, lse=None, workspace=None, partials_only=False, flags=0,
+                              check_status=None):
+    """mla_decode_append_bf16 over an fp8 cache uint8 [num_pages, page_size, 656] (rows quantised as
+    mla_cache_write quantises them)."""
+    return _decode_append("mla_decode_append_fp8_656", torch.uint8, 656, False, q, new_latent, new_k_pe, new_slots,
+                          kv_cache, block_table, seq_lens, softmax_scale, num_splits, out, lse, workspace,
+                          partials_only, flags=flags, check_status=check_status)
+
+
+def mla_decode_append_balanced_bf16(q, new_latent, new_k_pe, new_slots, kv_cache, block_table, seq_lens,
+                                    softmax_scale, num_workgroups=0, out=None, lse=None, workspace=None,
+                                    partials_only=False, flags=0, check_status=None):
+    """mla_decode_append_bf16 under the batch-balanced schedule (as mla_decode_mtp_balanced_bf16);
+    partials_only=True returns the workspace for mla_merge_lse_balanced(ws, B, q_len * H, num_workgroups)."""
+    return _decode_append("mla_decode_append_balanced_bf16", torch.bfloat16, ROW, True, q, new_latent, new_k_pe,
+                          new_slots, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups, out, lse,
+                          workspace, partials_only, flags=flags, check_status=check_status)
+
+
+def mla_decode_append_balanced_fp8_656(q, new_latent, new_k_pe, new_slots, kv_cache, block_table, seq_lens,
+                                       softmax_scale, num_workgroups=0, out=None, lse=None, workspace=None,
+                                       partials_only=False, flags=0, check_status=None):
+    """mla_decode_append_balanced_bf16 over an fp8 cache uint8 [num_pages, page_size, 656]."""
+    return _decode_append("mla_decode_append_balanced_fp8_656", torch.uint8, 656, True, q, new_latent, new_k_pe,
+                          new_slots, kv_cache, block_table, seq_lens, softmax_scale, num_workgroups, out, lse,
+                          workspace, partials_only, flags=flags, check_status=check_status)
 
 
 def mla_decode_rank256_bf16(q, kv_cache, block_table, seq_lens, softmax_scale, num_splits=1, out=None, lse=None,

@@ -39,6 +39,7 @@
 //    folded into P for that block's PV, so no dequantised value is ever rounded.
 #include <type_traits>
 
+#include "cache_rows.h"
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -523,6 +524,75 @@ __device__ __forceinline__ void finish_rows(uint8_t* smem, const f32x4 (&O)[TF::
 // kSparse (single-token decodes only): the block table is a per-query list of cache slots
 // (page size 1) whose negative entries select nothing: such a token is loaded from slot 0 and
 // masked out of the scores (a 16-bit validity mask per tile, taken when the tile's slots are read).
+// ------------------------------------------------------------------------------------
+// The step's new rows, written by the decode (the cache-write step fused into the launch).  New
+// row i of request b is context position L - q_len + i; the segment whose token range holds a
+// position writes that row, and no other workgroup reads it.  Its inputs are requested at the
+// segment's start, beside the q loads (append_begin); the stores go out just before the
+// segment's first row load, are waited for (vmcnt 0: the vector-memory counter does not order
+// stores against loads) and a barrier orders them before every wave's row loads
+// (append_end), which then read the new rows from this XCD's L2.  Wave w writes the segment's
+// new rows w, w + 4, ...; only segments that hold new rows pay the extra round trip.
+// ------------------------------------------------------------------------------------
+struct AppendRows {
+  int64_t lo = 0;  // position of the segment's first new row
+  int count = 0;   // new rows in the segment (workgroup-uniform)
+  int64_t slot = -1;
+  RowIn in;        // this wave's first row's inputs
+};
+
+template <class Fmt>
+__device__ __forceinline__ AppendRows append_begin(const DecodeParams& p, int b, int64_t L, int64_t t0, int64_t t1,
+                                                   int wave, int lane) {
+  AppendRows a;
+  if constexpr (Fmt::kLatent == kLatent) {
+    if (p.new_latent == nullptr) return a;
+    const int64_t base = L - p.q_len;  // position of new row 0
+    const int64_t lo = base > t0 ? base : t0, hi = L < t1 ? L : t1;
+    if (lo >= hi) return a;
+    a.lo = lo;
+    a.count = (int)(hi - lo);
+    if (wave < a.count) {
+      const int64_t tok = (int64_t)b * p.q_len + (lo + wave - base);
+      a.slot = p.new_slots[tok];
+      a.in = load_row(p.new_latent + tok * kLatent, p.new_k_pe == nullptr ? nullptr : p.new_k_pe + tok * kRope, lane);
+    }
+  }
+  return a;
+}
+
+template <class Fmt>
+__device__ __forceinline__ void append_end(const DecodeParams& p, int b, int64_t L, const AppendRows& a, int wave,
+                                           int lane, uint32_t& bad) {
+  if constexpr (Fmt::kLatent == kLatent) {
+    if (a.count == 0) return;
+    constexpr bool kFp8 = Fmt::kRowBytes == kRowBytesFp8;
+    const int64_t base = L - p.q_len;
+    const int64_t slots = p.num_pages * (int64_t)p.page_size;
+    for (int j = wave; j < a.count; j += kWaves) {
+      int64_t slot = a.slot;
+      RowIn in = a.in;
+      if (j != wave) {  // rows past the first four (q_len > 4)
+        const int64_t tok = (int64_t)b * p.q_len + (a.lo + j - base);
+        slot = p.new_slots[tok];
+        in = load_row(p.new_latent + tok * kLatent, p.new_k_pe == nullptr ? nullptr : p.new_k_pe + tok * kRope, lane);
+      }
+      if (slot < 0) continue;
+      if (kChecked && slot >= slots) {  // a row outside the pool: not written
+        bad |= kCheckBlockId;
+        continue;
+      }
+      if constexpr (kFp8) {
+        store_row_fp8(in, p.cache_w + slot * (int64_t)kRowBytesFp8, lane);
+      } else {
+        store_row_bf16(in, p.cache_w + slot * (int64_t)kRowBytesBf16, lane);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+}
+
 template <class Fmt, int G, bool kGla2, bool kSparse = false>
 __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* smem, int b, int64_t L,
                                                int64_t t0_abs, int64_t t1_abs, float* out, float* lse) {
@@ -551,6 +621,9 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   // partition, clamped to its end.
   const int64_t lim = L - p.q_len + 1 + (row < R ? row / H : 0);
   const int n_vis = (int)(min(rg.t1, lim) - rg.t0);
+  // the step's new rows in this segment (none for index lists)
+  AppendRows app;
+  if constexpr (!kSparse) app = append_begin<Fmt>(p, b, L, rg.t0, rg.t1, wave, lane);
 
   // q as the B operand of the QK MFMA: lane (row m, slice g) holds q[row][32j + 8g .. +8].
   constexpr int QS = Fmt::kQSteps;
@@ -795,6 +868,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
     }
 #pragma unroll
     for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
+    if constexpr (!kSparse) append_end<Fmt>(p, b, L, app, wave, lane, bad);
     wait_vmcnt<0>();
     if (first_tiles) {
 #pragma unroll
@@ -830,6 +904,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
     for (int t = 0; t < NB - 1; ++t)
 #pragma unroll
       for (int i = 0; i < TPL; ++i) asm volatile("" ::"v"(page_first[t][i]));
+    if constexpr (!kSparse) append_end<Fmt>(p, b, L, app, wave, lane, bad);
     if (first_tiles) {
 #pragma unroll
       for (int t = 0; t < NB - 1; ++t) {
@@ -1099,6 +1174,7 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
   const int row = 16 * wave + m;  // this lane's query row in the scores (row group = wave)
   const int64_t lim = L - p.q_len + 1 + (row < R ? row / H : 0);
   const int n_vis = (int)(min(rg.t1, lim) - rg.t0);
+  const AppendRows app = append_begin<Fmt>(p, b, L, rg.t0, rg.t1, wave, lane);  // the step's new rows here
 
   // q as the B operand of the QK MFMA: lane (row m, slice g) holds q[row][32j + 8g .. + 8].  bf16:
   // the own row group's 18 K-steps.  fp8: [0, 9) the own row group's, [9, 18) the partner row
@@ -1205,6 +1281,7 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
       for (int t = 0; t < NB - 1; ++t) fetch_page(tile_of_step(t), xlds + 256 * t);
 #pragma unroll
       for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
+      append_end<Fmt>(p, b, L, app, wave, lane, bad);
       wait_vmcnt<0>();
 #pragma unroll
       for (int t = 0; t < NB - 1; ++t) {
@@ -1225,6 +1302,7 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
       for (int t = 0; t < NB - 1; ++t)
 #pragma unroll
         for (int i = 0; i < TPL; ++i) asm volatile("" ::"v"(page_first[t][i]));
+      append_end<Fmt>(p, b, L, app, wave, lane, bad);
 #pragma unroll
       for (int t = 0; t < NB - 1; ++t) {
         fetch_page(tile_of_step(t + NB - 1), slot_lds(t + NB - 1));

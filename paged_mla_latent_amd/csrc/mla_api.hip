@@ -125,11 +125,37 @@ enum DecodeKind {
   kRank768Bf16 = 7, kRank1792Bf16 = 8
 };
 
+// The step's new rows of the mla_decode_append_* calls (the cache write fused into the decode).
+struct AppendArgs {
+  const void* new_latent;
+  const void* new_k_pe;
+  const int64_t* new_slots;
+  void* kv_cache;
+};
+
+int check_append(const char* fn, const AppendArgs* app) {
+  if (!app) return MLA_OK;
+  if (!app->new_latent) return fail(MLA_ERR_NULL, "%s: new_latent is NULL", fn);
+  if (!app->new_slots) return fail(MLA_ERR_NULL, "%s: new_slots is NULL", fn);
+  if (!aligned16(app->new_latent) || !aligned16(app->new_k_pe) || !aligned16(app->new_slots))
+    return fail(MLA_ERR_ALIGN, "%s: every tensor pointer must be 16-byte aligned", fn);
+  return MLA_OK;
+}
+
+void set_append(mla::DecodeParams& p, const AppendArgs* app) {
+  if (!app) return;
+  p.new_latent = static_cast<const uint16_t*>(app->new_latent);
+  p.new_k_pe = static_cast<const uint16_t*>(app->new_k_pe);
+  p.new_slots = app->new_slots;
+  p.cache_w = static_cast<uint8_t*>(app->kv_cache);
+}
+
 int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, int64_t num_pages,
                   const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
                   int32_t batch, int32_t num_heads, int32_t page_size, float softmax_scale,
                   int32_t num_splits, float* out, float* lse, void* workspace, size_t workspace_bytes,
-                  uint32_t flags, int32_t* check_status, void* stream, bool use_scratch = false) {
+                  uint32_t flags, int32_t* check_status, void* stream, bool use_scratch = false,
+                  const AppendArgs* app = nullptr) {
   static const char* const kNames[] = {"mla_decode_bf16",         "mla_decode_fp8_656",
                                        "mla_decode_nope_bf16",    "mla_decode_nope_fp8_656",
                                        "mla_decode_rank256_bf16", "mla_decode_gla2_bf16",
@@ -142,9 +168,11 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
                         : kind == kRank1792Bf16       ? 1792
                                                       : MLA_LATENT;
   const char* fn = use_scratch ? "mla_decode_bf16_noalloc"
+                   : app         ? (kind == kBf16 ? "mla_decode_append_bf16" : "mla_decode_append_fp8_656")
                    : q_len == 1  ? kNames[kind]
                                  : (kind == kBf16 ? "mla_decode_mtp_bf16" : "mla_decode_mtp_fp8_656");
   if (int rc0 = check_options(fn, flags, check_status)) return rc0;
+  if (int rc0 = check_append(fn, app)) return rc0;
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
@@ -228,6 +256,7 @@ int decode_common(int kind, int32_t q_len, const void* q, const void* kv_cache, 
   p.stream_rows = (flags & MLA_FLAG_CACHED_ROWS) == 0;
   p.num_pages = num_pages;
   p.check_status = check_status;
+  set_append(p, app);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t launched;
   switch (kind) {
@@ -276,15 +305,17 @@ int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void
                     const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
                     int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out,
                     float* lse, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status,
-                    void* stream) {
+                    void* stream, const AppendArgs* app = nullptr) {
   static const char* const kNames[] = {"mla_decode_balanced_bf16", "mla_decode_balanced_fp8_656",
                                        "mla_decode_balanced_nope_bf16", "mla_decode_balanced_nope_fp8_656"};
   static const char* const kMtpNames[] = {"mla_decode_mtp_balanced_bf16", "mla_decode_mtp_balanced_fp8_656"};
   const bool gla = kind == kGla2Bf16 || kind == kGla2Fp8;
   const char* fn = gla   ? (kind == kGla2Fp8 ? "mla_decode_gla2_balanced_fp8_656" : "mla_decode_gla2_balanced_bf16")
+                   : app ? (kind == kFp8 ? "mla_decode_append_balanced_fp8_656" : "mla_decode_append_balanced_bf16")
                    : mtp ? kMtpNames[kind == kFp8]
                          : kNames[kind];
   if (int rc0 = check_options(fn, flags, check_status)) return rc0;
+  if (int rc0 = check_append(fn, app)) return rc0;
   if (!q) return fail(MLA_ERR_NULL, "%s: q is NULL", fn);
   if (!kv_cache) return fail(MLA_ERR_NULL, "%s: kv_cache is NULL", fn);
   if (!block_table) return fail(MLA_ERR_NULL, "%s: block_table is NULL", fn);
@@ -361,6 +392,7 @@ int decode_balanced(int kind, bool mtp, int32_t q_len, const void* q, const void
   p.stream_rows = (flags & MLA_FLAG_CACHED_ROWS) == 0;
   p.num_pages = num_pages;
   p.check_status = check_status;
+  set_append(p, app);
   static_assert(MLA_MAX_BALANCED_BATCH == mla::kMaxBalancedBatch, "batch limit of the balanced kernels");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t launched;
@@ -638,6 +670,55 @@ int mla_decode_mtp_fp8_656(const void* q, const void* kv_cache, int64_t num_page
                            float* lse, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
   return decode_common(kFp8, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
                        num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags, check_status, stream);
+}
+
+int mla_decode_append_bf16(const void* q, const void* new_latent, const void* new_k_pe, const int64_t* new_slots,
+                           void* kv_cache, int64_t num_pages, const int32_t* block_table, int64_t block_table_stride,
+                           const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t num_heads, int32_t page_size,
+                           float softmax_scale, int32_t num_splits, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, uint32_t flags, int32_t* check_status, void* stream) {
+  const AppendArgs app = {new_latent, new_k_pe, new_slots, kv_cache};
+  return decode_common(kBf16, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags,
+                       check_status, stream, false, &app);
+}
+
+int mla_decode_append_fp8_656(const void* q, const void* new_latent, const void* new_k_pe, const int64_t* new_slots,
+                              void* kv_cache, int64_t num_pages, const int32_t* block_table,
+                              int64_t block_table_stride, const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                              int32_t num_heads, int32_t page_size, float softmax_scale, int32_t num_splits,
+                              float* out, float* lse, void* workspace, size_t workspace_bytes, uint32_t flags,
+                              int32_t* check_status, void* stream) {
+  const AppendArgs app = {new_latent, new_k_pe, new_slots, kv_cache};
+  return decode_common(kFp8, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens, batch,
+                       num_heads, page_size, softmax_scale, num_splits, out, lse, workspace, workspace_bytes, flags,
+                       check_status, stream, false, &app);
+}
+
+int mla_decode_append_balanced_bf16(const void* q, const void* new_latent, const void* new_k_pe,
+                                    const int64_t* new_slots, void* kv_cache, int64_t num_pages,
+                                    const int32_t* block_table, int64_t block_table_stride, const int32_t* seq_lens,
+                                    int32_t batch, int32_t q_len, int32_t num_heads, int32_t page_size,
+                                    float softmax_scale, int32_t num_workgroups, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, uint32_t flags, int32_t* check_status,
+                                    void* stream) {
+  const AppendArgs app = {new_latent, new_k_pe, new_slots, kv_cache};
+  return decode_balanced(kBf16, q_len > 1, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens,
+                         batch, num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace,
+                         workspace_bytes, flags, check_status, stream, &app);
+}
+
+int mla_decode_append_balanced_fp8_656(const void* q, const void* new_latent, const void* new_k_pe,
+                                       const int64_t* new_slots, void* kv_cache, int64_t num_pages,
+                                       const int32_t* block_table, int64_t block_table_stride,
+                                       const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t num_heads,
+                                       int32_t page_size, float softmax_scale, int32_t num_workgroups, float* out,
+                                       float* lse, void* workspace, size_t workspace_bytes, uint32_t flags,
+                                       int32_t* check_status, void* stream) {
+  const AppendArgs app = {new_latent, new_k_pe, new_slots, kv_cache};
+  return decode_balanced(kFp8, q_len > 1, q_len, q, kv_cache, num_pages, block_table, block_table_stride, seq_lens,
+                         batch, num_heads, page_size, softmax_scale, num_workgroups, out, lse, workspace,
+                         workspace_bytes, flags, check_status, stream, &app);
 }
 
 int mla_decode_rank256_bf16(const void* q, const void* kv_cache, int64_t num_pages, const int32_t* block_table,

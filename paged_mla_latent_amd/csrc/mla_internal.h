@@ -31,6 +31,12 @@ struct DecodeParams {
   int stream_rows;             // non-temporal row loads (no MLA_FLAG_CACHED_ROWS)
   int64_t num_pages;           // pages in the pool (checked build: block ids are tested against it)
   int32_t* check_status;       // checked build: MLA_CHECK_* bits are ORed in here (may be NULL)
+  // The step's new rows, written by the decode itself before it reads them (NULL: none).  New
+  // row i of request b (index b * q_len + i) is context position L_b - q_len + i.
+  const uint16_t* new_latent = nullptr;  // bf16 [B][q_len][512]
+  const uint16_t* new_k_pe = nullptr;    // bf16 [B][q_len][64], or NULL: rope part written as zeros
+  const int64_t* new_slots = nullptr;    // int64 [B][q_len]: slot of each new row; negative = not written
+  uint8_t* cache_w = nullptr;            // the cache again, writable (set with new_latent)
 };
 
 // ------------------------------------------------------------------------------------

@@ -154,6 +154,19 @@ int main() {
     expect(fn(P, P, 100, idx, 64, MLA_MAX_SPARSE_TOKENS, 16, 0.07f, 65535, f, f, P, 1, 0, nullptr, nullptr) ==
                MLA_ERR_WORKSPACE, "sparse largest workspace");
   }
+  // decodes that write the step's new rows: the longest names, a missing new_slots, a NULL new_k_pe
+  for (auto fn : {mla_decode_append_bf16, mla_decode_append_fp8_656, mla_decode_append_balanced_bf16,
+                  mla_decode_append_balanced_fp8_656}) {
+    const int32_t* i32 = static_cast<const int32_t*>(P);
+    const int64_t* slots = static_cast<const int64_t*>(P);
+    float* f = static_cast<float*>(P);
+    expect(fn(P, P, nullptr, slots, P, 10, i32, 4, i32, 2, 4, 16, 64, 0.07f, 1, f, f, P, 1 << 30, 0, nullptr,
+              nullptr) == MLA_ERR_ARCH, "append valid without k_pe");
+    expect(fn(P, P, P, nullptr, P, 10, i32, 4, i32, 2, 4, 16, 64, 0.07f, 1, f, f, P, 1 << 30, 0, nullptr,
+              nullptr) == MLA_ERR_NULL && std::strstr(mla_last_error_message(), "new_slots"), "append null slots");
+    expect(fn(P, P, P, slots, P, 10, i32, 4, i32, 2, 17, 4, 64, 0.07f, 1, f, f, P, 1 << 30, 0, nullptr,
+              nullptr) == MLA_ERR_SHAPE, "append q_len 17");
+  }
   for (int st = -3; st < 10; ++st) expect(std::strlen(mla_status_string(st)) > 0, "status string");
 
   // the host precondition check against the reference on random tables (ragged, with -1 tails,

@@ -220,6 +220,58 @@ def test_mtp_balanced_workspace_counts_query_rows(lib, fn):
     assert rc == 3 and "aligned" in msg
 
 
+APPEND = ["mla_decode_append_bf16", "mla_decode_append_fp8_656", "mla_decode_append_balanced_bf16",
+          "mla_decode_append_balanced_fp8_656"]
+
+
+def _append(lib, fn, **kw):
+    args = dict(q=P, nl=P, npe=P, ns=P, kv=P, num_pages=10, bt=P, stride=4, lens=P, batch=2, q_len=1, heads=16,
+                ps=64, scale=0.07, count=1, out=P, lse=P, ws=P, ws_bytes=1 << 30, flags=0, cs=None)
+    args.update(kw)
+    rc = getattr(lib, fn)(args["q"], args["nl"], args["npe"], args["ns"], args["kv"], args["num_pages"], args["bt"],
+                          args["stride"], args["lens"], args["batch"], args["q_len"], args["heads"], args["ps"],
+                          args["scale"], args["count"], args["out"], args["lse"], args["ws"], args["ws_bytes"],
+                          args["flags"], args["cs"], None)
+    return rc, lib.mla_last_error_message().decode()
+
+
+@pytest.mark.parametrize("fn", APPEND)
+@pytest.mark.parametrize("field", ["q", "nl", "ns", "kv", "bt", "lens", "out", "lse"])
+def test_append_rejects_null(lib, fn, field):
+    rc, msg = _append(lib, fn, **{field: None})
+    assert rc == 1 and "NULL" in msg and fn in msg
+
+
+@pytest.mark.parametrize("fn", APPEND)
+@pytest.mark.parametrize("field", ["nl", "npe", "ns"])
+def test_append_rejects_misaligned_rows(lib, fn, field):
+    rc, msg = _append(lib, fn, **{field: MIS})
+    assert rc == 3 and "aligned" in msg and fn in msg
+
+
+@pytest.mark.parametrize("fn", APPEND)
+@pytest.mark.parametrize("kw, word", [
+    (dict(q_len=0), "q_len"), (dict(q_len=17), "q_len"), (dict(q_len=5, heads=16), "q_len * num_heads"),
+    (dict(heads=0), "num_heads"), (dict(batch=0), "batch"), (dict(ps=0), "page_size"),
+    (dict(scale=float("nan")), "softmax_scale"),
+])
+def test_append_rejects_bad_shapes(lib, fn, kw, word):
+    rc, msg = _append(lib, fn, **kw)
+    assert rc == 2 and word in msg and fn in msg
+
+
+def test_append_takes_no_k_pe_and_the_schedules_counts(lib):
+    # a NULL new_k_pe is valid (rope part written as zeros): only the missing device stops it
+    for fn in APPEND:
+        assert _append(lib, fn, npe=None)[0] == 5
+    rc, msg = _append(lib, "mla_decode_append_bf16", count=0)
+    assert rc == 2 and "num_splits" in msg
+    rc, msg = _append(lib, "mla_decode_append_balanced_fp8_656", count=-1)
+    assert rc == 2 and "num_workgroups" in msg
+    rc, msg = _append(lib, "mla_decode_append_fp8_656", count=4, ws=None)
+    assert rc == 4 and "workspace" in msg
+
+
 def test_merge_balanced_takes_verify_rows(lib):
     need = mla.mla_decode_balanced_workspace_size(4, 64, 256)
     # 64 query rows per request (q_len 4 x 16 heads): valid, only the missing device stops it

@@ -1,0 +1,168 @@
+"""Decode steps that write their own new rows (mla_decode_append_*), against the two-call form.
+
+Each case builds two device pools holding every context row except the step's new ones, whose
+slots keep the NaN poison.  Pool B gets the new rows from mla_cache_write and is decoded by the
+plain call (mla_decode_mtp_* / mla_decode_mtp_balanced_*); pool A is handed to the append call
+with the same rows.  The outputs must be bit-identical (the same kernels read the same bytes),
+pool A must end byte-identical to pool B (the rows are encoded as the cache write encodes them;
+rows at negative positions are not written), and the output meets the oracle.  A read of a new
+row before its store would return the poison and turn the output into NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_mla_latent_amd as mla
+import workloads
+from gpu_util import FMT_CODE, OUT_REL, LSE_ABS, bf16_dev, device_pool, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _new_rows(w, T, free_slot):
+    """Rows of positions L - T .. L - 1 of every request, [B, T, ...]; a negative position gets the
+    (unused) slot free_slot, which the append call must leave alone, and zero rows."""
+    B, ps = w.batch, w.page_size
+    lat = np.zeros((B, T, 512), np.uint16)
+    pe = np.zeros((B, T, 64), np.uint16)
+    slots = np.full((B, T), free_slot, np.int64)
+    for b in range(B):
+        L = int(w.seq_lens[b])
+        for i in range(T):
+            P = L - T + i
+            if P < 0:
+                continue
+            s = oracle.slot_of(w.block_table, b, P, ps)
+            r = int(np.searchsorted(w.slots, s))
+            assert w.slots[r] == s
+            lat[b, i], pe[b, i], slots[b, i] = w.latent[r], w.k_pe[r], s
+    return lat, pe, slots
+
+
+def _pools(w, slots_new):
+    """Device pool without the new rows (their slots poisoned), twice."""
+    keep = ~np.isin(w.slots, slots_new[slots_new >= 0])
+    a = device_pool(w, latent=w.latent[keep], k_pe=w.k_pe[keep], slots=w.slots[keep])
+    return a, a.clone()
+
+
+def _run_case(w, T, q, balanced, count, free_slot):
+    lat, pe, slots = _new_rows(w, T, free_slot)
+    pa, pb = _pools(w, slots)
+    qd, bt, lens = bf16_dev(q), torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    ld, ped, sd = bf16_dev(lat), bf16_dev(pe), torch.from_numpy(slots).cuda()
+    # two-call form: the rows at non-negative positions only
+    live = slots.reshape(-1) != free_slot
+    mla.mla_cache_write(bf16_dev(lat.reshape(-1, 512)[live]), bf16_dev(pe.reshape(-1, 64)[live]),
+                        torch.from_numpy(slots.reshape(-1)[live]).cuda(), pb, FMT_CODE[w.fmt])
+    if balanced:
+        plain = mla.mla_decode_mtp_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_balanced_fp8_656
+        fused = mla.mla_decode_append_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_append_balanced_fp8_656
+        ob, lb = plain(qd, pb, bt, lens, w.scale, num_workgroups=count)
+        oa, la = fused(qd, ld, ped, sd, pa, bt, lens, w.scale, num_workgroups=count)
+    else:
+        plain = mla.mla_decode_mtp_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_fp8_656
+        fused = mla.mla_decode_append_bf16 if w.fmt == "bf16" else mla.mla_decode_append_fp8_656
+        ob, lb = plain(qd, pb, bt, lens, w.scale, num_splits=count)
+        oa, la = fused(qd, ld, ped, sd, pa, bt, lens, w.scale, num_splits=count)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(la, lb), "append call differs from cache write + decode"
+    assert torch.equal(pa.view(torch.uint8), pb.view(torch.uint8)), "pools differ after the append call"
+    return oa.cpu().numpy().astype(np.float64), la.cpu().numpy().astype(np.float64)
+
+
+def _oracle_check(w, T, q, out, lse, what):
+    ph = w.poisoned_pool()
+    oracle.cache_write(ph, w.latent, w.k_pe, w.slots, w.fmt)
+    ref_o, ref_l = oracle.decode_mtp(q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt)
+    worst = 0.0
+    for b in range(w.batch):
+        for t in range(T):
+            sees = int(w.seq_lens[b]) - T + 1 + t
+            if sees <= 0:
+                assert np.isneginf(lse[b, t]).all() and (out[b, t] == 0).all(), f"{what} b={b} t={t}"
+                continue
+            err = np.abs(out[b, t] - ref_o[b, t]).max(axis=1)
+            scale = np.abs(ref_o[b, t]).max(axis=1)
+            assert (err <= OUT_REL * scale).all(), f"{what} b={b} t={t}: out rel err {(err / scale).max():.3e}"
+            assert (np.abs(lse[b, t] - ref_l[b, t]) <= LSE_ABS).all(), f"{what} b={b} t={t}: lse"
+            worst = max(worst, float((err / scale).max()))
+    say(f"  {what}: worst out rel err {worst:.2e}")
+
+
+# Lengths: empty, shorter than q_len, 66 (with page size 16 and 3 partitions its last partition holds
+# two tokens, so four new rows straddle a partition boundary), ragged others.
+LENS = [3000, 0, 1, 66, 17, 700, 64, 1500]
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("T,H", [(1, 16), (2, 16), (4, 16), (8, 8)])
+def test_append_matches_write_then_decode(fmt, T, H):
+    w = workloads.make_workload(f"append_{fmt}_{T}", seq_lens=LENS, heads=H, page_size=16, num_pages=420, fmt=fmt,
+                                seed=40 + T)
+    free_slot = min(set(range(w.num_pages)) - set((w.slots // w.page_size).tolist())) * w.page_size + 3  # unused page
+    q = workloads.bf16_bits(np.random.default_rng(50 + T).standard_normal((w.batch, T, H, 576)).astype(np.float32))
+    for balanced, count in ((False, 1), (False, 3), (False, 16), (True, 3), (True, 64), (True, 256), (True, 12000)):
+        what = f"append {fmt} T={T} H={H} {'W' if balanced else 'S'}={count}"
+        say(f"case {what}")
+        out, lse = _run_case(w, T, q, balanced, count, free_slot)
+        if count in (3, 256):
+            _oracle_check(w, T, q, out, lse, what)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_append_balanced_partials_then_merge(fmt):
+    """Balanced append call with out == lse == NULL, then mla_merge_lse_balanced: the one-call bits."""
+    T, H, W = 2, 16, 40
+    w = workloads.make_workload("append_two_step", seq_lens=[900, 0, 3, 2500], heads=H, page_size=64,
+                                num_pages=80, fmt=fmt, seed=61)
+    q = workloads.bf16_bits(np.random.default_rng(62).standard_normal((w.batch, T, H, 576)).astype(np.float32))
+    lat, pe, slots = _new_rows(w, T, -1)
+    fused = mla.mla_decode_append_balanced_bf16 if fmt == "bf16" else mla.mla_decode_append_balanced_fp8_656
+    pa, _ = _pools(w, slots)
+    pb = pa.clone()
+    args = (bf16_dev(q), bf16_dev(lat), bf16_dev(pe), torch.from_numpy(slots).cuda())
+    bt, lens = torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    o1, l1 = fused(*args, pa, bt, lens, w.scale, num_workgroups=W)
+    ws = fused(*args, pb, bt, lens, w.scale, num_workgroups=W, partials_only=True)
+    o2, l2 = mla.mla_merge_lse_balanced(ws, w.batch, T * H, W)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(w.batch, T * H, -1), o2) and torch.equal(l1.view(w.batch, T * H), l2)
+    assert torch.equal(pa.view(torch.uint8), pb.view(torch.uint8))
+
+
+@pytest.mark.parametrize("name,balanced,count", [("long_context", False, 64), ("fp8_ragged", True, 256)])
+def test_append_full_size(name, balanced, count):
+    """The bench's step configurations at full size: the append call gives the bits of cache write +
+    decode, and the pools agree on every new row."""
+    w = workloads.NAMED[name]()
+    T = 1
+    say(f"case append full size {name} {'W' if balanced else 'S'}={count}")
+    q = w.q.reshape(w.batch, 1, w.heads, 576)
+    lat, pe, slots = _new_rows(w, T, -1)
+    pa, pb = _pools(w, slots)
+    live = slots.reshape(-1) >= 0
+    qd, bt, lens = bf16_dev(q), torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    mla.mla_cache_write(bf16_dev(lat.reshape(-1, 512)[live]), bf16_dev(pe.reshape(-1, 64)[live]),
+                        torch.from_numpy(slots.reshape(-1)[live]).cuda(), pb, FMT_CODE[w.fmt])
+    if balanced:
+        plain = mla.mla_decode_mtp_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_balanced_fp8_656
+        fused = mla.mla_decode_append_balanced_bf16 if w.fmt == "bf16" else mla.mla_decode_append_balanced_fp8_656
+        ob, lb = plain(qd, pb, bt, lens, w.scale, num_workgroups=count)
+        oa, la = fused(qd, bf16_dev(lat), bf16_dev(pe), torch.from_numpy(slots).cuda(), pa, bt, lens, w.scale,
+                       num_workgroups=count)
+    else:
+        plain = mla.mla_decode_mtp_bf16 if w.fmt == "bf16" else mla.mla_decode_mtp_fp8_656
+        fused = mla.mla_decode_append_bf16 if w.fmt == "bf16" else mla.mla_decode_append_fp8_656
+        ob, lb = plain(qd, pb, bt, lens, w.scale, num_splits=count)
+        oa, la = fused(qd, bf16_dev(lat), bf16_dev(pe), torch.from_numpy(slots).cuda(), pa, bt, lens, w.scale,
+                       num_splits=count)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    R = w.row_bytes
+    idx = torch.from_numpy(slots.reshape(-1)[live]).cuda()
+    assert torch.equal(pa.view(torch.uint8).view(-1, R).index_select(0, idx),
+                       pb.view(torch.uint8).view(-1, R).index_select(0, idx))
+    seen = w.seq_lens > 0
+    assert torch.isfinite(oa[torch.from_numpy(seen).cuda()]).all()
