@@ -128,9 +128,9 @@ LLC_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 
 def _read_ceiling(dev, stream, gib=2, reps=20, workgroups=2048):
     """Same-run streaming-read reference: median HIP-event time of `mla_bench_stream_read`
-    (libmla_bench.so: every 16-byte word of a `gib` GiB buffer read once by a grid-stride walk,
-    eight loads in flight per thread), with plain loads and with the non-temporal hint; `gbs`
-    is the faster of the two.  This is what this machine streams from HBM with a kernel that does
+    (libmla_bench.so: every 16-byte word of a `gib` GiB buffer read once, each workgroup reading a
+    contiguous range, four loads in flight per thread), with plain loads and with the non-temporal
+    hint; `gbs` is the faster of the two.  This is what this machine streams from HBM with a kernel that does
     nothing but read."""
     import ctypes
     import torch
@@ -244,7 +244,7 @@ def _cpu_baseline(w, requests, nope=False, q_mtp=None, geometry="mla", min_secon
 
 
 KERNEL_SOURCES = ("paged_mla_latent_amd/csrc/decode.hip", "paged_mla_latent_amd/csrc/mla_device.h",
-                  "paged_mla_latent_amd/csrc/mla_internal.h")
+                  "paged_mla_latent_amd/csrc/mla_internal.h", "paged_mla_latent_amd/csrc/cache_rows.h")
 
 
 def _profiled_traffic(workload: str, kernel: str):

@@ -593,7 +593,7 @@ __device__ __forceinline__ void append_end(const DecodeParams& p, int b, int64_t
   }
 }
 
-template <class Fmt, int G, bool kGla2, bool kSparse = false>
+template <class Fmt, int G, bool kGla2, bool kSparse = false, bool kAppend = false>
 __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* smem, int b, int64_t L,
                                                int64_t t0_abs, int64_t t1_abs, float* out, float* lse) {
   static_assert(!kSparse || (G == 1 && !kGla2), "index lists: single-token queries");
@@ -621,9 +621,9 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
   // partition, clamped to its end.
   const int64_t lim = L - p.q_len + 1 + (row < R ? row / H : 0);
   const int n_vis = (int)(min(rg.t1, lim) - rg.t0);
-  // the step's new rows in this segment (none for index lists)
+  // the step's new rows in this segment (kernels of the append calls only)
   AppendRows app;
-  if constexpr (!kSparse) app = append_begin<Fmt>(p, b, L, rg.t0, rg.t1, wave, lane);
+  if constexpr (kAppend) app = append_begin<Fmt>(p, b, L, rg.t0, rg.t1, wave, lane);
 
   // q as the B operand of the QK MFMA: lane (row m, slice g) holds q[row][32j + 8g .. +8].
   constexpr int QS = Fmt::kQSteps;
@@ -868,7 +868,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
     }
 #pragma unroll
     for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
-    if constexpr (!kSparse) append_end<Fmt>(p, b, L, app, wave, lane, bad);
+    if constexpr (kAppend) append_end<Fmt>(p, b, L, app, wave, lane, bad);
     wait_vmcnt<0>();
     if (first_tiles) {
 #pragma unroll
@@ -904,7 +904,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& p, uint8_t* s
     for (int t = 0; t < NB - 1; ++t)
 #pragma unroll
       for (int i = 0; i < TPL; ++i) asm volatile("" ::"v"(page_first[t][i]));
-    if constexpr (!kSparse) append_end<Fmt>(p, b, L, app, wave, lane, bad);
+    if constexpr (kAppend) append_end<Fmt>(p, b, L, app, wave, lane, bad);
     if (first_tiles) {
 #pragma unroll
       for (int t = 0; t < NB - 1; ++t) {
@@ -1152,7 +1152,7 @@ __device__ __forceinline__ void score_tiles_half(const uint8_t* const (&tile)[4]
   }
 }
 
-template <class Fmt>
+template <class Fmt, bool kAppend = false>
 __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t* smem, int b, int64_t L,
                                                   int64_t t0_abs, int64_t t1_abs, float* out, float* lse) {
   using CS = ColSplit<Fmt>;
@@ -1174,7 +1174,8 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
   const int row = 16 * wave + m;  // this lane's query row in the scores (row group = wave)
   const int64_t lim = L - p.q_len + 1 + (row < R ? row / H : 0);
   const int n_vis = (int)(min(rg.t1, lim) - rg.t0);
-  const AppendRows app = append_begin<Fmt>(p, b, L, rg.t0, rg.t1, wave, lane);  // the step's new rows here
+  AppendRows app;  // the step's new rows in this segment (kernels of the append calls only)
+  if constexpr (kAppend) app = append_begin<Fmt>(p, b, L, rg.t0, rg.t1, wave, lane);
 
   // q as the B operand of the QK MFMA: lane (row m, slice g) holds q[row][32j + 8g .. + 8].  bf16:
   // the own row group's 18 K-steps.  fp8: [0, 9) the own row group's, [9, 18) the partner row
@@ -1281,7 +1282,7 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
       for (int t = 0; t < NB - 1; ++t) fetch_page(tile_of_step(t), xlds + 256 * t);
 #pragma unroll
       for (int j = 0; j < QS; ++j) asm volatile("" : "+a"(qf[j]));
-      append_end<Fmt>(p, b, L, app, wave, lane, bad);
+      if constexpr (kAppend) append_end<Fmt>(p, b, L, app, wave, lane, bad);
       wait_vmcnt<0>();
 #pragma unroll
       for (int t = 0; t < NB - 1; ++t) {
@@ -1302,7 +1303,7 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
       for (int t = 0; t < NB - 1; ++t)
 #pragma unroll
         for (int i = 0; i < TPL; ++i) asm volatile("" ::"v"(page_first[t][i]));
-      append_end<Fmt>(p, b, L, app, wave, lane, bad);
+      if constexpr (kAppend) append_end<Fmt>(p, b, L, app, wave, lane, bad);
 #pragma unroll
       for (int t = 0; t < NB - 1; ++t) {
         fetch_page(tile_of_step(t + NB - 1), slot_lds(t + NB - 1));
@@ -1540,16 +1541,21 @@ constexpr int kernel_smem_bytes() {
   }
 }
 
-template <class Fmt, int G, bool kGla2>
+template <class Fmt, int G, bool kGla2, bool kAppend>
 __device__ __forceinline__ void decode_rows(const DecodeParams& p, uint8_t* smem, int b, int64_t L, int64_t t0,
                                             int64_t t1, float* out, float* lse) {
   if constexpr (kColSplit<Fmt, G>) {
     static_assert(!kGla2, "GLA-g2 decodes one row group");
-    decode_segment_cs<Fmt>(p, smem, b, L, t0, t1, out, lse);
+    decode_segment_cs<Fmt, kAppend>(p, smem, b, L, t0, t1, out, lse);
   } else {
-    decode_segment<Fmt, G, kGla2>(p, smem, b, L, t0, t1, out, lse);
+    decode_segment<Fmt, G, kGla2, false, kAppend>(p, smem, b, L, t0, t1, out, lse);
   }
 }
+
+// Rows whose kernels also come in the form that writes the step's new rows (the append calls):
+// the 576-value rows with their rope part.
+template <class Fmt>
+constexpr bool kAppendable = std::is_same<Fmt, Bf16Rows<512, 64>>::value || std::is_same<Fmt, Fp8Rows<64>>::value;
 
 // Prefix sums over the requests of a batch of B <= kMaxBalancedBatch: out[0] = 0, out[b + 1] =
 // out[b] + value(b).  Thread t takes requests 4t .. 4t + 3; the 256 sums are scanned with wave
@@ -1612,7 +1618,7 @@ __device__ __forceinline__ int find_request(const T* pre, int B, T x) {
 // partitions (request-major), the rest write the empty ones' (0, -inf), so no non-empty
 // partition waits behind empty ones for a compute unit.  The partial slots (s, b) and the
 // merge are the same either way.
-template <class Fmt, int G, bool kGla2 = false>
+template <class Fmt, int G, bool kGla2 = false, bool kAppend = false>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kernel_smem_bytes<Fmt, G>()];
   constexpr int kOut = kGla2 ? 256 : Fmt::kLatent;
@@ -1660,7 +1666,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   const bool split = p.num_splits > 1;
   float* out = split ? p.part_out + ((int64_t)s * p.batch * R + row_b) * kOut : p.out + row_b * kOut;
   float* lse = split ? p.part_lse + (int64_t)s * p.batch * R + row_b : p.lse + row_b;
-  decode_rows<Fmt, G, kGla2>(p, smem, b, L, rg.t0, rg.t1, out, lse);
+  decode_rows<Fmt, G, kGla2, kAppend>(p, smem, b, L, rg.t0, rg.t1, out, lse);
 }
 
 // Decode over per-query index lists: grid (query token, partition).  Query t attends to the
@@ -1687,7 +1693,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_sparse_kernel(DecodePar
 // b occupies [v[b], v[b + 1]) with v[b + 1] - v[b] = kSegmentCost + L_b for L_b > 0 (0 for
 // an empty request), its tokens at the last L_b positions; the first kSegmentCost stand
 // for the start-up of a segment (first loads in flight, epilogue), measured at about as
-// long as streaming that many rows.  The axis, of length V = v[B], is cut into W =
+// long as streaming that many rows.  (The single-token kernels that write the step's new
+// rows add kAppendTail tokenless positions after the tokens, for the wait on those stores.)  The axis, of length V = v[B], is cut into W =
 // min(gridDim.x, V) equal ranges [floor(wV/W), floor((w+1)V/W)); workgroup w decodes the
 // tokens of every request its range meets (possibly none, when the range lies in a
 // request's start-up part) into partial slot b + w (unique: along the axis, b or w grows at
@@ -1702,7 +1709,7 @@ constexpr int kAxisBytes = (kWaves + kMaxBalancedBatch + 1) * 8;
 template <class Fmt, int G>
 constexpr bool kAxisApart = kernel_smem_bytes<Fmt, G>() + kAxisBytes <= 160 * 1024;
 
-template <class Fmt, int G, bool kGla2 = false>
+template <class Fmt, int G, bool kGla2 = false, bool kAppend = false>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParams p) {
   constexpr int kOut = kGla2 ? 256 : Fmt::kLatent;  // output values per query row
   constexpr int kTileMem = kernel_smem_bytes<Fmt, G>();
@@ -1714,9 +1721,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
   asm volatile("" ::"s"(grid_w));
   const int B = p.batch;
   uint32_t lbad = 0;  // checked build: a length outside [0, bt_stride * page_size]
+  constexpr int64_t kTail = (kAppend && G == 1) ? kAppendTail : 0;  // see kAppendTail
   auto cost = [&](int r) -> int64_t {
     const int64_t L = checked_len(p.seq_lens[r], p.bt_stride, p.page_size, lbad);
-    return L > 0 ? L + kSegmentCost : 0;
+    return L > 0 ? L + kSegmentCost + kTail : 0;
   };
   // The axis v [B + 1] is scanned into LDS; each workgroup then keeps the start of its first
   // request and walks forward from there.  Where the LDS has room the axis stays apart from the
@@ -1752,46 +1760,65 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_flat_kernel(DecodeParam
       continue;
     }
     const int64_t s0 = v0 + kSegmentCost;  // axis position of token 0
-    const int64_t L = v1 - s0;
+    const int64_t L = v1 - s0 - kTail;
     // Token boundaries fall on multiples of 16 (a tile), so that the tiles of a segment start
     // where a page's tiles do; both workgroups that share a boundary round it alike.
     auto on_tile = [&](int64_t t) -> int64_t { return t >= L ? L : t & ~(int64_t)(kTile - 1); };
     const int64_t t0 = on_tile(max(lo, s0) - s0);
     const int64_t t1 = on_tile(max(min(hi, v1) - s0, (int64_t)0));  // 0: the range holds start-up only
     const int64_t slot = (int64_t)b + w;
-    decode_rows<Fmt, G, kGla2>(p, smem, b, L, t0, max(t0, t1), p.part_out + slot * R * kOut,
+    decode_rows<Fmt, G, kGla2, kAppend>(p, smem, b, L, t0, max(t0, t1), p.part_out + slot * R * kOut,
                                p.part_lse + slot * R);
     __syncthreads();  // the epilogue's LDS reads finish before the next segment's loads land
     v0 = v1;
   }
 }
 
-template <class Fmt>
-hipError_t launch(const DecodeParams& p, hipStream_t stream) {
+template <class Fmt, bool kAppend>
+hipError_t launch_rows(const DecodeParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.batch, (unsigned)p.num_splits);
   const int R = p.q_len * p.heads;
   if (R <= 16)
-    hipLaunchKernelGGL((decode_kernel<Fmt, 1>), grid, dim3(kWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<Fmt, 1, false, kAppend>), grid, dim3(kWaves * 64), 0, stream, p);
   else if (R <= 32)
-    hipLaunchKernelGGL((decode_kernel<Fmt, 2>), grid, dim3(kWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<Fmt, 2, false, kAppend>), grid, dim3(kWaves * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<Fmt, 4>), grid, dim3(kWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<Fmt, 4, false, kAppend>), grid, dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+// The per-request launch; with the step's new rows (p.new_latent) the kernels that write them.
+template <class Fmt>
+hipError_t launch(const DecodeParams& p, hipStream_t stream) {
+  if constexpr (kAppendable<Fmt>) {
+    if (p.new_latent != nullptr) return launch_rows<Fmt, true>(p, stream);
+  }
+  if (p.new_latent != nullptr) return hipErrorInvalidValue;
+  return launch_rows<Fmt, false>(p, stream);
 }
 
 // Balanced launches: one row group per 16 of the R = q_len x heads query rows (kMaxG = 1: the
 // single-token geometries).
-template <class Fmt, int kMaxG>
-hipError_t launch_flat(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
+template <class Fmt, int kMaxG, bool kAppend>
+hipError_t launch_flat_rows(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
   const int R = p.q_len * p.heads;
   const dim3 grid((unsigned)num_workgroups), block(kWaves * 64);
   if (kMaxG == 1 || R <= 16)
-    hipLaunchKernelGGL((decode_flat_kernel<Fmt, 1>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_flat_kernel<Fmt, 1, false, kAppend>), grid, block, 0, stream, p);
   else if (R <= 32)
-    hipLaunchKernelGGL((decode_flat_kernel<Fmt, kMaxG >= 2 ? 2 : 1>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_flat_kernel<Fmt, kMaxG >= 2 ? 2 : 1, false, kAppend>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_flat_kernel<Fmt, kMaxG>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_flat_kernel<Fmt, kMaxG, false, kAppend>), grid, block, 0, stream, p);
   return hipGetLastError();
+}
+
+template <class Fmt, int kMaxG>
+hipError_t launch_flat(const DecodeParams& p, int num_workgroups, hipStream_t stream) {
+  if constexpr (kAppendable<Fmt>) {
+    if (p.new_latent != nullptr) return launch_flat_rows<Fmt, kMaxG, true>(p, num_workgroups, stream);
+  }
+  if (p.new_latent != nullptr) return hipErrorInvalidValue;
+  return launch_flat_rows<Fmt, kMaxG, false>(p, num_workgroups, stream);
 }
 
 }  // namespace

@@ -3,10 +3,12 @@
 Each case builds two device pools holding every context row except the step's new ones, whose
 slots keep the NaN poison.  Pool B gets the new rows from mla_cache_write and is decoded by the
 plain call (mla_decode_mtp_* / mla_decode_mtp_balanced_*); pool A is handed to the append call
-with the same rows.  The outputs must be bit-identical (the same kernels read the same bytes),
-pool A must end byte-identical to pool B (the rows are encoded as the cache write encodes them;
-rows at negative positions are not written), and the output meets the oracle.  A read of a new
-row before its store would return the poison and turn the output into NaN.
+with the same rows.  Pool A must end byte-identical to pool B (the rows are encoded as the cache
+write encodes them; rows at negative positions are not written).  Per-request partitions: the
+outputs must be bit-identical (the same partitions, the same bytes read).  Batch-balanced: the
+append kernels charge every request a tokenless tail on the cost axis, so their ranges differ
+from the plain call's; both outputs meet the oracle.  A read of a new row before its store would
+return the poison and turn the output into NaN.
 """
 import numpy as np
 import pytest
@@ -40,6 +42,11 @@ def _new_rows(w, T, free_slot):
     return lat, pe, slots
 
 
+def _req_slots(w, b):
+    t = np.arange(int(w.seq_lens[b]), dtype=np.int64)
+    return w.block_table[b].astype(np.int64)[t // w.page_size] * w.page_size + t % w.page_size
+
+
 def _pools(w, slots_new):
     """Device pool without the new rows (their slots poisoned), twice."""
     keep = ~np.isin(w.slots, slots_new[slots_new >= 0])
@@ -67,17 +74,23 @@ def _run_case(w, T, q, balanced, count, free_slot):
         ob, lb = plain(qd, pb, bt, lens, w.scale, num_splits=count)
         oa, la = fused(qd, ld, ped, sd, pa, bt, lens, w.scale, num_splits=count)
     torch.cuda.synchronize()
-    assert torch.equal(oa, ob) and torch.equal(la, lb), "append call differs from cache write + decode"
+    if not balanced:
+        assert torch.equal(oa, ob) and torch.equal(la, lb), "append call differs from cache write + decode"
     assert torch.equal(pa.view(torch.uint8), pb.view(torch.uint8)), "pools differ after the append call"
-    return oa.cpu().numpy().astype(np.float64), la.cpu().numpy().astype(np.float64)
+    return ((oa.cpu().numpy().astype(np.float64), la.cpu().numpy().astype(np.float64)),
+            (ob.cpu().numpy().astype(np.float64), lb.cpu().numpy().astype(np.float64)))
 
 
-def _oracle_check(w, T, q, out, lse, what):
+def _oracle(w, q, requests=None):
     ph = w.poisoned_pool()
     oracle.cache_write(ph, w.latent, w.k_pe, w.slots, w.fmt)
-    ref_o, ref_l = oracle.decode_mtp(q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt)
+    return oracle.decode_mtp(q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=requests)
+
+
+def _oracle_check(w, T, ref, out, lse, what, requests=None):
+    ref_o, ref_l = ref
     worst = 0.0
-    for b in range(w.batch):
+    for b in (range(w.batch) if requests is None else requests):
         for t in range(T):
             sees = int(w.seq_lens[b]) - T + 1 + t
             if sees <= 0:
@@ -103,12 +116,15 @@ def test_append_matches_write_then_decode(fmt, T, H):
                                 seed=40 + T)
     free_slot = min(set(range(w.num_pages)) - set((w.slots // w.page_size).tolist())) * w.page_size + 3  # unused page
     q = workloads.bf16_bits(np.random.default_rng(50 + T).standard_normal((w.batch, T, H, 576)).astype(np.float32))
+    ref = _oracle(w, q)
     for balanced, count in ((False, 1), (False, 3), (False, 16), (True, 3), (True, 64), (True, 256), (True, 12000)):
         what = f"append {fmt} T={T} H={H} {'W' if balanced else 'S'}={count}"
         say(f"case {what}")
-        out, lse = _run_case(w, T, q, balanced, count, free_slot)
-        if count in (3, 256):
-            _oracle_check(w, T, q, out, lse, what)
+        (out, lse), (out_b, lse_b) = _run_case(w, T, q, balanced, count, free_slot)
+        if balanced or count == 3:
+            _oracle_check(w, T, ref, out, lse, what)
+        if balanced:
+            _oracle_check(w, T, ref, out_b, lse_b, what + " (two calls)")
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
@@ -134,8 +150,9 @@ def test_append_balanced_partials_then_merge(fmt):
 
 @pytest.mark.parametrize("name,balanced,count", [("long_context", False, 64), ("fp8_ragged", True, 256)])
 def test_append_full_size(name, balanced, count):
-    """The bench's step configurations at full size: the append call gives the bits of cache write +
-    decode, and the pools agree on every new row."""
+    """The bench's step configurations at full size: the pools agree on every new row; per request the
+    append call gives the bits of cache write + decode, batch-balanced the oracle checks the first, a
+    middle and the last non-empty request."""
     w = workloads.NAMED[name]()
     T = 1
     say(f"case append full size {name} {'W' if balanced else 'S'}={count}")
@@ -159,7 +176,17 @@ def test_append_full_size(name, balanced, count):
         oa, la = fused(qd, bf16_dev(lat), bf16_dev(pe), torch.from_numpy(slots).cuda(), pa, bt, lens, w.scale,
                        num_splits=count)
     torch.cuda.synchronize()
-    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    if balanced:
+        live_req = np.flatnonzero(w.seq_lens > 0)
+        req = sorted({int(live_req[0]), int(live_req[len(live_req) // 2]), int(live_req[-1])})
+        ph = w.poisoned_pool()
+        idx = np.unique(np.concatenate([np.searchsorted(w.slots, _req_slots(w, b)) for b in req]))
+        ph.reshape(-1, w.row_bytes)[w.slots[idx]] = oracle.pack_rows(w.latent[idx], w.k_pe[idx], w.fmt)
+        ref = oracle.decode_mtp(q, ph, w.block_table, w.seq_lens, w.page_size, w.scale, w.fmt, requests=req)
+        _oracle_check(w, T, ref, oa.cpu().numpy().astype(np.float64), la.cpu().numpy().astype(np.float64),
+                      f"append full size {name}", requests=req)
+    else:
+        assert torch.equal(oa, ob) and torch.equal(la, lb)
     R = w.row_bytes
     idx = torch.from_numpy(slots.reshape(-1)[live]).cuda()
     assert torch.equal(pa.view(torch.uint8).view(-1, R).index_select(0, idx),
