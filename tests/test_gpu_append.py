@@ -193,3 +193,85 @@ def test_append_full_size(name, balanced, count):
                        pb.view(torch.uint8).view(-1, R).index_select(0, idx))
     seen = w.seq_lens > 0
     assert torch.isfinite(oa[torch.from_numpy(seen).cuda()]).all()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_append_step_replays_from_a_hip_graph(fmt):
+    """A step of the append call (split decode writing its new rows, with the library's merge)
+    captured in a HIP graph gives the eager bits on every replay, eager work between the replays;
+    every replay rewrites the same rows."""
+    T, H, S = 2, 16, 8
+    w = workloads.make_workload("append_graph", seq_lens=[2000, 0, 513, 64], heads=H, page_size=64, num_pages=80,
+                                fmt=fmt, seed=71)
+    q = bf16_dev(workloads.bf16_bits(np.random.default_rng(72).standard_normal((w.batch, T, H, 576))
+                                     .astype(np.float32)))
+    lat, pe, slots = _new_rows(w, T, -1)
+    pool, _ = _pools(w, slots)
+    ld, ped, sd = bf16_dev(lat), bf16_dev(pe), torch.from_numpy(slots).cuda()
+    bt, lens = torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda()
+    ws = torch.empty(mla.mla_decode_workspace_size(w.batch, T * H, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, T, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, T, H), dtype=torch.float32, device="cuda")
+    fn = mla.mla_decode_append_bf16 if fmt == "bf16" else mla.mla_decode_append_fp8_656
+
+    def step():
+        fn(q, ld, ped, sd, pool, bt, lens, w.scale, num_splits=S, out=out, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = (out.clone(), lse.clone(), pool.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.fill_(7.0)  # eager work between the replays
+        lse.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[0]) and torch.equal(lse, eager[1])
+        assert torch.equal(pool.view(torch.uint8), eager[2].view(torch.uint8))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_checked_append_skips_slots_outside_the_pool(fmt):
+    """Checked build: a new row whose slot lies outside [0, num_pages * page_size) is not written and
+    sets MLA_CHECK_BLOCK_ID.  The pool the kernels see is a view into a larger allocation whose
+    pages past the view stay poisoned, so a missing test would show up as a changed byte there,
+    never as a fault; the other requests still meet the oracle."""
+    T, H, guard = 1, 16, 4
+    w = workloads.make_workload("append_checked", seq_lens=[300, 0, 17, 64], heads=H, page_size=16, num_pages=40,
+                                fmt=fmt, seed=73)
+    lat, pe, slots = _new_rows(w, T, -1)
+    keep = ~np.isin(w.slots, slots[slots >= 0])
+    width = 576 if fmt == "bf16" else 656
+    if fmt == "bf16":
+        big = torch.full((w.num_pages + guard, w.page_size, width), 0x7FC0, dtype=torch.int16,
+                         device="cuda").view(torch.bfloat16)
+    else:
+        big = torch.full((w.num_pages + guard, w.page_size, width), 0xFF, dtype=torch.uint8, device="cuda")
+    view = big[: w.num_pages]
+    mla.mla_cache_write(bf16_dev(w.latent[keep]), bf16_dev(w.k_pe[keep]), torch.from_numpy(w.slots[keep]).cuda(),
+                        view, FMT_CODE[fmt])
+    torch.cuda.synchronize()
+    guard_before = big[w.num_pages:].clone()
+    bad = slots.copy()
+    bad[2, 0] = w.num_pages * w.page_size + 5  # request 2's newest row: a slot in the first page past the view
+    fn = mla.mla_decode_append_bf16 if fmt == "bf16" else mla.mla_decode_append_fp8_656
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q = workloads.bf16_bits(np.random.default_rng(74).standard_normal((w.batch, T, H, 576)).astype(np.float32))
+    out, lse = fn(bf16_dev(q), bf16_dev(lat), bf16_dev(pe), torch.from_numpy(bad).cuda(), view,
+                  torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda(), w.scale,
+                  num_splits=3, check_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == mla.MLA_CHECK_BLOCK_ID
+    assert torch.equal(big[w.num_pages:].view(torch.uint8), guard_before.view(torch.uint8)), "a row left the pool"
+    ref = _oracle(w, q, requests=[0, 3])
+    _oracle_check(w, T, ref, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                  f"checked append {fmt}", requests=[0, 3])
