@@ -386,8 +386,9 @@ MLA_API int mla_decode_mtp_balanced_fp8_656(const void* q, const void* kv_cache,
  * kv_cache   written (the new rows, encoded as mla_cache_write encodes them) and read.
  * Precondition (as for the separate calls): new_slots[b][i] is the slot the block table gives
  * for that position, page_id * page_size + position % page_size, and the slots are distinct;
- * the checked build leaves a slot outside [0, num_pages * page_size) unwritten and reports
- * MLA_CHECK_BLOCK_ID.  q_len 1..MLA_MAX_Q_LEN (q_len = 1: the single-token decode).
+ * the checked build leaves a row unwritten, and reports MLA_CHECK_BLOCK_ID, when its slot lies
+ * outside [0, num_pages * page_size) or differs from that slot.  q_len 1..MLA_MAX_Q_LEN
+ * (q_len = 1: the single-token decode).
  * mla_decode_append_*: every other argument, result and error as mla_decode_mtp_*;
  * mla_decode_append_balanced_*: as mla_decode_mtp_balanced_* (num_workgroups, workspace,
  * out == lse == NULL for the partials). */

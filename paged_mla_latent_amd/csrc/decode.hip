@@ -578,9 +578,14 @@ __device__ __forceinline__ void append_end(const DecodeParams& p, int b, int64_t
         in = load_row(p.new_latent + tok * kLatent, p.new_k_pe == nullptr ? nullptr : p.new_k_pe + tok * kRope, lane);
       }
       if (slot < 0) continue;
-      if (kChecked && slot >= slots) {  // a row outside the pool: not written
-        bad |= kCheckBlockId;
-        continue;
+      if constexpr (kChecked) {
+        // a row outside the pool, or not at the slot the block table gives its position: not written
+        const int64_t pos = a.lo + j;
+        const int32_t pg = p.block_table[(int64_t)b * p.bt_stride + pos / p.page_size];
+        if (slot >= slots || slot != (int64_t)pg * p.page_size + pos % p.page_size) {
+          bad |= kCheckBlockId;
+          continue;
+        }
       }
       if constexpr (kFp8) {
         store_row_fp8(in, p.cache_w + slot * (int64_t)kRowBytesFp8, lane);

@@ -241,10 +241,11 @@ def test_append_step_replays_from_a_hip_graph(fmt):
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_checked_append_skips_slots_outside_the_pool(fmt):
-    """Checked build: a new row whose slot lies outside [0, num_pages * page_size) is not written and
-    sets MLA_CHECK_BLOCK_ID.  The pool the kernels see is a view into a larger allocation whose
-    pages past the view stay poisoned, so a missing test would show up as a changed byte there,
-    never as a fault; the other requests still meet the oracle."""
+    """Checked build: a new row whose slot lies outside [0, num_pages * page_size), or differs from
+    the block table's slot for its position, is not written and sets MLA_CHECK_BLOCK_ID.  The pool
+    the kernels see is a view into a larger allocation whose pages past the view stay poisoned, so a
+    missing test would show up as a changed byte there, never as a fault; request 0 still meets the
+    oracle."""
     T, H, guard = 1, 16, 4
     w = workloads.make_workload("append_checked", seq_lens=[300, 0, 17, 64], heads=H, page_size=16, num_pages=40,
                                 fmt=fmt, seed=73)
@@ -263,6 +264,11 @@ def test_checked_append_skips_slots_outside_the_pool(fmt):
     guard_before = big[w.num_pages:].clone()
     bad = slots.copy()
     bad[2, 0] = w.num_pages * w.page_size + 5  # request 2's newest row: a slot in the first page past the view
+    # request 3's newest row: a slot inside the pool but not the block table's for its position
+    # (the row before it); it must stay as it is
+    wrong = int(slots[3, 0]) - 1
+    bad[3, 0] = wrong
+    before_wrong = view.view(torch.uint8).reshape(-1, w.row_bytes)[wrong].clone()
     fn = mla.mla_decode_append_bf16 if fmt == "bf16" else mla.mla_decode_append_fp8_656
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     q = workloads.bf16_bits(np.random.default_rng(74).standard_normal((w.batch, T, H, 576)).astype(np.float32))
@@ -272,6 +278,7 @@ def test_checked_append_skips_slots_outside_the_pool(fmt):
     torch.cuda.synchronize()
     assert st.item() == mla.MLA_CHECK_BLOCK_ID
     assert torch.equal(big[w.num_pages:].view(torch.uint8), guard_before.view(torch.uint8)), "a row left the pool"
-    ref = _oracle(w, q, requests=[0, 3])
+    assert torch.equal(view.view(torch.uint8).reshape(-1, w.row_bytes)[wrong], before_wrong), "a mismatched slot was written"
+    ref = _oracle(w, q, requests=[0])
     _oracle_check(w, T, ref, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
-                  f"checked append {fmt}", requests=[0, 3])
+                  f"checked append {fmt}", requests=[0])
