@@ -600,7 +600,7 @@ def _bench_sparse(args):
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     decode_gbs = step_bytes / (t_decode * 1e-3) / 1e9
     rope = 0 if nope else 64
-    kernel = f"decode_sparse_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}>'}>"
+    kernel = f"decode_sparse_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}, {str(nope).lower()}>'}>"
     result = {
         "metric": "sparse decode GB/s (listed cache rows read)", "value": round(gbs, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -719,7 +719,7 @@ def main():
         decode = mla.mla_decode_bf16 if w.fmt == "bf16" else mla.mla_decode_fp8_656
     groups = 1 if rows <= 16 else (2 if rows <= 32 else 4)
     rope = 0 if nope else 64
-    kernel = f"decode_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}>'}, {groups}>"
+    kernel = f"decode_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}, false>'}, {groups}, false>"
     geom, width, write_rows, row_bytes_read = args.geometry, 512, True, w.row_bytes - (128 if nope else 0)
     if geom != "mla":
         if nope or T > 1:
@@ -728,7 +728,7 @@ def main():
         q = bf16(_geometry_q(w))
         if geom == "gla2":
             decode = mla.mla_decode_gla2_bf16 if w.fmt == "bf16" else mla.mla_decode_gla2_fp8_656
-            kernel = f"decode_kernel<{'Bf16Rows<512, 64>' if w.fmt == 'bf16' else 'Fp8Rows<64>'}, 1, true>"
+            kernel = f"decode_kernel<{'Bf16Rows<512, 64>' if w.fmt == 'bf16' else 'Fp8Rows<64, false>'}, 1, true>"
         else:
             if w.fmt != "bf16":
                 raise SystemExit(f"--geometry {geom} needs a bf16 workload")
@@ -747,7 +747,7 @@ def main():
             decode = {256: mla.mla_decode_rank256_bf16, 768: mla.mla_decode_rank768_bf16,
                       1792: mla.mla_decode_rank1792_bf16}[D]
             write_rows, row_bytes_read = False, 2 * K
-            kernel = "decode_kernel<Bf16Rows<256, 64>, 1>" if D == 256 else f"decode_wide_kernel<{D}>"
+            kernel = "decode_kernel<Bf16Rows<256, 64>, 1, false>" if D == 256 else f"decode_wide_kernel<{D}>"
             if D > 512:
                 ws = torch.empty(max(1, mla.mla_decode_rank_workspace_size(w.batch, rows, S, D)), dtype=torch.uint8,
                                  device=dev)
@@ -767,11 +767,13 @@ def main():
         ws = torch.empty(mla.mla_decode_balanced_workspace_size(w.batch, rows, balanced), dtype=torch.uint8,
                          device=dev)
         S = 1
-        kernel = f"decode_flat_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}>'}, {groups}>"
+        kernel = f"decode_flat_kernel<{f'Bf16Rows<512, {rope}>' if w.fmt == 'bf16' else f'Fp8Rows<{rope}, false>'}, {groups}, false>"
         if gla_balanced:
-            kernel = f"decode_flat_kernel<{'Bf16Rows<512, 64>' if w.fmt == 'bf16' else 'Fp8Rows<64>'}, 1, true>"
+            kernel = f"decode_flat_kernel<{'Bf16Rows<512, 64>' if w.fmt == 'bf16' else 'Fp8Rows<64, false>'}, 1, true>"
     # The decode writes the step's new rows itself (one launch fewer) where it has that call.
     fused_write = write_rows and not args.separate_write and geom == "mla" and not nope
+    if kernel.startswith(("decode_kernel<", "decode_flat_kernel<")):  # the row-writing template argument
+        kernel = kernel[:-1] + (", true>" if fused_write else ", false>")
     if fused_write:
         a_lat, a_pe, a_slots = _append_rows(w, T)
         a_lat, a_pe, a_slots = bf16(a_lat), bf16(a_pe), torch.from_numpy(a_slots).to(dev)
