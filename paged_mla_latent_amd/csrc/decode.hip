@@ -1353,12 +1353,16 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
         }
       }
     }
-    // bf16: one row-load instruction after each K-step of the scores.
-    auto dma_part = [&](int j) {
-      if constexpr (!CS::kFp8) {
-        if (have_next) Fmt::issue_one(next_rows, buf_lds(i + NB - 1), lane, p.stream_rows != 0, j);
-      }
+    // bf16: one row-load instruction after each K-step of the scores; the scores come in three
+    // copies (streaming loads, cached loads, no next tile) chosen once per step, so that no
+    // K-step branches.
+    auto dma_nt = [&](int j) {
+      if constexpr (!CS::kFp8) Fmt::issue_one(next_rows, buf_lds(i + NB - 1), lane, true, j);
     };
+    auto dma_cached = [&](int j) {
+      if constexpr (!CS::kFp8) Fmt::issue_one(next_rows, buf_lds(i + NB - 1), lane, false, j);
+    };
+    auto dma_none = [&](int) {};
     // fp8: the whole tile between the two halves of the scores.
     auto issue_next_fp8 = [&]() {
       if constexpr (CS::kFp8) {
@@ -1387,7 +1391,12 @@ __device__ __forceinline__ void decode_segment_cs(const DecodeParams& p, uint8_t
 #pragma unroll
       for (int v = 0; v < 4; ++v) raw[v] += xi[64 * v];
     } else {
-      score_tiles<Fmt>(tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3), m, g, qf, raw, dma_part);
+      if (!have_next)
+        score_tiles<Fmt>(tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3), m, g, qf, raw, dma_none);
+      else if (p.stream_rows != 0)
+        score_tiles<Fmt>(tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3), m, g, qf, raw, dma_nt);
+      else
+        score_tiles<Fmt>(tile_ptr(i, 0), tile_ptr(i, 1), tile_ptr(i, 2), tile_ptr(i, 3), m, g, qf, raw, dma_cached);
     }
     float sc[4][4];
     float mx = -INFINITY;
